@@ -1,0 +1,620 @@
+// DualQuant dual-scale BCD solver: plain, slow CPU oracle.
+//
+// TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call this
+// file; only the tests, the smoke check and the benchmark's CPU-baseline leg do.  It
+// shares no code, header, table or constant with the GPU library.
+//
+// What it computes (DualQuant, "Dual-scale Calibration-free Weight-and-Activation
+// Quantization for LLMs"; the listing page's abstract, the conference entry's longer
+// abstract, and the news summary's mechanism paragraph):
+//   minimise  || W - diag(r) . Qhat . diag(c) ||_F^2
+// over a row-scale vector r, a column-scale vector c (the activation rescaling beta)
+// and the block fake-quantised matrix Qhat = FQ_f(W ./ (r c^T)), by block coordinate
+// descent whose subproblems have closed forms, projecting each scale update onto the
+// format's admissible set.  The pages print no equation; every reading taken where
+// they are silent is restated next to the code that implements it.
+//
+// Style: brute-force nearest-grid rounding with explicit tie rules, fp64 accumulation,
+// fixed summation order (results do not depend on the thread count).  The quantiser's
+// own decisions are taken in fp32, the precision the block formats are defined in.
+// Build with -ffp-contract=off and without fast-math.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <thread>
+#include <vector>
+
+namespace {
+
+enum Fmt { FMT_INT4 = 0, FMT_MXINT4 = 1, FMT_MXFP4 = 2, FMT_NVFP4 = 3 };
+enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
+enum Status { OK = 0, ERR_NULL = -1, ERR_SHAPE = -2, ERR_FORMAT = -4, ERR_VALUE = -8 };
+
+// ---------------------------------------------------------------- bit helpers
+float f_of(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
+uint32_t u_of(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
+float bf16_to_f32(uint16_t h) { return f_of((uint32_t)h << 16); }
+
+// ---------------------------------------------------------------- threading
+int g_threads = 1;
+
+template <class F>
+void parallel_rows(int64_t n, F fn) {
+  int nt = std::max(1, std::min<int>(g_threads, (int)std::max<int64_t>(1, n)));
+  if (nt == 1) { fn((int64_t)0, n); return; }
+  std::vector<std::thread> th;
+  int64_t chunk = (n + nt - 1) / nt;
+  for (int t = 0; t < nt; ++t) {
+    int64_t b = t * chunk, e = std::min(n, b + chunk);
+    if (b >= e) break;
+    th.emplace_back([=] { fn(b, e); });
+  }
+  for (auto& x : th) x.join();
+}
+
+// ---------------------------------------------------------------- element grids
+// E2M1 (OCP MX v1.0 FP4): 1 sign, 2 exponent, 1 mantissa bit.  The magnitude code k
+// (0..7) encodes these values; the mantissa bit is k & 1.
+const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+// Nearest E2M1 magnitude, ties to the even mantissa bit; anything beyond 6 saturates to
+// 6 (the nearest finite point).  The sign bit is kept, so a negative input that rounds
+// to zero encodes as 0b1000.
+uint8_t e2m1_encode(float x) {
+  // Above 7 the nearest grid point is 6 whatever the value; clamping there keeps the
+  // distances below exact in fp64 for huge inputs.
+  double ax = std::min(std::fabs((double)x), 7.0);
+  int best = 0;
+  double bestd = ax;
+  for (int k = 1; k < 8; ++k) {
+    double d = std::fabs(ax - kE2M1[k]);
+    if (d < bestd || (d == bestd && (k % 2) == 0)) { best = k; bestd = d; }
+  }
+  return (uint8_t)((std::signbit(x) ? 8 : 0) | best);
+}
+double e2m1_decode(uint8_t code) {
+  double m = kE2M1[code & 7];
+  return (code & 8) ? -m : m;
+}
+
+// E4M3FN (OCP FP8): bias 7, no infinities, 0x7F is NaN; largest finite value 448.
+double e4m3_value(int code) {
+  int e = (code >> 3) & 15, m = code & 7;
+  if (e == 0) return std::ldexp((double)m, -9);
+  return std::ldexp(1.0 + m / 8.0, e - 7);
+}
+// Nearest non-negative E4M3FN value (codes 0..126) to x >= 0, ties to the even code;
+// values beyond 448 saturate to 448.
+int e4m3_encode_nonneg(float x, int lowest_code) {
+  double ax = std::min((double)x, 480.0);  // beyond 480 the nearest value is 448 anyway
+  int best = lowest_code;
+  double bestd = std::fabs(ax - e4m3_value(lowest_code));
+  for (int k = lowest_code + 1; k <= 126; ++k) {
+    double d = std::fabs(ax - e4m3_value(k));
+    if (d < bestd || (d == bestd && (k % 2) == 0)) { best = k; bestd = d; }
+  }
+  return best;
+}
+
+// Nearest bfloat16 to a finite fp32 x, ties to even: the two candidates are x with its
+// low 16 bits cleared and the next bf16 further from zero.
+float bf16_round(float x) {
+  uint32_t u = u_of(x);
+  float lo = f_of(u & 0xFFFF0000u);
+  float hi = f_of((u & 0xFFFF0000u) + 0x10000u);
+  double dlo = std::fabs((double)x - (double)lo);
+  double dhi = std::fabs((double)hi - (double)x);
+  if (dlo < dhi) return lo;
+  if (dhi < dlo) return hi;
+  return ((u >> 16) & 1u) ? hi : lo;
+}
+
+// Nearest integer in [-qmax, qmax] to x, ties to even.
+int int_round_clamp(float x, int qmax) {
+  double ax = std::max(-(double)qmax - 1.0, std::min((double)x, (double)qmax + 1.0));
+  int best = -qmax;
+  double bestd = std::fabs(ax + qmax);
+  for (int k = -qmax + 1; k <= qmax; ++k) {
+    double d = std::fabs(ax - k);
+    if (d < bestd || (d == bestd && (k % 2) == 0)) { best = k; bestd = d; }
+  }
+  return best;
+}
+
+// floor(log2 a) for a finite a > 0 (exact, from frexp).
+int floor_log2(float a) {
+  int k;
+  std::frexp((double)a, &k);
+  return k - 1;
+}
+
+// ---------------------------------------------------------------- scale projections
+// After each closed-form update, the scale is projected onto the format's admissible
+// set (the conference abstract: "projecting scales onto their format-specific admissible
+// set after each update").  For a 1-D quadratic D (s - x)^2 the constrained minimiser is
+// the admissible point nearest to x, so "projection" is the nearest point.
+//   MX formats: powers of two 2^k, k in [-127, 127] (E8M0 range); ties go to the larger.
+//   NVFP4:      positive E4M3FN values [2^-9, 448]; ties to the even code.
+//   INT4:       positive bf16 values [2^-126, max bf16]; ties to even.
+float project(int fmt, float x) {
+  if (fmt == FMT_MXINT4 || fmt == FMT_MXFP4) {
+    double best = std::ldexp(1.0, -127), bestd = std::fabs((double)x - best);
+    for (int k = -126; k <= 127; ++k) {
+      double p = std::ldexp(1.0, k), d = std::fabs((double)x - p);
+      if (d <= bestd) { best = p; bestd = d; }  // ascending scan: ties go to the larger
+    }
+    return (float)best;
+  }
+  if (fmt == FMT_NVFP4) return (float)e4m3_value(e4m3_encode_nonneg(x, 1));
+  // INT4: bf16
+  const float lo = std::ldexp(1.0f, -126);
+  const float hi = f_of(0x7F7F0000u);
+  float b = bf16_round(std::min(x, hi));
+  return std::max(lo, std::min(hi, b));
+}
+
+// ---------------------------------------------------------------- block quantisers
+// FQ_f on a normalised row-major matrix V (rows x cols); blocks of g consecutive
+// elements along a row.  Outputs: packed codes (two per byte, low nibble = even
+// column), block scales (bf16 for INT4, E8M0 byte for MX, E4M3 byte for NVFP4),
+// the NVFP4 fp32 tensor scale, and Qhat (the dequantised values, fp32).
+struct FQOut {
+  uint8_t* codes;      // rows * cols / 2
+  void* scales;        // rows * cols / g
+  float* tscale;       // 1 (NVFP4)
+  float* qhat;         // rows * cols (may be null)
+  uint32_t flags;
+};
+
+void put_code(uint8_t* codes, int64_t idx, uint8_t nib) {
+  uint8_t& b = codes[idx >> 1];
+  if (idx & 1) b = (uint8_t)((b & 0x0F) | (nib << 4));
+  else b = (uint8_t)((b & 0xF0) | (nib & 0x0F));
+}
+
+// INT4, symmetric: s = bf16(a / 7), codes = clamp(rint(v * (1/s)), -7, 7) (two's
+// complement nibble), Qhat = q * s.  An all-zero block stores scale 0.
+void fq_int4_row(const float* v, int64_t row, int64_t cols, int g, FQOut& o) {
+  uint16_t* sc = (uint16_t*)o.scales;
+  for (int64_t b = 0; b < cols / g; ++b) {
+    const float* x = v + b * g;
+    float a = 0.0f;
+    for (int k = 0; k < g; ++k) a = std::max(a, std::fabs(x[k]));
+    float s = (a > 0.0f) ? bf16_round(a / 7.0f) : 0.0f;
+    sc[row * (cols / g) + b] = (uint16_t)(u_of(s) >> 16);
+    float is = (s > 0.0f) ? 1.0f / s : 0.0f;
+    for (int k = 0; k < g; ++k) {
+      int q = (s > 0.0f) ? int_round_clamp(x[k] * is, 7) : 0;
+      int64_t idx = row * cols + b * g + k;
+      put_code(o.codes, idx, (uint8_t)(q & 0xF));
+      if (o.qhat) o.qhat[idx] = (float)q * s;
+    }
+  }
+}
+
+// MXINT4 (by analogy with OCP MXINT8): shared exponent e = floor(log2 amax), elements
+// are 4-bit two's-complement integers with an implicit 2^-2, clamped symmetrically to
+// [-7, 7]: q = clamp(rint(v * 2^(2-e)), -7, 7), Qhat = q * 2^(e-2).  Scale byte e+127.
+// MXFP4 (OCP MX v1.0): e = floor(log2 amax) - 2, q = E2M1(v * 2^-e), Qhat = q * 2^e.
+// Exponents clamp to [-127, 127]; an all-zero block stores scale byte 0 and codes 0.
+void fq_mx_row(int fmt, const float* v, int64_t row, int64_t cols, int g, FQOut& o) {
+  uint8_t* sc = (uint8_t*)o.scales;
+  for (int64_t b = 0; b < cols / g; ++b) {
+    const float* x = v + b * g;
+    float a = 0.0f;
+    for (int k = 0; k < g; ++k) a = std::max(a, std::fabs(x[k]));
+    int e = -127;
+    if (a > 0.0f) e = std::max(-127, std::min(127, floor_log2(a) - (fmt == FMT_MXFP4 ? 2 : 0)));
+    sc[row * (cols / g) + b] = (uint8_t)(e + 127);
+    for (int k = 0; k < g; ++k) {
+      int64_t idx = row * cols + b * g + k;
+      uint8_t nib = 0;
+      float qh = 0.0f;
+      if (a > 0.0f) {
+        if (fmt == FMT_MXFP4) {
+          nib = e2m1_encode(std::ldexp(x[k], -e));
+          qh = std::ldexp((float)e2m1_decode(nib), e);
+        } else {
+          int q = int_round_clamp(std::ldexp(x[k], 2 - e), 7);
+          nib = (uint8_t)(q & 0xF);
+          qh = std::ldexp((float)q, e - 2);
+        }
+      }
+      put_code(o.codes, idx, nib);
+      if (o.qhat) o.qhat[idx] = qh;
+    }
+  }
+}
+
+// NVFP4 (NVIDIA's public two-level scheme): A = max|V| over the matrix,
+// s_t = A / 2688 (2688 = 6 * 448), k6 = 1 / (6 s_t); per 16-element block
+// sb = E4M3(a * k6) (saturating), d = sb * s_t, q = E2M1(v * (1/d)), Qhat = q * d.
+// A block whose scale rounds to zero is all zero (flag bit 8).
+void fq_nvfp4_row(const float* v, int64_t row, int64_t cols, float s_t, float k6, FQOut& o,
+                  uint32_t* flags) {
+  uint8_t* sc = (uint8_t*)o.scales;
+  const int g = 16;
+  for (int64_t b = 0; b < cols / g; ++b) {
+    const float* x = v + b * g;
+    float a = 0.0f;
+    for (int k = 0; k < g; ++k) a = std::max(a, std::fabs(x[k]));
+    int sbc = (s_t > 0.0f) ? e4m3_encode_nonneg(a * k6, 0) : 0;
+    if (sbc == 0 && a > 0.0f) *flags |= 8u;
+    sc[row * (cols / g) + b] = (uint8_t)sbc;
+    float d = (float)e4m3_value(sbc) * s_t;
+    float id = (sbc > 0) ? 1.0f / d : 0.0f;
+    for (int k = 0; k < g; ++k) {
+      int64_t idx = row * cols + b * g + k;
+      uint8_t nib = 0;
+      float qh = 0.0f;
+      if (sbc > 0) {
+        nib = e2m1_encode(x[k] * id);
+        qh = (float)e2m1_decode(nib) * d;
+      }
+      put_code(o.codes, idx, nib);
+      if (o.qhat) o.qhat[idx] = qh;
+    }
+  }
+}
+
+int group_ok(int fmt, int g) {
+  if (fmt == FMT_INT4) return g == 64 || g == 128;
+  if (fmt == FMT_MXINT4 || fmt == FMT_MXFP4) return g == 32;
+  if (fmt == FMT_NVFP4) return g == 16;
+  return 0;
+}
+
+// FQ over a normalised matrix; returns the NVFP4 tensor scale through o.tscale.
+void fq_matrix(int fmt, int g, const float* V, int64_t rows, int64_t cols, FQOut& o) {
+  float s_t = 0.0f, k6 = 0.0f;
+  if (fmt == FMT_NVFP4) {
+    float A = 0.0f;
+    for (int64_t i = 0; i < rows * cols; ++i) A = std::max(A, std::fabs(V[i]));
+    s_t = A / 2688.0f;
+    float six_st = 6.0f * s_t;
+    k6 = (s_t > 0.0f) ? 1.0f / six_st : 0.0f;
+    // A tensor scale so small that 1/(6 s_t) overflows leaves no representable block
+    // scale: the whole matrix quantises to zero (flag bit 16).
+    if (!(s_t > 0.0f) || !std::isfinite(k6)) {
+      if (A > 0.0f) o.flags |= 16u;
+      s_t = 0.0f;
+      k6 = 0.0f;
+    }
+    if (o.tscale) *o.tscale = s_t;
+  }
+  std::vector<uint32_t> fl(std::max<int64_t>(rows, 1), 0u);
+  parallel_rows(rows, [&](int64_t b, int64_t e) {
+    for (int64_t i = b; i < e; ++i) {
+      const float* v = V + i * cols;
+      if (fmt == FMT_INT4) fq_int4_row(v, i, cols, g, o);
+      else if (fmt == FMT_NVFP4) fq_nvfp4_row(v, i, cols, s_t, k6, o, &fl[i]);
+      else fq_mx_row(fmt, v, i, cols, g, o);
+    }
+  });
+  // codes of odd/even columns of one row share bytes, and rows never share bytes
+  // (cols is a multiple of the group, hence even), so the row-parallel writes are safe.
+  for (auto f : fl) o.flags |= f;
+}
+
+// Normalisation used by every quantiser call: ir = 1/r, ic = 1/c (fp32, correctly
+// rounded), v = (W * ir) * ic, two fp32 multiplies in that order.
+void normalise(const float* W, int64_t rows, int64_t cols, const float* r, const float* c,
+               float* V) {
+  std::vector<float> ic(cols);
+  for (int64_t j = 0; j < cols; ++j) ic[j] = 1.0f / c[j];
+  parallel_rows(rows, [&](int64_t b, int64_t e) {
+    for (int64_t i = b; i < e; ++i) {
+      float ir = 1.0f / r[i];
+      for (int64_t j = 0; j < cols; ++j) {
+        float t = W[i * cols + j] * ir;
+        V[i * cols + j] = t * ic[j];
+      }
+    }
+  });
+}
+
+void load_w(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, float* out) {
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t j = 0; j < cols; ++j)
+      out[i * cols + j] = (dtype == DT_F32) ? ((const float*)W)[i * ld + j]
+                                            : bf16_to_f32(((const uint16_t*)W)[i * ld + j]);
+}
+
+bool all_finite(const float* x, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    if (!std::isfinite(x[i])) return false;
+  return true;
+}
+
+// F(r, c, Q) = sum_ij (W_ij - r_i Q_ij c_j)^2 in fp64, rows summed in order.
+double recon_error(const float* W, const float* Q, const float* r, const float* c,
+                   int64_t rows, int64_t cols) {
+  std::vector<double> rowF(rows, 0.0);
+  parallel_rows(rows, [&](int64_t b, int64_t e) {
+    for (int64_t i = b; i < e; ++i) {
+      double s = 0.0;
+      for (int64_t j = 0; j < cols; ++j) {
+        double d = (double)W[i * cols + j] - (double)r[i] * (double)Q[i * cols + j] * (double)c[j];
+        s += d * d;
+      }
+      rowF[i] = s;
+    }
+  });
+  double F = 0.0;
+  for (double x : rowF) F += x;
+  return F;
+}
+
+}  // namespace
+
+extern "C" {
+
+void o_set_threads(int n) { g_threads = std::max(1, n); }
+int o_get_threads() { return g_threads; }
+
+// ---- scalar rounding, vectorised for tests
+void o_e2m1_encode(const float* x, uint8_t* code, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) code[i] = e2m1_encode(x[i]);
+}
+void o_e2m1_decode(const uint8_t* code, float* x, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) x[i] = (float)e2m1_decode(code[i]);
+}
+// x >= 0 expected; returns codes 0..126
+void o_e4m3_encode(const float* x, uint8_t* code, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) code[i] = (uint8_t)e4m3_encode_nonneg(x[i], 0);
+}
+void o_e4m3_decode(const uint8_t* code, float* x, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) x[i] = (float)e4m3_value(code[i] & 0x7F);
+}
+void o_bf16_round(const float* x, float* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = bf16_round(x[i]);
+}
+void o_int_round(const float* x, int8_t* q, int64_t n, int qmax) {
+  for (int64_t i = 0; i < n; ++i) q[i] = (int8_t)int_round_clamp(x[i], qmax);
+}
+void o_project(int fmt, const float* x, float* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = project(fmt, x[i]);
+}
+
+// ---- FQ on an already-normalised matrix
+int o_fq(int fmt, int g, const float* V, int64_t rows, int64_t cols, uint8_t* codes,
+         void* scales, float* tscale, float* qhat, uint32_t* flags) {
+  if (!V || !codes || !scales) return ERR_NULL;
+  if (!group_ok(fmt, g)) return ERR_FORMAT;
+  if (rows < 0 || cols < 0 || cols % g) return ERR_SHAPE;
+  if (!all_finite(V, rows * cols)) return ERR_VALUE;
+  FQOut o{codes, scales, tscale, qhat, 0u};
+  if (fmt == FMT_NVFP4 && !tscale) return ERR_NULL;
+  fq_matrix(fmt, g, V, rows, cols, o);
+  if (flags) *flags = o.flags;
+  return OK;
+}
+
+// ---- Qhat-step at given scales: FQ_f(W ./ (r c^T)).  r or c null means ones.
+int o_quantize_weights(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       const float* r, const float* c, int fmt, int g, uint8_t* codes,
+                       void* scales, float* tscale, float* qhat) {
+  if (!W || !codes || !scales) return ERR_NULL;
+  if (!group_ok(fmt, g)) return ERR_FORMAT;
+  if (rows < 0 || cols < 0 || cols % g || ld < cols) return ERR_SHAPE;
+  std::vector<float> Wf(rows * cols), V(rows * cols);
+  load_w(W, dtype, rows, cols, ld, Wf.data());
+  if (!all_finite(Wf.data(), rows * cols)) return ERR_VALUE;
+  std::vector<float> rr(rows, 1.0f), cc(cols, 1.0f);
+  if (r) std::copy(r, r + rows, rr.begin());
+  if (c) std::copy(c, c + cols, cc.begin());
+  normalise(Wf.data(), rows, cols, rr.data(), cc.data(), V.data());
+  return o_fq(fmt, g, V.data(), rows, cols, codes, scales, tscale, qhat, nullptr);
+}
+
+// ---- dequantise codes + scales into Qhat values (fp32)
+int o_dequantize(int fmt, int g, const uint8_t* codes, const void* scales, float tscale,
+                 int64_t rows, int64_t cols, float* out) {
+  if (!codes || !scales || !out) return ERR_NULL;
+  if (!group_ok(fmt, g)) return ERR_FORMAT;
+  if (cols % g) return ERR_SHAPE;
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t j = 0; j < cols; ++j) {
+      int64_t idx = i * cols + j;
+      uint8_t nib = (codes[idx >> 1] >> ((idx & 1) * 4)) & 0xF;
+      int64_t bi = i * (cols / g) + j / g;
+      float v = 0.0f;
+      if (fmt == FMT_INT4) {
+        float s = bf16_to_f32(((const uint16_t*)scales)[bi]);
+        int q = (nib & 8) ? (int)nib - 16 : (int)nib;
+        v = (float)q * s;
+      } else if (fmt == FMT_MXINT4) {
+        int e = (int)((const uint8_t*)scales)[bi] - 127;
+        int q = (nib & 8) ? (int)nib - 16 : (int)nib;
+        v = std::ldexp((float)q, e - 2);
+      } else if (fmt == FMT_MXFP4) {
+        int e = (int)((const uint8_t*)scales)[bi] - 127;
+        v = std::ldexp((float)e2m1_decode(nib), e);
+      } else {
+        int sbc = ((const uint8_t*)scales)[bi];
+        float d = (float)e4m3_value(sbc) * tscale;
+        v = (sbc > 0) ? (float)e2m1_decode(nib) * d : 0.0f;
+      }
+      out[idx] = v;
+    }
+  return OK;
+}
+
+// ---- the BCD solve.
+// Iteration order (a reading: the pages do not fix it): starting from r = c = 1 (or the
+// given initial scales) and Q^0 = FQ(W ./ r c^T), each iteration t = 1..T does
+//   r-step: for every row,    N = sum_j W_ij Q_ij c_j,  D = sum_j (Q_ij c_j)^2,
+//           r_i <- Proj(fl32(N / D)) when D > 0 (else r_i is kept);
+//   c-step: for every column, N = sum_i r_i W_ij Q_ij,  D = sum_i (r_i Q_ij)^2,
+//           c_j <- Proj(fl32(N / D)) when D > 0, using the new r;
+//   Q-step: candidate Qc = FQ(W ./ r c^T), kept only if it does not raise F at the
+//           current scales (ties are kept); otherwise Q stays and the step counts as
+//           rejected.  This safeguard makes the normalised MSE non-increasing, the
+//           property the pages state as Theorem 1(i) (Fig. 2b, Fig. 3b).
+//   stats:  nmse[t] = F(r, c, Q^t) / ||W||^2,
+//           relchg[t] = ||Q^t - Q^{t-1}||_F / ||Q^{t-1}||_F   (0 when the denominator is 0).
+// The two scale steps minimise F exactly over the admissible sets (each is a separable
+// 1-D quadratic whose constrained minimiser is the projection of N/D).
+// Outputs: final r, c; codes, block scales and tensor scale of Q^T; histories
+// nmse[0..T], relchg[0..T] (relchg[0] = 0); rejected-step count; and, when given,
+// the last iteration's unprojected closed-form values r_pre, c_pre (NaN where D = 0).
+int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int g,
+            int iters, const float* r_init, const float* c_init, float* r_out, float* c_out,
+            uint8_t* codes, void* scales, float* tscale, double* nmse_hist, double* relchg_hist,
+            int* rejected_out, float* r_pre, float* c_pre, uint32_t* flags_out) {
+  if (!W || !r_out || !c_out || !codes || !scales) return ERR_NULL;
+  if (!group_ok(fmt, g)) return ERR_FORMAT;
+  if (rows < 0 || cols < 0 || cols % g || ld < cols || iters < 0) return ERR_SHAPE;
+  if (fmt == FMT_NVFP4 && !tscale) return ERR_NULL;
+  const int64_t N = rows * cols;
+  const int64_t nblk = N / g;
+  std::vector<float> Wf(N);
+  load_w(W, dtype, rows, cols, ld, Wf.data());
+  if (!all_finite(Wf.data(), N)) return ERR_VALUE;
+
+  std::vector<float> r(rows, 1.0f), c(cols, 1.0f);
+  if (r_init) std::copy(r_init, r_init + rows, r.begin());
+  if (c_init) std::copy(c_init, c_init + cols, c.begin());
+
+  double normW2 = 0.0;
+  for (int64_t i = 0; i < N; ++i) normW2 += (double)Wf[i] * (double)Wf[i];
+
+  const size_t sc_bytes = (fmt == FMT_INT4) ? 2 : 1;
+  std::vector<float> V(N), Q(N), Qc(N);
+  std::vector<uint8_t> codesA(N / 2), codesC(N / 2);
+  std::vector<uint8_t> scA(nblk * sc_bytes), scC(nblk * sc_bytes);
+  float tsA = 0.0f, tsC = 0.0f;
+  uint32_t flags = 0;
+
+  normalise(Wf.data(), rows, cols, r.data(), c.data(), V.data());
+  {
+    FQOut o{codesA.data(), scA.data(), &tsA, Q.data(), 0u};
+    fq_matrix(fmt, g, V.data(), rows, cols, o);
+    flags |= o.flags;
+  }
+  auto nmse_of = [&](double F) { return normW2 > 0.0 ? F / normW2 : 0.0; };
+  if (nmse_hist) nmse_hist[0] = nmse_of(recon_error(Wf.data(), Q.data(), r.data(), c.data(), rows, cols));
+  if (relchg_hist) relchg_hist[0] = 0.0;
+  int rejected = 0;
+
+  std::vector<double> rowN(rows), rowD(rows), colN(cols), colD(cols);
+  for (int t = 1; t <= iters; ++t) {
+    // r-step
+    parallel_rows(rows, [&](int64_t b, int64_t e) {
+      for (int64_t i = b; i < e; ++i) {
+        double n_ = 0.0, d_ = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+          double u = (double)Q[i * cols + j] * (double)c[j];
+          n_ += (double)Wf[i * cols + j] * u;
+          d_ += u * u;
+        }
+        rowN[i] = n_;
+        rowD[i] = d_;
+      }
+    });
+    for (int64_t i = 0; i < rows; ++i) {
+      float x = std::numeric_limits<float>::quiet_NaN();
+      if (rowD[i] > 0.0) {
+        x = (float)(rowN[i] / rowD[i]);
+        r[i] = project(fmt, x);
+      }
+      if (t == iters && r_pre) r_pre[i] = x;
+    }
+    // c-step (loop interchanged per column range; each column still sums rows in order)
+    parallel_rows(cols, [&](int64_t jb, int64_t je) {
+      for (int64_t j = jb; j < je; ++j) { colN[j] = 0.0; colD[j] = 0.0; }
+      for (int64_t i = 0; i < rows; ++i) {
+        double ri = (double)r[i];
+        for (int64_t j = jb; j < je; ++j) {
+          double q = (double)Q[i * cols + j];
+          colN[j] += ri * (double)Wf[i * cols + j] * q;
+          double u = ri * q;
+          colD[j] += u * u;
+        }
+      }
+    });
+    for (int64_t j = 0; j < cols; ++j) {
+      float x = std::numeric_limits<float>::quiet_NaN();
+      if (colD[j] > 0.0) {
+        x = (float)(colN[j] / colD[j]);
+        c[j] = project(fmt, x);
+      }
+      if (t == iters && c_pre) c_pre[j] = x;
+    }
+    // Q-step with safeguard
+    normalise(Wf.data(), rows, cols, r.data(), c.data(), V.data());
+    FQOut o{codesC.data(), scC.data(), &tsC, Qc.data(), 0u};
+    fq_matrix(fmt, g, V.data(), rows, cols, o);
+    flags |= o.flags;
+    double Fc = recon_error(Wf.data(), Qc.data(), r.data(), c.data(), rows, cols);
+    double Fp = recon_error(Wf.data(), Q.data(), r.data(), c.data(), rows, cols);
+    if (Fc <= Fp) {
+      double num = 0.0, den = 0.0;
+      for (int64_t i = 0; i < N; ++i) {
+        double dq = (double)Qc[i] - (double)Q[i];
+        num += dq * dq;
+        den += (double)Q[i] * (double)Q[i];
+      }
+      if (relchg_hist) relchg_hist[t] = den > 0.0 ? std::sqrt(num) / std::sqrt(den) : 0.0;
+      if (nmse_hist) nmse_hist[t] = nmse_of(Fc);
+      Q.swap(Qc);
+      codesA.swap(codesC);
+      scA.swap(scC);
+      tsA = tsC;
+    } else {
+      ++rejected;
+      if (relchg_hist) relchg_hist[t] = 0.0;
+      if (nmse_hist) nmse_hist[t] = nmse_of(Fp);
+    }
+  }
+  std::copy(r.begin(), r.end(), r_out);
+  std::copy(c.begin(), c.end(), c_out);
+  std::memcpy(codes, codesA.data(), codesA.size());
+  std::memcpy(scales, scA.data(), scA.size());
+  if (fmt == FMT_NVFP4) *tscale = tsA;
+  if (rejected_out) *rejected_out = rejected;
+  if (flags_out) *flags_out = flags;
+  return OK;
+}
+
+// ---- activation path: x' = x * c_j (fp32; exact for admissible c), then FQ_f per
+// token row along the in-dimension.  c null means no rescaling (beta not applied).
+int o_rescale_quantize_acts(const uint16_t* X, int64_t tokens, int64_t cols, int64_t ld,
+                            const float* c, int fmt, int g, uint8_t* codes, void* scales,
+                            float* tscale, float* xq_rescaled) {
+  if (!X || !codes || !scales) return ERR_NULL;
+  if (!group_ok(fmt, g)) return ERR_FORMAT;
+  if (tokens < 0 || cols < 0 || cols % g || ld < cols) return ERR_SHAPE;
+  std::vector<float> Xs(tokens * cols);
+  for (int64_t t = 0; t < tokens; ++t)
+    for (int64_t j = 0; j < cols; ++j) {
+      float x = bf16_to_f32(X[t * ld + j]);
+      Xs[t * cols + j] = c ? x * c[j] : x;
+    }
+  if (!all_finite(Xs.data(), tokens * cols)) return ERR_VALUE;
+  return o_fq(fmt, g, Xs.data(), tokens, cols, codes, scales, tscale, xq_rescaled, nullptr);
+}
+
+// ---- activation SQNR in the activation domain: xhat = deq(FQ(x * c)) / c,
+// SQNR = 10 log10( sum x^2 / sum (x - xhat)^2 ).  c null means ones.
+double o_act_sqnr(const uint16_t* X, int64_t tokens, int64_t cols, int64_t ld, const float* c,
+                  int fmt, int g, const uint8_t* codes, const void* scales, float tscale) {
+  std::vector<float> deq(tokens * cols);
+  if (o_dequantize(fmt, g, codes, scales, tscale, tokens, cols, deq.data()) != OK)
+    return std::numeric_limits<double>::quiet_NaN();
+  double sx = 0.0, se = 0.0;
+  for (int64_t t = 0; t < tokens; ++t)
+    for (int64_t j = 0; j < cols; ++j) {
+      double x = (double)bf16_to_f32(X[t * ld + j]);
+      double xh = (double)deq[t * cols + j] / (c ? (double)c[j] : 1.0);
+      sx += x * x;
+      se += (x - xh) * (x - xh);
+    }
+  if (se == 0.0) return std::numeric_limits<double>::infinity();
+  return 10.0 * std::log10(sx / se);
+}
+
+}  // extern "C"
