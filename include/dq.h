@@ -1,0 +1,182 @@
+/* dq.h — C ABI of the DualQuant dual-scale weight-reconstruction library (MI355X, gfx950).
+ *
+ * DualQuant ("DualQuant: Dual-scale Calibration-free Weight-and-Activation Quantization
+ * for LLMs") fits a weight matrix W (rows = output channels, cols = input channels) as
+ *
+ *     W ~= diag(r) . Qhat . diag(c),   Qhat = FQ_f(W ./ (r c^T)),
+ *
+ * where FQ_f is the block fake-quantiser of format f used as a black box, r is a row-scale
+ * vector and c a column-scale vector.  It minimises the reconstruction MSE by block
+ * coordinate descent with closed-form scale updates, projecting each scale onto the
+ * format's admissible set after each update (listing page abstract; conference entry's
+ * abstract; news summary, mechanism paragraph).  The column scales are the activation
+ * rescaling beta: activation channel j is multiplied by c_j before it is quantised
+ * (listing page Table 1 caption and Table 6; news summary).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or retains them; scratch memory comes in through `workspace`.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is stream-ordered;
+ *     dq_solve additionally blocks the calling thread until the solve has finished.
+ *   - Matrices are row-major; `ld` is the row pitch in elements (ld >= cols).  Blocks of
+ *     `group` consecutive elements run along a row.  Base pointers and the row pitch in
+ *     bytes must be multiples of 16.  cols must be a multiple of the group and at most
+ *     16384.
+ *   - Codes: two 4-bit codes per byte, low nibble = even column, [rows][cols/2].  INT4 and
+ *     MXINT4 codes are two's complement; MXFP4/NVFP4 codes are E2M1 sign-magnitude (the
+ *     sign of a negative value that rounds to zero is kept: code 0x8).
+ *   - Block scales: [rows][cols/group].  INT4: bf16 bit patterns (uint16), value
+ *     bf16(amax/7).  MXINT4/MXFP4: one E8M0 byte, value 2^(byte-127).  NVFP4: one E4M3FN
+ *     byte, multiplied by the fp32 tensor scale.
+ *   - Dequantised value of an element: INT4 q*s; MXINT4 q*2^(e-2); MXFP4 e2m1(q)*2^e;
+ *     NVFP4 e2m1(q)*(e4m3(sb)*tensor_scale).
+ *   - Errors are returned synchronously.  Every argument check happens before any GPU work
+ *     is enqueued, so a call that returns an error has enqueued nothing.  Conditions that
+ *     depend on the data are reported as flag bits (DQ_FLAG_*) in dq_report.
+ */
+#ifndef DQ_H
+#define DQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status codes */
+enum {
+  DQ_OK = 0,
+  DQ_ERR_NULL = -1,       /* a required pointer is NULL */
+  DQ_ERR_SHAPE = -2,      /* bad rows/cols/ld, cols not a multiple of the group, cols > 16384 */
+  DQ_ERR_ALIGN = -3,      /* base pointer or row pitch not 16-byte aligned */
+  DQ_ERR_FORMAT = -4,     /* unknown format, group or dtype */
+  DQ_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required */
+  DQ_ERR_HIP = -6,        /* a HIP runtime call failed */
+  DQ_ERR_ARG = -7         /* other invalid argument (iteration count, problem count) */
+};
+
+/* ---------------------------------------------------------------- formats and dtypes */
+enum {
+  DQ_FMT_INT4 = 0,    /* symmetric INT4, per-group bf16 scale, group 64 or 128 */
+  DQ_FMT_MXINT4 = 1,  /* 32-element blocks, E8M0 scale, 4-bit integers with implicit 2^-2 */
+  DQ_FMT_MXFP4 = 2,   /* 32-element blocks, E8M0 scale, E2M1 elements (OCP MX v1.0) */
+  DQ_FMT_NVFP4 = 3    /* 16-element blocks, E4M3 block scale, fp32 tensor scale, E2M1 */
+};
+enum { DQ_F32 = 0, DQ_BF16 = 1 };
+
+/* ---------------------------------------------------------------- report flags */
+enum {
+  DQ_FLAG_NONFINITE = 1,           /* W contained NaN or Inf (results are not meaningful) */
+  DQ_FLAG_ZERO_ROW = 2,            /* a row had D = 0 in an r-step: its scale was kept */
+  DQ_FLAG_ZERO_COL = 4,            /* a column had D = 0 in a c-step: its scale was kept */
+  DQ_FLAG_NV_BLOCK_UNDERFLOW = 8,  /* an NVFP4 block scale rounded to zero (block zeroed) */
+  DQ_FLAG_NV_TENSOR_UNDERFLOW = 16 /* NVFP4 tensor scale too small: matrix quantised to 0 */
+};
+
+typedef struct {
+  int32_t fmt;    /* DQ_FMT_* */
+  int32_t group;  /* block size; 0 = the format's default (INT4 128, MX 32, NVFP4 16) */
+} dq_quant_spec;
+
+typedef struct {
+  int32_t iters;     /* BCD iterations T >= 0 */
+  float tol_relchg;  /* > 0: stop after the first iteration whose relative change of Qhat is
+                        <= tol_relchg; 0: run all T iterations */
+} dq_solve_opts;
+
+typedef struct {
+  int32_t iters_run;       /* iterations completed */
+  int32_t rejected_steps;  /* Qhat-steps whose candidate was not kept (it would raise the MSE) */
+  uint32_t flags;          /* DQ_FLAG_* */
+  int32_t sweeps;          /* passes over W the solve made (diagnostic) */
+} dq_report;
+
+/* One matrix of a (possibly batched) solve. */
+typedef struct {
+  const void* W;        /* [rows][ld] fp32 or bf16 */
+  int32_t w_dtype;      /* DQ_F32 or DQ_BF16 */
+  int32_t reserved;
+  int64_t rows, cols, ld;
+  const float* r_init;  /* [rows] initial row scales, or NULL for ones */
+  const float* c_init;  /* [cols] initial column scales, or NULL for ones */
+  float* r;             /* out [rows]: final row scales (admissible values) */
+  float* c;             /* out [cols]: final column scales = beta (admissible values) */
+  uint8_t* codes;       /* out [rows*cols/2]: codes of the final Qhat */
+  void* block_scales;   /* out [rows*cols/group]: block scales of the final Qhat */
+  float* tensor_scale;  /* out [1]: NVFP4 tensor scale of the final Qhat (ignored otherwise) */
+  double* nmse_hist;    /* out [iters+1] or NULL: ||W - diag(r)Qhat diag(c)||^2 / ||W||^2 */
+  double* relchg_hist;  /* out [iters+1] or NULL: ||Qhat_t - Qhat_{t-1}|| / ||Qhat_{t-1}||, [0] = 0 */
+  float* r_trace;       /* out [iters][rows] or NULL: each r-step's closed form N/D before projection (NaN if D = 0) */
+  float* c_trace;       /* out [iters][cols] or NULL: each c-step's closed form N/D before projection (NaN if D = 0) */
+  dq_report* report;    /* HOST pointer or NULL: filled when dq_solve returns */
+} dq_problem;
+
+/* Bytes of workspace dq_solve needs for this batch (0 on invalid arguments). */
+size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_spec spec,
+                          const dq_solve_opts* opts);
+
+/* The DualQuant solve (listing page abstract: variable splitting + block coordinate
+ * descent with closed-form subproblems; conference entry: quantiser as a black box,
+ * scales projected onto the format's admissible set after each update; listing page
+ * Fig. 2 / Fig. 3 for the statistics).  For each problem, starting from r = r_init and
+ * c = c_init (ones when NULL) and Qhat_0 = FQ_f(W ./ r c^T), each iteration runs
+ *   r-step  r_i <- Proj(N_i / D_i), N_i = sum_j W_ij Qhat_ij c_j, D_i = sum_j (Qhat_ij c_j)^2;
+ *   c-step  c_j <- Proj(N_j / D_j), N_j = sum_i r_i W_ij Qhat_ij, D_j = sum_i (r_i Qhat_ij)^2,
+ *           with the new r;  a scale whose D is 0 is kept;
+ *   Qhat-step  candidate FQ_f(W ./ r c^T), kept unless it raises the MSE at the current
+ *           scales (so the MSE never increases);
+ * where Proj is the nearest admissible value: powers of two 2^k, k in [-127,127] (MX,
+ * ties up), E4M3 values in [2^-9, 448] (NVFP4), bf16 values >= 2^-126 (INT4).
+ * Problems are independent; count > 1 runs them together on one GPU.  Blocks the calling
+ * thread until done.  `workspace` must hold dq_workspace_bytes(...) bytes of device
+ * memory; its contents on entry do not matter. */
+int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
+             const dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace dq_quantize_weights / dq_rescale_quantize_acts need. */
+size_t dq_quantize_workspace_bytes(int64_t rows, int64_t cols, dq_quant_spec spec);
+
+/* The Qhat-step on its own: codes, block scales and (NVFP4) tensor scale of
+ * FQ_f(W ./ (r c^T)) (conference entry: the quantiser used as a black box).  r and/or c
+ * may be NULL (ones).  The NVFP4 tensor scale is max|W ./ r c^T| / 2688.  Asynchronous. */
+int dq_quantize_weights(const void* W, int32_t w_dtype, int64_t rows, int64_t cols, int64_t ld,
+                        const float* r, const float* c, dq_quant_spec spec, uint8_t* codes,
+                        void* block_scales, float* tensor_scale, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Activation rescale + quantise (listing page abstract and Table 11, "activation
+ * quantization (incl. beta)"; Table 6; news summary): x'_tj = x_tj * c_j (exact in fp32
+ * for admissible c), then FQ_f along each token row.  c may be NULL (beta not applied).
+ * X is [tokens][ld], fp32 or bf16.  Asynchronous. */
+int dq_rescale_quantize_acts(const void* X, int32_t x_dtype, int64_t tokens, int64_t cols,
+                             int64_t ld, const float* c, dq_quant_spec spec, uint8_t* codes,
+                             void* block_scales, float* tensor_scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Decode codes + block scales (+ tensor scale) into fp32 values [rows][cols].  When r and/or
+ * c are given the output is diag(r) Qhat diag(c) (the reconstruction), else Qhat.
+ * Asynchronous. */
+int dq_dequantize(dq_quant_spec spec, const uint8_t* codes, const void* block_scales,
+                  const float* tensor_scale, int64_t rows, int64_t cols, const float* r,
+                  const float* c, float* out, void* stream);
+
+/* Human-readable text of a status code. */
+const char* dq_status_string(int status);
+
+/* ---------------------------------------------------------------- diagnostics
+ * Apply one of the library's scalar device rounding routines elementwise (n values):
+ *   DQ_ROUND_E2M1      x -> E2M1 code byte (ties to even, saturating, sign kept)
+ *   DQ_ROUND_E4M3      x >= 0 -> E4M3FN code byte (ties to even, saturating at 448)
+ *   DQ_ROUND_BF16      x -> nearest bf16 value (fp32 out)
+ *   DQ_ROUND_INT4      x -> nearest integer in [-7, 7], ties to even (int8 out)
+ *   DQ_PROJ_POW2 / DQ_PROJ_E4M3 / DQ_PROJ_BF16   x > 0 -> projected scale (fp32 out)
+ * Used to check the device routines against an independent implementation. */
+enum { DQ_ROUND_E2M1 = 0, DQ_ROUND_E4M3 = 1, DQ_ROUND_BF16 = 2, DQ_ROUND_INT4 = 3,
+       DQ_PROJ_POW2 = 4, DQ_PROJ_E4M3 = 5, DQ_PROJ_BF16 = 6 };
+int dq_debug_round(int32_t fn, const float* x, void* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DQ_H */

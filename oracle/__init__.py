@@ -65,8 +65,8 @@ def lib():
         L.o_quantize_weights.restype = C.c_int
         L.o_dequantize.argtypes = [C.c_int, C.c_int, p, p, C.c_float, i64, i64, p]
         L.o_dequantize.restype = C.c_int
-        L.o_solve.argtypes = [p, C.c_int, i64, i64, i64, C.c_int, C.c_int, C.c_int, p, p, p, p,
-                              p, p, p, p, p, p, p, p, p]
+        L.o_solve.argtypes = [p, C.c_int, i64, i64, i64, C.c_int, C.c_int, C.c_int, C.c_float,
+                              p, p, p, p, p, p, p, p, p, p, p, p, p, p]
         L.o_solve.restype = C.c_int
         L.o_rescale_quantize_acts.argtypes = [p, i64, i64, i64, p, C.c_int, C.c_int, p, p, p, p]
         L.o_rescale_quantize_acts.restype = C.c_int
@@ -199,9 +199,10 @@ def dequantize(codes, scales, tscale: float, fmt: str, rows: int, cols: int,
 
 
 def solve(W: np.ndarray, fmt: str, iters: int, group: int | None = None, r_init=None,
-          c_init=None) -> dict:
+          c_init=None, tol: float = 0.0) -> dict:
     """The BCD solve; returns r, c, codes, scales, tscale, nmse, relchg, rejected,
-    r_pre, c_pre (last iteration's unprojected closed forms) and flags."""
+    iters_run, r_trace / c_trace (every iteration's unprojected closed forms, NaN where
+    D = 0; r_pre / c_pre are the last rows) and flags."""
     group = group or DEFAULT_GROUP[fmt]
     W = np.ascontiguousarray(W)
     rows, cols = W.shape
@@ -215,16 +216,19 @@ def solve(W: np.ndarray, fmt: str, iters: int, group: int | None = None, r_init=
     nmse = np.zeros(iters + 1, dtype=np.float64)
     relchg = np.zeros(iters + 1, dtype=np.float64)
     rej = np.zeros(1, dtype=np.int32)
-    r_pre = np.full(rows, np.nan, dtype=np.float32)
-    c_pre = np.full(cols, np.nan, dtype=np.float32)
+    run = np.zeros(1, dtype=np.int32)
+    r_tr = np.full((max(iters, 1), rows), np.nan, dtype=np.float32)
+    c_tr = np.full((max(iters, 1), cols), np.nan, dtype=np.float32)
     flags = np.zeros(1, dtype=np.uint32)
     _check(lib().o_solve(_ptr(W), _w_dtype(W), rows, cols, cols, FMT[fmt], group, iters,
-                         _ptr(ri), _ptr(ci), _ptr(r), _ptr(c), _ptr(codes), _ptr(scales),
-                         _ptr(ts), _ptr(nmse), _ptr(relchg), _ptr(rej), _ptr(r_pre),
-                         _ptr(c_pre), _ptr(flags)), "solve")
-    return dict(r=r, c=c, codes=codes, scales=scales, tscale=float(ts[0]), nmse=nmse,
-                relchg=relchg, rejected=int(rej[0]), r_pre=r_pre, c_pre=c_pre,
-                flags=int(flags[0]))
+                         float(tol), _ptr(ri), _ptr(ci), _ptr(r), _ptr(c), _ptr(codes),
+                         _ptr(scales), _ptr(ts), _ptr(nmse), _ptr(relchg), _ptr(rej), _ptr(run),
+                         _ptr(r_tr), _ptr(c_tr), _ptr(flags)), "solve")
+    k = int(run[0])
+    return dict(r=r, c=c, codes=codes, scales=scales, tscale=float(ts[0]), nmse=nmse[:k + 1],
+                relchg=relchg[:k + 1], rejected=int(rej[0]), iters_run=k, r_trace=r_tr[:iters],
+                c_trace=c_tr[:iters], r_pre=r_tr[iters - 1] if iters else r_tr[0],
+                c_pre=c_tr[iters - 1] if iters else c_tr[0], flags=int(flags[0]))
 
 
 def rescale_quantize_acts(X: np.ndarray, c, fmt: str, group: int | None = None):

@@ -276,9 +276,9 @@ void fq_matrix(int fmt, int g, const float* V, int64_t rows, int64_t cols, FQOut
     s_t = A / 2688.0f;
     float six_st = 6.0f * s_t;
     k6 = (s_t > 0.0f) ? 1.0f / six_st : 0.0f;
-    // A tensor scale so small that 1/(6 s_t) overflows leaves no representable block
-    // scale: the whole matrix quantises to zero (flag bit 16).
-    if (!(s_t > 0.0f) || !std::isfinite(k6)) {
+    // A tensor scale below 2^-100 (amax below about 2^-88.6) leaves block scales whose
+    // reciprocals overflow fp32; the whole matrix then quantises to zero (flag bit 16).
+    if (!(s_t >= std::ldexp(1.0f, -100)) || !std::isfinite(k6)) {
       if (A > 0.0f) o.flags |= 16u;
       s_t = 0.0f;
       k6 = 0.0f;
@@ -460,11 +460,14 @@ int o_dequantize(int fmt, int g, const uint8_t* codes, const void* scales, float
 // 1-D quadratic whose constrained minimiser is the projection of N/D).
 // Outputs: final r, c; codes, block scales and tensor scale of Q^T; histories
 // nmse[0..T], relchg[0..T] (relchg[0] = 0); rejected-step count; and, when given,
-// the last iteration's unprojected closed-form values r_pre, c_pre (NaN where D = 0).
+// traces of every iteration's unprojected closed-form values, r_trace [T][rows] and
+// c_trace [T][cols] (NaN where D = 0).  tol > 0 stops after the first iteration whose
+// relchg is <= tol (a rejected step has relchg 0); iters_run reports the count.
 int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int g,
-            int iters, const float* r_init, const float* c_init, float* r_out, float* c_out,
-            uint8_t* codes, void* scales, float* tscale, double* nmse_hist, double* relchg_hist,
-            int* rejected_out, float* r_pre, float* c_pre, uint32_t* flags_out) {
+            int iters, float tol, const float* r_init, const float* c_init, float* r_out,
+            float* c_out, uint8_t* codes, void* scales, float* tscale, double* nmse_hist,
+            double* relchg_hist, int* rejected_out, int* iters_run, float* r_trace,
+            float* c_trace, uint32_t* flags_out) {
   if (!W || !r_out || !c_out || !codes || !scales) return ERR_NULL;
   if (!group_ok(fmt, g)) return ERR_FORMAT;
   if (rows < 0 || cols < 0 || cols % g || ld < cols || iters < 0) return ERR_SHAPE;
@@ -498,7 +501,7 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
   auto nmse_of = [&](double F) { return normW2 > 0.0 ? F / normW2 : 0.0; };
   if (nmse_hist) nmse_hist[0] = nmse_of(recon_error(Wf.data(), Q.data(), r.data(), c.data(), rows, cols));
   if (relchg_hist) relchg_hist[0] = 0.0;
-  int rejected = 0;
+  int rejected = 0, done = 0;
 
   std::vector<double> rowN(rows), rowD(rows), colN(cols), colD(cols);
   for (int t = 1; t <= iters; ++t) {
@@ -521,7 +524,7 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
         x = (float)(rowN[i] / rowD[i]);
         r[i] = project(fmt, x);
       }
-      if (t == iters && r_pre) r_pre[i] = x;
+      if (r_trace) r_trace[(int64_t)(t - 1) * rows + i] = x;
     }
     // c-step (loop interchanged per column range; each column still sums rows in order)
     parallel_rows(cols, [&](int64_t jb, int64_t je) {
@@ -542,7 +545,7 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
         x = (float)(colN[j] / colD[j]);
         c[j] = project(fmt, x);
       }
-      if (t == iters && c_pre) c_pre[j] = x;
+      if (c_trace) c_trace[(int64_t)(t - 1) * cols + j] = x;
     }
     // Q-step with safeguard
     normalise(Wf.data(), rows, cols, r.data(), c.data(), V.data());
@@ -551,6 +554,7 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
     flags |= o.flags;
     double Fc = recon_error(Wf.data(), Qc.data(), r.data(), c.data(), rows, cols);
     double Fp = recon_error(Wf.data(), Q.data(), r.data(), c.data(), rows, cols);
+    double relv = 0.0;
     if (Fc <= Fp) {
       double num = 0.0, den = 0.0;
       for (int64_t i = 0; i < N; ++i) {
@@ -558,7 +562,8 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
         num += dq * dq;
         den += (double)Q[i] * (double)Q[i];
       }
-      if (relchg_hist) relchg_hist[t] = den > 0.0 ? std::sqrt(num) / std::sqrt(den) : 0.0;
+      relv = den > 0.0 ? std::sqrt(num) / std::sqrt(den) : 0.0;
+      if (relchg_hist) relchg_hist[t] = relv;
       if (nmse_hist) nmse_hist[t] = nmse_of(Fc);
       Q.swap(Qc);
       codesA.swap(codesC);
@@ -569,6 +574,8 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
       if (relchg_hist) relchg_hist[t] = 0.0;
       if (nmse_hist) nmse_hist[t] = nmse_of(Fp);
     }
+    done = t;
+    if (tol > 0.0f && relv <= (double)tol) break;
   }
   std::copy(r.begin(), r.end(), r_out);
   std::copy(c.begin(), c.end(), c_out);
@@ -576,6 +583,7 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
   std::memcpy(scales, scA.data(), scA.size());
   if (fmt == FMT_NVFP4) *tscale = tsA;
   if (rejected_out) *rejected_out = rejected;
+  if (iters_run) *iters_run = done;
   if (flags_out) *flags_out = flags;
   return OK;
 }

@@ -1,0 +1,273 @@
+"""Python binding of the DualQuant dual-scale solver library (libdq.so, gfx950).
+
+The functions named like the C entry points (``dq_solve``, ``dq_quantize_weights``,
+``dq_rescale_quantize_acts``, ``dq_dequantize``, ``dq_workspace_bytes``,
+``dq_quantize_workspace_bytes``, ``dq_status_string``, ``dq_debug_round``) only marshal
+arguments: torch tensors supply device memory and the current HIP stream; every step of
+the computation runs in the library's HIP kernels.  ``solve``, ``quantize_weights``,
+``rescale_quantize_acts`` and ``dequantize`` are conveniences that allocate the outputs
+with torch and call those entry points.
+
+There is no fallback: importing the package fails if ``libdq.so`` has not been built
+(``python -m post_quantization_dq_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from pathlib import Path
+
+import torch
+
+_LIB_PATH = Path(__file__).resolve().parent / "libdq.so"
+if not _LIB_PATH.exists():
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m post_quantization_dq_amd.build`")
+_lib = C.CDLL(str(_LIB_PATH))
+
+FMT = {"INT4": 0, "MXINT4": 1, "MXFP4": 2, "NVFP4": 3}
+DEFAULT_GROUP = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16}
+DT = {torch.float32: 0, torch.bfloat16: 1}
+FLAGS = {1: "nonfinite", 2: "zero_row", 4: "zero_col", 8: "nv_block_underflow", 16: "nv_tensor_underflow"}
+ROUND_FN = {"e2m1": 0, "e4m3": 1, "bf16": 2, "int4": 3, "proj_pow2": 4, "proj_e4m3": 5, "proj_bf16": 6}
+
+
+class dq_quant_spec(C.Structure):
+    _fields_ = [("fmt", C.c_int32), ("group", C.c_int32)]
+
+
+class dq_solve_opts(C.Structure):
+    _fields_ = [("iters", C.c_int32), ("tol_relchg", C.c_float)]
+
+
+class dq_report(C.Structure):
+    _fields_ = [("iters_run", C.c_int32), ("rejected_steps", C.c_int32), ("flags", C.c_uint32),
+                ("sweeps", C.c_int32)]
+
+
+class dq_problem(C.Structure):
+    _fields_ = [("W", C.c_void_p), ("w_dtype", C.c_int32), ("reserved", C.c_int32),
+                ("rows", C.c_int64), ("cols", C.c_int64), ("ld", C.c_int64),
+                ("r_init", C.c_void_p), ("c_init", C.c_void_p), ("r", C.c_void_p),
+                ("c", C.c_void_p), ("codes", C.c_void_p), ("block_scales", C.c_void_p),
+                ("tensor_scale", C.c_void_p), ("nmse_hist", C.c_void_p),
+                ("relchg_hist", C.c_void_p), ("r_trace", C.c_void_p), ("c_trace", C.c_void_p),
+                ("report", C.POINTER(dq_report))]
+
+
+_vp, _i32, _i64, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+_lib.dq_status_string.argtypes = [C.c_int]
+_lib.dq_status_string.restype = C.c_char_p
+_lib.dq_workspace_bytes.argtypes = [C.POINTER(dq_problem), _i32, dq_quant_spec, C.POINTER(dq_solve_opts)]
+_lib.dq_workspace_bytes.restype = _sz
+_lib.dq_solve.argtypes = [C.POINTER(dq_problem), _i32, dq_quant_spec, C.POINTER(dq_solve_opts), _vp, _sz, _vp]
+_lib.dq_solve.restype = C.c_int
+_lib.dq_quantize_workspace_bytes.argtypes = [_i64, _i64, dq_quant_spec]
+_lib.dq_quantize_workspace_bytes.restype = _sz
+_lib.dq_quantize_weights.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, dq_quant_spec, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dq_quantize_weights.restype = C.c_int
+_lib.dq_rescale_quantize_acts.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, dq_quant_spec, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dq_rescale_quantize_acts.restype = C.c_int
+_lib.dq_dequantize.argtypes = [dq_quant_spec, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]
+_lib.dq_dequantize.restype = C.c_int
+_lib.dq_debug_round.argtypes = [_i32, _vp, _vp, _i64, _vp]
+_lib.dq_debug_round.restype = C.c_int
+
+EXPORTED = ("dq_workspace_bytes", "dq_solve", "dq_quantize_workspace_bytes", "dq_quantize_weights",
+            "dq_rescale_quantize_acts", "dq_dequantize", "dq_status_string", "dq_debug_round")
+
+
+class DQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {dq_status_string(status)} ({status})")
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise DQError(rc, what)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def spec_of(fmt: str, group: int | None = None) -> dq_quant_spec:
+    return dq_quant_spec(FMT[fmt], int(group or 0))
+
+
+def scale_dtype(fmt: str) -> torch.dtype:
+    return torch.int16 if fmt == "INT4" else torch.uint8
+
+
+# ------------------------------------------------------------------ C-ABI mirrors
+def dq_status_string(status: int) -> str:
+    return _lib.dq_status_string(int(status)).decode()
+
+
+@dataclass
+class Problem:
+    """One matrix of a solve; every tensor lives on the GPU."""
+    W: torch.Tensor
+    r: torch.Tensor
+    c: torch.Tensor
+    codes: torch.Tensor
+    block_scales: torch.Tensor
+    tensor_scale: torch.Tensor | None = None
+    r_init: torch.Tensor | None = None
+    c_init: torch.Tensor | None = None
+    nmse_hist: torch.Tensor | None = None
+    relchg_hist: torch.Tensor | None = None
+    r_trace: torch.Tensor | None = None
+    c_trace: torch.Tensor | None = None
+
+    def to_c(self, report: dq_report | None) -> dq_problem:
+        W = self.W
+        rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (0, 0)
+        return dq_problem(
+            W=_ptr(W), w_dtype=DT.get(W.dtype, -1), reserved=0, rows=rows, cols=cols,
+            ld=W.stride(0) if W.dim() == 2 and W.numel() else cols,
+            r_init=_ptr(self.r_init), c_init=_ptr(self.c_init), r=_ptr(self.r), c=_ptr(self.c),
+            codes=_ptr(self.codes), block_scales=_ptr(self.block_scales),
+            tensor_scale=_ptr(self.tensor_scale), nmse_hist=_ptr(self.nmse_hist),
+            relchg_hist=_ptr(self.relchg_hist), r_trace=_ptr(self.r_trace), c_trace=_ptr(self.c_trace),
+            report=C.pointer(report) if report is not None else None)
+
+
+def _problem_array(problems, reports):
+    arr = (dq_problem * len(problems))()
+    for k, p in enumerate(problems):
+        arr[k] = p.to_c(reports[k] if reports is not None else None)
+    return arr
+
+
+def dq_workspace_bytes(problems, spec: dq_quant_spec, opts: dq_solve_opts) -> int:
+    arr = _problem_array(problems, None)
+    return int(_lib.dq_workspace_bytes(arr, len(problems), spec, C.byref(opts)))
+
+
+def dq_solve(problems, spec: dq_quant_spec, opts: dq_solve_opts, workspace: torch.Tensor,
+             stream=None) -> list[dq_report]:
+    reports = [dq_report() for _ in problems]
+    arr = _problem_array(problems, reports)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.dq_solve(arr, len(problems), spec, C.byref(opts), _ptr(workspace), nbytes,
+                         _stream(stream)), "dq_solve")
+    return reports
+
+
+def dq_quantize_workspace_bytes(rows: int, cols: int, spec: dq_quant_spec) -> int:
+    return int(_lib.dq_quantize_workspace_bytes(rows, cols, spec))
+
+
+def dq_quantize_weights(W, r, c, spec, codes, block_scales, tensor_scale, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.dq_quantize_weights(_ptr(W), DT.get(W.dtype, -1), W.shape[0], W.shape[1],
+                                    W.stride(0) if W.numel() else W.shape[1], _ptr(r), _ptr(c),
+                                    spec, _ptr(codes), _ptr(block_scales), _ptr(tensor_scale),
+                                    _ptr(workspace), nbytes, _stream(stream)),
+           "dq_quantize_weights")
+
+
+def dq_rescale_quantize_acts(X, c, spec, codes, block_scales, tensor_scale, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.dq_rescale_quantize_acts(_ptr(X), DT.get(X.dtype, -1), X.shape[0], X.shape[1],
+                                         X.stride(0) if X.numel() else X.shape[1], _ptr(c), spec,
+                                         _ptr(codes), _ptr(block_scales), _ptr(tensor_scale),
+                                         _ptr(workspace), nbytes, _stream(stream)),
+           "dq_rescale_quantize_acts")
+
+
+def dq_dequantize(spec, codes, block_scales, tensor_scale, rows, cols, r, c, out, stream=None):
+    _check(_lib.dq_dequantize(spec, _ptr(codes), _ptr(block_scales), _ptr(tensor_scale), rows,
+                              cols, _ptr(r), _ptr(c), _ptr(out), _stream(stream)), "dq_dequantize")
+
+
+def dq_debug_round(fn: str, x: torch.Tensor, out: torch.Tensor, stream=None):
+    _check(_lib.dq_debug_round(ROUND_FN[fn], _ptr(x), _ptr(out), x.numel(), _stream(stream)),
+           "dq_debug_round")
+
+
+# ------------------------------------------------------------------ conveniences
+def _outputs(rows: int, cols: int, fmt: str, group: int, device):
+    codes = torch.empty(rows * cols // 2, dtype=torch.uint8, device=device)
+    scales = torch.empty(rows * cols // group, dtype=scale_dtype(fmt), device=device)
+    ts = torch.zeros(1, dtype=torch.float32, device=device)
+    return codes, scales, ts
+
+
+def make_problem(W: torch.Tensor, fmt: str, iters: int, group: int | None = None,
+                 r_init=None, c_init=None, trace: bool = False) -> Problem:
+    group = group or DEFAULT_GROUP[fmt]
+    rows, cols = W.shape
+    dev = W.device
+    codes, scales, ts = _outputs(rows, cols, fmt, group, dev)
+    return Problem(
+        W=W, r=torch.empty(rows, dtype=torch.float32, device=dev),
+        c=torch.empty(cols, dtype=torch.float32, device=dev), codes=codes, block_scales=scales,
+        tensor_scale=ts, r_init=r_init, c_init=c_init,
+        nmse_hist=torch.zeros(iters + 1, dtype=torch.float64, device=dev),
+        relchg_hist=torch.zeros(iters + 1, dtype=torch.float64, device=dev),
+        r_trace=torch.full((max(iters, 1), rows), float("nan"), device=dev) if trace else None,
+        c_trace=torch.full((max(iters, 1), cols), float("nan"), device=dev) if trace else None)
+
+
+def solve_many(problems, fmt: str, iters: int, group: int | None = None, tol: float = 0.0,
+               stream=None):
+    spec = spec_of(fmt, group)
+    opts = dq_solve_opts(int(iters), float(tol))
+    nbytes = dq_workspace_bytes(problems, spec, opts)
+    if nbytes == 0:
+        raise DQError(-7, "dq_workspace_bytes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=problems[0].W.device)
+    return dq_solve(problems, spec, opts, ws, stream)
+
+
+def solve(W: torch.Tensor, fmt: str, iters: int, group: int | None = None, r_init=None,
+          c_init=None, tol: float = 0.0, trace: bool = False, stream=None) -> dict:
+    """Run the solve on one matrix; returns the output tensors and the report.  With
+    trace=True, r_trace / c_trace hold every iteration's unprojected closed forms."""
+    p = make_problem(W, fmt, iters, group, r_init, c_init, trace)
+    rep = solve_many([p], fmt, iters, group, tol, stream)[0]
+    k = rep.iters_run
+    return dict(r=p.r, c=p.c, codes=p.codes, scales=p.block_scales, tscale=p.tensor_scale,
+                nmse=p.nmse_hist[:k + 1], relchg=p.relchg_hist[:k + 1],
+                r_trace=None if p.r_trace is None else p.r_trace[:iters],
+                c_trace=None if p.c_trace is None else p.c_trace[:iters],
+                iters_run=rep.iters_run, rejected=rep.rejected_steps, flags=rep.flags,
+                sweeps=rep.sweeps)
+
+
+def quantize_weights(W: torch.Tensor, r=None, c=None, fmt: str = "NVFP4", group: int | None = None,
+                     stream=None):
+    group = group or DEFAULT_GROUP[fmt]
+    spec = spec_of(fmt, group)
+    codes, scales, ts = _outputs(W.shape[0], W.shape[1], fmt, group, W.device)
+    nb = dq_quantize_workspace_bytes(W.shape[0], W.shape[1], spec)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=W.device)
+    dq_quantize_weights(W, r, c, spec, codes, scales, ts, ws, stream)
+    return codes, scales, ts
+
+
+def rescale_quantize_acts(X: torch.Tensor, c=None, fmt: str = "NVFP4", group: int | None = None,
+                          stream=None):
+    group = group or DEFAULT_GROUP[fmt]
+    spec = spec_of(fmt, group)
+    codes, scales, ts = _outputs(X.shape[0], X.shape[1], fmt, group, X.device)
+    nb = dq_quantize_workspace_bytes(X.shape[0], X.shape[1], spec)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=X.device)
+    dq_rescale_quantize_acts(X, c, spec, codes, scales, ts, ws, stream)
+    return codes, scales, ts
+
+
+def dequantize(codes, scales, tscale, rows: int, cols: int, fmt: str, group: int | None = None,
+               r=None, c=None, stream=None) -> torch.Tensor:
+    out = torch.empty(rows, cols, dtype=torch.float32, device=codes.device)
+    dq_dequantize(spec_of(fmt, group), codes, scales, tscale, rows, cols, r, c, out, stream)
+    return out

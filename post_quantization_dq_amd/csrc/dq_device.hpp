@@ -1,0 +1,265 @@
+// Device-side numerics of the DualQuant solver for gfx950: element and scale rounding,
+// scale projection, and the per-format block quantiser applied to one lane's chunk of 16
+// consecutive elements of a row.
+//
+// Formats (conference entry: INT4, the MX family and NVFP4; news summary: INT4, MXINT4,
+// MXFP4, NVFP4):
+//   INT4    symmetric, group 64 or 128, bf16 scale s = bf16(amax/7), q = rint(v * (1/s)) in [-7,7]
+//   MXINT4  32-element block, E8M0 exponent e = floor(log2 amax), q = rint(v * 2^(2-e)) in [-7,7]
+//   MXFP4   32-element block, E8M0 exponent e = floor(log2 amax) - 2, q = E2M1(v * 2^-e)
+//   NVFP4   16-element block, E4M3 scale sb = E4M3(amax * k6), d = sb * s_t, q = E2M1(v * (1/d))
+// E2M1 rounding is to nearest with ties to the even mantissa bit, saturating at 6, keeping
+// the sign of zero; it uses the gfx950 scaled FP4 conversions, whose scale operand only
+// contributes its exponent field (a power-of-two division), exactly what the MX block
+// exponent needs.  E4M3 uses the OCP FP8 conversion after clamping to 448 (the conversion
+// itself overflows to NaN above 464).
+
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dqk {
+
+enum Fmt { INT4 = 0, MXINT4 = 1, MXFP4 = 2, NVFP4 = 3 };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+
+// ---------------------------------------------------------------- scalar rounding
+// bf16 round-to-nearest-even of a finite fp32 (carry into the exponent is the correct
+// rounding up to the next binade).
+__device__ __forceinline__ float bf16_rne(float x) {
+  uint32_t u = f2u(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u2f(u & 0xFFFF0000u);
+}
+
+// E4M3FN code of x >= 0 (finite), nearest with ties to even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_code_sat(float x) {
+  x = fminf(x, 448.0f);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0u, false) & 0xFFu;
+}
+
+// Value of a non-negative E4M3FN code (0..126): subnormals m * 2^-9, normals (8+m) * 2^(e-10).
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  uint32_t e = (code >> 3) & 15u, m = code & 7u;
+  return e ? ldexpf((float)(8u + m), (int)e - 10) : ldexpf((float)m, -9);
+}
+
+// floor(log2 a) for finite a > 0 (exact, also for subnormals).
+__device__ __forceinline__ int floor_log2(float a) { return __builtin_amdgcn_frexp_expf(a) - 1; }
+
+// fp32 operand whose exponent field encodes 2^e for the scaled FP4 conversions
+// (valid for e in [-126, 127]; callers keep e >= -100).
+__device__ __forceinline__ float pow2_operand(int e) { return u2f((uint32_t)(e + 127) << 23); }
+
+// Nearest integer in [-7, 7], ties to even.
+__device__ __forceinline__ float int4_round(float x) {
+  return __builtin_amdgcn_fmed3f(__builtin_rintf(x), -7.0f, 7.0f);
+}
+
+// ---------------------------------------------------------------- scale projections
+// Nearest admissible scale to x > 0 (conference entry: scales are projected onto the
+// format's admissible set after each update; the nearest point is the exact minimiser of
+// the 1-D quadratic each closed-form step solves).
+__device__ __forceinline__ float proj_pow2(float x) {   // 2^k, k in [-127, 127], ties up
+  int k = __builtin_amdgcn_frexp_expf(x);               // x = m 2^k, m in [0.5, 1)
+  float m = __builtin_amdgcn_frexp_mantf(x);
+  int e = (m >= 0.75f) ? k : k - 1;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return ldexpf(1.0f, e);
+}
+__device__ __forceinline__ float proj_e4m3(float x) {   // E4M3FN values in [2^-9, 448]
+  uint32_t c = e4m3_code_sat(x);
+  return e4m3_value(c ? c : 1u);
+}
+__device__ __forceinline__ float proj_bf16(float x) {   // bf16 values in [2^-126, max bf16]
+  const float hi = u2f(0x7F7F0000u);
+  float b = bf16_rne(fminf(x, hi));
+  return fmaxf(u2f(0x00800000u), fminf(hi, b));
+}
+template <int FMT>
+__device__ __forceinline__ float project(float x) {
+  if (FMT == MXINT4 || FMT == MXFP4) return proj_pow2(x);
+  if (FMT == NVFP4) return proj_e4m3(x);
+  return proj_bf16(x);
+}
+
+// ---------------------------------------------------------------- cross-lane helpers
+// Max over the L consecutive lanes that share a block (L in {1,2,4,8}).
+template <int L>
+__device__ __forceinline__ float block_max(float a) {
+  if (L >= 2) a = fmaxf(a, __shfl_xor(a, 1));
+  if (L >= 4) a = fmaxf(a, __shfl_xor(a, 2));
+  if (L >= 8) a = fmaxf(a, __shfl_xor(a, 4));
+  return a;
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// ---------------------------------------------------------------- format traits
+template <int FMT> struct Traits;
+template <> struct Traits<INT4> { static constexpr int DEF_G = 128; static constexpr int SCALE_BYTES = 2; };
+template <> struct Traits<MXINT4> { static constexpr int DEF_G = 32; static constexpr int SCALE_BYTES = 1; };
+template <> struct Traits<MXFP4> { static constexpr int DEF_G = 32; static constexpr int SCALE_BYTES = 1; };
+template <> struct Traits<NVFP4> { static constexpr int DEF_G = 16; static constexpr int SCALE_BYTES = 1; };
+
+// NVFP4 per-sweep tables: for every E4M3 code, d = fl(e4m3(code) * s_t) and id = fl(1/d).
+struct NvTab {
+  float d[128];
+  float id[128];
+};
+
+// Everything a lane needs to quantise its chunk: the NVFP4 tensor-scale terms and table.
+struct QCtx {
+  float k6;        // NVFP4: fl(1 / fl(6 s_t)); 0 means "tensor scale zero: all blocks zero"
+  const NvTab* tab;
+};
+
+// Result of quantising one chunk (16 elements): Qhat_k = p[k] * f exactly, where p is the
+// element-grid value (E2M1 value or integer) and f the block's dequantisation factor
+// (NVFP4 d = e4m3(sb) * s_t, MXFP4 2^e, MXINT4 2^(e-2), INT4 s).
+struct Chunk {
+  uint32_t code[2];   // 16 nibbles, element k in bits 4k..4k+3 of the 64-bit pair
+  uint32_t scode;     // block scale code (bf16 bits, E8M0 byte or E4M3 byte)
+  float f;            // block factor
+  float p[16];        // grid values
+  bool underflow;     // NVFP4: non-zero block whose scale rounded to zero
+};
+
+// E2M1 codes of x[0..15] (scale operand `sc` divides by a power of two) and their values.
+__device__ __forceinline__ void fp4_encode16(const float (&x)[16], float sc, uint32_t& c0,
+                                             uint32_t& c1) {
+  c0 = 0u;
+  c1 = 0u;
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, x[0], x[1], sc, 0);
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, x[2], x[3], sc, 1);
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, x[4], x[5], sc, 2);
+  c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c0, x[6], x[7], sc, 3);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, x[8], x[9], sc, 0);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, x[10], x[11], sc, 1);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, x[12], x[13], sc, 2);
+  c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c1, x[14], x[15], sc, 3);
+}
+__device__ __forceinline__ void fp4_decode16(uint32_t c0, uint32_t c1, float (&p)[16]) {
+  f32x2 t[8];
+  t[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, 1.0f, 0);
+  t[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, 1.0f, 1);
+  t[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, 1.0f, 2);
+  t[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c0, 1.0f, 3);
+  t[4] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, 1.0f, 0);
+  t[5] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, 1.0f, 1);
+  t[6] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, 1.0f, 2);
+  t[7] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c1, 1.0f, 3);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) { p[2 * k] = t[k].x; p[2 * k + 1] = t[k].y; }
+}
+__device__ __forceinline__ void int4_decode16(uint32_t c0, uint32_t c1, float (&p)[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    uint32_t w = (k < 8) ? c0 : c1;
+    p[k] = (float)(((int)(w << (28 - 4 * (k & 7)))) >> 28);   // sign-extended nibble
+  }
+}
+
+// Quantise one lane's 16 normalised values v (one chunk of a block of L*16).
+template <int FMT, int L>
+__device__ __forceinline__ void quantize_chunk(const float (&v)[16], const QCtx& ctx, Chunk& o) {
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) a = fmaxf(a, fabsf(v[k]));
+  a = block_max<L>(a);
+  o.underflow = false;
+  if (FMT == NVFP4) {
+    const uint32_t sbc = (ctx.k6 > 0.0f) ? e4m3_code_sat(a * ctx.k6) : 0u;
+    o.scode = sbc;
+    o.underflow = (sbc == 0u) && (a > 0.0f);
+    const float id = ctx.tab->id[sbc];   // entry 0 holds 0
+    o.f = ctx.tab->d[sbc];
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = v[k] * id;
+    uint32_t c0, c1;
+    fp4_encode16(x, 1.0f, c0, c1);
+    if (sbc == 0u) { c0 = 0u; c1 = 0u; }
+    o.code[0] = c0;
+    o.code[1] = c1;
+    fp4_decode16(c0, c1, o.p);
+  } else if (FMT == MXFP4) {
+    int e = (a > 0.0f) ? floor_log2(a) - 2 : -127;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    o.scode = (uint32_t)(e + 127);
+    o.f = ldexpf(1.0f, e);
+    uint32_t c0, c1;
+    if (e >= -100) {        // the scale operand carries 2^e: the conversion divides exactly
+      fp4_encode16(v, pow2_operand(e), c0, c1);
+    } else {                // tiny blocks: scale by 2^-e first (exact), convert unscaled
+      float x[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) x[k] = ldexpf(v[k], -e);
+      fp4_encode16(x, 1.0f, c0, c1);
+    }
+    if (a == 0.0f) { c0 = 0u; c1 = 0u; }
+    o.code[0] = c0;
+    o.code[1] = c1;
+    fp4_decode16(c0, c1, o.p);
+  } else if (FMT == MXINT4) {
+    int e = (a > 0.0f) ? floor_log2(a) : -127;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    o.scode = (uint32_t)(e + 127);
+    o.f = ldexpf(1.0f, e - 2);
+    uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float q = (a > 0.0f) ? int4_round(ldexpf(v[k], 2 - e)) : 0.0f;
+      const uint32_t nib = (uint32_t)(int)q & 0xFu;
+      if (k < 8) c0 |= nib << (4 * k); else c1 |= nib << (4 * (k - 8));
+      o.p[k] = q;
+    }
+    o.code[0] = c0;
+    o.code[1] = c1;
+  } else {  // INT4
+    const float s = (a > 0.0f) ? bf16_rne(a / 7.0f) : 0.0f;
+    o.scode = f2u(s) >> 16;
+    o.f = s;
+    const float is = (s > 0.0f) ? 1.0f / s : 0.0f;
+    uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float q = (s > 0.0f) ? int4_round(v[k] * is) : 0.0f;
+      const uint32_t nib = (uint32_t)(int)q & 0xFu;
+      if (k < 8) c0 |= nib << (4 * k); else c1 |= nib << (4 * (k - 8));
+      o.p[k] = q;
+    }
+    o.code[0] = c0;
+    o.code[1] = c1;
+  }
+}
+
+// Block factor of a stored scale code (NVFP4 uses the table of the tensor scale the codes
+// were made with).
+template <int FMT>
+__device__ __forceinline__ float block_factor(uint32_t scode, const NvTab* tab) {
+  if (FMT == NVFP4) return tab->d[scode & 127u];
+  if (FMT == MXFP4) return ldexpf(1.0f, (int)scode - 127);
+  if (FMT == MXINT4) return ldexpf(1.0f, (int)scode - 129);
+  return u2f(scode << 16);
+}
+
+// Grid values of a stored chunk.
+template <int FMT>
+__device__ __forceinline__ void decode_grid(uint32_t c0, uint32_t c1, float (&p)[16]) {
+  if (FMT == NVFP4 || FMT == MXFP4) fp4_decode16(c0, c1, p);
+  else int4_decode16(c0, c1, p);
+}
+
+}  // namespace dqk

@@ -1,0 +1,554 @@
+// C-ABI host layer of the DualQuant solver library (gfx950): argument validation,
+// workspace layout, launch planning and the iteration driver.  See include/dq.h for the
+// contract of every entry point.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <vector>
+
+#include "../../include/dq.h"
+#include "dq_kernels.hpp"
+
+using namespace dqk;
+
+namespace {
+
+constexpr int kMaxCols = 16384;
+constexpr int kTargetWgs = 256;   // one row strip per CU for a single large matrix
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+int default_group(int fmt) {
+  switch (fmt) {
+    case DQ_FMT_INT4: return 128;
+    case DQ_FMT_MXINT4: return 32;
+    case DQ_FMT_MXFP4: return 32;
+    case DQ_FMT_NVFP4: return 16;
+    default: return 0;
+  }
+}
+
+int resolve_group(const dq_quant_spec& s) {
+  if (s.fmt < DQ_FMT_INT4 || s.fmt > DQ_FMT_NVFP4) return -1;
+  int g = s.group ? s.group : default_group(s.fmt);
+  if (s.fmt == DQ_FMT_INT4 && g != 64 && g != 128) return -1;
+  if ((s.fmt == DQ_FMT_MXINT4 || s.fmt == DQ_FMT_MXFP4) && g != 32) return -1;
+  if (s.fmt == DQ_FMT_NVFP4 && g != 16) return -1;
+  return g;
+}
+
+int scale_bytes(int fmt) { return fmt == DQ_FMT_INT4 ? 2 : 1; }
+// Column partials per row strip: N, D (and the NVFP4 column amax); fp64 for INT4.
+size_t partial_bytes(int fmt, int64_t strips, int64_t cols) {
+  const int nq = fmt == DQ_FMT_NVFP4 ? 3 : 2;
+  const size_t el = fmt == DQ_FMT_INT4 ? sizeof(double) : sizeof(float);
+  return (size_t)strips * nq * cols * el;
+}
+int elem_bytes(int dt) { return dt == DQ_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks shared by every entry point that reads a [rows][ld] matrix.
+int check_matrix(const void* X, int32_t dt, int64_t rows, int64_t cols, int64_t ld, int g) {
+  if (dt != DQ_F32 && dt != DQ_BF16) return DQ_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || ld < cols) return DQ_ERR_SHAPE;
+  if (cols % g != 0 || cols > kMaxCols) return DQ_ERR_SHAPE;
+  if (rows > 0 && cols > 0) {
+    if (!X) return DQ_ERR_NULL;
+    if (!aligned16(X) || ((ld * elem_bytes(dt)) % 16) != 0) return DQ_ERR_ALIGN;
+  }
+  return DQ_OK;
+}
+
+// Sweep geometry: a row of cols/16 chunks is held by lpr lanes (a multiple of 64) with
+// K chunks each; workgroups have at most 512 threads (256 registers per lane).
+int sweep_chunks_per_lane(int64_t cols) { return cols / 16 > 512 ? 2 : 1; }
+int sweep_lanes_per_row(int64_t cols) {
+  int64_t nch = cols / 16, K = sweep_chunks_per_lane(cols);
+  return (int)std::max<int64_t>(64, ((nch + K - 1) / K + 63) / 64 * 64);
+}
+// Row slots per workgroup: up to 512 threads, and the slot-combine buffer of the sweep
+// ((H-1) * lpr * 16 accumulators, fp64 for INT4) within 48 KB of LDS.
+int sweep_row_slots(int lpr, int fmt) {
+  const int cap = fmt == DQ_FMT_INT4 ? 384 : 768;
+  return std::max(1, std::min(512 / lpr, 1 + cap / lpr));
+}
+// Standalone quantiser geometry: one chunk per lane, up to 1024 threads.
+int lanes_per_row(int64_t cols) { return (int)std::max<int64_t>(64, (cols / 16 + 63) / 64 * 64); }
+int row_slots(int lpr) { return std::max(1, 1024 / lpr); }
+
+struct Plan {
+  // per problem
+  std::vector<ProbDev> dev;
+  std::vector<int> group_of;   // launch group index, -1 for empty problems
+  // per launch group: (dtype, lpr)
+  struct Group {
+    int dtype, lpr, H, K;
+    std::vector<WgEntry> sweep, fin;
+    size_t sweep_off, fin_off;  // offsets of the tables in the workspace
+    int max_init_wgs;
+  };
+  std::vector<Group> groups;
+  size_t probs_off = 0, total = 0;
+  std::vector<size_t> prob_off, prob_bytes;
+};
+
+// Lays out the workspace and the launch tables.  With ws == nullptr only sizes are
+// computed (pointers in `dev` are then offsets, unused).
+int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Plan& pl) {
+  pl.dev.assign(count, ProbDev{});
+  pl.group_of.assign(count, -1);
+  pl.prob_off.assign(count, 0);
+  pl.prob_bytes.assign(count, 0);
+  std::map<std::pair<int, int>, int> gid;
+  std::vector<int64_t> group_rows;
+  for (int k = 0; k < count; ++k) {
+    if (p[k].rows == 0 || p[k].cols == 0) continue;
+    int lpr = sweep_lanes_per_row(p[k].cols);
+    auto key = std::make_pair((int)p[k].w_dtype, lpr);
+    auto it = gid.find(key);
+    if (it == gid.end()) {
+      Plan::Group G;
+      G.dtype = p[k].w_dtype;
+      G.lpr = lpr;
+      G.H = sweep_row_slots(lpr, fmt);
+      G.K = sweep_chunks_per_lane(p[k].cols);
+      G.max_init_wgs = 0;
+      it = gid.emplace(key, (int)pl.groups.size()).first;
+      pl.groups.push_back(G);
+      group_rows.push_back(0);
+    }
+    pl.group_of[k] = it->second;
+    group_rows[it->second] += p[k].rows;
+  }
+  size_t off = 0;
+  for (int k = 0; k < count; ++k) {
+    ProbDev& d = pl.dev[k];
+    d.rows = p[k].rows;
+    d.cols = p[k].cols;
+    d.ld = p[k].ld;
+    d.iters = iters;
+    d.dtype = p[k].w_dtype;
+    if (pl.group_of[k] < 0) continue;
+    Plan::Group& G = pl.groups[pl.group_of[k]];
+    int64_t R = (group_rows[pl.group_of[k]] + kTargetWgs - 1) / kTargetWgs;
+    R = std::max<int64_t>(G.H, (R + G.H - 1) / G.H * G.H);
+    d.lpr = G.lpr;
+    d.hslots = G.H;
+    d.rows_per_strip = (int32_t)R;
+    d.strips = (int32_t)((d.rows + R - 1) / R);
+    d.fin_wgs = (int32_t)((d.cols + 63) / 64);
+    d.init_wgs = (int32_t)std::min<int64_t>(1024, d.rows);
+    G.max_init_wgs = std::max(G.max_init_wgs, d.init_wgs);
+    size_t start = off;
+    pl.prob_off[k] = off;
+    off = align_up(off + sizeof(State));
+    off = align_up(off + 4 * sizeof(float) * d.rows);                  // r[2], ir[2]
+    off = align_up(off + 4 * sizeof(float) * d.cols);                  // c[2], ic[2]
+    off = align_up(off + (size_t)d.rows * d.cols / 2);                 // codes buffer 1
+    off = align_up(off + (size_t)d.rows * d.cols / g * scale_bytes(fmt));
+    off = align_up(off + partial_bytes(fmt, d.strips, d.cols));
+    off = align_up(off + (size_t)d.strips * 4 * sizeof(double));
+    off = align_up(off + (size_t)d.fin_wgs * sizeof(float));
+    off = align_up(off + (size_t)d.init_wgs * 2 * sizeof(double));
+    off = align_up(off + 2 * (size_t)(iters + 1) * sizeof(double));   // histories if caller has none
+    pl.prob_bytes[k] = off - start;
+    for (int s = 0; s < d.strips; ++s) G.sweep.push_back(WgEntry{k, s});
+    for (int f = 0; f < d.fin_wgs; ++f) G.fin.push_back(WgEntry{k, f});
+  }
+  pl.probs_off = off;
+  off = align_up(off + sizeof(ProbDev) * std::max(1, (int)count));
+  for (auto& G : pl.groups) {
+    G.sweep_off = off;
+    off = align_up(off + sizeof(WgEntry) * G.sweep.size());
+    G.fin_off = off;
+    off = align_up(off + sizeof(WgEntry) * G.fin.size());
+  }
+  pl.total = off;
+  return DQ_OK;
+}
+
+void bind_pointers(const dq_problem* p, int32_t count, int g, int fmt, int iters, char* ws,
+                   Plan& pl) {
+  for (int k = 0; k < count; ++k) {
+    if (pl.group_of[k] < 0) continue;
+    ProbDev& d = pl.dev[k];
+    char* q = ws + pl.prob_off[k];
+    auto take = [&](size_t bytes) { char* r = q; q += align_up(bytes); return r; };
+    d.st = (State*)take(sizeof(State));
+    float* rr = (float*)take(4 * sizeof(float) * d.rows);
+    d.r[0] = rr; d.r[1] = rr + d.rows; d.ir[0] = rr + 2 * d.rows; d.ir[1] = rr + 3 * d.rows;
+    float* cc = (float*)take(4 * sizeof(float) * d.cols);
+    d.c[0] = cc; d.c[1] = cc + d.cols; d.ic[0] = cc + 2 * d.cols; d.ic[1] = cc + 3 * d.cols;
+    d.codes[0] = p[k].codes;
+    d.codes[1] = (uint8_t*)take((size_t)d.rows * d.cols / 2);
+    d.scales[0] = p[k].block_scales;
+    d.scales[1] = take((size_t)d.rows * d.cols / g * scale_bytes(fmt));
+    d.colP = take(partial_bytes(fmt, d.strips, d.cols));
+    d.swp = (double*)take((size_t)d.strips * 4 * sizeof(double));
+    d.fwp = (float*)take((size_t)d.fin_wgs * sizeof(float));
+    d.initp = (double*)take((size_t)d.init_wgs * 2 * sizeof(double));
+    double* hist = (double*)take(2 * (size_t)(iters + 1) * sizeof(double));
+    d.nmse = p[k].nmse_hist ? p[k].nmse_hist : hist;
+    d.relchg = p[k].relchg_hist ? p[k].relchg_hist : hist + (iters + 1);
+    d.W = p[k].W;
+    d.r_trace = p[k].r_trace;
+    d.c_trace = p[k].c_trace;
+    d.r_init = p[k].r_init;
+    d.c_init = p[k].c_init;
+  }
+}
+
+// ---------------------------------------------------------------- template dispatch
+template <int FMT>
+constexpr int lanes_per_block(int g) { return g / 16; }
+
+#define DQ_HIP(call)                                   \
+  do {                                                 \
+    if ((call) != hipSuccess) return DQ_ERR_HIP;       \
+  } while (0)
+
+template <int FMT, int DT, int L>
+int launch_sweep(const Plan::Group& G, const ProbDev* probs, const WgEntry* tab,
+                 hipStream_t s) {
+  size_t dyn = (size_t)(G.H - 1) * G.lpr * 16 * (FMT == INT4 ? sizeof(double) : sizeof(float));
+  dim3 grid((unsigned)G.sweep.size()), block((unsigned)(G.lpr * G.H));
+  if (G.K == 1) hipLaunchKernelGGL((k_sweep<FMT, DT, L, 1>), grid, block, dyn, s, probs, tab);
+  else hipLaunchKernelGGL((k_sweep<FMT, DT, L, 2>), grid, block, dyn, s, probs, tab);
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
+template <int FMT, int L>
+int launch_sweep_dt(int dt, const Plan::Group& G, const ProbDev* probs, const WgEntry* tab,
+                    hipStream_t s) {
+  return dt == DQ_F32 ? launch_sweep<FMT, 0, L>(G, probs, tab, s)
+                      : launch_sweep<FMT, 1, L>(G, probs, tab, s);
+}
+
+int launch_sweep_any(int fmt, int g, const Plan::Group& G, const ProbDev* probs,
+                     const WgEntry* tab, hipStream_t s) {
+  switch (fmt) {
+    case DQ_FMT_INT4:
+      return g == 64 ? launch_sweep_dt<INT4, 4>(G.dtype, G, probs, tab, s)
+                     : launch_sweep_dt<INT4, 8>(G.dtype, G, probs, tab, s);
+    case DQ_FMT_MXINT4: return launch_sweep_dt<MXINT4, 2>(G.dtype, G, probs, tab, s);
+    case DQ_FMT_MXFP4: return launch_sweep_dt<MXFP4, 2>(G.dtype, G, probs, tab, s);
+    default: return launch_sweep_dt<NVFP4, 1>(G.dtype, G, probs, tab, s);
+  }
+}
+
+int launch_finalize_any(int fmt, const Plan::Group& G, const ProbDev* probs,
+                        const WgEntry* tab, hipStream_t s) {
+  dim3 grid((unsigned)G.fin.size()), block(256);
+  switch (fmt) {
+    case DQ_FMT_INT4: hipLaunchKernelGGL((k_finalize<INT4>), grid, block, 0, s, probs, tab); break;
+    case DQ_FMT_MXINT4: hipLaunchKernelGGL((k_finalize<MXINT4>), grid, block, 0, s, probs, tab); break;
+    case DQ_FMT_MXFP4: hipLaunchKernelGGL((k_finalize<MXFP4>), grid, block, 0, s, probs, tab); break;
+    default: hipLaunchKernelGGL((k_finalize<NVFP4>), grid, block, 0, s, probs, tab); break;
+  }
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
+template <int FMT>
+int launch_init_t(int dt, dim3 grid, const ProbDev* probs, hipStream_t s) {
+  if (dt == DQ_F32) hipLaunchKernelGGL((k_init<FMT, 0>), grid, dim3(256), 0, s, probs);
+  else hipLaunchKernelGGL((k_init<FMT, 1>), grid, dim3(256), 0, s, probs);
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
+int launch_init_any(int fmt, int dt, dim3 grid, const ProbDev* probs, hipStream_t s) {
+  switch (fmt) {
+    case DQ_FMT_INT4: return launch_init_t<INT4>(dt, grid, probs, s);
+    case DQ_FMT_MXINT4: return launch_init_t<MXINT4>(dt, grid, probs, s);
+    case DQ_FMT_MXFP4: return launch_init_t<MXFP4>(dt, grid, probs, s);
+    default: return launch_init_t<NVFP4>(dt, grid, probs, s);
+  }
+}
+
+// Standalone quantiser (weights: MODEV 0; activations: MODEV 1).
+template <int FMT, int DT, int L, int MODEV>
+int launch_quant_t(const void* X, int64_t rows, int64_t cols, int64_t ld, const float* r,
+                   const float* c, uint8_t* codes, void* scales, float* ts, float* part,
+                   int nparts, hipStream_t s) {
+  if (FMT == NVFP4)
+    hipLaunchKernelGGL((k_qamax<DT, MODEV>), dim3(nparts), dim3(256), 0, s, X, rows, cols, ld,
+                       r, c, part);
+  int lpr = lanes_per_row(cols), H = row_slots(lpr);
+  hipLaunchKernelGGL((k_quant<FMT, DT, L, MODEV>), dim3((unsigned)((rows + H - 1) / H)),
+                     dim3(lpr * H), 0, s, X, rows, cols, ld, r, c, codes, scales, ts, part,
+                     nparts, lpr, H);
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
+template <int MODEV>
+int launch_quant_any(int fmt, int g, int dt, const void* X, int64_t rows, int64_t cols,
+                     int64_t ld, const float* r, const float* c, uint8_t* codes, void* scales,
+                     float* ts, float* part, int nparts, hipStream_t s) {
+#define DQ_Q(F, L)                                                                           \
+  return dt == DQ_F32                                                                        \
+             ? launch_quant_t<F, 0, L, MODEV>(X, rows, cols, ld, r, c, codes, scales, ts,    \
+                                              part, nparts, s)                               \
+             : launch_quant_t<F, 1, L, MODEV>(X, rows, cols, ld, r, c, codes, scales, ts,    \
+                                              part, nparts, s)
+  switch (fmt) {
+    case DQ_FMT_INT4:
+      if (g == 64) { DQ_Q(INT4, 4); }
+      DQ_Q(INT4, 8);
+    case DQ_FMT_MXINT4: DQ_Q(MXINT4, 2);
+    case DQ_FMT_MXFP4: DQ_Q(MXFP4, 2);
+    default: DQ_Q(NVFP4, 1);
+  }
+#undef DQ_Q
+}
+
+constexpr int kQuantParts = 1024;
+
+}  // namespace
+
+// ============================================================================ C ABI
+extern "C" {
+
+const char* dq_status_string(int status) {
+  switch (status) {
+    case DQ_OK: return "ok";
+    case DQ_ERR_NULL: return "a required pointer is NULL";
+    case DQ_ERR_SHAPE: return "invalid shape (rows/cols/ld, cols not a multiple of the group, or cols > 16384)";
+    case DQ_ERR_ALIGN: return "base pointer or row pitch not 16-byte aligned";
+    case DQ_ERR_FORMAT: return "unknown format, group or dtype";
+    case DQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case DQ_ERR_HIP: return "HIP runtime error";
+    case DQ_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+static int validate_solve(const dq_problem* p, int32_t count, dq_quant_spec spec,
+                          const dq_solve_opts* o, int* g_out) {
+  if (!p || !o) return DQ_ERR_NULL;
+  if (count < 1) return DQ_ERR_ARG;
+  int g = resolve_group(spec);
+  if (g < 0) return DQ_ERR_FORMAT;
+  if (o->iters < 0 || !(o->tol_relchg >= 0.0f)) return DQ_ERR_ARG;
+  for (int k = 0; k < count; ++k) {
+    int rc = check_matrix(p[k].W, p[k].w_dtype, p[k].rows, p[k].cols, p[k].ld, g);
+    if (rc) return rc;
+    if (p[k].rows == 0 || p[k].cols == 0) continue;
+    if (!p[k].r || !p[k].c || !p[k].codes || !p[k].block_scales) return DQ_ERR_NULL;
+    if (spec.fmt == DQ_FMT_NVFP4 && !p[k].tensor_scale) return DQ_ERR_NULL;
+    if (!aligned16(p[k].codes) || !aligned16(p[k].block_scales)) return DQ_ERR_ALIGN;
+    if (p[k].r_init && !aligned16(p[k].r_init)) return DQ_ERR_ALIGN;
+    if (p[k].c_init && !aligned16(p[k].c_init)) return DQ_ERR_ALIGN;
+  }
+  *g_out = g;
+  return DQ_OK;
+}
+
+size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_spec spec,
+                          const dq_solve_opts* opts) {
+  int g = 0;
+  if (validate_solve(problems, count, spec, opts, &g) != DQ_OK) return 0;
+  Plan pl;
+  make_plan(problems, count, g, spec.fmt, opts->iters, pl);
+  return pl.total;
+}
+
+int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
+             const dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
+  int g = 0;
+  int rc = validate_solve(problems, count, spec, opts, &g);
+  if (rc) return rc;
+  Plan pl;
+  make_plan(problems, count, g, spec.fmt, opts->iters, pl);
+  if (!workspace) return DQ_ERR_WORKSPACE;
+  if (workspace_bytes < pl.total) return DQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DQ_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  bind_pointers(problems, count, g, spec.fmt, opts->iters, ws, pl);
+  for (auto& d : pl.dev) d.tol = opts->tol_relchg;
+  const int iters = opts->iters;
+
+  // empty problems: zero histories, report immediately
+  for (int k = 0; k < count; ++k) {
+    if (pl.group_of[k] >= 0) continue;
+    if (problems[k].nmse_hist)
+      DQ_HIP(hipMemsetAsync(problems[k].nmse_hist, 0, sizeof(double) * (iters + 1), s));
+    if (problems[k].relchg_hist)
+      DQ_HIP(hipMemsetAsync(problems[k].relchg_hist, 0, sizeof(double) * (iters + 1), s));
+  }
+  if (pl.groups.empty()) {
+    DQ_HIP(hipStreamSynchronize(s));
+    for (int k = 0; k < count; ++k)
+      if (problems[k].report) *problems[k].report = dq_report{iters, 0, 0u, 0};
+    return DQ_OK;
+  }
+
+  ProbDev* dprobs = (ProbDev*)(ws + pl.probs_off);
+  DQ_HIP(hipMemcpyAsync(dprobs, pl.dev.data(), sizeof(ProbDev) * count, hipMemcpyHostToDevice, s));
+  for (auto& G : pl.groups) {
+    DQ_HIP(hipMemcpyAsync(ws + G.sweep_off, G.sweep.data(), sizeof(WgEntry) * G.sweep.size(),
+                          hipMemcpyHostToDevice, s));
+    DQ_HIP(hipMemcpyAsync(ws + G.fin_off, G.fin.data(), sizeof(WgEntry) * G.fin.size(),
+                          hipMemcpyHostToDevice, s));
+  }
+
+  int64_t maxdim = 1;
+  int max_init = 1;
+  for (int k = 0; k < count; ++k) {
+    if (pl.group_of[k] < 0) continue;
+    maxdim = std::max(maxdim, std::max(pl.dev[k].rows, pl.dev[k].cols));
+    max_init = std::max(max_init, pl.dev[k].init_wgs);
+  }
+  hipLaunchKernelGGL(k_setup, dim3((unsigned)((maxdim + 255) / 256), (unsigned)count), dim3(256),
+                     0, s, dprobs);
+  DQ_HIP(hipGetLastError());
+  for (int dt = 0; dt < 2; ++dt) {
+    bool any = false;
+    for (int k = 0; k < count; ++k) any |= (pl.group_of[k] >= 0 && problems[k].w_dtype == dt);
+    if (!any) continue;
+    rc = launch_init_any(spec.fmt, dt, dim3((unsigned)max_init, (unsigned)count), dprobs, s);
+    if (rc) return rc;
+  }
+
+  std::vector<State> hst(count);
+  int pending = 1 + iters;   // INIT sweep + one sweep per iteration, if nothing is rejected
+  // at most one extra (re-solve) sweep per rejected iteration
+  const int max_sweeps = 2 * iters + 2;
+  int launched = 0;
+  while (pending > 0) {
+    if (launched + pending > max_sweeps) return DQ_ERR_HIP;
+    launched += pending;
+    for (int sw = 0; sw < pending; ++sw) {
+      for (auto& G : pl.groups) {
+        rc = launch_sweep_any(spec.fmt, g, G, dprobs, (const WgEntry*)(ws + G.sweep_off), s);
+        if (rc) return rc;
+      }
+      for (auto& G : pl.groups) {
+        rc = launch_finalize_any(spec.fmt, G, dprobs, (const WgEntry*)(ws + G.fin_off), s);
+        if (rc) return rc;
+      }
+    }
+    DQ_HIP(hipStreamSynchronize(s));
+    pending = 0;
+    for (int k = 0; k < count; ++k) {
+      if (pl.group_of[k] < 0) continue;
+      DQ_HIP(hipMemcpy(&hst[k], pl.dev[k].st, sizeof(State), hipMemcpyDeviceToHost));
+      if (hst[k].mode == MODE_DONE) continue;
+      int need = (iters - hst[k].it_done) + (hst[k].mode == MODE_FIXUP ? 1 : 0);
+      pending = std::max(pending, need);
+    }
+  }
+
+  // outputs: final scales, kept codes, tensor scale, reports
+  for (int k = 0; k < count; ++k) {
+    if (pl.group_of[k] < 0) continue;
+    const ProbDev& d = pl.dev[k];
+    const State& S = hst[k];
+    DQ_HIP(hipMemcpyAsync(problems[k].r, d.r[S.rs], sizeof(float) * d.rows, hipMemcpyDeviceToDevice, s));
+    DQ_HIP(hipMemcpyAsync(problems[k].c, d.c[S.cs], sizeof(float) * d.cols, hipMemcpyDeviceToDevice, s));
+    if (S.acc == 1) {
+      DQ_HIP(hipMemcpyAsync(d.codes[0], d.codes[1], (size_t)d.rows * d.cols / 2,
+                            hipMemcpyDeviceToDevice, s));
+      DQ_HIP(hipMemcpyAsync(d.scales[0], d.scales[1],
+                            (size_t)d.rows * d.cols / g * scale_bytes(spec.fmt),
+                            hipMemcpyDeviceToDevice, s));
+    }
+    if (spec.fmt == DQ_FMT_NVFP4)
+      DQ_HIP(hipMemcpyAsync(problems[k].tensor_scale, &d.st->st_acc, sizeof(float),
+                            hipMemcpyDeviceToDevice, s));
+  }
+  DQ_HIP(hipStreamSynchronize(s));
+  for (int k = 0; k < count; ++k) {
+    if (!problems[k].report) continue;
+    if (pl.group_of[k] < 0) { *problems[k].report = dq_report{iters, 0, 0u, 0}; continue; }
+    const State& S = hst[k];
+    *problems[k].report = dq_report{S.it_done, S.rejected, S.flags, S.sweeps};
+  }
+  return DQ_OK;
+}
+
+size_t dq_quantize_workspace_bytes(int64_t rows, int64_t cols, dq_quant_spec spec) {
+  (void)rows;
+  (void)cols;
+  return spec.fmt == DQ_FMT_NVFP4 ? kQuantParts * sizeof(float) : 0;
+}
+
+static int quantize_common(int modev, const void* X, int32_t dt, int64_t rows, int64_t cols,
+                           int64_t ld, const float* r, const float* c, dq_quant_spec spec,
+                           uint8_t* codes, void* scales, float* ts, void* ws, size_t wsb,
+                           void* stream) {
+  int g = resolve_group(spec);
+  if (g < 0) return DQ_ERR_FORMAT;
+  int rc = check_matrix(X, dt, rows, cols, ld, g);
+  if (rc) return rc;
+  if (rows == 0 || cols == 0) return DQ_OK;
+  if (!codes || !scales) return DQ_ERR_NULL;
+  if (spec.fmt == DQ_FMT_NVFP4 && !ts) return DQ_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(scales)) return DQ_ERR_ALIGN;
+  if (spec.fmt == DQ_FMT_NVFP4) {
+    if (!ws) return DQ_ERR_WORKSPACE;
+    if (wsb < dq_quantize_workspace_bytes(rows, cols, spec)) return DQ_ERR_WORKSPACE;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (modev == 0)
+    return launch_quant_any<0>(spec.fmt, g, dt, X, rows, cols, ld, r, c, codes, scales, ts,
+                               (float*)ws, kQuantParts, s);
+  return launch_quant_any<1>(spec.fmt, g, dt, X, rows, cols, ld, nullptr, c, codes, scales, ts,
+                             (float*)ws, kQuantParts, s);
+}
+
+int dq_quantize_weights(const void* W, int32_t w_dtype, int64_t rows, int64_t cols, int64_t ld,
+                        const float* r, const float* c, dq_quant_spec spec, uint8_t* codes,
+                        void* block_scales, float* tensor_scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return quantize_common(0, W, w_dtype, rows, cols, ld, r, c, spec, codes, block_scales,
+                         tensor_scale, workspace, workspace_bytes, stream);
+}
+
+int dq_rescale_quantize_acts(const void* X, int32_t x_dtype, int64_t tokens, int64_t cols,
+                             int64_t ld, const float* c, dq_quant_spec spec, uint8_t* codes,
+                             void* block_scales, float* tensor_scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return quantize_common(1, X, x_dtype, tokens, cols, ld, nullptr, c, spec, codes, block_scales,
+                         tensor_scale, workspace, workspace_bytes, stream);
+}
+
+int dq_dequantize(dq_quant_spec spec, const uint8_t* codes, const void* block_scales,
+                  const float* tensor_scale, int64_t rows, int64_t cols, const float* r,
+                  const float* c, float* out, void* stream) {
+  int g = resolve_group(spec);
+  if (g < 0) return DQ_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || cols % g) return DQ_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return DQ_OK;
+  if (!codes || !block_scales || !out) return DQ_ERR_NULL;
+  if (spec.fmt == DQ_FMT_NVFP4 && !tensor_scale) return DQ_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  int64_t nthreads = rows * (cols / 16);
+  dim3 grid((unsigned)((nthreads + 255) / 256)), block(256);
+  switch (spec.fmt) {
+    case DQ_FMT_INT4:
+      if (g == 64) hipLaunchKernelGGL((k_dequant<INT4, 4>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out);
+      else hipLaunchKernelGGL((k_dequant<INT4, 8>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out);
+      break;
+    case DQ_FMT_MXINT4: hipLaunchKernelGGL((k_dequant<MXINT4, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
+    case DQ_FMT_MXFP4: hipLaunchKernelGGL((k_dequant<MXFP4, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
+    default: hipLaunchKernelGGL((k_dequant<NVFP4, 1>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
+  }
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
+int dq_debug_round(int32_t fn, const float* x, void* out, int64_t n, void* stream) {
+  if (fn < DQ_ROUND_E2M1 || fn > DQ_PROJ_BF16) return DQ_ERR_ARG;
+  if (n < 0) return DQ_ERR_SHAPE;
+  if (n == 0) return DQ_OK;
+  if (!x || !out) return DQ_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(k_debug_round, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (int)fn,
+                     x, out, n);
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
+}  // extern "C"

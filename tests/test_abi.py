@@ -1,0 +1,91 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point the header
+declares, and rejects bad arguments synchronously (before any HIP call)."""
+
+import ctypes as C
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+@pytest.fixture(scope="module")
+def dq():
+    import post_quantization_dq_amd as dq
+
+    return dq
+
+
+def _declared():
+    text = (ROOT / "include" / "dq.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(dq):
+    names = _declared()
+    assert set(names) == set(dq.EXPORTED)
+    lib = C.CDLL(str(ROOT / "post_quantization_dq_amd" / "libdq.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(dq):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert dq.dq_status_string(s) and dq.dq_status_string(s) != "unknown status"
+
+
+def _problem(dq, rows=64, cols=256, ld=None, dtype=1, W=0x10000, codes=0x20000):
+    return dq.dq_problem(W=W, w_dtype=dtype, reserved=0, rows=rows, cols=cols,
+                         ld=ld if ld is not None else cols, r_init=None, c_init=None, r=0x30000,
+                         c=0x40000, codes=codes, block_scales=0x50000, tensor_scale=0x60000,
+                         nmse_hist=None, relchg_hist=None, r_pre=None, c_pre=None, report=None)
+
+
+def _solve_rc(dq, probs, fmt=3, group=0, iters=4, ws=0x70000, wsb=1 << 40):
+    arr = (dq.dq_problem * len(probs))(*probs)
+    opts = dq.dq_solve_opts(iters, 0.0)
+    return dq._lib.dq_solve(arr, len(probs), dq.dq_quant_spec(fmt, group), C.byref(opts), ws, wsb, None)
+
+
+def test_solve_argument_errors(dq):
+    ok = _problem(dq)
+    assert _solve_rc(dq, [ok], fmt=7) == -4                         # unknown format
+    assert _solve_rc(dq, [ok], fmt=0, group=32) == -4               # INT4 needs 64 or 128
+    assert _solve_rc(dq, [_problem(dq, cols=200)]) == -2            # not a whole number of blocks
+    assert _solve_rc(dq, [_problem(dq, cols=32768)]) == -2          # wider than 16384
+    assert _solve_rc(dq, [_problem(dq, ld=100)]) == -2              # ld < cols
+    assert _solve_rc(dq, [_problem(dq, W=0x10004)]) == -3           # misaligned W
+    assert _solve_rc(dq, [_problem(dq, ld=260)]) == -3              # row pitch not 16-byte multiple
+    assert _solve_rc(dq, [_problem(dq, W=0)]) == -1                 # null W
+    assert _solve_rc(dq, [_problem(dq, dtype=5)]) == -4             # unknown dtype
+    assert _solve_rc(dq, [ok], iters=-1) == -7
+    assert _solve_rc(dq, [ok], ws=0) == -5                          # no workspace
+    assert _solve_rc(dq, [ok], wsb=16) == -5                        # workspace too small
+    arr = (dq.dq_problem * 1)(ok)
+    assert dq._lib.dq_solve(arr, 0, dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(1, 0.0)), 0x70000, 1 << 40, None) == -7
+
+
+def test_workspace_bytes_accounting(dq):
+    ok = _problem(dq, rows=4096, cols=14336)
+    arr = (dq.dq_problem * 1)(ok)
+    nb = dq._lib.dq_workspace_bytes(arr, 1, dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(16, 0.0)))
+    # at least the second code/scale buffer, scales, column partials for one strip per CU
+    assert nb >= 4096 * 14336 // 2 + 4096 * 14336 // 16
+    assert nb < 4096 * 14336 * 2   # below the size of W itself
+    bad = (dq.dq_problem * 1)(_problem(dq, cols=200))
+    assert dq._lib.dq_workspace_bytes(bad, 1, dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(16, 0.0))) == 0
+
+
+def test_quantize_argument_errors(dq):
+    L = dq._lib
+    sp = dq.dq_quant_spec(3, 0)
+    assert L.dq_quantize_weights(0x10000, 1, 8, 200, 200, None, None, sp, 0x20000, 0x30000, 0x40000, 0x50000, 4096, None) == -2
+    assert L.dq_quantize_weights(0x10000, 1, 8, 256, 256, None, None, sp, 0x20000, 0x30000, 0x40000, 0, 0, None) == -5
+    assert L.dq_quantize_weights(0x10000, 1, 8, 256, 256, None, None, dq.dq_quant_spec(9, 0), 0x20000, 0x30000, 0x40000, 0x50000, 4096, None) == -4
+    assert L.dq_rescale_quantize_acts(0x10000, 1, 8, 256, 256, None, sp, 0, 0x30000, 0x40000, 0x50000, 4096, None) == -1
+    assert L.dq_rescale_quantize_acts(0x10002, 1, 8, 256, 256, None, sp, 0x20000, 0x30000, 0x40000, 0x50000, 4096, None) == -3
+    assert L.dq_quantize_weights(0x10000, 1, 0, 256, 256, None, None, sp, 0, 0, 0, 0, 0, None) == 0   # empty
+    assert L.dq_dequantize(dq.dq_quant_spec(2, 0), 0x10000, 0x20000, None, 4, 48, None, None, 0x30000, None) == -2
+    assert L.dq_debug_round(99, 0x10000, 0x20000, 4, None) == -7

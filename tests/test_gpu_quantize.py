@@ -1,0 +1,86 @@
+"""dq_quantize_weights / dq_rescale_quantize_acts / dq_dequantize against the oracle:
+codes, block scales and tensor scale bit-exact given identical scales."""
+
+import numpy as np
+import pytest
+import torch
+
+import post_quantization_dq_amd as dq
+import synth
+from gpu_util import DEV, FORMATS, GROUPS, scales_np, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(64, 256), (37, 512), (3, 16384), (1, 128), (130, 14336)]
+
+
+def _w(rows, cols, dtype, seed):
+    spec = synth.MatrixSpec(rows, cols, "student_t", 0.02, nu=3, outliers=max(1, cols // 100),
+                            outlier_scale=25.0, dtype=dtype, stream=40 + seed)
+    return synth.matrix(spec, seed)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_quantize_weights_bit_exact(oracle_lib, fmt, dtype, shape):
+    rows, cols = shape
+    if cols % GROUPS[fmt]:
+        pytest.skip("shape not a whole number of blocks")
+    W = _w(rows, cols, dtype, 1)
+    rng = np.random.default_rng(rows * 7 + cols)
+    for with_scales in (False, True):
+        r = c = None
+        if with_scales:
+            r = oracle_lib.project(fmt, np.exp2(rng.uniform(-2, 2, rows)).astype(np.float32))
+            c = oracle_lib.project(fmt, np.exp2(rng.uniform(-2, 2, cols)).astype(np.float32))
+        codes, scales, ts, _ = oracle_lib.quantize_weights(W, r, c, fmt)
+        gc, gs, gt = dq.quantize_weights(to_dev(W), None if r is None else to_dev(r),
+                                         None if c is None else to_dev(c), fmt)
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.cpu().numpy(), codes)
+        assert np.array_equal(scales_np(gs, fmt), scales)
+        if fmt == "NVFP4":
+            assert gt.item() == np.float32(ts)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_rescale_quantize_acts_bit_exact(oracle_lib, fmt):
+    X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(96, 1024), 0)
+    rng = np.random.default_rng(3)
+    c = oracle_lib.project(fmt, np.exp2(rng.uniform(-3, 3, 1024)).astype(np.float32))
+    for cc in (None, c):
+        codes, scales, ts, _ = oracle_lib.rescale_quantize_acts(X, cc, fmt)
+        gc, gs, gt = dq.rescale_quantize_acts(to_dev(X), None if cc is None else to_dev(cc), fmt)
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.cpu().numpy(), codes)
+        assert np.array_equal(scales_np(gs, fmt), scales)
+        if fmt == "NVFP4":
+            assert gt.item() == np.float32(ts)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_dequantize_matches_oracle(oracle_lib, fmt):
+    W = _w(48, 512, "bf16", 4)
+    codes, scales, ts, qhat = oracle_lib.quantize_weights(W, None, None, fmt)
+    sdt = torch.int16 if fmt == "INT4" else torch.uint8
+    sc = torch.from_numpy(scales.view(np.int16) if fmt == "INT4" else scales).to(DEV)
+    out = dq.dequantize(torch.from_numpy(codes).to(DEV), sc, torch.tensor([ts], dtype=torch.float32, device=DEV),
+                        48, 512, fmt)
+    torch.cuda.synchronize()
+    assert sc.dtype == sdt
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), qhat.view(np.uint32))
+    r = np.linspace(0.5, 2, 48).astype(np.float32)
+    c = np.linspace(0.25, 4, 512).astype(np.float32)
+    out2 = dq.dequantize(torch.from_numpy(codes).to(DEV), sc, torch.tensor([ts], dtype=torch.float32, device=DEV),
+                         48, 512, fmt, r=to_dev(r), c=to_dev(c))
+    torch.cuda.synchronize()
+    want = ((r[:, None] * qhat).astype(np.float32) * c[None, :]).astype(np.float32)
+    assert np.array_equal(out2.cpu().numpy(), want)
+
+
+def test_empty_inputs():
+    W = torch.empty(0, 256, dtype=torch.bfloat16, device=DEV)
+    gc, gs, gt = dq.quantize_weights(W, None, None, "NVFP4")
+    torch.cuda.synchronize()
+    assert gc.numel() == 0
