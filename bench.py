@@ -1,0 +1,217 @@
+"""Benchmark of the DualQuant dual-scale BCD solver on one MI355X.
+
+One step = the whole hot path over one synthetic input: a dual-scale solve of a
+down_proj-shaped 4096x14336 bf16 weight to NVFP4 (16 BCD iterations: init, sweeps,
+finalizes, output pack), then the activation rescale-and-quantize of a 2048-token bf16
+batch with the column scales the solve produced.  Inputs are resident in HBM before the
+timed region.
+
+Printed (one JSON line): whole-job throughput in Gelem/s per iteration (rows*cols*T /
+step time); the roofline of the dominant kernel -- whichever of the row pass and the column
+pass takes longer per step -- as algorithmic bytes (one read of W plus the scale vectors)
+over its average launch duration from HIP event pairs attached to its launches in the timed
+region, against the 8 TB/s HBM peak, with the counter-measured traffic recorded under
+profiles/ when the kernel source is unchanged; and the CPU oracle timed on a bounded sample
+on this host.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --copy-calibration     # plain copy of known size, for counter scaling
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "down4096x14336_nvfp4"
+ACT_TOKENS = 2048
+METRIC = "BCD solver Gelem/s per iteration + achieved HBM GB/s vs peak (4096×14336 NVFP4)"
+
+
+KERNELS = ("k_rowpass", "k_colpass", "k_finalize")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("dq_device.hpp", "dq_kernels.hpp"):
+        h.update((ROOT / "post_quantization_dq_amd" / "csrc" / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """Counter-measured HBM bytes per launch of `kernel` from profiles/, if the counters were
+    taken on the current kernel source."""
+    f = ROOT / "profiles" / f"{kernel}_{workload}_counters.md"
+    if not f.exists():
+        return None
+    text = f.read_text()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def copy_calibration():
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+
+
+def cpu_baseline(W, fmt, iters=2):
+    import oracle
+
+    cores = min(16, os.cpu_count() or 1)
+    oracle.set_threads(cores)
+    t0 = time.perf_counter()
+    oracle.solve(W, fmt, iters)
+    dt = time.perf_counter() - t0
+    m, n = W.shape
+    return {"value": m * n * iters / dt / 1e9, "unit": "Gelem/s", "cores": cores, "kind": "oracle",
+            "sample": f"full {m}x{n} bf16 matrix, {fmt}, {iters} BCD iterations including init "
+                      f"({dt:.1f} s on {cores} threads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the solve runs on a single MI355X and this build "
+              "has no multi-GPU path (pass --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    import post_quantization_dq_amd as dq
+    import synth
+
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    fmt, group, T = wl["fmt"], wl["group"], wl["iters"]
+    W_np = synth.matrix(wl["W"], 0)
+    m, n = W_np.shape
+    xspec = synth.MatrixSpec(ACT_TOKENS, n, "normal", 1.0, outliers=synth.outlier_count(n, 0.01),
+                             outlier_scale=50.0, stream=9)
+    X_np = synth.matrix(xspec, 0)
+    W = torch.from_numpy(W_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    X = torch.from_numpy(X_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    print(f"[bench] workload {args.workload}: W {m}x{n} bf16, {fmt}, T={T}; acts {ACT_TOKENS}x{n}", flush=True)
+
+    prob = dq.make_problem(W, fmt, T, group)
+    spec = dq.spec_of(fmt, group)
+    ws = torch.empty(dq.dq_workspace_bytes([prob], spec, dq.dq_solve_opts(T, 0.0, None, 0, 0)),
+                     dtype=torch.uint8, device=dev)
+    a_codes, a_scales, a_ts = dq._outputs(ACT_TOKENS, n, fmt, group or dq.DEFAULT_GROUP[fmt], dev)
+    a_ws = torch.empty(max(1, dq.dq_quantize_workspace_bytes(ACT_TOKENS, n, spec)), dtype=torch.uint8, device=dev)
+
+    def step(passes=None):
+        rep = dq.solve_many([prob], fmt, T, group, workspace=ws, pass_ms=passes)[0]
+        dq.dq_rescale_quantize_acts(X, prob.c, spec, a_codes, a_scales, a_ts, a_ws)
+        return rep
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    passes = []
+    reps = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        reps.append(step(passes))
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms)", flush=True)
+
+    # per-kernel launch durations over the timed region (event pairs attached to the launches)
+    per = np.asarray(passes, dtype=np.float64).reshape(-1, 3)
+    avg = {k: float(per[:, q].mean()) for q, k in enumerate(KERNELS)}
+    per_step = {k: float(per[:, q].sum()) / args.steps for q, k in enumerate(KERNELS)}
+    dom = max(KERNELS[:2], key=lambda k: per_step[k])
+    print("[bench] per-launch ms: " + ", ".join(f"{k} {avg[k] * 1e3:.1f} us" for k in KERNELS), flush=True)
+    # algorithmic bytes of one pass over W: one read of W plus the r and c vectors
+    alg_bytes = m * n * W.element_size() + 8 * (m + n)
+    achieved = alg_bytes / (avg[dom] * 1e-3) / 1e9
+    t_iter_ms = float(per.sum(axis=1).mean())
+    traffic = recorded_traffic(dom, args.workload)
+    nm = prob.nmse_hist.cpu().numpy()
+    value = m * n * T / (ms_step * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"down_proj-shaped {m}x{n} bf16 weight (Student-t nu=3, std 0.015, "
+                        f"0.5% outlier columns x25), {fmt} g={group}, {T} BCD iterations; then "
+                        f"{ACT_TOKENS}x{n} bf16 activations rescaled by c and {fmt}-quantised",
+            "rows": m, "cols": n, "format": fmt, "iters": T, "act_tokens": ACT_TOKENS,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": alg_bytes,
+            "avg_launch_ms": round(avg[dom], 5),
+            "launches": int(per.shape[0]),
+        },
+        "kernel_avg_us": {k: round(avg[k] * 1e3, 2) for k in KERNELS},
+        "iteration_us": round(t_iter_ms * 1e3, 2),
+        "iteration_hbm_frac": round(alg_bytes / (t_iter_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "sweeps_per_step": int(reps[-1].sweeps),
+        "rejected_steps": int(reps[-1].rejected_steps),
+        "nmse_first_last": [float(nm[0]), float(nm[-1])],
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample ...", flush=True)
+        out["cpu_baseline"] = cpu_baseline(W_np, fmt)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -83,6 +83,12 @@ typedef struct {
   int32_t iters;     /* BCD iterations T >= 0 */
   float tol_relchg;  /* > 0: stop after the first iteration whose relative change of Qhat is
                         <= tol_relchg; 0: run all T iterations */
+  float* pass_ms;     /* HOST array or NULL: per sweep over W, three durations in ms -- the
+                          row pass, the column pass and the finalize (all problems of the
+                          call) -- from HIP event pairs attached to the kernel launches on
+                          `stream` (kernel begin and end; no extra stream commands) */
+  int32_t pass_ms_capacity;  /* sweeps that fit in pass_ms (3 floats each) */
+  int32_t pass_ms_count;     /* out: sweeps written */
 } dq_solve_opts;
 
 typedef struct {
@@ -132,7 +138,7 @@ size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_sp
  * thread until done.  `workspace` must hold dq_workspace_bytes(...) bytes of device
  * memory; its contents on entry do not matter. */
 int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
-             const dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream);
+             dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace dq_quantize_weights / dq_rescale_quantize_acts need. */
 size_t dq_quantize_workspace_bytes(int64_t rows, int64_t cols, dq_quant_spec spec);

@@ -37,7 +37,9 @@ class dq_quant_spec(C.Structure):
 
 
 class dq_solve_opts(C.Structure):
-    _fields_ = [("iters", C.c_int32), ("tol_relchg", C.c_float)]
+    _fields_ = [("iters", C.c_int32), ("tol_relchg", C.c_float),
+                ("pass_ms", C.POINTER(C.c_float)), ("pass_ms_capacity", C.c_int32),
+                ("pass_ms_count", C.c_int32)]
 
 
 class dq_report(C.Structure):
@@ -219,14 +221,28 @@ def make_problem(W: torch.Tensor, fmt: str, iters: int, group: int | None = None
 
 
 def solve_many(problems, fmt: str, iters: int, group: int | None = None, tol: float = 0.0,
-               stream=None):
+               stream=None, workspace: torch.Tensor | None = None, pass_ms: list | None = None):
+    """Solve a batch of problems.  `workspace` may be passed in to reuse one allocation;
+    when `pass_ms` is a list it receives one (row pass, column pass, finalize) tuple of
+    event-timed durations in ms per sweep over W."""
     spec = spec_of(fmt, group)
-    opts = dq_solve_opts(int(iters), float(tol))
+    opts = dq_solve_opts(int(iters), float(tol), None, 0, 0)
+    buf = None
+    if pass_ms is not None:
+        cap = 2 * int(iters) + 2
+        buf = (C.c_float * (3 * cap))()
+        opts.pass_ms = C.cast(buf, C.POINTER(C.c_float))
+        opts.pass_ms_capacity = cap
     nbytes = dq_workspace_bytes(problems, spec, opts)
     if nbytes == 0:
         raise DQError(-7, "dq_workspace_bytes")
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=problems[0].W.device)
-    return dq_solve(problems, spec, opts, ws, stream)
+    ws = workspace
+    if ws is None or ws.numel() * ws.element_size() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=problems[0].W.device)
+    reps = dq_solve(problems, spec, opts, ws, stream)
+    if pass_ms is not None:
+        pass_ms.extend(tuple(float(buf[3 * k + q]) for q in range(3)) for k in range(opts.pass_ms_count))
+    return reps
 
 
 def solve(W: torch.Tensor, fmt: str, iters: int, group: int | None = None, r_init=None,

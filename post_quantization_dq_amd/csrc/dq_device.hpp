@@ -23,6 +23,18 @@ namespace dqk {
 enum Fmt { INT4 = 0, MXINT4 = 1, MXFP4 = 2, NVFP4 = 3 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Global-memory views of the generic pointers the kernels receive: loads and stores through
+// them compile to global_* instructions, which the wait counters track apart from LDS, so
+// LDS reads do not wait for outstanding HBM loads.
+#define DQ_GAS __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const DQ_GAS T* gp(const T* p) { return (const DQ_GAS T*)p; }
+template <typename T>
+__device__ __forceinline__ DQ_GAS T* gp(T* p) { return (DQ_GAS T*)p; }
 
 __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }

@@ -1,21 +1,22 @@
 // HIP kernels of the DualQuant dual-scale BCD solver for gfx950.
 //
-// One pass over W ("sweep") per BCD iteration.  Sweep s takes the scales (r^s, c^s) and
-//   * quantises the candidate Qc = FQ_f(W ./ r^s c^s^T)       (Qhat-step of iteration s),
-//   * measures F(r^s,c^s,Qc) and the change against the kept Qhat^{s-1} read back from its
-//     stored codes: relchg numerator, and dF = F(Qc) - F(Qhat^{s-1}) accumulated per lane
-//     and row (so unchanged elements contribute exactly 0 to the safeguard decision),
-//   * assuming the candidate is kept, runs the r-step of iteration s+1 (row reduction over
-//     the whole row inside the workgroup) and accumulates the c-step column sums with the
-//     new r (per-lane registers, one partial per row strip).
-// A small finalize kernel then reduces the column partials, projects c, and its last
-// workgroup takes the safeguard decision and advances the per-problem state machine.  If
-// the candidate is rejected the speculative r/c are discarded and the next sweep runs in
-// FIXUP mode (r/c steps from the kept Qhat) before continuing.
-//
-// Layout: workgroup = H row slots x LPR lanes; lane l of a slot owns columns
-// [16l, 16l+16) of its row ("chunk"), so a row of up to 16384 columns is held by one
-// slot and the column accumulators stay in the lane's registers across the strip.
+// Each BCD iteration is three launches over all problems of a batch:
+//   k_rowpass   one wave per row (no workgroup barriers in the row loop); c and 1/c of every
+//               column sit in LDS.  It quantises the candidate Qc = FQ_f(W ./ r^s c^s^T)
+//               (Qhat-step of iteration s) and stores its codes, measures F(r^s,c^s,Qc), the
+//               change against the kept Qhat^{s-1} read back from its codes (relchg numerator,
+//               and dF = F(Qc) - F(Qhat^{s-1}) accumulated per lane, so unchanged elements add
+//               exactly 0 to the safeguard decision), and, assuming the candidate is kept,
+//               runs the r-step of iteration s+1 (whole-row sums, fp64 across lanes).
+//   k_colpass   workgroups own 1024-column strips and a range of rows; with the new r it
+//               accumulates the c-step sums N_j, D_j (and the NVFP4 column amax of W ./ r)
+//               in registers and writes one partial per row range.
+//   k_finalize  reduces the partials, projects c, and its last workgroup takes the
+//               safeguard decision and advances the per-problem state machine.  If the
+//               candidate is rejected the speculative r/c are discarded and the next
+//               iteration re-runs the r/c steps from the kept Qhat (FIXUP mode).
+// Lane l of a wave owns chunks of 16 consecutive columns; blocks of MX (32) and INT4
+// (64/128) formats span 2..8 adjacent lanes.
 
 #pragma once
 #include <type_traits>
@@ -43,8 +44,8 @@ struct ProbDev {
   float* ic[2];
   uint8_t* codes[2];
   void* scales[2];
-  void* colP;       // [strips][NQ][cols] column partials (fp64 for INT4, else fp32)
-  double* swp;      // [strips][4]: F(Qc), dF, relchg numerator, ||Qc||^2
+  void* colP;       // [rranges][NQ][cols] column partials (fp64 for INT4, else fp32)
+  double* swp;      // [rowblocks][4]: F(Qc), dF, relchg numerator, ||Qc||^2
   float* fwp;       // [fin_wgs]: NVFP4 amax partials
   double* initp;    // [init_wgs][2]
   State* st;
@@ -54,10 +55,11 @@ struct ProbDev {
   float* c_trace;   // [iters][cols] or null: unprojected c-step values
   const float* r_init;
   const float* c_init;
-  int32_t strips, rows_per_strip, fin_wgs, iters;
-  int32_t lpr, hslots, init_wgs, dtype;
+  int32_t rowblocks, rows_per_blk, fin_wgs, iters;   // row pass: blocks of rows per workgroup
+  int32_t nstrips, rranges, rows_per_range, init_wgs; // column pass: 1024-column strips x row ranges
+  int32_t dtype;
   float tol;
-  int32_t pad[3];
+  int32_t pad[2];
 };
 
 struct WgEntry {
@@ -70,12 +72,11 @@ constexpr float kTinyTensorScale = 7.888609052210118e-31f;  // 2^-100
 template <int FMT, int L>
 __device__ __forceinline__ void store_chunk(uint8_t* codes, void* scales, int64_t i, int64_t n,
                                             int l, int g, const Chunk& ch) {
-  uint2* cp = (uint2*)(codes + ((i * n) >> 1) + 8 * (int64_t)l);
-  *cp = make_uint2(ch.code[0], ch.code[1]);
+  *gp((u32x2*)(codes + ((i * n) >> 1) + 8 * (int64_t)l)) = u32x2{ch.code[0], ch.code[1]};
   if ((l % L) == 0) {
     int64_t bi = i * (n / g) + l / L;
-    if (Traits<FMT>::SCALE_BYTES == 2) ((uint16_t*)scales)[bi] = (uint16_t)ch.scode;
-    else ((uint8_t*)scales)[bi] = (uint8_t)ch.scode;
+    if (Traits<FMT>::SCALE_BYTES == 2) gp((uint16_t*)scales)[bi] = (uint16_t)ch.scode;
+    else gp((uint8_t*)scales)[bi] = (uint8_t)ch.scode;
   }
 }
 
@@ -83,12 +84,12 @@ template <int FMT, int L>
 __device__ __forceinline__ void load_codes(const uint8_t* codes, const void* scales, int64_t i,
                                            int64_t n, int l, int g, uint32_t& c0, uint32_t& c1,
                                            uint32_t& sc) {
-  uint2 cw = *(const uint2*)(codes + ((i * n) >> 1) + 8 * (int64_t)l);
+  const u32x2 cw = *gp((const u32x2*)(codes + ((i * n) >> 1) + 8 * (int64_t)l));
   c0 = cw.x;
   c1 = cw.y;
   int64_t bi = i * (n / g) + l / L;
-  sc = (Traits<FMT>::SCALE_BYTES == 2) ? (uint32_t)((const uint16_t*)scales)[bi]
-                                       : (uint32_t)((const uint8_t*)scales)[bi];
+  sc = (Traits<FMT>::SCALE_BYTES == 2) ? (uint32_t)gp((const uint16_t*)scales)[bi]
+                                       : (uint32_t)gp((const uint8_t*)scales)[bi];
 }
 
 __device__ __forceinline__ void build_nvtab(NvTab& tab, float s_t) {
@@ -119,14 +120,14 @@ __global__ void k_setup(const ProbDev* __restrict__ probs) {
   if (P.rows == 0 || P.cols == 0) return;   // empty problems have no buffers
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k < P.rows) {
-    float r = P.r_init ? P.r_init[k] : 1.0f;
-    P.r[0][k] = r;
-    P.ir[0][k] = 1.0f / r;
+    float r = P.r_init ? gp(P.r_init)[k] : 1.0f;
+    gp(P.r[0])[k] = r;
+    gp(P.ir[0])[k] = 1.0f / r;
   }
   if (k < P.cols) {
-    float c = P.c_init ? P.c_init[k] : 1.0f;
-    P.c[0][k] = c;
-    P.ic[0][k] = 1.0f / c;
+    float c = P.c_init ? gp(P.c_init)[k] : 1.0f;
+    gp(P.c[0])[k] = c;
+    gp(P.ic[0])[k] = 1.0f / c;
   }
   if (k == 0) {
     State* s = P.st;
@@ -158,14 +159,50 @@ __global__ __launch_bounds__(256) void k_init(const ProbDev* __restrict__ probs)
   double s2 = 0.0;
   float amax = 0.0f;
   bool bad = false;
+  constexpr int VEC = (DT == 1) ? 8 : 4;   // elements per 16-byte load
+  constexpr int U = 4;                      // loads in flight per thread
+  const int64_t nv = n / VEC;
+  const int64_t rowbytes = P.ld * (DT == 1 ? 2 : 4);
+  const DQ_GAS f32x4* ic4 = gp((const f32x4*)P.ic[0]);
   for (int64_t i = r0; i < r1; ++i) {
-    float ir = P.ir[0][i];
-    for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
-      float w = (DT == 1) ? u2f((uint32_t)((const uint16_t*)P.W)[i * P.ld + j] << 16)
-                          : ((const float*)P.W)[i * P.ld + j];
-      bad |= !isfinite(w);
-      s2 += (double)w * (double)w;
-      if (FMT == NVFP4) amax = fmaxf(amax, fabsf((w * ir) * P.ic[0][j]));
+    const float ir = gp(P.ir[0])[i];
+    const DQ_GAS u32x4* rowp = gp((const u32x4*)((const char*)P.W + i * rowbytes));
+    for (int64_t v0 = threadIdx.x; v0 < nv; v0 += (int64_t)blockDim.x * U) {
+      u32x4 u[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int64_t v = v0 + (int64_t)q * blockDim.x;
+        if (v < nv) u[q] = rowp[v];
+        else u[q] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int64_t v = v0 + (int64_t)q * blockDim.x;
+        if (v >= nv) break;
+        float w[VEC];
+        const uint32_t uu[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+        if (DT == 1) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) { w[2 * k] = u2f(uu[k] << 16); w[2 * k + 1] = u2f(uu[k] & 0xFFFF0000u); }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[k] = u2f(uu[k]);
+        }
+        float icv[VEC];
+        if (FMT == NVFP4) {
+#pragma unroll
+          for (int k = 0; k < VEC / 4; ++k) {
+            const f32x4 a = ic4[v * (VEC / 4) + k];
+            icv[4 * k] = a.x; icv[4 * k + 1] = a.y; icv[4 * k + 2] = a.z; icv[4 * k + 3] = a.w;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          bad |= !isfinite(w[k]);
+          s2 += (double)w[k] * (double)w[k];
+          if (FMT == NVFP4) amax = fmaxf(amax, fabsf((w[k] * ir) * icv[k]));
+        }
+      }
     }
   }
   __shared__ double ss[4];
@@ -177,22 +214,31 @@ __global__ __launch_bounds__(256) void k_init(const ProbDev* __restrict__ probs)
   if ((threadIdx.x & 63) == 0) { ss[wv] = s2; sm[wv] = amax; }
   bad = __syncthreads_or(bad);
   if (threadIdx.x == 0) {
-    P.initp[2 * blockIdx.x] = ((ss[0] + ss[1]) + ss[2]) + ss[3];
-    P.initp[2 * blockIdx.x + 1] = (double)fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    gp(P.initp)[2 * blockIdx.x] = ((ss[0] + ss[1]) + ss[2]) + ss[3];
+    gp(P.initp)[2 * blockIdx.x + 1] = (double)fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
     if (bad) atomicOr(&P.st->flags, 1u);
     __threadfence();
     unsigned prev = atomicAdd(&P.st->init_counter, 1u);
     last = (prev == (unsigned)P.init_wgs - 1);
   }
   __syncthreads();
-  if (!last || threadIdx.x != 0) return;
+  if (!last) return;
   __threadfence();
+  // the last workgroup combines the partials: strided per thread, then in fixed order
   double tot = 0.0;
   float A = 0.0f;
-  for (int b = 0; b < P.init_wgs; ++b) {
-    tot += P.initp[2 * b];
-    A = fmaxf(A, (float)P.initp[2 * b + 1]);
+  for (int b = threadIdx.x; b < P.init_wgs; b += blockDim.x) {
+    tot += gp(P.initp)[2 * b];
+    A = fmaxf(A, (float)gp(P.initp)[2 * b + 1]);
   }
+  tot = wave_sum(tot);
+  A = wave_max(A);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { ss[wv] = tot; sm[wv] = A; }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  tot = ((ss[0] + ss[1]) + ss[2]) + ss[3];
+  A = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
   State* s = P.st;
   s->normW2 = tot;
   if (FMT == NVFP4) {
@@ -206,18 +252,15 @@ __global__ __launch_bounds__(256) void k_init(const ProbDev* __restrict__ probs)
   s->init_counter = 0;
 }
 
-// ---------------------------------------------------------------- the sweep
-// K = chunks of 16 columns per lane (chunk index l + k * lpr).  With K == 1 the row's
-// values and grid values stay in registers for the column phase; with K == 2 they are
-// re-derived from the raw row and the codes to keep the register file within budget.
+// ---------------------------------------------------------------- raw rows
 template <int DT>
 struct RawRow;
 template <>
 struct RawRow<1> {   // bf16: 8 packed words per chunk
   uint32_t u[8];
   __device__ __forceinline__ void load(const void* base, int64_t i, int64_t ld, int j0) {
-    const uint4* p = (const uint4*)((const uint16_t*)base + i * ld + j0);
-    uint4 a = p[0], b = p[1];
+    const DQ_GAS u32x4* p = gp((const u32x4*)((const uint16_t*)base + i * ld + j0));
+    const u32x4 a = p[0], b = p[1];
     u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w; u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
   }
   __device__ __forceinline__ void zero() {
@@ -233,10 +276,10 @@ template <>
 struct RawRow<0> {   // fp32: 16 floats per chunk
   float f[16];
   __device__ __forceinline__ void load(const void* base, int64_t i, int64_t ld, int j0) {
-    const float4* p = (const float4*)((const float*)base + i * ld + j0);
+    const DQ_GAS f32x4* p = gp((const f32x4*)((const float*)base + i * ld + j0));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float4 a = p[k];
+      const f32x4 a = p[k];
       f[4 * k] = a.x; f[4 * k + 1] = a.y; f[4 * k + 2] = a.z; f[4 * k + 3] = a.w;
     }
   }
@@ -250,126 +293,134 @@ struct RawRow<0> {   // fp32: 16 floats per chunk
   }
 };
 
-template <int FMT, int DT, int L, int K>
-__global__ __launch_bounds__(512) void k_sweep(const ProbDev* __restrict__ probs,
-                                               const WgEntry* __restrict__ table) {
+__device__ __forceinline__ void lds_load16(const float* base, float (&x)[16]) {
+  const float4* p = (const float4*)base;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float4 a = p[k];
+    x[4 * k] = a.x; x[4 * k + 1] = a.y; x[4 * k + 2] = a.z; x[4 * k + 3] = a.w;
+  }
+}
+
+// Which iteration a pass belongs to, read from the problem's state at kernel entry.
+struct PassInfo {
+  int mode, it, rs, cs, acc, cb, tr;
+  bool cand, stats, next;
+  __device__ __forceinline__ PassInfo(const State* st, int iters) {
+    mode = st->mode;
+    it = (mode == MODE_INIT) ? 0 : st->it_done + 1;
+    cand = (mode != MODE_FIXUP);
+    stats = (mode == MODE_NORMAL);
+    next = (mode == MODE_FIXUP) || (it < iters);
+    rs = st->rs;
+    cs = st->cs;
+    acc = st->acc;
+    cb = (mode == MODE_INIT) ? 0 : 1 - acc;      // buffer the candidate is written to
+    tr = (mode == MODE_FIXUP) ? it - 1 : it;     // trace row of the r/c steps computed now
+  }
+};
+
+// ---------------------------------------------------------------- row pass
+template <int FMT, int DT, int L>
+__global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ probs,
+                                                  const WgEntry* __restrict__ table) {
   const WgEntry we = table[blockIdx.x];
   const ProbDev& P = probs[we.prob];
   State* st = P.st;
-  const int mode = st->mode;
-  if (mode == MODE_DONE) return;
-  const int it = (mode == MODE_INIT) ? 0 : st->it_done + 1;
-  const bool cand = (mode != MODE_FIXUP);
-  const bool stats = (mode == MODE_NORMAL);
-  const bool next = (mode == MODE_FIXUP) || (it < P.iters);
-  const int rs = st->rs, cs = st->cs, acc = st->acc;
-  const int cb = (mode == MODE_INIT) ? 0 : 1 - acc;
+  if (st->mode == MODE_DONE) return;
+  const PassInfo pi(st, P.iters);
+  constexpr bool A64 = (FMT == INT4);   // INT4: exact products accumulated in fp64
   const int g = L * 16;
-  constexpr bool HOLD = (K == 1);
-  // INT4 (fine bf16 scale grid) accumulates exact products in fp64 so that its projected
-  // scales agree with an fp64 reference essentially always; the other formats use fp32
-  // partials per lane and row strip with fp64 combines.
-  constexpr bool A64 = (FMT == INT4);
-  typedef typename std::conditional<A64, double, float>::type acc_t;
-  constexpr int NQ = (FMT == NVFP4) ? 3 : 2;
-  const int tr = (mode == MODE_FIXUP) ? it - 1 : it;   // trace row of the r-step computed here
-
-  __shared__ NvTab tab_c, tab_p;
-  __shared__ double red[2][8][2];
-  __shared__ double redw[8][4];
-  extern __shared__ float xs[];
-
-  if (FMT == NVFP4) {
-    build_nvtab(tab_c, st->st_cur);
-    build_nvtab(tab_p, st->st_acc);
-    __syncthreads();
-  }
-
-  const int t = threadIdx.x, lpr = P.lpr, H = P.hslots;
-  const int h = t / lpr, l = t - h * lpr;
   const int64_t n = P.cols;
   const int nch = (int)(n >> 4);
-  const int wave = t >> 6, wps = lpr >> 6;
 
-  float cc[K][16], icc[K][16];
-  acc_t colN[K][16], colD[K][16];
-  float colM[K][16];
-#pragma unroll
-  for (int kc = 0; kc < K; ++kc) {
-    const int ch = l + kc * lpr;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      cc[kc][k] = 0.0f; icc[kc][k] = 0.0f;
-      colN[kc][k] = (acc_t)0; colD[kc][k] = (acc_t)0; colM[kc][k] = 0.0f;
-    }
-    if (ch < nch) {
-      const float4* cp = (const float4*)(P.c[cs] + 16 * ch);
-      const float4* icp = (const float4*)(P.ic[cs] + 16 * ch);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float4 a = cp[k], b = icp[k];
-        cc[kc][4 * k] = a.x; cc[kc][4 * k + 1] = a.y; cc[kc][4 * k + 2] = a.z; cc[kc][4 * k + 3] = a.w;
-        icc[kc][4 * k] = b.x; icc[kc][4 * k + 1] = b.y; icc[kc][4 * k + 2] = b.z; icc[kc][4 * k + 3] = b.w;
-      }
+  extern __shared__ float lds[];
+  float* s_c = lds;
+  float* s_ic = lds + n;
+  NvTab* tab_c = (NvTab*)(lds + 2 * n);
+  NvTab* tab_p = tab_c + 1;
+  __shared__ double redw[16][4];
+
+  {
+    const DQ_GAS f32x4* c4 = gp((const f32x4*)P.c[pi.cs]);
+    const DQ_GAS f32x4* ic4 = gp((const f32x4*)P.ic[pi.cs]);
+    f32x4* sc4 = (f32x4*)s_c;
+    f32x4* sic4 = (f32x4*)s_ic;
+    for (int k = threadIdx.x; k < (int)(n >> 2); k += blockDim.x) { sc4[k] = c4[k]; sic4[k] = ic4[k]; }
+    if (FMT == NVFP4) {
+      build_nvtab(*tab_c, st->st_cur);
+      build_nvtab(*tab_p, st->st_acc);
     }
   }
-  double aFc = 0.0, adF = 0.0, arel = 0.0, aqn = 0.0;
-  bool uflow = false, zrow = false;
+  __syncthreads();
 
-  const int64_t row0 = (int64_t)we.idx * P.rows_per_strip;
-  const int64_t row1 = min(P.rows, row0 + P.rows_per_strip);
-  const float* rcur = P.r[rs];
-  const float* ircur = P.ir[rs];
-  float* rnext = P.r[1 - rs];
-  float* irnext = P.ir[1 - rs];
-  uint8_t* ccodes = P.codes[cb];
-  void* cscales = P.scales[cb];
-  const uint8_t* acodes = P.codes[acc];
-  const void* ascales = P.scales[acc];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, nw = (int)(blockDim.x >> 6);
+  const DQ_GAS float* rcur = gp(P.r[pi.rs]);
+  const DQ_GAS float* ircur = gp(P.ir[pi.rs]);
+  DQ_GAS float* rnext = gp(P.r[1 - pi.rs]);
+  DQ_GAS float* irnext = gp(P.ir[1 - pi.rs]);
+  uint8_t* ccodes = P.codes[pi.cb];
+  void* cscales = P.scales[pi.cb];
+  const uint8_t* acodes = P.codes[pi.acc];
+  const void* ascales = P.scales[pi.acc];
   QCtx qc;
   qc.k6 = st->k6_cur;
-  qc.tab = &tab_c;
-  const int ngroups = (P.rows_per_strip + H - 1) / H;
+  qc.tab = tab_c;
 
-  for (int gi = 0; gi < ngroups; ++gi) {
-    const int64_t i = row0 + (int64_t)gi * H + h;
-    const bool rowok = i < row1;
-    const float r_ = rowok ? rcur[i] : 1.0f;
-    const float ir_ = rowok ? ircur[i] : 1.0f;
+  double aFc = 0.0, adF = 0.0, arel = 0.0, aqn = 0.0;
+  bool uflow = false, zrow = false;
+  const int64_t row0 = (int64_t)we.idx * P.rows_per_blk;
+  const int64_t row1 = min(P.rows, row0 + P.rows_per_blk);
+  const int nloop = (nch + 63) >> 6;
+
+  for (int64_t i = row0 + wave; i < row1; i += nw) {
+    const float r_ = rcur[i];
+    const float ir_ = ircur[i];
     double Nrow = 0.0, Drow = 0.0;
-    RawRow<DT> raw[K];
-    uint32_t kc0[K], kc1[K];
-    float kf[K];
-    float wh[HOLD ? K : 1][16], ph[HOLD ? K : 1][16];
-#pragma unroll
-    for (int kc = 0; kc < K; ++kc) {
-      const int chn = l + kc * lpr;
-      const bool valid = rowok && (chn < nch);
+    for (int kk = 0; kk < nloop; ++kk) {
+      const int chn = lane + 64 * kk;
+      const bool valid = chn < nch;
       const int j0 = 16 * chn;
-      if (valid) raw[kc].load(P.W, i, P.ld, j0); else raw[kc].zero();
+      RawRow<DT> raw;
+      if (valid) raw.load(P.W, i, P.ld, j0); else raw.zero();
+      uint32_t p0 = 0, p1 = 0, ps = 0;
+      if (valid && !(pi.mode == MODE_INIT)) load_codes<FMT, L>(acodes, ascales, i, n, chn, g, p0, p1, ps);
       float w[16];
-      raw[kc].unpack(w);
+      raw.unpack(w);
       float p[16];
       float f;
       float Nb = 0.0f, Db = 0.0f;
       double Nbd = 0.0, Dbd = 0.0;
-      if (cand) {
+      float cc[16];
+      if (pi.cand) {
         float v[16];
+        {
+          float icc[16];
+          if (valid) lds_load16(s_ic + j0, icc);
+          else {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = (w[k] * ir_) * icc[kc][k];
+            for (int k = 0; k < 16; ++k) icc[k] = 0.0f;
+          }
+#pragma unroll
+          for (int k = 0; k < 16; ++k) v[k] = (w[k] * ir_) * icc[k];
+        }
         Chunk ch;
         quantize_chunk<FMT, L>(v, qc, ch);
         if (valid) store_chunk<FMT, L>(ccodes, cscales, i, n, chn, g, ch);
         uflow |= ch.underflow && valid;
         f = ch.f;
-        kc0[kc] = ch.code[0];
-        kc1[kc] = ch.code[1];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) p[k] = ch.p[k];
+        if (valid) lds_load16(s_c + j0, cc);
+        else {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) cc[k] = 0.0f;
+        }
         const float rf = r_ * f;
         float Fl = 0.0f, ql = 0.0f;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          p[k] = ch.p[k];
-          const float pc = p[k] * cc[kc][k];
+          const float pc = p[k] * cc[k];
           const float e = fmaf(-rf, pc, w[k]);
           Fl = fmaf(e, e, Fl);
           if (A64) {
@@ -382,16 +433,14 @@ __global__ __launch_bounds__(512) void k_sweep(const ProbDev* __restrict__ probs
           ql = fmaf(p[k], p[k], ql);
         }
         float Fpl = 0.0f, rl = 0.0f;
-        if (stats) {
-          uint32_t p0 = 0, p1 = 0, ps = 0;
-          if (valid) load_codes<FMT, L>(acodes, ascales, i, n, chn, g, p0, p1, ps);
+        if (pi.stats) {
           float pp[16];
           decode_grid<FMT>(p0, p1, pp);
-          const float fp = block_factor<FMT>(ps, &tab_p);
+          const float fp = block_factor<FMT>(ps, tab_p);
           const float rfp = r_ * fp;
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
-            const float ppc = pp[k] * cc[kc][k];
+            const float ppc = pp[k] * cc[k];
             const float ep = fmaf(-rfp, ppc, w[k]);
             Fpl = fmaf(ep, ep, Fpl);
             const float df = fmaf(p[k], f, -(pp[k] * fp));
@@ -405,15 +454,16 @@ __global__ __launch_bounds__(512) void k_sweep(const ProbDev* __restrict__ probs
           aqn += (double)(f * f) * (double)ql;
         }
       } else {
-        uint32_t p0 = 0, p1 = 0, ps = 0;
-        if (valid) load_codes<FMT, L>(acodes, ascales, i, n, chn, g, p0, p1, ps);
         decode_grid<FMT>(p0, p1, p);
-        f = block_factor<FMT>(ps, &tab_p);
-        kc0[kc] = p0;
-        kc1[kc] = p1;
+        f = block_factor<FMT>(ps, tab_p);
+        if (valid) lds_load16(s_c + j0, cc);
+        else {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) cc[k] = 0.0f;
+        }
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          const float pc = p[k] * cc[kc][k];
+          const float pc = p[k] * cc[k];
           if (A64) {
             Nbd = fma((double)w[k], (double)pc, Nbd);
             Dbd = fma((double)pc, (double)pc, Dbd);
@@ -423,7 +473,6 @@ __global__ __launch_bounds__(512) void k_sweep(const ProbDev* __restrict__ probs
           }
         }
       }
-      kf[kc] = f;
       if (valid) {
         if (A64) {
           Nrow += (double)f * Nbd;
@@ -433,24 +482,12 @@ __global__ __launch_bounds__(512) void k_sweep(const ProbDev* __restrict__ probs
           Drow += (double)(f * f) * (double)Db;
         }
       }
-      if (HOLD) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) { wh[HOLD ? kc : 0][k] = w[k]; ph[HOLD ? kc : 0][k] = p[k]; }
-      }
     }
-    if (next) {
-      // r-step of the next iteration: whole-row sums, fp64 across lanes and waves
-      const double Nd = wave_sum(Nrow), Dd = wave_sum(Drow);
-      if ((t & 63) == 0) { red[gi & 1][wave][0] = Nd; red[gi & 1][wave][1] = Dd; }
-      __syncthreads();
-      double N = 0.0, D = 0.0;
-      for (int k = 0; k < wps; ++k) {
-        N += red[gi & 1][h * wps + k][0];
-        D += red[gi & 1][h * wps + k][1];
-      }
-      float rnew = 1.0f, irn = 1.0f;
-      if (rowok) {
-        float x = __builtin_nanf("");
+    if (pi.next) {
+      // r-step of the next iteration from the whole row (fixed butterfly order in fp64)
+      const double N = wave_sum(Nrow), D = wave_sum(Drow);
+      if (lane == 0) {
+        float x = __builtin_nanf(""), rnew;
         if (D > 0.0) {
           x = (float)(N / D);
           rnew = project<FMT>(x);
@@ -458,103 +495,165 @@ __global__ __launch_bounds__(512) void k_sweep(const ProbDev* __restrict__ probs
           rnew = r_;
           zrow = true;
         }
-        irn = 1.0f / rnew;
-        if (l == 0) {
-          rnext[i] = rnew;
-          irnext[i] = irn;
-          if (P.r_trace) P.r_trace[(int64_t)tr * P.rows + i] = x;
-        }
-      }
-#pragma unroll
-      for (int kc = 0; kc < K; ++kc) {
-        const int chn = l + kc * lpr;
-        if (!(rowok && chn < nch)) continue;
-        float w[16], p[16];
-        if (HOLD) {
-#pragma unroll
-          for (int k = 0; k < 16; ++k) { w[k] = wh[HOLD ? kc : 0][k]; p[k] = ph[HOLD ? kc : 0][k]; }
-        } else {
-          raw[kc].unpack(w);
-          decode_grid<FMT>(kc0[kc], kc1[kc], p);
-        }
-        const float rf = rnew * kf[kc];
-        const float rf2 = rf * rf;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          if (A64) {   // INT4: rf = r * s and rf * p are exact in fp32; the products below are exact in fp64
-            colN[kc][k] = fma((double)rf, (double)w[k] * (double)p[k], (double)colN[kc][k]);
-            const double rp = (double)(rf * p[k]);
-            colD[kc][k] = fma(rp, rp, (double)colD[kc][k]);
-          } else {
-            colN[kc][k] = fmaf(rf, w[k] * p[k], (float)colN[kc][k]);
-            colD[kc][k] = fmaf(rf2, p[k] * p[k], (float)colD[kc][k]);
-          }
-          if (FMT == NVFP4) colM[kc][k] = fmaxf(colM[kc][k], fabsf(w[k] * irn));
-        }
+        rnext[i] = rnew;
+        irnext[i] = 1.0f / rnew;
+        if (P.r_trace) gp(P.r_trace)[(int64_t)pi.tr * P.rows + i] = x;
       }
     }
   }
 
-  if (next) {
-    // combine the row slots' column partials (fixed slot order), then write this strip's
-    if (H > 1) {
-      acc_t* xa = (acc_t*)xs;
-      for (int qi = 0; qi < NQ; ++qi) {
-        __syncthreads();
-        if (h >= 1 && l < nch) {
-#pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const acc_t v = (qi == 0) ? colN[0][k] : (qi == 1) ? colD[0][k] : (acc_t)colM[0][k];
-            xa[(k * (H - 1) + (h - 1)) * lpr + l] = v;
-          }
-        }
-        __syncthreads();
-        if (h == 0 && l < nch) {
-          for (int hh = 1; hh < H; ++hh) {
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-              const acc_t o = xa[(k * (H - 1) + (hh - 1)) * lpr + l];
-              if (qi == 0) colN[0][k] += o;
-              else if (qi == 1) colD[0][k] += o;
-              else colM[0][k] = fmaxf(colM[0][k], (float)o);
-            }
-          }
-        }
-      }
-    }
-    if (h == 0) {
-#pragma unroll
-      for (int kc = 0; kc < K; ++kc) {
-        const int chn = l + kc * lpr;
-        if (chn >= nch) continue;
-        acc_t* base = (acc_t*)P.colP + (size_t)we.idx * NQ * (size_t)n + 16 * chn;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          base[k] = colN[kc][k];
-          base[n + k] = colD[kc][k];
-          if (FMT == NVFP4) base[2 * n + k] = (acc_t)colM[kc][k];
-        }
-      }
-    }
-  }
-
-  if (cand) {
+  if (pi.cand) {
     const double a0 = wave_sum(aFc), a1 = wave_sum(adF), a2 = wave_sum(arel), a3 = wave_sum(aqn);
-    if ((t & 63) == 0) { redw[wave][0] = a0; redw[wave][1] = a1; redw[wave][2] = a2; redw[wave][3] = a3; }
+    if (lane == 0) { redw[wave][0] = a0; redw[wave][1] = a1; redw[wave][2] = a2; redw[wave][3] = a3; }
   }
   const bool anyu = __syncthreads_or(uflow);
   const bool anyz = __syncthreads_or(zrow);
   if (t == 0) {
-    if (cand) {
+    if (pi.cand) {
       double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-      const int nw = (int)(blockDim.x >> 6);
       for (int k = 0; k < nw; ++k) { s0 += redw[k][0]; s1 += redw[k][1]; s2 += redw[k][2]; s3 += redw[k][3]; }
-      double* o = P.swp + 4 * (size_t)we.idx;
+      DQ_GAS double* o = gp(P.swp + 4 * (size_t)we.idx);
       o[0] = s0; o[1] = s1; o[2] = s2; o[3] = s3;
     }
     const uint32_t fl = (anyu ? 8u : 0u) | (anyz ? 2u : 0u);
     if (fl) atomicOr(&st->flags, fl);
   }
+}
+
+// ---------------------------------------------------------------- column pass
+// Workgroup = 8 waves on one strip of 64 chunks (1024 columns) and one range of rows; wave
+// w takes rows w, w+8, ... of the range.  The waves' accumulators are combined in LDS in
+// fixed wave order and written as this range's partial.  fp32 accumulation keeps a wave
+// within 128 VGPRs (two workgroups per CU); INT4's fp64 accumulators need the wider budget.
+template <int FMT, int DT, int L>
+__device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
+                                             const WgEntry* __restrict__ table) {
+  const WgEntry we = table[blockIdx.x];
+  const ProbDev& P = probs[we.prob];
+  State* st = P.st;
+  if (st->mode == MODE_DONE) return;
+  const PassInfo pi(st, P.iters);
+  if (!pi.next) return;
+  constexpr bool A64 = (FMT == INT4);
+  typedef typename std::conditional<A64, double, float>::type acc_t;
+  constexpr int NQ = (FMT == NVFP4) ? 3 : 2;
+  const int g = L * 16;
+  const int64_t n = P.cols;
+  const int nch = (int)(n >> 4);
+  const int strip = we.idx % P.nstrips, rr = we.idx / P.nstrips;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int chn = strip * 64 + lane;
+  const bool act = chn < nch;
+  const int j0 = 16 * chn;
+  // the Qhat these sums use: the candidate just written (kept speculatively), or the kept one
+  const int qb = (pi.mode == MODE_FIXUP) ? pi.acc : pi.cb;
+  const uint8_t* qcodes = P.codes[qb];
+  const void* qscales = P.scales[qb];
+  const DQ_GAS float* rnew = gp(P.r[1 - pi.rs]);
+  const DQ_GAS float* irnew = gp(P.ir[1 - pi.rs]);
+  __shared__ NvTab tab;
+  if (FMT == NVFP4) {
+    build_nvtab(tab, (pi.mode == MODE_FIXUP) ? st->st_acc : st->st_cur);
+    __syncthreads();
+  }
+
+  acc_t cN[16], cD[16];
+  float cM[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) { cN[k] = (acc_t)0; cD[k] = (acc_t)0; cM[k] = 0.0f; }
+  const int64_t row0 = (int64_t)rr * P.rows_per_range;
+  const int64_t row1 = min(P.rows, row0 + P.rows_per_range);
+  constexpr int U = A64 ? 1 : 2;   // rows in flight per wave
+  if (act) {
+    for (int64_t i0 = row0 + wave; i0 < row1; i0 += 8 * U) {
+      RawRow<DT> raw[U];
+      uint32_t c0[U], c1[U], sc[U];
+      float rr_[U], irn[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + 8 * u;
+        if (i < row1) {
+          raw[u].load(P.W, i, P.ld, j0);
+          load_codes<FMT, L>(qcodes, qscales, i, n, chn, g, c0[u], c1[u], sc[u]);
+          rr_[u] = rnew[i];
+          irn[u] = (FMT == NVFP4) ? irnew[i] : 0.0f;
+        } else {
+          raw[u].zero();
+          c0[u] = c1[u] = sc[u] = 0u;
+          rr_[u] = 0.0f;
+          irn[u] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (i0 + 8 * u >= row1) break;
+        float w[16], p[16];
+        raw[u].unpack(w);
+        decode_grid<FMT>(c0[u], c1[u], p);
+        const float f = block_factor<FMT>(sc[u], &tab);
+        const float rf = rr_[u] * f;
+        const float rf2 = rf * rf;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          if (A64) {   // INT4: rf = r * s and rf * p are exact in fp32; products exact in fp64
+            cN[k] = fma((double)rf, (double)w[k] * (double)p[k], (double)cN[k]);
+            const double rp = (double)(rf * p[k]);
+            cD[k] = fma(rp, rp, (double)cD[k]);
+          } else {
+            cN[k] = fmaf(rf, w[k] * p[k], (float)cN[k]);
+            cD[k] = fmaf(rf2, p[k] * p[k], (float)cD[k]);
+          }
+          if (FMT == NVFP4) cM[k] = fmaxf(cM[k], fabsf(w[k] * irn[u]));
+        }
+      }
+    }
+  }
+  // combine the 8 waves in fixed order
+  extern __shared__ float xs[];
+  acc_t* xa = (acc_t*)xs;
+  for (int qi = 0; qi < NQ; ++qi) {
+    __syncthreads();
+    if (wave >= 1) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const acc_t v = (qi == 0) ? cN[k] : (qi == 1) ? cD[k] : (acc_t)cM[k];
+        xa[(k * 7 + (wave - 1)) * 64 + lane] = v;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int ww = 1; ww < 8; ++ww) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const acc_t o = xa[(k * 7 + (ww - 1)) * 64 + lane];
+          if (qi == 0) cN[k] += o;
+          else if (qi == 1) cD[k] += o;
+          else cM[k] = fmaxf(cM[k], (float)o);
+        }
+      }
+    }
+  }
+  if (wave == 0 && act) {
+    DQ_GAS acc_t* base = gp((acc_t*)P.colP + (size_t)rr * NQ * (size_t)n + j0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      base[k] = cN[k];
+      base[n + k] = cD[k];
+      if (FMT == NVFP4) base[2 * n + k] = (acc_t)cM[k];
+    }
+  }
+}
+
+template <int FMT, int DT, int L>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_colpass(
+    const ProbDev* __restrict__ probs, const WgEntry* __restrict__ table) {
+  colpass_body<FMT, DT, L>(probs, table);
+}
+
+template <int FMT, int DT, int L>
+__global__ __launch_bounds__(512) void k_colpass_wide(const ProbDev* __restrict__ probs,
+                                                      const WgEntry* __restrict__ table) {
+  colpass_body<FMT, DT, L>(probs, table);
 }
 
 // ---------------------------------------------------------------- finalize
@@ -573,8 +672,6 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   const int cs = st->cs;
   const int64_t n = P.cols;
 
-  __shared__ double sN[4][64], sD[4][64];
-  __shared__ float sM[4][64];
   __shared__ float wmax[4];
   __shared__ double sred[256][4];
   __shared__ int last;
@@ -582,44 +679,47 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   const int t = threadIdx.x;
   bool zcol = false;
   if (next) {
-    const int part = t >> 6, cl = t & 63;
-    const int64_t j = (int64_t)we.idx * 64 + cl;
-    double N = 0.0, D = 0.0;
-    float M = 0.0f;
-    if (j < n) {
-      const int S = P.strips;
-      const int s0 = part * S / 4, s1 = (part + 1) * S / 4;
-      constexpr int NQ = (FMT == NVFP4) ? 3 : 2;
-      typedef typename std::conditional<FMT == INT4, double, float>::type acc_t;
-      for (int s = s0; s < s1; ++s) {
-        const acc_t* b = (const acc_t*)P.colP + (size_t)s * NQ * (size_t)n;
-        N += (double)b[j];
-        D += (double)b[n + j];
-        if (FMT == NVFP4) M = fmaxf(M, (float)b[2 * n + j]);
-      }
-    }
-    sN[part][cl] = N;
-    sD[part][cl] = D;
-    sM[part][cl] = M;
-    __syncthreads();
+    constexpr int NQ = (FMT == NVFP4) ? 3 : 2;
+    typedef typename std::conditional<FMT == INT4, double, float>::type acc_t;
+    const int64_t j = (int64_t)we.idx * 256 + t;
     float am = 0.0f;
-    if (part == 0 && j < n) {
-      N = ((sN[0][cl] + sN[1][cl]) + sN[2][cl]) + sN[3][cl];
-      D = ((sD[0][cl] + sD[1][cl]) + sD[2][cl]) + sD[3][cl];
-      M = fmaxf(fmaxf(sM[0][cl], sM[1][cl]), fmaxf(sM[2][cl], sM[3][cl]));
+    if (j < n) {
+      // sum the row-range partials in range order, eight loads in flight at a time
+      double N = 0.0, D = 0.0;
+      float M = 0.0f;
+      const int S = P.rranges;
+      const DQ_GAS acc_t* b = gp((const acc_t*)P.colP + j);
+      const size_t stride = (size_t)NQ * (size_t)n;
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        acc_t vn[8], vd[8], vm[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bool ok = s0 + u < S;
+          const DQ_GAS acc_t* q = b + (size_t)(s0 + u) * stride;
+          vn[u] = ok ? q[0] : (acc_t)0;
+          vd[u] = ok ? q[n] : (acc_t)0;
+          vm[u] = (ok && FMT == NVFP4) ? q[2 * n] : (acc_t)0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          N += (double)vn[u];
+          D += (double)vd[u];
+          if (FMT == NVFP4) M = fmaxf(M, (float)vm[u]);
+        }
+      }
       float x = __builtin_nanf("");
       float cnew;
       if (D > 0.0) {
         x = (float)(N / D);
         cnew = project<FMT>(x);
       } else {
-        cnew = P.c[cs][j];
+        cnew = gp(P.c[cs])[j];
         zcol = true;
       }
       const float icn = 1.0f / cnew;
-      P.c[1 - cs][j] = cnew;
-      P.ic[1 - cs][j] = icn;
-      if (P.c_trace) P.c_trace[(int64_t)((mode == MODE_FIXUP) ? it - 1 : it) * n + j] = x;
+      gp(P.c[1 - cs])[j] = cnew;
+      gp(P.ic[1 - cs])[j] = icn;
+      if (P.c_trace) gp(P.c_trace)[(int64_t)((mode == MODE_FIXUP) ? it - 1 : it) * n + j] = x;
       if (FMT == NVFP4) am = M * icn;
     }
     if (FMT == NVFP4) {
@@ -629,7 +729,7 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   }
   zcol = __syncthreads_or(zcol);
   if (t == 0) {
-    if (next && FMT == NVFP4) P.fwp[we.idx] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (next && FMT == NVFP4) gp(P.fwp)[we.idx] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     if (zcol) atomicOr(&st->flags, 4u);
     __threadfence();
     unsigned prev = atomicAdd(&st->counter, 1u);
@@ -642,14 +742,14 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   // fixed-order reductions of the sweep's strip partials and the amax partials
   double f0 = 0.0, f1 = 0.0, f2 = 0.0, f3 = 0.0;
   if (mode != MODE_FIXUP) {
-    for (int s = t; s < P.strips; s += 256) {
-      const double* o = P.swp + 4 * (size_t)s;
+    for (int s = t; s < P.rowblocks; s += 256) {
+      const DQ_GAS double* o = gp(P.swp + 4 * (size_t)s);
       f0 += o[0]; f1 += o[1]; f2 += o[2]; f3 += o[3];
     }
   }
   float A = 0.0f;
   if (next && FMT == NVFP4) {
-    for (int k = t; k < P.fin_wgs; k += 256) A = fmaxf(A, P.fwp[k]);
+    for (int k = t; k < P.fin_wgs; k += 256) A = fmaxf(A, gp(P.fwp)[k]);
   }
   sred[t][0] = f0; sred[t][1] = f1; sred[t][2] = f2; sred[t][3] = f3;
   A = wave_max(A);
@@ -717,28 +817,71 @@ __global__ __launch_bounds__(256) void k_qamax(const void* __restrict__ X, int64
                                                const float* __restrict__ r,
                                                const float* __restrict__ c,
                                                float* __restrict__ part) {
+  constexpr int VEC = (DT == 1) ? 8 : 4;   // elements per 16-byte load
+  constexpr int U = 4;                      // loads in flight per thread
+  const int64_t rpb = (rows + gridDim.x - 1) / gridDim.x;
+  const int64_t r0 = (int64_t)blockIdx.x * rpb, r1 = min(rows, r0 + rpb);
+  const int64_t nv = cols / VEC;
+  const int64_t rowbytes = ld * (DT == 1 ? 2 : 4);
   float m = 0.0f;
-  const int64_t total = rows * cols;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t i = e / cols, j = e - i * cols;
-    float x = (DT == 1) ? u2f((uint32_t)((const uint16_t*)X)[i * ld + j] << 16)
-                        : ((const float*)X)[i * ld + j];
-    float v;
-    if (MODEV == 0) {
-      const float ir = r ? 1.0f / r[i] : 1.0f;
-      const float ic = c ? 1.0f / c[j] : 1.0f;
-      v = (x * ir) * ic;
-    } else {
-      v = c ? x * c[j] : x;
+  for (int64_t i = r0; i < r1; ++i) {
+    const float ir = (MODEV == 0 && r) ? 1.0f / gp(r)[i] : 1.0f;
+    const DQ_GAS u32x4* rowp = gp((const u32x4*)((const char*)X + i * rowbytes));
+    for (int64_t v0 = threadIdx.x; v0 < nv; v0 += (int64_t)blockDim.x * U) {
+      u32x4 u[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int64_t v = v0 + (int64_t)q * blockDim.x;
+        if (v < nv) u[q] = rowp[v];
+        else u[q] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int64_t v = v0 + (int64_t)q * blockDim.x;
+        if (v >= nv) break;
+        float w[VEC];
+        const uint32_t uu[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+        if (DT == 1) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) { w[2 * k] = u2f(uu[k] << 16); w[2 * k + 1] = u2f(uu[k] & 0xFFFF0000u); }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[k] = u2f(uu[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          float val = w[k];
+          if (MODEV == 0) {
+            const float ic = c ? 1.0f / gp(c)[v * VEC + k] : 1.0f;
+            val = (val * ir) * ic;
+          } else if (c) {
+            val = val * gp(c)[v * VEC + k];
+          }
+          m = fmaxf(m, fabsf(val));
+        }
+      }
     }
-    m = fmaxf(m, fabsf(v));
   }
   m = wave_max(m);
   __shared__ float sm[4];
   if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  if (threadIdx.x == 0) gp(part)[blockIdx.x] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+}
+
+// 16 consecutive floats (vector loads when the base is 16-byte aligned).
+__device__ __forceinline__ void load16_global(const float* p, bool aligned, float (&x)[16]) {
+  if (aligned) {
+    const DQ_GAS f32x4* q = gp((const f32x4*)p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 a = q[k];
+      x[4 * k] = a.x; x[4 * k + 1] = a.y; x[4 * k + 2] = a.z; x[4 * k + 3] = a.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = gp(p)[k];
+  }
 }
 
 // Pass 2: quantise; workgroup = H row slots x LPR lanes, one chunk per lane.
@@ -756,9 +899,15 @@ __global__ __launch_bounds__(1024) void k_quant(const void* __restrict__ X, int6
   qc.k6 = 0.0f;
   qc.tab = &tab;
   if (FMT == NVFP4) {
+    __shared__ float smax[16];
+    float a = 0.0f;
+    for (int k = threadIdx.x; k < nparts; k += blockDim.x) a = fmaxf(a, gp(part)[k]);
+    a = wave_max(a);
+    if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = a;
+    __syncthreads();
     if (threadIdx.x == 0) {
       float A = 0.0f;
-      for (int k = 0; k < nparts; ++k) A = fmaxf(A, part[k]);
+      for (int k = 0; k < (int)(blockDim.x >> 6); ++k) A = fmaxf(A, smax[k]);
       sA = A;
     }
     __syncthreads();
@@ -767,7 +916,7 @@ __global__ __launch_bounds__(1024) void k_quant(const void* __restrict__ X, int6
     nv_tensor_terms(sA, s_t, k6, tiny);
     qc.k6 = k6;
     build_nvtab(tab, s_t);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gp(tensor_scale) = s_t;
     __syncthreads();
   }
   const int t = threadIdx.x;
@@ -779,16 +928,23 @@ __global__ __launch_bounds__(1024) void k_quant(const void* __restrict__ X, int6
   RawRow<DT> raw;
   if (act) raw.load(X, i, ld, j0); else raw.zero();
   raw.unpack(w);
+  float cv[16];
+  if (act && c) {
+    load16_global(c + j0, ((uintptr_t)c & 15u) == 0, cv);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) cv[k] = 1.0f;
+  }
   if (MODEV == 0) {
-    const float ir = (act && r) ? 1.0f / r[i] : 1.0f;
+    const float ir = (act && r) ? 1.0f / gp(r)[i] : 1.0f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const float ic = (act && c) ? 1.0f / c[j0 + k] : 1.0f;
+      const float ic = c ? 1.0f / cv[k] : 1.0f;
       v[k] = (w[k] * ir) * ic;
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = (act && c) ? w[k] * c[j0 + k] : w[k];
+    for (int k = 0; k < 16; ++k) v[k] = c ? w[k] * cv[k] : w[k];
   }
   Chunk ch;
   quantize_chunk<FMT, L>(v, qc, ch);

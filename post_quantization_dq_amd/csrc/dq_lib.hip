@@ -2,6 +2,7 @@
 // workspace layout, launch planning and the iteration driver.  See include/dq.h for the
 // contract of every entry point.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -17,7 +18,6 @@ using namespace dqk;
 namespace {
 
 constexpr int kMaxCols = 16384;
-constexpr int kTargetWgs = 256;   // one row strip per CU for a single large matrix
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -42,7 +42,7 @@ int resolve_group(const dq_quant_spec& s) {
 }
 
 int scale_bytes(int fmt) { return fmt == DQ_FMT_INT4 ? 2 : 1; }
-// Column partials per row strip: N, D (and the NVFP4 column amax); fp64 for INT4.
+// Column partials per row range: N, D (and the NVFP4 column amax); fp64 for INT4.
 size_t partial_bytes(int fmt, int64_t strips, int64_t cols) {
   const int nq = fmt == DQ_FMT_NVFP4 ? 3 : 2;
   const size_t el = fmt == DQ_FMT_INT4 ? sizeof(double) : sizeof(float);
@@ -63,67 +63,58 @@ int check_matrix(const void* X, int32_t dt, int64_t rows, int64_t cols, int64_t 
   return DQ_OK;
 }
 
-// Sweep geometry: a row of cols/16 chunks is held by lpr lanes (a multiple of 64) with
-// K chunks each; workgroups have at most 512 threads (256 registers per lane).
-int sweep_chunks_per_lane(int64_t cols) { return cols / 16 > 512 ? 2 : 1; }
-int sweep_lanes_per_row(int64_t cols) {
-  int64_t nch = cols / 16, K = sweep_chunks_per_lane(cols);
-  return (int)std::max<int64_t>(64, ((nch + K - 1) / K + 63) / 64 * 64);
-}
-// Row slots per workgroup: up to 512 threads, and the slot-combine buffer of the sweep
-// ((H-1) * lpr * 16 accumulators, fp64 for INT4) within 48 KB of LDS.
-int sweep_row_slots(int lpr, int fmt) {
-  const int cap = fmt == DQ_FMT_INT4 ? 384 : 768;
-  return std::max(1, std::min(512 / lpr, 1 + cap / lpr));
-}
+// Row pass: workgroups of 16 waves, one wave per row; enough rows per wave that a single
+// large matrix gives about one workgroup per CU.
+constexpr int kRowWaves = 16;
+constexpr int kTargetRowWaves = 256 * kRowWaves;
+// Column pass: workgroups of 8 waves on a 1024-column strip; about two per CU.
+constexpr int kTargetColWgs = 512;
 // Standalone quantiser geometry: one chunk per lane, up to 1024 threads.
 int lanes_per_row(int64_t cols) { return (int)std::max<int64_t>(64, (cols / 16 + 63) / 64 * 64); }
 int row_slots(int lpr) { return std::max(1, 1024 / lpr); }
+size_t rowpass_lds(int fmt, int64_t cols) {
+  return 2 * sizeof(float) * (size_t)cols + (fmt == DQ_FMT_NVFP4 ? 2 * sizeof(NvTab) : 0);
+}
+size_t colpass_lds(int fmt) { return (size_t)7 * 16 * 64 * (fmt == DQ_FMT_INT4 ? 8 : 4); }
 
 struct Plan {
-  // per problem
   std::vector<ProbDev> dev;
   std::vector<int> group_of;   // launch group index, -1 for empty problems
-  // per launch group: (dtype, lpr)
-  struct Group {
-    int dtype, lpr, H, K;
-    std::vector<WgEntry> sweep, fin;
-    size_t sweep_off, fin_off;  // offsets of the tables in the workspace
-    int max_init_wgs;
+  struct Group {               // problems sharing (dtype, cols) share the launches
+    int dtype;
+    int64_t cols;
+    std::vector<WgEntry> row, col, fin;
+    size_t row_off, col_off, fin_off;  // offsets of the tables in the workspace
   };
   std::vector<Group> groups;
   size_t probs_off = 0, total = 0;
-  std::vector<size_t> prob_off, prob_bytes;
+  std::vector<size_t> prob_off;
 };
 
-// Lays out the workspace and the launch tables.  With ws == nullptr only sizes are
-// computed (pointers in `dev` are then offsets, unused).
+// Lays out the workspace and the launch tables (sizes only; pointers are bound later).
 int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Plan& pl) {
   pl.dev.assign(count, ProbDev{});
   pl.group_of.assign(count, -1);
   pl.prob_off.assign(count, 0);
-  pl.prob_bytes.assign(count, 0);
-  std::map<std::pair<int, int>, int> gid;
-  std::vector<int64_t> group_rows;
+  std::map<std::pair<int, int64_t>, int> gid;
+  int64_t total_rows = 0;
   for (int k = 0; k < count; ++k) {
     if (p[k].rows == 0 || p[k].cols == 0) continue;
-    int lpr = sweep_lanes_per_row(p[k].cols);
-    auto key = std::make_pair((int)p[k].w_dtype, lpr);
+    total_rows += p[k].rows;
+    auto key = std::make_pair((int)p[k].w_dtype, (int64_t)p[k].cols);
     auto it = gid.find(key);
     if (it == gid.end()) {
       Plan::Group G;
       G.dtype = p[k].w_dtype;
-      G.lpr = lpr;
-      G.H = sweep_row_slots(lpr, fmt);
-      G.K = sweep_chunks_per_lane(p[k].cols);
-      G.max_init_wgs = 0;
+      G.cols = p[k].cols;
       it = gid.emplace(key, (int)pl.groups.size()).first;
       pl.groups.push_back(G);
-      group_rows.push_back(0);
     }
     pl.group_of[k] = it->second;
-    group_rows[it->second] += p[k].rows;
   }
+  const int64_t rows_per_wave = std::max<int64_t>(1, (total_rows + kTargetRowWaves - 1) / kTargetRowWaves);
+  const int nq = fmt == DQ_FMT_NVFP4 ? 3 : 2;
+  const size_t acc_bytes = fmt == DQ_FMT_INT4 ? 8 : 4;
   size_t off = 0;
   for (int k = 0; k < count; ++k) {
     ProbDev& d = pl.dev[k];
@@ -134,36 +125,37 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     d.dtype = p[k].w_dtype;
     if (pl.group_of[k] < 0) continue;
     Plan::Group& G = pl.groups[pl.group_of[k]];
-    int64_t R = (group_rows[pl.group_of[k]] + kTargetWgs - 1) / kTargetWgs;
-    R = std::max<int64_t>(G.H, (R + G.H - 1) / G.H * G.H);
-    d.lpr = G.lpr;
-    d.hslots = G.H;
-    d.rows_per_strip = (int32_t)R;
-    d.strips = (int32_t)((d.rows + R - 1) / R);
-    d.fin_wgs = (int32_t)((d.cols + 63) / 64);
+    d.rows_per_blk = (int32_t)(kRowWaves * rows_per_wave);
+    d.rowblocks = (int32_t)((d.rows + d.rows_per_blk - 1) / d.rows_per_blk);
+    d.nstrips = (int32_t)((d.cols / 16 + 63) / 64);
+    int64_t want = (kTargetColWgs * d.rows + total_rows - 1) / total_rows;   // this matrix's share
+    int64_t rr = std::max<int64_t>(1, std::min<int64_t>(d.rows, (want + d.nstrips - 1) / d.nstrips));
+    d.rows_per_range = (int32_t)((d.rows + rr - 1) / rr);
+    d.rranges = (int32_t)((d.rows + d.rows_per_range - 1) / d.rows_per_range);
+    d.fin_wgs = (int32_t)((d.cols + 255) / 256);
     d.init_wgs = (int32_t)std::min<int64_t>(1024, d.rows);
-    G.max_init_wgs = std::max(G.max_init_wgs, d.init_wgs);
-    size_t start = off;
     pl.prob_off[k] = off;
     off = align_up(off + sizeof(State));
     off = align_up(off + 4 * sizeof(float) * d.rows);                  // r[2], ir[2]
     off = align_up(off + 4 * sizeof(float) * d.cols);                  // c[2], ic[2]
     off = align_up(off + (size_t)d.rows * d.cols / 2);                 // codes buffer 1
     off = align_up(off + (size_t)d.rows * d.cols / g * scale_bytes(fmt));
-    off = align_up(off + partial_bytes(fmt, d.strips, d.cols));
-    off = align_up(off + (size_t)d.strips * 4 * sizeof(double));
+    off = align_up(off + (size_t)d.rranges * nq * d.cols * acc_bytes);  // column partials
+    off = align_up(off + (size_t)d.rowblocks * 4 * sizeof(double));
     off = align_up(off + (size_t)d.fin_wgs * sizeof(float));
     off = align_up(off + (size_t)d.init_wgs * 2 * sizeof(double));
     off = align_up(off + 2 * (size_t)(iters + 1) * sizeof(double));   // histories if caller has none
-    pl.prob_bytes[k] = off - start;
-    for (int s = 0; s < d.strips; ++s) G.sweep.push_back(WgEntry{k, s});
+    for (int b = 0; b < d.rowblocks; ++b) G.row.push_back(WgEntry{k, b});
+    for (int b = 0; b < d.nstrips * d.rranges; ++b) G.col.push_back(WgEntry{k, b});
     for (int f = 0; f < d.fin_wgs; ++f) G.fin.push_back(WgEntry{k, f});
   }
   pl.probs_off = off;
   off = align_up(off + sizeof(ProbDev) * std::max(1, (int)count));
   for (auto& G : pl.groups) {
-    G.sweep_off = off;
-    off = align_up(off + sizeof(WgEntry) * G.sweep.size());
+    G.row_off = off;
+    off = align_up(off + sizeof(WgEntry) * G.row.size());
+    G.col_off = off;
+    off = align_up(off + sizeof(WgEntry) * G.col.size());
     G.fin_off = off;
     off = align_up(off + sizeof(WgEntry) * G.fin.size());
   }
@@ -187,8 +179,8 @@ void bind_pointers(const dq_problem* p, int32_t count, int g, int fmt, int iters
     d.codes[1] = (uint8_t*)take((size_t)d.rows * d.cols / 2);
     d.scales[0] = p[k].block_scales;
     d.scales[1] = take((size_t)d.rows * d.cols / g * scale_bytes(fmt));
-    d.colP = take(partial_bytes(fmt, d.strips, d.cols));
-    d.swp = (double*)take((size_t)d.strips * 4 * sizeof(double));
+    d.colP = take(partial_bytes(fmt, d.rranges, d.cols));
+    d.swp = (double*)take((size_t)d.rowblocks * 4 * sizeof(double));
     d.fwp = (float*)take((size_t)d.fin_wgs * sizeof(float));
     d.initp = (double*)take((size_t)d.init_wgs * 2 * sizeof(double));
     double* hist = (double*)take(2 * (size_t)(iters + 1) * sizeof(double));
@@ -206,37 +198,67 @@ void bind_pointers(const dq_problem* p, int32_t count, int g, int fmt, int iters
 template <int FMT>
 constexpr int lanes_per_block(int g) { return g / 16; }
 
+// Events attached to the next solver-pass launch (kernel begin / end timestamps, no extra
+// stream packets); set by the iteration driver when per-kernel timing is requested.
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+template <typename K, typename... A>
+void launch_timed(K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s, A... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, s, t_ev_start, t_ev_stop, 0u, args...);
+  t_ev_start = nullptr;
+  t_ev_stop = nullptr;
+}
+
 #define DQ_HIP(call)                                   \
   do {                                                 \
     if ((call) != hipSuccess) return DQ_ERR_HIP;       \
   } while (0)
 
 template <int FMT, int DT, int L>
-int launch_sweep(const Plan::Group& G, const ProbDev* probs, const WgEntry* tab,
-                 hipStream_t s) {
-  size_t dyn = (size_t)(G.H - 1) * G.lpr * 16 * (FMT == INT4 ? sizeof(double) : sizeof(float));
-  dim3 grid((unsigned)G.sweep.size()), block((unsigned)(G.lpr * G.H));
-  if (G.K == 1) hipLaunchKernelGGL((k_sweep<FMT, DT, L, 1>), grid, block, dyn, s, probs, tab);
-  else hipLaunchKernelGGL((k_sweep<FMT, DT, L, 2>), grid, block, dyn, s, probs, tab);
+int launch_passes(const Plan::Group& G, const ProbDev* probs, const WgEntry* rtab,
+                  const WgEntry* ctab, hipStream_t s) {
+  const size_t rl = rowpass_lds(FMT, G.cols);
+  if (rl > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)k_rowpass<FMT, DT, L>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl) != hipSuccess)
+    return DQ_ERR_HIP;
+  launch_timed(k_rowpass<FMT, DT, L>, dim3((unsigned)G.row.size()), dim3(kRowWaves * 64), rl, s,
+               probs, rtab);
+  if (hipGetLastError() != hipSuccess) return DQ_ERR_HIP;
+  return DQ_OK;
+}
+
+template <int FMT, int DT, int L>
+int launch_colpass(const Plan::Group& G, const ProbDev* probs, const WgEntry* ctab, hipStream_t s) {
+  if (FMT == INT4)
+    launch_timed(k_colpass_wide<FMT, DT, L>, dim3((unsigned)G.col.size()), dim3(512),
+                 colpass_lds(FMT), s, probs, ctab);
+  else
+    launch_timed(k_colpass<FMT, DT, L>, dim3((unsigned)G.col.size()), dim3(512), colpass_lds(FMT),
+                 s, probs, ctab);
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
 template <int FMT, int L>
-int launch_sweep_dt(int dt, const Plan::Group& G, const ProbDev* probs, const WgEntry* tab,
-                    hipStream_t s) {
-  return dt == DQ_F32 ? launch_sweep<FMT, 0, L>(G, probs, tab, s)
-                      : launch_sweep<FMT, 1, L>(G, probs, tab, s);
+int launch_pass_dt(int which, const Plan::Group& G, const ProbDev* probs, const WgEntry* rtab,
+                   const WgEntry* ctab, hipStream_t s) {
+  if (which == 0)
+    return G.dtype == DQ_F32 ? launch_passes<FMT, 0, L>(G, probs, rtab, ctab, s)
+                             : launch_passes<FMT, 1, L>(G, probs, rtab, ctab, s);
+  return G.dtype == DQ_F32 ? launch_colpass<FMT, 0, L>(G, probs, ctab, s)
+                           : launch_colpass<FMT, 1, L>(G, probs, ctab, s);
 }
 
-int launch_sweep_any(int fmt, int g, const Plan::Group& G, const ProbDev* probs,
-                     const WgEntry* tab, hipStream_t s) {
+// which = 0: row pass, 1: column pass
+int launch_pass_any(int which, int fmt, int g, const Plan::Group& G, const ProbDev* probs,
+                    const WgEntry* rtab, const WgEntry* ctab, hipStream_t s) {
   switch (fmt) {
     case DQ_FMT_INT4:
-      return g == 64 ? launch_sweep_dt<INT4, 4>(G.dtype, G, probs, tab, s)
-                     : launch_sweep_dt<INT4, 8>(G.dtype, G, probs, tab, s);
-    case DQ_FMT_MXINT4: return launch_sweep_dt<MXINT4, 2>(G.dtype, G, probs, tab, s);
-    case DQ_FMT_MXFP4: return launch_sweep_dt<MXFP4, 2>(G.dtype, G, probs, tab, s);
-    default: return launch_sweep_dt<NVFP4, 1>(G.dtype, G, probs, tab, s);
+      return g == 64 ? launch_pass_dt<INT4, 4>(which, G, probs, rtab, ctab, s)
+                     : launch_pass_dt<INT4, 8>(which, G, probs, rtab, ctab, s);
+    case DQ_FMT_MXINT4: return launch_pass_dt<MXINT4, 2>(which, G, probs, rtab, ctab, s);
+    case DQ_FMT_MXFP4: return launch_pass_dt<MXFP4, 2>(which, G, probs, rtab, ctab, s);
+    default: return launch_pass_dt<NVFP4, 1>(which, G, probs, rtab, ctab, s);
   }
 }
 
@@ -244,10 +266,10 @@ int launch_finalize_any(int fmt, const Plan::Group& G, const ProbDev* probs,
                         const WgEntry* tab, hipStream_t s) {
   dim3 grid((unsigned)G.fin.size()), block(256);
   switch (fmt) {
-    case DQ_FMT_INT4: hipLaunchKernelGGL((k_finalize<INT4>), grid, block, 0, s, probs, tab); break;
-    case DQ_FMT_MXINT4: hipLaunchKernelGGL((k_finalize<MXINT4>), grid, block, 0, s, probs, tab); break;
-    case DQ_FMT_MXFP4: hipLaunchKernelGGL((k_finalize<MXFP4>), grid, block, 0, s, probs, tab); break;
-    default: hipLaunchKernelGGL((k_finalize<NVFP4>), grid, block, 0, s, probs, tab); break;
+    case DQ_FMT_INT4: launch_timed(k_finalize<INT4>, grid, block, 0, s, probs, tab); break;
+    case DQ_FMT_MXINT4: launch_timed(k_finalize<MXINT4>, grid, block, 0, s, probs, tab); break;
+    case DQ_FMT_MXFP4: launch_timed(k_finalize<MXFP4>, grid, block, 0, s, probs, tab); break;
+    default: launch_timed(k_finalize<NVFP4>, grid, block, 0, s, probs, tab); break;
   }
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
@@ -327,6 +349,7 @@ const char* dq_status_string(int status) {
 
 static int validate_solve(const dq_problem* p, int32_t count, dq_quant_spec spec,
                           const dq_solve_opts* o, int* g_out) {
+  if (o && o->pass_ms && o->pass_ms_capacity < 0) return DQ_ERR_ARG;
   if (!p || !o) return DQ_ERR_NULL;
   if (count < 1) return DQ_ERR_ARG;
   int g = resolve_group(spec);
@@ -356,7 +379,7 @@ size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_sp
 }
 
 int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
-             const dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
+             dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
   int g = 0;
   int rc = validate_solve(problems, count, spec, opts, &g);
   if (rc) return rc;
@@ -389,7 +412,9 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
   ProbDev* dprobs = (ProbDev*)(ws + pl.probs_off);
   DQ_HIP(hipMemcpyAsync(dprobs, pl.dev.data(), sizeof(ProbDev) * count, hipMemcpyHostToDevice, s));
   for (auto& G : pl.groups) {
-    DQ_HIP(hipMemcpyAsync(ws + G.sweep_off, G.sweep.data(), sizeof(WgEntry) * G.sweep.size(),
+    DQ_HIP(hipMemcpyAsync(ws + G.row_off, G.row.data(), sizeof(WgEntry) * G.row.size(),
+                          hipMemcpyHostToDevice, s));
+    DQ_HIP(hipMemcpyAsync(ws + G.col_off, G.col.data(), sizeof(WgEntry) * G.col.size(),
                           hipMemcpyHostToDevice, s));
     DQ_HIP(hipMemcpyAsync(ws + G.fin_off, G.fin.data(), sizeof(WgEntry) * G.fin.size(),
                           hipMemcpyHostToDevice, s));
@@ -413,35 +438,75 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
     if (rc) return rc;
   }
 
+  // optional per-kernel timing: a begin/end event pair attached to each pass's launches
+  const bool timed = opts->pass_ms != nullptr && opts->pass_ms_capacity > 0;
+  std::vector<hipEvent_t> ev;
+  opts->pass_ms_count = 0;
+  auto cleanup = [&]() {
+    for (auto e : ev) (void)hipEventDestroy(e);
+    ev.clear();
+  };
+  auto new_event = [&](hipEvent_t* e) -> bool {
+    if (hipEventCreate(e) != hipSuccess) return false;
+    ev.push_back(*e);
+    return true;
+  };
   std::vector<State> hst(count);
   int pending = 1 + iters;   // INIT sweep + one sweep per iteration, if nothing is rejected
   // at most one extra (re-solve) sweep per rejected iteration
   const int max_sweeps = 2 * iters + 2;
   int launched = 0;
+  const size_t ng = pl.groups.size();
   while (pending > 0) {
-    if (launched + pending > max_sweeps) return DQ_ERR_HIP;
+    if (launched + pending > max_sweeps) { cleanup(); return DQ_ERR_HIP; }
     launched += pending;
+    const size_t ev0 = ev.size();
     for (int sw = 0; sw < pending; ++sw) {
-      for (auto& G : pl.groups) {
-        rc = launch_sweep_any(spec.fmt, g, G, dprobs, (const WgEntry*)(ws + G.sweep_off), s);
-        if (rc) return rc;
-      }
-      for (auto& G : pl.groups) {
-        rc = launch_finalize_any(spec.fmt, G, dprobs, (const WgEntry*)(ws + G.fin_off), s);
-        if (rc) return rc;
+      const bool tm = timed && (int)(ev.size() / 6) < opts->pass_ms_capacity;
+      hipEvent_t e[6] = {};
+      if (tm)
+        for (int q = 0; q < 6; ++q)
+          if (!new_event(&e[q])) { cleanup(); return DQ_ERR_HIP; }
+      for (int which = 0; which < 3; ++which) {
+        for (size_t gi = 0; gi < ng; ++gi) {
+          const auto& G = pl.groups[gi];
+          if (tm) {
+            t_ev_start = gi == 0 ? e[2 * which] : nullptr;
+            t_ev_stop = gi + 1 == ng ? e[2 * which + 1] : nullptr;
+          }
+          rc = which < 2 ? launch_pass_any(which, spec.fmt, g, G, dprobs,
+                                           (const WgEntry*)(ws + G.row_off),
+                                           (const WgEntry*)(ws + G.col_off), s)
+                         : launch_finalize_any(spec.fmt, G, dprobs,
+                                               (const WgEntry*)(ws + G.fin_off), s);
+          t_ev_start = t_ev_stop = nullptr;
+          if (rc) { cleanup(); return rc; }
+        }
       }
     }
-    DQ_HIP(hipStreamSynchronize(s));
+    if (hipStreamSynchronize(s) != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
+    for (size_t k = ev0; k + 5 < ev.size(); k += 6) {
+      for (int q = 0; q < 3; ++q) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, ev[k + 2 * q], ev[k + 2 * q + 1]) != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
+        opts->pass_ms[3 * opts->pass_ms_count + q] = ms;
+      }
+      opts->pass_ms_count++;
+    }
     pending = 0;
     for (int k = 0; k < count; ++k) {
       if (pl.group_of[k] < 0) continue;
-      DQ_HIP(hipMemcpy(&hst[k], pl.dev[k].st, sizeof(State), hipMemcpyDeviceToHost));
+      if (hipMemcpy(&hst[k], pl.dev[k].st, sizeof(State), hipMemcpyDeviceToHost) != hipSuccess) {
+        cleanup();
+        return DQ_ERR_HIP;
+      }
       if (hst[k].mode == MODE_DONE) continue;
       int need = (iters - hst[k].it_done) + (hst[k].mode == MODE_FIXUP ? 1 : 0);
       pending = std::max(pending, need);
     }
   }
 
+  cleanup();
   // outputs: final scales, kept codes, tensor scale, reports
   for (int k = 0; k < count; ++k) {
     if (pl.group_of[k] < 0) continue;

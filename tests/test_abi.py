@@ -45,7 +45,7 @@ def _problem(dq, rows=64, cols=256, ld=None, dtype=1, W=0x10000, codes=0x20000):
 
 def _solve_rc(dq, probs, fmt=3, group=0, iters=4, ws=0x70000, wsb=1 << 40):
     arr = (dq.dq_problem * len(probs))(*probs)
-    opts = dq.dq_solve_opts(iters, 0.0)
+    opts = dq.dq_solve_opts(iters, 0.0, None, 0, 0)
     return dq._lib.dq_solve(arr, len(probs), dq.dq_quant_spec(fmt, group), C.byref(opts), ws, wsb, None)
 
 
@@ -64,18 +64,18 @@ def test_solve_argument_errors(dq):
     assert _solve_rc(dq, [ok], ws=0) == -5                          # no workspace
     assert _solve_rc(dq, [ok], wsb=16) == -5                        # workspace too small
     arr = (dq.dq_problem * 1)(ok)
-    assert dq._lib.dq_solve(arr, 0, dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(1, 0.0)), 0x70000, 1 << 40, None) == -7
+    assert dq._lib.dq_solve(arr, 0, dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(1, 0.0, None, 0, 0)), 0x70000, 1 << 40, None) == -7
 
 
 def test_workspace_bytes_accounting(dq):
     ok = _problem(dq, rows=4096, cols=14336)
     arr = (dq.dq_problem * 1)(ok)
-    nb = dq._lib.dq_workspace_bytes(arr, 1, dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(16, 0.0)))
+    nb = dq._lib.dq_workspace_bytes(arr, 1, dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(16, 0.0, None, 0, 0)))
     # at least the second code/scale buffer, scales, column partials for one strip per CU
     assert nb >= 4096 * 14336 // 2 + 4096 * 14336 // 16
     assert nb < 4096 * 14336 * 2   # below the size of W itself
     bad = (dq.dq_problem * 1)(_problem(dq, cols=200))
-    assert dq._lib.dq_workspace_bytes(bad, 1, dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(16, 0.0))) == 0
+    assert dq._lib.dq_workspace_bytes(bad, 1, dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(16, 0.0, None, 0, 0))) == 0
 
 
 def test_quantize_argument_errors(dq):
