@@ -293,12 +293,13 @@ struct RawRow<0> {   // fp32: 16 floats per chunk
   }
 };
 
-__device__ __forceinline__ void lds_load16(const float* base, float (&x)[16]) {
-  const float4* p = (const float4*)base;
+// 16 values of chunk ch from an LDS vector stored chunk-interleaved: float4 number q (0..3)
+// of chunk ch at index q * nch + ch, so consecutive lanes read consecutive 16-byte words.
+__device__ __forceinline__ void lds_load16(const f32x4* base, int nch, int ch, float (&x)[16]) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float4 a = p[k];
-    x[4 * k] = a.x; x[4 * k + 1] = a.y; x[4 * k + 2] = a.z; x[4 * k + 3] = a.w;
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 a = base[q * nch + ch];
+    x[4 * q] = a.x; x[4 * q + 1] = a.y; x[4 * q + 2] = a.z; x[4 * q + 3] = a.w;
   }
 }
 
@@ -335,8 +336,8 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
   const int nch = (int)(n >> 4);
 
   extern __shared__ float lds[];
-  float* s_c = lds;
-  float* s_ic = lds + n;
+  f32x4* s_c4 = (f32x4*)lds;           // c, chunk-interleaved (see lds_load16)
+  f32x4* s_ic4 = s_c4 + 4 * nch;       // 1/c, same layout
   NvTab* tab_c = (NvTab*)(lds + 2 * n);
   NvTab* tab_p = tab_c + 1;
   __shared__ double redw[16][4];
@@ -344,9 +345,11 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
   {
     const DQ_GAS f32x4* c4 = gp((const f32x4*)P.c[pi.cs]);
     const DQ_GAS f32x4* ic4 = gp((const f32x4*)P.ic[pi.cs]);
-    f32x4* sc4 = (f32x4*)s_c;
-    f32x4* sic4 = (f32x4*)s_ic;
-    for (int k = threadIdx.x; k < (int)(n >> 2); k += blockDim.x) { sc4[k] = c4[k]; sic4[k] = ic4[k]; }
+    for (int e = threadIdx.x; e < 4 * nch; e += blockDim.x) {
+      const int ch = e >> 2, q = e & 3;
+      s_c4[q * nch + ch] = c4[e];
+      s_ic4[q * nch + ch] = ic4[e];
+    }
     if (FMT == NVFP4) {
       build_nvtab(*tab_c, st->st_cur);
       build_nvtab(*tab_p, st->st_acc);
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         float v[16];
         {
           float icc[16];
-          if (valid) lds_load16(s_ic + j0, icc);
+          if (valid) lds_load16(s_ic4, nch, chn, icc);
           else {
 #pragma unroll
             for (int k = 0; k < 16; ++k) icc[k] = 0.0f;
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         f = ch.f;
 #pragma unroll
         for (int k = 0; k < 16; ++k) p[k] = ch.p[k];
-        if (valid) lds_load16(s_c + j0, cc);
+        if (valid) lds_load16(s_c4, nch, chn, cc);
         else {
 #pragma unroll
           for (int k = 0; k < 16; ++k) cc[k] = 0.0f;
@@ -456,7 +459,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
       } else {
         decode_grid<FMT>(p0, p1, p);
         f = block_factor<FMT>(ps, tab_p);
-        if (valid) lds_load16(s_c + j0, cc);
+        if (valid) lds_load16(s_c4, nch, chn, cc);
         else {
 #pragma unroll
           for (int k = 0; k < 16; ++k) cc[k] = 0.0f;
@@ -608,38 +611,34 @@ __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
       }
     }
   }
-  // combine the 8 waves in fixed order
+  // combine the 8 waves: one quantity per round, every wave stores its 16 values per lane in
+  // LDS, then thread (lane chunk l, quad kq) sums the 8 waves in wave order and stores 4
+  // consecutive columns, so a wave writes 1 KB of the partial contiguously
+  typedef acc_t vec4 __attribute__((ext_vector_type(4)));
   extern __shared__ float xs[];
-  acc_t* xa = (acc_t*)xs;
+  vec4* xa = (vec4*)xs;                     // [8 waves][64 chunks][4 quads]
+  DQ_GAS acc_t* base = gp((acc_t*)P.colP + (size_t)rr * NQ * (size_t)n + 16 * (size_t)strip * 64);
+  const int ol = t >> 2, oq = t & 3;        // output chunk (0..127, only < 64 used) and quad
   for (int qi = 0; qi < NQ; ++qi) {
-    __syncthreads();
-    if (wave >= 1) {
+    if (qi) __syncthreads();
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const acc_t v = (qi == 0) ? cN[k] : (qi == 1) ? cD[k] : (acc_t)cM[k];
-        xa[(k * 7 + (wave - 1)) * 64 + lane] = v;
-      }
+    for (int kq = 0; kq < 4; ++kq) {
+      vec4 v;
+      if (qi == 0) v = vec4{cN[4 * kq], cN[4 * kq + 1], cN[4 * kq + 2], cN[4 * kq + 3]};
+      else if (qi == 1) v = vec4{cD[4 * kq], cD[4 * kq + 1], cD[4 * kq + 2], cD[4 * kq + 3]};
+      else v = vec4{(acc_t)cM[4 * kq], (acc_t)cM[4 * kq + 1], (acc_t)cM[4 * kq + 2], (acc_t)cM[4 * kq + 3]};
+      xa[(wave * 64 + lane) * 4 + kq] = v;
     }
     __syncthreads();
-    if (wave == 0) {
-      for (int ww = 1; ww < 8; ++ww) {
+    if (ol < 64 && strip * 64 + ol < nch) {
+      vec4 a = xa[ol * 4 + oq];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const acc_t o = xa[(k * 7 + (ww - 1)) * 64 + lane];
-          if (qi == 0) cN[k] += o;
-          else if (qi == 1) cD[k] += o;
-          else cM[k] = fmaxf(cM[k], (float)o);
-        }
+      for (int w = 1; w < 8; ++w) {
+        const vec4 o = xa[(w * 64 + ol) * 4 + oq];
+        if (qi < 2) a += o;
+        else { a.x = fmaxf(a.x, o.x); a.y = fmaxf(a.y, o.y); a.z = fmaxf(a.z, o.z); a.w = fmaxf(a.w, o.w); }
       }
-    }
-  }
-  if (wave == 0 && act) {
-    DQ_GAS acc_t* base = gp((acc_t*)P.colP + (size_t)rr * NQ * (size_t)n + j0);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      base[k] = cN[k];
-      base[n + k] = cD[k];
-      if (FMT == NVFP4) base[2 * n + k] = (acc_t)cM[k];
+      *(DQ_GAS vec4*)(base + (size_t)qi * n + 16 * ol + 4 * oq) = a;
     }
   }
 }
@@ -690,15 +689,15 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
       const int S = P.rranges;
       const DQ_GAS acc_t* b = gp((const acc_t*)P.colP + j);
       const size_t stride = (size_t)NQ * (size_t)n;
-      for (int s0 = 0; s0 < S; s0 += 8) {
+      int s0 = 0;
+      for (; s0 + 8 <= S; s0 += 8) {
         acc_t vn[8], vd[8], vm[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const bool ok = s0 + u < S;
           const DQ_GAS acc_t* q = b + (size_t)(s0 + u) * stride;
-          vn[u] = ok ? q[0] : (acc_t)0;
-          vd[u] = ok ? q[n] : (acc_t)0;
-          vm[u] = (ok && FMT == NVFP4) ? q[2 * n] : (acc_t)0;
+          vn[u] = q[0];
+          vd[u] = q[n];
+          if (FMT == NVFP4) vm[u] = q[2 * n];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -706,6 +705,12 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
           D += (double)vd[u];
           if (FMT == NVFP4) M = fmaxf(M, (float)vm[u]);
         }
+      }
+      for (; s0 < S; ++s0) {
+        const DQ_GAS acc_t* q = b + (size_t)s0 * stride;
+        N += (double)q[0];
+        D += (double)q[n];
+        if (FMT == NVFP4) M = fmaxf(M, (float)q[2 * n]);
       }
       float x = __builtin_nanf("");
       float cnew;

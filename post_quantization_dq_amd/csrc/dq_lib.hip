@@ -75,7 +75,7 @@ int row_slots(int lpr) { return std::max(1, 1024 / lpr); }
 size_t rowpass_lds(int fmt, int64_t cols) {
   return 2 * sizeof(float) * (size_t)cols + (fmt == DQ_FMT_NVFP4 ? 2 * sizeof(NvTab) : 0);
 }
-size_t colpass_lds(int fmt) { return (size_t)7 * 16 * 64 * (fmt == DQ_FMT_INT4 ? 8 : 4); }
+size_t colpass_lds(int fmt) { return (size_t)8 * 64 * 16 * (fmt == DQ_FMT_INT4 ? 8 : 4); }
 
 struct Plan {
   std::vector<ProbDev> dev;
@@ -230,9 +230,14 @@ int launch_passes(const Plan::Group& G, const ProbDev* probs, const WgEntry* rta
 
 template <int FMT, int DT, int L>
 int launch_colpass(const Plan::Group& G, const ProbDev* probs, const WgEntry* ctab, hipStream_t s) {
-  if (FMT == INT4)
+  if (FMT == INT4) {
+    if (hipFuncSetAttribute((const void*)k_colpass_wide<FMT, DT, L>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)colpass_lds(FMT)) != hipSuccess)
+      return DQ_ERR_HIP;
     launch_timed(k_colpass_wide<FMT, DT, L>, dim3((unsigned)G.col.size()), dim3(512),
                  colpass_lds(FMT), s, probs, ctab);
+  }
   else
     launch_timed(k_colpass<FMT, DT, L>, dim3((unsigned)G.col.size()), dim3(512), colpass_lds(FMT),
                  s, probs, ctab);
