@@ -84,9 +84,10 @@ typedef struct {
   float tol_relchg;  /* > 0: stop after the first iteration whose relative change of Qhat is
                         <= tol_relchg; 0: run all T iterations */
   float* pass_ms;     /* HOST array or NULL: per sweep over W, three durations in ms -- the
-                          row pass, the column pass and the finalize (all problems of the
-                          call) -- from HIP event pairs attached to the kernel launches on
-                          `stream` (kernel begin and end; no extra stream commands) */
+                          row pass, the column pass, and the column finalize plus the
+                          safeguard decision (all problems of the call) -- from HIP event
+                          pairs attached to the kernel launches on `stream` (kernel begin
+                          and end) */
   int32_t pass_ms_capacity;  /* sweeps that fit in pass_ms (3 floats each) */
   int32_t pass_ms_count;     /* out: sweeps written */
 } dq_solve_opts;

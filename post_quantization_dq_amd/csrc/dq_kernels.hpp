@@ -1,6 +1,6 @@
 // HIP kernels of the DualQuant dual-scale BCD solver for gfx950.
 //
-// Each BCD iteration is three launches over all problems of a batch:
+// Each BCD iteration is four launches over all problems of a batch:
 //   k_rowpass   one wave per row (no workgroup barriers in the row loop); c and 1/c of every
 //               column sit in LDS.  It quantises the candidate Qc = FQ_f(W ./ r^s c^s^T)
 //               (Qhat-step of iteration s) and stores its codes, measures F(r^s,c^s,Qc), the
@@ -11,10 +11,11 @@
 //   k_colpass   workgroups own 1024-column strips and a range of rows; with the new r it
 //               accumulates the c-step sums N_j, D_j (and the NVFP4 column amax of W ./ r)
 //               in registers and writes one partial per row range.
-//   k_finalize  reduces the partials, projects c, and its last workgroup takes the
-//               safeguard decision and advances the per-problem state machine.  If the
-//               candidate is rejected the speculative r/c are discarded and the next
-//               iteration re-runs the r/c steps from the kept Qhat (FIXUP mode).
+//   k_finalize  reduces the partials and projects c.
+//   k_decide    one workgroup per problem takes the safeguard decision and advances the
+//               per-problem state machine.  If the candidate is rejected the speculative
+//               r/c are discarded and the next iteration re-runs the r/c steps from the kept
+//               Qhat (FIXUP mode).
 // Lane l of a wave owns chunks of 16 consecutive columns; blocks of MX (32) and INT4
 // (64/128) formats span 2..8 adjacent lanes.
 
@@ -207,24 +208,26 @@ __global__ __launch_bounds__(256) void k_init(const ProbDev* __restrict__ probs)
   }
   __shared__ double ss[4];
   __shared__ float sm[4];
-  __shared__ int last;
   s2 = wave_sum(s2);
   amax = wave_max(amax);
-  int wv = threadIdx.x >> 6;
+  const int wv = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) { ss[wv] = s2; sm[wv] = amax; }
   bad = __syncthreads_or(bad);
   if (threadIdx.x == 0) {
     gp(P.initp)[2 * blockIdx.x] = ((ss[0] + ss[1]) + ss[2]) + ss[3];
     gp(P.initp)[2 * blockIdx.x + 1] = (double)fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
     if (bad) atomicOr(&P.st->flags, 1u);
-    __threadfence();
-    unsigned prev = atomicAdd(&P.st->init_counter, 1u);
-    last = (prev == (unsigned)P.init_wgs - 1);
   }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  // the last workgroup combines the partials: strided per thread, then in fixed order
+}
+
+// Combines k_init's partials (one workgroup per problem): strided per thread, then in
+// fixed order; sets ||W||^2 and the initial NVFP4 tensor-scale terms.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_init_reduce(const ProbDev* __restrict__ probs) {
+  const ProbDev& P = probs[blockIdx.x];
+  if (P.rows == 0 || P.cols == 0) return;
+  __shared__ double ss[4];
+  __shared__ float sm[4];
   double tot = 0.0;
   float A = 0.0f;
   for (int b = threadIdx.x; b < P.init_wgs; b += blockDim.x) {
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256) void k_init(const ProbDev* __restrict__ probs)
   }
   tot = wave_sum(tot);
   A = wave_max(A);
-  __syncthreads();
+  const int wv = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) { ss[wv] = tot; sm[wv] = A; }
   __syncthreads();
   if (threadIdx.x != 0) return;
@@ -247,9 +250,8 @@ __global__ __launch_bounds__(256) void k_init(const ProbDev* __restrict__ probs)
     nv_tensor_terms(A, st_, k6_, tiny);
     s->st_cur = st_;
     s->k6_cur = k6_;
-    if (tiny) atomicOr(&s->flags, (uint32_t)16u);
+    if (tiny) s->flags |= 16u;
   }
-  s->init_counter = 0;
 }
 
 // ---------------------------------------------------------------- raw rows
@@ -656,8 +658,9 @@ __global__ __launch_bounds__(512) void k_colpass_wide(const ProbDev* __restrict_
 }
 
 // ---------------------------------------------------------------- finalize
-// Column reduction of the strip partials, c-step projection, next NVFP4 tensor scale, and
-// (last workgroup of each problem) the safeguard decision and state update.
+// Column reduction of the row-range partials, c-step projection and the per-workgroup amax
+// for the next NVFP4 tensor scale.  A workgroup covers 64 columns with 4 threads per column; thread part p sums ranges p, p+4,
+// ... (sixteen loads in flight), and the four parts are added in part order.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ probs,
                                                   const WgEntry* __restrict__ table) {
@@ -671,47 +674,51 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   const int cs = st->cs;
   const int64_t n = P.cols;
 
-  __shared__ float wmax[4];
-  __shared__ double sred[256][4];
-  __shared__ int last;
+  __shared__ double sred[2][4][64];   // [quantity][part][column]
+  __shared__ float smax[4][64];
+  __shared__ float wmax[1];
 
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, col = t & 63, part = t >> 6;
   bool zcol = false;
   if (next) {
     constexpr int NQ = (FMT == NVFP4) ? 3 : 2;
     typedef typename std::conditional<FMT == INT4, double, float>::type acc_t;
-    const int64_t j = (int64_t)we.idx * 256 + t;
-    float am = 0.0f;
+    const int64_t j = (int64_t)we.idx * 64 + col;
+    double N = 0.0, D = 0.0;
+    float M = 0.0f;
     if (j < n) {
-      // sum the row-range partials in range order, eight loads in flight at a time
-      double N = 0.0, D = 0.0;
-      float M = 0.0f;
       const int S = P.rranges;
       const DQ_GAS acc_t* b = gp((const acc_t*)P.colP + j);
       const size_t stride = (size_t)NQ * (size_t)n;
-      int s0 = 0;
-      for (; s0 + 8 <= S; s0 += 8) {
-        acc_t vn[8], vd[8], vm[8];
+      for (int b0 = 0; b0 < S; b0 += 64) {
+        acc_t vn[16], vd[16], vm[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const DQ_GAS acc_t* q = b + (size_t)(s0 + u) * stride;
+        for (int u = 0; u < 16; ++u) {   // clamped index: every load is issued, unused ones dropped
+          const int sr = min(b0 + part + 4 * u, S - 1);
+          const DQ_GAS acc_t* q = b + (size_t)sr * stride;
           vn[u] = q[0];
           vd[u] = q[n];
           if (FMT == NVFP4) vm[u] = q[2 * n];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          N += (double)vn[u];
-          D += (double)vd[u];
-          if (FMT == NVFP4) M = fmaxf(M, (float)vm[u]);
+        for (int u = 0; u < 16; ++u) {
+          if (b0 + part + 4 * u < S) {
+            N += (double)vn[u];
+            D += (double)vd[u];
+            if (FMT == NVFP4) M = fmaxf(M, (float)vm[u]);
+          }
         }
       }
-      for (; s0 < S; ++s0) {
-        const DQ_GAS acc_t* q = b + (size_t)s0 * stride;
-        N += (double)q[0];
-        D += (double)q[n];
-        if (FMT == NVFP4) M = fmaxf(M, (float)q[2 * n]);
-      }
+    }
+    sred[0][part][col] = N;
+    sred[1][part][col] = D;
+    smax[part][col] = M;
+    __syncthreads();
+    float am = 0.0f;
+    if (part == 0 && j < n) {
+      N = ((sred[0][0][col] + sred[0][1][col]) + sred[0][2][col]) + sred[0][3][col];
+      D = ((sred[1][0][col] + sred[1][1][col]) + sred[1][2][col]) + sred[1][3][col];
+      M = fmaxf(fmaxf(smax[0][col], smax[1][col]), fmaxf(smax[2][col], smax[3][col]));
       float x = __builtin_nanf("");
       float cnew;
       if (D > 0.0) {
@@ -727,42 +734,58 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
       if (P.c_trace) gp(P.c_trace)[(int64_t)((mode == MODE_FIXUP) ? it - 1 : it) * n + j] = x;
       if (FMT == NVFP4) am = M * icn;
     }
-    if (FMT == NVFP4) {
+    if (FMT == NVFP4 && part == 0) {
       am = wave_max(am);
-      if ((t & 63) == 0) wmax[t >> 6] = am;
+      if (t == 0) wmax[0] = am;
     }
   }
   zcol = __syncthreads_or(zcol);
   if (t == 0) {
-    if (next && FMT == NVFP4) gp(P.fwp)[we.idx] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (next && FMT == NVFP4) gp(P.fwp)[we.idx] = wmax[0];
     if (zcol) atomicOr(&st->flags, 4u);
-    __threadfence();
-    unsigned prev = atomicAdd(&st->counter, 1u);
-    last = (prev == (unsigned)P.fin_wgs - 1);
   }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+}
 
-  // fixed-order reductions of the sweep's strip partials and the amax partials
-  double f0 = 0.0, f1 = 0.0, f2 = 0.0, f3 = 0.0;
+// Safeguard decision and state update of each problem (one workgroup per problem, after
+// k_finalize): fixed-order reductions of the row pass's partials and of the amax partials,
+// strided per thread, then a pairwise tree over the 256 threads.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_decide(const ProbDev* __restrict__ probs) {
+  const ProbDev& P = probs[blockIdx.x];
+  if (P.rows == 0 || P.cols == 0) return;
+  State* st = P.st;
+  const int mode = st->mode;
+  if (mode == MODE_DONE) return;
+  const int it = (mode == MODE_INIT) ? 0 : st->it_done + 1;
+  const bool next = (mode == MODE_FIXUP) || (it < P.iters);
+  const int t = threadIdx.x;
+  __shared__ double tr[4 * 256];
+  __shared__ float wmax[4];
+  double f[4] = {0.0, 0.0, 0.0, 0.0};
   if (mode != MODE_FIXUP) {
     for (int s = t; s < P.rowblocks; s += 256) {
       const DQ_GAS double* o = gp(P.swp + 4 * (size_t)s);
-      f0 += o[0]; f1 += o[1]; f2 += o[2]; f3 += o[3];
+      f[0] += o[0]; f[1] += o[1]; f[2] += o[2]; f[3] += o[3];
     }
   }
   float A = 0.0f;
   if (next && FMT == NVFP4) {
     for (int k = t; k < P.fin_wgs; k += 256) A = fmaxf(A, gp(P.fwp)[k]);
   }
-  sred[t][0] = f0; sred[t][1] = f1; sred[t][2] = f2; sred[t][3] = f3;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) tr[q * 256 + t] = f[q];
   A = wave_max(A);
   if ((t & 63) == 0) wmax[t >> 6] = A;
+  for (int w = 128; w >= 1; w >>= 1) {
+    __syncthreads();
+    if (t < w) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tr[q * 256 + t] += tr[q * 256 + t + w];
+    }
+  }
   __syncthreads();
   if (t != 0) return;
-  double Fc = 0.0, dF = 0.0, rel = 0.0, qn = 0.0;
-  for (int k = 0; k < 256; ++k) { Fc += sred[k][0]; dF += sred[k][1]; rel += sred[k][2]; qn += sred[k][3]; }
+  const double Fc = tr[0], dF = tr[256], rel = tr[512], qn = tr[768];
   A = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 
   const double nW = st->normW2;
@@ -810,7 +833,6 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
     st->mode = MODE_FIXUP;
   }
   st->sweeps += 1;
-  st->counter = 0;
 }
 
 // ---------------------------------------------------------------- standalone quantiser

@@ -67,8 +67,8 @@ int check_matrix(const void* X, int32_t dt, int64_t rows, int64_t cols, int64_t 
 // large matrix gives about one workgroup per CU.
 constexpr int kRowWaves = 16;
 constexpr int kTargetRowWaves = 256 * kRowWaves;
-// Column pass: workgroups of 8 waves on a 1024-column strip; about two per CU.
-constexpr int kTargetColWgs = 512;
+// Column pass: workgroups of 8 waves on a 1024-column strip; about one per CU.
+constexpr int kTargetColWgs = 256;
 // Standalone quantiser geometry: one chunk per lane, up to 1024 threads.
 int lanes_per_row(int64_t cols) { return (int)std::max<int64_t>(64, (cols / 16 + 63) / 64 * 64); }
 int row_slots(int lpr) { return std::max(1, 1024 / lpr); }
@@ -132,7 +132,7 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     int64_t rr = std::max<int64_t>(1, std::min<int64_t>(d.rows, (want + d.nstrips - 1) / d.nstrips));
     d.rows_per_range = (int32_t)((d.rows + rr - 1) / rr);
     d.rranges = (int32_t)((d.rows + d.rows_per_range - 1) / d.rows_per_range);
-    d.fin_wgs = (int32_t)((d.cols + 255) / 256);
+    d.fin_wgs = (int32_t)((d.cols + 63) / 64);
     d.init_wgs = (int32_t)std::min<int64_t>(1024, d.rows);
     pl.prob_off[k] = off;
     off = align_up(off + sizeof(State));
@@ -279,10 +279,32 @@ int launch_finalize_any(int fmt, const Plan::Group& G, const ProbDev* probs,
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
+int launch_decide_any(int fmt, int count, const ProbDev* probs, hipStream_t s) {
+  dim3 grid((unsigned)count), block(256);
+  switch (fmt) {
+    case DQ_FMT_INT4: launch_timed(k_decide<INT4>, grid, block, 0, s, probs); break;
+    case DQ_FMT_MXINT4: launch_timed(k_decide<MXINT4>, grid, block, 0, s, probs); break;
+    case DQ_FMT_MXFP4: launch_timed(k_decide<MXFP4>, grid, block, 0, s, probs); break;
+    default: launch_timed(k_decide<NVFP4>, grid, block, 0, s, probs); break;
+  }
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
 template <int FMT>
 int launch_init_t(int dt, dim3 grid, const ProbDev* probs, hipStream_t s) {
   if (dt == DQ_F32) hipLaunchKernelGGL((k_init<FMT, 0>), grid, dim3(256), 0, s, probs);
   else hipLaunchKernelGGL((k_init<FMT, 1>), grid, dim3(256), 0, s, probs);
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
+int launch_init_reduce_any(int fmt, int count, const ProbDev* probs, hipStream_t s) {
+  dim3 grid((unsigned)count), block(256);
+  switch (fmt) {
+    case DQ_FMT_INT4: hipLaunchKernelGGL((k_init_reduce<INT4>), grid, block, 0, s, probs); break;
+    case DQ_FMT_MXINT4: hipLaunchKernelGGL((k_init_reduce<MXINT4>), grid, block, 0, s, probs); break;
+    case DQ_FMT_MXFP4: hipLaunchKernelGGL((k_init_reduce<MXFP4>), grid, block, 0, s, probs); break;
+    default: hipLaunchKernelGGL((k_init_reduce<NVFP4>), grid, block, 0, s, probs); break;
+  }
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
@@ -442,6 +464,8 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
     rc = launch_init_any(spec.fmt, dt, dim3((unsigned)max_init, (unsigned)count), dprobs, s);
     if (rc) return rc;
   }
+  rc = launch_init_reduce_any(spec.fmt, count, dprobs, s);
+  if (rc) return rc;
 
   // optional per-kernel timing: a begin/end event pair attached to each pass's launches
   const bool timed = opts->pass_ms != nullptr && opts->pass_ms_capacity > 0;
@@ -477,7 +501,8 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
           const auto& G = pl.groups[gi];
           if (tm) {
             t_ev_start = gi == 0 ? e[2 * which] : nullptr;
-            t_ev_stop = gi + 1 == ng ? e[2 * which + 1] : nullptr;
+            // the third pair spans the finalize launches and the decision launch
+            t_ev_stop = (gi + 1 == ng && which < 2) ? e[2 * which + 1] : nullptr;
           }
           rc = which < 2 ? launch_pass_any(which, spec.fmt, g, G, dprobs,
                                            (const WgEntry*)(ws + G.row_off),
@@ -488,6 +513,10 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
           if (rc) { cleanup(); return rc; }
         }
       }
+      if (tm) t_ev_stop = e[5];
+      rc = launch_decide_any(spec.fmt, count, dprobs, s);
+      t_ev_start = t_ev_stop = nullptr;
+      if (rc) { cleanup(); return rc; }
     }
     if (hipStreamSynchronize(s) != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
     for (size_t k = ev0; k + 5 < ev.size(); k += 6) {
