@@ -385,6 +385,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
     for (int kk = 0; kk < nloop; ++kk) {
       const int chn = lane + 64 * kk;
       const bool valid = chn < nch;
+      const int cl = valid ? chn : 0;   // LDS reads stay in range; invalid lanes work on zeros
       const int j0 = 16 * chn;
       RawRow<DT> raw;
       if (valid) raw.load(P.W, i, P.ld, j0); else raw.zero();
@@ -401,11 +402,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         float v[16];
         {
           float icc[16];
-          if (valid) lds_load16(s_ic4, nch, chn, icc);
-          else {
-#pragma unroll
-            for (int k = 0; k < 16; ++k) icc[k] = 0.0f;
-          }
+          lds_load16(s_ic4, nch, cl, icc);
 #pragma unroll
           for (int k = 0; k < 16; ++k) v[k] = (w[k] * ir_) * icc[k];
         }
@@ -416,11 +413,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         f = ch.f;
 #pragma unroll
         for (int k = 0; k < 16; ++k) p[k] = ch.p[k];
-        if (valid) lds_load16(s_c4, nch, chn, cc);
-        else {
-#pragma unroll
-          for (int k = 0; k < 16; ++k) cc[k] = 0.0f;
-        }
+        lds_load16(s_c4, nch, cl, cc);
         const float rf = r_ * f;
         float Fl = 0.0f, ql = 0.0f;
 #pragma unroll
@@ -461,11 +454,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
       } else {
         decode_grid<FMT>(p0, p1, p);
         f = block_factor<FMT>(ps, tab_p);
-        if (valid) lds_load16(s_c4, nch, chn, cc);
-        else {
-#pragma unroll
-          for (int k = 0; k < 16; ++k) cc[k] = 0.0f;
-        }
+        lds_load16(s_c4, nch, cl, cc);
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const float pc = p[k] * cc[k];
