@@ -21,7 +21,6 @@ on this host.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -43,13 +42,6 @@ METRIC = "BCD solver Gelem/s per iteration + achieved HBM GB/s vs peak (4096×14
 KERNELS = ("k_rowpass", "k_colpass", "k_finalize")
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("dq_device.hpp", "dq_kernels.hpp"):
-        h.update((ROOT / "post_quantization_dq_amd" / "csrc" / f).read_bytes())
-    return h.hexdigest()[:16]
-
-
 def recorded_traffic(kernel: str, workload: str):
     """Counter-measured HBM bytes per launch of `kernel` from profiles/, if the counters were
     taken on the current kernel source."""
@@ -59,6 +51,8 @@ def recorded_traffic(kernel: str, workload: str):
     text = f.read_text()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    from post_quantization_dq_amd.profiling import kernel_source_hash
+
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))

@@ -1,6 +1,6 @@
 // HIP kernels of the DualQuant dual-scale BCD solver for gfx950.
 //
-// Each BCD iteration is four launches over all problems of a batch:
+// Each BCD iteration is three launches over all problems of a batch:
 //   k_rowpass   one wave per row (no workgroup barriers in the row loop); c and 1/c of every
 //               column sit in LDS.  It quantises the candidate Qc = FQ_f(W ./ r^s c^s^T)
 //               (Qhat-step of iteration s) and stores its codes, measures F(r^s,c^s,Qc), the
@@ -11,11 +11,10 @@
 //   k_colpass   workgroups own 1024-column strips and a range of rows; with the new r it
 //               accumulates the c-step sums N_j, D_j (and the NVFP4 column amax of W ./ r)
 //               in registers and writes one partial per row range.
-//   k_finalize  reduces the partials and projects c.
-//   k_decide    one workgroup per problem takes the safeguard decision and advances the
-//               per-problem state machine.  If the candidate is rejected the speculative
-//               r/c are discarded and the next iteration re-runs the r/c steps from the kept
-//               Qhat (FIXUP mode).
+//   k_finalize  reduces the partials and projects c; its first workgroup per problem takes
+//               the safeguard decision and writes the next sweep's state.  If the candidate
+//               is rejected the speculative r/c are discarded and the next iteration re-runs
+//               the r/c steps from the kept Qhat (FIXUP mode).
 // Lane l of a wave owns chunks of 16 consecutive columns; blocks of MX (32) and INT4
 // (64/128) formats span 2..8 adjacent lanes.
 
@@ -28,10 +27,12 @@ namespace dqk {
 
 enum Mode { MODE_INIT = 0, MODE_NORMAL = 1, MODE_FIXUP = 2, MODE_DONE = 3 };
 
+// Per-problem solver state.  It is double-buffered by sweep parity: the kernels of sweep sw
+// read st[sw & 1], and the decision at the end of sweep sw (k_finalize) writes the whole of
+// st[(sw + 1) & 1], so no kernel reads a state that is being written.
 struct alignas(16) State {
   int32_t mode, it_done, acc, rs;
-  int32_t cs, rejected, sweeps, pad0;
-  uint32_t flags, counter, init_counter, pad1;
+  int32_t cs, rejected, sweeps, needs_ts;   // needs_ts: NVFP4 tensor scale from fwp pending
   float st_cur, k6_cur, st_acc, pad2;
   double normW2, qn2_acc;
 };
@@ -49,7 +50,8 @@ struct ProbDev {
   double* swp;      // [rowblocks][4]: F(Qc), dF, relchg numerator, ||Qc||^2
   float* fwp;       // [fin_wgs]: NVFP4 amax partials
   double* initp;    // [init_wgs][2]
-  State* st;
+  State* st;        // [2], by sweep parity
+  uint32_t* flags;  // DQ_FLAG_* bits, set with atomics by any kernel
   double* nmse;     // [iters+1]
   double* relchg;   // [iters+1]
   float* r_trace;   // [iters][rows] or null: unprojected r-step values
@@ -139,12 +141,11 @@ __global__ void k_setup(const ProbDev* __restrict__ probs) {
     s->cs = 0;
     s->rejected = 0;
     s->sweeps = 0;
-    s->flags = 0;
-    s->counter = 0;
-    s->init_counter = 0;
+    s->needs_ts = 0;
     s->st_cur = s->k6_cur = s->st_acc = 0.0f;
     s->normW2 = 0.0;
     s->qn2_acc = 0.0;
+    *P.flags = 0u;
   }
 }
 
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(256) void k_init(const ProbDev* __restrict__ probs)
   if (threadIdx.x == 0) {
     gp(P.initp)[2 * blockIdx.x] = ((ss[0] + ss[1]) + ss[2]) + ss[3];
     gp(P.initp)[2 * blockIdx.x + 1] = (double)fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-    if (bad) atomicOr(&P.st->flags, 1u);
+    if (bad) atomicOr(P.flags, 1u);
   }
 }
 
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(256) void k_init_reduce(const ProbDev* __restrict__
     nv_tensor_terms(A, st_, k6_, tiny);
     s->st_cur = st_;
     s->k6_cur = k6_;
-    if (tiny) s->flags |= 16u;
+    if (tiny) atomicOr(P.flags, 16u);
   }
 }
 
@@ -326,10 +327,10 @@ struct PassInfo {
 // ---------------------------------------------------------------- row pass
 template <int FMT, int DT, int L>
 __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ probs,
-                                                  const WgEntry* __restrict__ table) {
+                                                  const WgEntry* __restrict__ table, int sw) {
   const WgEntry we = table[blockIdx.x];
   const ProbDev& P = probs[we.prob];
-  State* st = P.st;
+  State* st = P.st + (sw & 1);
   if (st->mode == MODE_DONE) return;
   const PassInfo pi(st, P.iters);
   constexpr bool A64 = (FMT == INT4);   // INT4: exact products accumulated in fp64
@@ -343,6 +344,33 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
   NvTab* tab_c = (NvTab*)(lds + 2 * n);
   NvTab* tab_p = tab_c + 1;
   __shared__ double redw[16][4];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, nw = (int)(blockDim.x >> 6);
+
+  // NVFP4 tensor scale of this sweep's candidate.  After a kept step it follows from the
+  // amax of W ./ r c^T at the new scales, i.e. from the finalize partials: every workgroup
+  // derives the same value, and the first one records it for the later kernels of the sweep.
+  float s_t = 0.0f, k6 = 0.0f;
+  if (FMT == NVFP4) {
+    s_t = st->st_cur;
+    k6 = st->k6_cur;
+    if (st->needs_ts) {
+      __shared__ float sa[16];
+      float a = 0.0f;
+      for (int k = t; k < P.fin_wgs; k += blockDim.x) a = fmaxf(a, gp(P.fwp)[k]);
+      a = wave_max(a);
+      if (lane == 0) sa[wave] = a;
+      __syncthreads();
+      a = sa[0];
+      for (int w = 1; w < nw; ++w) a = fmaxf(a, sa[w]);
+      bool tiny;
+      nv_tensor_terms(a, s_t, k6, tiny);
+      if (we.idx == 0 && t == 0) {
+        st->st_cur = s_t;
+        st->k6_cur = k6;
+        if (tiny) atomicOr(P.flags, 16u);
+      }
+    }
+  }
 
   {
     const DQ_GAS f32x4* c4 = gp((const f32x4*)P.c[pi.cs]);
@@ -353,13 +381,12 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
       s_ic4[q * nch + ch] = ic4[e];
     }
     if (FMT == NVFP4) {
-      build_nvtab(*tab_c, st->st_cur);
+      build_nvtab(*tab_c, s_t);
       build_nvtab(*tab_p, st->st_acc);
     }
   }
   __syncthreads();
 
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, nw = (int)(blockDim.x >> 6);
   const DQ_GAS float* rcur = gp(P.r[pi.rs]);
   const DQ_GAS float* ircur = gp(P.ir[pi.rs]);
   DQ_GAS float* rnext = gp(P.r[1 - pi.rs]);
@@ -369,7 +396,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
   const uint8_t* acodes = P.codes[pi.acc];
   const void* ascales = P.scales[pi.acc];
   QCtx qc;
-  qc.k6 = st->k6_cur;
+  qc.k6 = k6;
   qc.tab = tab_c;
 
   double aFc = 0.0, adF = 0.0, arel = 0.0, aqn = 0.0;
@@ -510,7 +537,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
       o[0] = s0; o[1] = s1; o[2] = s2; o[3] = s3;
     }
     const uint32_t fl = (anyu ? 8u : 0u) | (anyz ? 2u : 0u);
-    if (fl) atomicOr(&st->flags, fl);
+    if (fl) atomicOr(P.flags, fl);
   }
 }
 
@@ -521,10 +548,10 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
 // within 128 VGPRs (two workgroups per CU); INT4's fp64 accumulators need the wider budget.
 template <int FMT, int DT, int L>
 __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
-                                             const WgEntry* __restrict__ table) {
+                                             const WgEntry* __restrict__ table, int sw) {
   const WgEntry we = table[blockIdx.x];
   const ProbDev& P = probs[we.prob];
-  State* st = P.st;
+  const State* st = P.st + (sw & 1);
   if (st->mode == MODE_DONE) return;
   const PassInfo pi(st, P.iters);
   if (!pi.next) return;
@@ -636,28 +663,35 @@ __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
 
 template <int FMT, int DT, int L>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_colpass(
-    const ProbDev* __restrict__ probs, const WgEntry* __restrict__ table) {
-  colpass_body<FMT, DT, L>(probs, table);
+    const ProbDev* __restrict__ probs, const WgEntry* __restrict__ table, int sw) {
+  colpass_body<FMT, DT, L>(probs, table, sw);
 }
 
 template <int FMT, int DT, int L>
 __global__ __launch_bounds__(512) void k_colpass_wide(const ProbDev* __restrict__ probs,
-                                                      const WgEntry* __restrict__ table) {
-  colpass_body<FMT, DT, L>(probs, table);
+                                                      const WgEntry* __restrict__ table, int sw) {
+  colpass_body<FMT, DT, L>(probs, table, sw);
 }
 
 // ---------------------------------------------------------------- finalize
 // Column reduction of the row-range partials, c-step projection and the per-workgroup amax
-// for the next NVFP4 tensor scale.  A workgroup covers 64 columns with 4 threads per column; thread part p sums ranges p, p+4,
-// ... (sixteen loads in flight), and the four parts are added in part order.
+// for the next NVFP4 tensor scale.  A workgroup covers 64 columns with 4 threads per column;
+// thread part p sums ranges p, p+4, ... (sixteen loads in flight), and the four parts are
+// added in part order.  The first workgroup of each problem then takes the safeguard
+// decision from the row pass's partials (written by an earlier kernel) and writes the state
+// of the next sweep; the amax it cannot see yet is reduced by the next row pass.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ probs,
-                                                  const WgEntry* __restrict__ table) {
+                                                  const WgEntry* __restrict__ table, int sw) {
   const WgEntry we = table[blockIdx.x];
   const ProbDev& P = probs[we.prob];
-  State* st = P.st;
+  const State* st = P.st + (sw & 1);
+  State* sn = P.st + ((sw + 1) & 1);
   const int mode = st->mode;
-  if (mode == MODE_DONE) return;
+  if (mode == MODE_DONE) {   // carry a finished state forward to the next sweep's slot
+    if (we.idx == 0 && threadIdx.x == 0) *sn = *st;
+    return;
+  }
   const int it = (mode == MODE_INIT) ? 0 : st->it_done + 1;
   const bool next = (mode == MODE_FIXUP) || (it < P.iters);
   const int cs = st->cs;
@@ -666,6 +700,7 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   __shared__ double sred[2][4][64];   // [quantity][part][column]
   __shared__ float smax[4][64];
   __shared__ float wmax[1];
+  __shared__ double tr[4 * 256];
 
   const int t = threadIdx.x, col = t & 63, part = t >> 6;
   bool zcol = false;
@@ -731,25 +766,12 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   zcol = __syncthreads_or(zcol);
   if (t == 0) {
     if (next && FMT == NVFP4) gp(P.fwp)[we.idx] = wmax[0];
-    if (zcol) atomicOr(&st->flags, 4u);
+    if (zcol) atomicOr(P.flags, 4u);
   }
-}
+  if (we.idx != 0) return;
 
-// Safeguard decision and state update of each problem (one workgroup per problem, after
-// k_finalize): fixed-order reductions of the row pass's partials and of the amax partials,
-// strided per thread, then a pairwise tree over the 256 threads.
-template <int FMT>
-__global__ __launch_bounds__(256) void k_decide(const ProbDev* __restrict__ probs) {
-  const ProbDev& P = probs[blockIdx.x];
-  if (P.rows == 0 || P.cols == 0) return;
-  State* st = P.st;
-  const int mode = st->mode;
-  if (mode == MODE_DONE) return;
-  const int it = (mode == MODE_INIT) ? 0 : st->it_done + 1;
-  const bool next = (mode == MODE_FIXUP) || (it < P.iters);
-  const int t = threadIdx.x;
-  __shared__ double tr[4 * 256];
-  __shared__ float wmax[4];
+  // decision: fixed-order reductions of the row pass's partials, strided per thread, then a
+  // pairwise tree over the 256 threads
   double f[4] = {0.0, 0.0, 0.0, 0.0};
   if (mode != MODE_FIXUP) {
     for (int s = t; s < P.rowblocks; s += 256) {
@@ -757,14 +779,8 @@ __global__ __launch_bounds__(256) void k_decide(const ProbDev* __restrict__ prob
       f[0] += o[0]; f[1] += o[1]; f[2] += o[2]; f[3] += o[3];
     }
   }
-  float A = 0.0f;
-  if (next && FMT == NVFP4) {
-    for (int k = t; k < P.fin_wgs; k += 256) A = fmaxf(A, gp(P.fwp)[k]);
-  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) tr[q * 256 + t] = f[q];
-  A = wave_max(A);
-  if ((t & 63) == 0) wmax[t >> 6] = A;
   for (int w = 128; w >= 1; w >>= 1) {
     __syncthreads();
     if (t < w) {
@@ -775,88 +791,88 @@ __global__ __launch_bounds__(256) void k_decide(const ProbDev* __restrict__ prob
   __syncthreads();
   if (t != 0) return;
   const double Fc = tr[0], dF = tr[256], rel = tr[512], qn = tr[768];
-  A = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 
+  State ns = *st;
   const double nW = st->normW2;
   bool accepted = true;
   double relv = 0.0;
   if (mode == MODE_INIT) {
     if (P.nmse) P.nmse[0] = nW > 0.0 ? Fc / nW : 0.0;
     if (P.relchg) P.relchg[0] = 0.0;
-    st->acc = 0;
-    st->qn2_acc = qn;
-    st->st_acc = st->st_cur;
-    st->it_done = 0;
+    ns.acc = 0;
+    ns.qn2_acc = qn;
+    ns.st_acc = st->st_cur;
+    ns.it_done = 0;
   } else if (mode == MODE_NORMAL) {
     accepted = (dF <= 0.0);
     if (accepted) {
       relv = st->qn2_acc > 0.0 ? sqrt(rel) / sqrt(st->qn2_acc) : 0.0;
       if (P.nmse) P.nmse[it] = nW > 0.0 ? Fc / nW : 0.0;
-      st->acc = 1 - st->acc;
-      st->qn2_acc = qn;
-      st->st_acc = st->st_cur;
+      ns.acc = 1 - st->acc;
+      ns.qn2_acc = qn;
+      ns.st_acc = st->st_cur;
     } else {
-      st->rejected += 1;
+      ns.rejected += 1;
       if (P.nmse) P.nmse[it] = nW > 0.0 ? (Fc - dF) / nW : 0.0;
     }
     if (P.relchg) P.relchg[it] = relv;
-    st->it_done = it;
+    ns.it_done = it;
   }
   const bool stop = (mode != MODE_FIXUP) &&
                     (it >= P.iters || (mode == MODE_NORMAL && P.tol > 0.0f && relv <= (double)P.tol));
+  ns.needs_ts = 0;
   if (stop) {
-    st->mode = MODE_DONE;
+    ns.mode = MODE_DONE;
   } else if (accepted) {
-    st->rs = 1 - st->rs;
-    st->cs = 1 - st->cs;
-    if (FMT == NVFP4) {
-      float s_, k_;
-      bool tiny;
-      nv_tensor_terms(A, s_, k_, tiny);
-      st->st_cur = s_;
-      st->k6_cur = k_;
-      if (tiny) st->flags |= 16u;
-    }
-    st->mode = MODE_NORMAL;
+    ns.rs = 1 - st->rs;
+    ns.cs = 1 - st->cs;
+    ns.needs_ts = (FMT == NVFP4) ? 1 : 0;   // from this finalize's amax partials
+    ns.mode = MODE_NORMAL;
   } else {
-    st->mode = MODE_FIXUP;
+    ns.mode = MODE_FIXUP;
   }
-  st->sweeps += 1;
+  ns.sweeps += 1;
+  *sn = ns;
 }
 
 // ---------------------------------------------------------------- standalone quantiser
 // MODEV = 0: weights, v = (W * (1/r_i)) * (1/c_j);  MODEV = 1: activations, v = x * c_j.
-// Pass 1 (NVFP4 only): per-workgroup amax of v.
+// Pass 1 (NVFP4 only): per-workgroup amax of v.  Rounding is monotone, so the amax of a
+// column is fl(max_i |inner_ij| * s_j) with inner = fl(x * (1/r_i)) (weights) or x
+// (activations) and s_j = 1/c_j or c_j: each thread keeps the running column maxima of the
+// eight or four columns of one 16-byte vector over a range of rows and scales them once.
+// Workgroup = 256 vectors x a range of rows; blockIdx.x = strip + nstrips * range.
 template <int DT, int MODEV>
 __global__ __launch_bounds__(256) void k_qamax(const void* __restrict__ X, int64_t rows,
                                                int64_t cols, int64_t ld,
                                                const float* __restrict__ r,
                                                const float* __restrict__ c,
-                                               float* __restrict__ part) {
+                                               float* __restrict__ part, int nstrips,
+                                               int rows_per_range) {
   constexpr int VEC = (DT == 1) ? 8 : 4;   // elements per 16-byte load
   constexpr int U = 4;                      // loads in flight per thread
-  const int64_t rpb = (rows + gridDim.x - 1) / gridDim.x;
-  const int64_t r0 = (int64_t)blockIdx.x * rpb, r1 = min(rows, r0 + rpb);
+  const int strip = (int)(blockIdx.x % nstrips), rr = (int)(blockIdx.x / nstrips);
   const int64_t nv = cols / VEC;
+  const int64_t v = (int64_t)strip * 256 + threadIdx.x;
+  const int64_t r0 = (int64_t)rr * rows_per_range, r1 = min(rows, r0 + rows_per_range);
   const int64_t rowbytes = ld * (DT == 1 ? 2 : 4);
-  float m = 0.0f;
-  for (int64_t i = r0; i < r1; ++i) {
-    const float ir = (MODEV == 0 && r) ? 1.0f / gp(r)[i] : 1.0f;
-    const DQ_GAS u32x4* rowp = gp((const u32x4*)((const char*)X + i * rowbytes));
-    for (int64_t v0 = threadIdx.x; v0 < nv; v0 += (int64_t)blockDim.x * U) {
+  float cm[VEC];
+#pragma unroll
+  for (int k = 0; k < VEC; ++k) cm[k] = 0.0f;
+  if (v < nv) {
+    for (int64_t i0 = r0; i0 < r1; i0 += U) {
       u32x4 u[U];
+      float ir[U];
 #pragma unroll
       for (int q = 0; q < U; ++q) {
-        const int64_t v = v0 + (int64_t)q * blockDim.x;
-        if (v < nv) u[q] = rowp[v];
-        else u[q] = u32x4{0u, 0u, 0u, 0u};
+        const int64_t i = min(i0 + q, r1 - 1);   // clamped: a repeated row does not change a max
+        u[q] = gp((const u32x4*)((const char*)X + i * rowbytes))[v];
+        ir[q] = (MODEV == 0 && r) ? 1.0f / gp(r)[i] : 1.0f;
       }
 #pragma unroll
       for (int q = 0; q < U; ++q) {
-        const int64_t v = v0 + (int64_t)q * blockDim.x;
-        if (v >= nv) break;
-        float w[VEC];
         const uint32_t uu[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+        float w[VEC];
         if (DT == 1) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) { w[2 * k] = u2f(uu[k] << 16); w[2 * k + 1] = u2f(uu[k] & 0xFFFF0000u); }
@@ -865,17 +881,17 @@ __global__ __launch_bounds__(256) void k_qamax(const void* __restrict__ X, int64
           for (int k = 0; k < 4; ++k) w[k] = u2f(uu[k]);
         }
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-          float val = w[k];
-          if (MODEV == 0) {
-            const float ic = c ? 1.0f / gp(c)[v * VEC + k] : 1.0f;
-            val = (val * ir) * ic;
-          } else if (c) {
-            val = val * gp(c)[v * VEC + k];
-          }
-          m = fmaxf(m, fabsf(val));
-        }
+        for (int k = 0; k < VEC; ++k) cm[k] = fmaxf(cm[k], MODEV == 0 ? fabsf(w[k] * ir[q]) : fabsf(w[k]));
       }
+    }
+  }
+  float m = 0.0f;
+  if (v < nv) {
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+      float sj = 1.0f;
+      if (c) sj = (MODEV == 0) ? 1.0f / gp(c)[v * VEC + k] : fabsf(gp(c)[v * VEC + k]);
+      m = fmaxf(m, (MODEV == 0) ? fabsf(cm[k] * sj) : cm[k] * sj);
     }
   }
   m = wave_max(m);
@@ -900,7 +916,8 @@ __device__ __forceinline__ void load16_global(const float* p, bool aligned, floa
   }
 }
 
-// Pass 2: quantise; workgroup = H row slots x LPR lanes, one chunk per lane.
+// Pass 2: quantise; workgroup = H row slots x LPR lanes, one chunk per lane, looping over
+// row groups so the tensor-scale table is built once per workgroup.
 template <int FMT, int DT, int L, int MODEV>
 __global__ __launch_bounds__(1024) void k_quant(const void* __restrict__ X, int64_t rows,
                                                 int64_t cols, int64_t ld,
@@ -937,34 +954,38 @@ __global__ __launch_bounds__(1024) void k_quant(const void* __restrict__ X, int6
   }
   const int t = threadIdx.x;
   const int h = t / lpr, l = t - h * lpr;
-  const int64_t i = (int64_t)blockIdx.x * H + h;
-  const bool act = (l < (int)(cols >> 4)) && (i < rows);
-  const int j0 = l * 16;
-  float w[16], v[16];
-  RawRow<DT> raw;
-  if (act) raw.load(X, i, ld, j0); else raw.zero();
-  raw.unpack(w);
-  float cv[16];
-  if (act && c) {
+  const bool lane_ok = l < (int)(cols >> 4);
+  const int j0 = lane_ok ? l * 16 : 0;
+  float cv[16];   // c (or its reciprocal for weights) of this lane's columns, for every row
+  if (lane_ok && c) {
     load16_global(c + j0, ((uintptr_t)c & 15u) == 0, cv);
+    if (MODEV == 0) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) cv[k] = 1.0f / cv[k];
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < 16; ++k) cv[k] = 1.0f;
   }
-  if (MODEV == 0) {
-    const float ir = (act && r) ? 1.0f / gp(r)[i] : 1.0f;
+  // row groups of H rows, strided over the grid
+  for (int64_t i = (int64_t)blockIdx.x * H + h; i - h < rows; i += (int64_t)gridDim.x * H) {
+    const bool act = lane_ok && i < rows;
+    float w[16], v[16];
+    RawRow<DT> raw;
+    if (act) raw.load(X, i, ld, j0); else raw.zero();
+    raw.unpack(w);
+    if (MODEV == 0) {
+      const float ir = (act && r) ? 1.0f / gp(r)[i] : 1.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float ic = c ? 1.0f / cv[k] : 1.0f;
-      v[k] = (w[k] * ir) * ic;
+      for (int k = 0; k < 16; ++k) v[k] = (w[k] * ir) * cv[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = c ? w[k] * cv[k] : w[k];
     }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = c ? w[k] * cv[k] : w[k];
+    Chunk ch;
+    quantize_chunk<FMT, L>(v, qc, ch);
+    if (act) store_chunk<FMT, L>(codes, scales, i, cols, l, L * 16, ch);
   }
-  Chunk ch;
-  quantize_chunk<FMT, L>(v, qc, ch);
-  if (act) store_chunk<FMT, L>(codes, scales, i, cols, l, L * 16, ch);
 }
 
 // ---------------------------------------------------------------- dequantise

@@ -135,7 +135,7 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     d.fin_wgs = (int32_t)((d.cols + 63) / 64);
     d.init_wgs = (int32_t)std::min<int64_t>(1024, d.rows);
     pl.prob_off[k] = off;
-    off = align_up(off + sizeof(State));
+    off = align_up(off + 2 * sizeof(State) + sizeof(uint32_t));
     off = align_up(off + 4 * sizeof(float) * d.rows);                  // r[2], ir[2]
     off = align_up(off + 4 * sizeof(float) * d.cols);                  // c[2], ic[2]
     off = align_up(off + (size_t)d.rows * d.cols / 2);                 // codes buffer 1
@@ -170,7 +170,11 @@ void bind_pointers(const dq_problem* p, int32_t count, int g, int fmt, int iters
     ProbDev& d = pl.dev[k];
     char* q = ws + pl.prob_off[k];
     auto take = [&](size_t bytes) { char* r = q; q += align_up(bytes); return r; };
-    d.st = (State*)take(sizeof(State));
+    {
+      char* sp = take(2 * sizeof(State) + sizeof(uint32_t));
+      d.st = (State*)sp;
+      d.flags = (uint32_t*)(sp + 2 * sizeof(State));
+    }
     float* rr = (float*)take(4 * sizeof(float) * d.rows);
     d.r[0] = rr; d.r[1] = rr + d.rows; d.ir[0] = rr + 2 * d.rows; d.ir[1] = rr + 3 * d.rows;
     float* cc = (float*)take(4 * sizeof(float) * d.cols);
@@ -216,76 +220,86 @@ void launch_timed(K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s, 
 
 template <int FMT, int DT, int L>
 int launch_passes(const Plan::Group& G, const ProbDev* probs, const WgEntry* rtab,
-                  const WgEntry* ctab, hipStream_t s) {
+                  const WgEntry* ctab, hipStream_t s, int sw) {
   const size_t rl = rowpass_lds(FMT, G.cols);
-  if (rl > 64 * 1024 &&
-      hipFuncSetAttribute((const void*)k_rowpass<FMT, DT, L>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl) != hipSuccess)
-    return DQ_ERR_HIP;
   launch_timed(k_rowpass<FMT, DT, L>, dim3((unsigned)G.row.size()), dim3(kRowWaves * 64), rl, s,
-               probs, rtab);
+               probs, rtab, sw);
   if (hipGetLastError() != hipSuccess) return DQ_ERR_HIP;
   return DQ_OK;
 }
 
 template <int FMT, int DT, int L>
-int launch_colpass(const Plan::Group& G, const ProbDev* probs, const WgEntry* ctab, hipStream_t s) {
-  if (FMT == INT4) {
-    if (hipFuncSetAttribute((const void*)k_colpass_wide<FMT, DT, L>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)colpass_lds(FMT)) != hipSuccess)
-      return DQ_ERR_HIP;
+int launch_colpass(const Plan::Group& G, const ProbDev* probs, const WgEntry* ctab, hipStream_t s,
+                   int sw) {
+  if (FMT == INT4)
     launch_timed(k_colpass_wide<FMT, DT, L>, dim3((unsigned)G.col.size()), dim3(512),
-                 colpass_lds(FMT), s, probs, ctab);
-  }
+                 colpass_lds(FMT), s, probs, ctab, sw);
   else
     launch_timed(k_colpass<FMT, DT, L>, dim3((unsigned)G.col.size()), dim3(512), colpass_lds(FMT),
-                 s, probs, ctab);
+                 s, probs, ctab, sw);
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
 template <int FMT, int L>
 int launch_pass_dt(int which, const Plan::Group& G, const ProbDev* probs, const WgEntry* rtab,
-                   const WgEntry* ctab, hipStream_t s) {
+                   const WgEntry* ctab, hipStream_t s, int sw) {
   if (which == 0)
-    return G.dtype == DQ_F32 ? launch_passes<FMT, 0, L>(G, probs, rtab, ctab, s)
-                             : launch_passes<FMT, 1, L>(G, probs, rtab, ctab, s);
-  return G.dtype == DQ_F32 ? launch_colpass<FMT, 0, L>(G, probs, ctab, s)
-                           : launch_colpass<FMT, 1, L>(G, probs, ctab, s);
+    return G.dtype == DQ_F32 ? launch_passes<FMT, 0, L>(G, probs, rtab, ctab, s, sw)
+                             : launch_passes<FMT, 1, L>(G, probs, rtab, ctab, s, sw);
+  return G.dtype == DQ_F32 ? launch_colpass<FMT, 0, L>(G, probs, ctab, s, sw)
+                           : launch_colpass<FMT, 1, L>(G, probs, ctab, s, sw);
+}
+
+// Dynamic LDS limits of a group's pass kernels (set once per solve, before the launches).
+template <int FMT, int DT, int L>
+int prepare_passes(const Plan::Group& G) {
+  const size_t rl = rowpass_lds(FMT, G.cols);
+  if (rl > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)k_rowpass<FMT, DT, L>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl) != hipSuccess)
+    return DQ_ERR_HIP;
+  if (FMT == INT4 &&
+      hipFuncSetAttribute((const void*)k_colpass_wide<FMT, DT, L>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)colpass_lds(FMT)) != hipSuccess)
+    return DQ_ERR_HIP;
+  return DQ_OK;
+}
+
+int prepare_passes_any(int fmt, int g, const Plan::Group& G) {
+#define DQ_P(F, L) return G.dtype == DQ_F32 ? prepare_passes<F, 0, L>(G) : prepare_passes<F, 1, L>(G)
+  switch (fmt) {
+    case DQ_FMT_INT4:
+      if (g == 64) { DQ_P(INT4, 4); }
+      DQ_P(INT4, 8);
+    case DQ_FMT_MXINT4: DQ_P(MXINT4, 2);
+    case DQ_FMT_MXFP4: DQ_P(MXFP4, 2);
+    default: DQ_P(NVFP4, 1);
+  }
+#undef DQ_P
 }
 
 // which = 0: row pass, 1: column pass
 int launch_pass_any(int which, int fmt, int g, const Plan::Group& G, const ProbDev* probs,
-                    const WgEntry* rtab, const WgEntry* ctab, hipStream_t s) {
+                    const WgEntry* rtab, const WgEntry* ctab, hipStream_t s, int sw) {
   switch (fmt) {
     case DQ_FMT_INT4:
-      return g == 64 ? launch_pass_dt<INT4, 4>(which, G, probs, rtab, ctab, s)
-                     : launch_pass_dt<INT4, 8>(which, G, probs, rtab, ctab, s);
-    case DQ_FMT_MXINT4: return launch_pass_dt<MXINT4, 2>(which, G, probs, rtab, ctab, s);
-    case DQ_FMT_MXFP4: return launch_pass_dt<MXFP4, 2>(which, G, probs, rtab, ctab, s);
-    default: return launch_pass_dt<NVFP4, 1>(which, G, probs, rtab, ctab, s);
+      return g == 64 ? launch_pass_dt<INT4, 4>(which, G, probs, rtab, ctab, s, sw)
+                     : launch_pass_dt<INT4, 8>(which, G, probs, rtab, ctab, s, sw);
+    case DQ_FMT_MXINT4: return launch_pass_dt<MXINT4, 2>(which, G, probs, rtab, ctab, s, sw);
+    case DQ_FMT_MXFP4: return launch_pass_dt<MXFP4, 2>(which, G, probs, rtab, ctab, s, sw);
+    default: return launch_pass_dt<NVFP4, 1>(which, G, probs, rtab, ctab, s, sw);
   }
 }
 
 int launch_finalize_any(int fmt, const Plan::Group& G, const ProbDev* probs,
-                        const WgEntry* tab, hipStream_t s) {
+                        const WgEntry* tab, hipStream_t s, int sw) {
   dim3 grid((unsigned)G.fin.size()), block(256);
   switch (fmt) {
-    case DQ_FMT_INT4: launch_timed(k_finalize<INT4>, grid, block, 0, s, probs, tab); break;
-    case DQ_FMT_MXINT4: launch_timed(k_finalize<MXINT4>, grid, block, 0, s, probs, tab); break;
-    case DQ_FMT_MXFP4: launch_timed(k_finalize<MXFP4>, grid, block, 0, s, probs, tab); break;
-    default: launch_timed(k_finalize<NVFP4>, grid, block, 0, s, probs, tab); break;
-  }
-  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
-}
-
-int launch_decide_any(int fmt, int count, const ProbDev* probs, hipStream_t s) {
-  dim3 grid((unsigned)count), block(256);
-  switch (fmt) {
-    case DQ_FMT_INT4: launch_timed(k_decide<INT4>, grid, block, 0, s, probs); break;
-    case DQ_FMT_MXINT4: launch_timed(k_decide<MXINT4>, grid, block, 0, s, probs); break;
-    case DQ_FMT_MXFP4: launch_timed(k_decide<MXFP4>, grid, block, 0, s, probs); break;
-    default: launch_timed(k_decide<NVFP4>, grid, block, 0, s, probs); break;
+    case DQ_FMT_INT4: launch_timed(k_finalize<INT4>, grid, block, 0, s, probs, tab, sw); break;
+    case DQ_FMT_MXINT4: launch_timed(k_finalize<MXINT4>, grid, block, 0, s, probs, tab, sw); break;
+    case DQ_FMT_MXFP4: launch_timed(k_finalize<MXFP4>, grid, block, 0, s, probs, tab, sw); break;
+    default: launch_timed(k_finalize<NVFP4>, grid, block, 0, s, probs, tab, sw); break;
   }
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
@@ -317,18 +331,28 @@ int launch_init_any(int fmt, int dt, dim3 grid, const ProbDev* probs, hipStream_
   }
 }
 
-// Standalone quantiser (weights: MODEV 0; activations: MODEV 1).
+// Standalone quantiser (weights: MODEV 0; activations: MODEV 1).  The quantiser grid is
+// capped so each workgroup handles several row groups.
+constexpr int64_t kQuantGroupsMax = 1024;
 template <int FMT, int DT, int L, int MODEV>
 int launch_quant_t(const void* X, int64_t rows, int64_t cols, int64_t ld, const float* r,
                    const float* c, uint8_t* codes, void* scales, float* ts, float* part,
                    int nparts, hipStream_t s) {
-  if (FMT == NVFP4)
-    hipLaunchKernelGGL((k_qamax<DT, MODEV>), dim3(nparts), dim3(256), 0, s, X, rows, cols, ld,
-                       r, c, part);
-  int lpr = lanes_per_row(cols), H = row_slots(lpr);
-  hipLaunchKernelGGL((k_quant<FMT, DT, L, MODEV>), dim3((unsigned)((rows + H - 1) / H)),
-                     dim3(lpr * H), 0, s, X, rows, cols, ld, r, c, codes, scales, ts, part,
-                     nparts, lpr, H);
+  if (FMT == NVFP4) {
+    const int64_t nv = cols / (DT == DQ_F32 ? 4 : 8);
+    const int nstrips = (int)((nv + 255) / 256);
+    const int64_t ranges = std::max<int64_t>(1, std::min<int64_t>(rows, nparts / nstrips));
+    const int rpr = (int)((rows + ranges - 1) / ranges);
+    const int nwg = nstrips * (int)((rows + rpr - 1) / rpr);   // <= nparts
+    nparts = nwg;
+    hipLaunchKernelGGL((k_qamax<DT, MODEV>), dim3((unsigned)nwg), dim3(256), 0, s, X, rows, cols,
+                       ld, r, c, part, nstrips, rpr);
+  }
+  const int lpr = lanes_per_row(cols), H = row_slots(lpr);
+  const int64_t groups = (rows + H - 1) / H;
+  const unsigned grid = (unsigned)std::min<int64_t>(groups, kQuantGroupsMax);
+  hipLaunchKernelGGL((k_quant<FMT, DT, L, MODEV>), dim3(grid), dim3(lpr * H), 0, s, X, rows,
+                     cols, ld, r, c, codes, scales, ts, part, nparts, lpr, H);
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
@@ -467,6 +491,11 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
   rc = launch_init_reduce_any(spec.fmt, count, dprobs, s);
   if (rc) return rc;
 
+  for (auto& G : pl.groups) {
+    rc = prepare_passes_any(spec.fmt, g, G);
+    if (rc) return rc;
+  }
+
   // optional per-kernel timing: a begin/end event pair attached to each pass's launches
   const bool timed = opts->pass_ms != nullptr && opts->pass_ms_capacity > 0;
   std::vector<hipEvent_t> ev;
@@ -481,6 +510,7 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
     return true;
   };
   std::vector<State> hst(count);
+  std::vector<uint32_t> hflags(count, 0u);
   int pending = 1 + iters;   // INIT sweep + one sweep per iteration, if nothing is rejected
   // at most one extra (re-solve) sweep per rejected iteration
   const int max_sweeps = 2 * iters + 2;
@@ -490,7 +520,8 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
     if (launched + pending > max_sweeps) { cleanup(); return DQ_ERR_HIP; }
     launched += pending;
     const size_t ev0 = ev.size();
-    for (int sw = 0; sw < pending; ++sw) {
+    for (int q = 0; q < pending; ++q) {
+      const int sw = launched - pending + q;   // sweep index: selects the state slot
       const bool tm = timed && (int)(ev.size() / 6) < opts->pass_ms_capacity;
       hipEvent_t e[6] = {};
       if (tm)
@@ -501,22 +532,17 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
           const auto& G = pl.groups[gi];
           if (tm) {
             t_ev_start = gi == 0 ? e[2 * which] : nullptr;
-            // the third pair spans the finalize launches and the decision launch
-            t_ev_stop = (gi + 1 == ng && which < 2) ? e[2 * which + 1] : nullptr;
+            t_ev_stop = gi + 1 == ng ? e[2 * which + 1] : nullptr;
           }
           rc = which < 2 ? launch_pass_any(which, spec.fmt, g, G, dprobs,
                                            (const WgEntry*)(ws + G.row_off),
-                                           (const WgEntry*)(ws + G.col_off), s)
+                                           (const WgEntry*)(ws + G.col_off), s, sw)
                          : launch_finalize_any(spec.fmt, G, dprobs,
-                                               (const WgEntry*)(ws + G.fin_off), s);
+                                               (const WgEntry*)(ws + G.fin_off), s, sw);
           t_ev_start = t_ev_stop = nullptr;
           if (rc) { cleanup(); return rc; }
         }
       }
-      if (tm) t_ev_stop = e[5];
-      rc = launch_decide_any(spec.fmt, count, dprobs, s);
-      t_ev_start = t_ev_stop = nullptr;
-      if (rc) { cleanup(); return rc; }
     }
     if (hipStreamSynchronize(s) != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
     for (size_t k = ev0; k + 5 < ev.size(); k += 6) {
@@ -530,7 +556,11 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
     pending = 0;
     for (int k = 0; k < count; ++k) {
       if (pl.group_of[k] < 0) continue;
-      if (hipMemcpy(&hst[k], pl.dev[k].st, sizeof(State), hipMemcpyDeviceToHost) != hipSuccess) {
+      // the decision of the last sweep launched wrote the slot of sweep `launched`
+      if (hipMemcpy(&hst[k], pl.dev[k].st + (launched & 1), sizeof(State),
+                    hipMemcpyDeviceToHost) != hipSuccess ||
+          hipMemcpy(&hflags[k], pl.dev[k].flags, sizeof(uint32_t), hipMemcpyDeviceToHost) !=
+              hipSuccess) {
         cleanup();
         return DQ_ERR_HIP;
       }
@@ -556,7 +586,7 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
                             hipMemcpyDeviceToDevice, s));
     }
     if (spec.fmt == DQ_FMT_NVFP4)
-      DQ_HIP(hipMemcpyAsync(problems[k].tensor_scale, &d.st->st_acc, sizeof(float),
+      DQ_HIP(hipMemcpyAsync(problems[k].tensor_scale, &d.st[launched & 1].st_acc, sizeof(float),
                             hipMemcpyDeviceToDevice, s));
   }
   DQ_HIP(hipStreamSynchronize(s));
@@ -564,7 +594,7 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
     if (!problems[k].report) continue;
     if (pl.group_of[k] < 0) { *problems[k].report = dq_report{iters, 0, 0u, 0}; continue; }
     const State& S = hst[k];
-    *problems[k].report = dq_report{S.it_done, S.rejected, S.flags, S.sweeps};
+    *problems[k].report = dq_report{S.it_done, S.rejected, hflags[k], S.sweeps};
   }
   return DQ_OK;
 }
