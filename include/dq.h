@@ -90,7 +90,14 @@ typedef struct {
                           and end) */
   int32_t pass_ms_capacity;  /* sweeps that fit in pass_ms (3 floats each) */
   int32_t pass_ms_count;     /* out: sweeps written */
+  int32_t scale_steps;  /* which scale steps run: DQ_STEP_ROW | DQ_STEP_COL, 0 = both.  With
+                           one bit the other scale vector stays at its initial value and its
+                           trace rows stay NaN (the news summary's ablation: row scales only
+                           or column scales only) */
 } dq_solve_opts;
+
+#define DQ_STEP_ROW 1
+#define DQ_STEP_COL 2
 
 typedef struct {
   int32_t iters_run;       /* iterations completed */

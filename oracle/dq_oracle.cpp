@@ -467,8 +467,9 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
             int iters, float tol, const float* r_init, const float* c_init, float* r_out,
             float* c_out, uint8_t* codes, void* scales, float* tscale, double* nmse_hist,
             double* relchg_hist, int* rejected_out, int* iters_run, float* r_trace,
-            float* c_trace, uint32_t* flags_out) {
+            float* c_trace, uint32_t* flags_out, int steps) {
   if (!W || !r_out || !c_out || !codes || !scales) return ERR_NULL;
+  if (steps < 0 || steps > 3) return ERR_SHAPE;
   if (!group_ok(fmt, g)) return ERR_FORMAT;
   if (rows < 0 || cols < 0 || cols % g || ld < cols || iters < 0) return ERR_SHAPE;
   if (fmt == FMT_NVFP4 && !tscale) return ERR_NULL;
@@ -505,7 +506,8 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
 
   std::vector<double> rowN(rows), rowD(rows), colN(cols), colD(cols);
   for (int t = 1; t <= iters; ++t) {
-    // r-step
+    // r-step (skipped, r kept, when the row scales are frozen)
+    if (steps & 1) {
     parallel_rows(rows, [&](int64_t b, int64_t e) {
       for (int64_t i = b; i < e; ++i) {
         double n_ = 0.0, d_ = 0.0;
@@ -526,7 +528,10 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
       }
       if (r_trace) r_trace[(int64_t)(t - 1) * rows + i] = x;
     }
-    // c-step (loop interchanged per column range; each column still sums rows in order)
+    }
+    // c-step (loop interchanged per column range; each column still sums rows in order);
+    // skipped, c kept, when the column scales are frozen
+    if (steps & 2) {
     parallel_rows(cols, [&](int64_t jb, int64_t je) {
       for (int64_t j = jb; j < je; ++j) { colN[j] = 0.0; colD[j] = 0.0; }
       for (int64_t i = 0; i < rows; ++i) {
@@ -546,6 +551,7 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
         c[j] = project(fmt, x);
       }
       if (c_trace) c_trace[(int64_t)(t - 1) * cols + j] = x;
+    }
     }
     // Q-step with safeguard
     normalise(Wf.data(), rows, cols, r.data(), c.data(), V.data());

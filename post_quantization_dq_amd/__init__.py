@@ -36,10 +36,13 @@ class dq_quant_spec(C.Structure):
     _fields_ = [("fmt", C.c_int32), ("group", C.c_int32)]
 
 
+DQ_STEP_ROW, DQ_STEP_COL = 1, 2   # dq_solve_opts.scale_steps bits (0 = both)
+
+
 class dq_solve_opts(C.Structure):
     _fields_ = [("iters", C.c_int32), ("tol_relchg", C.c_float),
                 ("pass_ms", C.POINTER(C.c_float)), ("pass_ms_capacity", C.c_int32),
-                ("pass_ms_count", C.c_int32)]
+                ("pass_ms_count", C.c_int32), ("scale_steps", C.c_int32)]
 
 
 class dq_report(C.Structure):
@@ -221,12 +224,14 @@ def make_problem(W: torch.Tensor, fmt: str, iters: int, group: int | None = None
 
 
 def solve_many(problems, fmt: str, iters: int, group: int | None = None, tol: float = 0.0,
-               stream=None, workspace: torch.Tensor | None = None, pass_ms: list | None = None):
+               stream=None, workspace: torch.Tensor | None = None, pass_ms: list | None = None,
+               steps: int = 0):
     """Solve a batch of problems.  `workspace` may be passed in to reuse one allocation;
     when `pass_ms` is a list it receives one (row pass, column pass, finalize) tuple of
-    event-timed durations in ms per sweep over W."""
+    event-timed durations in ms per sweep over W.  `steps` selects the scale steps
+    (DQ_STEP_ROW | DQ_STEP_COL; 0 = both)."""
     spec = spec_of(fmt, group)
-    opts = dq_solve_opts(int(iters), float(tol), None, 0, 0)
+    opts = dq_solve_opts(int(iters), float(tol), None, 0, 0, int(steps))
     buf = None
     if pass_ms is not None:
         cap = 2 * int(iters) + 2
@@ -246,11 +251,11 @@ def solve_many(problems, fmt: str, iters: int, group: int | None = None, tol: fl
 
 
 def solve(W: torch.Tensor, fmt: str, iters: int, group: int | None = None, r_init=None,
-          c_init=None, tol: float = 0.0, trace: bool = False, stream=None) -> dict:
+          c_init=None, tol: float = 0.0, trace: bool = False, stream=None, steps: int = 0) -> dict:
     """Run the solve on one matrix; returns the output tensors and the report.  With
     trace=True, r_trace / c_trace hold every iteration's unprojected closed forms."""
     p = make_problem(W, fmt, iters, group, r_init, c_init, trace)
-    rep = solve_many([p], fmt, iters, group, tol, stream)[0]
+    rep = solve_many([p], fmt, iters, group, tol, stream, steps=steps)[0]
     k = rep.iters_run
     return dict(r=p.r, c=p.c, codes=p.codes, scales=p.block_scales, tscale=p.tensor_scale,
                 nmse=p.nmse_hist[:k + 1], relchg=p.relchg_hist[:k + 1],

@@ -62,7 +62,8 @@ struct ProbDev {
   int32_t nstrips, rranges, rows_per_range, init_wgs; // column pass: 1024-column strips x row ranges
   int32_t dtype;
   float tol;
-  int32_t pad[2];
+  int32_t steps;   // scale steps that run: bit 0 row scales, bit 1 column scales
+  int32_t pad;
 };
 
 struct WgEntry {
@@ -468,7 +469,9 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
             const float ppc = pp[k] * cc[k];
             const float ep = fmaf(-rfp, ppc, w[k]);
             Fpl = fmaf(ep, ep, Fpl);
-            const float df = fmaf(p[k], f, -(pp[k] * fp));
+            // difference of the two dequantised values, each rounded to fp32 as the
+            // values themselves are: exactly 0 where Qhat did not change
+            const float df = p[k] * f - pp[k] * fp;
             rl = fmaf(df, df, rl);
           }
         }
@@ -508,12 +511,13 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
       // r-step of the next iteration from the whole row (fixed butterfly order in fp64)
       const double N = wave_sum(Nrow), D = wave_sum(Drow);
       if (lane == 0) {
-        float x = __builtin_nanf(""), rnew;
-        if (D > 0.0) {
+        float x = __builtin_nanf(""), rnew = r_;
+        if (!(P.steps & 1)) {
+          // row scales frozen: r is kept and no closed form is recorded
+        } else if (D > 0.0) {
           x = (float)(N / D);
           rnew = project<FMT>(x);
         } else {
-          rnew = r_;
           zrow = true;
         }
         rnext[i] = rnew;
@@ -745,7 +749,9 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
       M = fmaxf(fmaxf(smax[0][col], smax[1][col]), fmaxf(smax[2][col], smax[3][col]));
       float x = __builtin_nanf("");
       float cnew;
-      if (D > 0.0) {
+      if (!(P.steps & 2)) {   // column scales frozen: c is kept
+        cnew = gp(P.c[cs])[j];
+      } else if (D > 0.0) {
         x = (float)(N / D);
         cnew = project<FMT>(x);
       } else {

@@ -406,6 +406,7 @@ static int validate_solve(const dq_problem* p, int32_t count, dq_quant_spec spec
   int g = resolve_group(spec);
   if (g < 0) return DQ_ERR_FORMAT;
   if (o->iters < 0 || !(o->tol_relchg >= 0.0f)) return DQ_ERR_ARG;
+  if (o->scale_steps < 0 || o->scale_steps > (DQ_STEP_ROW | DQ_STEP_COL)) return DQ_ERR_ARG;
   for (int k = 0; k < count; ++k) {
     int rc = check_matrix(p[k].W, p[k].w_dtype, p[k].rows, p[k].cols, p[k].ld, g);
     if (rc) return rc;
@@ -442,7 +443,10 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   bind_pointers(problems, count, g, spec.fmt, opts->iters, ws, pl);
-  for (auto& d : pl.dev) d.tol = opts->tol_relchg;
+  for (auto& d : pl.dev) {
+    d.tol = opts->tol_relchg;
+    d.steps = opts->scale_steps ? opts->scale_steps : (DQ_STEP_ROW | DQ_STEP_COL);
+  }
   const int iters = opts->iters;
 
   // empty problems: zero histories, report immediately

@@ -197,3 +197,19 @@ def test_early_stop_and_degenerate(oracle_lib):
     Wf[3, 5] = np.nan
     got = _gpu_solve(Wf, "NVFP4", 1)
     assert got["flags"] & 1
+
+
+@pytest.mark.parametrize("steps", [1, 2])
+@pytest.mark.parametrize("name,rows,cols,iters", [("w256x512_int4", 256, 512, 16),
+                                                  ("down4096x14336_nvfp4", 197, 9216, 12),
+                                                  ("k1024x4096_mxint4", 129, 2048, 8)])
+def test_scale_step_ablation(oracle_lib, steps, name, rows, cols, iters):
+    """Row scales only / column scales only, against the oracle."""
+    w = synth.WORKLOADS[name]
+    W = synth.matrix(w["W"].scaled(rows, cols), 0)
+    ref = oracle_lib.solve(W, w["fmt"], iters, steps=steps)
+    got = _gpu_solve(W, w["fmt"], iters, trace=True, steps=steps)
+    _compare_e2e(oracle_lib, ref, got, w["fmt"], f"{name} steps={steps}", iters)
+    frozen = {1: ["c"], 2: ["r"]}[steps]
+    for v in frozen:
+        assert np.all(got[v] == 1.0), v

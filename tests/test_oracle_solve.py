@@ -110,6 +110,34 @@ def test_monotone_and_no_worse_than_single_scale(oracle_lib, name, rows, cols):
     assert last_change <= 22
 
 
+@pytest.mark.parametrize("name,rows,cols", SMALL[:3])
+def test_scale_step_ablation(oracle_lib, name, rows, cols):
+    """Row scales only / column scales only (the news summary's ablation).  With no scale
+    step the solve is the single-scale quantisation, repeated: every candidate equals the
+    start.  With one step the other scale vector never moves, the history is still
+    monotone and no worse than the start, and the running step is still the exact
+    constrained minimiser of its objective (the frozen one is not)."""
+    W, fmt = _workload_small(name, rows, cols)
+    base = oracle_lib.solve(W, fmt, 0)
+    none = oracle_lib.solve(W, fmt, 6, steps=0)
+    assert np.all(none["nmse"] == none["nmse"][0]) and none["nmse"][0] == base["nmse"][0]
+    assert np.array_equal(none["codes"], base["codes"]) and none["rejected"] == 0
+    assert np.all(none["r"] == 1) and np.all(none["c"] == 1)
+    assert np.all(np.isnan(none["r_trace"])) and np.all(np.isnan(none["c_trace"]))
+    for steps, moving, frozen in ((1, "r", "c"), (2, "c", "r")):
+        res = oracle_lib.solve(W, fmt, 12, steps=steps)
+        assert np.all(res[frozen] == 1), (steps, frozen)
+        assert np.all(np.isnan(res[frozen + "_trace"]))
+        assert not np.all(np.isnan(res[moving + "_trace"]))
+        assert np.all(np.diff(res["nmse"]) <= 0.0)
+        assert res["nmse"][-1] <= res["nmse"][0]
+    # the first row-only iteration equals the first dual iteration's r-step
+    one_r = oracle_lib.solve(W, fmt, 1, steps=1)
+    one = oracle_lib.solve(W, fmt, 1)
+    assert np.array_equal(one_r["r"], one["r"]) and np.array_equal(
+        one_r["r_trace"], one["r_trace"], equal_nan=True)
+
+
 def test_history_recomputed_from_outputs(oracle_lib):
     W, fmt = _workload_small("down4096x14336_nvfp4", 64, 512)
     Wf = synth.bf16_bits_to_f32(W).astype(np.float64)
