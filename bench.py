@@ -16,6 +16,7 @@ on this host.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
   python bench.py --copy-calibration     # plain copy of known size, for counter scaling
+  python bench.py --workload llama31_8b_nvfp4 --steps 3 --warmup 1   # the batched 224-matrix set
 """
 
 from __future__ import annotations
@@ -87,6 +88,60 @@ def cpu_baseline(W, X, fmt, iters):
                       f"plus the {X.shape[0]}x{n} activation quantise ({dt:.1f} s on {cores} threads)"}
 
 
+def bench_llama_set(args):
+    """The batched synthetic Llama-3.1-8B projection set (224 matrices, NVFP4, T = 20) as one
+    dq_solve call; weights drawn on the GPU (the set is 14 GB)."""
+    import torch
+
+    import post_quantization_dq_amd as dq
+    import synth
+
+    dev = torch.device("cuda:0")
+    T = 20
+    probs = []
+    for layer in range(synth.LLAMA31_8B_LAYERS):
+        for pi in range(len(synth.LLAMA31_8B_PROJ)):
+            W = synth.matrix_device(synth.llama_projection_spec(layer, pi), 0, dev)
+            probs.append(dq.make_problem(W, "NVFP4", T))
+    elems = sum(p.W.numel() for p in probs)
+    print(f"[bench] llama31_8b_nvfp4: {len(probs)} matrices, {elems / 1e9:.2f} G bf16 weights, T={T}", flush=True)
+    spec = dq.spec_of("NVFP4", None)
+    ws = torch.empty(dq.dq_workspace_bytes(probs, spec, dq.dq_solve_opts(T, 0.0, None, 0, 0)),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        dq.solve_many(probs, "NVFP4", T, workspace=ws)
+    torch.cuda.synchronize()
+    passes = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(args.steps):
+        dq.solve_many(probs, "NVFP4", T, workspace=ws, pass_ms=passes if k == args.steps - 1 else None)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    per = np.asarray(passes, dtype=np.float64).reshape(-1, 3)
+    avg = {k: float(per[:, q].mean()) for q, k in enumerate(KERNELS)}
+    dom = max(KERNELS[:2], key=lambda k: float(per[:, KERNELS.index(k)].sum()))
+    alg_bytes = elems * 2 + 8 * sum(p.W.shape[0] + p.W.shape[1] for p in probs)
+    achieved = alg_bytes / (avg[dom] * 1e-3) / 1e9
+    out = {
+        "metric": "BCD solver Gelem/s per iteration (batched Llama-3.1-8B projection set, NVFP4)",
+        "value": round(elems * T / (ms_step * 1e-3) / 1e9, 3), "unit": "Gelem/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "224 Llama-3.1-8B-shaped projections (32 layers x q,k,v,o,gate,up,down), "
+                               "bf16 Student-t nu=4 std 0.02, 1% outlier columns x15, NVFP4, 20 BCD "
+                               "iterations, one batched dq_solve", "elements": elems, "iters": T},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(avg[dom], 4),
+                     "launches": int(per.shape[0])},
+        "kernel_avg_us": {k: round(avg[k] * 1e3, 1) for k in KERNELS},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +158,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload == "llama31_8b_nvfp4":
+        bench_llama_set(args)
         return
 
     import torch

@@ -69,6 +69,10 @@ constexpr int kRowWaves = 16;
 constexpr int kTargetRowWaves = 256 * kRowWaves;
 // Column pass: workgroups of 8 waves on a 1024-column strip; about one per CU.
 constexpr int kTargetColWgs = 256;
+// Caps for large batches: many workgroups of bounded size keep the last wave of workgroups
+// short; a single projection-sized matrix stays below both.
+constexpr int64_t kMaxRowsPerBlk = 256;
+constexpr int64_t kMaxRowsPerRange = 512;
 // Standalone quantiser geometry: one chunk per lane, up to 1024 threads.
 int lanes_per_row(int64_t cols) { return (int)std::max<int64_t>(64, (cols / 16 + 63) / 64 * 64); }
 int row_slots(int lpr) { return std::max(1, 1024 / lpr); }
@@ -125,12 +129,14 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     d.dtype = p[k].w_dtype;
     if (pl.group_of[k] < 0) continue;
     Plan::Group& G = pl.groups[pl.group_of[k]];
-    d.rows_per_blk = (int32_t)(kRowWaves * rows_per_wave);
+    // row blocks: one wave per row, at most kMaxRowsPerBlk rows per workgroup so a large batch
+    // splits into many similar workgroups (balanced tail)
+    d.rows_per_blk = (int32_t)std::min<int64_t>(kMaxRowsPerBlk, kRowWaves * rows_per_wave);
     d.rowblocks = (int32_t)((d.rows + d.rows_per_blk - 1) / d.rows_per_blk);
     d.nstrips = (int32_t)((d.cols / 16 + 63) / 64);
     int64_t want = (kTargetColWgs * d.rows + total_rows - 1) / total_rows;   // this matrix's share
     int64_t rr = std::max<int64_t>(1, std::min<int64_t>(d.rows, (want + d.nstrips - 1) / d.nstrips));
-    d.rows_per_range = (int32_t)((d.rows + rr - 1) / rr);
+    d.rows_per_range = (int32_t)std::min<int64_t>(kMaxRowsPerRange, (d.rows + rr - 1) / rr);
     d.rranges = (int32_t)((d.rows + d.rows_per_range - 1) / d.rows_per_range);
     d.fin_wgs = (int32_t)((d.cols + 63) / 64);
     d.init_wgs = (int32_t)std::min<int64_t>(1024, d.rows);

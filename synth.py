@@ -135,6 +135,37 @@ def llama_projection_spec(layer: int, proj_index: int) -> MatrixSpec:
                       outlier_scale=15.0, stream=100 + 7 * layer + proj_index)
 
 
+def matrix_device(spec: MatrixSpec, seed: int, device):
+    """The same recipe drawn on a GPU with torch's seeded generator (its own random stream,
+    not the numpy draws above): for large batches whose members are checked by properties
+    rather than against the oracle.  Returns a bf16 (or fp32) torch tensor on `device`."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed((int(seed) * 1_000_003 + int(spec.stream)) & 0x7FFFFFFFFFFF)
+    shape = (spec.rows, spec.cols)
+    if spec.dist == "normal":
+        x = torch.randn(shape, generator=gen, device=device) * spec.std
+    elif spec.dist == "student_t":
+        z = torch.randn(shape, generator=gen, device=device)
+        chi2 = torch.zeros(shape, device=device)
+        for _ in range(int(spec.nu)):   # chi-square with nu degrees of freedom
+            chi2 += torch.randn(shape, generator=gen, device=device) ** 2
+        x = z / torch.sqrt(chi2 / spec.nu) * (spec.std / math.sqrt(spec.nu / (spec.nu - 2.0)))
+        del z, chi2
+    elif spec.dist == "laplace":
+        u = torch.rand(shape, generator=gen, device=device) - 0.5
+        x = -torch.sign(u) * torch.log1p(-2.0 * u.abs()) * (spec.std / math.sqrt(2.0))
+    else:
+        raise ValueError(f"unknown distribution {spec.dist!r}")
+    if spec.outliers:
+        cg = torch.Generator()
+        cg.manual_seed((int(seed) * 1_000_003 + int(spec.stream) + 1_000_003) & 0x7FFFFFFFFFFF)
+        cols = torch.randperm(spec.cols, generator=cg)[:spec.outliers].to(device)
+        x[:, cols] *= spec.outlier_scale
+    return x.to(torch.bfloat16 if spec.dtype == "bf16" else torch.float32).contiguous()
+
+
 def workload(name: str, seed: int = 0):
     """(W, X or None, fmt, group, iters) for a named workload."""
     w = WORKLOADS[name]
