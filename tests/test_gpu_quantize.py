@@ -84,3 +84,30 @@ def test_empty_inputs():
     gc, gs, gt = dq.quantize_weights(W, None, None, "NVFP4")
     torch.cuda.synchronize()
     assert gc.numel() == 0
+
+
+def test_k_proj_activation_sqnr(oracle_lib):
+    """The k_proj workload end to end: solve W (MXINT4, T = 16) on the GPU, rescale the
+    2048-token activations by the solved column scales and MXINT4-quantise them.  The
+    activation codes must equal the oracle's for the same c, and the activation-domain
+    SQNR (with and without the column scales) is reported."""
+    W, X, fmt, g, T = synth.workload("k1024x4096_mxint4")
+    res = dq.solve(to_dev(W), fmt, T)
+    torch.cuda.synchronize()
+    c = res["c"]
+    ref = oracle_lib.solve(W, fmt, T)
+    assert np.array_equal(c.cpu().numpy(), ref["c"])
+    Xd = to_dev(X)
+    out = {}
+    for label, cv in (("with beta", c), ("without beta", None)):
+        codes, scales, ts = dq.rescale_quantize_acts(Xd, cv, fmt)
+        torch.cuda.synchronize()
+        cn = None if cv is None else cv.cpu().numpy()
+        rcodes, rscales, rts, _ = oracle_lib.rescale_quantize_acts(X, cn, fmt)
+        assert np.array_equal(codes.cpu().numpy(), rcodes)
+        assert np.array_equal(scales_np(scales, fmt), rscales)
+        out[label] = oracle_lib.act_sqnr(X, cn, codes.cpu().numpy(), scales_np(scales, fmt),
+                                         float(ts.item()), fmt)
+        assert np.isfinite(out[label])
+    print(f"[sqnr] k_proj MXINT4 activation SQNR: {out['with beta']:.3f} dB with the column "
+          f"scales, {out['without beta']:.3f} dB without", flush=True)
