@@ -22,8 +22,14 @@ _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "dq_oracle.cpp"
 _LIB_PATH = _HERE / "_build" / "libdq_oracle.so"
 
-FMT = {"INT4": 0, "MXINT4": 1, "MXFP4": 2, "NVFP4": 3}
-DEFAULT_GROUP = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16}
+FMT = {"INT4": 0, "MXINT4": 1, "MXFP4": 2, "NVFP4": 3, "INT8": 4, "MXINT8": 5}
+DEFAULT_GROUP = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16, "INT8": 128, "MXINT8": 32}
+CODE_BITS = {"INT4": 4, "MXINT4": 4, "MXFP4": 4, "NVFP4": 4, "INT8": 8, "MXINT8": 8}
+
+
+def code_bytes(rows: int, cols: int, fmt: str) -> int:
+    """Bytes of packed element codes: two per byte for the 4-bit formats, one for 8-bit."""
+    return rows * cols * CODE_BITS[fmt] // 8
 
 
 def build(force: bool = True) -> Path:
@@ -100,7 +106,7 @@ def _w_dtype(W: np.ndarray) -> int:
 
 
 def _scale_dtype(fmt: str):
-    return np.uint16 if fmt == "INT4" else np.uint8
+    return np.uint16 if fmt in ("INT4", "INT8") else np.uint8
 
 
 # ------------------------------------------------------------------ scalar rounding
@@ -160,7 +166,7 @@ def fq(V: np.ndarray, fmt: str, group: int | None = None):
     group = group or DEFAULT_GROUP[fmt]
     V = np.ascontiguousarray(V, dtype=np.float32)
     rows, cols = V.shape
-    codes = np.zeros(rows * cols // 2, dtype=np.uint8)
+    codes = np.zeros(code_bytes(rows, cols, fmt), dtype=np.uint8)
     scales = np.zeros(rows * cols // group, dtype=_scale_dtype(fmt))
     ts = np.zeros(1, dtype=np.float32)
     qhat = np.zeros((rows, cols), dtype=np.float32)
@@ -177,7 +183,7 @@ def quantize_weights(W: np.ndarray, r, c, fmt: str, group: int | None = None):
     rows, cols = W.shape
     r = None if r is None else np.ascontiguousarray(r, dtype=np.float32)
     c = None if c is None else np.ascontiguousarray(c, dtype=np.float32)
-    codes = np.zeros(rows * cols // 2, dtype=np.uint8)
+    codes = np.zeros(code_bytes(rows, cols, fmt), dtype=np.uint8)
     scales = np.zeros(rows * cols // group, dtype=_scale_dtype(fmt))
     ts = np.zeros(1, dtype=np.float32)
     qhat = np.zeros((rows, cols), dtype=np.float32)
@@ -212,7 +218,7 @@ def solve(W: np.ndarray, fmt: str, iters: int, group: int | None = None, r_init=
     ci = None if c_init is None else np.ascontiguousarray(c_init, dtype=np.float32)
     r = np.zeros(rows, dtype=np.float32)
     c = np.zeros(cols, dtype=np.float32)
-    codes = np.zeros(rows * cols // 2, dtype=np.uint8)
+    codes = np.zeros(code_bytes(rows, cols, fmt), dtype=np.uint8)
     scales = np.zeros(rows * cols // group, dtype=_scale_dtype(fmt))
     ts = np.zeros(1, dtype=np.float32)
     nmse = np.zeros(iters + 1, dtype=np.float64)
@@ -239,7 +245,7 @@ def rescale_quantize_acts(X: np.ndarray, c, fmt: str, group: int | None = None):
     X = np.ascontiguousarray(X, dtype=np.uint16)
     tokens, cols = X.shape
     c = None if c is None else np.ascontiguousarray(c, dtype=np.float32)
-    codes = np.zeros(tokens * cols // 2, dtype=np.uint8)
+    codes = np.zeros(code_bytes(tokens, cols, fmt), dtype=np.uint8)
     scales = np.zeros(tokens * cols // group, dtype=_scale_dtype(fmt))
     ts = np.zeros(1, dtype=np.float32)
     xq = np.zeros((tokens, cols), dtype=np.float32)

@@ -29,7 +29,12 @@
 
 namespace {
 
-enum Fmt { FMT_INT4 = 0, FMT_MXINT4 = 1, FMT_MXFP4 = 2, FMT_NVFP4 = 3 };
+enum Fmt { FMT_INT4 = 0, FMT_MXINT4 = 1, FMT_MXFP4 = 2, FMT_NVFP4 = 3, FMT_INT8 = 4, FMT_MXINT8 = 5 };
+
+// Element code width: 4 bits (two per byte) or 8 bits (one per byte).
+int code_bits(int fmt) { return (fmt == FMT_INT8 || fmt == FMT_MXINT8) ? 8 : 4; }
+bool is_mx(int fmt) { return fmt == FMT_MXINT4 || fmt == FMT_MXFP4 || fmt == FMT_MXINT8; }
+bool is_int_grouped(int fmt) { return fmt == FMT_INT4 || fmt == FMT_INT8; }
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
 enum Status { OK = 0, ERR_NULL = -1, ERR_SHAPE = -2, ERR_FORMAT = -4, ERR_VALUE = -8 };
 
@@ -138,9 +143,9 @@ int floor_log2(float a) {
 // the admissible point nearest to x, so "projection" is the nearest point.
 //   MX formats: powers of two 2^k, k in [-127, 127] (E8M0 range); ties go to the larger.
 //   NVFP4:      positive E4M3FN values [2^-9, 448]; ties to the even code.
-//   INT4:       positive bf16 values [2^-126, max bf16]; ties to even.
+//   INT4, INT8: positive bf16 values [2^-126, max bf16]; ties to even.
 float project(int fmt, float x) {
-  if (fmt == FMT_MXINT4 || fmt == FMT_MXFP4) {
+  if (is_mx(fmt)) {
     double best = std::ldexp(1.0, -127), bestd = std::fabs((double)x - best);
     for (int k = -126; k <= 127; ++k) {
       double p = std::ldexp(1.0, k), d = std::fabs((double)x - p);
@@ -149,7 +154,7 @@ float project(int fmt, float x) {
     return (float)best;
   }
   if (fmt == FMT_NVFP4) return (float)e4m3_value(e4m3_encode_nonneg(x, 1));
-  // INT4: bf16
+  // INT4 / INT8: bf16
   const float lo = std::ldexp(1.0f, -126);
   const float hi = f_of(0x7F7F0000u);
   float b = bf16_round(std::min(x, hi));
@@ -158,11 +163,12 @@ float project(int fmt, float x) {
 
 // ---------------------------------------------------------------- block quantisers
 // FQ_f on a normalised row-major matrix V (rows x cols); blocks of g consecutive
-// elements along a row.  Outputs: packed codes (two per byte, low nibble = even
-// column), block scales (bf16 for INT4, E8M0 byte for MX, E4M3 byte for NVFP4),
-// the NVFP4 fp32 tensor scale, and Qhat (the dequantised values, fp32).
+// elements along a row.  Outputs: packed codes (4-bit formats: two per byte, low nibble =
+// even column; 8-bit formats: one byte per element), block scales (bf16 for INT4/INT8,
+// E8M0 byte for MX, E4M3 byte for NVFP4), the NVFP4 fp32 tensor scale, and Qhat (the
+// dequantised values, fp32).
 struct FQOut {
-  uint8_t* codes;      // rows * cols / 2
+  uint8_t* codes;      // rows * cols * bits / 8
   void* scales;        // rows * cols / g
   float* tscale;       // 1 (NVFP4)
   float* qhat;         // rows * cols (may be null)
@@ -175,21 +181,30 @@ void put_code(uint8_t* codes, int64_t idx, uint8_t nib) {
   else b = (uint8_t)((b & 0xF0) | (nib & 0x0F));
 }
 
-// INT4, symmetric: s = bf16(a / 7), codes = clamp(rint(v * (1/s)), -7, 7) (two's
-// complement nibble), Qhat = q * s.  An all-zero block stores scale 0.
-void fq_int4_row(const float* v, int64_t row, int64_t cols, int g, FQOut& o) {
+// Code of element idx at the format's width (two's complement for the integer formats).
+void put_code_w(int bits, uint8_t* codes, int64_t idx, int q) {
+  if (bits == 8) codes[idx] = (uint8_t)(q & 0xFF);
+  else put_code(codes, idx, (uint8_t)(q & 0xF));
+}
+
+// Grouped symmetric integers (INT4: qmax 7; INT8: qmax 127): s = bf16(a / qmax),
+// codes = clamp(rint(v * (1/s)), -qmax, qmax), Qhat = q * s.  An all-zero block stores
+// scale 0.
+void fq_int_row(int fmt, const float* v, int64_t row, int64_t cols, int g, FQOut& o) {
+  const int qmax = (fmt == FMT_INT8) ? 127 : 7;
+  const int bits = code_bits(fmt);
   uint16_t* sc = (uint16_t*)o.scales;
   for (int64_t b = 0; b < cols / g; ++b) {
     const float* x = v + b * g;
     float a = 0.0f;
     for (int k = 0; k < g; ++k) a = std::max(a, std::fabs(x[k]));
-    float s = (a > 0.0f) ? bf16_round(a / 7.0f) : 0.0f;
+    float s = (a > 0.0f) ? bf16_round(a / (float)qmax) : 0.0f;
     sc[row * (cols / g) + b] = (uint16_t)(u_of(s) >> 16);
     float is = (s > 0.0f) ? 1.0f / s : 0.0f;
     for (int k = 0; k < g; ++k) {
-      int q = (s > 0.0f) ? int_round_clamp(x[k] * is, 7) : 0;
+      int q = (s > 0.0f) ? int_round_clamp(x[k] * is, qmax) : 0;
       int64_t idx = row * cols + b * g + k;
-      put_code(o.codes, idx, (uint8_t)(q & 0xF));
+      put_code_w(bits, o.codes, idx, q);
       if (o.qhat) o.qhat[idx] = (float)q * s;
     }
   }
@@ -198,6 +213,9 @@ void fq_int4_row(const float* v, int64_t row, int64_t cols, int g, FQOut& o) {
 // MXINT4 (by analogy with OCP MXINT8): shared exponent e = floor(log2 amax), elements
 // are 4-bit two's-complement integers with an implicit 2^-2, clamped symmetrically to
 // [-7, 7]: q = clamp(rint(v * 2^(2-e)), -7, 7), Qhat = q * 2^(e-2).  Scale byte e+127.
+// MXINT8 (OCP MX v1.0): 8-bit two's-complement elements with an implicit 2^-6, largest
+// magnitude below 2 so the shared exponent is e = floor(log2 amax):
+// q = clamp(rint(v * 2^(6-e)), -127, 127), Qhat = q * 2^(e-6).
 // MXFP4 (OCP MX v1.0): e = floor(log2 amax) - 2, q = E2M1(v * 2^-e), Qhat = q * 2^e.
 // Exponents clamp to [-127, 127]; an all-zero block stores scale byte 0 and codes 0.
 void fq_mx_row(int fmt, const float* v, int64_t row, int64_t cols, int g, FQOut& o) {
@@ -217,13 +235,18 @@ void fq_mx_row(int fmt, const float* v, int64_t row, int64_t cols, int g, FQOut&
         if (fmt == FMT_MXFP4) {
           nib = e2m1_encode(std::ldexp(x[k], -e));
           qh = std::ldexp((float)e2m1_decode(nib), e);
+        } else if (fmt == FMT_MXINT8) {
+          int q = int_round_clamp(std::ldexp(x[k], 6 - e), 127);
+          nib = (uint8_t)(q & 0xFF);
+          qh = std::ldexp((float)q, e - 6);
         } else {
           int q = int_round_clamp(std::ldexp(x[k], 2 - e), 7);
           nib = (uint8_t)(q & 0xF);
           qh = std::ldexp((float)q, e - 2);
         }
       }
-      put_code(o.codes, idx, nib);
+      if (fmt == FMT_MXINT8) o.codes[idx] = nib;
+      else put_code(o.codes, idx, nib);
       if (o.qhat) o.qhat[idx] = qh;
     }
   }
@@ -261,8 +284,8 @@ void fq_nvfp4_row(const float* v, int64_t row, int64_t cols, float s_t, float k6
 }
 
 int group_ok(int fmt, int g) {
-  if (fmt == FMT_INT4) return g == 64 || g == 128;
-  if (fmt == FMT_MXINT4 || fmt == FMT_MXFP4) return g == 32;
+  if (is_int_grouped(fmt)) return g == 64 || g == 128;
+  if (is_mx(fmt)) return g == 32;
   if (fmt == FMT_NVFP4) return g == 16;
   return 0;
 }
@@ -289,12 +312,12 @@ void fq_matrix(int fmt, int g, const float* V, int64_t rows, int64_t cols, FQOut
   parallel_rows(rows, [&](int64_t b, int64_t e) {
     for (int64_t i = b; i < e; ++i) {
       const float* v = V + i * cols;
-      if (fmt == FMT_INT4) fq_int4_row(v, i, cols, g, o);
+      if (is_int_grouped(fmt)) fq_int_row(fmt, v, i, cols, g, o);
       else if (fmt == FMT_NVFP4) fq_nvfp4_row(v, i, cols, s_t, k6, o, &fl[i]);
       else fq_mx_row(fmt, v, i, cols, g, o);
     }
   });
-  // codes of odd/even columns of one row share bytes, and rows never share bytes
+  // 4-bit codes of odd/even columns of one row share bytes, and rows never share bytes
   // (cols is a multiple of the group, hence even), so the row-parallel writes are safe.
   for (auto f : fl) o.flags |= f;
 }
@@ -419,9 +442,16 @@ int o_dequantize(int fmt, int g, const uint8_t* codes, const void* scales, float
   for (int64_t i = 0; i < rows; ++i)
     for (int64_t j = 0; j < cols; ++j) {
       int64_t idx = i * cols + j;
-      uint8_t nib = (codes[idx >> 1] >> ((idx & 1) * 4)) & 0xF;
       int64_t bi = i * (cols / g) + j / g;
       float v = 0.0f;
+      if (code_bits(fmt) == 8) {
+        const int q = (int)(int8_t)codes[idx];
+        if (fmt == FMT_INT8) v = (float)q * bf16_to_f32(((const uint16_t*)scales)[bi]);
+        else v = std::ldexp((float)q, (int)((const uint8_t*)scales)[bi] - 127 - 6);
+        out[idx] = v;
+        continue;
+      }
+      uint8_t nib = (codes[idx >> 1] >> ((idx & 1) * 4)) & 0xF;
       if (fmt == FMT_INT4) {
         float s = bf16_to_f32(((const uint16_t*)scales)[bi]);
         int q = (nib & 8) ? (int)nib - 16 : (int)nib;
@@ -486,9 +516,10 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
   double normW2 = 0.0;
   for (int64_t i = 0; i < N; ++i) normW2 += (double)Wf[i] * (double)Wf[i];
 
-  const size_t sc_bytes = (fmt == FMT_INT4) ? 2 : 1;
+  const size_t sc_bytes = is_int_grouped(fmt) ? 2 : 1;
+  const int64_t code_bytes = N * code_bits(fmt) / 8;
   std::vector<float> V(N), Q(N), Qc(N);
-  std::vector<uint8_t> codesA(N / 2), codesC(N / 2);
+  std::vector<uint8_t> codesA(code_bytes), codesC(code_bytes);
   std::vector<uint8_t> scA(nblk * sc_bytes), scC(nblk * sc_bytes);
   float tsA = 0.0f, tsC = 0.0f;
   uint32_t flags = 0;
