@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--format", default=None,
+                    help="solve the workload's weight in another format (e.g. INT8, MXINT8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -171,6 +173,8 @@ def main():
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
     fmt, group, T = wl["fmt"], wl["group"], wl["iters"]
+    if args.format:
+        fmt, group = args.format, None
     W_np = synth.matrix(wl["W"], 0)
     m, n = W_np.shape
     xspec = synth.MatrixSpec(ACT_TOKENS, n, "normal", 1.0, outliers=synth.outlier_count(n, 0.01),
@@ -239,8 +243,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"down_proj-shaped {m}x{n} bf16 weight (Student-t nu=3, std 0.015, "
-                        f"0.5% outlier columns x25), {fmt} g={group}, {T} BCD iterations; then "
+            "workload": f"{args.workload}: {m}x{n} bf16 weight ({wl['W'].dist}, std {wl['W'].std}, "
+                        f"{wl['W'].outliers} outlier columns x{wl['W'].outlier_scale:g}), {fmt} "
+                        f"g={group or dq.DEFAULT_GROUP[fmt]}, {T} BCD iterations; then "
                         f"{ACT_TOKENS}x{n} bf16 activations rescaled by c and {fmt}-quantised",
             "rows": m, "cols": n, "format": fmt, "iters": T, "act_tokens": ACT_TOKENS,
         },

@@ -22,14 +22,16 @@
  *     `group` consecutive elements run along a row.  Base pointers and the row pitch in
  *     bytes must be multiples of 16.  cols must be a multiple of the group and at most
  *     16384.
- *   - Codes: two 4-bit codes per byte, low nibble = even column, [rows][cols/2].  INT4 and
- *     MXINT4 codes are two's complement; MXFP4/NVFP4 codes are E2M1 sign-magnitude (the
- *     sign of a negative value that rounds to zero is kept: code 0x8).
- *   - Block scales: [rows][cols/group].  INT4: bf16 bit patterns (uint16), value
- *     bf16(amax/7).  MXINT4/MXFP4: one E8M0 byte, value 2^(byte-127).  NVFP4: one E4M3FN
- *     byte, multiplied by the fp32 tensor scale.
- *   - Dequantised value of an element: INT4 q*s; MXINT4 q*2^(e-2); MXFP4 e2m1(q)*2^e;
- *     NVFP4 e2m1(q)*(e4m3(sb)*tensor_scale).
+ *   - Codes of the 4-bit formats: two per byte, low nibble = even column, [rows][cols/2].
+ *     INT4 and MXINT4 codes are two's complement; MXFP4/NVFP4 codes are E2M1
+ *     sign-magnitude (the sign of a negative value that rounds to zero is kept: code 0x8).
+ *     Codes of the 8-bit formats (INT8, MXINT8): one two's-complement byte per element,
+ *     [rows][cols].
+ *   - Block scales: [rows][cols/group].  INT4/INT8: bf16 bit patterns (uint16), value
+ *     bf16(amax/7) or bf16(amax/127).  MX formats: one E8M0 byte, value 2^(byte-127).
+ *     NVFP4: one E4M3FN byte, multiplied by the fp32 tensor scale.
+ *   - Dequantised value of an element: INT4/INT8 q*s; MXINT4 q*2^(e-2); MXINT8 q*2^(e-6);
+ *     MXFP4 e2m1(q)*2^e; NVFP4 e2m1(q)*(e4m3(sb)*tensor_scale).
  *   - Errors are returned synchronously.  Every argument check happens before any GPU work
  *     is enqueued, so a call that returns an error has enqueued nothing.  Conditions that
  *     depend on the data are reported as flag bits (DQ_FLAG_*) in dq_report.
@@ -61,7 +63,9 @@ enum {
   DQ_FMT_INT4 = 0,    /* symmetric INT4, per-group bf16 scale, group 64 or 128 */
   DQ_FMT_MXINT4 = 1,  /* 32-element blocks, E8M0 scale, 4-bit integers with implicit 2^-2 */
   DQ_FMT_MXFP4 = 2,   /* 32-element blocks, E8M0 scale, E2M1 elements (OCP MX v1.0) */
-  DQ_FMT_NVFP4 = 3    /* 16-element blocks, E4M3 block scale, fp32 tensor scale, E2M1 */
+  DQ_FMT_NVFP4 = 3,   /* 16-element blocks, E4M3 block scale, fp32 tensor scale, E2M1 */
+  DQ_FMT_INT8 = 4,    /* symmetric INT8, per-group bf16 scale, group 64 or 128 */
+  DQ_FMT_MXINT8 = 5   /* 32-element blocks, E8M0 scale, INT8 elements x 2^-6 (OCP MX v1.0) */
 };
 enum { DQ_F32 = 0, DQ_BF16 = 1 };
 
@@ -76,7 +80,7 @@ enum {
 
 typedef struct {
   int32_t fmt;    /* DQ_FMT_* */
-  int32_t group;  /* block size; 0 = the format's default (INT4 128, MX 32, NVFP4 16) */
+  int32_t group;  /* block size; 0 = the format's default (INT4/INT8 128, MX 32, NVFP4 16) */
 } dq_quant_spec;
 
 typedef struct {
@@ -116,7 +120,7 @@ typedef struct {
   const float* c_init;  /* [cols] initial column scales, or NULL for ones */
   float* r;             /* out [rows]: final row scales (admissible values) */
   float* c;             /* out [cols]: final column scales = beta (admissible values) */
-  uint8_t* codes;       /* out [rows*cols/2]: codes of the final Qhat */
+  uint8_t* codes;       /* out [rows*cols/2] (8-bit formats: [rows*cols]): codes of the final Qhat */
   void* block_scales;   /* out [rows*cols/group]: block scales of the final Qhat */
   float* tensor_scale;  /* out [1]: NVFP4 tensor scale of the final Qhat (ignored otherwise) */
   double* nmse_hist;    /* out [iters+1] or NULL: ||W - diag(r)Qhat diag(c)||^2 / ||W||^2 */
@@ -141,7 +145,7 @@ size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_sp
  *   Qhat-step  candidate FQ_f(W ./ r c^T), kept unless it raises the MSE at the current
  *           scales (so the MSE never increases);
  * where Proj is the nearest admissible value: powers of two 2^k, k in [-127,127] (MX,
- * ties up), E4M3 values in [2^-9, 448] (NVFP4), bf16 values >= 2^-126 (INT4).
+ * ties up), E4M3 values in [2^-9, 448] (NVFP4), bf16 values >= 2^-126 (INT4, INT8).
  * Problems are independent; count > 1 runs them together on one GPU.  Blocks the calling
  * thread until done.  `workspace` must hold dq_workspace_bytes(...) bytes of device
  * memory; its contents on entry do not matter. */

@@ -25,8 +25,9 @@ if not _LIB_PATH.exists():
     raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m post_quantization_dq_amd.build`")
 _lib = C.CDLL(str(_LIB_PATH))
 
-FMT = {"INT4": 0, "MXINT4": 1, "MXFP4": 2, "NVFP4": 3}
-DEFAULT_GROUP = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16}
+FMT = {"INT4": 0, "MXINT4": 1, "MXFP4": 2, "NVFP4": 3, "INT8": 4, "MXINT8": 5}
+DEFAULT_GROUP = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16, "INT8": 128, "MXINT8": 32}
+CODE_BITS = {"INT4": 4, "MXINT4": 4, "MXFP4": 4, "NVFP4": 4, "INT8": 8, "MXINT8": 8}
 DT = {torch.float32: 0, torch.bfloat16: 1}
 FLAGS = {1: "nonfinite", 2: "zero_row", 4: "zero_col", 8: "nv_block_underflow", 16: "nv_tensor_underflow"}
 ROUND_FN = {"e2m1": 0, "e4m3": 1, "bf16": 2, "int4": 3, "proj_pow2": 4, "proj_e4m3": 5, "proj_bf16": 6}
@@ -108,7 +109,7 @@ def spec_of(fmt: str, group: int | None = None) -> dq_quant_spec:
 
 
 def scale_dtype(fmt: str) -> torch.dtype:
-    return torch.int16 if fmt == "INT4" else torch.uint8
+    return torch.int16 if fmt in ("INT4", "INT8") else torch.uint8
 
 
 # ------------------------------------------------------------------ C-ABI mirrors
@@ -201,7 +202,7 @@ def dq_debug_round(fn: str, x: torch.Tensor, out: torch.Tensor, stream=None):
 
 # ------------------------------------------------------------------ conveniences
 def _outputs(rows: int, cols: int, fmt: str, group: int, device):
-    codes = torch.empty(rows * cols // 2, dtype=torch.uint8, device=device)
+    codes = torch.empty(rows * cols * CODE_BITS[fmt] // 8, dtype=torch.uint8, device=device)
     scales = torch.empty(rows * cols // group, dtype=scale_dtype(fmt), device=device)
     ts = torch.zeros(1, dtype=torch.float32, device=device)
     return codes, scales, ts

@@ -20,7 +20,7 @@
 
 namespace dqk {
 
-enum Fmt { INT4 = 0, MXINT4 = 1, MXFP4 = 2, NVFP4 = 3 };
+enum Fmt { INT4 = 0, MXINT4 = 1, MXFP4 = 2, NVFP4 = 3, INT8 = 4, MXINT8 = 5 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -71,6 +71,10 @@ __device__ __forceinline__ float pow2_operand(int e) { return u2f((uint32_t)(e +
 __device__ __forceinline__ float int4_round(float x) {
   return __builtin_amdgcn_fmed3f(__builtin_rintf(x), -7.0f, 7.0f);
 }
+// Nearest integer in [-127, 127], ties to even.
+__device__ __forceinline__ float int8_round(float x) {
+  return __builtin_amdgcn_fmed3f(__builtin_rintf(x), -127.0f, 127.0f);
+}
 
 // ---------------------------------------------------------------- scale projections
 // Nearest admissible scale to x > 0 (conference entry: scales are projected onto the
@@ -94,9 +98,9 @@ __device__ __forceinline__ float proj_bf16(float x) {   // bf16 values in [2^-12
 }
 template <int FMT>
 __device__ __forceinline__ float project(float x) {
-  if (FMT == MXINT4 || FMT == MXFP4) return proj_pow2(x);
+  if (FMT == MXINT4 || FMT == MXFP4 || FMT == MXINT8) return proj_pow2(x);
   if (FMT == NVFP4) return proj_e4m3(x);
-  return proj_bf16(x);
+  return proj_bf16(x);   // INT4, INT8
 }
 
 // ---------------------------------------------------------------- cross-lane helpers
@@ -124,6 +128,13 @@ template <> struct Traits<INT4> { static constexpr int DEF_G = 128; static const
 template <> struct Traits<MXINT4> { static constexpr int DEF_G = 32; static constexpr int SCALE_BYTES = 1; };
 template <> struct Traits<MXFP4> { static constexpr int DEF_G = 32; static constexpr int SCALE_BYTES = 1; };
 template <> struct Traits<NVFP4> { static constexpr int DEF_G = 16; static constexpr int SCALE_BYTES = 1; };
+template <> struct Traits<INT8> { static constexpr int DEF_G = 128; static constexpr int SCALE_BYTES = 2; };
+template <> struct Traits<MXINT8> { static constexpr int DEF_G = 32; static constexpr int SCALE_BYTES = 1; };
+// 32-bit words of element codes per 16-element chunk: 4-bit codes pack into 2, 8-bit into 4.
+template <int FMT>
+constexpr int code_words() { return (FMT == INT8 || FMT == MXINT8) ? 4 : 2; }
+template <int FMT>
+constexpr bool grouped_int() { return FMT == INT4 || FMT == INT8; }
 
 // NVFP4 per-sweep tables: for every E4M3 code, d = fl(e4m3(code) * s_t) and id = fl(1/d).
 struct NvTab {
@@ -137,11 +148,12 @@ struct QCtx {
   const NvTab* tab;
 };
 
-// Result of quantising one chunk (16 elements): Qhat_k = p[k] * f exactly, where p is the
+// Result of quantising one chunk (16 elements): Qhat_k = p[k] * f, where p is the
 // element-grid value (E2M1 value or integer) and f the block's dequantisation factor
-// (NVFP4 d = e4m3(sb) * s_t, MXFP4 2^e, MXINT4 2^(e-2), INT4 s).
+// (NVFP4 d = e4m3(sb) * s_t, MXFP4 2^e, MXINT4 2^(e-2), MXINT8 2^(e-6), INT4/INT8 s).
 struct Chunk {
-  uint32_t code[2];   // 16 nibbles, element k in bits 4k..4k+3 of the 64-bit pair
+  uint32_t code[4];   // 4-bit formats: 16 nibbles, element k in bits 4k..4k+3 of words 0-1;
+                      // 8-bit formats: 16 bytes, element k in byte k of words 0-3
   uint32_t scode;     // block scale code (bf16 bits, E8M0 byte or E4M3 byte)
   float f;            // block factor
   float p[16];        // grid values
@@ -181,6 +193,11 @@ __device__ __forceinline__ void int4_decode16(uint32_t c0, uint32_t c1, float (&
     uint32_t w = (k < 8) ? c0 : c1;
     p[k] = (float)(((int)(w << (28 - 4 * (k & 7)))) >> 28);   // sign-extended nibble
   }
+}
+__device__ __forceinline__ void int8_decode16(const uint32_t (&c)[4], float (&p)[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    p[k] = (float)(((int)(c[k >> 2] << (24 - 8 * (k & 3)))) >> 24);   // sign-extended byte
 }
 
 // Quantise one lane's 16 normalised values v (one chunk of a block of L*16).
@@ -239,6 +256,36 @@ __device__ __forceinline__ void quantize_chunk(const float (&v)[16], const QCtx&
     }
     o.code[0] = c0;
     o.code[1] = c1;
+  } else if (FMT == MXINT8) {
+    // OCP MX v1.0 MXINT8: elements q * 2^-6 with q in [-127, 127]; shared exponent
+    // floor(log2 amax)
+    int e = (a > 0.0f) ? floor_log2(a) : -127;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    o.scode = (uint32_t)(e + 127);
+    o.f = ldexpf(1.0f, e - 6);
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float q = (a > 0.0f) ? int8_round(ldexpf(v[k], 6 - e)) : 0.0f;
+      c[k >> 2] |= ((uint32_t)(int)q & 0xFFu) << (8 * (k & 3));
+      o.p[k] = q;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o.code[w] = c[w];
+  } else if (FMT == INT8) {
+    const float s = (a > 0.0f) ? bf16_rne(a / 127.0f) : 0.0f;
+    o.scode = f2u(s) >> 16;
+    o.f = s;
+    const float is = (s > 0.0f) ? 1.0f / s : 0.0f;
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float q = (s > 0.0f) ? int8_round(v[k] * is) : 0.0f;
+      c[k >> 2] |= ((uint32_t)(int)q & 0xFFu) << (8 * (k & 3));
+      o.p[k] = q;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o.code[w] = c[w];
   } else {  // INT4
     const float s = (a > 0.0f) ? bf16_rne(a / 7.0f) : 0.0f;
     o.scode = f2u(s) >> 16;
@@ -264,14 +311,16 @@ __device__ __forceinline__ float block_factor(uint32_t scode, const NvTab* tab) 
   if (FMT == NVFP4) return tab->d[scode & 127u];
   if (FMT == MXFP4) return ldexpf(1.0f, (int)scode - 127);
   if (FMT == MXINT4) return ldexpf(1.0f, (int)scode - 129);
-  return u2f(scode << 16);
+  if (FMT == MXINT8) return ldexpf(1.0f, (int)scode - 133);
+  return u2f(scode << 16);   // INT4, INT8: bf16 scale
 }
 
-// Grid values of a stored chunk.
+// Grid values of a stored chunk (code words as stored: 2 for 4-bit, 4 for 8-bit formats).
 template <int FMT>
-__device__ __forceinline__ void decode_grid(uint32_t c0, uint32_t c1, float (&p)[16]) {
-  if (FMT == NVFP4 || FMT == MXFP4) fp4_decode16(c0, c1, p);
-  else int4_decode16(c0, c1, p);
+__device__ __forceinline__ void decode_grid(const uint32_t (&c)[4], float (&p)[16]) {
+  if (FMT == NVFP4 || FMT == MXFP4) fp4_decode16(c[0], c[1], p);
+  else if (FMT == INT8 || FMT == MXINT8) int8_decode16(c, p);
+  else int4_decode16(c[0], c[1], p);
 }
 
 }  // namespace dqk

@@ -15,7 +15,7 @@
 //               the safeguard decision and writes the next sweep's state.  If the candidate
 //               is rejected the speculative r/c are discarded and the next iteration re-runs
 //               the r/c steps from the kept Qhat (FIXUP mode).
-// Lane l of a wave owns chunks of 16 consecutive columns; blocks of MX (32) and INT4
+// Lane l of a wave owns chunks of 16 consecutive columns; blocks of MX (32) and INT4/INT8
 // (64/128) formats span 2..8 adjacent lanes.
 
 #pragma once
@@ -46,7 +46,7 @@ struct ProbDev {
   float* ic[2];
   uint8_t* codes[2];
   void* scales[2];
-  void* colP;       // [rranges][NQ][cols] column partials (fp64 for INT4, else fp32)
+  void* colP;       // [rranges][NQ][cols] column partials (fp64 for INT4/INT8, else fp32)
   double* swp;      // [rowblocks][4]: F(Qc), dF, relchg numerator, ||Qc||^2
   float* fwp;       // [fin_wgs]: NVFP4 amax partials
   double* initp;    // [init_wgs][2]
@@ -73,10 +73,14 @@ struct WgEntry {
 constexpr float kTinyTensorScale = 7.888609052210118e-31f;  // 2^-100
 
 // ---------------------------------------------------------------- loads and stores
+// Codes of chunk l of row i: 8 bytes (4-bit formats) or 16 bytes (8-bit formats).
 template <int FMT, int L>
 __device__ __forceinline__ void store_chunk(uint8_t* codes, void* scales, int64_t i, int64_t n,
                                             int l, int g, const Chunk& ch) {
-  *gp((u32x2*)(codes + ((i * n) >> 1) + 8 * (int64_t)l)) = u32x2{ch.code[0], ch.code[1]};
+  if (code_words<FMT>() == 4)
+    *gp((u32x4*)(codes + i * n + 16 * (int64_t)l)) = u32x4{ch.code[0], ch.code[1], ch.code[2], ch.code[3]};
+  else
+    *gp((u32x2*)(codes + ((i * n) >> 1) + 8 * (int64_t)l)) = u32x2{ch.code[0], ch.code[1]};
   if ((l % L) == 0) {
     int64_t bi = i * (n / g) + l / L;
     if (Traits<FMT>::SCALE_BYTES == 2) gp((uint16_t*)scales)[bi] = (uint16_t)ch.scode;
@@ -86,11 +90,15 @@ __device__ __forceinline__ void store_chunk(uint8_t* codes, void* scales, int64_
 
 template <int FMT, int L>
 __device__ __forceinline__ void load_codes(const uint8_t* codes, const void* scales, int64_t i,
-                                           int64_t n, int l, int g, uint32_t& c0, uint32_t& c1,
+                                           int64_t n, int l, int g, uint32_t (&c)[4],
                                            uint32_t& sc) {
-  const u32x2 cw = *gp((const u32x2*)(codes + ((i * n) >> 1) + 8 * (int64_t)l));
-  c0 = cw.x;
-  c1 = cw.y;
+  if (code_words<FMT>() == 4) {
+    const u32x4 cw = *gp((const u32x4*)(codes + i * n + 16 * (int64_t)l));
+    c[0] = cw.x; c[1] = cw.y; c[2] = cw.z; c[3] = cw.w;
+  } else {
+    const u32x2 cw = *gp((const u32x2*)(codes + ((i * n) >> 1) + 8 * (int64_t)l));
+    c[0] = cw.x; c[1] = cw.y; c[2] = 0u; c[3] = 0u;
+  }
   int64_t bi = i * (n / g) + l / L;
   sc = (Traits<FMT>::SCALE_BYTES == 2) ? (uint32_t)gp((const uint16_t*)scales)[bi]
                                        : (uint32_t)gp((const uint8_t*)scales)[bi];
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
   State* st = P.st + (sw & 1);
   if (st->mode == MODE_DONE) return;
   const PassInfo pi(st, P.iters);
-  constexpr bool A64 = (FMT == INT4);   // INT4: exact products accumulated in fp64
+  constexpr bool A64 = grouped_int<FMT>();   // INT4/INT8: exact products accumulated in fp64
   const int g = L * 16;
   const int64_t n = P.cols;
   const int nch = (int)(n >> 4);
@@ -417,8 +425,8 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
       const int j0 = 16 * chn;
       RawRow<DT> raw;
       if (valid) raw.load(P.W, i, P.ld, j0); else raw.zero();
-      uint32_t p0 = 0, p1 = 0, ps = 0;
-      if (valid && !(pi.mode == MODE_INIT)) load_codes<FMT, L>(acodes, ascales, i, n, chn, g, p0, p1, ps);
+      uint32_t pk[4] = {0u, 0u, 0u, 0u}, ps = 0;
+      if (valid && !(pi.mode == MODE_INIT)) load_codes<FMT, L>(acodes, ascales, i, n, chn, g, pk, ps);
       float w[16];
       raw.unpack(w);
       float p[16];
@@ -461,7 +469,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         float Fpl = 0.0f, rl = 0.0f;
         if (pi.stats) {
           float pp[16];
-          decode_grid<FMT>(p0, p1, pp);
+          decode_grid<FMT>(pk, pp);
           const float fp = block_factor<FMT>(ps, tab_p);
           const float rfp = r_ * fp;
 #pragma unroll
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
           aqn += (double)(f * f) * (double)ql;
         }
       } else {
-        decode_grid<FMT>(p0, p1, p);
+        decode_grid<FMT>(pk, p);
         f = block_factor<FMT>(ps, tab_p);
         lds_load16(s_c4, nch, cl, cc);
 #pragma unroll
@@ -549,7 +557,8 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
 // Workgroup = 8 waves on one strip of 64 chunks (1024 columns) and one range of rows; wave
 // w takes rows w, w+8, ... of the range.  The waves' accumulators are combined in LDS in
 // fixed wave order and written as this range's partial.  fp32 accumulation keeps a wave
-// within 128 VGPRs (two workgroups per CU); INT4's fp64 accumulators need the wider budget.
+// within 128 VGPRs (two workgroups per CU); INT4/INT8's fp64 accumulators need the wider
+// budget.
 template <int FMT, int DT, int L>
 __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
                                              const WgEntry* __restrict__ table, int sw) {
@@ -559,7 +568,7 @@ __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
   if (st->mode == MODE_DONE) return;
   const PassInfo pi(st, P.iters);
   if (!pi.next) return;
-  constexpr bool A64 = (FMT == INT4);
+  constexpr bool A64 = grouped_int<FMT>();
   typedef typename std::conditional<A64, double, float>::type acc_t;
   constexpr int NQ = (FMT == NVFP4) ? 3 : 2;
   const int g = L * 16;
@@ -592,19 +601,19 @@ __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
   if (act) {
     for (int64_t i0 = row0 + wave; i0 < row1; i0 += 8 * U) {
       RawRow<DT> raw[U];
-      uint32_t c0[U], c1[U], sc[U];
+      uint32_t cw[U][4], sc[U];
       float rr_[U], irn[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t i = i0 + 8 * u;
         if (i < row1) {
           raw[u].load(P.W, i, P.ld, j0);
-          load_codes<FMT, L>(qcodes, qscales, i, n, chn, g, c0[u], c1[u], sc[u]);
+          load_codes<FMT, L>(qcodes, qscales, i, n, chn, g, cw[u], sc[u]);
           rr_[u] = rnew[i];
           irn[u] = (FMT == NVFP4) ? irnew[i] : 0.0f;
         } else {
           raw[u].zero();
-          c0[u] = c1[u] = sc[u] = 0u;
+          cw[u][0] = cw[u][1] = cw[u][2] = cw[u][3] = sc[u] = 0u;
           rr_[u] = 0.0f;
           irn[u] = 0.0f;
         }
@@ -614,13 +623,14 @@ __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
         if (i0 + 8 * u >= row1) break;
         float w[16], p[16];
         raw[u].unpack(w);
-        decode_grid<FMT>(c0[u], c1[u], p);
+        decode_grid<FMT>(cw[u], p);
         const float f = block_factor<FMT>(sc[u], &tab);
         const float rf = rr_[u] * f;
         const float rf2 = rf * rf;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          if (A64) {   // INT4: rf = r * s and rf * p are exact in fp32; products exact in fp64
+          if (A64) {   // INT4/INT8: rf = r * s and rf * p are exact in fp32 (bf16 x bf16 x at
+                       // most 7 bits); products exact in fp64
             cN[k] = fma((double)rf, (double)w[k] * (double)p[k], (double)cN[k]);
             const double rp = (double)(rf * p[k]);
             cD[k] = fma(rp, rp, (double)cD[k]);
@@ -710,7 +720,7 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   bool zcol = false;
   if (next) {
     constexpr int NQ = (FMT == NVFP4) ? 3 : 2;
-    typedef typename std::conditional<FMT == INT4, double, float>::type acc_t;
+    typedef typename std::conditional<grouped_int<FMT>(), double, float>::type acc_t;
     const int64_t j = (int64_t)we.idx * 64 + col;
     double N = 0.0, D = 0.0;
     float M = 0.0f;
@@ -1013,10 +1023,10 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
   if (e >= rows * nch) return;
   const int64_t i = e / nch;
   const int l = (int)(e - i * nch);
-  uint32_t c0, c1, sc;
-  load_codes<FMT, L>(codes, scales, i, cols, l, L * 16, c0, c1, sc);
+  uint32_t cw[4], sc;
+  load_codes<FMT, L>(codes, scales, i, cols, l, L * 16, cw, sc);
   float p[16], q[16];
-  decode_grid<FMT>(c0, c1, p);
+  decode_grid<FMT>(cw, p);
   const float f = block_factor<FMT>(sc, &tab);
 #pragma unroll
   for (int k = 0; k < 16; ++k) q[k] = p[k] * f;

@@ -25,6 +25,8 @@ size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 int default_group(int fmt) {
   switch (fmt) {
     case DQ_FMT_INT4: return 128;
+    case DQ_FMT_INT8: return 128;
+    case DQ_FMT_MXINT8: return 32;
     case DQ_FMT_MXINT4: return 32;
     case DQ_FMT_MXFP4: return 32;
     case DQ_FMT_NVFP4: return 16;
@@ -33,19 +35,26 @@ int default_group(int fmt) {
 }
 
 int resolve_group(const dq_quant_spec& s) {
-  if (s.fmt < DQ_FMT_INT4 || s.fmt > DQ_FMT_NVFP4) return -1;
+  if (s.fmt < DQ_FMT_INT4 || s.fmt > DQ_FMT_MXINT8) return -1;
   int g = s.group ? s.group : default_group(s.fmt);
-  if (s.fmt == DQ_FMT_INT4 && g != 64 && g != 128) return -1;
-  if ((s.fmt == DQ_FMT_MXINT4 || s.fmt == DQ_FMT_MXFP4) && g != 32) return -1;
+  if ((s.fmt == DQ_FMT_INT4 || s.fmt == DQ_FMT_INT8) && g != 64 && g != 128) return -1;
+  if ((s.fmt == DQ_FMT_MXINT4 || s.fmt == DQ_FMT_MXFP4 || s.fmt == DQ_FMT_MXINT8) && g != 32)
+    return -1;
   if (s.fmt == DQ_FMT_NVFP4 && g != 16) return -1;
   return g;
 }
 
-int scale_bytes(int fmt) { return fmt == DQ_FMT_INT4 ? 2 : 1; }
+bool grouped_int_fmt(int fmt) { return fmt == DQ_FMT_INT4 || fmt == DQ_FMT_INT8; }
+int scale_bytes(int fmt) { return grouped_int_fmt(fmt) ? 2 : 1; }
+// Bytes of element codes of a rows x cols matrix: 4-bit formats two per byte, 8-bit one.
+size_t code_bytes(int fmt, int64_t rows, int64_t cols) {
+  const bool wide = fmt == DQ_FMT_INT8 || fmt == DQ_FMT_MXINT8;
+  return (size_t)rows * (size_t)cols / (wide ? 1 : 2);
+}
 // Column partials per row range: N, D (and the NVFP4 column amax); fp64 for INT4.
 size_t partial_bytes(int fmt, int64_t strips, int64_t cols) {
   const int nq = fmt == DQ_FMT_NVFP4 ? 3 : 2;
-  const size_t el = fmt == DQ_FMT_INT4 ? sizeof(double) : sizeof(float);
+  const size_t el = grouped_int_fmt(fmt) ? sizeof(double) : sizeof(float);
   return (size_t)strips * nq * cols * el;
 }
 int elem_bytes(int dt) { return dt == DQ_F32 ? 4 : 2; }
@@ -79,7 +88,7 @@ int row_slots(int lpr) { return std::max(1, 1024 / lpr); }
 size_t rowpass_lds(int fmt, int64_t cols) {
   return 2 * sizeof(float) * (size_t)cols + (fmt == DQ_FMT_NVFP4 ? 2 * sizeof(NvTab) : 0);
 }
-size_t colpass_lds(int fmt) { return (size_t)8 * 64 * 16 * (fmt == DQ_FMT_INT4 ? 8 : 4); }
+size_t colpass_lds(int fmt) { return (size_t)8 * 64 * 16 * (grouped_int_fmt(fmt) ? 8 : 4); }
 
 struct Plan {
   std::vector<ProbDev> dev;
@@ -118,7 +127,7 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
   }
   const int64_t rows_per_wave = std::max<int64_t>(1, (total_rows + kTargetRowWaves - 1) / kTargetRowWaves);
   const int nq = fmt == DQ_FMT_NVFP4 ? 3 : 2;
-  const size_t acc_bytes = fmt == DQ_FMT_INT4 ? 8 : 4;
+  const size_t acc_bytes = grouped_int_fmt(fmt) ? 8 : 4;
   size_t off = 0;
   for (int k = 0; k < count; ++k) {
     ProbDev& d = pl.dev[k];
@@ -144,7 +153,7 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     off = align_up(off + 2 * sizeof(State) + sizeof(uint32_t));
     off = align_up(off + 4 * sizeof(float) * d.rows);                  // r[2], ir[2]
     off = align_up(off + 4 * sizeof(float) * d.cols);                  // c[2], ic[2]
-    off = align_up(off + (size_t)d.rows * d.cols / 2);                 // codes buffer 1
+    off = align_up(off + code_bytes(fmt, d.rows, d.cols));             // codes buffer 1
     off = align_up(off + (size_t)d.rows * d.cols / g * scale_bytes(fmt));
     off = align_up(off + (size_t)d.rranges * nq * d.cols * acc_bytes);  // column partials
     off = align_up(off + (size_t)d.rowblocks * 4 * sizeof(double));
@@ -186,7 +195,7 @@ void bind_pointers(const dq_problem* p, int32_t count, int g, int fmt, int iters
     float* cc = (float*)take(4 * sizeof(float) * d.cols);
     d.c[0] = cc; d.c[1] = cc + d.cols; d.ic[0] = cc + 2 * d.cols; d.ic[1] = cc + 3 * d.cols;
     d.codes[0] = p[k].codes;
-    d.codes[1] = (uint8_t*)take((size_t)d.rows * d.cols / 2);
+    d.codes[1] = (uint8_t*)take(code_bytes(fmt, d.rows, d.cols));
     d.scales[0] = p[k].block_scales;
     d.scales[1] = take((size_t)d.rows * d.cols / g * scale_bytes(fmt));
     d.colP = take(partial_bytes(fmt, d.rranges, d.cols));
@@ -237,7 +246,7 @@ int launch_passes(const Plan::Group& G, const ProbDev* probs, const WgEntry* rta
 template <int FMT, int DT, int L>
 int launch_colpass(const Plan::Group& G, const ProbDev* probs, const WgEntry* ctab, hipStream_t s,
                    int sw) {
-  if (FMT == INT4)
+  if constexpr (grouped_int<FMT>())
     launch_timed(k_colpass_wide<FMT, DT, L>, dim3((unsigned)G.col.size()), dim3(512),
                  colpass_lds(FMT), s, probs, ctab, sw);
   else
@@ -264,7 +273,7 @@ int prepare_passes(const Plan::Group& G) {
       hipFuncSetAttribute((const void*)k_rowpass<FMT, DT, L>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl) != hipSuccess)
     return DQ_ERR_HIP;
-  if (FMT == INT4 &&
+  if (grouped_int<FMT>() &&
       hipFuncSetAttribute((const void*)k_colpass_wide<FMT, DT, L>,
                           hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)colpass_lds(FMT)) != hipSuccess)
@@ -278,7 +287,11 @@ int prepare_passes_any(int fmt, int g, const Plan::Group& G) {
     case DQ_FMT_INT4:
       if (g == 64) { DQ_P(INT4, 4); }
       DQ_P(INT4, 8);
+    case DQ_FMT_INT8:
+      if (g == 64) { DQ_P(INT8, 4); }
+      DQ_P(INT8, 8);
     case DQ_FMT_MXINT4: DQ_P(MXINT4, 2);
+    case DQ_FMT_MXINT8: DQ_P(MXINT8, 2);
     case DQ_FMT_MXFP4: DQ_P(MXFP4, 2);
     default: DQ_P(NVFP4, 1);
   }
@@ -292,7 +305,11 @@ int launch_pass_any(int which, int fmt, int g, const Plan::Group& G, const ProbD
     case DQ_FMT_INT4:
       return g == 64 ? launch_pass_dt<INT4, 4>(which, G, probs, rtab, ctab, s, sw)
                      : launch_pass_dt<INT4, 8>(which, G, probs, rtab, ctab, s, sw);
+    case DQ_FMT_INT8:
+      return g == 64 ? launch_pass_dt<INT8, 4>(which, G, probs, rtab, ctab, s, sw)
+                     : launch_pass_dt<INT8, 8>(which, G, probs, rtab, ctab, s, sw);
     case DQ_FMT_MXINT4: return launch_pass_dt<MXINT4, 2>(which, G, probs, rtab, ctab, s, sw);
+    case DQ_FMT_MXINT8: return launch_pass_dt<MXINT8, 2>(which, G, probs, rtab, ctab, s, sw);
     case DQ_FMT_MXFP4: return launch_pass_dt<MXFP4, 2>(which, G, probs, rtab, ctab, s, sw);
     default: return launch_pass_dt<NVFP4, 1>(which, G, probs, rtab, ctab, s, sw);
   }
@@ -303,6 +320,8 @@ int launch_finalize_any(int fmt, const Plan::Group& G, const ProbDev* probs,
   dim3 grid((unsigned)G.fin.size()), block(256);
   switch (fmt) {
     case DQ_FMT_INT4: launch_timed(k_finalize<INT4>, grid, block, 0, s, probs, tab, sw); break;
+    case DQ_FMT_INT8: launch_timed(k_finalize<INT8>, grid, block, 0, s, probs, tab, sw); break;
+    case DQ_FMT_MXINT8: launch_timed(k_finalize<MXINT8>, grid, block, 0, s, probs, tab, sw); break;
     case DQ_FMT_MXINT4: launch_timed(k_finalize<MXINT4>, grid, block, 0, s, probs, tab, sw); break;
     case DQ_FMT_MXFP4: launch_timed(k_finalize<MXFP4>, grid, block, 0, s, probs, tab, sw); break;
     default: launch_timed(k_finalize<NVFP4>, grid, block, 0, s, probs, tab, sw); break;
@@ -321,6 +340,8 @@ int launch_init_reduce_any(int fmt, int count, const ProbDev* probs, hipStream_t
   dim3 grid((unsigned)count), block(256);
   switch (fmt) {
     case DQ_FMT_INT4: hipLaunchKernelGGL((k_init_reduce<INT4>), grid, block, 0, s, probs); break;
+    case DQ_FMT_INT8: hipLaunchKernelGGL((k_init_reduce<INT8>), grid, block, 0, s, probs); break;
+    case DQ_FMT_MXINT8: hipLaunchKernelGGL((k_init_reduce<MXINT8>), grid, block, 0, s, probs); break;
     case DQ_FMT_MXINT4: hipLaunchKernelGGL((k_init_reduce<MXINT4>), grid, block, 0, s, probs); break;
     case DQ_FMT_MXFP4: hipLaunchKernelGGL((k_init_reduce<MXFP4>), grid, block, 0, s, probs); break;
     default: hipLaunchKernelGGL((k_init_reduce<NVFP4>), grid, block, 0, s, probs); break;
@@ -331,6 +352,8 @@ int launch_init_reduce_any(int fmt, int count, const ProbDev* probs, hipStream_t
 int launch_init_any(int fmt, int dt, dim3 grid, const ProbDev* probs, hipStream_t s) {
   switch (fmt) {
     case DQ_FMT_INT4: return launch_init_t<INT4>(dt, grid, probs, s);
+    case DQ_FMT_INT8: return launch_init_t<INT8>(dt, grid, probs, s);
+    case DQ_FMT_MXINT8: return launch_init_t<MXINT8>(dt, grid, probs, s);
     case DQ_FMT_MXINT4: return launch_init_t<MXINT4>(dt, grid, probs, s);
     case DQ_FMT_MXFP4: return launch_init_t<MXFP4>(dt, grid, probs, s);
     default: return launch_init_t<NVFP4>(dt, grid, probs, s);
@@ -376,7 +399,11 @@ int launch_quant_any(int fmt, int g, int dt, const void* X, int64_t rows, int64_
     case DQ_FMT_INT4:
       if (g == 64) { DQ_Q(INT4, 4); }
       DQ_Q(INT4, 8);
+    case DQ_FMT_INT8:
+      if (g == 64) { DQ_Q(INT8, 4); }
+      DQ_Q(INT8, 8);
     case DQ_FMT_MXINT4: DQ_Q(MXINT4, 2);
+    case DQ_FMT_MXINT8: DQ_Q(MXINT8, 2);
     case DQ_FMT_MXFP4: DQ_Q(MXFP4, 2);
     default: DQ_Q(NVFP4, 1);
   }
@@ -589,7 +616,7 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
     DQ_HIP(hipMemcpyAsync(problems[k].r, d.r[S.rs], sizeof(float) * d.rows, hipMemcpyDeviceToDevice, s));
     DQ_HIP(hipMemcpyAsync(problems[k].c, d.c[S.cs], sizeof(float) * d.cols, hipMemcpyDeviceToDevice, s));
     if (S.acc == 1) {
-      DQ_HIP(hipMemcpyAsync(d.codes[0], d.codes[1], (size_t)d.rows * d.cols / 2,
+      DQ_HIP(hipMemcpyAsync(d.codes[0], d.codes[1], code_bytes(spec.fmt, d.rows, d.cols),
                             hipMemcpyDeviceToDevice, s));
       DQ_HIP(hipMemcpyAsync(d.scales[0], d.scales[1],
                             (size_t)d.rows * d.cols / g * scale_bytes(spec.fmt),
@@ -672,7 +699,12 @@ int dq_dequantize(dq_quant_spec spec, const uint8_t* codes, const void* block_sc
       if (g == 64) hipLaunchKernelGGL((k_dequant<INT4, 4>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out);
       else hipLaunchKernelGGL((k_dequant<INT4, 8>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out);
       break;
+    case DQ_FMT_INT8:
+      if (g == 64) hipLaunchKernelGGL((k_dequant<INT8, 4>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out);
+      else hipLaunchKernelGGL((k_dequant<INT8, 8>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out);
+      break;
     case DQ_FMT_MXINT4: hipLaunchKernelGGL((k_dequant<MXINT4, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
+    case DQ_FMT_MXINT8: hipLaunchKernelGGL((k_dequant<MXINT8, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
     case DQ_FMT_MXFP4: hipLaunchKernelGGL((k_dequant<MXFP4, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
     default: hipLaunchKernelGGL((k_dequant<NVFP4, 1>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
   }

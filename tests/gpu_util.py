@@ -4,7 +4,9 @@ import numpy as np
 import torch
 
 FORMATS = ["INT4", "MXINT4", "MXFP4", "NVFP4"]
-GROUPS = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16}
+FORMATS8 = ["INT8", "MXINT8"]
+ALL_FORMATS = FORMATS + FORMATS8
+GROUPS = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16, "INT8": 128, "MXINT8": 32}
 DEV = "cuda:0"
 
 
@@ -17,11 +19,16 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
 
 def scales_np(t: torch.Tensor, fmt: str) -> np.ndarray:
     a = t.cpu().numpy()
-    return a.view(np.uint16) if fmt == "INT4" else a
+    return a.view(np.uint16) if fmt in ("INT4", "INT8") else a
 
 
 def nibbles(codes: np.ndarray) -> np.ndarray:
     return np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(-1)
+
+
+def elements(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """One entry per element: nibbles of the 4-bit formats, bytes of the 8-bit ones."""
+    return codes.reshape(-1) if fmt in ("INT8", "MXINT8") else nibbles(codes)
 
 
 def rel_err(a, b, floor=1e-30):

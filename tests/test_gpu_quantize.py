@@ -7,7 +7,7 @@ import torch
 
 import post_quantization_dq_amd as dq
 import synth
-from gpu_util import DEV, FORMATS, GROUPS, scales_np, to_dev
+from gpu_util import ALL_FORMATS, DEV, GROUPS, scales_np, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -20,7 +20,7 @@ def _w(rows, cols, dtype, seed):
     return synth.matrix(spec, seed)
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_quantize_weights_bit_exact(oracle_lib, fmt, dtype, shape):
@@ -44,7 +44,7 @@ def test_quantize_weights_bit_exact(oracle_lib, fmt, dtype, shape):
             assert gt.item() == np.float32(ts)
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
 def test_rescale_quantize_acts_bit_exact(oracle_lib, fmt):
     X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(96, 1024), 0)
     rng = np.random.default_rng(3)
@@ -59,12 +59,13 @@ def test_rescale_quantize_acts_bit_exact(oracle_lib, fmt):
             assert gt.item() == np.float32(ts)
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
 def test_dequantize_matches_oracle(oracle_lib, fmt):
     W = _w(48, 512, "bf16", 4)
     codes, scales, ts, qhat = oracle_lib.quantize_weights(W, None, None, fmt)
-    sdt = torch.int16 if fmt == "INT4" else torch.uint8
-    sc = torch.from_numpy(scales.view(np.int16) if fmt == "INT4" else scales).to(DEV)
+    wide_scale = fmt in ("INT4", "INT8")
+    sdt = torch.int16 if wide_scale else torch.uint8
+    sc = torch.from_numpy(scales.view(np.int16) if wide_scale else scales).to(DEV)
     out = dq.dequantize(torch.from_numpy(codes).to(DEV), sc, torch.tensor([ts], dtype=torch.float32, device=DEV),
                         48, 512, fmt)
     torch.cuda.synchronize()

@@ -16,7 +16,8 @@ import torch
 
 import post_quantization_dq_amd as dq
 import synth
-from gpu_util import DEV, FORMATS, GROUPS, nibbles, near_projection_boundary, rel_err, scales_np, to_dev
+from gpu_util import (ALL_FORMATS, DEV, FORMATS, GROUPS, elements, near_projection_boundary, rel_err,
+                      scales_np, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +62,7 @@ def _compare_e2e(oracle, ref, got, fmt, what, T):
     if t_div > T:
         assert np.all(rel_err(got["r"], ref["r"]) <= 1e-5), what
         assert np.all(rel_err(got["c"], ref["c"]) <= 1e-5), what
-        nb = nibbles(got["codes"]) != nibbles(ref["codes"])
+        nb = elements(got["codes"], fmt) != elements(ref["codes"], fmt)
         assert nb.mean() <= 1e-4, (what, nb.sum())
         assert (got["scales"] != ref["scales"]).mean() <= 1e-4, what
         if fmt == "NVFP4":
@@ -92,6 +93,24 @@ def test_end_to_end_reduced(oracle_lib, name, rows, cols, iters):
     _compare_e2e(oracle_lib, ref, got, w["fmt"], name, iters)
 
 
+# the 8-bit formats on the same recipes (INT8 with both groups, fp32 and bf16 inputs)
+E2E_8BIT = [
+    ("INT8", 128, "w256x512_int4", 256, 512, 16),
+    ("INT8", 64, "down4096x14336_nvfp4", 197, 9216, 12),
+    ("MXINT8", 32, "k1024x4096_mxint4", 129, 2048, 12),
+    ("MXINT8", 32, "q4096x4096_mxfp4", 256, 4096, 8),
+]
+
+
+@pytest.mark.parametrize("fmt,group,name,rows,cols,iters", E2E_8BIT)
+def test_end_to_end_8bit(oracle_lib, fmt, group, name, rows, cols, iters):
+    W = synth.matrix(synth.WORKLOADS[name]["W"].scaled(rows, cols), 0)
+    ref = oracle_lib.solve(W, fmt, iters, group=group)
+    got = _gpu_solve(W, fmt, iters, group=group, trace=True)
+    assert got["codes"].size == rows * cols
+    _compare_e2e(oracle_lib, ref, got, fmt, f"{fmt} g{group} {name}", iters)
+
+
 @pytest.mark.parametrize("name", ["w256x512_int4", "k1024x4096_mxint4", "q4096x4096_mxfp4",
                                   "down4096x14336_nvfp4"])
 def test_end_to_end_full_size(oracle_lib, name):
@@ -115,11 +134,12 @@ def test_rejections_and_resolve_path(oracle_lib):
     assert t_div > 40, "INT4 accumulates in fp64: no boundary divergence expected"
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
 def test_teacher_forced_step(oracle_lib, fmt):
     name = {"INT4": "w256x512_int4", "MXINT4": "k1024x4096_mxint4", "MXFP4": "q4096x4096_mxfp4",
-            "NVFP4": "down4096x14336_nvfp4"}[fmt]
-    W = synth.matrix(synth.WORKLOADS[name]["W"].scaled(256, 4096 if fmt != "INT4" else 512), 0)
+            "NVFP4": "down4096x14336_nvfp4", "INT8": "w256x512_int4",
+            "MXINT8": "k1024x4096_mxint4"}[fmt]
+    W = synth.matrix(synth.WORKLOADS[name]["W"].scaled(256, 512 if name == "w256x512_int4" else 4096), 0)
     rng = np.random.default_rng(5)
     states = [oracle_lib.solve(W, fmt, k) for k in (0, 3)]
     starts = [(s["r"], s["c"]) for s in states]
@@ -142,7 +162,7 @@ def test_teacher_forced_step(oracle_lib, fmt):
         assert rel_err(got["nmse"][0], ref["nmse"][0]) <= 1e-6
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
 def test_iteration_zero_is_bit_exact(oracle_lib, fmt):
     W = synth.matrix(synth.WORKLOADS["down4096x14336_nvfp4"]["W"].scaled(77, 2048), 1)
     rng = np.random.default_rng(6)
