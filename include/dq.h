@@ -172,6 +172,32 @@ int dq_rescale_quantize_acts(const void* X, int32_t x_dtype, int64_t tokens, int
                              void* block_scales, float* tensor_scale, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Activation rescale + quantise for several projections that read the same activations
+ * (q/k/v of an attention block, gate/up of an MLP block), each with its own solved column
+ * scales c_k (same passages as dq_rescale_quantize_acts: beta is applied per consuming
+ * weight, so each projection needs its own copy of the quantised activations).  Output k is
+ * exactly what dq_rescale_quantize_acts(X, ..., c[k], spec, codes[k], block_scales[k],
+ * tensor_scales[k], ...) writes; X is read once per pass instead of once per output.
+ *   count          1..DQ_MAX_MULTI outputs.
+ *   c              HOST array of `count` device pointers (an entry may be NULL: no beta);
+ *                  c itself may be NULL (no beta for any output).
+ *   codes, block_scales, tensor_scales
+ *                  HOST arrays of `count` device pointers, each laid out as for the
+ *                  single-output call (tensor_scales only read for NVFP4; may be NULL
+ *                  otherwise).
+ *   workspace      dq_quantize_multi_workspace_bytes(...) bytes of device memory.
+ * Returns DQ_ERR_ARG for count outside 1..DQ_MAX_MULTI, otherwise the single-output call's
+ * statuses.  Asynchronous. */
+#define DQ_MAX_MULTI 8
+size_t dq_quantize_multi_workspace_bytes(int64_t tokens, int64_t cols, int32_t count,
+                                         dq_quant_spec spec);
+int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t tokens,
+                                   int64_t cols, int64_t ld, int32_t count,
+                                   const float* const* c, dq_quant_spec spec,
+                                   uint8_t* const* codes, void* const* block_scales,
+                                   float* const* tensor_scales, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* Decode codes + block scales (+ tensor scale) into fp32 values [rows][cols].  When r and/or
  * c are given the output is diag(r) Qhat diag(c) (the reconstruction), else Qhat.
  * Asynchronous. */

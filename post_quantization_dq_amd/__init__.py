@@ -1,11 +1,12 @@
 """Python binding of the DualQuant dual-scale solver library (libdq.so, gfx950).
 
 The functions named like the C entry points (``dq_solve``, ``dq_quantize_weights``,
-``dq_rescale_quantize_acts``, ``dq_dequantize``, ``dq_workspace_bytes``,
-``dq_quantize_workspace_bytes``, ``dq_status_string``, ``dq_debug_round``) only marshal
+``dq_rescale_quantize_acts``, ``dq_rescale_quantize_acts_multi``, ``dq_dequantize``,
+``dq_workspace_bytes``, ``dq_quantize_workspace_bytes``, ``dq_quantize_multi_workspace_bytes``,
+``dq_status_string``, ``dq_debug_round``) only marshal
 arguments: torch tensors supply device memory and the current HIP stream; every step of
 the computation runs in the library's HIP kernels.  ``solve``, ``quantize_weights``,
-``rescale_quantize_acts`` and ``dequantize`` are conveniences that allocate the outputs
+``rescale_quantize_acts``, ``rescale_quantize_acts_multi`` and ``dequantize`` are conveniences that allocate the outputs
 with torch and call those entry points.
 
 There is no fallback: importing the package fails if ``libdq.so`` has not been built
@@ -38,6 +39,7 @@ class dq_quant_spec(C.Structure):
 
 
 DQ_STEP_ROW, DQ_STEP_COL = 1, 2   # dq_solve_opts.scale_steps bits (0 = both)
+DQ_MAX_MULTI = 8                   # outputs of one dq_rescale_quantize_acts_multi call
 
 
 class dq_solve_opts(C.Structure):
@@ -74,13 +76,19 @@ _lib.dq_quantize_weights.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, dq_q
 _lib.dq_quantize_weights.restype = C.c_int
 _lib.dq_rescale_quantize_acts.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, dq_quant_spec, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dq_rescale_quantize_acts.restype = C.c_int
+_lib.dq_quantize_multi_workspace_bytes.argtypes = [_i64, _i64, _i32, dq_quant_spec]
+_lib.dq_quantize_multi_workspace_bytes.restype = _sz
+_lib.dq_rescale_quantize_acts_multi.argtypes = [_vp, _i32, _i64, _i64, _i64, _i32, _vp, dq_quant_spec,
+                                                _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dq_rescale_quantize_acts_multi.restype = C.c_int
 _lib.dq_dequantize.argtypes = [dq_quant_spec, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]
 _lib.dq_dequantize.restype = C.c_int
 _lib.dq_debug_round.argtypes = [_i32, _vp, _vp, _i64, _vp]
 _lib.dq_debug_round.restype = C.c_int
 
 EXPORTED = ("dq_workspace_bytes", "dq_solve", "dq_quantize_workspace_bytes", "dq_quantize_weights",
-            "dq_rescale_quantize_acts", "dq_dequantize", "dq_status_string", "dq_debug_round")
+            "dq_rescale_quantize_acts", "dq_quantize_multi_workspace_bytes",
+            "dq_rescale_quantize_acts_multi", "dq_dequantize", "dq_status_string", "dq_debug_round")
 
 
 class DQError(RuntimeError):
@@ -190,6 +198,28 @@ def dq_rescale_quantize_acts(X, c, spec, codes, block_scales, tensor_scale, work
            "dq_rescale_quantize_acts")
 
 
+def dq_quantize_multi_workspace_bytes(rows: int, cols: int, count: int, spec: dq_quant_spec) -> int:
+    return int(_lib.dq_quantize_multi_workspace_bytes(rows, cols, count, spec))
+
+
+def _ptr_array(ts) -> C.Array:
+    return (C.c_void_p * len(ts))(*[_ptr(t) for t in ts])
+
+
+def dq_rescale_quantize_acts_multi(X, cs, spec, codes, block_scales, tensor_scales, workspace,
+                                   stream=None):
+    """`cs`, `codes`, `block_scales`, `tensor_scales`: one entry per output (c entries may be
+    None); they are handed to the library as host arrays of device pointers."""
+    n = len(codes)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    c_arr = _ptr_array(cs) if cs is not None else None
+    _check(_lib.dq_rescale_quantize_acts_multi(
+        _ptr(X), DT.get(X.dtype, -1), X.shape[0], X.shape[1],
+        X.stride(0) if X.numel() else X.shape[1], n, c_arr, spec, _ptr_array(codes),
+        _ptr_array(block_scales), _ptr_array(tensor_scales), _ptr(workspace), nbytes,
+        _stream(stream)), "dq_rescale_quantize_acts_multi")
+
+
 def dq_dequantize(spec, codes, block_scales, tensor_scale, rows, cols, r, c, out, stream=None):
     _check(_lib.dq_dequantize(spec, _ptr(codes), _ptr(block_scales), _ptr(tensor_scale), rows,
                               cols, _ptr(r), _ptr(c), _ptr(out), _stream(stream)), "dq_dequantize")
@@ -286,6 +316,21 @@ def rescale_quantize_acts(X: torch.Tensor, c=None, fmt: str = "NVFP4", group: in
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=X.device)
     dq_rescale_quantize_acts(X, c, spec, codes, scales, ts, ws, stream)
     return codes, scales, ts
+
+
+def rescale_quantize_acts_multi(X: torch.Tensor, cs, fmt: str = "NVFP4", group: int | None = None,
+                                stream=None):
+    """One activation matrix, several column-scale vectors (None = no beta): returns a list
+    of (codes, scales, tensor scale), one per entry of `cs`, each equal to
+    rescale_quantize_acts(X, cs[k], ...)."""
+    group = group or DEFAULT_GROUP[fmt]
+    spec = spec_of(fmt, group)
+    outs = [_outputs(X.shape[0], X.shape[1], fmt, group, X.device) for _ in cs]
+    nb = dq_quantize_multi_workspace_bytes(X.shape[0], X.shape[1], len(cs), spec)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=X.device)
+    dq_rescale_quantize_acts_multi(X, list(cs), spec, [o[0] for o in outs], [o[1] for o in outs],
+                                   [o[2] for o in outs], ws, stream)
+    return outs
 
 
 def dequantize(codes, scales, tscale, rows: int, cols: int, fmt: str, group: int | None = None,

@@ -1004,6 +1004,145 @@ __global__ __launch_bounds__(1024) void k_quant(const void* __restrict__ X, int6
   }
 }
 
+// ---------------------------------------------------------------- multi-output activations
+// Several projections that read the same activations (q/k/v, gate/up), each with its own
+// column scales: X is read once per pass and every output gets exactly what the
+// single-output activation quantiser would produce for its c.
+constexpr int kMaxMulti = 8;
+struct MultiOut {
+  const float* c[kMaxMulti];   // column scales of each output, or null (no rescaling)
+  uint8_t* codes[kMaxMulti];
+  void* scales[kMaxMulti];
+  float* ts[kMaxMulti];
+  int count;
+};
+
+// NVFP4 amax pre-pass: the column maxima of |x| are shared; each output scales them by its
+// own |c| (rounding is monotone) and keeps one partial per workgroup: part[k][blockIdx.x].
+template <int DT>
+__global__ __launch_bounds__(256) void k_qamax_multi(const void* __restrict__ X, int64_t rows,
+                                                     int64_t cols, int64_t ld, MultiOut mo,
+                                                     float* __restrict__ part, int nstrips,
+                                                     int rows_per_range) {
+  constexpr int VEC = (DT == 1) ? 8 : 4;
+  constexpr int U = 4;
+  const int strip = (int)(blockIdx.x % nstrips), rr = (int)(blockIdx.x / nstrips);
+  const int64_t nv = cols / VEC;
+  const int64_t v = (int64_t)strip * 256 + threadIdx.x;
+  const int64_t r0 = (int64_t)rr * rows_per_range, r1 = min(rows, r0 + rows_per_range);
+  const int64_t rowbytes = ld * (DT == 1 ? 2 : 4);
+  float cm[VEC];
+#pragma unroll
+  for (int k = 0; k < VEC; ++k) cm[k] = 0.0f;
+  if (v < nv) {
+    for (int64_t i0 = r0; i0 < r1; i0 += U) {
+      u32x4 u[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int64_t i = min(i0 + q, r1 - 1);
+        u[q] = gp((const u32x4*)((const char*)X + i * rowbytes))[v];
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const uint32_t uu[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+        float w[VEC];
+        if (DT == 1) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) { w[2 * k] = u2f(uu[k] << 16); w[2 * k + 1] = u2f(uu[k] & 0xFFFF0000u); }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[k] = u2f(uu[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) cm[k] = fmaxf(cm[k], fabsf(w[k]));
+      }
+    }
+  }
+  __shared__ float sm[kMaxMulti][4];
+  // unrolled with constant indices so the pointer table stays in kernel-argument registers
+#pragma unroll
+  for (int o = 0; o < kMaxMulti; ++o) {
+    if (o >= mo.count) break;
+    float m = 0.0f;
+    if (v < nv) {
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        const float sj = mo.c[o] ? fabsf(gp(mo.c[o])[v * VEC + k]) : 1.0f;
+        m = fmaxf(m, cm[k] * sj);
+      }
+    }
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) sm[o][threadIdx.x >> 6] = m;
+  }
+  __syncthreads();
+  if (threadIdx.x < (unsigned)mo.count) {
+    const int o = threadIdx.x;
+    gp(part)[(size_t)o * gridDim.x + blockIdx.x] =
+        fmaxf(fmaxf(sm[o][0], sm[o][1]), fmaxf(sm[o][2], sm[o][3]));
+  }
+}
+
+template <int FMT, int DT, int L>
+__global__ __launch_bounds__(1024) void k_quant_multi(const void* __restrict__ X, int64_t rows,
+                                                      int64_t cols, int64_t ld, MultiOut mo,
+                                                      const float* __restrict__ part, int nparts,
+                                                      int lpr, int H) {
+  __shared__ NvTab tabs[kMaxMulti];
+  __shared__ float sk6[kMaxMulti];
+  if (FMT == NVFP4) {
+    __shared__ float smax[16];
+#pragma unroll
+    for (int o = 0; o < kMaxMulti; ++o) {
+      if (o >= mo.count) break;
+      float a = 0.0f;
+      for (int k = threadIdx.x; k < nparts; k += blockDim.x) a = fmaxf(a, gp(part)[(size_t)o * nparts + k]);
+      a = wave_max(a);
+      if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = a;
+      __syncthreads();
+      float A = 0.0f;
+      for (int k = 0; k < (int)(blockDim.x >> 6); ++k) A = fmaxf(A, smax[k]);
+      float s_t, k6;
+      bool tiny;
+      nv_tensor_terms(A, s_t, k6, tiny);
+      build_nvtab(tabs[o], s_t);
+      if (threadIdx.x == 0) sk6[o] = k6;
+      if (blockIdx.x == 0 && threadIdx.x == 0) *gp(mo.ts[o]) = s_t;
+      __syncthreads();   // smax is reused by the next output
+    }
+  }
+  const int t = threadIdx.x;
+  const int h = t / lpr, l = t - h * lpr;
+  const bool lane_ok = l < (int)(cols >> 4);
+  const int j0 = lane_ok ? l * 16 : 0;
+  for (int64_t i = (int64_t)blockIdx.x * H + h; i - h < rows; i += (int64_t)gridDim.x * H) {
+    const bool act = lane_ok && i < rows;
+    float w[16];
+    RawRow<DT> raw;
+    if (act) raw.load(X, i, ld, j0); else raw.zero();
+    raw.unpack(w);
+#pragma unroll
+    for (int o = 0; o < kMaxMulti; ++o) {
+      if (o >= mo.count) break;
+      float v[16];
+      if (mo.c[o]) {
+        float cv[16];
+        load16_global(mo.c[o] + j0, ((uintptr_t)mo.c[o] & 15u) == 0, cv);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = w[k] * cv[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = w[k];
+      }
+      QCtx qc;
+      qc.k6 = (FMT == NVFP4) ? sk6[o] : 0.0f;
+      qc.tab = &tabs[o];
+      Chunk ch;
+      quantize_chunk<FMT, L>(v, qc, ch);
+      if (act) store_chunk<FMT, L>(mo.codes[o], mo.scales[o], i, cols, l, L * 16, ch);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dequantise
 template <int FMT, int L>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,

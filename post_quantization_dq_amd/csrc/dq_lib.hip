@@ -412,6 +412,50 @@ int launch_quant_any(int fmt, int g, int dt, const void* X, int64_t rows, int64_
 
 constexpr int kQuantParts = 1024;
 
+static_assert(kMaxMulti == DQ_MAX_MULTI, "kernel and header output limits differ");
+
+template <int FMT, int DT, int L>
+int launch_quant_multi_t(const void* X, int64_t rows, int64_t cols, int64_t ld,
+                         const MultiOut& mo, float* part, int nparts, hipStream_t s) {
+  if (FMT == NVFP4) {
+    const int64_t nv = cols / (DT == DQ_F32 ? 4 : 8);
+    const int nstrips = (int)((nv + 255) / 256);
+    const int64_t ranges = std::max<int64_t>(1, std::min<int64_t>(rows, nparts / nstrips));
+    const int rpr = (int)((rows + ranges - 1) / ranges);
+    const int nwg = nstrips * (int)((rows + rpr - 1) / rpr);   // <= nparts
+    nparts = nwg;
+    hipLaunchKernelGGL((k_qamax_multi<DT>), dim3((unsigned)nwg), dim3(256), 0, s, X, rows, cols,
+                       ld, mo, part, nstrips, rpr);
+  }
+  const int lpr = lanes_per_row(cols), H = row_slots(lpr);
+  const int64_t groups = (rows + H - 1) / H;
+  const unsigned grid = (unsigned)std::min<int64_t>(groups, kQuantGroupsMax);
+  hipLaunchKernelGGL((k_quant_multi<FMT, DT, L>), dim3(grid), dim3(lpr * H), 0, s, X, rows,
+                     cols, ld, mo, part, nparts, lpr, H);
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
+int launch_quant_multi_any(int fmt, int g, int dt, const void* X, int64_t rows, int64_t cols,
+                           int64_t ld, const MultiOut& mo, float* part, int nparts,
+                           hipStream_t s) {
+#define DQ_Q(F, L)                                                                     \
+  return dt == DQ_F32 ? launch_quant_multi_t<F, 0, L>(X, rows, cols, ld, mo, part, nparts, s) \
+                      : launch_quant_multi_t<F, 1, L>(X, rows, cols, ld, mo, part, nparts, s)
+  switch (fmt) {
+    case DQ_FMT_INT4:
+      if (g == 64) { DQ_Q(INT4, 4); }
+      DQ_Q(INT4, 8);
+    case DQ_FMT_INT8:
+      if (g == 64) { DQ_Q(INT8, 4); }
+      DQ_Q(INT8, 8);
+    case DQ_FMT_MXINT4: DQ_Q(MXINT4, 2);
+    case DQ_FMT_MXINT8: DQ_Q(MXINT8, 2);
+    case DQ_FMT_MXFP4: DQ_Q(MXFP4, 2);
+    default: DQ_Q(NVFP4, 1);
+  }
+#undef DQ_Q
+}
+
 }  // namespace
 
 // ============================================================================ C ABI
@@ -680,6 +724,48 @@ int dq_rescale_quantize_acts(const void* X, int32_t x_dtype, int64_t tokens, int
                              size_t workspace_bytes, void* stream) {
   return quantize_common(1, X, x_dtype, tokens, cols, ld, nullptr, c, spec, codes, block_scales,
                          tensor_scale, workspace, workspace_bytes, stream);
+}
+
+size_t dq_quantize_multi_workspace_bytes(int64_t tokens, int64_t cols, int32_t count,
+                                         dq_quant_spec spec) {
+  (void)tokens;
+  (void)cols;
+  if (count < 1 || count > DQ_MAX_MULTI) return 0;
+  return spec.fmt == DQ_FMT_NVFP4 ? (size_t)count * kQuantParts * sizeof(float) : 0;
+}
+
+int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t tokens,
+                                   int64_t cols, int64_t ld, int32_t count,
+                                   const float* const* c, dq_quant_spec spec,
+                                   uint8_t* const* codes, void* const* block_scales,
+                                   float* const* tensor_scales, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (count < 1 || count > DQ_MAX_MULTI) return DQ_ERR_ARG;
+  int g = resolve_group(spec);
+  if (g < 0) return DQ_ERR_FORMAT;
+  int rc = check_matrix(X, x_dtype, tokens, cols, ld, g);
+  if (rc) return rc;
+  if (tokens == 0 || cols == 0) return DQ_OK;
+  if (!codes || !block_scales) return DQ_ERR_NULL;
+  if (spec.fmt == DQ_FMT_NVFP4 && !tensor_scales) return DQ_ERR_NULL;
+  MultiOut mo{};
+  mo.count = count;
+  for (int k = 0; k < count; ++k) {
+    if (!codes[k] || !block_scales[k]) return DQ_ERR_NULL;
+    if (!aligned16(codes[k]) || !aligned16(block_scales[k])) return DQ_ERR_ALIGN;
+    if (spec.fmt == DQ_FMT_NVFP4 && !tensor_scales[k]) return DQ_ERR_NULL;
+    mo.c[k] = c ? c[k] : nullptr;
+    mo.codes[k] = codes[k];
+    mo.scales[k] = block_scales[k];
+    mo.ts[k] = (spec.fmt == DQ_FMT_NVFP4) ? tensor_scales[k] : nullptr;
+  }
+  if (spec.fmt == DQ_FMT_NVFP4) {
+    if (!workspace) return DQ_ERR_WORKSPACE;
+    if (workspace_bytes < dq_quantize_multi_workspace_bytes(tokens, cols, count, spec))
+      return DQ_ERR_WORKSPACE;
+  }
+  return launch_quant_multi_any(spec.fmt, g, x_dtype, X, tokens, cols, ld, mo,
+                                (float*)workspace, kQuantParts, (hipStream_t)stream);
 }
 
 int dq_dequantize(dq_quant_spec spec, const uint8_t* codes, const void* block_scales,

@@ -89,3 +89,25 @@ def test_quantize_argument_errors(dq):
     assert L.dq_quantize_weights(0x10000, 1, 0, 256, 256, None, None, sp, 0, 0, 0, 0, 0, None) == 0   # empty
     assert L.dq_dequantize(dq.dq_quant_spec(2, 0), 0x10000, 0x20000, None, 4, 48, None, None, 0x30000, None) == -2
     assert L.dq_debug_round(99, 0x10000, 0x20000, 4, None) == -7
+
+
+def test_quantize_multi_argument_errors(dq):
+    L = dq._lib
+    sp = dq.dq_quant_spec(3, 0)
+    ptrs = (C.c_void_p * 8)(*([0x20000] * 8))
+    for n in (0, 9, -1):
+        assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 8, 256, 256, n, None, sp, ptrs, ptrs, ptrs, 0x50000, 1 << 20, None) == -7
+        assert L.dq_quantize_multi_workspace_bytes(8, 256, n, sp) == 0
+    assert L.dq_quantize_multi_workspace_bytes(8, 256, 3, sp) == 3 * L.dq_quantize_workspace_bytes(8, 256, sp)
+    assert L.dq_quantize_multi_workspace_bytes(8, 256, 3, dq.dq_quant_spec(1, 0)) == 0
+    assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 8, 200, 200, 3, None, sp, ptrs, ptrs, ptrs, 0x50000, 1 << 20, None) == -2
+    assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 8, 256, 256, 3, None, sp, None, ptrs, ptrs, 0x50000, 1 << 20, None) == -1
+    holes = (C.c_void_p * 3)(0x20000, None, 0x20000)
+    assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 8, 256, 256, 3, None, sp, holes, ptrs, ptrs, 0x50000, 1 << 20, None) == -1
+    assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 8, 256, 256, 3, None, sp, ptrs, ptrs, holes, 0x50000, 1 << 20, None) == -1
+    odd = (C.c_void_p * 3)(0x20000, 0x20008, 0x20000)
+    assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 8, 256, 256, 3, None, sp, odd, ptrs, ptrs, 0x50000, 1 << 20, None) == -3
+    assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 8, 256, 256, 3, None, sp, ptrs, ptrs, ptrs, 0x50000, 16, None) == -5
+    assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 8, 256, 256, 3, None, sp, ptrs, ptrs, ptrs, 0, 0, None) == -5
+    # tensor scales are not needed outside NVFP4
+    assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 0, 256, 256, 3, None, dq.dq_quant_spec(1, 0), ptrs, ptrs, None, None, 0, None) == 0

@@ -59,6 +59,69 @@ def test_rescale_quantize_acts_bit_exact(oracle_lib, fmt):
             assert gt.item() == np.float32(ts)
 
 
+def _check_acts(oracle_lib, X, cc, fmt, group, got):
+    gc, gs, gt = got
+    codes, scales, ts, _ = oracle_lib.rescale_quantize_acts(X, cc, fmt, group)
+    assert np.array_equal(gc.cpu().numpy(), codes)
+    assert np.array_equal(scales_np(gs, fmt), scales)
+    if fmt == "NVFP4":
+        assert gt.item() == np.float32(ts)
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(70, 1024), (5, 4096), (1, 128)])
+def test_rescale_quantize_acts_multi(oracle_lib, fmt, dtype, shape):
+    """Several column-scale vectors over one activation matrix (q/k/v-style): every output
+    bit-exact with the oracle and with the single-output entry point."""
+    from dataclasses import replace
+
+    tokens, cols = shape
+    if cols % GROUPS[fmt]:
+        pytest.skip("shape not a whole number of blocks")
+    spec = replace(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(tokens, cols), dtype=dtype)
+    X = synth.matrix(spec, 2)
+    rng = np.random.default_rng(tokens + cols)
+    cs = [oracle_lib.project(fmt, np.exp2(rng.uniform(-3, 3, cols)).astype(np.float32)),
+          None,
+          oracle_lib.project(fmt, np.exp2(rng.uniform(-1, 1, cols)).astype(np.float32))]
+    Xd = to_dev(X)
+    got = dq.rescale_quantize_acts_multi(Xd, [None if c is None else to_dev(c) for c in cs], fmt)
+    torch.cuda.synchronize()
+    assert len(got) == 3
+    for cc, g in zip(cs, got):
+        if dtype == "bf16":   # the oracle's activation entry reads bf16 activations
+            _check_acts(oracle_lib, X, cc, fmt, GROUPS[fmt], g)
+        one = dq.rescale_quantize_acts(Xd, None if cc is None else to_dev(cc), fmt)
+        torch.cuda.synchronize()
+        for a, b in zip(g, one):
+            assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("fmt", ["NVFP4", "MXINT4", "INT8"])
+def test_rescale_quantize_acts_multi_max_outputs(oracle_lib, fmt):
+    """DQ_MAX_MULTI outputs in one call, then a smaller call reusing nothing: each output
+    equals the single-output entry point's; the NVFP4 tensor scale is per output."""
+    X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(33, 2048), 5)
+    Xd = to_dev(X)
+    rng = np.random.default_rng(11)
+    cs = [to_dev(oracle_lib.project(fmt, np.exp2(rng.uniform(-4, 4, 2048)).astype(np.float32)))
+          for _ in range(dq.DQ_MAX_MULTI)]
+    for n in (dq.DQ_MAX_MULTI, 2):
+        got = dq.rescale_quantize_acts_multi(Xd, cs[:n], fmt)
+        torch.cuda.synchronize()
+        tss = set()
+        for c, g in zip(cs[:n], got):
+            one = dq.rescale_quantize_acts(Xd, c, fmt)
+            torch.cuda.synchronize()
+            for a, b in zip(g, one):
+                assert torch.equal(a, b)
+            tss.add(float(g[2].item()))
+        if fmt == "NVFP4":
+            assert len(tss) > 1
+    _check_acts(oracle_lib, X, cs[1].cpu().numpy(), fmt, GROUPS[fmt], got[1])
+
+
 @pytest.mark.parametrize("fmt", ALL_FORMATS)
 def test_dequantize_matches_oracle(oracle_lib, fmt):
     W = _w(48, 512, "bf16", 4)
