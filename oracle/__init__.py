@@ -22,9 +22,12 @@ _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "dq_oracle.cpp"
 _LIB_PATH = _HERE / "_build" / "libdq_oracle.so"
 
-FMT = {"INT4": 0, "MXINT4": 1, "MXFP4": 2, "NVFP4": 3, "INT8": 4, "MXINT8": 5}
-DEFAULT_GROUP = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16, "INT8": 128, "MXINT8": 32}
-CODE_BITS = {"INT4": 4, "MXINT4": 4, "MXFP4": 4, "NVFP4": 4, "INT8": 8, "MXINT8": 8}
+FMT = {"INT4": 0, "MXINT4": 1, "MXFP4": 2, "NVFP4": 3, "INT8": 4, "MXINT8": 5,
+       "MXFP8_E4M3": 6, "MXFP8_E5M2": 7, "MXFP6_E2M3": 8, "MXFP6_E3M2": 9}
+DEFAULT_GROUP = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16, "INT8": 128, "MXINT8": 32,
+                 "MXFP8_E4M3": 32, "MXFP8_E5M2": 32, "MXFP6_E2M3": 32, "MXFP6_E3M2": 32}
+CODE_BITS = {"INT4": 4, "MXINT4": 4, "MXFP4": 4, "NVFP4": 4, "INT8": 8, "MXINT8": 8,
+             "MXFP8_E4M3": 8, "MXFP8_E5M2": 8, "MXFP6_E2M3": 6, "MXFP6_E3M2": 6}
 
 
 def code_bytes(rows: int, cols: int, fmt: str) -> int:
@@ -63,6 +66,10 @@ def lib():
         for name in ("o_e2m1_decode", "o_e4m3_decode", "o_bf16_round"):
             getattr(L, name).argtypes = [p, p, i64]
         L.o_int_round.argtypes = [p, p, i64, C.c_int]
+        L.o_mini_encode.argtypes = [C.c_int, p, p, i64]
+        L.o_mini_encode.restype = C.c_int
+        L.o_mini_decode.argtypes = [C.c_int, p, p, i64]
+        L.o_mini_decode.restype = C.c_int
         L.o_project.argtypes = [C.c_int, p, p, i64]
         L.o_fq.argtypes = [C.c_int, C.c_int, p, i64, i64, p, p, p, p, p]
         L.o_fq.restype = C.c_int
@@ -136,6 +143,23 @@ def e4m3_decode(code: np.ndarray) -> np.ndarray:
     code = np.ascontiguousarray(code, dtype=np.uint8)
     out = np.empty(code.shape, dtype=np.float32)
     lib().o_e4m3_decode(_ptr(code), _ptr(out), code.size)
+    return out
+
+
+def mini_encode(fmt: str, x: np.ndarray) -> np.ndarray:
+    """Code (sign bit above the magnitude bits) of the nearest element of an MX FP8/FP6
+    type, ties to even, saturating."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _check(lib().o_mini_encode(FMT[fmt], _ptr(x), _ptr(out), x.size), "mini_encode")
+    return out
+
+
+def mini_decode(fmt: str, code: np.ndarray) -> np.ndarray:
+    """Values of MX FP8/FP6 element codes (NaN for the non-finite codes)."""
+    code = np.ascontiguousarray(code, dtype=np.uint8)
+    out = np.empty(code.shape, dtype=np.float32)
+    _check(lib().o_mini_decode(FMT[fmt], _ptr(code), _ptr(out), code.size), "mini_decode")
     return out
 
 

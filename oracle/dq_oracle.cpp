@@ -29,11 +29,20 @@
 
 namespace {
 
-enum Fmt { FMT_INT4 = 0, FMT_MXINT4 = 1, FMT_MXFP4 = 2, FMT_NVFP4 = 3, FMT_INT8 = 4, FMT_MXINT8 = 5 };
+enum Fmt { FMT_INT4 = 0, FMT_MXINT4 = 1, FMT_MXFP4 = 2, FMT_NVFP4 = 3, FMT_INT8 = 4, FMT_MXINT8 = 5,
+           FMT_MXFP8_E4M3 = 6, FMT_MXFP8_E5M2 = 7, FMT_MXFP6_E2M3 = 8, FMT_MXFP6_E3M2 = 9 };
 
-// Element code width: 4 bits (two per byte) or 8 bits (one per byte).
-int code_bits(int fmt) { return (fmt == FMT_INT8 || fmt == FMT_MXINT8) ? 8 : 4; }
-bool is_mx(int fmt) { return fmt == FMT_MXINT4 || fmt == FMT_MXFP4 || fmt == FMT_MXINT8; }
+bool is_mx_minifloat(int fmt) { return fmt >= FMT_MXFP8_E4M3 && fmt <= FMT_MXFP6_E3M2; }
+// Element code width: 4 bits (two per byte), 6 bits (a packed bit stream) or 8 bits (one
+// per byte).
+int code_bits(int fmt) {
+  if (fmt == FMT_INT8 || fmt == FMT_MXINT8 || fmt == FMT_MXFP8_E4M3 || fmt == FMT_MXFP8_E5M2) return 8;
+  if (fmt == FMT_MXFP6_E2M3 || fmt == FMT_MXFP6_E3M2) return 6;
+  return 4;
+}
+bool is_mx(int fmt) {
+  return fmt == FMT_MXINT4 || fmt == FMT_MXFP4 || fmt == FMT_MXINT8 || is_mx_minifloat(fmt);
+}
 bool is_int_grouped(int fmt) { return fmt == FMT_INT4 || fmt == FMT_INT8; }
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
 enum Status { OK = 0, ERR_NULL = -1, ERR_SHAPE = -2, ERR_FORMAT = -4, ERR_VALUE = -8 };
@@ -102,6 +111,71 @@ int e4m3_encode_nonneg(float x, int lowest_code) {
     if (d < bestd || (d == bestd && (k % 2) == 0)) { best = k; bestd = d; }
   }
   return best;
+}
+
+// The OCP MX v1.0 FP8 and FP6 element types: sign, ebits exponent bits with the given
+// bias, mbits mantissa bits, subnormals when the exponent field is 0.  E4M3 keeps only
+// the all-ones code as NaN (largest finite 448); E5M2 reserves the all-ones exponent for
+// infinities and NaN (largest finite 57344); the FP6 types have no special codes (E2M3
+// largest 7.5, E3M2 largest 28).  emax is the exponent of the largest binade, the offset
+// the MX shared scale removes.
+struct Minifloat {
+  int ebits, mbits, bias, emax;
+};
+Minifloat minifloat_of(int fmt) {
+  switch (fmt) {
+    case FMT_MXFP8_E4M3: return {4, 3, 7, 8};
+    case FMT_MXFP8_E5M2: return {5, 2, 15, 15};
+    case FMT_MXFP6_E2M3: return {2, 3, 1, 2};
+    default: return {3, 2, 3, 4};   // FMT_MXFP6_E3M2
+  }
+}
+// Whether a magnitude code is a finite number.
+bool mini_finite(int fmt, int mag) {
+  const Minifloat m = minifloat_of(fmt);
+  if (fmt == FMT_MXFP8_E4M3) return mag != 0x7F;
+  if (fmt == FMT_MXFP8_E5M2) return (mag >> m.mbits) != (1 << m.ebits) - 1;
+  return true;
+}
+// Value of a finite magnitude code, from the definition.
+double mini_value(int fmt, int mag) {
+  const Minifloat m = minifloat_of(fmt);
+  const int e = mag >> m.mbits, f = mag & ((1 << m.mbits) - 1);
+  if (e == 0) return std::ldexp((double)f, 1 - m.bias - m.mbits);
+  return std::ldexp(1.0 + std::ldexp((double)f, -m.mbits), e - m.bias);
+}
+int mini_mag_codes(int fmt) {
+  const Minifloat m = minifloat_of(fmt);
+  return 1 << (m.ebits + m.mbits);
+}
+double mini_max(int fmt) {
+  double best = 0.0;
+  for (int k = 0; k < mini_mag_codes(fmt); ++k)
+    if (mini_finite(fmt, k)) best = std::max(best, mini_value(fmt, k));
+  return best;
+}
+// Nearest finite value of the type to x, ties to the even code (the code's low bit is the
+// mantissa's low bit); magnitudes beyond the largest finite value saturate to it (the
+// reading taken for every MX element type, as for E2M1).  The sign bit is kept, so a
+// negative input that rounds to zero encodes as negative zero.
+int mini_encode(int fmt, float x) {
+  const double mx = mini_max(fmt);
+  const double ax = std::min(std::fabs((double)x), 2.0 * mx);
+  int best = 0;
+  double bestd = ax;
+  for (int k = 1; k < mini_mag_codes(fmt); ++k) {
+    if (!mini_finite(fmt, k)) continue;
+    const double d = std::fabs(ax - mini_value(fmt, k));
+    if (d < bestd || (d == bestd && (k % 2) == 0)) { best = k; bestd = d; }
+  }
+  const Minifloat m = minifloat_of(fmt);
+  return (std::signbit(x) ? (1 << (m.ebits + m.mbits)) : 0) | best;
+}
+double mini_decode(int fmt, int code) {
+  const Minifloat m = minifloat_of(fmt);
+  const int mag = code & ((1 << (m.ebits + m.mbits)) - 1);
+  const double v = mini_value(fmt, mag);
+  return (code >> (m.ebits + m.mbits)) & 1 ? -v : v;
 }
 
 // Nearest bfloat16 to a finite fp32 x, ties to even: the two candidates are x with its
@@ -181,9 +255,29 @@ void put_code(uint8_t* codes, int64_t idx, uint8_t nib) {
   else b = (uint8_t)((b & 0xF0) | (nib & 0x0F));
 }
 
+// 6-bit codes: element idx occupies bits 6*idx .. 6*idx+5 of the little-endian bit
+// stream of the code buffer (four elements in three bytes).
+void put_code6(uint8_t* codes, int64_t idx, int code) {
+  for (int b = 0; b < 6; ++b) {
+    const int64_t bit = 6 * idx + b;
+    uint8_t& byte = codes[bit >> 3];
+    const uint8_t mask = (uint8_t)(1u << (bit & 7));
+    byte = (uint8_t)(((code >> b) & 1) ? (byte | mask) : (byte & ~mask));
+  }
+}
+int get_code6(const uint8_t* codes, int64_t idx) {
+  int code = 0;
+  for (int b = 0; b < 6; ++b) {
+    const int64_t bit = 6 * idx + b;
+    code |= ((codes[bit >> 3] >> (bit & 7)) & 1) << b;
+  }
+  return code;
+}
+
 // Code of element idx at the format's width (two's complement for the integer formats).
 void put_code_w(int bits, uint8_t* codes, int64_t idx, int q) {
   if (bits == 8) codes[idx] = (uint8_t)(q & 0xFF);
+  else if (bits == 6) put_code6(codes, idx, q & 0x3F);
   else put_code(codes, idx, (uint8_t)(q & 0xF));
 }
 
@@ -217,15 +311,36 @@ void fq_int_row(int fmt, const float* v, int64_t row, int64_t cols, int g, FQOut
 // magnitude below 2 so the shared exponent is e = floor(log2 amax):
 // q = clamp(rint(v * 2^(6-e)), -127, 127), Qhat = q * 2^(e-6).
 // MXFP4 (OCP MX v1.0): e = floor(log2 amax) - 2, q = E2M1(v * 2^-e), Qhat = q * 2^e.
+// MXFP8 (E4M3, E5M2) and MXFP6 (E2M3, E3M2), OCP MX v1.0: e = floor(log2 amax) - emax of
+// the element type, q = nearest element value to v * 2^-e (saturating), Qhat = q * 2^e.
 // Exponents clamp to [-127, 127]; an all-zero block stores scale byte 0 and codes 0.
 void fq_mx_row(int fmt, const float* v, int64_t row, int64_t cols, int g, FQOut& o) {
   uint8_t* sc = (uint8_t*)o.scales;
+  const int bits = code_bits(fmt);
+  int off = 0;
+  if (fmt == FMT_MXFP4) off = 2;
+  if (is_mx_minifloat(fmt)) off = minifloat_of(fmt).emax;
   for (int64_t b = 0; b < cols / g; ++b) {
     const float* x = v + b * g;
     float a = 0.0f;
     for (int k = 0; k < g; ++k) a = std::max(a, std::fabs(x[k]));
     int e = -127;
-    if (a > 0.0f) e = std::max(-127, std::min(127, floor_log2(a) - (fmt == FMT_MXFP4 ? 2 : 0)));
+    if (a > 0.0f) e = std::max(-127, std::min(127, floor_log2(a) - off));
+    if (is_mx_minifloat(fmt)) {
+      sc[row * (cols / g) + b] = (uint8_t)(e + 127);
+      for (int k = 0; k < g; ++k) {
+        const int64_t idx = row * cols + b * g + k;
+        int code = 0;
+        float qh = 0.0f;
+        if (a > 0.0f) {
+          code = mini_encode(fmt, std::ldexp(x[k], -e));
+          qh = std::ldexp((float)mini_decode(fmt, code), e);
+        }
+        put_code_w(bits, o.codes, idx, code);
+        if (o.qhat) o.qhat[idx] = qh;
+      }
+      continue;
+    }
     sc[row * (cols / g) + b] = (uint8_t)(e + 127);
     for (int k = 0; k < g; ++k) {
       int64_t idx = row * cols + b * g + k;
@@ -317,8 +432,9 @@ void fq_matrix(int fmt, int g, const float* V, int64_t rows, int64_t cols, FQOut
       else fq_mx_row(fmt, v, i, cols, g, o);
     }
   });
-  // 4-bit codes of odd/even columns of one row share bytes, and rows never share bytes
-  // (cols is a multiple of the group, hence even), so the row-parallel writes are safe.
+  // 4-bit and 6-bit codes of neighbouring columns of one row share bytes, and rows never
+  // share bytes (cols is a multiple of the group, hence of 16), so the row-parallel
+  // writes are safe.
   for (auto f : fl) o.flags |= f;
 }
 
@@ -392,6 +508,23 @@ void o_e4m3_encode(const float* x, uint8_t* code, int64_t n) {
 void o_e4m3_decode(const uint8_t* code, float* x, int64_t n) {
   for (int64_t i = 0; i < n; ++i) x[i] = (float)e4m3_value(code[i] & 0x7F);
 }
+// MX FP8 / FP6 element codes (sign bit above the magnitude bits) and their values.
+int o_mini_encode(int fmt, const float* x, uint8_t* code, int64_t n) {
+  if (!is_mx_minifloat(fmt)) return ERR_FORMAT;
+  for (int64_t i = 0; i < n; ++i) code[i] = (uint8_t)mini_encode(fmt, x[i]);
+  return OK;
+}
+int o_mini_decode(int fmt, const uint8_t* code, float* x, int64_t n) {
+  if (!is_mx_minifloat(fmt)) return ERR_FORMAT;
+  const Minifloat m = minifloat_of(fmt);
+  const int mask = (1 << (m.ebits + m.mbits + 1)) - 1;
+  for (int64_t i = 0; i < n; ++i) {
+    const int c = code[i] & mask;
+    x[i] = mini_finite(fmt, c & (mask >> 1)) ? (float)mini_decode(fmt, c) : std::nanf("");
+  }
+  return OK;
+}
+
 void o_bf16_round(const float* x, float* y, int64_t n) {
   for (int64_t i = 0; i < n; ++i) y[i] = bf16_round(x[i]);
 }
@@ -444,6 +577,12 @@ int o_dequantize(int fmt, int g, const uint8_t* codes, const void* scales, float
       int64_t idx = i * cols + j;
       int64_t bi = i * (cols / g) + j / g;
       float v = 0.0f;
+      if (is_mx_minifloat(fmt)) {
+        const int code = code_bits(fmt) == 8 ? (int)codes[idx] : get_code6(codes, idx);
+        const int e = (int)((const uint8_t*)scales)[bi] - 127;
+        out[idx] = std::ldexp((float)mini_decode(fmt, code), e);
+        continue;
+      }
       if (code_bits(fmt) == 8) {
         const int q = (int)(int8_t)codes[idx];
         if (fmt == FMT_INT8) v = (float)q * bf16_to_f32(((const uint16_t*)scales)[bi]);
