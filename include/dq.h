@@ -25,13 +25,19 @@
  *   - Codes of the 4-bit formats: two per byte, low nibble = even column, [rows][cols/2].
  *     INT4 and MXINT4 codes are two's complement; MXFP4/NVFP4 codes are E2M1
  *     sign-magnitude (the sign of a negative value that rounds to zero is kept: code 0x8).
- *     Codes of the 8-bit formats (INT8, MXINT8): one two's-complement byte per element,
- *     [rows][cols].
+ *     Codes of the 8-bit formats: one byte per element, [rows][cols]; INT8 and MXINT8
+ *     two's complement, MXFP8 the OCP E4M3FN / E5M2 byte.
+ *     Codes of the 6-bit formats (MXFP6 E2M3 / E3M2, sign in bit 5): a little-endian bit
+ *     stream, element j of a row in bits 6j .. 6j+5 of the row's 3*cols/4 bytes.
+ *     The sign of a negative value that rounds to zero is kept in every float format.
  *   - Block scales: [rows][cols/group].  INT4/INT8: bf16 bit patterns (uint16), value
  *     bf16(amax/7) or bf16(amax/127).  MX formats: one E8M0 byte, value 2^(byte-127).
  *     NVFP4: one E4M3FN byte, multiplied by the fp32 tensor scale.
  *   - Dequantised value of an element: INT4/INT8 q*s; MXINT4 q*2^(e-2); MXINT8 q*2^(e-6);
- *     MXFP4 e2m1(q)*2^e; NVFP4 e2m1(q)*(e4m3(sb)*tensor_scale).
+ *     MXFP4 e2m1(q)*2^e; MXFP8/MXFP6 value(q)*2^e; NVFP4 e2m1(q)*(e4m3(sb)*tensor_scale).
+ *     The MX shared exponent is e = floor(log2 amax) - emax of the element type (MXFP4 2,
+ *     E4M3 8, E5M2 15, E2M3 2, E3M2 4; MXINT4 and MXINT8 0), elements round to nearest
+ *     with ties to even and saturate at the type's largest finite value.
  *   - Errors are returned synchronously.  Every argument check happens before any GPU work
  *     is enqueued, so a call that returns an error has enqueued nothing.  Conditions that
  *     depend on the data are reported as flag bits (DQ_FLAG_*) in dq_report.
@@ -65,7 +71,11 @@ enum {
   DQ_FMT_MXFP4 = 2,   /* 32-element blocks, E8M0 scale, E2M1 elements (OCP MX v1.0) */
   DQ_FMT_NVFP4 = 3,   /* 16-element blocks, E4M3 block scale, fp32 tensor scale, E2M1 */
   DQ_FMT_INT8 = 4,    /* symmetric INT8, per-group bf16 scale, group 64 or 128 */
-  DQ_FMT_MXINT8 = 5   /* 32-element blocks, E8M0 scale, INT8 elements x 2^-6 (OCP MX v1.0) */
+  DQ_FMT_MXINT8 = 5,  /* 32-element blocks, E8M0 scale, INT8 elements x 2^-6 (OCP MX v1.0) */
+  DQ_FMT_MXFP8_E4M3 = 6,  /* 32-element blocks, E8M0 scale, FP8 E4M3 elements (OCP MX v1.0) */
+  DQ_FMT_MXFP8_E5M2 = 7,  /* 32-element blocks, E8M0 scale, FP8 E5M2 elements */
+  DQ_FMT_MXFP6_E2M3 = 8,  /* 32-element blocks, E8M0 scale, FP6 E2M3 elements */
+  DQ_FMT_MXFP6_E3M2 = 9   /* 32-element blocks, E8M0 scale, FP6 E3M2 elements */
 };
 enum { DQ_F32 = 0, DQ_BF16 = 1 };
 

@@ -26,9 +26,12 @@ if not _LIB_PATH.exists():
     raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m post_quantization_dq_amd.build`")
 _lib = C.CDLL(str(_LIB_PATH))
 
-FMT = {"INT4": 0, "MXINT4": 1, "MXFP4": 2, "NVFP4": 3, "INT8": 4, "MXINT8": 5}
-DEFAULT_GROUP = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16, "INT8": 128, "MXINT8": 32}
-CODE_BITS = {"INT4": 4, "MXINT4": 4, "MXFP4": 4, "NVFP4": 4, "INT8": 8, "MXINT8": 8}
+FMT = {"INT4": 0, "MXINT4": 1, "MXFP4": 2, "NVFP4": 3, "INT8": 4, "MXINT8": 5,
+       "MXFP8_E4M3": 6, "MXFP8_E5M2": 7, "MXFP6_E2M3": 8, "MXFP6_E3M2": 9}
+DEFAULT_GROUP = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16, "INT8": 128, "MXINT8": 32,
+                 "MXFP8_E4M3": 32, "MXFP8_E5M2": 32, "MXFP6_E2M3": 32, "MXFP6_E3M2": 32}
+CODE_BITS = {"INT4": 4, "MXINT4": 4, "MXFP4": 4, "NVFP4": 4, "INT8": 8, "MXINT8": 8,
+             "MXFP8_E4M3": 8, "MXFP8_E5M2": 8, "MXFP6_E2M3": 6, "MXFP6_E3M2": 6}
 DT = {torch.float32: 0, torch.bfloat16: 1}
 FLAGS = {1: "nonfinite", 2: "zero_row", 4: "zero_col", 8: "nv_block_underflow", 16: "nv_tensor_underflow"}
 ROUND_FN = {"e2m1": 0, "e4m3": 1, "bf16": 2, "int4": 3, "proj_pow2": 4, "proj_e4m3": 5, "proj_bf16": 6}

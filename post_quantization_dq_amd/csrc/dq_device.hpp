@@ -20,7 +20,24 @@
 
 namespace dqk {
 
-enum Fmt { INT4 = 0, MXINT4 = 1, MXFP4 = 2, NVFP4 = 3, INT8 = 4, MXINT8 = 5 };
+enum Fmt { INT4 = 0, MXINT4 = 1, MXFP4 = 2, NVFP4 = 3, INT8 = 4, MXINT8 = 5,
+           MXFP8_E4M3 = 6, MXFP8_E5M2 = 7, MXFP6_E2M3 = 8, MXFP6_E3M2 = 9 };
+
+// The OCP MX FP8 / FP6 element types (a minifloat under an E8M0 shared exponent).
+template <int FMT>
+constexpr bool mx_mini() { return FMT >= MXFP8_E4M3 && FMT <= MXFP6_E3M2; }
+template <int FMT>
+constexpr bool mx_fp6() { return FMT == MXFP6_E2M3 || FMT == MXFP6_E3M2; }
+// Exponent of the element type's largest binade: the MX shared scale is
+// 2^(floor(log2 amax) - emax).
+template <int FMT>
+constexpr int mini_emax() {
+  return FMT == MXFP8_E4M3 ? 8 : FMT == MXFP8_E5M2 ? 15 : FMT == MXFP6_E2M3 ? 2 : 4;
+}
+template <int FMT>
+constexpr float mini_max() {
+  return FMT == MXFP8_E4M3 ? 448.0f : FMT == MXFP8_E5M2 ? 57344.0f : FMT == MXFP6_E2M3 ? 7.5f : 28.0f;
+}
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -98,7 +115,7 @@ __device__ __forceinline__ float proj_bf16(float x) {   // bf16 values in [2^-12
 }
 template <int FMT>
 __device__ __forceinline__ float project(float x) {
-  if (FMT == MXINT4 || FMT == MXFP4 || FMT == MXINT8) return proj_pow2(x);
+  if (FMT == MXINT4 || FMT == MXFP4 || FMT == MXINT8 || mx_mini<FMT>()) return proj_pow2(x);
   if (FMT == NVFP4) return proj_e4m3(x);
   return proj_bf16(x);   // INT4, INT8
 }
@@ -130,9 +147,18 @@ template <> struct Traits<MXFP4> { static constexpr int DEF_G = 32; static const
 template <> struct Traits<NVFP4> { static constexpr int DEF_G = 16; static constexpr int SCALE_BYTES = 1; };
 template <> struct Traits<INT8> { static constexpr int DEF_G = 128; static constexpr int SCALE_BYTES = 2; };
 template <> struct Traits<MXINT8> { static constexpr int DEF_G = 32; static constexpr int SCALE_BYTES = 1; };
-// 32-bit words of element codes per 16-element chunk: 4-bit codes pack into 2, 8-bit into 4.
+template <> struct Traits<MXFP8_E4M3> { static constexpr int DEF_G = 32; static constexpr int SCALE_BYTES = 1; };
+template <> struct Traits<MXFP8_E5M2> { static constexpr int DEF_G = 32; static constexpr int SCALE_BYTES = 1; };
+template <> struct Traits<MXFP6_E2M3> { static constexpr int DEF_G = 32; static constexpr int SCALE_BYTES = 1; };
+template <> struct Traits<MXFP6_E3M2> { static constexpr int DEF_G = 32; static constexpr int SCALE_BYTES = 1; };
+// 32-bit words of element codes per 16-element chunk: 4-bit codes pack into 2, 6-bit into
+// 3 (a bit stream), 8-bit into 4.
 template <int FMT>
-constexpr int code_words() { return (FMT == INT8 || FMT == MXINT8) ? 4 : 2; }
+constexpr int code_words() {
+  return (FMT == INT8 || FMT == MXINT8 || FMT == MXFP8_E4M3 || FMT == MXFP8_E5M2) ? 4
+         : mx_fp6<FMT>()                                                          ? 3
+                                                                                  : 2;
+}
 template <int FMT>
 constexpr bool grouped_int() { return FMT == INT4 || FMT == INT8; }
 
@@ -153,6 +179,7 @@ struct QCtx {
 // (NVFP4 d = e4m3(sb) * s_t, MXFP4 2^e, MXINT4 2^(e-2), MXINT8 2^(e-6), INT4/INT8 s).
 struct Chunk {
   uint32_t code[4];   // 4-bit formats: 16 nibbles, element k in bits 4k..4k+3 of words 0-1;
+                      // 6-bit formats: element k in bits 6k..6k+5 of words 0-2;
                       // 8-bit formats: 16 bytes, element k in byte k of words 0-3
   uint32_t scode;     // block scale code (bf16 bits, E8M0 byte or E4M3 byte)
   float f;            // block factor
@@ -198,6 +225,103 @@ __device__ __forceinline__ void int8_decode16(const uint32_t (&c)[4], float (&p)
 #pragma unroll
   for (int k = 0; k < 16; ++k)
     p[k] = (float)(((int)(c[k >> 2] << (24 - 8 * (k & 3)))) >> 24);   // sign-extended byte
+}
+
+// FP8 codes of x[0..15] (already within the type's finite range) and their values, with
+// the hardware conversions (round to nearest even; OCP E4M3FN / E5M2 encodings).
+template <int FMT>
+__device__ __forceinline__ void fp8_encode16(const float (&x)[16], uint32_t (&c)[4], float (&p)[16]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t u = 0u;
+    if (FMT == MXFP8_E4M3) {
+      u = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w], x[4 * w + 1], u, false);
+      u = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2], x[4 * w + 3], u, true);
+    } else {
+      u = __builtin_amdgcn_cvt_pk_bf8_f32(x[4 * w], x[4 * w + 1], u, false);
+      u = __builtin_amdgcn_cvt_pk_bf8_f32(x[4 * w + 2], x[4 * w + 3], u, true);
+    }
+    c[w] = u;
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f32x2 lo, hi;
+    if (FMT == MXFP8_E4M3) {
+      lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[w], false);
+      hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[w], true);
+    } else {
+      lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)c[w], false);
+      hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)c[w], true);
+    }
+    p[4 * w] = lo.x; p[4 * w + 1] = lo.y; p[4 * w + 2] = hi.x; p[4 * w + 3] = hi.y;
+  }
+}
+template <int FMT>
+__device__ __forceinline__ void fp8_decode16(const uint32_t (&c)[4], float (&p)[16]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f32x2 lo, hi;
+    if (FMT == MXFP8_E4M3) {
+      lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[w], false);
+      hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[w], true);
+    } else {
+      lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)c[w], false);
+      hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)c[w], true);
+    }
+    p[4 * w] = lo.x; p[4 * w + 1] = lo.y; p[4 * w + 2] = hi.x; p[4 * w + 3] = hi.y;
+  }
+}
+
+// FP6 (E2M3: bias 1, 3 mantissa bits; E3M2: bias 3, 2 mantissa bits; no special codes).
+// Nearest value to x, ties to even, saturating; returns the 6-bit code (sign in bit 5)
+// and the value (negative zero for a negative input that rounds to zero).  Below the
+// smallest normal the grid is fixed-point with step 2^(1-bias-mbits); above it the fp32
+// mantissa is rounded to mbits bits (a carry moves into the next binade).
+template <int FMT>
+__device__ __forceinline__ uint32_t fp6_encode(float x, float& val) {
+  constexpr int MB = (FMT == MXFP6_E2M3) ? 3 : 2;
+  constexpr int BIAS = (FMT == MXFP6_E2M3) ? 1 : 3;
+  constexpr float MIN_NORMAL = (FMT == MXFP6_E2M3) ? 1.0f : 0.25f;
+  constexpr float SUB_STEP_INV = (FMT == MXFP6_E2M3) ? 8.0f : 16.0f;   // 2^(bias-1+mbits)
+  const float ax = fminf(fabsf(x), mini_max<FMT>());
+  const uint32_t sgn = f2u(x) & 0x80000000u;
+  // subnormal range
+  const float q = __builtin_rintf(ax * SUB_STEP_INV);
+  const uint32_t mag_s = (uint32_t)q;
+  const float av_s = q * (1.0f / SUB_STEP_INV);
+  // normal range
+  uint32_t u = f2u(ax);
+  u += (1u << (22 - MB)) - 1u + ((u >> (23 - MB)) & 1u);
+  u &= ~((1u << (23 - MB)) - 1u);
+  const uint32_t mag_n = ((((u >> 23) - 127u + BIAS) << MB) | ((u >> (23 - MB)) & ((1u << MB) - 1u))) & 31u;
+  const bool sub = ax < MIN_NORMAL;
+  val = u2f(f2u(sub ? av_s : u2f(u)) | sgn);
+  return (sub ? mag_s : mag_n) | (sgn >> 26);
+}
+template <int FMT>
+__device__ __forceinline__ float fp6_value(uint32_t code) {
+  constexpr int MB = (FMT == MXFP6_E2M3) ? 3 : 2;
+  constexpr int BIAS = (FMT == MXFP6_E2M3) ? 1 : 3;
+  constexpr float SUB_STEP = (FMT == MXFP6_E2M3) ? 0.125f : 0.0625f;
+  const uint32_t e = (code >> MB) & ((1u << (5 - MB)) - 1u), m = code & ((1u << MB) - 1u);
+  const float av = e ? u2f(((e + 127u - BIAS) << 23) | (m << (23 - MB))) : (float)m * SUB_STEP;
+  return u2f(f2u(av) | ((code & 32u) << 26));
+}
+// 16 six-bit codes as a 96-bit stream: element k in bits 6k .. 6k+5 of words 0-2.
+__device__ __forceinline__ void fp6_pack16(const uint32_t (&k6)[16], uint32_t (&c)[4]) {
+  c[0] = c[1] = c[2] = c[3] = 0u;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int bit = 6 * k, w = bit >> 5, sh = bit & 31;
+    c[w] |= k6[k] << sh;
+    if (sh > 26) c[w + 1] |= k6[k] >> (32 - sh);
+  }
+}
+__device__ __forceinline__ uint32_t fp6_unpack(const uint32_t (&c)[4], int k) {
+  const int bit = 6 * k, w = bit >> 5, sh = bit & 31;
+  uint32_t v = c[w] >> sh;
+  if (sh > 26) v |= c[w + 1] << (32 - sh);
+  return v & 63u;
 }
 
 // Quantise one lane's 16 normalised values v (one chunk of a block of L*16).
@@ -256,6 +380,31 @@ __device__ __forceinline__ void quantize_chunk(const float (&v)[16], const QCtx&
     }
     o.code[0] = c0;
     o.code[1] = c1;
+  } else if (mx_mini<FMT>()) {
+    // OCP MX v1.0 FP8 / FP6 elements: shared exponent floor(log2 amax) - emax, elements
+    // the nearest value of v * 2^-e (scaling by a power of two is exact), saturating
+    int e = (a > 0.0f) ? floor_log2(a) - mini_emax<FMT>() : -127;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    o.scode = (uint32_t)(e + 127);
+    o.f = ldexpf(1.0f, e);
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      x[k] = __builtin_amdgcn_fmed3f(ldexpf(v[k], -e), -mini_max<FMT>(), mini_max<FMT>());
+    if (mx_fp6<FMT>()) {
+      uint32_t k6[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) k6[k] = fp6_encode<FMT>(x[k], o.p[k]);
+      fp6_pack16(k6, o.code);
+    } else {
+      fp8_encode16<FMT>(x, o.code, o.p);
+    }
+    if (a == 0.0f) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o.code[w] = 0u;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) o.p[k] = 0.0f;
+    }
   } else if (FMT == MXINT8) {
     // OCP MX v1.0 MXINT8: elements q * 2^-6 with q in [-127, 127]; shared exponent
     // floor(log2 amax)
@@ -312,14 +461,21 @@ __device__ __forceinline__ float block_factor(uint32_t scode, const NvTab* tab) 
   if (FMT == MXFP4) return ldexpf(1.0f, (int)scode - 127);
   if (FMT == MXINT4) return ldexpf(1.0f, (int)scode - 129);
   if (FMT == MXINT8) return ldexpf(1.0f, (int)scode - 133);
+  if (mx_mini<FMT>()) return ldexpf(1.0f, (int)scode - 127);
   return u2f(scode << 16);   // INT4, INT8: bf16 scale
 }
 
-// Grid values of a stored chunk (code words as stored: 2 for 4-bit, 4 for 8-bit formats).
+// Grid values of a stored chunk (code words as stored: 2 for 4-bit, 3 for 6-bit, 4 for 8-bit
+// formats).
 template <int FMT>
 __device__ __forceinline__ void decode_grid(const uint32_t (&c)[4], float (&p)[16]) {
   if (FMT == NVFP4 || FMT == MXFP4) fp4_decode16(c[0], c[1], p);
   else if (FMT == INT8 || FMT == MXINT8) int8_decode16(c, p);
+  else if (FMT == MXFP8_E4M3 || FMT == MXFP8_E5M2) fp8_decode16<FMT>(c, p);
+  else if (mx_fp6<FMT>()) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) p[k] = fp6_value<FMT>(fp6_unpack(c, k));
+  }
   else int4_decode16(c[0], c[1], p);
 }
 

@@ -73,13 +73,18 @@ struct WgEntry {
 constexpr float kTinyTensorScale = 7.888609052210118e-31f;  // 2^-100
 
 // ---------------------------------------------------------------- loads and stores
-// Codes of chunk l of row i: 8 bytes (4-bit formats) or 16 bytes (8-bit formats).
+// Codes of chunk l of row i: 8 bytes (4-bit formats), 12 bytes (6-bit) or 16 bytes (8-bit).
 template <int FMT, int L>
 __device__ __forceinline__ void store_chunk(uint8_t* codes, void* scales, int64_t i, int64_t n,
                                             int l, int g, const Chunk& ch) {
-  if (code_words<FMT>() == 4)
+  if (code_words<FMT>() == 4) {
     *gp((u32x4*)(codes + i * n + 16 * (int64_t)l)) = u32x4{ch.code[0], ch.code[1], ch.code[2], ch.code[3]};
-  else
+  } else if (code_words<FMT>() == 3) {
+    DQ_GAS uint32_t* q = gp((uint32_t*)(codes + ((i * n * 3) >> 2) + 12 * (int64_t)l));
+    q[0] = ch.code[0];
+    q[1] = ch.code[1];
+    q[2] = ch.code[2];
+  } else
     *gp((u32x2*)(codes + ((i * n) >> 1) + 8 * (int64_t)l)) = u32x2{ch.code[0], ch.code[1]};
   if ((l % L) == 0) {
     int64_t bi = i * (n / g) + l / L;
@@ -95,6 +100,9 @@ __device__ __forceinline__ void load_codes(const uint8_t* codes, const void* sca
   if (code_words<FMT>() == 4) {
     const u32x4 cw = *gp((const u32x4*)(codes + i * n + 16 * (int64_t)l));
     c[0] = cw.x; c[1] = cw.y; c[2] = cw.z; c[3] = cw.w;
+  } else if (code_words<FMT>() == 3) {
+    const DQ_GAS uint32_t* q = gp((const uint32_t*)(codes + ((i * n * 3) >> 2) + 12 * (int64_t)l));
+    c[0] = q[0]; c[1] = q[1]; c[2] = q[2]; c[3] = 0u;
   } else {
     const u32x2 cw = *gp((const u32x2*)(codes + ((i * n) >> 1) + 8 * (int64_t)l));
     c[0] = cw.x; c[1] = cw.y; c[2] = 0u; c[3] = 0u;

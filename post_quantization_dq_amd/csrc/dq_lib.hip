@@ -27,6 +27,10 @@ int default_group(int fmt) {
     case DQ_FMT_INT4: return 128;
     case DQ_FMT_INT8: return 128;
     case DQ_FMT_MXINT8: return 32;
+    case DQ_FMT_MXFP8_E4M3: return 32;
+    case DQ_FMT_MXFP8_E5M2: return 32;
+    case DQ_FMT_MXFP6_E2M3: return 32;
+    case DQ_FMT_MXFP6_E3M2: return 32;
     case DQ_FMT_MXINT4: return 32;
     case DQ_FMT_MXFP4: return 32;
     case DQ_FMT_NVFP4: return 16;
@@ -35,21 +39,28 @@ int default_group(int fmt) {
 }
 
 int resolve_group(const dq_quant_spec& s) {
-  if (s.fmt < DQ_FMT_INT4 || s.fmt > DQ_FMT_MXINT8) return -1;
+  if (s.fmt < DQ_FMT_INT4 || s.fmt > DQ_FMT_MXFP6_E3M2) return -1;
   int g = s.group ? s.group : default_group(s.fmt);
   if ((s.fmt == DQ_FMT_INT4 || s.fmt == DQ_FMT_INT8) && g != 64 && g != 128) return -1;
-  if ((s.fmt == DQ_FMT_MXINT4 || s.fmt == DQ_FMT_MXFP4 || s.fmt == DQ_FMT_MXINT8) && g != 32)
-    return -1;
+  const bool mx = s.fmt == DQ_FMT_MXINT4 || s.fmt == DQ_FMT_MXFP4 || s.fmt == DQ_FMT_MXINT8 ||
+                  (s.fmt >= DQ_FMT_MXFP8_E4M3 && s.fmt <= DQ_FMT_MXFP6_E3M2);
+  if (mx && g != 32) return -1;
   if (s.fmt == DQ_FMT_NVFP4 && g != 16) return -1;
   return g;
 }
 
 bool grouped_int_fmt(int fmt) { return fmt == DQ_FMT_INT4 || fmt == DQ_FMT_INT8; }
 int scale_bytes(int fmt) { return grouped_int_fmt(fmt) ? 2 : 1; }
-// Bytes of element codes of a rows x cols matrix: 4-bit formats two per byte, 8-bit one.
+// Bits per element code: 4 (two per byte), 6 (a bit stream) or 8.
+int code_bits(int fmt) {
+  if (fmt == DQ_FMT_INT8 || fmt == DQ_FMT_MXINT8 || fmt == DQ_FMT_MXFP8_E4M3 ||
+      fmt == DQ_FMT_MXFP8_E5M2)
+    return 8;
+  if (fmt == DQ_FMT_MXFP6_E2M3 || fmt == DQ_FMT_MXFP6_E3M2) return 6;
+  return 4;
+}
 size_t code_bytes(int fmt, int64_t rows, int64_t cols) {
-  const bool wide = fmt == DQ_FMT_INT8 || fmt == DQ_FMT_MXINT8;
-  return (size_t)rows * (size_t)cols / (wide ? 1 : 2);
+  return (size_t)rows * (size_t)cols * (size_t)code_bits(fmt) / 8;
 }
 // Column partials per row range: N, D (and the NVFP4 column amax); fp64 for INT4.
 size_t partial_bytes(int fmt, int64_t strips, int64_t cols) {
@@ -273,11 +284,12 @@ int prepare_passes(const Plan::Group& G) {
       hipFuncSetAttribute((const void*)k_rowpass<FMT, DT, L>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl) != hipSuccess)
     return DQ_ERR_HIP;
-  if (grouped_int<FMT>() &&
-      hipFuncSetAttribute((const void*)k_colpass_wide<FMT, DT, L>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)colpass_lds(FMT)) != hipSuccess)
-    return DQ_ERR_HIP;
+  if constexpr (grouped_int<FMT>()) {
+    if (hipFuncSetAttribute((const void*)k_colpass_wide<FMT, DT, L>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)colpass_lds(FMT)) != hipSuccess)
+      return DQ_ERR_HIP;
+  }
   return DQ_OK;
 }
 
@@ -292,6 +304,10 @@ int prepare_passes_any(int fmt, int g, const Plan::Group& G) {
       DQ_P(INT8, 8);
     case DQ_FMT_MXINT4: DQ_P(MXINT4, 2);
     case DQ_FMT_MXINT8: DQ_P(MXINT8, 2);
+    case DQ_FMT_MXFP8_E4M3: DQ_P(MXFP8_E4M3, 2);
+    case DQ_FMT_MXFP8_E5M2: DQ_P(MXFP8_E5M2, 2);
+    case DQ_FMT_MXFP6_E2M3: DQ_P(MXFP6_E2M3, 2);
+    case DQ_FMT_MXFP6_E3M2: DQ_P(MXFP6_E3M2, 2);
     case DQ_FMT_MXFP4: DQ_P(MXFP4, 2);
     default: DQ_P(NVFP4, 1);
   }
@@ -310,6 +326,10 @@ int launch_pass_any(int which, int fmt, int g, const Plan::Group& G, const ProbD
                      : launch_pass_dt<INT8, 8>(which, G, probs, rtab, ctab, s, sw);
     case DQ_FMT_MXINT4: return launch_pass_dt<MXINT4, 2>(which, G, probs, rtab, ctab, s, sw);
     case DQ_FMT_MXINT8: return launch_pass_dt<MXINT8, 2>(which, G, probs, rtab, ctab, s, sw);
+    case DQ_FMT_MXFP8_E4M3: return launch_pass_dt<MXFP8_E4M3, 2>(which, G, probs, rtab, ctab, s, sw);
+    case DQ_FMT_MXFP8_E5M2: return launch_pass_dt<MXFP8_E5M2, 2>(which, G, probs, rtab, ctab, s, sw);
+    case DQ_FMT_MXFP6_E2M3: return launch_pass_dt<MXFP6_E2M3, 2>(which, G, probs, rtab, ctab, s, sw);
+    case DQ_FMT_MXFP6_E3M2: return launch_pass_dt<MXFP6_E3M2, 2>(which, G, probs, rtab, ctab, s, sw);
     case DQ_FMT_MXFP4: return launch_pass_dt<MXFP4, 2>(which, G, probs, rtab, ctab, s, sw);
     default: return launch_pass_dt<NVFP4, 1>(which, G, probs, rtab, ctab, s, sw);
   }
@@ -322,6 +342,10 @@ int launch_finalize_any(int fmt, const Plan::Group& G, const ProbDev* probs,
     case DQ_FMT_INT4: launch_timed(k_finalize<INT4>, grid, block, 0, s, probs, tab, sw); break;
     case DQ_FMT_INT8: launch_timed(k_finalize<INT8>, grid, block, 0, s, probs, tab, sw); break;
     case DQ_FMT_MXINT8: launch_timed(k_finalize<MXINT8>, grid, block, 0, s, probs, tab, sw); break;
+    case DQ_FMT_MXFP8_E4M3: launch_timed(k_finalize<MXFP8_E4M3>, grid, block, 0, s, probs, tab, sw); break;
+    case DQ_FMT_MXFP8_E5M2: launch_timed(k_finalize<MXFP8_E5M2>, grid, block, 0, s, probs, tab, sw); break;
+    case DQ_FMT_MXFP6_E2M3: launch_timed(k_finalize<MXFP6_E2M3>, grid, block, 0, s, probs, tab, sw); break;
+    case DQ_FMT_MXFP6_E3M2: launch_timed(k_finalize<MXFP6_E3M2>, grid, block, 0, s, probs, tab, sw); break;
     case DQ_FMT_MXINT4: launch_timed(k_finalize<MXINT4>, grid, block, 0, s, probs, tab, sw); break;
     case DQ_FMT_MXFP4: launch_timed(k_finalize<MXFP4>, grid, block, 0, s, probs, tab, sw); break;
     default: launch_timed(k_finalize<NVFP4>, grid, block, 0, s, probs, tab, sw); break;
@@ -342,6 +366,10 @@ int launch_init_reduce_any(int fmt, int count, const ProbDev* probs, hipStream_t
     case DQ_FMT_INT4: hipLaunchKernelGGL((k_init_reduce<INT4>), grid, block, 0, s, probs); break;
     case DQ_FMT_INT8: hipLaunchKernelGGL((k_init_reduce<INT8>), grid, block, 0, s, probs); break;
     case DQ_FMT_MXINT8: hipLaunchKernelGGL((k_init_reduce<MXINT8>), grid, block, 0, s, probs); break;
+    case DQ_FMT_MXFP8_E4M3: hipLaunchKernelGGL((k_init_reduce<MXFP8_E4M3>), grid, block, 0, s, probs); break;
+    case DQ_FMT_MXFP8_E5M2: hipLaunchKernelGGL((k_init_reduce<MXFP8_E5M2>), grid, block, 0, s, probs); break;
+    case DQ_FMT_MXFP6_E2M3: hipLaunchKernelGGL((k_init_reduce<MXFP6_E2M3>), grid, block, 0, s, probs); break;
+    case DQ_FMT_MXFP6_E3M2: hipLaunchKernelGGL((k_init_reduce<MXFP6_E3M2>), grid, block, 0, s, probs); break;
     case DQ_FMT_MXINT4: hipLaunchKernelGGL((k_init_reduce<MXINT4>), grid, block, 0, s, probs); break;
     case DQ_FMT_MXFP4: hipLaunchKernelGGL((k_init_reduce<MXFP4>), grid, block, 0, s, probs); break;
     default: hipLaunchKernelGGL((k_init_reduce<NVFP4>), grid, block, 0, s, probs); break;
@@ -354,6 +382,10 @@ int launch_init_any(int fmt, int dt, dim3 grid, const ProbDev* probs, hipStream_
     case DQ_FMT_INT4: return launch_init_t<INT4>(dt, grid, probs, s);
     case DQ_FMT_INT8: return launch_init_t<INT8>(dt, grid, probs, s);
     case DQ_FMT_MXINT8: return launch_init_t<MXINT8>(dt, grid, probs, s);
+    case DQ_FMT_MXFP8_E4M3: return launch_init_t<MXFP8_E4M3>(dt, grid, probs, s);
+    case DQ_FMT_MXFP8_E5M2: return launch_init_t<MXFP8_E5M2>(dt, grid, probs, s);
+    case DQ_FMT_MXFP6_E2M3: return launch_init_t<MXFP6_E2M3>(dt, grid, probs, s);
+    case DQ_FMT_MXFP6_E3M2: return launch_init_t<MXFP6_E3M2>(dt, grid, probs, s);
     case DQ_FMT_MXINT4: return launch_init_t<MXINT4>(dt, grid, probs, s);
     case DQ_FMT_MXFP4: return launch_init_t<MXFP4>(dt, grid, probs, s);
     default: return launch_init_t<NVFP4>(dt, grid, probs, s);
@@ -404,6 +436,10 @@ int launch_quant_any(int fmt, int g, int dt, const void* X, int64_t rows, int64_
       DQ_Q(INT8, 8);
     case DQ_FMT_MXINT4: DQ_Q(MXINT4, 2);
     case DQ_FMT_MXINT8: DQ_Q(MXINT8, 2);
+    case DQ_FMT_MXFP8_E4M3: DQ_Q(MXFP8_E4M3, 2);
+    case DQ_FMT_MXFP8_E5M2: DQ_Q(MXFP8_E5M2, 2);
+    case DQ_FMT_MXFP6_E2M3: DQ_Q(MXFP6_E2M3, 2);
+    case DQ_FMT_MXFP6_E3M2: DQ_Q(MXFP6_E3M2, 2);
     case DQ_FMT_MXFP4: DQ_Q(MXFP4, 2);
     default: DQ_Q(NVFP4, 1);
   }
@@ -450,6 +486,10 @@ int launch_quant_multi_any(int fmt, int g, int dt, const void* X, int64_t rows, 
       DQ_Q(INT8, 8);
     case DQ_FMT_MXINT4: DQ_Q(MXINT4, 2);
     case DQ_FMT_MXINT8: DQ_Q(MXINT8, 2);
+    case DQ_FMT_MXFP8_E4M3: DQ_Q(MXFP8_E4M3, 2);
+    case DQ_FMT_MXFP8_E5M2: DQ_Q(MXFP8_E5M2, 2);
+    case DQ_FMT_MXFP6_E2M3: DQ_Q(MXFP6_E2M3, 2);
+    case DQ_FMT_MXFP6_E3M2: DQ_Q(MXFP6_E3M2, 2);
     case DQ_FMT_MXFP4: DQ_Q(MXFP4, 2);
     default: DQ_Q(NVFP4, 1);
   }
@@ -791,6 +831,10 @@ int dq_dequantize(dq_quant_spec spec, const uint8_t* codes, const void* block_sc
       break;
     case DQ_FMT_MXINT4: hipLaunchKernelGGL((k_dequant<MXINT4, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
     case DQ_FMT_MXINT8: hipLaunchKernelGGL((k_dequant<MXINT8, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
+    case DQ_FMT_MXFP8_E4M3: hipLaunchKernelGGL((k_dequant<MXFP8_E4M3, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
+    case DQ_FMT_MXFP8_E5M2: hipLaunchKernelGGL((k_dequant<MXFP8_E5M2, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
+    case DQ_FMT_MXFP6_E2M3: hipLaunchKernelGGL((k_dequant<MXFP6_E2M3, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
+    case DQ_FMT_MXFP6_E3M2: hipLaunchKernelGGL((k_dequant<MXFP6_E3M2, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
     case DQ_FMT_MXFP4: hipLaunchKernelGGL((k_dequant<MXFP4, 2>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
     default: hipLaunchKernelGGL((k_dequant<NVFP4, 1>), grid, block, 0, s, codes, block_scales, tensor_scale, rows, cols, r, c, out); break;
   }

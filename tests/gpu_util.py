@@ -5,8 +5,13 @@ import torch
 
 FORMATS = ["INT4", "MXINT4", "MXFP4", "NVFP4"]
 FORMATS8 = ["INT8", "MXINT8"]
-ALL_FORMATS = FORMATS + FORMATS8
-GROUPS = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16, "INT8": 128, "MXINT8": 32}
+FORMATS_MINI = ["MXFP8_E4M3", "MXFP8_E5M2", "MXFP6_E2M3", "MXFP6_E3M2"]
+ALL_FORMATS = FORMATS + FORMATS8 + FORMATS_MINI
+GROUPS = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16, "INT8": 128, "MXINT8": 32,
+          "MXFP8_E4M3": 32, "MXFP8_E5M2": 32, "MXFP6_E2M3": 32, "MXFP6_E3M2": 32}
+BITS = {f: 4 for f in FORMATS}
+BITS.update({"INT8": 8, "MXINT8": 8, "MXFP8_E4M3": 8, "MXFP8_E5M2": 8, "MXFP6_E2M3": 6,
+             "MXFP6_E3M2": 6})
 DEV = "cuda:0"
 
 
@@ -27,8 +32,15 @@ def nibbles(codes: np.ndarray) -> np.ndarray:
 
 
 def elements(codes: np.ndarray, fmt: str) -> np.ndarray:
-    """One entry per element: nibbles of the 4-bit formats, bytes of the 8-bit ones."""
-    return codes.reshape(-1) if fmt in ("INT8", "MXINT8") else nibbles(codes)
+    """One entry per element: nibbles of the 4-bit formats, 6-bit fields of the bit stream
+    of the 6-bit ones, bytes of the 8-bit ones."""
+    codes = np.ascontiguousarray(codes).reshape(-1).view(np.uint8)
+    if BITS[fmt] == 8:
+        return codes
+    if BITS[fmt] == 6:
+        bits = np.unpackbits(codes, bitorder="little").reshape(-1, 6)
+        return (bits << np.arange(6, dtype=np.uint8)).sum(axis=1).astype(np.uint8)
+    return nibbles(codes)
 
 
 def rel_err(a, b, floor=1e-30):

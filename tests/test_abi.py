@@ -51,7 +51,8 @@ def _solve_rc(dq, probs, fmt=3, group=0, iters=4, ws=0x70000, wsb=1 << 40):
 
 def test_solve_argument_errors(dq):
     ok = _problem(dq)
-    assert _solve_rc(dq, [ok], fmt=7) == -4                         # unknown format
+    assert _solve_rc(dq, [ok], fmt=10) == -4                        # unknown format
+    assert _solve_rc(dq, [ok], fmt=8, group=16) == -4               # MX blocks are 32 elements
     assert _solve_rc(dq, [ok], fmt=0, group=32) == -4               # INT4 needs 64 or 128
     assert _solve_rc(dq, [_problem(dq, cols=200)]) == -2            # not a whole number of blocks
     assert _solve_rc(dq, [_problem(dq, cols=32768)]) == -2          # wider than 16384
@@ -83,7 +84,7 @@ def test_quantize_argument_errors(dq):
     sp = dq.dq_quant_spec(3, 0)
     assert L.dq_quantize_weights(0x10000, 1, 8, 200, 200, None, None, sp, 0x20000, 0x30000, 0x40000, 0x50000, 4096, None) == -2
     assert L.dq_quantize_weights(0x10000, 1, 8, 256, 256, None, None, sp, 0x20000, 0x30000, 0x40000, 0, 0, None) == -5
-    assert L.dq_quantize_weights(0x10000, 1, 8, 256, 256, None, None, dq.dq_quant_spec(9, 0), 0x20000, 0x30000, 0x40000, 0x50000, 4096, None) == -4
+    assert L.dq_quantize_weights(0x10000, 1, 8, 256, 256, None, None, dq.dq_quant_spec(10, 0), 0x20000, 0x30000, 0x40000, 0x50000, 4096, None) == -4
     assert L.dq_rescale_quantize_acts(0x10000, 1, 8, 256, 256, None, sp, 0, 0x30000, 0x40000, 0x50000, 4096, None) == -1
     assert L.dq_rescale_quantize_acts(0x10002, 1, 8, 256, 256, None, sp, 0x20000, 0x30000, 0x40000, 0x50000, 4096, None) == -3
     assert L.dq_quantize_weights(0x10000, 1, 0, 256, 256, None, None, sp, 0, 0, 0, 0, 0, None) == 0   # empty

@@ -111,6 +111,24 @@ def test_end_to_end_8bit(oracle_lib, fmt, group, name, rows, cols, iters):
     _compare_e2e(oracle_lib, ref, got, fmt, f"{fmt} g{group} {name}", iters)
 
 
+E2E_MX_MINI = [
+    ("MXFP8_E4M3", "q4096x4096_mxfp4", 256, 4096, 10),
+    ("MXFP8_E5M2", "k1024x4096_mxint4", 129, 2048, 10),
+    ("MXFP6_E2M3", "down4096x14336_nvfp4", 197, 9216, 10),
+    ("MXFP6_E3M2", "q4096x4096_mxfp4", 256, 4096, 10),
+    ("MXFP6_E2M3", "w256x512_int4", 256, 512, 16),
+]
+
+
+@pytest.mark.parametrize("fmt,name,rows,cols,iters", E2E_MX_MINI)
+def test_end_to_end_mx_minifloat(oracle_lib, fmt, name, rows, cols, iters):
+    W = synth.matrix(synth.WORKLOADS[name]["W"].scaled(rows, cols), 0)
+    ref = oracle_lib.solve(W, fmt, iters)
+    got = _gpu_solve(W, fmt, iters, trace=True)
+    assert got["codes"].size == rows * cols * dq.CODE_BITS[fmt] // 8
+    _compare_e2e(oracle_lib, ref, got, fmt, f"{fmt} {name}", iters)
+
+
 @pytest.mark.parametrize("name", ["w256x512_int4", "k1024x4096_mxint4", "q4096x4096_mxfp4",
                                   "down4096x14336_nvfp4"])
 def test_end_to_end_full_size(oracle_lib, name):
@@ -138,7 +156,9 @@ def test_rejections_and_resolve_path(oracle_lib):
 def test_teacher_forced_step(oracle_lib, fmt):
     name = {"INT4": "w256x512_int4", "MXINT4": "k1024x4096_mxint4", "MXFP4": "q4096x4096_mxfp4",
             "NVFP4": "down4096x14336_nvfp4", "INT8": "w256x512_int4",
-            "MXINT8": "k1024x4096_mxint4"}[fmt]
+            "MXINT8": "k1024x4096_mxint4", "MXFP8_E4M3": "q4096x4096_mxfp4",
+            "MXFP8_E5M2": "k1024x4096_mxint4", "MXFP6_E2M3": "q4096x4096_mxfp4",
+            "MXFP6_E3M2": "down4096x14336_nvfp4"}[fmt]
     W = synth.matrix(synth.WORKLOADS[name]["W"].scaled(256, 512 if name == "w256x512_int4" else 4096), 0)
     rng = np.random.default_rng(5)
     states = [oracle_lib.solve(W, fmt, k) for k in (0, 3)]
