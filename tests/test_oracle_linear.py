@@ -1,0 +1,108 @@
+"""Pins for the oracle's quantised linear layer Y = deq(A) deq(B)^T diag(r) (the layer
+that consumes the activation codes and the solved weight codes; listing page Tables 11-12).
+
+Pinned by:
+- a hand-computed MXFP4 example (codes and scales written out bit by bit);
+- one-hot weights, which turn the product into a gather of the activations and so expose
+  any transposed operand or index slip;
+- MXFP8 products recomputed with torch's float8 decoding and a float64 matmul;
+- exact power-of-two scaling laws;
+- the sampled-entry variant equal to the full product.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+FMTS = ["MXFP4", "MXFP6_E2M3", "MXFP6_E3M2", "MXFP8_E4M3", "MXFP8_E5M2"]
+BITS = {"MXFP4": 4, "MXFP6_E2M3": 6, "MXFP6_E3M2": 6, "MXFP8_E4M3": 8, "MXFP8_E5M2": 8}
+
+
+def _pack(elems: np.ndarray, bits: int) -> np.ndarray:
+    """Row-major element codes -> the library's code layout (nibbles low-first, a 6-bit
+    little-endian bit stream, or bytes)."""
+    e = np.asarray(elems, dtype=np.uint8).reshape(-1)
+    if bits == 8:
+        return e.copy()
+    if bits == 4:
+        return (e[0::2] | (e[1::2] << 4)).astype(np.uint8)
+    b = ((e[:, None] >> np.arange(6, dtype=np.uint8)) & 1).astype(np.uint8).reshape(-1)
+    return np.packbits(b, bitorder="little")
+
+
+def _random_codes(rng, fmt, rows, cols):
+    bits = BITS[fmt]
+    e = rng.integers(0, 1 << bits, rows * cols).astype(np.uint8)
+    if fmt == "MXFP8_E4M3":
+        e[(e & 0x7F) == 0x7F] = 0x38
+    if fmt == "MXFP8_E5M2":
+        e[((e >> 2) & 31) == 31] = 0x3C
+    return e
+
+
+def test_hand_example_mxfp4(oracle_lib):
+    # A row: 1.0, -2.0, 0.5, 6.0 (E2M1 codes 2, 8|4, 1, 7), block scale 2^1 (byte 128)
+    # B row: 3.0, 1.5, -4.0, 0.5 (codes 5, 3, 8|6, 1), block scale 2^-1 (byte 126)
+    # sum = 1*3 - 2*1.5 - 0.5*4 + 6*0.5 = 1;  times 2 * 0.5 = 1;  r = 0.25 -> 0.25
+    a = np.zeros(32, np.uint8)
+    a[:4] = [2, 12, 1, 7]
+    b = np.zeros(32, np.uint8)
+    b[:4] = [5, 3, 14, 1]
+    y = oracle_lib.quantized_linear(_pack(a, 4), np.array([128], np.uint8), 1, _pack(b, 4),
+                                    np.array([126], np.uint8), 1, 32, "MXFP4",
+                                    r=np.array([0.25], np.float32))
+    assert y.shape == (1, 1) and y[0, 0] == 0.25
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_one_hot_weights_gather_activations(oracle_lib, fmt):
+    rng = np.random.default_rng(1)
+    M, N, K = 7, 5, 96
+    ae = _random_codes(rng, fmt, M, K)
+    asc = rng.integers(120, 135, M * K // 32).astype(np.uint8)
+    one = oracle_lib.mini_encode(fmt, np.array([1.0], np.float32))[0] if fmt != "MXFP4" else 2
+    perm = rng.permutation(K)[:N]
+    be = np.zeros((N, K), np.uint8)
+    be[np.arange(N), perm] = one
+    bsc = np.full(N * K // 32, 127, np.uint8)
+    r = np.exp2(rng.integers(-3, 4, N)).astype(np.float32)
+    y = oracle_lib.quantized_linear(_pack(ae, BITS[fmt]), asc, M, _pack(be, BITS[fmt]), bsc, N, K,
+                                    fmt, r=r)
+    deqA = oracle_lib.dequantize(_pack(ae, BITS[fmt]), asc, 0.0, fmt, M, K).astype(np.float64)
+    assert np.array_equal(y, deqA[:, perm] * r[None, :])
+
+
+@pytest.mark.parametrize("fmt,dt", [("MXFP8_E4M3", torch.float8_e4m3fn), ("MXFP8_E5M2", torch.float8_e5m2)])
+def test_fp8_against_torch(oracle_lib, fmt, dt):
+    rng = np.random.default_rng(2)
+    M, N, K = 9, 11, 160
+    ae, be = _random_codes(rng, fmt, M, K), _random_codes(rng, fmt, N, K)
+    asc = rng.integers(118, 137, M * K // 32).astype(np.uint8)
+    bsc = rng.integers(118, 137, N * K // 32).astype(np.uint8)
+    y = oracle_lib.quantized_linear(ae, asc, M, be, bsc, N, K, fmt)
+
+    def deq(e, s, rows):
+        v = torch.from_numpy(e.reshape(rows, K)).view(dt).double()
+        return v * torch.from_numpy(np.ldexp(1.0, s.astype(np.int64) - 127)).repeat_interleave(32).reshape(rows, K)
+
+    want = (deq(ae, asc, M) @ deq(be, bsc, N).T).numpy()
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_scaling_laws_and_entries(oracle_lib, fmt):
+    rng = np.random.default_rng(3)
+    M, N, K = 6, 8, 128
+    ae, be = _random_codes(rng, fmt, M, K), _random_codes(rng, fmt, N, K)
+    asc = rng.integers(122, 132, M * K // 32).astype(np.uint8)
+    bsc = rng.integers(122, 132, N * K // 32).astype(np.uint8)
+    pa, pb = _pack(ae, BITS[fmt]), _pack(be, BITS[fmt])
+    y = oracle_lib.quantized_linear(pa, asc, M, pb, bsc, N, K, fmt)
+    y2 = oracle_lib.quantized_linear(pa, asc + 1, M, pb, bsc, N, K, fmt)
+    assert np.array_equal(y2, 2 * y)
+    r = np.exp2(rng.integers(-2, 3, N)).astype(np.float32)
+    yr = oracle_lib.quantized_linear(pa, asc, M, pb, bsc, N, K, fmt, r=r)
+    assert np.array_equal(yr, y * r[None, :])
+    mi, ni = rng.integers(0, M, 20), rng.integers(0, N, 20)
+    ye, ay = oracle_lib.quantized_linear_entries(pa, asc, M, pb, bsc, N, K, fmt, mi, ni, r=r)
+    assert np.array_equal(ye, yr[mi, ni]) and np.all(ay >= np.abs(ye))
