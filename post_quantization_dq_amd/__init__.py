@@ -1,7 +1,8 @@
 """Python binding of the DualQuant dual-scale solver library (libdq.so, gfx950).
 
 The functions named like the C entry points (``dq_solve``, ``dq_quantize_weights``,
-``dq_rescale_quantize_acts``, ``dq_rescale_quantize_acts_multi``, ``dq_dequantize``,
+``dq_rescale_quantize_acts``, ``dq_rescale_quantize_acts_multi``, ``dq_quantized_linear``,
+``dq_dequantize``,
 ``dq_workspace_bytes``, ``dq_quantize_workspace_bytes``, ``dq_quantize_multi_workspace_bytes``,
 ``dq_status_string``, ``dq_debug_round``) only marshal
 arguments: torch tensors supply device memory and the current HIP stream; every step of
@@ -84,6 +85,9 @@ _lib.dq_quantize_multi_workspace_bytes.restype = _sz
 _lib.dq_rescale_quantize_acts_multi.argtypes = [_vp, _i32, _i64, _i64, _i64, _i32, _vp, dq_quant_spec,
                                                 _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dq_rescale_quantize_acts_multi.restype = C.c_int
+_lib.dq_quantized_linear.argtypes = [dq_quant_spec, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp,
+                                     _i32, _i64, _vp]
+_lib.dq_quantized_linear.restype = C.c_int
 _lib.dq_dequantize.argtypes = [dq_quant_spec, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]
 _lib.dq_dequantize.restype = C.c_int
 _lib.dq_debug_round.argtypes = [_i32, _vp, _vp, _i64, _vp]
@@ -91,7 +95,8 @@ _lib.dq_debug_round.restype = C.c_int
 
 EXPORTED = ("dq_workspace_bytes", "dq_solve", "dq_quantize_workspace_bytes", "dq_quantize_weights",
             "dq_rescale_quantize_acts", "dq_quantize_multi_workspace_bytes",
-            "dq_rescale_quantize_acts_multi", "dq_dequantize", "dq_status_string", "dq_debug_round")
+            "dq_rescale_quantize_acts_multi", "dq_quantized_linear", "dq_dequantize",
+            "dq_status_string", "dq_debug_round")
 
 
 class DQError(RuntimeError):
@@ -223,6 +228,14 @@ def dq_rescale_quantize_acts_multi(X, cs, spec, codes, block_scales, tensor_scal
         _stream(stream)), "dq_rescale_quantize_acts_multi")
 
 
+def dq_quantized_linear(spec, a_codes, a_scales, M, b_codes, b_scales, N, K, r, y, stream=None):
+    """y: a 2-D fp32 or bf16 tensor [M][>= N] (row pitch y.stride(0))."""
+    _check(_lib.dq_quantized_linear(spec, _ptr(a_codes), _ptr(a_scales), M, _ptr(b_codes),
+                                    _ptr(b_scales), N, K, _ptr(r), _ptr(y), DT.get(y.dtype, -1),
+                                    y.stride(0) if y.numel() else N, _stream(stream)),
+           "dq_quantized_linear")
+
+
 def dq_dequantize(spec, codes, block_scales, tensor_scale, rows, cols, r, c, out, stream=None):
     _check(_lib.dq_dequantize(spec, _ptr(codes), _ptr(block_scales), _ptr(tensor_scale), rows,
                               cols, _ptr(r), _ptr(c), _ptr(out), _stream(stream)), "dq_dequantize")
@@ -334,6 +347,15 @@ def rescale_quantize_acts_multi(X: torch.Tensor, cs, fmt: str = "NVFP4", group: 
     dq_rescale_quantize_acts_multi(X, list(cs), spec, [o[0] for o in outs], [o[1] for o in outs],
                                    [o[2] for o in outs], ws, stream)
     return outs
+
+
+def quantized_linear(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, fmt: str,
+                     r=None, out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    """Y [M][N] = deq(A) deq(B)^T diag(r) from activation codes A [M][K] and weight codes
+    B [N][K] of an MX format."""
+    y = torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
+    dq_quantized_linear(spec_of(fmt), a_codes, a_scales, M, b_codes, b_scales, N, K, r, y, stream)
+    return y
 
 
 def dequantize(codes, scales, tscale, rows: int, cols: int, fmt: str, group: int | None = None,

@@ -12,6 +12,7 @@
 
 #include "../../include/dq.h"
 #include "dq_kernels.hpp"
+#include "dq_linear.hpp"
 
 using namespace dqk;
 
@@ -448,6 +449,17 @@ int launch_quant_any(int fmt, int g, int dt, const void* X, int64_t rows, int64_
 
 constexpr int kQuantParts = 1024;
 
+// Quantised linear layer: dynamic LDS above 64 KiB is opted into once per instantiation.
+template <int FMT, int OB>
+int launch_linear(dim3 grid, hipStream_t s, const LinArgs& p) {
+  static const bool ready =
+      hipFuncSetAttribute((const void*)k_linear<FMT, OB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          LinGeom<FMT>::LDS) == hipSuccess;
+  if (!ready) return DQ_ERR_HIP;
+  hipLaunchKernelGGL((k_linear<FMT, OB>), grid, dim3(256), LinGeom<FMT>::LDS, s, p);
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
 static_assert(kMaxMulti == DQ_MAX_MULTI, "kernel and header output limits differ");
 
 template <int FMT, int DT, int L>
@@ -806,6 +818,43 @@ int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t token
   }
   return launch_quant_multi_any(spec.fmt, g, x_dtype, X, tokens, cols, ld, mo,
                                 (float*)workspace, kQuantParts, (hipStream_t)stream);
+}
+
+int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_t* a_scales,
+                        int64_t M, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N,
+                        int64_t K, const float* r, void* y, int32_t y_dtype, int64_t ldy,
+                        void* stream) {
+  const int g = resolve_group(spec);
+  if (g < 0) return DQ_ERR_FORMAT;
+  const int f = spec.fmt;
+  if (f != DQ_FMT_MXFP4 && f != DQ_FMT_MXFP8_E4M3 && f != DQ_FMT_MXFP8_E5M2 &&
+      f != DQ_FMT_MXFP6_E2M3 && f != DQ_FMT_MXFP6_E3M2)
+    return DQ_ERR_FORMAT;
+  if (y_dtype != DQ_F32 && y_dtype != DQ_BF16) return DQ_ERR_FORMAT;
+  if (M < 0 || N < 0 || K < 0 || K % 32 || ldy < N) return DQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return DQ_OK;
+  if (!y) return DQ_ERR_NULL;
+  if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return DQ_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(b_codes) || ((uintptr_t)y % (y_dtype == DQ_F32 ? 4 : 2)))
+    return DQ_ERR_ALIGN;
+  const int64_t tm = (M + kLinTile - 1) / kLinTile, tn = (N + kLinTile - 1) / kLinTile;
+  if (tm * tn > (int64_t)0x7FFFFFFF) return DQ_ERR_SHAPE;
+  LinArgs p{a_codes, a_scales, b_codes, b_scales, r, y, M, N, K, ldy, (int32_t)tm, (int32_t)tn};
+  hipStream_t s = (hipStream_t)stream;
+  dim3 grid((unsigned)(tm * tn)), block(256);
+#define DQ_L(F)                                                                          \
+  rc = (y_dtype == DQ_BF16) ? launch_linear<F, 1>(grid, s, p) : launch_linear<F, 0>(grid, s, p); \
+  break
+  int rc = DQ_OK;
+  switch (f) {
+    case DQ_FMT_MXFP4: DQ_L(MXFP4);
+    case DQ_FMT_MXFP8_E4M3: DQ_L(MXFP8_E4M3);
+    case DQ_FMT_MXFP8_E5M2: DQ_L(MXFP8_E5M2);
+    case DQ_FMT_MXFP6_E2M3: DQ_L(MXFP6_E2M3);
+    default: DQ_L(MXFP6_E3M2);
+  }
+#undef DQ_L
+  return rc;
 }
 
 int dq_dequantize(dq_quant_spec spec, const uint8_t* codes, const void* block_scales,

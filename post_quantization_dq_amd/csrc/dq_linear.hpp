@@ -1,0 +1,244 @@
+// Quantised linear layer on the gfx950 block-scaled matrix cores.
+//
+// The layer that consumes what the solver and the activation quantiser produce (listing
+// page Table 11, "quantized linears"; Table 12, packed 4-bit weights; news summary: the
+// column scales fold into the activation quantiser and the row scales into the output):
+//
+//     Y = X W^T ~ Aq . Q^T . diag(r),    Aq = FQ(X diag(c)),   W ~ diag(r) Q diag(c),
+//
+// with Aq [M][K] and Q [N][K] in an MX format (32-element blocks along K, E8M0 scales).
+// One V_MFMA_SCALE_F32_16X16X128_F8F6F4 multiplies a 16x128 tile of Aq by a 128x16 tile of
+// Q^T, applying both operands' block scales; its operand layout (measured):
+//   - lane l holds row (l % 16) of its tile and K-group g = l / 16;
+//   - FP4 / FP6: the 32 consecutive K elements of block g, packed as in memory (nibbles low
+//     first, or the 6-bit little-endian stream);
+//   - FP8: bytes 0-15 hold K 16g .. 16g+15 and bytes 16-31 hold K 64+16g .. 64+16g+15;
+//   - the lane's scale byte is the E8M0 scale of block g of its row;
+//   - result: lane l, element v holds C[4 (l / 16) + v][l % 16].
+// The codes are staged through LDS in their memory layout: whole-row global reads, then
+// each lane reads its fragment (one to three LDS reads) with no repacking.
+#pragma once
+
+#include <type_traits>
+
+namespace dqk {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+template <int FMT>
+constexpr int mfma_elem_fmt() {   // the instruction's element-format selector
+  return FMT == MXFP8_E4M3 ? 0 : FMT == MXFP8_E5M2 ? 1 : FMT == MXFP6_E2M3 ? 2 : FMT == MXFP6_E3M2 ? 3 : 4;
+}
+template <int FMT>
+constexpr int elem_bits() {
+  return (FMT == MXFP8_E4M3 || FMT == MXFP8_E5M2) ? 8 : mx_fp6<FMT>() ? 6 : 4;
+}
+
+constexpr int kLinTile = 128;   // workgroup tile (M and N); four waves of 64 x 64
+constexpr int kLinK = 128;      // K per instruction
+
+struct LinArgs {
+  const uint8_t* a;    // activation codes [M][K * bits / 8]
+  const uint8_t* as;   // activation block scales [M][K / 32]
+  const uint8_t* b;    // weight codes [N][K * bits / 8]
+  const uint8_t* bs;   // weight block scales [N][K / 32]
+  const float* r;      // row scales of the weights (output columns) [N], or null
+  void* y;             // output [M][ldy], fp32 or bf16
+  int64_t M, N, K, ldy;
+  int32_t tiles_m, tiles_n;
+};
+
+// Tile of this workgroup.  Workgroups are dispatched round-robin over the 8 XCDs; each XCD
+// gets a contiguous range of tiles, ordered down the M tiles of one N column first, so the
+// tiles that share weight rows (and, across columns, the activations) meet in one L2.
+__device__ __forceinline__ void lin_tile(int ntiles, int tiles_m, int& tm, int& tn) {
+  const int bid = blockIdx.x, x = bid & 7, q = ntiles >> 3, rem = ntiles & 7;
+  const int t = x * q + (x < rem ? x : rem) + (bid >> 3);
+  tm = t % tiles_m;
+  tn = t / tiles_m;
+}
+
+// Staging geometry per element width: K per stage (one or two instructions), bytes of a
+// row per stage, the global-load chunk, the padded LDS row pitch (consecutive rows start
+// 36 or 28 banks apart, so the 16 rows a fragment read touches fall on distinct banks) and
+// the scale bytes of a row per stage.
+template <int FMT>
+struct LinGeom {
+  static constexpr int EB = elem_bits<FMT>();
+  static constexpr int KS = (EB == 4) ? 256 : 128;
+  static constexpr int NI = KS / kLinK;
+  static constexpr int ROWB = KS * EB / 8;          // 128, 96, 128
+  static constexpr int CH = (EB == 6) ? 8 : 16;     // FP6 blocks are 24 bytes
+  static constexpr int CPR = ROWB / CH;             // chunks per row
+  static constexpr int PITCH = ROWB + 16;
+  static constexpr int SPR = KS / 32;               // blocks per row per stage
+  static constexpr int BB = 4 * EB;                 // bytes per block
+  static constexpr int TILE = kLinTile * PITCH;     // one operand's codes
+  static constexpr int STILE = kLinTile * SPR;      // one operand's scales
+  static constexpr int STAGE = 2 * TILE + 2 * STILE;
+  static constexpr int LDS = 2 * STAGE;             // double buffered
+  static constexpr int NCH = kLinTile * CPR / 256;  // global chunks per thread per operand
+  static constexpr int NSC = kLinTile * SPR / 256;  // scale bytes per thread per operand
+};
+
+// Global -> registers -> LDS for one stage of one operand (rows r0 .. r0+127 of a [rows][K]
+// code matrix): 256 threads read consecutive chunks, eight (or twelve) to a row, so each
+// row's stage bytes come in as whole cache-line segments.  Rows past the end read the last
+// row (their results are not stored); chunks at or beyond K read the row start and are
+// written to LDS as zeros, so the selection waits for nothing the store does not need.
+template <int FMT>
+struct LinStage {
+  using G = LinGeom<FMT>;
+  typedef uint32_t chunk_t __attribute__((ext_vector_type(G::CH / 4)));
+  chunk_t c[2][G::NCH];
+  uint32_t sc[2][G::NSC];
+
+  template <int OP>
+  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                       int64_t r0, int64_t K, int64_t st) {
+    const int64_t rowbytes = K * G::EB / 8, nblk = K / 32;
+#pragma unroll
+    for (int j = 0; j < G::NCH; ++j) {
+      const int q = threadIdx.x + 256 * j, rr = q / G::CPR, cc = q % G::CPR;
+      int64_t row = r0 + rr;
+      row = row < rows ? row : rows - 1;
+      const int64_t blk = st * G::SPR + (cc * G::CH) / G::BB;
+      const int64_t off = blk < nblk ? st * G::ROWB + cc * G::CH : 0;
+      c[OP][j] = *gp((const chunk_t*)(codes + row * rowbytes + off));
+    }
+#pragma unroll
+    for (int j = 0; j < G::NSC; ++j) {
+      const int q = threadIdx.x + 256 * j, rr = q / G::SPR, bb = q % G::SPR;
+      int64_t row = r0 + rr;
+      row = row < rows ? row : rows - 1;
+      int64_t blk = st * G::SPR + bb;
+      blk = blk < nblk ? blk : 0;
+      sc[OP][j] = gp(scales)[row * nblk + blk];
+    }
+  }
+  template <int OP>
+  __device__ __forceinline__ void store(uint8_t* lds, int64_t K, int64_t st) const {
+    uint8_t* tile = lds + OP * G::TILE;
+    uint8_t* stile = lds + 2 * G::TILE + OP * G::STILE;
+    const int64_t nblk = K / 32;
+#pragma unroll
+    for (int j = 0; j < G::NCH; ++j) {
+      const int q = threadIdx.x + 256 * j, rr = q / G::CPR, cc = q % G::CPR;
+      const bool ok = st * G::SPR + (cc * G::CH) / G::BB < nblk;
+      *(chunk_t*)(tile + rr * G::PITCH + cc * G::CH) = ok ? c[OP][j] : chunk_t(0u);
+    }
+#pragma unroll
+    for (int j = 0; j < G::NSC; ++j) stile[threadIdx.x + 256 * j] = (uint8_t)sc[OP][j];
+  }
+};
+
+// Fragment of instruction u of a stage from LDS: this lane's tile row `row` (0..127) and
+// K-group g, as the instruction wants it (see the layout at the top of this file).
+template <int FMT>
+__device__ __forceinline__ void lin_frag(const uint8_t* tile, int row, int u, int g, v8i& v) {
+  using G = LinGeom<FMT>;
+  const uint8_t* rp = tile + row * G::PITCH;
+  if (G::EB == 4) {
+    const u32x4 x = *(const u32x4*)(rp + 64 * u + 16 * g);
+    v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+  } else if (G::EB == 6) {
+    const u32x2* q = (const u32x2*)(rp + 24 * g);
+    const u32x2 x0 = q[0], x1 = q[1], x2 = q[2];
+    v = v8i{(int)x0.x, (int)x0.y, (int)x1.x, (int)x1.y, (int)x2.x, (int)x2.y, 0, 0};
+  } else {
+    const u32x4 x = *(const u32x4*)(rp + 16 * g);
+    const u32x4 y = *(const u32x4*)(rp + 64 + 16 * g);
+    v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+  }
+}
+
+// One workgroup = a 128 x 128 tile of Y; four waves of 64 x 64 (4 x 4 instruction tiles).
+// Per stage: the next stage's codes and scales are read from HBM into registers while this
+// stage's products run from LDS; then they are written to the other LDS buffer and the
+// workgroup synchronises once.
+template <int FMT, int OUT_BF16>
+__global__ __launch_bounds__(256) void k_linear(LinArgs p) {
+  using G = LinGeom<FMT>;
+  constexpr int F = mfma_elem_fmt<FMT>();
+  extern __shared__ __align__(16) uint8_t lin_lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int tm, tn;
+  lin_tile(p.tiles_m * p.tiles_n, p.tiles_m, tm, tn);
+  const int64_t mt0 = (int64_t)tm * kLinTile, nt0 = (int64_t)tn * kLinTile;
+  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int g = lane >> 4, r16 = lane & 15;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t nst = (p.K + G::KS - 1) / G::KS;
+  LinStage<FMT> stg;
+  auto fetch = [&](int64_t st) {
+    stg.template load<0>(p.a, p.as, p.M, mt0, p.K, st);
+    stg.template load<1>(p.b, p.bs, p.N, nt0, p.K, st);
+  };
+  auto put = [&](int64_t st, uint8_t* buf) {
+    stg.template store<0>(buf, p.K, st);
+    stg.template store<1>(buf, p.K, st);
+  };
+  if (nst > 0) {
+    fetch(0);
+    put(0, lin_lds);
+    __syncthreads();
+  }
+  for (int64_t st = 0; st < nst; ++st) {
+    uint8_t* cur = lin_lds + (st & 1) * G::STAGE;
+    uint8_t* nxt = lin_lds + ((st + 1) & 1) * G::STAGE;
+    const bool more = st + 1 < nst;
+    if (more) fetch(st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* ta = cur;
+    const uint8_t* tb = cur + G::TILE;
+    const uint8_t* sa_t = cur + 2 * G::TILE;
+    const uint8_t* sb_t = sa_t + G::STILE;
+#pragma unroll
+    for (int u = 0; u < G::NI; ++u) {
+      v8i a[4], b[4];
+      int sa[4], sb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lin_frag<FMT>(ta, wm + 16 * i + r16, u, g, a[i]);
+        lin_frag<FMT>(tb, wn + 16 * i + r16, u, g, b[i]);
+        sa[i] = sa_t[(wm + 16 * i + r16) * G::SPR + 4 * u + g];
+        sb[i] = sb_t[(wn + 16 * i + r16) * G::SPR + 4 * u + g];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], F, F, 0,
+                                                                        sa[i], 0, sb[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) put(st + 1, nxt);
+    __syncthreads();
+  }
+
+  // epilogue: Y[m][n] = acc * r[n]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = nt0 + wn + 16 * j + r16;
+    const float rn = (p.r && n < p.N) ? gp(p.r)[n] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = mt0 + wm + 16 * i + 4 * g + v;
+        if (m < p.M && n < p.N) {
+          const float yv = acc[i][j][v] * rn;
+          if (OUT_BF16) gp((uint16_t*)p.y)[m * p.ldy + n] = (uint16_t)(f2u(bf16_rne(yv)) >> 16);
+          else gp((float*)p.y)[m * p.ldy + n] = yv;
+        }
+      }
+  }
+}
+
+}  // namespace dqk

@@ -55,3 +55,25 @@ def near_projection_boundary(oracle, fmt: str, x: np.ndarray, tol: float = 1e-5)
     lo = oracle.project(fmt, (x * (1 - tol)).astype(np.float32))
     hi = oracle.project(fmt, (x * (1 + tol)).astype(np.float32))
     return lo != hi
+
+
+def pack_codes(elems: np.ndarray, bits: int) -> np.ndarray:
+    """Row-major element codes -> the library's code layout (nibbles low first, the 6-bit
+    little-endian bit stream, or bytes)."""
+    e = np.asarray(elems, dtype=np.uint8).reshape(-1)
+    if bits == 8:
+        return e.copy()
+    if bits == 4:
+        return (e[0::2] | (e[1::2] << 4)).astype(np.uint8)
+    b = ((e[:, None] >> np.arange(6, dtype=np.uint8)) & 1).astype(np.uint8).reshape(-1)
+    return np.packbits(b, bitorder="little")
+
+
+def random_codes(rng, fmt: str, rows: int, cols: int) -> np.ndarray:
+    """Uniformly random finite element codes of an MX format (row-major, one per element)."""
+    e = rng.integers(0, 1 << BITS[fmt], rows * cols).astype(np.uint8)
+    if fmt == "MXFP8_E4M3":
+        e[(e & 0x7F) == 0x7F] = 0x38
+    if fmt == "MXFP8_E5M2":
+        e[((e >> 2) & 31) == 31] = 0x3C
+    return e

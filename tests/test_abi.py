@@ -112,3 +112,19 @@ def test_quantize_multi_argument_errors(dq):
     assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 8, 256, 256, 3, None, sp, ptrs, ptrs, ptrs, 0, 0, None) == -5
     # tensor scales are not needed outside NVFP4
     assert L.dq_rescale_quantize_acts_multi(0x10000, 1, 0, 256, 256, 3, None, dq.dq_quant_spec(1, 0), ptrs, ptrs, None, None, 0, None) == 0
+
+
+def test_quantized_linear_argument_errors(dq):
+    L = dq._lib
+    mx = dq.dq_quant_spec(2, 0)
+    a = (0x10000, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, 0x50000)
+    assert L.dq_quantized_linear(dq.dq_quant_spec(3, 0), *a, 0, 64, None) == -4   # NVFP4
+    assert L.dq_quantized_linear(dq.dq_quant_spec(1, 0), *a, 0, 64, None) == -4   # MXINT4
+    assert L.dq_quantized_linear(mx, *a, 5, 64, None) == -4                       # dtype
+    assert L.dq_quantized_linear(mx, *a, 0, 63, None) == -2                       # ldy < N
+    assert L.dq_quantized_linear(mx, 0x10000, 0x20000, 64, 0x30000, 0x40000, 64, 100, None, 0x50000, 0, 64, None) == -2
+    assert L.dq_quantized_linear(mx, 0x10008, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, 0x50000, 0, 64, None) == -3
+    assert L.dq_quantized_linear(mx, 0x10000, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, 0x50002, 0, 64, None) == -3
+    assert L.dq_quantized_linear(mx, None, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, 0x50000, 0, 64, None) == -1
+    assert L.dq_quantized_linear(mx, 0x10000, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, None, 0, 64, None) == -1
+    assert L.dq_quantized_linear(mx, None, None, 0, None, None, 64, 256, None, None, 0, 64, None) == 0   # M = 0
