@@ -450,8 +450,21 @@ int launch_quant_any(int fmt, int g, int dt, const void* X, int64_t rows, int64_
 constexpr int kQuantParts = 1024;
 
 // Quantised linear layer: dynamic LDS above 64 KiB is opted into once per instantiation.
+// FP4 codes with K a multiple of 256 and FP8 codes with K a multiple of 128, with 4-byte
+// aligned scale arrays, take the direct-to-LDS ring; everything else the register-staged
+// kernel.
 template <int FMT, int OB>
 int launch_linear(dim3 grid, hipStream_t s, const LinArgs& p) {
+  if constexpr (elem_bits<FMT>() != 6) {
+    if (p.K % DmaGeom<FMT>::KS == 0 && ((uintptr_t)p.as & 3u) == 0 && ((uintptr_t)p.bs & 3u) == 0) {
+      static const bool ready_dma =
+          hipFuncSetAttribute((const void*)k_linear_dma<FMT, OB>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, DmaGeom<FMT>::LDS) == hipSuccess;
+      if (!ready_dma) return DQ_ERR_HIP;
+      hipLaunchKernelGGL((k_linear_dma<FMT, OB>), grid, dim3(256), DmaGeom<FMT>::LDS, s, p);
+      return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+    }
+  }
   static const bool ready =
       hipFuncSetAttribute((const void*)k_linear<FMT, OB>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           LinGeom<FMT>::LDS) == hipSuccess;

@@ -241,4 +241,174 @@ __global__ __launch_bounds__(256) void k_linear(LinArgs p) {
   }
 }
 
+// ---------------------------------------------------------------- direct-to-LDS variant
+// For FP4 codes with K a multiple of 256 and FP8 codes with K a multiple of 128.  Global loads write LDS directly
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the wave's LDS address + 16 l), so
+// no registers stage the tiles and a ring of D stages (128 K each) keeps D - 1 stages in
+// flight while one is multiplied (D = 2: the next stage loads during this one's products,
+// with no staging registers).  Rows are unpadded; within a row the 16-byte chunks are
+// XOR-swizzled by row so that the 16 rows one fragment read touches hit distinct banks.
+template <int FMT>
+struct DmaGeom {
+  static constexpr int EB = elem_bits<FMT>();
+  static constexpr int KS = (EB == 4) ? 256 : 128;      // K per stage: rows of 128 bytes
+  static constexpr int NI = KS / kLinK;                 // instructions per stage
+  static constexpr int ROWB = KS * EB / 8;              // 128
+  static constexpr int CPR = ROWB / 16;                 // 8 chunks per row
+  static constexpr int RPI = 64 / CPR;                  // 8 rows per wave instruction
+  static constexpr int SPR = KS / 32;                   // scale bytes per row per stage
+  static constexpr int TILE = kLinTile * ROWB;
+  static constexpr int STILE = kLinTile * SPR;
+  static constexpr int STAGE = 2 * TILE + 2 * STILE;
+  static constexpr int D = 2;                           // ring depth
+  static constexpr int LDS = D * STAGE;                 // 68 KiB (FP4), 66 KiB (FP8)
+  static constexpr int CODE_INSTS = kLinTile / RPI / 4; // per wave per operand per stage
+  static constexpr int SC_INSTS = SPR / 4;              // scale loads per wave per stage
+  static constexpr int INSTS = 2 * CODE_INSTS + SC_INSTS;
+};
+// Swizzle of the 16-byte chunk positions of row r (XOR into the low two bits, so a chunk
+// stays in its half of the row): the 8 rows of a fragment read's lane group start on
+// distinct banks.
+template <int FMT>
+__device__ __forceinline__ int dma_swz(int r) { return (r >> 1) & 3; }
+
+template <int FMT>
+__device__ __forceinline__ void dma_stage(const LinArgs& p, int64_t mt0, int64_t nt0, int64_t st,
+                                          uint8_t* buf) {
+  using G = DmaGeom<FMT>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rowbytes = p.K * G::EB / 8, nblk = p.K / 32;
+#pragma unroll
+  for (int op = 0; op < 2; ++op) {
+    const uint8_t* codes = op ? p.b : p.a;
+    const int64_t r0 = op ? nt0 : mt0, rows = op ? p.N : p.M;
+    uint8_t* tile = buf + op * G::TILE;
+#pragma unroll
+    for (int ii = 0; ii < G::CODE_INSTS; ++ii) {
+      const int rbase = (wave * G::CODE_INSTS + ii) * G::RPI;   // first tile row of this load
+      const int r = rbase + lane / G::CPR, c = lane % G::CPR;
+      int64_t row = r0 + r;
+      row = row < rows ? row : rows - 1;
+      const uint8_t* src = codes + row * rowbytes + st * G::ROWB + 16 * (c ^ dma_swz<FMT>(r));
+      __builtin_amdgcn_global_load_lds((const DQ_GAS void*)src,
+                                       (__attribute__((address_space(3))) void*)(tile + rbase * G::ROWB),
+                                       16, 0, 0);
+    }
+  }
+  // scales: each operand's [128][SPR] bytes in 256-byte pieces, dword q of a piece holding
+  // bytes 4 (q % (SPR / 4)) .. +3 of row q / (SPR / 4)
+#pragma unroll
+  for (int j = 0; j < G::SC_INSTS; ++j) {
+    const int q = wave * G::SC_INSTS + j;                  // 0 .. SPR - 1
+    const int op = q / (G::SPR / 2), part = q % (G::SPR / 2);
+    const int d = 64 * part + lane, r = d / (G::SPR / 4), word = d % (G::SPR / 4);
+    const uint8_t* scales = op ? p.bs : p.as;
+    const int64_t r0 = op ? nt0 : mt0, rows = op ? p.N : p.M;
+    int64_t row = r0 + r;
+    row = row < rows ? row : rows - 1;
+    const uint8_t* src = scales + row * nblk + st * G::SPR + 4 * word;
+    uint8_t* stile = buf + 2 * G::TILE + op * G::STILE + 256 * part;
+    __builtin_amdgcn_global_load_lds((const DQ_GAS void*)src,
+                                     (__attribute__((address_space(3))) void*)stile, 4, 0, 0);
+  }
+}
+
+// s_waitcnt immediate that waits until at most `vm` vector-memory operations are
+// outstanding and ignores the other counters (vmcnt in bits 3:0 and 15:14).
+__device__ __forceinline__ void wait_vmcnt(int vm) {
+  switch (vm) {
+#define DQ_W(n) case n: __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+    DQ_W(0) DQ_W(1) DQ_W(2) DQ_W(3) DQ_W(4) DQ_W(5) DQ_W(6) DQ_W(7) DQ_W(8) DQ_W(9) DQ_W(10)
+    DQ_W(11) DQ_W(12) DQ_W(13) DQ_W(14) DQ_W(15) DQ_W(16) DQ_W(17) DQ_W(18) DQ_W(19) DQ_W(20)
+#undef DQ_W
+    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
+  }
+}
+
+template <int FMT, int OUT_BF16>
+__global__ __launch_bounds__(256) void k_linear_dma(LinArgs p) {
+  using G = DmaGeom<FMT>;
+  constexpr int F = mfma_elem_fmt<FMT>();
+  extern __shared__ __align__(16) uint8_t lin_lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int tm, tn;
+  lin_tile(p.tiles_m * p.tiles_n, p.tiles_m, tm, tn);
+  const int64_t mt0 = (int64_t)tm * kLinTile, nt0 = (int64_t)tn * kLinTile;
+  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int g = lane >> 4, r16 = lane & 15;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t nst = p.K / G::KS;
+  for (int64_t s = 0; s < G::D - 1 && s < nst; ++s) dma_stage<FMT>(p, mt0, nt0, s, lin_lds + s * G::STAGE);
+  for (int64_t st = 0; st < nst; ++st) {
+    // this stage has landed once at most the later stages' loads are outstanding
+    const int64_t later = min((int64_t)(G::D - 2), nst - 1 - st);
+    wait_vmcnt((int)(later * G::INSTS));
+    // A bare barrier: every wave has waited for its own loads of this stage, and its reads
+    // of the buffer about to be refilled were consumed by its last products.  (The fence
+    // of __syncthreads would wait for all outstanding loads, draining the ring.)  The
+    // memory clobber keeps the compiler from moving LDS accesses across it.
+    asm volatile("s_barrier" ::: "memory");
+    if (st + G::D - 1 < nst)
+      dma_stage<FMT>(p, mt0, nt0, st + G::D - 1, lin_lds + ((st + G::D - 1) % G::D) * G::STAGE);
+    const uint8_t* cur = lin_lds + (st % G::D) * G::STAGE;
+    const uint8_t* sa_t = cur + 2 * G::TILE;
+    const uint8_t* sb_t = sa_t + G::STILE;
+#pragma unroll
+    for (int u = 0; u < G::NI; ++u) {
+      v8i a[4], b[4];
+      int sa[4], sb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int op = 0; op < 2; ++op) {
+          const int r = (op ? wn : wm) + 16 * i + r16;
+          const uint8_t* rp = cur + op * G::TILE + r * G::ROWB;
+          const int sw = dma_swz<FMT>(r);
+          v8i v;
+          if (G::EB == 4) {
+            const u32x4 x = *(const u32x4*)(rp + 16 * ((4 * u + g) ^ sw));
+            v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+          } else {
+            const u32x4 x = *(const u32x4*)(rp + 16 * (g ^ sw));
+            const u32x4 y = *(const u32x4*)(rp + 16 * ((4 + g) ^ sw));
+            v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+          }
+          if (op) b[i] = v; else a[i] = v;
+          const int sv = (op ? sb_t : sa_t)[r * G::SPR + 4 * u + g];
+          if (op) sb[i] = sv; else sa[i] = sv;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], F, F, 0,
+                                                                        sa[i], 0, sb[j]);
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = nt0 + wn + 16 * j + r16;
+    const float rn = (p.r && n < p.N) ? gp(p.r)[n] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = mt0 + wm + 16 * i + 4 * g + v;
+        if (m < p.M && n < p.N) {
+          const float yv = acc[i][j][v] * rn;
+          if (OUT_BF16) gp((uint16_t*)p.y)[m * p.ldy + n] = (uint16_t)(f2u(bf16_rne(yv)) >> 16);
+          else gp((float*)p.y)[m * p.ldy + n] = yv;
+        }
+      }
+  }
+}
+
 }  // namespace dqk
