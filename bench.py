@@ -17,6 +17,7 @@ on this host.
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
   python bench.py --copy-calibration     # plain copy of known size, for counter scaling
   python bench.py --workload llama31_8b_nvfp4 --steps 3 --warmup 1   # the batched 224-matrix set
+  python bench.py --workload linear_w4a4_mxfp4   # the quantised linear layer on solved codes
 """
 
 from __future__ import annotations
@@ -78,14 +79,17 @@ def cpu_baseline(W, X, fmt, iters):
 
     cores = min(16, os.cpu_count() or 1)
     oracle.set_threads(cores)
-    t0 = time.perf_counter()
-    res = oracle.solve(W, fmt, iters)
-    oracle.rescale_quantize_acts(X, res["c"], fmt)
-    dt = time.perf_counter() - t0
+    steps, t0 = 0, time.perf_counter()
+    while steps < 3 and (steps == 0 or time.perf_counter() - t0 < 10.0):   # 10 s of work or more
+        res = oracle.solve(W, fmt, iters)
+        oracle.rescale_quantize_acts(X, res["c"], fmt)
+        steps += 1
+    dt = (time.perf_counter() - t0) / steps
     m, n = W.shape
     return {"value": m * n * iters / dt / 1e9, "unit": "Gelem/s", "cores": cores, "kind": "oracle",
-            "sample": f"one whole step: {m}x{n} bf16 {fmt} solve with {iters} BCD iterations "
-                      f"plus the {X.shape[0]}x{n} activation quantise ({dt:.1f} s on {cores} threads)"}
+            "sample": f"{steps} whole steps: {m}x{n} bf16 {fmt} solve with {iters} BCD iterations "
+                      f"plus the {X.shape[0]}x{n} activation quantise ({dt:.1f} s per step on "
+                      f"{cores} threads)"}
 
 
 def bench_llama_set(args):
@@ -142,6 +146,61 @@ def bench_llama_set(args):
     print(json.dumps(out), flush=True)
 
 
+FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 matrix-core peak
+
+
+def bench_linear(args):
+    """The quantised linear layer on codes the solver and the activation quantiser made:
+    the q_proj-shaped 4096x4096 weight solved to MXFP4 (T = 16), 2048 tokens of activations
+    rescaled by the solved c and quantised to MXFP4, Y = Aq Q^T diag(r) in bf16."""
+    import torch
+
+    import post_quantization_dq_amd as dq
+    import synth
+
+    dev = torch.device("cuda:0")
+    W, _, fmt, _, T = synth.workload("q4096x4096_mxfp4")
+    N, K = W.shape
+    M = ACT_TOKENS
+    X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(M, K), 0)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    res = dq.solve(to_dev(W), fmt, T)
+    ac, asc, _ = dq.rescale_quantize_acts(to_dev(X), res["c"], fmt)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    spec = dq.spec_of(fmt)
+    call = lambda: dq.dq_quantized_linear(spec, ac, asc, M, res["codes"], res["scales"], N, K, res["r"], y)
+    print(f"[bench] quantised linear {fmt}: Y[{M}x{N}] = A[{M}x{K}] Q^T diag(r), bf16 out", flush=True)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = 2.0 * M * N * K
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "quantised linear layer TFLOP/s (W4A4 MXFP4 codes from the solver)",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
+        "config": {"workload": f"q_proj-shaped {N}x{K} weight solved to MXFP4 (T={T}); {M} tokens of "
+                               f"activations rescaled by the solved c and quantised to MXFP4; bf16 output",
+                   "M": M, "N": N, "K": K},
+        "roofline": {"bound": "mfma", "kernel": "k_linear_dma", "achieved": round(tflops, 1),
+                     "peak": FP4_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP4_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "alg_flops_per_launch": flops, "avg_launch_ms": round(ms, 4)},
+        "wall_ms_per_call": round(wall * 1e3, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,7 +214,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the solve runs on a single MI355X and this build "
+        print("bench.py measures one GPU: the solve runs on a single MI355X and the library "
               "has no multi-GPU path (pass --gpus 1).", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
@@ -163,6 +222,9 @@ def main():
         return
     if args.workload == "llama31_8b_nvfp4":
         bench_llama_set(args)
+        return
+    if args.workload == "linear_w4a4_mxfp4":
+        bench_linear(args)
         return
 
     import torch
