@@ -1,5 +1,5 @@
 // C-ABI host layer of the DualQuant solver library (gfx950): argument validation,
-// workspace layout, launch planning and the iteration driver.  See include/dq.h for the
+// workspace layout, launch planning and the iteration loop.  See include/dq.h for the
 // contract of every entry point.
 
 #include <hip/hip_ext.h>
@@ -235,7 +235,7 @@ template <int FMT>
 constexpr int lanes_per_block(int g) { return g / 16; }
 
 // Events attached to the next solver-pass launch (kernel begin / end timestamps, no extra
-// stream packets); set by the iteration driver when per-kernel timing is requested.
+// stream packets); set by the iteration loop when per-kernel timing is requested.
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
 template <typename K, typename... A>
