@@ -699,9 +699,10 @@ __global__ __launch_bounds__(512) void k_colpass_wide(const ProbDev* __restrict_
 // Column reduction of the row-range partials, c-step projection and the per-workgroup amax
 // for the next NVFP4 tensor scale.  A workgroup covers 64 columns with 4 threads per column;
 // thread part p sums ranges p, p+4, ... (sixteen loads in flight), and the four parts are
-// added in part order.  The first workgroup of each problem then takes the safeguard
-// decision from the row pass's partials (written by an earlier kernel) and writes the state
-// of the next sweep; the amax it cannot see yet is reduced by the next row pass.
+// added in part order.  One more workgroup per problem takes the safeguard decision from
+// the row pass's partials (written by an earlier kernel) and writes the state of the next
+// sweep, alongside the column workgroups; the amax partials it does not wait for are
+// reduced by the next row pass.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ probs,
                                                   const WgEntry* __restrict__ table, int sw) {
@@ -710,8 +711,11 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   const State* st = P.st + (sw & 1);
   State* sn = P.st + ((sw + 1) & 1);
   const int mode = st->mode;
+  // workgroups 0 .. fin_wgs-1 reduce columns; the one with index fin_wgs takes the
+  // safeguard decision (it needs only the row pass's partials, so it runs alongside)
+  const bool decider = (we.idx == P.fin_wgs);
   if (mode == MODE_DONE) {   // carry a finished state forward to the next sweep's slot
-    if (we.idx == 0 && threadIdx.x == 0) *sn = *st;
+    if (decider && threadIdx.x == 0) *sn = *st;
     return;
   }
   const int it = (mode == MODE_INIT) ? 0 : st->it_done + 1;
@@ -726,73 +730,75 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
 
   const int t = threadIdx.x, col = t & 63, part = t >> 6;
   bool zcol = false;
-  if (next) {
-    constexpr int NQ = (FMT == NVFP4) ? 3 : 2;
-    typedef typename std::conditional<grouped_int<FMT>(), double, float>::type acc_t;
-    const int64_t j = (int64_t)we.idx * 64 + col;
-    double N = 0.0, D = 0.0;
-    float M = 0.0f;
-    if (j < n) {
-      const int S = P.rranges;
-      const DQ_GAS acc_t* b = gp((const acc_t*)P.colP + j);
-      const size_t stride = (size_t)NQ * (size_t)n;
-      for (int b0 = 0; b0 < S; b0 += 64) {
-        acc_t vn[16], vd[16], vm[16];
+  if (!decider) {
+    if (next) {
+      constexpr int NQ = (FMT == NVFP4) ? 3 : 2;
+      typedef typename std::conditional<grouped_int<FMT>(), double, float>::type acc_t;
+      const int64_t j = (int64_t)we.idx * 64 + col;
+      double N = 0.0, D = 0.0;
+      float M = 0.0f;
+      if (j < n) {
+        const int S = P.rranges;
+        const DQ_GAS acc_t* b = gp((const acc_t*)P.colP + j);
+        const size_t stride = (size_t)NQ * (size_t)n;
+        for (int b0 = 0; b0 < S; b0 += 64) {
+          acc_t vn[16], vd[16], vm[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {   // clamped index: every load is issued, unused ones dropped
-          const int sr = min(b0 + part + 4 * u, S - 1);
-          const DQ_GAS acc_t* q = b + (size_t)sr * stride;
-          vn[u] = q[0];
-          vd[u] = q[n];
-          if (FMT == NVFP4) vm[u] = q[2 * n];
-        }
+          for (int u = 0; u < 16; ++u) {   // clamped index: every load is issued, unused ones dropped
+            const int sr = min(b0 + part + 4 * u, S - 1);
+            const DQ_GAS acc_t* q = b + (size_t)sr * stride;
+            vn[u] = q[0];
+            vd[u] = q[n];
+            if (FMT == NVFP4) vm[u] = q[2 * n];
+          }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (b0 + part + 4 * u < S) {
-            N += (double)vn[u];
-            D += (double)vd[u];
-            if (FMT == NVFP4) M = fmaxf(M, (float)vm[u]);
+          for (int u = 0; u < 16; ++u) {
+            if (b0 + part + 4 * u < S) {
+              N += (double)vn[u];
+              D += (double)vd[u];
+              if (FMT == NVFP4) M = fmaxf(M, (float)vm[u]);
+            }
           }
         }
       }
-    }
-    sred[0][part][col] = N;
-    sred[1][part][col] = D;
-    smax[part][col] = M;
-    __syncthreads();
-    float am = 0.0f;
-    if (part == 0 && j < n) {
-      N = ((sred[0][0][col] + sred[0][1][col]) + sred[0][2][col]) + sred[0][3][col];
-      D = ((sred[1][0][col] + sred[1][1][col]) + sred[1][2][col]) + sred[1][3][col];
-      M = fmaxf(fmaxf(smax[0][col], smax[1][col]), fmaxf(smax[2][col], smax[3][col]));
-      float x = __builtin_nanf("");
-      float cnew;
-      if (!(P.steps & 2)) {   // column scales frozen: c is kept
-        cnew = gp(P.c[cs])[j];
-      } else if (D > 0.0) {
-        x = (float)(N / D);
-        cnew = project<FMT>(x);
-      } else {
-        cnew = gp(P.c[cs])[j];
-        zcol = true;
+      sred[0][part][col] = N;
+      sred[1][part][col] = D;
+      smax[part][col] = M;
+      __syncthreads();
+      float am = 0.0f;
+      if (part == 0 && j < n) {
+        N = ((sred[0][0][col] + sred[0][1][col]) + sred[0][2][col]) + sred[0][3][col];
+        D = ((sred[1][0][col] + sred[1][1][col]) + sred[1][2][col]) + sred[1][3][col];
+        M = fmaxf(fmaxf(smax[0][col], smax[1][col]), fmaxf(smax[2][col], smax[3][col]));
+        float x = __builtin_nanf("");
+        float cnew;
+        if (!(P.steps & 2)) {   // column scales frozen: c is kept
+          cnew = gp(P.c[cs])[j];
+        } else if (D > 0.0) {
+          x = (float)(N / D);
+          cnew = project<FMT>(x);
+        } else {
+          cnew = gp(P.c[cs])[j];
+          zcol = true;
+        }
+        const float icn = 1.0f / cnew;
+        gp(P.c[1 - cs])[j] = cnew;
+        gp(P.ic[1 - cs])[j] = icn;
+        if (P.c_trace) gp(P.c_trace)[(int64_t)((mode == MODE_FIXUP) ? it - 1 : it) * n + j] = x;
+        if (FMT == NVFP4) am = M * icn;
       }
-      const float icn = 1.0f / cnew;
-      gp(P.c[1 - cs])[j] = cnew;
-      gp(P.ic[1 - cs])[j] = icn;
-      if (P.c_trace) gp(P.c_trace)[(int64_t)((mode == MODE_FIXUP) ? it - 1 : it) * n + j] = x;
-      if (FMT == NVFP4) am = M * icn;
+      if (FMT == NVFP4 && part == 0) {
+        am = wave_max(am);
+        if (t == 0) wmax[0] = am;
+      }
     }
-    if (FMT == NVFP4 && part == 0) {
-      am = wave_max(am);
-      if (t == 0) wmax[0] = am;
+    zcol = __syncthreads_or(zcol);
+    if (t == 0) {
+      if (next && FMT == NVFP4) gp(P.fwp)[we.idx] = wmax[0];
+      if (zcol) atomicOr(P.flags, 4u);
     }
+    return;
   }
-  zcol = __syncthreads_or(zcol);
-  if (t == 0) {
-    if (next && FMT == NVFP4) gp(P.fwp)[we.idx] = wmax[0];
-    if (zcol) atomicOr(P.flags, 4u);
-  }
-  if (we.idx != 0) return;
 
   // decision: fixed-order reductions of the row pass's partials, strided per thread, then a
   // pairwise tree over the 256 threads

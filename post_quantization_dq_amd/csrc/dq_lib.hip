@@ -179,6 +179,7 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     off = align_up(off + 2 * (size_t)(iters + 1) * sizeof(double));   // histories if caller has none
     for (int b = 0; b < d.rowblocks; ++b) G.row.push_back(WgEntry{k, b});
     for (int b = 0; b < d.nstrips * d.rranges; ++b) G.col.push_back(WgEntry{k, b});
+    G.fin.push_back(WgEntry{k, d.fin_wgs});   // the decision workgroup, dispatched first
     for (int f = 0; f < d.fin_wgs; ++f) G.fin.push_back(WgEntry{k, f});
   }
   pl.probs_off = off;
