@@ -18,6 +18,7 @@ on this host.
   python bench.py --copy-calibration     # plain copy of known size, for counter scaling
   python bench.py --workload llama31_8b_nvfp4 --steps 3 --warmup 1   # the batched 224-matrix set
   python bench.py --workload linear_w4a4_mxfp4   # the quantised linear layer on solved codes
+  python bench.py --workload qkv_acts_nvfp4      # fused q/k/v activation quantise
 """
 
 from __future__ import annotations
@@ -201,6 +202,63 @@ def bench_linear(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_qkv_acts(args):
+    """The fused multi-projection activation quantiser: 2048 tokens x 4096 bf16 activations
+    quantised to NVFP4 for three projections (q, k, v), each with its own column scales, in
+    one dq_rescale_quantize_acts_multi call; three single calls are timed beside it."""
+    import torch
+
+    import post_quantization_dq_amd as dq
+    import synth
+
+    dev = torch.device("cuda:0")
+    fmt, M, K, n_out = "NVFP4", ACT_TOKENS, 4096, 3
+    X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(M, K), 0)
+    Xd = torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).view(torch.bfloat16).to(dev)
+    rng = np.random.default_rng(5)
+    cs = [torch.from_numpy(np.exp2(rng.integers(-3, 4, K)).astype(np.float32)).to(dev) for _ in range(n_out)]
+    spec = dq.spec_of(fmt)
+    outs = [dq._outputs(M, K, fmt, dq.DEFAULT_GROUP[fmt], dev) for _ in cs]
+    ws = torch.empty(dq.dq_quantize_multi_workspace_bytes(M, K, n_out, spec), dtype=torch.uint8, device=dev)
+    multi = lambda: dq.dq_rescale_quantize_acts_multi(Xd, cs, spec, [o[0] for o in outs],
+                                                      [o[1] for o in outs], [o[2] for o in outs], ws)
+
+    def singles():
+        for c, o in zip(cs, outs):
+            dq.dq_rescale_quantize_acts(Xd, c, spec, o[0], o[1], o[2], ws)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    ms_multi, ms_single = timed(multi), timed(singles)
+    # algorithmic bytes: X read twice (amax pre-pass, quantise), codes + block scales written
+    alg = 2 * M * K * 2 + n_out * (M * K // 2 + M * K // 16)
+    gbs = alg / (ms_multi * 1e-3) / 1e9
+    out = {
+        "metric": "fused q/k/v activation quantise (NVFP4), tokens per second",
+        "value": round(M / (ms_multi * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_multi, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{M}x{K} bf16 activations, {n_out} outputs with their own column "
+                               f"scales, NVFP4", "tokens": M, "cols": K, "outputs": n_out},
+        "roofline": {"bound": "hbm", "kernel": "k_qamax_multi + k_quant_multi", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "alg_bytes_per_call": alg},
+        "three_single_calls_ms": round(ms_single, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +283,9 @@ def main():
         return
     if args.workload == "linear_w4a4_mxfp4":
         bench_linear(args)
+        return
+    if args.workload == "qkv_acts_nvfp4":
+        bench_qkv_acts(args)
         return
 
     import torch

@@ -1045,6 +1045,24 @@ __global__ __launch_bounds__(256) void k_qamax_multi(const void* __restrict__ X,
   const int64_t v = (int64_t)strip * 256 + threadIdx.x;
   const int64_t r0 = (int64_t)rr * rows_per_range, r1 = min(rows, r0 + rows_per_range);
   const int64_t rowbytes = ld * (DT == 1 ? 2 : 4);
+  // every output's |c| of this lane's columns, requested before the rows stream in so the
+  // loads complete under them
+  float sj[kMaxMulti][VEC];
+#pragma unroll
+  for (int o = 0; o < kMaxMulti; ++o) {
+    if (o < mo.count && mo.c[o] && v < nv && (((uintptr_t)mo.c[o] & 15u) == 0)) {
+#pragma unroll
+      for (int h = 0; h < VEC / 4; ++h) {
+        const f32x4 q = gp((const f32x4*)(mo.c[o] + v * VEC))[h];
+        sj[o][4 * h] = fabsf(q.x); sj[o][4 * h + 1] = fabsf(q.y);
+        sj[o][4 * h + 2] = fabsf(q.z); sj[o][4 * h + 3] = fabsf(q.w);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < VEC; ++k)
+        sj[o][k] = (o < mo.count && mo.c[o] && v < nv) ? fabsf(gp(mo.c[o])[v * VEC + k]) : 1.0f;
+    }
+  }
   float cm[VEC];
 #pragma unroll
   for (int k = 0; k < VEC; ++k) cm[k] = 0.0f;
@@ -1080,10 +1098,7 @@ __global__ __launch_bounds__(256) void k_qamax_multi(const void* __restrict__ X,
     float m = 0.0f;
     if (v < nv) {
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) {
-        const float sj = mo.c[o] ? fabsf(gp(mo.c[o])[v * VEC + k]) : 1.0f;
-        m = fmaxf(m, cm[k] * sj);
-      }
+      for (int k = 0; k < VEC; ++k) m = fmaxf(m, cm[k] * sj[o][k]);
     }
     m = wave_max(m);
     if ((threadIdx.x & 63) == 0) sm[o][threadIdx.x >> 6] = m;
@@ -1096,33 +1111,65 @@ __global__ __launch_bounds__(256) void k_qamax_multi(const void* __restrict__ X,
   }
 }
 
+// c_lds: every output's c sits in dynamic LDS (count * cols floats, chunk-interleaved as in
+// the row pass: float4 q of chunk ch of output o at (4 o + q) * nch + ch), so each row reads
+// it from LDS instead of reloading it from memory; otherwise it is read from memory per row.
 template <int FMT, int DT, int L>
 __global__ __launch_bounds__(1024) void k_quant_multi(const void* __restrict__ X, int64_t rows,
                                                       int64_t cols, int64_t ld, MultiOut mo,
                                                       const float* __restrict__ part, int nparts,
-                                                      int lpr, int H) {
+                                                      int lpr, int H, int c_lds) {
   __shared__ NvTab tabs[kMaxMulti];
   __shared__ float sk6[kMaxMulti];
+  extern __shared__ f32x4 cq[];
+  const int nch = (int)(cols >> 4);
+  if (c_lds) {
+    for (int e = threadIdx.x; e < mo.count * nch; e += blockDim.x) {
+      const int o = e / nch, ch = e - o * nch;
+      float cv[16];
+      if (mo.c[o]) load16_global(mo.c[o] + 16 * ch, ((uintptr_t)mo.c[o] & 15u) == 0, cv);
+      else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) cv[k] = 1.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        cq[(4 * o + q) * nch + ch] = f32x4{cv[4 * q], cv[4 * q + 1], cv[4 * q + 2], cv[4 * q + 3]};
+    }
+    __syncthreads();
+  }
   if (FMT == NVFP4) {
-    __shared__ float smax[16];
+    // every output's partial maxima are requested together, then reduced and turned into
+    // tables in one round (one round of load latency for all outputs, not one per output)
+    __shared__ float smax[kMaxMulti][16];
+    float a[kMaxMulti];
+#pragma unroll
+    for (int o = 0; o < kMaxMulti; ++o) a[o] = 0.0f;
+    for (int k = threadIdx.x; k < nparts; k += blockDim.x) {
+#pragma unroll
+      for (int o = 0; o < kMaxMulti; ++o)
+        if (o < mo.count) a[o] = fmaxf(a[o], gp(part)[(size_t)o * nparts + k]);
+    }
 #pragma unroll
     for (int o = 0; o < kMaxMulti; ++o) {
       if (o >= mo.count) break;
-      float a = 0.0f;
-      for (int k = threadIdx.x; k < nparts; k += blockDim.x) a = fmaxf(a, gp(part)[(size_t)o * nparts + k]);
-      a = wave_max(a);
-      if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = a;
-      __syncthreads();
+      const float w = wave_max(a[o]);
+      if ((threadIdx.x & 63) == 0) smax[o][threadIdx.x >> 6] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int o = 0; o < kMaxMulti; ++o) {
+      if (o >= mo.count) break;
       float A = 0.0f;
-      for (int k = 0; k < (int)(blockDim.x >> 6); ++k) A = fmaxf(A, smax[k]);
+      for (int k = 0; k < (int)(blockDim.x >> 6); ++k) A = fmaxf(A, smax[o][k]);
       float s_t, k6;
       bool tiny;
       nv_tensor_terms(A, s_t, k6, tiny);
       build_nvtab(tabs[o], s_t);
       if (threadIdx.x == 0) sk6[o] = k6;
       if (blockIdx.x == 0 && threadIdx.x == 0) *gp(mo.ts[o]) = s_t;
-      __syncthreads();   // smax is reused by the next output
     }
+    __syncthreads();
   }
   const int t = threadIdx.x;
   const int h = t / lpr, l = t - h * lpr;
@@ -1138,7 +1185,12 @@ __global__ __launch_bounds__(1024) void k_quant_multi(const void* __restrict__ X
     for (int o = 0; o < kMaxMulti; ++o) {
       if (o >= mo.count) break;
       float v[16];
-      if (mo.c[o]) {
+      if (c_lds && mo.c[o]) {
+        float cv[16];
+        lds_load16(cq + 4 * o * nch, nch, lane_ok ? l : 0, cv);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = w[k] * cv[k];
+      } else if (mo.c[o]) {
         float cv[16];
         load16_global(mo.c[o] + j0, ((uintptr_t)mo.c[o] & 15u) == 0, cv);
 #pragma unroll

@@ -399,9 +399,18 @@ int launch_init_any(int fmt, int dt, dim3 grid, const ProbDev* probs, hipStream_
   }
 }
 
+// Row ranges of the amax pre-pass: at most nparts workgroups in all, and at least
+// kAmaxMinRows rows per thread so each workgroup's fixed work (column scales, reduction)
+// is amortised over enough rows.
+constexpr int64_t kAmaxMinRows = 16;
+int64_t amax_ranges(int64_t rows, int nstrips, int nparts) {
+  const int64_t by_rows = std::max<int64_t>(1, rows / kAmaxMinRows);
+  return std::max<int64_t>(1, std::min<int64_t>(by_rows, nparts / nstrips));
+}
+
 // Standalone quantiser (weights: MODEV 0; activations: MODEV 1).  The quantiser grid is
 // capped so each workgroup handles several row groups.
-constexpr int64_t kQuantGroupsMax = 1024;
+constexpr int64_t kQuantGroupsMax = 256;
 template <int FMT, int DT, int L, int MODEV>
 int launch_quant_t(const void* X, int64_t rows, int64_t cols, int64_t ld, const float* r,
                    const float* c, uint8_t* codes, void* scales, float* ts, float* part,
@@ -409,7 +418,7 @@ int launch_quant_t(const void* X, int64_t rows, int64_t cols, int64_t ld, const 
   if (FMT == NVFP4) {
     const int64_t nv = cols / (DT == DQ_F32 ? 4 : 8);
     const int nstrips = (int)((nv + 255) / 256);
-    const int64_t ranges = std::max<int64_t>(1, std::min<int64_t>(rows, nparts / nstrips));
+    const int64_t ranges = amax_ranges(rows, nstrips, nparts);
     const int rpr = (int)((rows + ranges - 1) / ranges);
     const int nwg = nstrips * (int)((rows + rpr - 1) / rpr);   // <= nparts
     nparts = nwg;
@@ -480,6 +489,10 @@ int launch_linear(dim3 grid, hipStream_t s, const LinArgs& p) {
 }
 
 static_assert(kMaxMulti == DQ_MAX_MULTI, "kernel and header output limits differ");
+// The fused activation quantiser keeps every output's column scales in LDS up to this size
+// (q/k/v or gate/up of a 4096-wide model need 48 or 32 KiB); beyond it they are read from
+// memory per row.
+constexpr size_t kMultiCLds = 96 * 1024;
 
 template <int FMT, int DT, int L>
 int launch_quant_multi_t(const void* X, int64_t rows, int64_t cols, int64_t ld,
@@ -487,7 +500,7 @@ int launch_quant_multi_t(const void* X, int64_t rows, int64_t cols, int64_t ld,
   if (FMT == NVFP4) {
     const int64_t nv = cols / (DT == DQ_F32 ? 4 : 8);
     const int nstrips = (int)((nv + 255) / 256);
-    const int64_t ranges = std::max<int64_t>(1, std::min<int64_t>(rows, nparts / nstrips));
+    const int64_t ranges = amax_ranges(rows, nstrips, nparts);
     const int rpr = (int)((rows + ranges - 1) / ranges);
     const int nwg = nstrips * (int)((rows + rpr - 1) / rpr);   // <= nparts
     nparts = nwg;
@@ -497,8 +510,16 @@ int launch_quant_multi_t(const void* X, int64_t rows, int64_t cols, int64_t ld,
   const int lpr = lanes_per_row(cols), H = row_slots(lpr);
   const int64_t groups = (rows + H - 1) / H;
   const unsigned grid = (unsigned)std::min<int64_t>(groups, kQuantGroupsMax);
-  hipLaunchKernelGGL((k_quant_multi<FMT, DT, L>), dim3(grid), dim3(lpr * H), 0, s, X, rows,
-                     cols, ld, mo, part, nparts, lpr, H);
+  const size_t c_bytes = (size_t)mo.count * cols * sizeof(float);
+  const int c_lds = c_bytes <= kMultiCLds ? 1 : 0;
+  if (c_lds && c_bytes > 64 * 1024) {
+    static const bool ready = hipFuncSetAttribute((const void*)k_quant_multi<FMT, DT, L>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (int)kMultiCLds) == hipSuccess;
+    if (!ready) return DQ_ERR_HIP;
+  }
+  hipLaunchKernelGGL((k_quant_multi<FMT, DT, L>), dim3(grid), dim3(lpr * H), c_lds ? c_bytes : 0, s,
+                     X, rows, cols, ld, mo, part, nparts, lpr, H, c_lds);
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
