@@ -266,11 +266,11 @@ struct DmaGeom {
   static constexpr int SC_INSTS = SPR / 4;              // scale loads per wave per stage
   static constexpr int INSTS = 2 * CODE_INSTS + SC_INSTS;
 };
-// Swizzle of the 16-byte chunk positions of row r (XOR into the low two bits, so a chunk
-// stays in its half of the row): the 8 rows of a fragment read's lane group start on
-// distinct banks.
+// Swizzle of the 16-byte chunk positions of row r: a 128-byte row spans 32 banks, so rows
+// of one parity share banks, and XOR-ing the chunk index with (r >> 1) & 7 gives the 16 rows
+// of a fragment read 16 distinct 4-bank groups.
 template <int FMT>
-__device__ __forceinline__ int dma_swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int dma_swz(int r) { return (r >> 1) & 7; }
 
 template <int FMT>
 __device__ __forceinline__ void dma_stage(const LinArgs& p, int64_t mt0, int64_t nt0, int64_t st,
@@ -380,7 +380,10 @@ __global__ __launch_bounds__(256) void k_linear_dma(LinArgs p) {
             v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
           }
           if (op) b[i] = v; else a[i] = v;
-          const int sv = (op ? sb_t : sa_t)[r * G::SPR + 4 * u + g];
+          // the row's scale bytes of this stage in one read (the four lanes of a row share it)
+          const uint8_t* srow = (op ? sb_t : sa_t) + r * G::SPR;
+          const uint64_t sw8 = (G::SPR == 8) ? *(const uint64_t*)srow : (uint64_t)*(const uint32_t*)srow;
+          const int sv = (int)((sw8 >> (8 * (4 * u + g))) & 0xFFu);
           if (op) sb[i] = sv; else sa[i] = sv;
         }
       }
