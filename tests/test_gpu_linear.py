@@ -122,3 +122,30 @@ def test_layer_from_solved_weights(oracle_lib):
     rel = np.linalg.norm(yc - exact) / np.linalg.norm(exact)
     print(f"[linear] W4A4 MXFP4 layer relative error vs bf16 product: {rel:.4f}", flush=True)
     assert rel < 0.5
+
+
+@pytest.mark.parametrize("fmt", ["MXFP4", "MXFP8_E4M3", "MXFP8_E5M2"])
+def test_direct_and_staged_kernels_agree(oracle_lib, fmt):
+    """The direct-to-LDS kernel (4-byte aligned scale arrays, K a multiple of the stage)
+    and the register-staged kernel (the same scales at an odd address) multiply the same
+    codes in the same order: bitwise equal outputs, both within the oracle bound."""
+    M, N, K = 160, 200, 1024
+    a, asc, b, bsc, r = _inputs(fmt, M, N, K, 11)
+    dev = lambda x: torch.from_numpy(x).to(DEV)
+    A, B = dev(a), dev(b)
+    sa_al, sb_al = dev(asc), dev(bsc)
+    pad_a = torch.zeros(asc.size + 16, dtype=torch.uint8, device=DEV)
+    pad_b = torch.zeros(bsc.size + 16, dtype=torch.uint8, device=DEV)
+    pad_a[1:1 + asc.size] = sa_al
+    pad_b[1:1 + bsc.size] = sb_al
+    sa_odd, sb_odd = pad_a[1:1 + asc.size], pad_b[1:1 + bsc.size]
+    assert sa_odd.data_ptr() % 4 != 0 and sa_al.data_ptr() % 4 == 0
+    y1 = dq.quantized_linear(A, sa_al, B, sb_al, M, N, K, fmt, r=to_dev(r))
+    y2 = dq.quantized_linear(A, sa_odd, B, sb_odd, M, N, K, fmt, r=to_dev(r))
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    ref = oracle_lib.quantized_linear(a, asc, M, b, bsc, N, K, fmt, r=r)
+    mi, ni = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    _, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, fmt, mi.ravel(), ni.ravel(), r=r)
+    err = np.abs(y1.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= _tol(fmt, K, absy.reshape(M, N), ref, torch.float32))
