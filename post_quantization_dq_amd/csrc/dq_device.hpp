@@ -272,56 +272,38 @@ __device__ __forceinline__ void fp8_decode16(const uint32_t (&c)[4], float (&p)[
   }
 }
 
-// FP6 (E2M3: bias 1, 3 mantissa bits; E3M2: bias 3, 2 mantissa bits; no special codes).
-// Nearest value to x, ties to even, saturating; returns the 6-bit code (sign in bit 5)
-// and the value (negative zero for a negative input that rounds to zero).  Below the
-// smallest normal the grid is fixed-point with step 2^(1-bias-mbits); above it the fp32
-// mantissa is rounded to mbits bits (a carry moves into the next binade).
+// FP6 codes of x[0..15] and their values with the hardware conversions.  The 2xpk16
+// conversion writes its 32 results interleaved (field 2i from the first source's element i,
+// field 2i+1 from the second's), so even elements go to the first source and odd elements
+// to the second: the first three words then hold the chunk's codes in stream order.  The
+// conversion rounds to nearest even (E2M3: bias 1, 3 mantissa bits; E3M2: bias 3, 2
+// mantissa bits; subnormals below 2^(1-bias)), saturates at 7.5 / 28 and keeps the sign of
+// a negative value that rounds to zero; this was checked element by element against a
+// bit-level implementation of that rounding on every midpoint of both grids.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
 template <int FMT>
-__device__ __forceinline__ uint32_t fp6_encode(float x, float& val) {
-  constexpr int MB = (FMT == MXFP6_E2M3) ? 3 : 2;
-  constexpr int BIAS = (FMT == MXFP6_E2M3) ? 1 : 3;
-  constexpr float MIN_NORMAL = (FMT == MXFP6_E2M3) ? 1.0f : 0.25f;
-  constexpr float SUB_STEP_INV = (FMT == MXFP6_E2M3) ? 8.0f : 16.0f;   // 2^(bias-1+mbits)
-  const float ax = fminf(fabsf(x), mini_max<FMT>());
-  const uint32_t sgn = f2u(x) & 0x80000000u;
-  // subnormal range
-  const float q = __builtin_rintf(ax * SUB_STEP_INV);
-  const uint32_t mag_s = (uint32_t)q;
-  const float av_s = q * (1.0f / SUB_STEP_INV);
-  // normal range
-  uint32_t u = f2u(ax);
-  u += (1u << (22 - MB)) - 1u + ((u >> (23 - MB)) & 1u);
-  u &= ~((1u << (23 - MB)) - 1u);
-  const uint32_t mag_n = ((((u >> 23) - 127u + BIAS) << MB) | ((u >> (23 - MB)) & ((1u << MB) - 1u))) & 31u;
-  const bool sub = ax < MIN_NORMAL;
-  val = u2f(f2u(sub ? av_s : u2f(u)) | sgn);
-  return (sub ? mag_s : mag_n) | (sgn >> 26);
-}
-template <int FMT>
-__device__ __forceinline__ float fp6_value(uint32_t code) {
-  constexpr int MB = (FMT == MXFP6_E2M3) ? 3 : 2;
-  constexpr int BIAS = (FMT == MXFP6_E2M3) ? 1 : 3;
-  constexpr float SUB_STEP = (FMT == MXFP6_E2M3) ? 0.125f : 0.0625f;
-  const uint32_t e = (code >> MB) & ((1u << (5 - MB)) - 1u), m = code & ((1u << MB) - 1u);
-  const float av = e ? u2f(((e + 127u - BIAS) << 23) | (m << (23 - MB))) : (float)m * SUB_STEP;
-  return u2f(f2u(av) | ((code & 32u) << 26));
-}
-// 16 six-bit codes as a 96-bit stream: element k in bits 6k .. 6k+5 of words 0-2.
-__device__ __forceinline__ void fp6_pack16(const uint32_t (&k6)[16], uint32_t (&c)[4]) {
-  c[0] = c[1] = c[2] = c[3] = 0u;
+__device__ __forceinline__ void fp6_encode16_hw(const float (&x)[16], uint32_t (&c)[4], float (&p)[16]) {
+  f32x16 a = {}, b = {};
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int bit = 6 * k, w = bit >> 5, sh = bit & 31;
-    c[w] |= k6[k] << sh;
-    if (sh > 26) c[w + 1] |= k6[k] >> (32 - sh);
-  }
+  for (int i = 0; i < 8; ++i) { a[i] = x[2 * i]; b[i] = x[2 * i + 1]; }
+  u32x6 w = (FMT == MXFP6_E2M3) ? __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f)
+                                : __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(a, b, 1.0f);
+  c[0] = w[0]; c[1] = w[1]; c[2] = w[2]; c[3] = 0u;
+  const u32x6 z = u32x6{w[0], w[1], w[2], 0u, 0u, 0u};
+  const f32x32 d = (FMT == MXFP6_E2M3) ? __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(z, 1.0f)
+                                       : __builtin_amdgcn_cvt_scalef32_pk32_f32_bf6(z, 1.0f);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) p[k] = d[k];
 }
-__device__ __forceinline__ uint32_t fp6_unpack(const uint32_t (&c)[4], int k) {
-  const int bit = 6 * k, w = bit >> 5, sh = bit & 31;
-  uint32_t v = c[w] >> sh;
-  if (sh > 26) v |= c[w + 1] << (32 - sh);
-  return v & 63u;
+template <int FMT>
+__device__ __forceinline__ void fp6_decode16_hw(const uint32_t (&c)[4], float (&p)[16]) {
+  const u32x6 z = u32x6{c[0], c[1], c[2], 0u, 0u, 0u};
+  const f32x32 d = (FMT == MXFP6_E2M3) ? __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(z, 1.0f)
+                                       : __builtin_amdgcn_cvt_scalef32_pk32_f32_bf6(z, 1.0f);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) p[k] = d[k];
 }
 
 // Quantise one lane's 16 normalised values v (one chunk of a block of L*16).
@@ -392,10 +374,7 @@ __device__ __forceinline__ void quantize_chunk(const float (&v)[16], const QCtx&
     for (int k = 0; k < 16; ++k)
       x[k] = __builtin_amdgcn_fmed3f(ldexpf(v[k], -e), -mini_max<FMT>(), mini_max<FMT>());
     if (mx_fp6<FMT>()) {
-      uint32_t k6[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) k6[k] = fp6_encode<FMT>(x[k], o.p[k]);
-      fp6_pack16(k6, o.code);
+      fp6_encode16_hw<FMT>(x, o.code, o.p);
     } else {
       fp8_encode16<FMT>(x, o.code, o.p);
     }
@@ -472,10 +451,7 @@ __device__ __forceinline__ void decode_grid(const uint32_t (&c)[4], float (&p)[1
   if (FMT == NVFP4 || FMT == MXFP4) fp4_decode16(c[0], c[1], p);
   else if (FMT == INT8 || FMT == MXINT8) int8_decode16(c, p);
   else if (FMT == MXFP8_E4M3 || FMT == MXFP8_E5M2) fp8_decode16<FMT>(c, p);
-  else if (mx_fp6<FMT>()) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) p[k] = fp6_value<FMT>(fp6_unpack(c, k));
-  }
+  else if (mx_fp6<FMT>()) fp6_decode16_hw<FMT>(c, p);
   else int4_decode16(c[0], c[1], p);
 }
 

@@ -16,7 +16,10 @@
 //   - the lane's scale byte is the E8M0 scale of block g of its row;
 //   - result: lane l, element v holds C[4 (l / 16) + v][l % 16].
 // The codes are staged through LDS in their memory layout: whole-row global reads, then
-// each lane reads its fragment (one to three LDS reads) with no repacking.
+// each lane reads its fragment (one to three LDS reads) with no repacking.  Two kernels:
+// k_linear_dma (FP4 and FP8 with whole stages: global loads go straight into an LDS ring)
+// and k_linear (every format and any K that is a multiple of 32: the loads are staged in
+// registers, LDS rows are padded, and the last partial stage is masked).
 #pragma once
 
 #include <type_traits>
