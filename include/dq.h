@@ -235,6 +235,20 @@ int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_
                         int64_t K, const float* r, void* y, int32_t y_dtype, int64_t ldy,
                         void* stream);
 
+/* Exact re-encoding of MXINT4 codes as MXFP6 E2M3 codes, so that MXINT4 activations and
+ * weights can run through dq_quantized_linear (whose matrix cores take FP4/FP6/FP8 elements
+ * under E8M0 scales, not integers).  Each MXINT4 element q * 2^(e-2), q in [-7, 7], is the
+ * E2M3 value q under the scale 2^(e-2); when e - 2 is below the smallest E8M0 scale 2^-127
+ * it becomes q/2 or q/4 under 2^-127, still exact.  The dequantised values of the output
+ * equal those of the input bit for bit.
+ *   codes        [rows][cols/2] MXINT4 nibbles, 16-byte aligned;  block_scales [rows][cols/32].
+ *   out_codes    [rows][3*cols/4] MXFP6 E2M3 codes (the 6-bit stream layout), 8-byte aligned;
+ *   out_scales   [rows][cols/32] E8M0 bytes.
+ * cols must be a multiple of 32.  Asynchronous. */
+int dq_recode_mxint4_to_mxfp6(const uint8_t* codes, const uint8_t* block_scales, int64_t rows,
+                              int64_t cols, uint8_t* out_codes, uint8_t* out_scales,
+                              void* stream);
+
 /* Decode codes + block scales (+ tensor scale) into fp32 values [rows][cols].  When r and/or
  * c are given the output is diag(r) Qhat diag(c) (the reconstruction), else Qhat.
  * Asynchronous. */

@@ -88,6 +88,8 @@ _lib.dq_rescale_quantize_acts_multi.restype = C.c_int
 _lib.dq_quantized_linear.argtypes = [dq_quant_spec, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp,
                                      _i32, _i64, _vp]
 _lib.dq_quantized_linear.restype = C.c_int
+_lib.dq_recode_mxint4_to_mxfp6.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp]
+_lib.dq_recode_mxint4_to_mxfp6.restype = C.c_int
 _lib.dq_dequantize.argtypes = [dq_quant_spec, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]
 _lib.dq_dequantize.restype = C.c_int
 _lib.dq_debug_round.argtypes = [_i32, _vp, _vp, _i64, _vp]
@@ -95,7 +97,8 @@ _lib.dq_debug_round.restype = C.c_int
 
 EXPORTED = ("dq_workspace_bytes", "dq_solve", "dq_quantize_workspace_bytes", "dq_quantize_weights",
             "dq_rescale_quantize_acts", "dq_quantize_multi_workspace_bytes",
-            "dq_rescale_quantize_acts_multi", "dq_quantized_linear", "dq_dequantize",
+            "dq_rescale_quantize_acts_multi", "dq_quantized_linear", "dq_recode_mxint4_to_mxfp6",
+            "dq_dequantize",
             "dq_status_string", "dq_debug_round")
 
 
@@ -236,6 +239,11 @@ def dq_quantized_linear(spec, a_codes, a_scales, M, b_codes, b_scales, N, K, r, 
            "dq_quantized_linear")
 
 
+def dq_recode_mxint4_to_mxfp6(codes, block_scales, rows, cols, out_codes, out_scales, stream=None):
+    _check(_lib.dq_recode_mxint4_to_mxfp6(_ptr(codes), _ptr(block_scales), rows, cols, _ptr(out_codes),
+                                          _ptr(out_scales), _stream(stream)), "dq_recode_mxint4_to_mxfp6")
+
+
 def dq_dequantize(spec, codes, block_scales, tensor_scale, rows, cols, r, c, out, stream=None):
     _check(_lib.dq_dequantize(spec, _ptr(codes), _ptr(block_scales), _ptr(tensor_scale), rows,
                               cols, _ptr(r), _ptr(c), _ptr(out), _stream(stream)), "dq_dequantize")
@@ -349,10 +357,23 @@ def rescale_quantize_acts_multi(X: torch.Tensor, cs, fmt: str = "NVFP4", group: 
     return outs
 
 
+def recode_mxint4_to_mxfp6(codes, scales, rows: int, cols: int, stream=None):
+    """MXINT4 codes and scales -> the equal-valued MXFP6 E2M3 codes and scales."""
+    out_c = torch.empty(rows * cols * 3 // 4, dtype=torch.uint8, device=codes.device)
+    out_s = torch.empty(rows * cols // 32, dtype=torch.uint8, device=codes.device)
+    dq_recode_mxint4_to_mxfp6(codes, scales, rows, cols, out_c, out_s, stream)
+    return out_c, out_s
+
+
 def quantized_linear(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, fmt: str,
                      r=None, out_dtype=torch.float32, stream=None) -> torch.Tensor:
     """Y [M][N] = deq(A) deq(B)^T diag(r) from activation codes A [M][K] and weight codes
-    B [N][K] of an MX format."""
+    B [N][K] of an MX format.  MXINT4 operands are re-encoded as MXFP6 E2M3 first (exact;
+    for weights this can be done once and kept)."""
+    if fmt == "MXINT4":
+        a_codes, a_scales = recode_mxint4_to_mxfp6(a_codes, a_scales, M, K, stream)
+        b_codes, b_scales = recode_mxint4_to_mxfp6(b_codes, b_scales, N, K, stream)
+        fmt = "MXFP6_E2M3"
     y = torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
     dq_quantized_linear(spec_of(fmt), a_codes, a_scales, M, b_codes, b_scales, N, K, r, y, stream)
     return y

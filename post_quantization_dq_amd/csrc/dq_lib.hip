@@ -897,6 +897,19 @@ int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_
   return rc;
 }
 
+int dq_recode_mxint4_to_mxfp6(const uint8_t* codes, const uint8_t* block_scales, int64_t rows,
+                              int64_t cols, uint8_t* out_codes, uint8_t* out_scales,
+                              void* stream) {
+  if (rows < 0 || cols < 0 || cols % 32) return DQ_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return DQ_OK;
+  if (!codes || !block_scales || !out_codes || !out_scales) return DQ_ERR_NULL;
+  if (!aligned16(codes) || ((uintptr_t)out_codes & 7u)) return DQ_ERR_ALIGN;
+  const int64_t nb = rows * (cols / 32);
+  hipLaunchKernelGGL(k_recode_mxint4_e2m3, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, codes, block_scales, nb, out_codes, out_scales);
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
 int dq_dequantize(dq_quant_spec spec, const uint8_t* codes, const void* block_scales,
                   const float* tensor_scale, int64_t rows, int64_t cols, const float* r,
                   const float* c, float* out, void* stream) {

@@ -417,4 +417,36 @@ __global__ __launch_bounds__(256) void k_linear_dma(LinArgs p) {
   }
 }
 
+// ---------------------------------------------------------------- MXINT4 -> MXFP6 E2M3
+// The matrix cores take no integer elements under E8M0 scales, but every MXINT4 element
+// q * 2^(e-2) (q in [-7, 7]) is exactly an E2M3 value times an E8M0 scale: q itself under
+// scale 2^(e-2), or q / 2^(2-(e+127)) under the smallest scale 2^-127 when e - 2 is below
+// it (q / 2 and q / 4 are E2M3 values for every q).  One thread per 32-element block: read
+// its 16 bytes of nibbles and its scale, write 24 bytes of 6-bit codes and the new scale.
+__global__ __launch_bounds__(256) void k_recode_mxint4_e2m3(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t nblocks, uint8_t* out_codes,
+                                                            uint8_t* out_scales) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const u32x4 w = gp((const u32x4*)codes)[b];
+  const uint32_t sc = gp(scales)[b];
+  const float f = sc >= 2u ? 1.0f : (sc == 1u ? 0.5f : 0.25f);
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  f32x16 ev = {}, od = {};
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int q = ((int)(ww[k >> 3] << (28 - 4 * (k & 7)))) >> 28;   // sign-extended nibble
+    const float v = (float)q * f;                                       // exact
+    if (k & 1) od[k >> 1] = v; else ev[k >> 1] = v;
+  }
+  // the 2xpk16 conversion interleaves its sources: even elements first source, odd second
+  const u32x6 c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+  DQ_GAS u32x2* o = gp((u32x2*)(out_codes + 24 * b));
+  o[0] = u32x2{c[0], c[1]};
+  o[1] = u32x2{c[2], c[3]};
+  o[2] = u32x2{c[4], c[5]};
+  gp(out_scales)[b] = (uint8_t)(sc >= 2u ? sc - 2u : 0u);
+}
+
 }  // namespace dqk

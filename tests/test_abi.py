@@ -20,7 +20,7 @@ def dq():
 def _declared():
     text = (ROOT / "include" / "dq.h").read_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(dq):
@@ -128,3 +128,12 @@ def test_quantized_linear_argument_errors(dq):
     assert L.dq_quantized_linear(mx, None, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, 0x50000, 0, 64, None) == -1
     assert L.dq_quantized_linear(mx, 0x10000, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, None, 0, 64, None) == -1
     assert L.dq_quantized_linear(mx, None, None, 0, None, None, 64, 256, None, None, 0, 64, None) == 0   # M = 0
+
+
+def test_recode_argument_errors(dq):
+    L = dq._lib
+    assert L.dq_recode_mxint4_to_mxfp6(0x10000, 0x20000, 4, 48, 0x30000, 0x40000, None) == -2
+    assert L.dq_recode_mxint4_to_mxfp6(None, 0x20000, 4, 64, 0x30000, 0x40000, None) == -1
+    assert L.dq_recode_mxint4_to_mxfp6(0x10008, 0x20000, 4, 64, 0x30000, 0x40000, None) == -3
+    assert L.dq_recode_mxint4_to_mxfp6(0x10000, 0x20000, 4, 64, 0x30004, 0x40000, None) == -3
+    assert L.dq_recode_mxint4_to_mxfp6(None, None, 0, 64, None, None, None) == 0

@@ -97,21 +97,22 @@ def test_empty_and_zero_k(oracle_lib):
     assert y0.shape == (0, 1)
 
 
-def test_layer_from_solved_weights(oracle_lib):
-    """End to end on a 512 x 4096 slice of the q_proj weight: solve (MXFP4, T = 4), quantise
-    256 tokens of activations with the solved column scales, run the layer.  The output
-    matches the oracle's product of the same codes and approximates X W^T."""
-    W, _, fmt, g, _ = synth.workload("q4096x4096_mxfp4")
+@pytest.mark.parametrize("name", ["q4096x4096_mxfp4", "k1024x4096_mxint4"])
+def test_layer_from_solved_weights(oracle_lib, name):
+    """End to end on a 512 x 4096 slice of a weight: solve (its format, T = 4), quantise 256
+    tokens of activations with the solved column scales, run the layer.  The output matches
+    the oracle's product of the same codes and approximates X W^T."""
+    W, _, fmt, g, _ = synth.workload(name)
     W = np.ascontiguousarray(W[:512])
     X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(256, 4096), 3)
-    res = dq.solve(to_dev(W), "MXFP4", 4)
-    codes_x, scales_x, _ = dq.rescale_quantize_acts(to_dev(X), res["c"], "MXFP4")
-    y = dq.quantized_linear(codes_x, scales_x, res["codes"], res["scales"], 256, 512, 4096, "MXFP4",
+    res = dq.solve(to_dev(W), fmt, 4)
+    codes_x, scales_x, _ = dq.rescale_quantize_acts(to_dev(X), res["c"], fmt)
+    y = dq.quantized_linear(codes_x, scales_x, res["codes"], res["scales"], 256, 512, 4096, fmt,
                             r=res["r"])
     torch.cuda.synchronize()
     yc = y.cpu().numpy().astype(np.float64)
     args = (codes_x.cpu().numpy(), scales_x.cpu().numpy(), 256, res["codes"].cpu().numpy(),
-            res["scales"].cpu().numpy(), 512, 4096, "MXFP4")
+            res["scales"].cpu().numpy(), 512, 4096, fmt)
     ref = oracle_lib.quantized_linear(*args, r=res["r"].cpu().numpy())
     mi, ni = np.meshgrid(np.arange(256), np.arange(512), indexing="ij")
     _, absy = oracle_lib.quantized_linear_entries(*args, mi.ravel(), ni.ravel(), r=res["r"].cpu().numpy())
@@ -120,7 +121,7 @@ def test_layer_from_solved_weights(oracle_lib):
     Wf = (W.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     exact = Xf @ Wf.T
     rel = np.linalg.norm(yc - exact) / np.linalg.norm(exact)
-    print(f"[linear] W4A4 MXFP4 layer relative error vs bf16 product: {rel:.4f}", flush=True)
+    print(f"[linear] W4A4 {fmt} layer relative error vs bf16 product: {rel:.4f}", flush=True)
     assert rel < 0.5
 
 
@@ -149,3 +150,41 @@ def test_direct_and_staged_kernels_agree(oracle_lib, fmt):
     _, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, fmt, mi.ravel(), ni.ravel(), r=r)
     err = np.abs(y1.cpu().numpy().astype(np.float64) - ref)
     assert np.all(err <= _tol(fmt, K, absy.reshape(M, N), ref, torch.float32))
+
+
+def _mxint4_inputs(rng, rows, cols):
+    q = rng.integers(-7, 8, rows * cols)
+    codes = pack_codes((q & 0xF).astype(np.uint8), 4)
+    scales = rng.integers(0, 255, rows * cols // 32).astype(np.uint8)
+    scales[:8] = [0, 1, 2, 3, 127, 200, 254, 0]
+    return codes, scales
+
+
+def test_recode_mxint4_is_exact(oracle_lib):
+    """MXINT4 -> MXFP6 E2M3 re-encoding keeps every dequantised value, including the blocks
+    whose scale is 2^-127 or 2^-126 (their elements become q/4 and q/2)."""
+    rng = np.random.default_rng(12)
+    rows, cols = 37, 1024
+    codes, scales = _mxint4_inputs(rng, rows, cols)
+    oc, os_ = dq.recode_mxint4_to_mxfp6(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                                        rows, cols)
+    torch.cuda.synchronize()
+    want = oracle_lib.dequantize(codes, scales, 0.0, "MXINT4", rows, cols)
+    got = oracle_lib.dequantize(oc.cpu().numpy(), os_.cpu().numpy(), 0.0, "MXFP6_E2M3", rows, cols)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(100, 70, 384), (256, 256, 1024)])
+def test_mxint4_linear(oracle_lib, shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M + K)
+    a, asc = _mxint4_inputs(rng, M, K)
+    b, bsc = _mxint4_inputs(rng, N, K)
+    asc = np.clip(asc, 118, 136).astype(np.uint8)
+    bsc = np.clip(bsc, 118, 136).astype(np.uint8)
+    r = np.exp2(rng.uniform(-2, 2, N)).astype(np.float32)
+    y = _run(a, asc, b, bsc, M, N, K, "MXINT4", r, torch.float32)
+    ref = oracle_lib.quantized_linear(a, asc, M, b, bsc, N, K, "MXINT4", r=r)
+    mi, ni = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    _, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, "MXINT4", mi.ravel(), ni.ravel(), r=r)
+    assert np.all(np.abs(y - ref) <= _tol("MXFP6_E2M3", K, absy.reshape(M, N), ref, torch.float32))
