@@ -173,7 +173,8 @@ def bench_linear(args):
     ac, asc, _ = dq.rescale_quantize_acts(to_dev(X), res["c"], fmt)
     y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     spec = dq.spec_of(fmt)
-    call = lambda: dq.dq_quantized_linear(spec, ac, asc, M, res["codes"], res["scales"], N, K, res["r"], y)
+    call = lambda: dq.dq_quantized_linear(spec, ac, asc, None, M, res["codes"], res["scales"], None, N, K,
+                                          res["r"], y)
     print(f"[bench] quantised linear {fmt}: Y[{M}x{N}] = A[{M}x{K}] Q^T diag(r), bf16 out", flush=True)
     for _ in range(args.warmup):
         call()

@@ -208,30 +208,37 @@ int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t token
                                    float* const* tensor_scales, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
-/* Quantised linear layer on the block-scaled matrix cores (listing page Table 11,
- * "quantized linears", and Table 12's packed 4-bit weights; news summary: beta folds into
- * the activation quantiser, the row scales into the layer output):
+/* Quantised linear layer on the matrix cores (listing page Table 11, "quantized linears",
+ * and Table 12's packed 4-bit weights; news summary: beta folds into the activation
+ * quantiser, the row scales into the layer output):
  *     Y[m][n] = r[n] * sum_k Aq[m][k] * Q[n][k],
  * the product of the activation codes (dq_rescale_quantize_acts with the solved c, so
  * Aq = FQ(X diag(c))) and the weight codes (dq_solve or dq_quantize_weights), each element
- * dequantised with its block scale.  With W ~ diag(r) Q diag(c) this is Y ~ X W^T.
- *   spec       DQ_FMT_MXFP4, DQ_FMT_MXFP6_E2M3/E3M2 or DQ_FMT_MXFP8_E4M3/E5M2 (group 32),
- *              the same for both operands.
+ * dequantised with its block scale (and, for NVFP4, its tensor scale).  With
+ * W ~ diag(r) Q diag(c) this is Y ~ X W^T.
+ *   spec       DQ_FMT_MXFP4, DQ_FMT_MXFP6_E2M3/E3M2, DQ_FMT_MXFP8_E4M3/E5M2 (group 32) on
+ *              the block-scaled cores, or DQ_FMT_NVFP4 (group 16) on the bf16 cores: its
+ *              elements e2m1 * e4m3 are exact in bf16 and the tensor scales multiply the
+ *              fp32 result.  The same format for both operands (MXINT4: see
+ *              dq_recode_mxint4_to_mxfp6).
  *   a_codes    [M][K] activation codes in the format's layout (row pitch K*bits/8 bytes),
- *              16-byte aligned; a_scales [M][K/32] E8M0 bytes.
- *   b_codes    [N][K] weight codes, 16-byte aligned; b_scales [N][K/32].
+ *              16-byte aligned; a_scales [M][K/group] scale bytes; a_tensor_scale [1] fp32
+ *              (NVFP4 only, else ignored and may be NULL).
+ *   b_codes    [N][K] weight codes, 16-byte aligned; b_scales [N][K/group]; b_tensor_scale.
  *   K          a multiple of 32 (0 gives Y = 0).
  *   r          [N] fp32 row scales of the weights, or NULL (ones).
  *   y          [M][ldy] output, fp32 (y_dtype DQ_F32) or bf16 (DQ_BF16, round to nearest
  *              even); ldy >= N.
  * Accumulation is fp32 in the matrix cores.  For E2M1 and E2M3 elements every product and
- * partial sum of one instruction is exact, so only the fp32 accumulation rounds.  For E4M3,
- * E5M2 and E3M2 the cores' internal sum keeps fewer bits than fp32 (measured: about 2^-12
- * of sum |a b| over 128-element random-code dot products).  Returns DQ_ERR_FORMAT for other
- * formats, DQ_ERR_SHAPE for bad sizes, DQ_ERR_ALIGN for misaligned codes or output.
- * Asynchronous. */
+ * partial sum of one instruction is exact, so only the fp32 accumulation rounds; the bf16
+ * products of NVFP4 are exact too, but its tensor scales are applied once to the sum (the
+ * per-element dequantisation rounds e4m3 * s_t instead).  For E4M3, E5M2 and E3M2 the cores'
+ * internal sum keeps fewer bits than fp32 (measured: about 2^-12 of sum |a b| over
+ * 128-element random-code dot products).  Returns DQ_ERR_FORMAT for other formats,
+ * DQ_ERR_SHAPE for bad sizes, DQ_ERR_ALIGN for misaligned codes or output.  Asynchronous. */
 int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_t* a_scales,
-                        int64_t M, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N,
+                        const float* a_tensor_scale, int64_t M, const uint8_t* b_codes,
+                        const uint8_t* b_scales, const float* b_tensor_scale, int64_t N,
                         int64_t K, const float* r, void* y, int32_t y_dtype, int64_t ldy,
                         void* stream);
 

@@ -83,10 +83,11 @@ def lib():
         L.o_solve.restype = C.c_int
         L.o_rescale_quantize_acts.argtypes = [p, i64, i64, i64, p, C.c_int, C.c_int, p, p, p, p]
         L.o_rescale_quantize_acts.restype = C.c_int
-        L.o_quantized_linear.argtypes = [C.c_int, C.c_int, p, p, i64, p, p, i64, i64, p, p]
+        L.o_quantized_linear.argtypes = [C.c_int, C.c_int, p, p, C.c_float, i64, p, p, C.c_float,
+                                         i64, i64, p, p]
         L.o_quantized_linear.restype = C.c_int
-        L.o_quantized_linear_entries.argtypes = [C.c_int, C.c_int, p, p, i64, p, p, i64, i64, p,
-                                                 p, p, i64, p, p]
+        L.o_quantized_linear_entries.argtypes = [C.c_int, C.c_int, p, p, C.c_float, i64, p, p,
+                                                 C.c_float, i64, i64, p, p, p, i64, p, p]
         L.o_quantized_linear_entries.restype = C.c_int
         L.o_act_sqnr.argtypes = [p, i64, i64, i64, p, C.c_int, C.c_int, p, p, C.c_float]
         L.o_act_sqnr.restype = C.c_double
@@ -299,8 +300,10 @@ def act_sqnr(X: np.ndarray, c, codes, scales, tscale: float, fmt: str,
 
 # ------------------------------------------------------------------ quantised linear layer
 def quantized_linear(a_codes, a_scales, M: int, b_codes, b_scales, N: int, K: int, fmt: str,
-                     r=None, group: int | None = None) -> np.ndarray:
-    """Y = deq(A) . deq(B)^T . diag(r) in fp64 ([M][N]); A, B in the format's code layout."""
+                     r=None, group: int | None = None, a_ts: float = 1.0,
+                     b_ts: float = 1.0) -> np.ndarray:
+    """Y = deq(A) . deq(B)^T . diag(r) in fp64 ([M][N]); A, B in the format's code layout;
+    a_ts, b_ts are the NVFP4 tensor scales (ignored by the other formats)."""
     group = group or DEFAULT_GROUP[fmt]
     a_codes = np.ascontiguousarray(a_codes, dtype=np.uint8)
     b_codes = np.ascontiguousarray(b_codes, dtype=np.uint8)
@@ -308,13 +311,15 @@ def quantized_linear(a_codes, a_scales, M: int, b_codes, b_scales, N: int, K: in
     b_scales = np.ascontiguousarray(b_scales, dtype=_scale_dtype(fmt))
     r = None if r is None else np.ascontiguousarray(r, dtype=np.float32)
     Y = np.zeros((M, N), dtype=np.float64)
-    _check(lib().o_quantized_linear(FMT[fmt], group, _ptr(a_codes), _ptr(a_scales), M, _ptr(b_codes),
-                                    _ptr(b_scales), N, K, _ptr(r), _ptr(Y)), "quantized_linear")
+    _check(lib().o_quantized_linear(FMT[fmt], group, _ptr(a_codes), _ptr(a_scales), a_ts, M,
+                                    _ptr(b_codes), _ptr(b_scales), b_ts, N, K, _ptr(r), _ptr(Y)),
+           "quantized_linear")
     return Y
 
 
 def quantized_linear_entries(a_codes, a_scales, M: int, b_codes, b_scales, N: int, K: int,
-                             fmt: str, mi, ni, r=None, group: int | None = None):
+                             fmt: str, mi, ni, r=None, group: int | None = None,
+                             a_ts: float = 1.0, b_ts: float = 1.0):
     """Entries (mi[i], ni[i]) of quantized_linear and the sums of |products| (fp64)."""
     group = group or DEFAULT_GROUP[fmt]
     a_codes = np.ascontiguousarray(a_codes, dtype=np.uint8)
@@ -326,8 +331,9 @@ def quantized_linear_entries(a_codes, a_scales, M: int, b_codes, b_scales, N: in
     ni = np.ascontiguousarray(ni, dtype=np.int64)
     y = np.zeros(mi.size, dtype=np.float64)
     ay = np.zeros(mi.size, dtype=np.float64)
-    _check(lib().o_quantized_linear_entries(FMT[fmt], group, _ptr(a_codes), _ptr(a_scales), M,
-                                            _ptr(b_codes), _ptr(b_scales), N, K, _ptr(r), _ptr(mi),
+    _check(lib().o_quantized_linear_entries(FMT[fmt], group, _ptr(a_codes), _ptr(a_scales), a_ts,
+                                            M, _ptr(b_codes), _ptr(b_scales), b_ts, N, K, _ptr(r),
+                                            _ptr(mi),
                                             _ptr(ni), mi.size, _ptr(y), _ptr(ay)),
            "quantized_linear_entries")
     return y, ay

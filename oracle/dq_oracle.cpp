@@ -808,31 +808,35 @@ double o_act_sqnr(const uint16_t* X, int64_t tokens, int64_t cols, int64_t ld, c
 //   Y = X W^T ~ Aq . Q^T . diag(r),   Y_tn = r_n * sum_k Aq_tk Q_nk,
 // every element dequantised from its codes and block scales, products and sums in fp64.
 // r may be null (ones).  Y is [M][N] fp64.  Sampled variant: only the entries (m[i], n[i]).
+// NVFP4 elements are dequantised without their tensor scale (e2m1 * e4m3 is exact in fp32);
+// the callers multiply each product by a_ts * b_ts in fp64, so every element stands for
+// e2m1 * e4m3 * s_t exactly, as the format defines it.
 static int linear_deq(int fmt, int g, const uint8_t* a_codes, const void* a_scales, int64_t M,
                       const uint8_t* b_codes, const void* b_scales, int64_t N, int64_t K,
                       std::vector<float>& A, std::vector<float>& B) {
   if (!a_codes || !a_scales || !b_codes || !b_scales) return ERR_NULL;
-  if (!group_ok(fmt, g) || fmt == FMT_NVFP4) return ERR_FORMAT;
+  if (!group_ok(fmt, g)) return ERR_FORMAT;
   if (M < 0 || N < 0 || K < 0 || K % g) return ERR_SHAPE;
   A.assign((size_t)M * K, 0.0f);
   B.assign((size_t)N * K, 0.0f);
-  int rc = o_dequantize(fmt, g, a_codes, a_scales, 0.0f, M, K, A.data());
+  int rc = o_dequantize(fmt, g, a_codes, a_scales, 1.0f, M, K, A.data());
   if (rc != OK) return rc;
-  return o_dequantize(fmt, g, b_codes, b_scales, 0.0f, N, K, B.data());
+  return o_dequantize(fmt, g, b_codes, b_scales, 1.0f, N, K, B.data());
 }
 
-int o_quantized_linear(int fmt, int g, const uint8_t* a_codes, const void* a_scales, int64_t M,
-                       const uint8_t* b_codes, const void* b_scales, int64_t N, int64_t K,
-                       const float* r, double* Y) {
+int o_quantized_linear(int fmt, int g, const uint8_t* a_codes, const void* a_scales, float a_ts,
+                       int64_t M, const uint8_t* b_codes, const void* b_scales, float b_ts,
+                       int64_t N, int64_t K, const float* r, double* Y) {
   if (!Y) return ERR_NULL;
   std::vector<float> A, B;
   int rc = linear_deq(fmt, g, a_codes, a_scales, M, b_codes, b_scales, N, K, A, B);
   if (rc != OK) return rc;
+  const double ts = fmt == FMT_NVFP4 ? (double)a_ts * (double)b_ts : 1.0;
   parallel_rows(M, [&](int64_t b, int64_t e) {
     for (int64_t m = b; m < e; ++m)
       for (int64_t n = 0; n < N; ++n) {
         double acc = 0.0;
-        for (int64_t k = 0; k < K; ++k) acc += (double)A[m * K + k] * (double)B[n * K + k];
+        for (int64_t k = 0; k < K; ++k) acc += (double)A[m * K + k] * (double)B[n * K + k] * ts;
         Y[m * N + n] = acc * (r ? (double)r[n] : 1.0);
       }
   });
@@ -841,18 +845,20 @@ int o_quantized_linear(int fmt, int g, const uint8_t* a_codes, const void* a_sca
 
 // Entries (m[i], n[i]) of the same product, plus sum_k |Aq_mk Q_nk| |r_n| for error bounds.
 int o_quantized_linear_entries(int fmt, int g, const uint8_t* a_codes, const void* a_scales,
-                               int64_t M, const uint8_t* b_codes, const void* b_scales, int64_t N,
-                               int64_t K, const float* r, const int64_t* mi, const int64_t* ni,
+                               float a_ts, int64_t M, const uint8_t* b_codes,
+                               const void* b_scales, float b_ts, int64_t N, int64_t K,
+                               const float* r, const int64_t* mi, const int64_t* ni,
                                int64_t count, double* y, double* absy) {
   if (!mi || !ni || !y || !absy) return ERR_NULL;
   std::vector<float> A, B;
   int rc = linear_deq(fmt, g, a_codes, a_scales, M, b_codes, b_scales, N, K, A, B);
   if (rc != OK) return rc;
+  const double ts = fmt == FMT_NVFP4 ? (double)a_ts * (double)b_ts : 1.0;
   for (int64_t i = 0; i < count; ++i) {
     if (mi[i] < 0 || mi[i] >= M || ni[i] < 0 || ni[i] >= N) return ERR_SHAPE;
     double acc = 0.0, aa = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-      const double p = (double)A[mi[i] * K + k] * (double)B[ni[i] * K + k];
+      const double p = (double)A[mi[i] * K + k] * (double)B[ni[i] * K + k] * ts;
       acc += p;
       aa += std::fabs(p);
     }

@@ -85,8 +85,8 @@ _lib.dq_quantize_multi_workspace_bytes.restype = _sz
 _lib.dq_rescale_quantize_acts_multi.argtypes = [_vp, _i32, _i64, _i64, _i64, _i32, _vp, dq_quant_spec,
                                                 _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dq_rescale_quantize_acts_multi.restype = C.c_int
-_lib.dq_quantized_linear.argtypes = [dq_quant_spec, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp,
-                                     _i32, _i64, _vp]
+_lib.dq_quantized_linear.argtypes = [dq_quant_spec, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64,
+                                     _vp, _vp, _i32, _i64, _vp]
 _lib.dq_quantized_linear.restype = C.c_int
 _lib.dq_recode_mxint4_to_mxfp6.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp]
 _lib.dq_recode_mxint4_to_mxfp6.restype = C.c_int
@@ -231,10 +231,13 @@ def dq_rescale_quantize_acts_multi(X, cs, spec, codes, block_scales, tensor_scal
         _stream(stream)), "dq_rescale_quantize_acts_multi")
 
 
-def dq_quantized_linear(spec, a_codes, a_scales, M, b_codes, b_scales, N, K, r, y, stream=None):
-    """y: a 2-D fp32 or bf16 tensor [M][>= N] (row pitch y.stride(0))."""
-    _check(_lib.dq_quantized_linear(spec, _ptr(a_codes), _ptr(a_scales), M, _ptr(b_codes),
-                                    _ptr(b_scales), N, K, _ptr(r), _ptr(y), DT.get(y.dtype, -1),
+def dq_quantized_linear(spec, a_codes, a_scales, a_tensor_scale, M, b_codes, b_scales,
+                        b_tensor_scale, N, K, r, y, stream=None):
+    """y: a 2-D fp32 or bf16 tensor [M][>= N] (row pitch y.stride(0)); the tensor scales are
+    [1] fp32 device tensors (NVFP4) or None."""
+    _check(_lib.dq_quantized_linear(spec, _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), M,
+                                    _ptr(b_codes), _ptr(b_scales), _ptr(b_tensor_scale), N, K,
+                                    _ptr(r), _ptr(y), DT.get(y.dtype, -1),
                                     y.stride(0) if y.numel() else N, _stream(stream)),
            "dq_quantized_linear")
 
@@ -366,16 +369,19 @@ def recode_mxint4_to_mxfp6(codes, scales, rows: int, cols: int, stream=None):
 
 
 def quantized_linear(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, fmt: str,
-                     r=None, out_dtype=torch.float32, stream=None) -> torch.Tensor:
+                     r=None, out_dtype=torch.float32, stream=None, a_tensor_scale=None,
+                     b_tensor_scale=None) -> torch.Tensor:
     """Y [M][N] = deq(A) deq(B)^T diag(r) from activation codes A [M][K] and weight codes
-    B [N][K] of an MX format.  MXINT4 operands are re-encoded as MXFP6 E2M3 first (exact;
-    for weights this can be done once and kept)."""
+    B [N][K] of an MX format or NVFP4 (which also takes the two [1] fp32 tensor scales).
+    MXINT4 operands are re-encoded as MXFP6 E2M3 first (exact; for weights this can be done
+    once and kept)."""
     if fmt == "MXINT4":
         a_codes, a_scales = recode_mxint4_to_mxfp6(a_codes, a_scales, M, K, stream)
         b_codes, b_scales = recode_mxint4_to_mxfp6(b_codes, b_scales, N, K, stream)
         fmt = "MXFP6_E2M3"
     y = torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
-    dq_quantized_linear(spec_of(fmt), a_codes, a_scales, M, b_codes, b_scales, N, K, r, y, stream)
+    dq_quantized_linear(spec_of(fmt), a_codes, a_scales, a_tensor_scale, M, b_codes, b_scales,
+                        b_tensor_scale, N, K, r, y, stream)
     return y
 
 

@@ -488,6 +488,12 @@ int launch_linear(dim3 grid, hipStream_t s, const LinArgs& p) {
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
+template <int OB>
+int launch_linear_nv(dim3 grid, hipStream_t s, const LinArgs& p) {
+  hipLaunchKernelGGL((k_linear_nv<OB>), grid, dim3(256), NvGeom::LDS, s, p);   // 64 KiB
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
 static_assert(kMaxMulti == DQ_MAX_MULTI, "kernel and header output limits differ");
 // The fused activation quantiser keeps every output's column scales in LDS up to this size
 // (q/k/v or gate/up of a 4096-wide model need 48 or 32 KiB); beyond it they are read from
@@ -861,27 +867,32 @@ int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t token
 }
 
 int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_t* a_scales,
-                        int64_t M, const uint8_t* b_codes, const uint8_t* b_scales, int64_t N,
+                        const float* a_tensor_scale, int64_t M, const uint8_t* b_codes,
+                        const uint8_t* b_scales, const float* b_tensor_scale, int64_t N,
                         int64_t K, const float* r, void* y, int32_t y_dtype, int64_t ldy,
                         void* stream) {
   const int g = resolve_group(spec);
   if (g < 0) return DQ_ERR_FORMAT;
   const int f = spec.fmt;
+  const bool nv = f == DQ_FMT_NVFP4;
   if (f != DQ_FMT_MXFP4 && f != DQ_FMT_MXFP8_E4M3 && f != DQ_FMT_MXFP8_E5M2 &&
-      f != DQ_FMT_MXFP6_E2M3 && f != DQ_FMT_MXFP6_E3M2)
+      f != DQ_FMT_MXFP6_E2M3 && f != DQ_FMT_MXFP6_E3M2 && !nv)
     return DQ_ERR_FORMAT;
   if (y_dtype != DQ_F32 && y_dtype != DQ_BF16) return DQ_ERR_FORMAT;
   if (M < 0 || N < 0 || K < 0 || K % 32 || ldy < N) return DQ_ERR_SHAPE;
   if (M == 0 || N == 0) return DQ_OK;
   if (!y) return DQ_ERR_NULL;
   if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return DQ_ERR_NULL;
+  if (nv && (!a_tensor_scale || !b_tensor_scale)) return DQ_ERR_NULL;
   if (!aligned16(a_codes) || !aligned16(b_codes) || ((uintptr_t)y % (y_dtype == DQ_F32 ? 4 : 2)))
     return DQ_ERR_ALIGN;
   const int64_t tm = (M + kLinTile - 1) / kLinTile, tn = (N + kLinTile - 1) / kLinTile;
   if (tm * tn > (int64_t)0x7FFFFFFF) return DQ_ERR_SHAPE;
-  LinArgs p{a_codes, a_scales, b_codes, b_scales, r, y, M, N, K, ldy, (int32_t)tm, (int32_t)tn};
+  LinArgs p{a_codes, a_scales, b_codes, b_scales, r, a_tensor_scale, b_tensor_scale, y,
+            M, N, K, ldy, (int32_t)tm, (int32_t)tn};
   hipStream_t s = (hipStream_t)stream;
   dim3 grid((unsigned)(tm * tn)), block(256);
+  if (nv) return y_dtype == DQ_BF16 ? launch_linear_nv<1>(grid, s, p) : launch_linear_nv<0>(grid, s, p);
 #define DQ_L(F)                                                                          \
   rc = (y_dtype == DQ_BF16) ? launch_linear<F, 1>(grid, s, p) : launch_linear<F, 0>(grid, s, p); \
   break

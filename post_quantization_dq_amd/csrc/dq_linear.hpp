@@ -46,6 +46,8 @@ struct LinArgs {
   const uint8_t* b;    // weight codes [N][K * bits / 8]
   const uint8_t* bs;   // weight block scales [N][K / 32]
   const float* r;      // row scales of the weights (output columns) [N], or null
+  const float* ats;    // NVFP4: activation tensor scale [1]
+  const float* bts;    // NVFP4: weight tensor scale [1]
   void* y;             // output [M][ldy], fp32 or bf16
   int64_t M, N, K, ldy;
   int32_t tiles_m, tiles_n;
@@ -410,6 +412,146 @@ __global__ __launch_bounds__(256) void k_linear_dma(LinArgs p) {
         const int64_t m = mt0 + wm + 16 * i + 4 * g + v;
         if (m < p.M && n < p.N) {
           const float yv = acc[i][j][v] * rn;
+          if (OUT_BF16) gp((uint16_t*)p.y)[m * p.ldy + n] = (uint16_t)(f2u(bf16_rne(yv)) >> 16);
+          else gp((float*)p.y)[m * p.ldy + n] = yv;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------- NVFP4 on the bf16 cores
+// NVFP4 scales (E4M3 per 16 elements, fp32 per tensor) have no block-scaled matrix-core
+// form.  Within a tensor every element is e2m1(q) * e4m3(sb) * s_t, and e2m1(q) * e4m3(sb)
+// has at most 6 significant bits, so it is exact in bf16: the operands are dequantised to
+// that product on the way into LDS, multiplied on the bf16 cores (v_mfma_f32_16x16x32_bf16:
+// lane l holds row l % 16 and K 8 (l / 16) .. +7, measured), and the two tensor scales and
+// r are applied to the fp32 result.  Stage = 64 K: a 128-byte bf16 row per tile row.
+struct NvGeom {
+  static constexpr int KS = 64;
+  static constexpr int ROWB = KS * 2;               // 128 bytes of bf16
+  static constexpr int TILE = kLinTile * ROWB;      // 16 KiB
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int LDS = 2 * STAGE;             // 64 KiB
+};
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// One thread's share of a stage of one operand: tile row t / 2, 32 elements (two NVFP4
+// blocks) starting at K 32 (t % 2) of the stage.
+struct NvStage {
+  u32x4 code[2];
+  uint32_t sc[2];
+  template <int OP>
+  __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                       int64_t r0, int64_t K, int64_t st) {
+    const int rr = threadIdx.x >> 1, half = threadIdx.x & 1;
+    int64_t row = r0 + rr;
+    row = row < rows ? row : rows - 1;
+    int64_t k = st * NvGeom::KS + 32 * half;
+    k = k < K ? k : 0;   // a chunk at or beyond K reads the row start; it is zeroed on store
+    // K is a multiple of 32, so a chunk below K holds both of its blocks
+    code[OP] = *gp((const u32x4*)(codes + row * (K / 2) + k / 2));
+    const DQ_GAS uint8_t* sp = gp(scales + row * (K / 16) + k / 16);
+    sc[OP] = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+  }
+  template <int OP>
+  __device__ __forceinline__ void store(uint8_t* lds, int64_t K, int64_t st) const {
+    const int rr = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int64_t k0 = st * NvGeom::KS + 32 * half;
+    uint8_t* rp = lds + OP * NvGeom::TILE + rr * NvGeom::ROWB;
+    const uint32_t w[4] = {code[OP].x, code[OP].y, code[OP].z, code[OP].w};
+    const bool ok = k0 < K;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const float sbv = e4m3_value((sc[OP] >> (8 * blk)) & 127u);
+      float p[16];
+      fp4_decode16(w[2 * blk], w[2 * blk + 1], p);
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // e2m1 x e4m3 is exact in fp32 and has zero low halves: its top 16 bits are bf16
+        const uint32_t lo = f2u(ok ? p[2 * e] * sbv : 0.0f), hi = f2u(ok ? p[2 * e + 1] * sbv : 0.0f);
+        h[e] = (lo >> 16) | (hi & 0xFFFF0000u);
+      }
+      // 16 bf16 = two 16-byte chunks at K offset 32 half + 16 blk: chunks 4 half + 2 blk, +1
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = (4 * half + 2 * blk + q) ^ dma_swz<NVFP4>(rr);
+        *(u32x4*)(rp + 16 * c) = u32x4{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
+      }
+    }
+  }
+};
+
+template <int OUT_BF16>
+__global__ __launch_bounds__(256) void k_linear_nv(LinArgs p) {
+  extern __shared__ __align__(16) uint8_t lin_lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int tm, tn;
+  lin_tile(p.tiles_m * p.tiles_n, p.tiles_m, tm, tn);
+  const int64_t mt0 = (int64_t)tm * kLinTile, nt0 = (int64_t)tn * kLinTile;
+  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int g = lane >> 4, r16 = lane & 15;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t nst = (p.K + NvGeom::KS - 1) / NvGeom::KS;
+  NvStage stg;
+  auto fetch = [&](int64_t st) {
+    stg.template load<0>(p.a, p.as, p.M, mt0, p.K, st);
+    stg.template load<1>(p.b, p.bs, p.N, nt0, p.K, st);
+  };
+  auto put = [&](int64_t st, uint8_t* buf) {
+    stg.template store<0>(buf, p.K, st);
+    stg.template store<1>(buf, p.K, st);
+  };
+  if (nst > 0) {
+    fetch(0);
+    put(0, lin_lds);
+    __syncthreads();
+  }
+  for (int64_t st = 0; st < nst; ++st) {
+    uint8_t* cur = lin_lds + (st & 1) * NvGeom::STAGE;
+    uint8_t* nxt = lin_lds + ((st + 1) & 1) * NvGeom::STAGE;
+    const bool more = st + 1 < nst;
+    if (more) fetch(st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NvGeom::KS / 32; ++u) {
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = wm + 16 * i + r16, rb = wn + 16 * i + r16;
+        a[i] = *(const bf16x8*)(cur + ra * NvGeom::ROWB + 16 * ((4 * u + g) ^ dma_swz<NVFP4>(ra)));
+        b[i] = *(const bf16x8*)(cur + NvGeom::TILE + rb * NvGeom::ROWB +
+                                16 * ((4 * u + g) ^ dma_swz<NVFP4>(rb)));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) put(st + 1, nxt);
+    __syncthreads();
+  }
+
+  const float ts = gp(p.ats)[0] * gp(p.bts)[0];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = nt0 + wn + 16 * j + r16;
+    const float rn = (p.r && n < p.N) ? gp(p.r)[n] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = mt0 + wm + 16 * i + 4 * g + v;
+        if (m < p.M && n < p.N) {
+          const float yv = (acc[i][j][v] * ts) * rn;
           if (OUT_BF16) gp((uint16_t*)p.y)[m * p.ldy + n] = (uint16_t)(f2u(bf16_rne(yv)) >> 16);
           else gp((float*)p.y)[m * p.ldy + n] = yv;
         }

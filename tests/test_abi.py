@@ -117,17 +117,26 @@ def test_quantize_multi_argument_errors(dq):
 def test_quantized_linear_argument_errors(dq):
     L = dq._lib
     mx = dq.dq_quant_spec(2, 0)
-    a = (0x10000, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, 0x50000)
-    assert L.dq_quantized_linear(dq.dq_quant_spec(3, 0), *a, 0, 64, None) == -4   # NVFP4
-    assert L.dq_quantized_linear(dq.dq_quant_spec(1, 0), *a, 0, 64, None) == -4   # MXINT4
-    assert L.dq_quantized_linear(mx, *a, 5, 64, None) == -4                       # dtype
-    assert L.dq_quantized_linear(mx, *a, 0, 63, None) == -2                       # ldy < N
-    assert L.dq_quantized_linear(mx, 0x10000, 0x20000, 64, 0x30000, 0x40000, 64, 100, None, 0x50000, 0, 64, None) == -2
-    assert L.dq_quantized_linear(mx, 0x10008, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, 0x50000, 0, 64, None) == -3
-    assert L.dq_quantized_linear(mx, 0x10000, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, 0x50002, 0, 64, None) == -3
-    assert L.dq_quantized_linear(mx, None, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, 0x50000, 0, 64, None) == -1
-    assert L.dq_quantized_linear(mx, 0x10000, 0x20000, 64, 0x30000, 0x40000, 64, 256, None, None, 0, 64, None) == -1
-    assert L.dq_quantized_linear(mx, None, None, 0, None, None, 64, 256, None, None, 0, 64, None) == 0   # M = 0
+    nv = dq.dq_quant_spec(3, 0)
+
+    def call(spec, ac=0x10000, asc=0x20000, ats=None, M=64, bc=0x30000, bsc=0x40000, bts=None,
+             N=64, K=256, r=None, y=0x50000, dt=0, ldy=64):
+        return L.dq_quantized_linear(spec, ac, asc, ats, M, bc, bsc, bts, N, K, r, y, dt, ldy, None)
+
+    assert call(dq.dq_quant_spec(1, 0)) == -4            # MXINT4 (recode it first)
+    assert call(dq.dq_quant_spec(0, 0)) == -4            # INT4
+    assert call(mx, dt=5) == -4                          # output dtype
+    assert call(mx, ldy=63) == -2                        # ldy < N
+    assert call(mx, K=100) == -2                         # K not a multiple of 32
+    assert call(nv, K=48, ats=0x60000, bts=0x60000) == -2
+    assert call(mx, ac=0x10008) == -3                    # codes not 16-byte aligned
+    assert call(mx, y=0x50002) == -3                     # fp32 output misaligned
+    assert call(mx, ac=None) == -1
+    assert call(mx, y=None) == -1
+    assert call(nv) == -1                                # NVFP4 needs both tensor scales
+    assert call(nv, ats=0x60000) == -1
+    assert call(nv, bts=0x60000) == -1
+    assert call(mx, ac=None, asc=None, M=0, bc=None, bsc=None, y=None) == 0   # M = 0
 
 
 def test_recode_argument_errors(dq):

@@ -188,3 +188,100 @@ def test_mxint4_linear(oracle_lib, shape):
     mi, ni = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     _, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, "MXINT4", mi.ravel(), ni.ravel(), r=r)
     assert np.all(np.abs(y - ref) <= _tol("MXFP6_E2M3", K, absy.reshape(M, N), ref, torch.float32))
+
+
+# ---- NVFP4 on the bf16 matrix cores.  Every element e2m1 * e4m3 is exact in bf16, so the
+# products are exact and only fp32 sums round: the instructions' internal sums of 32 and the
+# accumulation over K/32 of them (bound (K/32 + 2) 2^-24 + 2^-21 of sum |a b|, the last
+# term leaving room for an internal sum kept in fewer bits), then the tensor-scale product,
+# its multiply and the r multiply (3 more roundings of the result).
+
+def _nv_inputs(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    a = pack_codes(rng.integers(0, 16, M * K).astype(np.uint8), 4)
+    b = pack_codes(rng.integers(0, 16, N * K).astype(np.uint8), 4)
+    # E4M3 block scales over every finite non-negative code: zero, subnormals, up to 448
+    asc = rng.integers(0, 0x7F, M * K // 16).astype(np.uint8)
+    bsc = rng.integers(0, 0x7F, N * K // 16).astype(np.uint8)
+    asc[:2], bsc[:2] = [1, 0x7E], [0x7E, 0]
+    r = np.exp2(rng.uniform(-2, 2, N)).astype(np.float32)
+    ats, bts = np.float32(rng.uniform(1e-3, 4.0)), np.float32(rng.uniform(1e-3, 4.0))
+    return a, asc, b, bsc, r, ats, bts
+
+
+def _nv_tol(K, absy, y, out_dtype):
+    t = ((K // 32 + 5) * 2.0 ** -24 + 2.0 ** -21) * absy
+    if out_dtype == torch.bfloat16:
+        t = t + 2.0 ** -8 * (np.abs(y) + t)
+    return t + 1e-37
+
+
+def _nv_run(a, asc, b, bsc, M, N, K, r, ats, bts, out_dtype):
+    dev = lambda x: torch.from_numpy(x).to(DEV)
+    y = dq.quantized_linear(dev(a), dev(asc), dev(b), dev(bsc), M, N, K, "NVFP4",
+                            r=None if r is None else to_dev(r), out_dtype=out_dtype,
+                            a_tensor_scale=to_dev(np.array([ats])),
+                            b_tensor_scale=to_dev(np.array([bts])))
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("shape", [(100, 70, 384), (1, 16, 32), (130, 257, 4128), (256, 256, 1024)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_nvfp4_random_codes(oracle_lib, shape, out_dtype):
+    """Ragged M and N tiles; K = 32 and 4128 leave the last stage half empty."""
+    M, N, K = shape
+    print(f"[linear] NVFP4 {M}x{N}x{K} {out_dtype}", flush=True)
+    a, asc, b, bsc, r, ats, bts = _nv_inputs(M, N, K, M + N + K)
+    for rr in (r, None):
+        y = _nv_run(a, asc, b, bsc, M, N, K, rr, ats, bts, out_dtype)
+        ref = oracle_lib.quantized_linear(a, asc, M, b, bsc, N, K, "NVFP4", r=rr, a_ts=ats, b_ts=bts)
+        mi, ni = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        _, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, "NVFP4", mi.ravel(),
+                                                      ni.ravel(), r=rr, a_ts=ats, b_ts=bts)
+        absy = absy.reshape(M, N)
+        err = np.abs(y - ref)
+        print(f"[linear] NVFP4 max err / sum|ab| = {float((err / (absy + 1e-300)).max()):.3g}", flush=True)
+        assert np.all(err <= _nv_tol(K, absy, ref, out_dtype))
+
+
+def test_nvfp4_full_size_sampled(oracle_lib):
+    """2048 tokens x 4096 outputs x 14336 inputs (the down projection): 256 sampled entries."""
+    M, N, K = 2048, 4096, 14336
+    print(f"[linear] NVFP4 {M}x{N}x{K}", flush=True)
+    a, asc, b, bsc, r, ats, bts = _nv_inputs(M, N, K, 9)
+    y = _nv_run(a, asc, b, bsc, M, N, K, r, ats, bts, torch.float32)
+    rng = np.random.default_rng(10)
+    mi, ni = rng.integers(0, M, 256), rng.integers(0, N, 256)
+    mi[:4], ni[:4] = [0, M - 1, 0, M - 1], [0, 0, N - 1, N - 1]
+    ref, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, "NVFP4", mi, ni, r=r,
+                                                    a_ts=ats, b_ts=bts)
+    assert np.all(np.abs(y[mi, ni] - ref) <= _nv_tol(K, absy, ref, torch.float32))
+
+
+def test_nvfp4_layer_from_solved_weights(oracle_lib):
+    """512 x 4096 slice of the q projection solved in NVFP4 (T = 4), 256 tokens quantised
+    with its column scales; the layer uses both tensor scales."""
+    W, _, _, _, _ = synth.workload("q4096x4096_mxfp4")
+    W = np.ascontiguousarray(W[:512])
+    X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(256, 4096), 3)
+    res = dq.solve(to_dev(W), "NVFP4", 4)
+    cx, sx, tx = dq.rescale_quantize_acts(to_dev(X), res["c"], "NVFP4")
+    y = dq.quantized_linear(cx, sx, res["codes"], res["scales"], 256, 512, 4096, "NVFP4",
+                            r=res["r"], a_tensor_scale=tx, b_tensor_scale=res["tscale"])
+    torch.cuda.synchronize()
+    yc = y.cpu().numpy().astype(np.float64)
+    ats, bts = float(tx.cpu()[0]), float(res["tscale"].cpu()[0])
+    args = (cx.cpu().numpy(), sx.cpu().numpy(), 256, res["codes"].cpu().numpy(),
+            res["scales"].cpu().numpy(), 512, 4096, "NVFP4")
+    rr = res["r"].cpu().numpy()
+    ref = oracle_lib.quantized_linear(*args, r=rr, a_ts=ats, b_ts=bts)
+    mi, ni = np.meshgrid(np.arange(256), np.arange(512), indexing="ij")
+    _, absy = oracle_lib.quantized_linear_entries(*args, mi.ravel(), ni.ravel(), r=rr, a_ts=ats, b_ts=bts)
+    assert np.all(np.abs(yc - ref) <= _nv_tol(4096, absy.reshape(256, 512), ref, torch.float32))
+    Xf = (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    Wf = (W.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    exact = Xf @ Wf.T
+    rel = np.linalg.norm(yc - exact) / np.linalg.norm(exact)
+    print(f"[linear] W4A4 NVFP4 layer relative error vs bf16 product: {rel:.4f}", flush=True)
+    assert rel < 0.5

@@ -106,3 +106,42 @@ def test_scaling_laws_and_entries(oracle_lib, fmt):
     mi, ni = rng.integers(0, M, 20), rng.integers(0, N, 20)
     ye, ay = oracle_lib.quantized_linear_entries(pa, asc, M, pb, bsc, N, K, fmt, mi, ni, r=r)
     assert np.array_equal(ye, yr[mi, ni]) and np.all(ay >= np.abs(ye))
+
+
+def test_hand_example_nvfp4(oracle_lib):
+    # A block: 1.0, -2.0, 0.5, 6.0 (codes 2, 12, 1, 7), E4M3 block scale 1.5 (0x3C), s_t 3.0
+    # B block: 3.0, 1.5, -4.0, 0.5 (codes 5, 3, 14, 1), E4M3 block scale 0.25 (0x28), s_t 0.125
+    # sum = 1;  times 1.5 * 0.25 * 3 * 0.125 = 0.140625;  r = 2 -> 0.28125
+    a = np.zeros(32, np.uint8)
+    a[:4] = [2, 12, 1, 7]
+    b = np.zeros(32, np.uint8)
+    b[:4] = [5, 3, 14, 1]
+    # second block: A 0.5 (code 1) at scale 0.001953125 (subnormal 0x01 = 2^-9), B -6 at
+    # scale 448 (0x7E): adds 0.5 * 2^-9 * -6 * 448 * 0.375 = -0.984375 before r
+    a[16], b[16] = 1, 15
+    y = oracle_lib.quantized_linear(_pack(a, 4), np.array([0x3C, 0x01], np.uint8), 1, _pack(b, 4),
+                                    np.array([0x28, 0x7E], np.uint8), 1, 32, "NVFP4",
+                                    r=np.array([2.0], np.float32), a_ts=3.0, b_ts=0.125)
+    assert y.shape == (1, 1) and y[0, 0] == 2.0 * (0.140625 - 0.984375)
+
+
+def test_nvfp4_one_hot_and_tensor_scales(oracle_lib):
+    rng = np.random.default_rng(4)
+    M, N, K = 7, 5, 96
+    ae = rng.integers(0, 16, M * K).astype(np.uint8)
+    asc = rng.integers(0, 0x7F, M * K // 16).astype(np.uint8)
+    perm = rng.permutation(K)[:N]
+    be = np.zeros((N, K), np.uint8)
+    be[np.arange(N), perm] = 2                       # e2m1 1.0
+    bsc = np.full(N * K // 16, 0x38, np.uint8)       # e4m3 1.0
+    r = np.exp2(rng.integers(-3, 4, N)).astype(np.float32)
+    pa, pb = _pack(ae, 4), _pack(be.reshape(-1), 4)
+    y = oracle_lib.quantized_linear(pa, asc, M, pb, bsc, N, K, "NVFP4", r=r, a_ts=0.25, b_ts=1.0)
+    deqA = oracle_lib.dequantize(pa, asc, 0.25, "NVFP4", M, K).astype(np.float64)
+    assert np.array_equal(y, deqA[:, perm] * r[None, :])
+    # the two tensor scales multiply the result (exactly, for powers of two)
+    y2 = oracle_lib.quantized_linear(pa, asc, M, pb, bsc, N, K, "NVFP4", r=r, a_ts=0.5, b_ts=4.0)
+    assert np.array_equal(y2, 8 * y)
+    ye, ay = oracle_lib.quantized_linear_entries(pa, asc, M, pb, bsc, N, K, "NVFP4", [0, M - 1],
+                                                 [N - 1, 0], r=r, a_ts=0.25, b_ts=1.0)
+    assert np.array_equal(ye, y[[0, M - 1], [N - 1, 0]]) and np.all(ay >= np.abs(ye))
