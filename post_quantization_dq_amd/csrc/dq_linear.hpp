@@ -419,21 +419,33 @@ __global__ __launch_bounds__(256) void k_linear_dma(LinArgs p) {
   }
 }
 
-// ---------------------------------------------------------------- NVFP4 on the bf16 cores
+// ---------------------------------------------------------------- NVFP4 on the f16 cores
 // NVFP4 scales (E4M3 per 16 elements, fp32 per tensor) have no block-scaled matrix-core
 // form.  Within a tensor every element is e2m1(q) * e4m3(sb) * s_t, and e2m1(q) * e4m3(sb)
-// has at most 6 significant bits, so it is exact in bf16: the operands are dequantised to
-// that product on the way into LDS, multiplied on the bf16 cores (v_mfma_f32_16x16x32_bf16:
-// lane l holds row l % 16 and K 8 (l / 16) .. +7, measured), and the two tensor scales and
-// r are applied to the fp32 result.  Stage = 64 K: a 128-byte bf16 row per tile row.
+// has at most 6 significant bits and lies in [2^-10, 2688] (or is zero), so it is exact in
+// fp16: the operands are dequantised to that product on the way into LDS (the hardware
+// FP4 -> packed f16 conversion, then one packed f16 multiply by the block scale: one
+// instruction per element), multiplied on the f16 cores (v_mfma_f32_16x16x32_f16: lane l
+// holds row l % 16 and K 8 (l / 16) .. +7, measured), and the two tensor scales and r are
+// applied to the fp32 result.  Stage = 64 K: a 128-byte f16 row per tile row.
 struct NvGeom {
   static constexpr int KS = 64;
-  static constexpr int ROWB = KS * 2;               // 128 bytes of bf16
+  static constexpr int ROWB = KS * 2;               // 128 bytes of f16
   static constexpr int TILE = kLinTile * ROWB;      // 16 KiB
   static constexpr int STAGE = 2 * TILE;
   static constexpr int LDS = 2 * STAGE;             // 64 KiB
 };
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Eight e2m1 codes (one word, low nibble first) times s, as four packed f16 pairs: byte b
+// of the word holds elements 2b (low nibble, low half) and 2b + 1.
+__device__ __forceinline__ void fp4_f16_scaled8(uint32_t w, f16x2 s, uint32_t* h) {
+  h[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s);
+  h[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s);
+  h[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s);
+  h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s);
+}
 
 // One thread's share of a stage of one operand: tile row t / 2, 32 elements (two NVFP4
 // blocks) starting at K 32 (t % 2) of the stage.
@@ -462,17 +474,13 @@ struct NvStage {
     const bool ok = k0 < K;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const float sbv = e4m3_value((sc[OP] >> (8 * blk)) & 127u);
-      float p[16];
-      fp4_decode16(w[2 * blk], w[2 * blk + 1], p);
+      // a chunk beyond K gets scale 0, so its elements store as zeros
+      const _Float16 sv = (_Float16)(ok ? e4m3_value((sc[OP] >> (8 * blk)) & 127u) : 0.0f);
+      const f16x2 s2 = {sv, sv};
       uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // e2m1 x e4m3 is exact in fp32 and has zero low halves: its top 16 bits are bf16
-        const uint32_t lo = f2u(ok ? p[2 * e] * sbv : 0.0f), hi = f2u(ok ? p[2 * e + 1] * sbv : 0.0f);
-        h[e] = (lo >> 16) | (hi & 0xFFFF0000u);
-      }
-      // 16 bf16 = two 16-byte chunks at K offset 32 half + 16 blk: chunks 4 half + 2 blk, +1
+      fp4_f16_scaled8(w[2 * blk], s2, h);
+      fp4_f16_scaled8(w[2 * blk + 1], s2, h + 4);
+      // 16 f16 = two 16-byte chunks at K offset 32 half + 16 blk: chunks 4 half + 2 blk, +1
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int c = (4 * half + 2 * blk + q) ^ dma_swz<NVFP4>(rr);
@@ -521,19 +529,19 @@ __global__ __launch_bounds__(256) void k_linear_nv(LinArgs p) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NvGeom::KS / 32; ++u) {
-      bf16x8 a[4], b[4];
+      f16x8 a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ra = wm + 16 * i + r16, rb = wn + 16 * i + r16;
-        a[i] = *(const bf16x8*)(cur + ra * NvGeom::ROWB + 16 * ((4 * u + g) ^ dma_swz<NVFP4>(ra)));
-        b[i] = *(const bf16x8*)(cur + NvGeom::TILE + rb * NvGeom::ROWB +
-                                16 * ((4 * u + g) ^ dma_swz<NVFP4>(rb)));
+        a[i] = *(const f16x8*)(cur + ra * NvGeom::ROWB + 16 * ((4 * u + g) ^ dma_swz<NVFP4>(ra)));
+        b[i] = *(const f16x8*)(cur + NvGeom::TILE + rb * NvGeom::ROWB +
+                               16 * ((4 * u + g) ^ dma_swz<NVFP4>(rb)));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (more) put(st + 1, nxt);
