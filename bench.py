@@ -18,6 +18,7 @@ on this host.
   python bench.py --copy-calibration     # plain copy of known size, for counter scaling
   python bench.py --workload llama31_8b_nvfp4 --steps 3 --warmup 1   # the batched 224-matrix set
   python bench.py --workload linear_w4a4_mxfp4   # the quantised linear layer on solved codes
+  python bench.py --workload linear_w4a4_nvfp4   # the same layer in NVFP4 (f16 cores)
   python bench.py --workload qkv_acts_nvfp4      # fused q/k/v activation quantise
 """
 
@@ -152,28 +153,34 @@ def bench_llama_set(args):
 
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 matrix-core peak
+F16_MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 matrix-core peak
 
 
-def bench_linear(args):
+def bench_linear(args, fmt):
     """The quantised linear layer on codes the solver and the activation quantiser made:
-    the q_proj-shaped 4096x4096 weight solved to MXFP4 (T = 16), 2048 tokens of activations
-    rescaled by the solved c and quantised to MXFP4, Y = Aq Q^T diag(r) in bf16."""
+    the q_proj-shaped 4096x4096 weight solved to `fmt` (MXFP4 or NVFP4, T = 16), 2048 tokens
+    of activations rescaled by the solved c and quantised to the same format,
+    Y = Aq Q^T diag(r) in bf16.  MXFP4 runs on the FP4 block-scaled matrix cores, NVFP4 on
+    the f16 cores after an exact dequantisation in the kernel."""
     import torch
 
     import post_quantization_dq_amd as dq
     import synth
 
     dev = torch.device("cuda:0")
-    W, _, fmt, _, T = synth.workload("q4096x4096_mxfp4")
+    W, _, _, _, T = synth.workload("q4096x4096_mxfp4")
     N, K = W.shape
     M = ACT_TOKENS
     X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(M, K), 0)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     res = dq.solve(to_dev(W), fmt, T)
-    ac, asc, _ = dq.rescale_quantize_acts(to_dev(X), res["c"], fmt)
+    ac, asc, ats = dq.rescale_quantize_acts(to_dev(X), res["c"], fmt)
+    nv = fmt == "NVFP4"
+    bts = res["tscale"] if nv else None
+    ats = ats if nv else None
     y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     spec = dq.spec_of(fmt)
-    call = lambda: dq.dq_quantized_linear(spec, ac, asc, None, M, res["codes"], res["scales"], None, N, K,
+    call = lambda: dq.dq_quantized_linear(spec, ac, asc, ats, M, res["codes"], res["scales"], bts, N, K,
                                           res["r"], y)
     print(f"[bench] quantised linear {fmt}: Y[{M}x{N}] = A[{M}x{K}] Q^T diag(r), bf16 out", flush=True)
     for _ in range(args.warmup):
@@ -190,18 +197,20 @@ def bench_linear(args):
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
+    peak = F16_MFMA_PEAK_TFLOPS if nv else FP4_MFMA_PEAK_TFLOPS
     out = {
-        "metric": "quantised linear layer TFLOP/s (W4A4 MXFP4 codes from the solver)",
+        "metric": f"quantised linear layer TFLOP/s (W4A4 {fmt} codes from the solver)",
         "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
-        "config": {"workload": f"q_proj-shaped {N}x{K} weight solved to MXFP4 (T={T}); {M} tokens of "
-                               f"activations rescaled by the solved c and quantised to MXFP4; bf16 output",
+        "scaling": "weak", "vs_baseline": None, "dtype": fmt.lower(), "data": "synthetic",
+        "config": {"workload": f"q_proj-shaped {N}x{K} weight solved to {fmt} (T={T}); {M} tokens of "
+                               f"activations rescaled by the solved c and quantised to {fmt}; bf16 output",
                    "M": M, "N": N, "K": K},
-        "roofline": {"bound": "mfma", "kernel": "k_linear_dma", "achieved": round(tflops, 1),
-                     "peak": FP4_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / FP4_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "alg_flops_per_launch": flops, "avg_launch_ms": round(ms, 4)},
+        "roofline": {"bound": "mfma", "kernel": "k_linear_nv" if nv else "k_linear_dma",
+                     "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "alg_flops_per_launch": flops, "avg_launch_ms": round(ms, 4),
+                     "cores": "f16 (exact e2m1 x e4m3 elements)" if nv else "fp4 block-scaled"},
         "wall_ms_per_call": round(wall * 1e3, 4),
     }
     print(json.dumps(out), flush=True)
@@ -286,8 +295,8 @@ def main():
     if args.workload == "llama31_8b_nvfp4":
         bench_llama_set(args)
         return
-    if args.workload == "linear_w4a4_mxfp4":
-        bench_linear(args)
+    if args.workload in ("linear_w4a4_mxfp4", "linear_w4a4_nvfp4"):
+        bench_linear(args, args.workload.rsplit("_", 1)[1].upper())
         return
     if args.workload == "qkv_acts_nvfp4":
         bench_qkv_acts(args)

@@ -447,15 +447,24 @@ __device__ __forceinline__ void fp4_f16_scaled8(uint32_t w, f16x2 s, uint32_t* h
   h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s);
 }
 
-// One thread's share of a stage of one operand: tile row t / 2, 32 elements (two NVFP4
-// blocks) starting at K 32 (t % 2) of the stage.
-struct NvStage {
+// Tile row of thread t (the other half of the row's stage is thread t ^ 1).  Each group of
+// 8 lanes takes four even or four odd rows whose swizzles differ, so the 16-byte chunks its
+// LDS stores hit are 8 distinct bank groups (pairs of consecutive rows, which share a
+// swizzle, in one group of 8 made every store a 2-way bank conflict).
+__device__ __forceinline__ int nv_row(int t) {
+  return 8 * (t >> 4) + 2 * ((t >> 1) & 3) + ((t >> 3) & 1);
+}
+
+// One thread's share of one stage of both operands: tile row nv_row(t), 32 elements (two
+// NVFP4 blocks) starting at K 32 (t % 2) of the stage, as loaded (codes and the two scale
+// bytes).
+struct NvRaw {
   u32x4 code[2];
   uint32_t sc[2];
   template <int OP>
   __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                        int64_t r0, int64_t K, int64_t st) {
-    const int rr = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int rr = nv_row(threadIdx.x), half = threadIdx.x & 1;
     int64_t row = r0 + rr;
     row = row < rows ? row : rows - 1;
     int64_t k = st * NvGeom::KS + 32 * half;
@@ -465,17 +474,20 @@ struct NvStage {
     const DQ_GAS uint8_t* sp = gp(scales + row * (K / 16) + k / 16);
     sc[OP] = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
   }
+  // Dequantise to f16 and write the two blocks into the LDS tile of operand OP.
   template <int OP>
   __device__ __forceinline__ void store(uint8_t* lds, int64_t K, int64_t st) const {
-    const int rr = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int rr = nv_row(threadIdx.x), half = threadIdx.x & 1;
     const int64_t k0 = st * NvGeom::KS + 32 * half;
     uint8_t* rp = lds + OP * NvGeom::TILE + rr * NvGeom::ROWB;
     const uint32_t w[4] = {code[OP].x, code[OP].y, code[OP].z, code[OP].w};
-    const bool ok = k0 < K;
+    // both block scales at once (E4M3 codes 0..126; the sign bits are cleared, as the format
+    // stores non-negative scales); a chunk beyond K gets scale 0 and so stores zeros
+    f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[OP] & 0x7F7Fu, 1.0f, false);
+    if (k0 >= K) s01 = f16x2{(_Float16)0.0f, (_Float16)0.0f};
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      // a chunk beyond K gets scale 0, so its elements store as zeros
-      const _Float16 sv = (_Float16)(ok ? e4m3_value((sc[OP] >> (8 * blk)) & 127u) : 0.0f);
+      const _Float16 sv = blk ? s01.y : s01.x;
       const f16x2 s2 = {sv, sv};
       uint32_t h[8];
       fp4_f16_scaled8(w[2 * blk], s2, h);
@@ -490,6 +502,17 @@ struct NvStage {
   }
 };
 
+// Wait for this wave's LDS writes, then a bare workgroup barrier.  Global loads of later
+// stages stay in flight (the fence of __syncthreads would wait for them too); the memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0), vmcnt and expcnt free
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Y tile 128 x 128 per workgroup, four waves of 64 x 64 (as k_linear).  Stages of 64 K:
+// raw codes are loaded into registers two stages ahead, dequantised into one of two f16
+// LDS buffers one stage ahead, and multiplied from the other.
 template <int OUT_BF16>
 __global__ __launch_bounds__(256) void k_linear_nv(LinArgs p) {
   extern __shared__ __align__(16) uint8_t lin_lds[];
@@ -507,35 +530,27 @@ __global__ __launch_bounds__(256) void k_linear_nv(LinArgs p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int64_t nst = (p.K + NvGeom::KS - 1) / NvGeom::KS;
-  NvStage stg;
-  auto fetch = [&](int64_t st) {
-    stg.template load<0>(p.a, p.as, p.M, mt0, p.K, st);
-    stg.template load<1>(p.b, p.bs, p.N, nt0, p.K, st);
+  uint8_t* const buf0 = lin_lds;
+  uint8_t* const buf1 = lin_lds + NvGeom::STAGE;
+  NvRaw ra, rb;
+  auto fetch = [&](NvRaw& R, int64_t st) {
+    R.template load<0>(p.a, p.as, p.M, mt0, p.K, st);
+    R.template load<1>(p.b, p.bs, p.N, nt0, p.K, st);
   };
-  auto put = [&](int64_t st, uint8_t* buf) {
-    stg.template store<0>(buf, p.K, st);
-    stg.template store<1>(buf, p.K, st);
+  auto put = [&](const NvRaw& R, int64_t st, uint8_t* buf) {
+    R.template store<0>(buf, p.K, st);
+    R.template store<1>(buf, p.K, st);
   };
-  if (nst > 0) {
-    fetch(0);
-    put(0, lin_lds);
-    __syncthreads();
-  }
-  for (int64_t st = 0; st < nst; ++st) {
-    uint8_t* cur = lin_lds + (st & 1) * NvGeom::STAGE;
-    uint8_t* nxt = lin_lds + ((st + 1) & 1) * NvGeom::STAGE;
-    const bool more = st + 1 < nst;
-    if (more) fetch(st + 1);
-    __builtin_amdgcn_sched_barrier(0);
+  auto mma = [&](const uint8_t* cur) {
 #pragma unroll
     for (int u = 0; u < NvGeom::KS / 32; ++u) {
       f16x8 a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ra = wm + 16 * i + r16, rb = wn + 16 * i + r16;
-        a[i] = *(const f16x8*)(cur + ra * NvGeom::ROWB + 16 * ((4 * u + g) ^ dma_swz<NVFP4>(ra)));
-        b[i] = *(const f16x8*)(cur + NvGeom::TILE + rb * NvGeom::ROWB +
-                               16 * ((4 * u + g) ^ dma_swz<NVFP4>(rb)));
+        const int ra_ = wm + 16 * i + r16, rb_ = wn + 16 * i + r16;
+        a[i] = *(const f16x8*)(cur + ra_ * NvGeom::ROWB + 16 * ((4 * u + g) ^ dma_swz<NVFP4>(ra_)));
+        b[i] = *(const f16x8*)(cur + NvGeom::TILE + rb_ * NvGeom::ROWB +
+                               16 * ((4 * u + g) ^ dma_swz<NVFP4>(rb_)));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -543,9 +558,29 @@ __global__ __launch_bounds__(256) void k_linear_nv(LinArgs p) {
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) put(st + 1, nxt);
-    __syncthreads();
+  };
+
+  if (nst > 0) fetch(ra, 0);
+  if (nst > 1) fetch(rb, 1);
+  if (nst > 0) {
+    put(ra, 0, buf0);
+    lds_barrier();
+  }
+  // two stages per trip, so that the two register sets keep fixed names
+  for (int64_t st = 0; st < nst; st += 2) {
+    // stage st is in buf0; rb holds stage st + 1
+    if (st + 2 < nst) fetch(ra, st + 2);
+    mma(buf0);
+    if (st + 1 >= nst) break;
+    put(rb, st + 1, buf1);
+    lds_barrier();
+    // stage st + 1 is in buf1; ra holds stage st + 2
+    if (st + 3 < nst) fetch(rb, st + 3);
+    mma(buf1);
+    if (st + 2 < nst) {
+      put(ra, st + 2, buf0);
+      lds_barrier();
+    }
   }
 
   const float ts = gp(p.ats)[0] * gp(p.bts)[0];
