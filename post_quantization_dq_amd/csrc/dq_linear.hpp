@@ -474,30 +474,31 @@ struct NvRaw {
     const DQ_GAS uint8_t* sp = gp(scales + row * (K / 16) + k / 16);
     sc[OP] = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
   }
-  // Dequantise to f16 and write the two blocks into the LDS tile of operand OP.
+  // The two block scales of operand OP as f16 (E4M3 codes 0..126; the sign bits are
+  // cleared, as the format stores non-negative scales); a chunk at or beyond K gets scale 0,
+  // so it stores zeros.
   template <int OP>
-  __device__ __forceinline__ void store(uint8_t* lds, int64_t K, int64_t st) const {
+  __device__ __forceinline__ f16x2 scales(int64_t K, int64_t st) const {
+    const int64_t k0 = st * NvGeom::KS + 32 * (threadIdx.x & 1);
+    const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[OP] & 0x7F7Fu, 1.0f, false);
+    return k0 < K ? s01 : f16x2{(_Float16)0.0f, (_Float16)0.0f};
+  }
+  // Block BLK of operand OP dequantised to f16 with its scale, written into OP's LDS tile:
+  // 16 f16 = two 16-byte chunks at K offset 32 half + 16 BLK, chunks 4 half + 2 BLK and +1.
+  template <int OP, int BLK>
+  __device__ __forceinline__ void store_blk(uint8_t* lds, f16x2 s01) const {
     const int rr = nv_row(threadIdx.x), half = threadIdx.x & 1;
-    const int64_t k0 = st * NvGeom::KS + 32 * half;
     uint8_t* rp = lds + OP * NvGeom::TILE + rr * NvGeom::ROWB;
-    const uint32_t w[4] = {code[OP].x, code[OP].y, code[OP].z, code[OP].w};
-    // both block scales at once (E4M3 codes 0..126; the sign bits are cleared, as the format
-    // stores non-negative scales); a chunk beyond K gets scale 0 and so stores zeros
-    f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[OP] & 0x7F7Fu, 1.0f, false);
-    if (k0 >= K) s01 = f16x2{(_Float16)0.0f, (_Float16)0.0f};
+    const uint32_t w0 = BLK ? code[OP].z : code[OP].x, w1 = BLK ? code[OP].w : code[OP].y;
+    const _Float16 sv = BLK ? s01.y : s01.x;
+    const f16x2 s2 = {sv, sv};
+    uint32_t h[8];
+    fp4_f16_scaled8(w0, s2, h);
+    fp4_f16_scaled8(w1, s2, h + 4);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const _Float16 sv = blk ? s01.y : s01.x;
-      const f16x2 s2 = {sv, sv};
-      uint32_t h[8];
-      fp4_f16_scaled8(w[2 * blk], s2, h);
-      fp4_f16_scaled8(w[2 * blk + 1], s2, h + 4);
-      // 16 f16 = two 16-byte chunks at K offset 32 half + 16 blk: chunks 4 half + 2 blk, +1
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int c = (4 * half + 2 * blk + q) ^ dma_swz<NVFP4>(rr);
-        *(u32x4*)(rp + 16 * c) = u32x4{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
-      }
+    for (int q = 0; q < 2; ++q) {
+      const int c = (4 * half + 2 * BLK + q) ^ dma_swz<NVFP4>(rr);
+      *(u32x4*)(rp + 16 * c) = u32x4{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
     }
   }
 };
@@ -537,50 +538,76 @@ __global__ __launch_bounds__(256) void k_linear_nv(LinArgs p) {
     R.template load<0>(p.a, p.as, p.M, mt0, p.K, st);
     R.template load<1>(p.b, p.bs, p.N, nt0, p.K, st);
   };
-  auto put = [&](const NvRaw& R, int64_t st, uint8_t* buf) {
-    R.template store<0>(buf, p.K, st);
-    R.template store<1>(buf, p.K, st);
-  };
-  auto mma = [&](const uint8_t* cur) {
+  auto frags = [&](const uint8_t* cur, int u, f16x8 (&a)[4], f16x8 (&b)[4]) {
 #pragma unroll
-    for (int u = 0; u < NvGeom::KS / 32; ++u) {
-      f16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra_ = wm + 16 * i + r16, rb_ = wn + 16 * i + r16;
-        a[i] = *(const f16x8*)(cur + ra_ * NvGeom::ROWB + 16 * ((4 * u + g) ^ dma_swz<NVFP4>(ra_)));
-        b[i] = *(const f16x8*)(cur + NvGeom::TILE + rb_ * NvGeom::ROWB +
-                               16 * ((4 * u + g) ^ dma_swz<NVFP4>(rb_)));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int ra_ = wm + 16 * i + r16, rb_ = wn + 16 * i + r16;
+      a[i] = *(const f16x8*)(cur + ra_ * NvGeom::ROWB + 16 * ((4 * u + g) ^ dma_swz<NVFP4>(ra_)));
+      b[i] = *(const f16x8*)(cur + NvGeom::TILE + rb_ * NvGeom::ROWB +
+                             16 * ((4 * u + g) ^ dma_swz<NVFP4>(rb_)));
     }
   };
+  auto mrow = [&](int i, const f16x8& a, const f16x8 (&b)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
+  };
+#define DQ_SB __builtin_amdgcn_sched_barrier(0)
+  // The products of the stage in `cur` (two K-steps of 32, four rows of four products
+  // each), with the dequantisation of the stage held in R (index sn) into `nb` cut into
+  // four blocks and placed between them: the matrix cores take 16 cycles per product, in
+  // which the wave issues the conversions of the next stage.
+  auto half_trip = [&](const uint8_t* cur, const NvRaw& R, int64_t sn, uint8_t* nb) {
+    f16x8 a0[4], b0[4], a1[4], b1[4];
+    frags(cur, 0, a0, b0);
+    const f16x2 s0 = R.template scales<0>(p.K, sn), s1 = R.template scales<1>(p.K, sn);
+    mrow(0, a0[0], b0);
+    DQ_SB;
+    R.template store_blk<0, 0>(nb, s0);
+    DQ_SB;
+    mrow(1, a0[1], b0);
+    DQ_SB;
+    frags(cur, 1, a1, b1);
+    DQ_SB;
+    mrow(2, a0[2], b0);
+    DQ_SB;
+    R.template store_blk<0, 1>(nb, s0);
+    DQ_SB;
+    mrow(3, a0[3], b0);
+    mrow(0, a1[0], b1);
+    DQ_SB;
+    R.template store_blk<1, 0>(nb, s1);
+    DQ_SB;
+    mrow(1, a1[1], b1);
+    mrow(2, a1[2], b1);
+    DQ_SB;
+    R.template store_blk<1, 1>(nb, s1);
+    DQ_SB;
+    mrow(3, a1[3], b1);
+  };
+#undef DQ_SB
 
-  if (nst > 0) fetch(ra, 0);
-  if (nst > 1) fetch(rb, 1);
+  // Two stages per trip, so that the two register sets keep fixed names.  The trip has no
+  // branches: stages at or beyond K load in-range bytes and store zeros (their products add
+  // nothing).
   if (nst > 0) {
-    put(ra, 0, buf0);
+    fetch(ra, 0);
+    fetch(rb, 1);
+    ra.template store_blk<0, 0>(buf0, ra.template scales<0>(p.K, 0));
+    ra.template store_blk<0, 1>(buf0, ra.template scales<0>(p.K, 0));
+    ra.template store_blk<1, 0>(buf0, ra.template scales<1>(p.K, 0));
+    ra.template store_blk<1, 1>(buf0, ra.template scales<1>(p.K, 0));
     lds_barrier();
   }
-  // two stages per trip, so that the two register sets keep fixed names
   for (int64_t st = 0; st < nst; st += 2) {
-    // stage st is in buf0; rb holds stage st + 1
-    if (st + 2 < nst) fetch(ra, st + 2);
-    mma(buf0);
-    if (st + 1 >= nst) break;
-    put(rb, st + 1, buf1);
+    // stage st is in buf0; rb holds stage st + 1; buf1 is free
+    fetch(ra, st + 2);
+    half_trip(buf0, rb, st + 1, buf1);
     lds_barrier();
-    // stage st + 1 is in buf1; ra holds stage st + 2
-    if (st + 3 < nst) fetch(rb, st + 3);
-    mma(buf1);
-    if (st + 2 < nst) {
-      put(ra, st + 2, buf0);
-      lds_barrier();
-    }
+    // stage st + 1 is in buf1; ra holds stage st + 2; buf0 is free
+    fetch(rb, st + 3);
+    half_trip(buf1, ra, st + 2, buf0);
+    lds_barrier();
   }
 
   const float ts = gp(p.ats)[0] * gp(p.bts)[0];
