@@ -63,6 +63,50 @@ __device__ __forceinline__ void lin_tile(int ntiles, int tiles_m, int& tm, int& 
   tn = t / tiles_m;
 }
 
+// Stores one wave's 64 x 64 block of Y from accumulators of (B A^T) products (the weight
+// fragment is the instruction's first operand): acc[i][j][v] holds
+// Y[m0 + 16 i + lane % 16][n0 + 16 j + 4 (lane / 16) + v].  So each lane writes four
+// consecutive columns of one row, one 8-byte (bf16) or 16-byte (fp32) store where the
+// output's alignment and row pitch allow it, as (acc * s) * r[n].
+template <int OUT_BF16>
+__device__ __forceinline__ void lin_store(const f32x4 (&acc)[4][4], const LinArgs& p, int64_t m0,
+                                          int64_t n0, float s) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const bool vec = (p.ldy & 3) == 0 && ((uintptr_t)p.y & (OUT_BF16 ? 7u : 15u)) == 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + 16 * j + 4 * g;
+    float rn[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) rn[v] = (p.r && n + v < p.N) ? gp(p.r)[n + v] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + 16 * i + r16;
+      if (m >= p.M) continue;
+      float yv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) yv[v] = (acc[i][j][v] * s) * rn[v];
+      const int64_t o = m * p.ldy + n;
+      if (vec && n + 3 < p.N) {
+        if (OUT_BF16) {
+          const uint32_t h0 = (f2u(bf16_rne(yv[0])) >> 16) | (f2u(bf16_rne(yv[1])) & 0xFFFF0000u);
+          const uint32_t h1 = (f2u(bf16_rne(yv[2])) >> 16) | (f2u(bf16_rne(yv[3])) & 0xFFFF0000u);
+          *gp((u32x2*)((uint16_t*)p.y + o)) = u32x2{h0, h1};
+        } else {
+          *gp((f32x4*)((float*)p.y + o)) = f32x4{yv[0], yv[1], yv[2], yv[3]};
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (n + v >= p.N) break;
+          if (OUT_BF16) gp((uint16_t*)p.y)[o + v] = (uint16_t)(f2u(bf16_rne(yv[v])) >> 16);
+          else gp((float*)p.y)[o + v] = yv[v];
+        }
+      }
+    }
+  }
+}
+
 // Staging geometry per element width: K per stage (one or two instructions), bytes of a
 // row per stage, the global-load chunk, the padded LDS row pitch (consecutive rows start
 // 36 or 28 banks apart, so the 16 rows a fragment read touches fall on distinct banks) and
@@ -219,31 +263,15 @@ __global__ __launch_bounds__(256) void k_linear(LinArgs p) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], F, F, 0,
-                                                                        sa[i], 0, sb[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j], a[i], acc[i][j], F, F, 0,
+                                                                        sb[j], 0, sa[i]);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (more) put(st + 1, nxt);
     __syncthreads();
   }
 
-  // epilogue: Y[m][n] = acc * r[n]
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = nt0 + wn + 16 * j + r16;
-    const float rn = (p.r && n < p.N) ? gp(p.r)[n] : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = mt0 + wm + 16 * i + 4 * g + v;
-        if (m < p.M && n < p.N) {
-          const float yv = acc[i][j][v] * rn;
-          if (OUT_BF16) gp((uint16_t*)p.y)[m * p.ldy + n] = (uint16_t)(f2u(bf16_rne(yv)) >> 16);
-          else gp((float*)p.y)[m * p.ldy + n] = yv;
-        }
-      }
-  }
+  lin_store<OUT_BF16>(acc, p, mt0 + wm, nt0 + wn, 1.0f);   // Y[m][n] = acc * r[n]
 }
 
 // ---------------------------------------------------------------- direct-to-LDS variant
@@ -259,8 +287,8 @@ struct DmaGeom {
   static constexpr int KS = (EB == 4) ? 256 : 128;      // K per stage: rows of 128 bytes
   static constexpr int NI = KS / kLinK;                 // instructions per stage
   static constexpr int ROWB = KS * EB / 8;              // 128
-  static constexpr int CPR = ROWB / 16;                 // 8 chunks per row
-  static constexpr int RPI = 64 / CPR;                  // 8 rows per wave instruction
+  static constexpr int CPR = ROWB / 16;                 // chunks per row
+  static constexpr int RPI = 64 / CPR;                  // rows per wave instruction
   static constexpr int SPR = KS / 32;                   // scale bytes per row per stage
   static constexpr int TILE = kLinTile * ROWB;
   static constexpr int STILE = kLinTile * SPR;
@@ -268,14 +296,17 @@ struct DmaGeom {
   static constexpr int D = 2;                           // ring depth
   static constexpr int LDS = D * STAGE;                 // 68 KiB (FP4), 66 KiB (FP8)
   static constexpr int CODE_INSTS = kLinTile / RPI / 4; // per wave per operand per stage
-  static constexpr int SC_INSTS = SPR / 4;              // scale loads per wave per stage
+  static constexpr int SC_INSTS = (SPR + 3) / 4;        // scale loads per wave per stage
   static constexpr int INSTS = 2 * CODE_INSTS + SC_INSTS;
 };
-// Swizzle of the 16-byte chunk positions of row r: a 128-byte row spans 32 banks, so rows
-// of one parity share banks, and XOR-ing the chunk index with (r >> 1) & 7 gives the 16 rows
-// of a fragment read 16 distinct 4-bank groups.
+// Swizzle of the 16-byte chunk positions of a 128-byte row r, so that the 16 rows one
+// fragment read touches (one chunk each) hit 16 distinct 4-bank groups: a 128-byte row spans
+// 32 banks, so rows of one parity share banks, and the chunk index is XOR-ed with
+// (r >> 1) & 7.  (Stages of 128 K, 64-byte rows, in a four-deep ring were slower: 52 us
+// against 36 us on 2048 x 4096 x 4096.)
+__device__ __forceinline__ int swz128(int r) { return (r >> 1) & 7; }
 template <int FMT>
-__device__ __forceinline__ int dma_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int dma_swz(int r) { return swz128(r); }
 
 template <int FMT>
 __device__ __forceinline__ void dma_stage(const LinArgs& p, int64_t mt0, int64_t nt0, int64_t st,
@@ -364,17 +395,22 @@ __global__ __launch_bounds__(256) void k_linear_dma(LinArgs p) {
     const uint8_t* cur = lin_lds + (st % G::D) * G::STAGE;
     const uint8_t* sa_t = cur + 2 * G::TILE;
     const uint8_t* sb_t = sa_t + G::STILE;
+    // every fragment and scale read of the stage first, then its products: one wait for
+    // the LDS instead of one per row of products
+    v8i a[G::NI][4], b[G::NI][4];
+    int sa[G::NI][4], sb[G::NI][4];
 #pragma unroll
-    for (int u = 0; u < G::NI; ++u) {
-      v8i a[4], b[4];
-      int sa[4], sb[4];
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int op = 0; op < 2; ++op) {
+        const int r = (op ? wn : wm) + 16 * i + r16;
+        const uint8_t* rp = cur + op * G::TILE + r * G::ROWB;
+        const int sw = dma_swz<FMT>(r);
+        // the row's scale bytes of this stage in one read (the four lanes of a row share it)
+        const uint8_t* srow = (op ? sb_t : sa_t) + r * G::SPR;
+        const uint64_t sw8 = (G::SPR == 8) ? *(const uint64_t*)srow : (uint64_t)*(const uint32_t*)srow;
 #pragma unroll
-        for (int op = 0; op < 2; ++op) {
-          const int r = (op ? wn : wm) + 16 * i + r16;
-          const uint8_t* rp = cur + op * G::TILE + r * G::ROWB;
-          const int sw = dma_swz<FMT>(r);
+        for (int u = 0; u < G::NI; ++u) {
           v8i v;
           if (G::EB == 4) {
             const u32x4 x = *(const u32x4*)(rp + 16 * ((4 * u + g) ^ sw));
@@ -384,39 +420,23 @@ __global__ __launch_bounds__(256) void k_linear_dma(LinArgs p) {
             const u32x4 y = *(const u32x4*)(rp + 16 * ((4 + g) ^ sw));
             v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
           }
-          if (op) b[i] = v; else a[i] = v;
-          // the row's scale bytes of this stage in one read (the four lanes of a row share it)
-          const uint8_t* srow = (op ? sb_t : sa_t) + r * G::SPR;
-          const uint64_t sw8 = (G::SPR == 8) ? *(const uint64_t*)srow : (uint64_t)*(const uint32_t*)srow;
           const int sv = (int)((sw8 >> (8 * (4 * u + g))) & 0xFFu);
-          if (op) sb[i] = sv; else sa[i] = sv;
+          if (op) { b[u][i] = v; sb[u][i] = sv; } else { a[u][i] = v; sa[u][i] = sv; }
         }
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < G::NI; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], F, F, 0,
-                                                                        sa[i], 0, sb[j]);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[u][j], a[u][i], acc[i][j], F,
+                                                                        F, 0, sb[u][j], 0, sa[u][i]);
   }
 
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = nt0 + wn + 16 * j + r16;
-    const float rn = (p.r && n < p.N) ? gp(p.r)[n] : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = mt0 + wm + 16 * i + 4 * g + v;
-        if (m < p.M && n < p.N) {
-          const float yv = acc[i][j][v] * rn;
-          if (OUT_BF16) gp((uint16_t*)p.y)[m * p.ldy + n] = (uint16_t)(f2u(bf16_rne(yv)) >> 16);
-          else gp((float*)p.y)[m * p.ldy + n] = yv;
-        }
-      }
-  }
+  lin_store<OUT_BF16>(acc, p, mt0 + wm, nt0 + wn, 1.0f);
 }
 
 // ---------------------------------------------------------------- NVFP4 on the f16 cores
@@ -497,7 +517,7 @@ struct NvRaw {
     fp4_f16_scaled8(w1, s2, h + 4);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int c = (4 * half + 2 * BLK + q) ^ dma_swz<NVFP4>(rr);
+      const int c = (4 * half + 2 * BLK + q) ^ swz128(rr);
       *(u32x4*)(rp + 16 * c) = u32x4{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
     }
   }
@@ -542,15 +562,15 @@ __global__ __launch_bounds__(256) void k_linear_nv(LinArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ra_ = wm + 16 * i + r16, rb_ = wn + 16 * i + r16;
-      a[i] = *(const f16x8*)(cur + ra_ * NvGeom::ROWB + 16 * ((4 * u + g) ^ dma_swz<NVFP4>(ra_)));
+      a[i] = *(const f16x8*)(cur + ra_ * NvGeom::ROWB + 16 * ((4 * u + g) ^ swz128(ra_)));
       b[i] = *(const f16x8*)(cur + NvGeom::TILE + rb_ * NvGeom::ROWB +
-                             16 * ((4 * u + g) ^ dma_swz<NVFP4>(rb_)));
+                             16 * ((4 * u + g) ^ swz128(rb_)));
     }
   };
   auto mrow = [&](int i, const f16x8& a, const f16x8 (&b)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j], a, acc[i][j], 0, 0, 0);
   };
 #define DQ_SB __builtin_amdgcn_sched_barrier(0)
   // The products of the stage in `cur` (two K-steps of 32, four rows of four products
@@ -610,23 +630,7 @@ __global__ __launch_bounds__(256) void k_linear_nv(LinArgs p) {
     lds_barrier();
   }
 
-  const float ts = gp(p.ats)[0] * gp(p.bts)[0];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = nt0 + wn + 16 * j + r16;
-    const float rn = (p.r && n < p.N) ? gp(p.r)[n] : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = mt0 + wm + 16 * i + 4 * g + v;
-        if (m < p.M && n < p.N) {
-          const float yv = (acc[i][j][v] * ts) * rn;
-          if (OUT_BF16) gp((uint16_t*)p.y)[m * p.ldy + n] = (uint16_t)(f2u(bf16_rne(yv)) >> 16);
-          else gp((float*)p.y)[m * p.ldy + n] = yv;
-        }
-      }
-  }
+  lin_store<OUT_BF16>(acc, p, mt0 + wm, nt0 + wn, gp(p.ats)[0] * gp(p.bts)[0]);
 }
 
 // ---------------------------------------------------------------- MXINT4 -> MXFP6 E2M3
