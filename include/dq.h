@@ -156,8 +156,9 @@ size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_sp
  *           scales (so the MSE never increases);
  * where Proj is the nearest admissible value: powers of two 2^k, k in [-127,127] (MX,
  * ties up), E4M3 values in [2^-9, 448] (NVFP4), bf16 values >= 2^-126 (INT4, INT8).
- * Problems are independent; count > 1 runs them together on one GPU.  Blocks the calling
- * thread until done.  `workspace` must hold dq_workspace_bytes(...) bytes of device
+ * Problems are independent; count (1..65535) > 1 runs them together on one GPU.  Blocks
+ * the calling thread until done (one synchronisation of `stream` per round of sweeps: a
+ * second round only follows a rejected step whose iteration has to be re-solved).  `workspace` must hold dq_workspace_bytes(...) bytes of device
  * memory; its contents on entry do not matter. */
 int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
              dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream);

@@ -58,6 +58,9 @@ struct ProbDev {
   float* c_trace;   // [iters][cols] or null: unprojected c-step values
   const float* r_init;
   const float* c_init;
+  float* r_out;     // the caller's outputs: final r [rows], c [cols], NVFP4 tensor scale [1]
+  float* c_out;
+  float* ts_out;    // null outside NVFP4
   int32_t rowblocks, rows_per_blk, fin_wgs, iters;   // row pass: blocks of rows per workgroup
   int32_t nstrips, rranges, rows_per_range, init_wgs; // column pass: 1024-column strips x row ranges
   int32_t dtype;
@@ -68,6 +71,12 @@ struct ProbDev {
 
 struct WgEntry {
   int32_t prob, idx;
+};
+
+// A problem's state and flags as the host reads them after a round of sweeps.
+struct alignas(16) StateOut {
+  State st;
+  uint32_t flags, pad[3];
 };
 
 constexpr float kTinyTensorScale = 7.888609052210118e-31f;  // 2^-100
@@ -863,6 +872,54 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   }
   ns.sweeps += 1;
   *sn = ns;
+}
+
+// ---------------------------------------------------------------- outputs
+// After a round of sweeps: every problem's current state (slot `slot`) and flags go to
+// out[problem], so the host reads all of them in one copy, and a finished problem gets its
+// final r, c, NVFP4 tensor scale and, when its kept Qhat is in the second code buffer, its
+// codes and block scales copied into the caller's buffers.  (A problem that needs more
+// sweeps is copied after its last one; the first code buffer is the caller's, so a copy
+// into it is only made once nothing reads it any more.)  Grid: x = workgroups per problem,
+// y = problem; empty problems have no state and are skipped.
+__device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, int64_t bytes,
+                                           int64_t tid, int64_t nthr) {
+  const int64_t n16 = bytes >> 4;   // both buffers are 16-byte aligned
+  const DQ_GAS u32x4* s4 = gp((const u32x4*)src);
+  DQ_GAS u32x4* d4 = gp((u32x4*)dst);
+  int64_t k = tid;
+  for (; k + 3 * nthr < n16; k += 4 * nthr) {   // four loads in flight per thread
+    const u32x4 v0 = s4[k], v1 = s4[k + nthr], v2 = s4[k + 2 * nthr], v3 = s4[k + 3 * nthr];
+    d4[k] = v0;
+    d4[k + nthr] = v1;
+    d4[k + 2 * nthr] = v2;
+    d4[k + 3 * nthr] = v3;
+  }
+  for (; k < n16; k += nthr) d4[k] = s4[k];
+  for (int64_t b = 16 * n16 + tid; b < bytes; b += nthr) gp(dst)[b] = gp(src)[b];
+}
+
+__global__ __launch_bounds__(256) void k_outputs(const ProbDev* __restrict__ probs, int slot,
+                                                 int code_bits, int scale_bytes, int g,
+                                                 StateOut* __restrict__ out) {
+  const ProbDev& P = probs[blockIdx.y];
+  if (!P.st) return;
+  const State s = P.st[slot];
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
+  if (tid == 0) {
+    out[blockIdx.y].st = s;
+    out[blockIdx.y].flags = *gp(P.flags);
+  }
+  if (s.mode != MODE_DONE) return;
+  for (int64_t i = tid; i < P.rows; i += nthr) gp(P.r_out)[i] = gp(P.r[s.rs])[i];
+  for (int64_t j = tid; j < P.cols; j += nthr) gp(P.c_out)[j] = gp(P.c[s.cs])[j];
+  if (tid == 0 && P.ts_out) *gp(P.ts_out) = s.st_acc;
+  if (s.acc == 1) {
+    const int64_t n = P.rows * P.cols;
+    copy_bytes(P.codes[0], P.codes[1], n * code_bits / 8, tid, nthr);
+    copy_bytes((uint8_t*)P.scales[0], (const uint8_t*)P.scales[1], n / g * scale_bytes, tid, nthr);
+  }
 }
 
 // ---------------------------------------------------------------- standalone quantiser

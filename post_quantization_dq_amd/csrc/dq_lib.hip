@@ -116,7 +116,7 @@ struct Plan {
     size_t row_off, col_off, fin_off;  // offsets of the tables in the workspace
   };
   std::vector<Group> groups;
-  size_t probs_off = 0, total = 0;
+  size_t probs_off = 0, sout_off = 0, total = 0;   // [probs_off, sout_off): uploaded at once
   std::vector<size_t> prob_off;
 };
 
@@ -192,6 +192,8 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     G.fin_off = off;
     off = align_up(off + sizeof(WgEntry) * G.fin.size());
   }
+  pl.sout_off = off;
+  off = align_up(off + sizeof(StateOut) * std::max(1, (int)count));
   pl.total = off;
   return DQ_OK;
 }
@@ -228,6 +230,9 @@ void bind_pointers(const dq_problem* p, int32_t count, int g, int fmt, int iters
     d.c_trace = p[k].c_trace;
     d.r_init = p[k].r_init;
     d.c_init = p[k].c_init;
+    d.r_out = p[k].r;
+    d.c_out = p[k].c;
+    d.ts_out = fmt == DQ_FMT_NVFP4 ? p[k].tensor_scale : nullptr;
   }
 }
 
@@ -577,7 +582,7 @@ static int validate_solve(const dq_problem* p, int32_t count, dq_quant_spec spec
                           const dq_solve_opts* o, int* g_out) {
   if (o && o->pass_ms && o->pass_ms_capacity < 0) return DQ_ERR_ARG;
   if (!p || !o) return DQ_ERR_NULL;
-  if (count < 1) return DQ_ERR_ARG;
+  if (count < 1 || count > 65535) return DQ_ERR_ARG;   // problems index the grid's y dimension
   int g = resolve_group(spec);
   if (g < 0) return DQ_ERR_FORMAT;
   if (o->iters < 0 || !(o->tol_relchg >= 0.0f)) return DQ_ERR_ARG;
@@ -639,16 +644,16 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
     return DQ_OK;
   }
 
+  // the problem descriptors and every launch table, in one upload
   ProbDev* dprobs = (ProbDev*)(ws + pl.probs_off);
-  DQ_HIP(hipMemcpyAsync(dprobs, pl.dev.data(), sizeof(ProbDev) * count, hipMemcpyHostToDevice, s));
+  std::vector<char> up(pl.sout_off - pl.probs_off);
+  std::memcpy(up.data(), pl.dev.data(), sizeof(ProbDev) * count);
   for (auto& G : pl.groups) {
-    DQ_HIP(hipMemcpyAsync(ws + G.row_off, G.row.data(), sizeof(WgEntry) * G.row.size(),
-                          hipMemcpyHostToDevice, s));
-    DQ_HIP(hipMemcpyAsync(ws + G.col_off, G.col.data(), sizeof(WgEntry) * G.col.size(),
-                          hipMemcpyHostToDevice, s));
-    DQ_HIP(hipMemcpyAsync(ws + G.fin_off, G.fin.data(), sizeof(WgEntry) * G.fin.size(),
-                          hipMemcpyHostToDevice, s));
+    std::memcpy(up.data() + (G.row_off - pl.probs_off), G.row.data(), sizeof(WgEntry) * G.row.size());
+    std::memcpy(up.data() + (G.col_off - pl.probs_off), G.col.data(), sizeof(WgEntry) * G.col.size());
+    std::memcpy(up.data() + (G.fin_off - pl.probs_off), G.fin.data(), sizeof(WgEntry) * G.fin.size());
   }
+  DQ_HIP(hipMemcpyAsync(dprobs, up.data(), up.size(), hipMemcpyHostToDevice, s));
 
   int64_t maxdim = 1;
   int max_init = 1;
@@ -690,6 +695,18 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
   };
   std::vector<State> hst(count);
   std::vector<uint32_t> hflags(count, 0u);
+  std::vector<StateOut> hout(count);
+  StateOut* dout = (StateOut*)(ws + pl.sout_off);
+  // workgroups per problem of the outputs kernel: one 64-byte slice per thread of the
+  // largest code copy, at most 2048 per problem and about 64 K over the batch (a problem whose
+  // kept codes are already in the caller's buffer leaves its workgroups idle)
+  int64_t max_copy = 1;
+  for (int k = 0; k < count; ++k)
+    if (pl.group_of[k] >= 0)
+      max_copy = std::max<int64_t>(max_copy, (int64_t)code_bytes(spec.fmt, pl.dev[k].rows, pl.dev[k].cols));
+  const int64_t out_x = std::max<int64_t>(
+      1, std::min<int64_t>({(max_copy + 16383) / 16384, 2048, std::max<int64_t>(1, 65536 / count)}));
+  const dim3 out_grid((unsigned)out_x, (unsigned)count);
   int pending = 1 + iters;   // INIT sweep + one sweep per iteration, if nothing is rejected
   // at most one extra (re-solve) sweep per rejected iteration
   const int max_sweeps = 2 * iters + 2;
@@ -723,7 +740,16 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
         }
       }
     }
-    if (hipStreamSynchronize(s) != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
+    // states of all problems for the host; outputs of the finished ones
+    hipLaunchKernelGGL(k_outputs, out_grid, dim3(256), 0, s, dprobs, launched & 1,
+                       code_bits(spec.fmt), scale_bytes(spec.fmt), g, dout);
+    if (hipGetLastError() != hipSuccess ||
+        hipMemcpyAsync(hout.data(), dout, sizeof(StateOut) * count, hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess) {
+      cleanup();
+      return DQ_ERR_HIP;
+    }
     for (size_t k = ev0; k + 5 < ev.size(); k += 6) {
       for (int q = 0; q < 3; ++q) {
         float ms = 0.0f;
@@ -736,13 +762,8 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
     for (int k = 0; k < count; ++k) {
       if (pl.group_of[k] < 0) continue;
       // the decision of the last sweep launched wrote the slot of sweep `launched`
-      if (hipMemcpy(&hst[k], pl.dev[k].st + (launched & 1), sizeof(State),
-                    hipMemcpyDeviceToHost) != hipSuccess ||
-          hipMemcpy(&hflags[k], pl.dev[k].flags, sizeof(uint32_t), hipMemcpyDeviceToHost) !=
-              hipSuccess) {
-        cleanup();
-        return DQ_ERR_HIP;
-      }
+      hst[k] = hout[k].st;
+      hflags[k] = hout[k].flags;
       if (hst[k].mode == MODE_DONE) continue;
       int need = (iters - hst[k].it_done) + (hst[k].mode == MODE_FIXUP ? 1 : 0);
       pending = std::max(pending, need);
@@ -750,25 +771,8 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
   }
 
   cleanup();
-  // outputs: final scales, kept codes, tensor scale, reports
-  for (int k = 0; k < count; ++k) {
-    if (pl.group_of[k] < 0) continue;
-    const ProbDev& d = pl.dev[k];
-    const State& S = hst[k];
-    DQ_HIP(hipMemcpyAsync(problems[k].r, d.r[S.rs], sizeof(float) * d.rows, hipMemcpyDeviceToDevice, s));
-    DQ_HIP(hipMemcpyAsync(problems[k].c, d.c[S.cs], sizeof(float) * d.cols, hipMemcpyDeviceToDevice, s));
-    if (S.acc == 1) {
-      DQ_HIP(hipMemcpyAsync(d.codes[0], d.codes[1], code_bytes(spec.fmt, d.rows, d.cols),
-                            hipMemcpyDeviceToDevice, s));
-      DQ_HIP(hipMemcpyAsync(d.scales[0], d.scales[1],
-                            (size_t)d.rows * d.cols / g * scale_bytes(spec.fmt),
-                            hipMemcpyDeviceToDevice, s));
-    }
-    if (spec.fmt == DQ_FMT_NVFP4)
-      DQ_HIP(hipMemcpyAsync(problems[k].tensor_scale, &d.st[launched & 1].st_acc, sizeof(float),
-                            hipMemcpyDeviceToDevice, s));
-  }
-  DQ_HIP(hipStreamSynchronize(s));
+  // every problem is finished: k_outputs of the last round wrote the final scales, kept
+  // codes and tensor scale, and the stream has been synchronised
   for (int k = 0; k < count; ++k) {
     if (!problems[k].report) continue;
     if (pl.group_of[k] < 0) { *problems[k].report = dq_report{iters, 0, 0u, 0}; continue; }
