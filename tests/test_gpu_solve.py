@@ -253,3 +253,31 @@ def test_scale_step_ablation(oracle_lib, steps, name, rows, cols, iters):
     frozen = {1: ["c"], 2: ["r"]}[steps]
     for v in frozen:
         assert np.all(got[v] == 1.0), v
+
+
+def test_batch_across_rounds_of_sweeps():
+    """A batch whose members finish in different rounds of sweeps (INT4 rejections add
+    re-solve sweeps for some matrices only) plus an empty problem: every member equals its
+    own solve (codes, scales, r, c, histories, report), whichever code buffer its kept Qhat
+    ended in."""
+    base = synth.WORKLOADS["w256x512_int4"]["W"]
+    Ws = [synth.workload("w256x512_int4")[0],
+          synth.matrix(base.scaled(96, 512), 7),
+          synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["W"].scaled(130, 1024), 8)]
+    iters = 40
+    probs = [dq.make_problem(to_dev(W), "INT4", iters) for W in Ws]
+    probs.insert(1, dq.make_problem(torch.empty(0, 512, dtype=torch.float32, device=DEV), "INT4", iters))
+    reps = dq.solve_many(probs, "INT4", iters)
+    torch.cuda.synchronize()
+    assert reps[1].iters_run == iters and reps[1].rejected_steps == 0
+    solo = [_gpu_solve(W, "INT4", iters) for W in Ws]
+    print("[batch] rejected per member:", [one["rejected"] for one in solo],
+          "sweeps:", [one["sweeps"] for one in solo], flush=True)
+    assert max(one["rejected"] for one in solo) > 5
+    for p, rep, one in zip([probs[0]] + probs[2:], [reps[0]] + reps[2:], solo):
+        assert np.array_equal(p.codes.cpu().numpy(), one["codes"])
+        assert np.array_equal(p.block_scales.cpu().numpy().view(np.uint16), one["scales"].view(np.uint16))
+        assert np.array_equal(p.r.cpu().numpy(), one["r"]) and np.array_equal(p.c.cpu().numpy(), one["c"])
+        assert np.array_equal(p.nmse_hist.cpu().numpy(), one["nmse"])
+        assert rep.rejected_steps == one["rejected"] and rep.iters_run == one["iters_run"]
+        assert rep.sweeps == one["sweeps"]
