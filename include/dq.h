@@ -218,8 +218,8 @@ int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t token
  * dequantised with its block scale (and, for NVFP4, its tensor scale).  With
  * W ~ diag(r) Q diag(c) this is Y ~ X W^T.
  *   spec       DQ_FMT_MXFP4, DQ_FMT_MXFP6_E2M3/E3M2, DQ_FMT_MXFP8_E4M3/E5M2 (group 32) on
- *              the block-scaled cores, or DQ_FMT_NVFP4 (group 16) on the bf16 cores: its
- *              elements e2m1 * e4m3 are exact in bf16 and the tensor scales multiply the
+ *              the block-scaled cores, or DQ_FMT_NVFP4 (group 16) on the f16 cores: its
+ *              elements e2m1 * e4m3 are exact in fp16 and the tensor scales multiply the
  *              fp32 result.  The same format for both operands (MXINT4: see
  *              dq_recode_mxint4_to_mxfp6).
  *   a_codes    [M][K] activation codes in the format's layout (row pitch K*bits/8 bytes),
@@ -231,7 +231,7 @@ int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t token
  *   y          [M][ldy] output, fp32 (y_dtype DQ_F32) or bf16 (DQ_BF16, round to nearest
  *              even); ldy >= N.
  * Accumulation is fp32 in the matrix cores.  For E2M1 and E2M3 elements every product and
- * partial sum of one instruction is exact, so only the fp32 accumulation rounds; the bf16
+ * partial sum of one instruction is exact, so only the fp32 accumulation rounds; the f16
  * products of NVFP4 are exact too, but its tensor scales are applied once to the sum (the
  * per-element dequantisation rounds e4m3 * s_t instead).  For E4M3, E5M2 and E3M2 the cores'
  * internal sum keeps fewer bits than fp32 (measured: about 2^-12 of sum |a b| over

@@ -251,6 +251,12 @@ void launch_timed(K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s, 
   t_ev_stop = nullptr;
 }
 
+// Dynamic-LDS limit of a kernel that takes more than the default 64 KiB, set before each
+// launch (on the current device; a cached flag would miss a second device).
+bool lds_limit(const void* kernel, int bytes) {
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess;
+}
+
 #define DQ_HIP(call)                                   \
   do {                                                 \
     if ((call) != hipSuccess) return DQ_ERR_HIP;       \
@@ -477,18 +483,12 @@ template <int FMT, int OB>
 int launch_linear(dim3 grid, hipStream_t s, const LinArgs& p) {
   if constexpr (elem_bits<FMT>() != 6) {
     if (p.K % DmaGeom<FMT>::KS == 0 && ((uintptr_t)p.as & 3u) == 0 && ((uintptr_t)p.bs & 3u) == 0) {
-      static const bool ready_dma =
-          hipFuncSetAttribute((const void*)k_linear_dma<FMT, OB>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, DmaGeom<FMT>::LDS) == hipSuccess;
-      if (!ready_dma) return DQ_ERR_HIP;
+      if (!lds_limit((const void*)k_linear_dma<FMT, OB>, DmaGeom<FMT>::LDS)) return DQ_ERR_HIP;
       hipLaunchKernelGGL((k_linear_dma<FMT, OB>), grid, dim3(256), DmaGeom<FMT>::LDS, s, p);
       return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
     }
   }
-  static const bool ready =
-      hipFuncSetAttribute((const void*)k_linear<FMT, OB>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          LinGeom<FMT>::LDS) == hipSuccess;
-  if (!ready) return DQ_ERR_HIP;
+  if (!lds_limit((const void*)k_linear<FMT, OB>, LinGeom<FMT>::LDS)) return DQ_ERR_HIP;
   hipLaunchKernelGGL((k_linear<FMT, OB>), grid, dim3(256), LinGeom<FMT>::LDS, s, p);
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
@@ -524,10 +524,7 @@ int launch_quant_multi_t(const void* X, int64_t rows, int64_t cols, int64_t ld,
   const size_t c_bytes = (size_t)mo.count * cols * sizeof(float);
   const int c_lds = c_bytes <= kMultiCLds ? 1 : 0;
   if (c_lds && c_bytes > 64 * 1024) {
-    static const bool ready = hipFuncSetAttribute((const void*)k_quant_multi<FMT, DT, L>,
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  (int)kMultiCLds) == hipSuccess;
-    if (!ready) return DQ_ERR_HIP;
+    if (!lds_limit((const void*)k_quant_multi<FMT, DT, L>, (int)kMultiCLds)) return DQ_ERR_HIP;
   }
   hipLaunchKernelGGL((k_quant_multi<FMT, DT, L>), dim3(grid), dim3(lpr * H), c_lds ? c_bytes : 0, s,
                      X, rows, cols, ld, mo, part, nparts, lpr, H, c_lds);

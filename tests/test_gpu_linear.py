@@ -190,7 +190,7 @@ def test_mxint4_linear(oracle_lib, shape):
     assert np.all(np.abs(y - ref) <= _tol("MXFP6_E2M3", K, absy.reshape(M, N), ref, torch.float32))
 
 
-# ---- NVFP4 on the bf16 matrix cores.  Every element e2m1 * e4m3 is exact in bf16, so the
+# ---- NVFP4 on the f16 matrix cores.  Every element e2m1 * e4m3 is exact in fp16, so the
 # products are exact and only fp32 sums round: the instructions' internal sums of 32 and the
 # accumulation over K/32 of them (bound (K/32 + 2) 2^-24 + 2^-21 of sum |a b|, the last
 # term leaving room for an internal sum kept in fewer bits), then the tensor-scale product,
