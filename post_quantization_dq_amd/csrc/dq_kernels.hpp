@@ -192,8 +192,12 @@ __global__ __launch_bounds__(256) void k_init(const ProbDev* __restrict__ probs)
   const int64_t nv = n / VEC;
   const int64_t rowbytes = P.ld * (DT == 1 ? 2 : 4);
   const DQ_GAS f32x4* ic4 = gp((const f32x4*)P.ic[0]);
+  // with the default initial column scales (all 1) and a row scale of 1, (w * ir) * ic is w
+  // exactly, so the NVFP4 amax needs no multiplies
+  const bool unit_c = P.c_init == nullptr;
   for (int64_t i = r0; i < r1; ++i) {
     const float ir = gp(P.ir[0])[i];
+    const bool unit = unit_c && ir == 1.0f;
     const DQ_GAS u32x4* rowp = gp((const u32x4*)((const char*)P.W + i * rowbytes));
     for (int64_t v0 = threadIdx.x; v0 < nv; v0 += (int64_t)blockDim.x * U) {
       u32x4 u[U];
@@ -216,19 +220,37 @@ __global__ __launch_bounds__(256) void k_init(const ProbDev* __restrict__ probs)
 #pragma unroll
           for (int k = 0; k < 4; ++k) w[k] = u2f(uu[k]);
         }
-        float icv[VEC];
-        if (FMT == NVFP4) {
+        // sum of squares: a bf16 square is exact in fp32 and eight of them are summed with
+        // a relative error below 2^-21 before the fp64 accumulation; an fp32 input's four
+        // squares round once each.  A partial that is not finite (a NaN or Inf element, or a
+        // square beyond the fp32 range) or below 2^-100 (where squares may underflow) is
+        // redone element by element in fp64.
+        float p2 = 0.0f;
 #pragma unroll
-          for (int k = 0; k < VEC / 4; ++k) {
-            const f32x4 a = ic4[v * (VEC / 4) + k];
-            icv[4 * k] = a.x; icv[4 * k + 1] = a.y; icv[4 * k + 2] = a.z; icv[4 * k + 3] = a.w;
+        for (int k = 0; k < VEC; ++k) p2 = fmaf(w[k], w[k], p2);
+        if (isfinite(p2) && p2 >= 0x1p-100f) {
+          s2 += (double)p2;
+        } else {
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) {
+            bad |= !isfinite(w[k]);
+            s2 += (double)w[k] * (double)w[k];
           }
         }
+        if (FMT == NVFP4) {
+          if (unit) {
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-          bad |= !isfinite(w[k]);
-          s2 += (double)w[k] * (double)w[k];
-          if (FMT == NVFP4) amax = fmaxf(amax, fabsf((w[k] * ir) * icv[k]));
+            for (int k = 0; k < VEC; ++k) amax = fmaxf(amax, fabsf(w[k]));
+          } else {
+            float icv[VEC];
+#pragma unroll
+            for (int k = 0; k < VEC / 4; ++k) {
+              const f32x4 a = ic4[v * (VEC / 4) + k];
+              icv[4 * k] = a.x; icv[4 * k + 1] = a.y; icv[4 * k + 2] = a.z; icv[4 * k + 3] = a.w;
+            }
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) amax = fmaxf(amax, fabsf((w[k] * ir) * icv[k]));
+          }
         }
       }
     }
