@@ -206,7 +206,7 @@ def bench_linear(args, fmt):
         "config": {"workload": f"q_proj-shaped {N}x{K} weight solved to {fmt} (T={T}); {M} tokens of "
                                f"activations rescaled by the solved c and quantised to {fmt}; bf16 output",
                    "M": M, "N": N, "K": K},
-        "roofline": {"bound": "mfma", "kernel": "k_linear_nv" if nv else "k_linear_dma",
+        "roofline": {"bound": "mfma", "kernel": "k_linear_nv_dma" if nv else "k_linear_dma",
                      "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": None,
                      "alg_flops_per_launch": flops, "avg_launch_ms": round(ms, 4),

@@ -495,6 +495,12 @@ int launch_linear(dim3 grid, hipStream_t s, const LinArgs& p) {
 
 template <int OB>
 int launch_linear_nv(dim3 grid, hipStream_t s, const LinArgs& p) {
+  // codes through LDS where K is a multiple of the 128-K stage and the scale arrays allow
+  // 4-byte loads; otherwise dequantised into LDS (any K that is a multiple of 32)
+  if (p.K % NvDmaGeom::KS == 0 && ((uintptr_t)p.as & 3u) == 0 && ((uintptr_t)p.bs & 3u) == 0) {
+    hipLaunchKernelGGL((k_linear_nv_dma<OB>), grid, dim3(256), NvDmaGeom::LDS, s, p);   // 54 KiB
+    return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+  }
   hipLaunchKernelGGL((k_linear_nv<OB>), grid, dim3(256), NvGeom::LDS, s, p);   // 64 KiB
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }

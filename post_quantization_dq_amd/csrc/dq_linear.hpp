@@ -633,6 +633,149 @@ __global__ __launch_bounds__(256) void k_linear_nv(LinArgs p) {
   lin_store<OUT_BF16>(acc, p, mt0 + wm, nt0 + wn, gp(p.ats)[0] * gp(p.bts)[0]);
 }
 
+// ---------------------------------------------------------------- NVFP4, codes through LDS
+// The same layer with the raw codes and scales moved into LDS by the direct-to-LDS ring and
+// dequantised in registers right before the products (LDS carries 4-bit codes, not f16
+// values, and no wave stores to LDS).  A stage is 128 K: 64 bytes of codes and 8 scale
+// bytes per tile row.  Within a stage lane group g takes blocks 2g and 2g + 1 (16
+// contiguous bytes: one read per row fragment): K-step u of the instruction gets block
+// 2g + u / 2, half u % 2.  Activations and weights use the same order, so the four
+// K-steps sum the stage's 128 products of every output.  Rows of 64 bytes span 16 banks,
+// so the chunk index is XOR-ed with (r >> 2) & 3 to give a fragment read's 16 rows
+// distinct banks.
+struct NvDmaGeom {
+  static constexpr int KS = 128;
+  static constexpr int ROWB = KS / 2;                    // 64 bytes of codes per row
+  static constexpr int CPR = ROWB / 16;                  // 4 chunks
+  static constexpr int RPI = 64 / CPR;                   // 16 rows per wave instruction
+  static constexpr int SPR = KS / 16;                    // 8 scale bytes per row
+  static constexpr int TILE = kLinTile * ROWB;           // 8 KiB
+  static constexpr int STILE = kLinTile * SPR;           // 1 KiB
+  static constexpr int STAGE = 2 * TILE + 2 * STILE;
+  static constexpr int D = 3;                            // ring depth
+  static constexpr int LDS = D * STAGE;                  // 54 KiB
+  static constexpr int CODE_INSTS = kLinTile / RPI / 4;  // 2 per wave per operand
+  static constexpr int SC_INSTS = 2 * kLinTile * SPR / 4 / 64 / 4;   // 2 per wave
+  static constexpr int INSTS = 2 * CODE_INSTS + SC_INSTS;
+};
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void nv_dma_stage(const LinArgs& p, int64_t mt0, int64_t nt0,
+                                             int64_t st, uint8_t* buf) {
+  using G = NvDmaGeom;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rowbytes = p.K / 2, nblk = p.K / 16;
+#pragma unroll
+  for (int op = 0; op < 2; ++op) {
+    const uint8_t* codes = op ? p.b : p.a;
+    const int64_t r0 = op ? nt0 : mt0, rows = op ? p.N : p.M;
+    uint8_t* tile = buf + op * G::TILE;
+#pragma unroll
+    for (int ii = 0; ii < G::CODE_INSTS; ++ii) {
+      const int rbase = (wave * G::CODE_INSTS + ii) * G::RPI;
+      const int r = rbase + lane / G::CPR, c = lane % G::CPR;
+      int64_t row = r0 + r;
+      row = row < rows ? row : rows - 1;
+      const uint8_t* src = codes + row * rowbytes + st * G::ROWB + 16 * (c ^ swz64(r));
+      __builtin_amdgcn_global_load_lds((const DQ_GAS void*)src,
+                                       (__attribute__((address_space(3))) void*)(tile + rbase * G::ROWB),
+                                       16, 0, 0);
+    }
+  }
+  // scales: each operand's [128][8] bytes as four pieces of 64 dwords; dword d of an
+  // operand holds bytes 4 (d % 2) .. +3 of row d / 2
+#pragma unroll
+  for (int j = 0; j < G::SC_INSTS; ++j) {
+    const int q = wave * G::SC_INSTS + j;               // 0 .. 7
+    const int op = q / 4, part = q % 4;
+    const int d = 64 * part + lane, r = d / 2, word = d % 2;
+    const uint8_t* scales = op ? p.bs : p.as;
+    const int64_t r0 = op ? nt0 : mt0, rows = op ? p.N : p.M;
+    int64_t row = r0 + r;
+    row = row < rows ? row : rows - 1;
+    const uint8_t* src = scales + row * nblk + st * G::SPR + 4 * word;
+    uint8_t* stile = buf + 2 * G::TILE + op * G::STILE + 256 * part;
+    __builtin_amdgcn_global_load_lds((const DQ_GAS void*)src,
+                                     (__attribute__((address_space(3))) void*)stile, 4, 0, 0);
+  }
+}
+
+// Row fragment of one operand for the stage: 16 bytes of codes (blocks 2g, 2g + 1 of the
+// stage) and their two E4M3 scales as f16 (sign bits cleared, as in k_linear_nv).
+struct NvFrag {
+  u32x4 q;
+  f16x2 s;
+};
+__device__ __forceinline__ NvFrag nv_frag(const uint8_t* tile, const uint8_t* stile, int r, int g) {
+  NvFrag f;
+  f.q = *(const u32x4*)(tile + r * NvDmaGeom::ROWB + 16 * (g ^ swz64(r)));
+  const uint32_t sb = *(const uint16_t*)(stile + r * NvDmaGeom::SPR + 2 * g);
+  f.s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb & 0x7F7Fu, 1.0f, false);
+  return f;
+}
+// The eight f16 of K-step u: word u of the codes times the scale of block u / 2.
+__device__ __forceinline__ f16x8 nv_expand(const NvFrag& f, int u) {
+  const uint32_t w = u == 0 ? f.q.x : (u == 1 ? f.q.y : (u == 2 ? f.q.z : f.q.w));
+  const _Float16 sv = (u < 2) ? f.s.x : f.s.y;
+  uint32_t h[4];
+  fp4_f16_scaled8(w, f16x2{sv, sv}, h);
+  f16x8 v;
+  __builtin_memcpy(&v, h, 16);
+  return v;
+}
+
+template <int OUT_BF16>
+__global__ __launch_bounds__(256) void k_linear_nv_dma(LinArgs p) {
+  using G = NvDmaGeom;
+  extern __shared__ __align__(16) uint8_t lin_lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int tm, tn;
+  lin_tile(p.tiles_m * p.tiles_n, p.tiles_m, tm, tn);
+  const int64_t mt0 = (int64_t)tm * kLinTile, nt0 = (int64_t)tn * kLinTile;
+  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int g = lane >> 4, r16 = lane & 15;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t nst = p.K / G::KS;
+  for (int64_t s = 0; s < G::D - 1 && s < nst; ++s) nv_dma_stage(p, mt0, nt0, s, lin_lds + s * G::STAGE);
+  for (int64_t st = 0; st < nst; ++st) {
+    const int64_t later = min((int64_t)(G::D - 2), nst - 1 - st);
+    wait_vmcnt((int)(later * G::INSTS));
+    // bare barrier, as in k_linear_dma: this stage has landed for every wave, and the
+    // buffer refilled next was last read before it
+    asm volatile("s_barrier" ::: "memory");
+    if (st + G::D - 1 < nst)
+      nv_dma_stage(p, mt0, nt0, st + G::D - 1, lin_lds + ((st + G::D - 1) % G::D) * G::STAGE);
+    const uint8_t* cur = lin_lds + (st % G::D) * G::STAGE;
+    NvFrag fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[i] = nv_frag(cur, cur + 2 * G::TILE, wm + 16 * i + r16, g);
+      fb[i] = nv_frag(cur + G::TILE, cur + 2 * G::TILE + G::STILE, wn + 16 * i + r16, g);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f16x8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = nv_expand(fa[i], u);
+        b[i] = nv_expand(fb[i], u);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+  }
+  lin_store<OUT_BF16>(acc, p, mt0 + wm, nt0 + wn, gp(p.ats)[0] * gp(p.bts)[0]);
+}
+
 // ---------------------------------------------------------------- MXINT4 -> MXFP6 E2M3
 // The matrix cores take no integer elements under E8M0 scales, but every MXINT4 element
 // q * 2^(e-2) (q in [-7, 7]) is exactly an E2M3 value times an E8M0 scale: q itself under
