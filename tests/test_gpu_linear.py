@@ -311,3 +311,28 @@ def test_output_row_pitch(oracle_lib, fmt, out_dtype):
     torch.cuda.synchronize()
     assert torch.equal(view, y0)
     assert torch.all(wide[:, N:] == -7.0)
+
+
+def test_nvfp4_both_kernels(oracle_lib):
+    """K = 1024 with 4-byte-aligned scales takes the kernel that dequantises in registers;
+    the same scales at an odd address take the one that dequantises into LDS.  They sum K
+    in different orders, so each is checked against the oracle (not bitwise against the
+    other)."""
+    M, N, K = 160, 200, 1024
+    a, asc, b, bsc, r, ats, bts = _nv_inputs(M, N, K, 41)
+    dev = lambda x: torch.from_numpy(x).to(DEV)
+    A, B = dev(a), dev(b)
+    pad_a = torch.zeros(asc.size + 16, dtype=torch.uint8, device=DEV)
+    pad_b = torch.zeros(bsc.size + 16, dtype=torch.uint8, device=DEV)
+    pad_a[1:1 + asc.size] = dev(asc)
+    pad_b[1:1 + bsc.size] = dev(bsc)
+    ts = dict(a_tensor_scale=to_dev(np.array([ats])), b_tensor_scale=to_dev(np.array([bts])))
+    ref = oracle_lib.quantized_linear(a, asc, M, b, bsc, N, K, "NVFP4", r=r, a_ts=ats, b_ts=bts)
+    mi, ni = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    _, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, "NVFP4", mi.ravel(),
+                                                  ni.ravel(), r=r, a_ts=ats, b_ts=bts)
+    tol = _nv_tol(K, absy.reshape(M, N), ref, torch.float32)
+    for sa, sb in ((dev(asc), dev(bsc)), (pad_a[1:1 + asc.size], pad_b[1:1 + bsc.size])):
+        y = dq.quantized_linear(A, sa, B, sb, M, N, K, "NVFP4", r=to_dev(r), **ts)
+        torch.cuda.synchronize()
+        assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - ref) <= tol)
