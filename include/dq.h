@@ -235,8 +235,10 @@ int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t token
  * products of NVFP4 are exact too, but its tensor scales are applied once to the sum (the
  * per-element dequantisation rounds e4m3 * s_t instead).  For E4M3, E5M2 and E3M2 the cores'
  * internal sum keeps fewer bits than fp32 (measured: about 2^-12 of sum |a b| over
- * 128-element random-code dot products).  Returns DQ_ERR_FORMAT for other formats,
- * DQ_ERR_SHAPE for bad sizes, DQ_ERR_ALIGN for misaligned codes or output.  Asynchronous. */
+ * 128-element random-code dot products).  Fastest with 4-byte-aligned scale arrays and K
+ * a multiple of 256 (FP4), 128 (FP8, NVFP4); other inputs take a register-staged kernel.
+ * Returns DQ_ERR_FORMAT for other formats, DQ_ERR_SHAPE for bad sizes, DQ_ERR_ALIGN for
+ * misaligned codes or output.  Asynchronous. */
 int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_t* a_scales,
                         const float* a_tensor_scale, int64_t M, const uint8_t* b_codes,
                         const uint8_t* b_scales, const float* b_tensor_scale, int64_t N,
