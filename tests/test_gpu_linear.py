@@ -336,3 +336,32 @@ def test_nvfp4_both_kernels(oracle_lib):
         y = dq.quantized_linear(A, sa, B, sb, M, N, K, "NVFP4", r=to_dev(r), **ts)
         torch.cuda.synchronize()
         assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - ref) <= tol)
+
+
+@pytest.mark.parametrize("fmt", ["MXFP4", "NVFP4"])
+def test_output_offsets_beyond_2_31(oracle_lib, fmt):
+    """A 32768 x 65552 bf16 output (element offsets past 2^31; N not a multiple of the tile)
+    with K = 256: entries sampled across it, including the last rows and columns, against
+    the oracle."""
+    M, N, K = 32768, 65552, 256
+    print(f"[linear] {fmt} {M}x{N}x{K} (4.3 GB output)", flush=True)
+    rng = np.random.default_rng(51)
+    if fmt == "NVFP4":
+        a, asc, b, bsc, r, ats, bts = _nv_inputs(M, N, K, 51)
+        ts = dict(a_tensor_scale=to_dev(np.array([ats])), b_tensor_scale=to_dev(np.array([bts])))
+        kw = dict(a_ts=ats, b_ts=bts)
+    else:
+        a, asc, b, bsc, r = _inputs(fmt, M, N, K, 51)
+        ts, kw = {}, {}
+    dev = lambda x: torch.from_numpy(x).to(DEV)
+    y = dq.quantized_linear(dev(a), dev(asc), dev(b), dev(bsc), M, N, K, fmt, r=to_dev(r),
+                            out_dtype=torch.bfloat16, **ts)
+    mi, ni = rng.integers(0, M, 400), rng.integers(0, N, 400)
+    mi[:6], ni[:6] = [M - 1, M - 1, M - 1, 0, M // 2, M - 2], [N - 1, 0, N - 17, N - 1, N - 1, N - 2]
+    assert int(mi.max()) * N + int(ni.max()) > 2 ** 31
+    got = y[torch.from_numpy(mi).to(DEV), torch.from_numpy(ni).to(DEV)].float().cpu().numpy().astype(np.float64)
+    del y
+    torch.cuda.synchronize()
+    ref, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, fmt, mi, ni, r=r, **kw)
+    tol = (_nv_tol if fmt == "NVFP4" else (lambda K_, ab, yy, od: _tol(fmt, K_, ab, yy, od)))(K, absy, ref, torch.bfloat16)
+    assert np.all(np.abs(got - ref) <= tol)
