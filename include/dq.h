@@ -21,7 +21,9 @@
  *   - Matrices are row-major; `ld` is the row pitch in elements (ld >= cols).  Blocks of
  *     `group` consecutive elements run along a row.  Base pointers and the row pitch in
  *     bytes must be multiples of 16.  cols must be a multiple of the group and at most
- *     16384.
+ *     65536 (the solver's row pass keeps the column scales in LDS while 8 bytes per column
+ *     fit a workgroup's LDS, always up to 16384 columns, and reads them from L2 beyond; the
+ *     quantisers cover wider rows in several passes of 16384 columns).
  *   - Codes of the 4-bit formats: two per byte, low nibble = even column, [rows][cols/2].
  *     INT4 and MXINT4 codes are two's complement; MXFP4/NVFP4 codes are E2M1
  *     sign-magnitude (the sign of a negative value that rounds to zero is kept: code 0x8).
@@ -56,7 +58,7 @@ extern "C" {
 enum {
   DQ_OK = 0,
   DQ_ERR_NULL = -1,       /* a required pointer is NULL */
-  DQ_ERR_SHAPE = -2,      /* bad rows/cols/ld, cols not a multiple of the group, cols > 16384 */
+  DQ_ERR_SHAPE = -2,      /* bad rows/cols/ld, cols not a multiple of the group, cols > 65536 */
   DQ_ERR_ALIGN = -3,      /* base pointer or row pitch not 16-byte aligned */
   DQ_ERR_FORMAT = -4,     /* unknown format, group or dtype */
   DQ_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required */

@@ -354,6 +354,21 @@ __device__ __forceinline__ void lds_load16(const f32x4* base, int nch, int ch, f
   }
 }
 
+// 16 consecutive floats (vector loads when the base is 16-byte aligned).
+__device__ __forceinline__ void load16_global(const float* p, bool aligned, float (&x)[16]) {
+  if (aligned) {
+    const DQ_GAS f32x4* q = gp((const f32x4*)p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 a = q[k];
+      x[4 * k] = a.x; x[4 * k + 1] = a.y; x[4 * k + 2] = a.z; x[4 * k + 3] = a.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) x[k] = gp(p)[k];
+  }
+}
+
 // Which iteration a pass belongs to, read from the problem's state at kernel entry.
 struct PassInfo {
   int mode, it, rs, cs, acc, cb, tr;
@@ -373,7 +388,9 @@ struct PassInfo {
 };
 
 // ---------------------------------------------------------------- row pass
-template <int FMT, int DT, int L>
+// CG = 1 (matrices wider than the LDS holds): c and 1/c are read from global memory (they
+// stay in L2) instead of LDS.
+template <int FMT, int DT, int L, int CG>
 __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ probs,
                                                   const WgEntry* __restrict__ table, int sw) {
   const WgEntry we = table[blockIdx.x];
@@ -389,7 +406,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
   extern __shared__ float lds[];
   f32x4* s_c4 = (f32x4*)lds;           // c, chunk-interleaved (see lds_load16)
   f32x4* s_ic4 = s_c4 + 4 * nch;       // 1/c, same layout
-  NvTab* tab_c = (NvTab*)(lds + 2 * n);
+  NvTab* tab_c = (NvTab*)(CG ? lds : lds + 2 * n);
   NvTab* tab_p = tab_c + 1;
   __shared__ double redw[16][4];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, nw = (int)(blockDim.x >> 6);
@@ -420,10 +437,12 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
     }
   }
 
+  const float* cglob = P.c[pi.cs];
+  const float* icglob = P.ic[pi.cs];
   {
-    const DQ_GAS f32x4* c4 = gp((const f32x4*)P.c[pi.cs]);
-    const DQ_GAS f32x4* ic4 = gp((const f32x4*)P.ic[pi.cs]);
-    for (int e = threadIdx.x; e < 4 * nch; e += blockDim.x) {
+    const DQ_GAS f32x4* c4 = gp((const f32x4*)cglob);
+    const DQ_GAS f32x4* ic4 = gp((const f32x4*)icglob);
+    for (int e = threadIdx.x; !CG && e < 4 * nch; e += blockDim.x) {
       const int ch = e >> 2, q = e & 3;
       s_c4[q * nch + ch] = c4[e];
       s_ic4[q * nch + ch] = ic4[e];
@@ -460,7 +479,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
     for (int kk = 0; kk < nloop; ++kk) {
       const int chn = lane + 64 * kk;
       const bool valid = chn < nch;
-      const int cl = valid ? chn : 0;   // LDS reads stay in range; invalid lanes work on zeros
+      const int cl = valid ? chn : 0;   // c reads stay in range; invalid lanes work on zeros
       const int j0 = 16 * chn;
       RawRow<DT> raw;
       if (valid) raw.load(P.W, i, P.ld, j0); else raw.zero();
@@ -477,7 +496,8 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         float v[16];
         {
           float icc[16];
-          lds_load16(s_ic4, nch, cl, icc);
+          if (CG) load16_global(icglob + 16 * (int64_t)cl, true, icc);
+          else lds_load16(s_ic4, nch, cl, icc);
 #pragma unroll
           for (int k = 0; k < 16; ++k) v[k] = (w[k] * ir_) * icc[k];
         }
@@ -488,7 +508,8 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         f = ch.f;
 #pragma unroll
         for (int k = 0; k < 16; ++k) p[k] = ch.p[k];
-        lds_load16(s_c4, nch, cl, cc);
+        if (CG) load16_global(cglob + 16 * (int64_t)cl, true, cc);
+        else lds_load16(s_c4, nch, cl, cc);
         const float rf = r_ * f;
         float Fl = 0.0f, ql = 0.0f;
 #pragma unroll
@@ -531,7 +552,8 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
       } else {
         decode_grid<FMT>(pk, p);
         f = block_factor<FMT>(ps, tab_p);
-        lds_load16(s_c4, nch, cl, cc);
+        if (CG) load16_global(cglob + 16 * (int64_t)cl, true, cc);
+        else lds_load16(s_c4, nch, cl, cc);
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const float pc = p[k] * cc[k];
@@ -1010,23 +1032,9 @@ __global__ __launch_bounds__(256) void k_qamax(const void* __restrict__ X, int64
   if (threadIdx.x == 0) gp(part)[blockIdx.x] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
 }
 
-// 16 consecutive floats (vector loads when the base is 16-byte aligned).
-__device__ __forceinline__ void load16_global(const float* p, bool aligned, float (&x)[16]) {
-  if (aligned) {
-    const DQ_GAS f32x4* q = gp((const f32x4*)p);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const f32x4 a = q[k];
-      x[4 * k] = a.x; x[4 * k + 1] = a.y; x[4 * k + 2] = a.z; x[4 * k + 3] = a.w;
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) x[k] = gp(p)[k];
-  }
-}
-
 // Pass 2: quantise; workgroup = H row slots x LPR lanes, one chunk per lane, looping over
-// row groups so the tensor-scale table is built once per workgroup.
+// row groups so the tensor-scale table is built once per workgroup.  A launch covers chunks
+// lbeg .. lbeg + LPR - 1 of every row (rows wider than 1024 chunks take several launches).
 template <int FMT, int DT, int L, int MODEV>
 __global__ __launch_bounds__(1024) void k_quant(const void* __restrict__ X, int64_t rows,
                                                 int64_t cols, int64_t ld,
@@ -1034,7 +1042,7 @@ __global__ __launch_bounds__(1024) void k_quant(const void* __restrict__ X, int6
                                                 const float* __restrict__ c, uint8_t* codes,
                                                 void* scales, float* tensor_scale,
                                                 const float* __restrict__ part, int nparts,
-                                                int lpr, int H) {
+                                                int lpr, int H, int lbeg) {
   __shared__ NvTab tab;
   __shared__ float sA;
   QCtx qc;
@@ -1062,7 +1070,7 @@ __global__ __launch_bounds__(1024) void k_quant(const void* __restrict__ X, int6
     __syncthreads();
   }
   const int t = threadIdx.x;
-  const int h = t / lpr, l = t - h * lpr;
+  const int h = t / lpr, l = lbeg + (t - h * lpr);   // this lane's chunk of the row
   const bool lane_ok = l < (int)(cols >> 4);
   const int j0 = lane_ok ? l * 16 : 0;
   float cv[16];   // c (or its reciprocal for weights) of this lane's columns, for every row
@@ -1197,7 +1205,7 @@ template <int FMT, int DT, int L>
 __global__ __launch_bounds__(1024) void k_quant_multi(const void* __restrict__ X, int64_t rows,
                                                       int64_t cols, int64_t ld, MultiOut mo,
                                                       const float* __restrict__ part, int nparts,
-                                                      int lpr, int H, int c_lds) {
+                                                      int lpr, int H, int c_lds, int lbeg) {
   __shared__ NvTab tabs[kMaxMulti];
   __shared__ float sk6[kMaxMulti];
   extern __shared__ f32x4 cq[];
@@ -1251,8 +1259,8 @@ __global__ __launch_bounds__(1024) void k_quant_multi(const void* __restrict__ X
     __syncthreads();
   }
   const int t = threadIdx.x;
-  const int h = t / lpr, l = t - h * lpr;
-  const bool lane_ok = l < (int)(cols >> 4);
+  const int h = t / lpr, l = lbeg + (t - h * lpr);   // this lane's chunk of the row
+  const bool lane_ok = l < nch;
   const int j0 = lane_ok ? l * 16 : 0;
   for (int64_t i = (int64_t)blockIdx.x * H + h; i - h < rows; i += (int64_t)gridDim.x * H) {
     const bool act = lane_ok && i < rows;

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <map>
 #include <vector>
@@ -18,7 +19,7 @@ using namespace dqk;
 
 namespace {
 
-constexpr int kMaxCols = 16384;
+constexpr int kMaxCols = 65536;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -84,10 +85,10 @@ int check_matrix(const void* X, int32_t dt, int64_t rows, int64_t cols, int64_t 
   return DQ_OK;
 }
 
-// Row pass: workgroups of 16 waves, one wave per row; enough rows per wave that a single
-// large matrix gives about one workgroup per CU.
+// Row pass: workgroups of 16 waves, one wave per row, one workgroup per CU (all registers).
 constexpr int kRowWaves = 16;
-constexpr int kTargetRowWaves = 256 * kRowWaves;
+constexpr int kRowWgs = 256;
+constexpr int kTargetRowWaves = kRowWgs * kRowWaves;
 // Column pass: workgroups of 8 waves on a 1024-column strip and a range of rows; about
 // four per CU, so each CU has several workgroups' loads in flight (one per CU left the
 // HBM reads latency-bound: 34 us instead of 29.5 us on a 4096 x 14336 weight).
@@ -98,11 +99,36 @@ constexpr int64_t kMaxRowRanges = 64;
 // short; a single projection-sized matrix stays below both.
 constexpr int64_t kMaxRowsPerBlk = 256;
 constexpr int64_t kMaxRowsPerRange = 512;
-// Standalone quantiser geometry: one chunk per lane, up to 1024 threads.
-int lanes_per_row(int64_t cols) { return (int)std::max<int64_t>(64, (cols / 16 + 63) / 64 * 64); }
+// Standalone quantiser geometry: one chunk per lane, up to 1024 threads; rows wider than
+// 16384 columns take several passes of 1024 chunks.
+int lanes_per_row(int64_t cols) {
+  return (int)std::min<int64_t>(1024, std::max<int64_t>(64, (cols / 16 + 63) / 64 * 64));
+}
 int row_slots(int lpr) { return std::max(1, 1024 / lpr); }
+// LDS one workgroup may take on the current device (160 KiB on gfx950), read once per device.
+int device_lds_limit() {
+  static std::atomic<int> cache[64];   // 0: not read yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        v <= 0)
+      v = -1;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return std::max(v, 0);
+}
+// The row pass keeps c and 1/c in LDS (8 bytes per column) when they fit, always up to
+// 16384 columns, and reads them from global memory (L2-resident) beyond.
+constexpr int64_t kRowPassLdsCols = 16384;
+size_t rowpass_tabs(int fmt) { return fmt == DQ_FMT_NVFP4 ? 2 * sizeof(NvTab) : 0; }
+bool rowpass_cg(int fmt, int64_t cols) {
+  if (cols <= kRowPassLdsCols) return false;
+  return 2 * sizeof(float) * (size_t)cols + rowpass_tabs(fmt) > (size_t)device_lds_limit();
+}
 size_t rowpass_lds(int fmt, int64_t cols) {
-  return 2 * sizeof(float) * (size_t)cols + (fmt == DQ_FMT_NVFP4 ? 2 * sizeof(NvTab) : 0);
+  return (rowpass_cg(fmt, cols) ? 0 : 2 * sizeof(float) * (size_t)cols) + rowpass_tabs(fmt);
 }
 size_t colpass_lds(int fmt) { return (size_t)8 * 64 * 16 * (grouped_int_fmt(fmt) ? 8 : 4); }
 
@@ -141,7 +167,29 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     }
     pl.group_of[k] = it->second;
   }
+  // Rows per row-pass workgroup.  A single matrix or a small batch takes the smallest block
+  // of at least 16 rows that puts every block in one round of one workgroup per CU, so the
+  // CUs share the rows evenly (5120 rows: 256 blocks of 20, not 160 blocks of 32 with 96
+  // CUs idle).  Otherwise: 16 rows per wave-round, at most kMaxRowsPerBlk (a large batch
+  // splits into many similar workgroups, balanced by the dispatcher).
   const int64_t rows_per_wave = std::max<int64_t>(1, (total_rows + kTargetRowWaves - 1) / kTargetRowWaves);
+  int64_t rows_per_blk = std::min<int64_t>(kMaxRowsPerBlk, kRowWaves * rows_per_wave);
+  {
+    std::vector<int64_t> rows_of;
+    for (int k = 0; k < count; ++k)
+      if (pl.group_of[k] >= 0) rows_of.push_back(p[k].rows);
+    if (!rows_of.empty() && rows_of.size() <= (size_t)kRowWgs) {
+      for (int64_t b = std::max<int64_t>(kRowWaves, (total_rows + kRowWgs - 1) / kRowWgs);
+           b <= kMaxRowsPerBlk; ++b) {
+        int64_t wgs = 0;
+        for (int64_t m : rows_of) wgs += (m + b - 1) / b;
+        if (wgs <= kRowWgs) {
+          rows_per_blk = b;
+          break;
+        }
+      }
+    }
+  }
   const int nq = fmt == DQ_FMT_NVFP4 ? 3 : 2;
   const size_t acc_bytes = grouped_int_fmt(fmt) ? 8 : 4;
   size_t off = 0;
@@ -154,9 +202,7 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     d.dtype = p[k].w_dtype;
     if (pl.group_of[k] < 0) continue;
     Plan::Group& G = pl.groups[pl.group_of[k]];
-    // row blocks: one wave per row, at most kMaxRowsPerBlk rows per workgroup so a large batch
-    // splits into many similar workgroups (balanced tail)
-    d.rows_per_blk = (int32_t)std::min<int64_t>(kMaxRowsPerBlk, kRowWaves * rows_per_wave);
+    d.rows_per_blk = (int32_t)rows_per_blk;
     d.rowblocks = (int32_t)((d.rows + d.rows_per_blk - 1) / d.rows_per_blk);
     d.nstrips = (int32_t)((d.cols / 16 + 63) / 64);
     int64_t want = (kTargetColWgs * d.rows + total_rows - 1) / total_rows;   // this matrix's share
@@ -266,8 +312,12 @@ template <int FMT, int DT, int L>
 int launch_passes(const Plan::Group& G, const ProbDev* probs, const WgEntry* rtab,
                   const WgEntry* ctab, hipStream_t s, int sw) {
   const size_t rl = rowpass_lds(FMT, G.cols);
-  launch_timed(k_rowpass<FMT, DT, L>, dim3((unsigned)G.row.size()), dim3(kRowWaves * 64), rl, s,
-               probs, rtab, sw);
+  if (rowpass_cg(FMT, G.cols))
+    launch_timed(k_rowpass<FMT, DT, L, 1>, dim3((unsigned)G.row.size()), dim3(kRowWaves * 64), rl,
+                 s, probs, rtab, sw);
+  else
+    launch_timed(k_rowpass<FMT, DT, L, 0>, dim3((unsigned)G.row.size()), dim3(kRowWaves * 64), rl,
+                 s, probs, rtab, sw);
   if (hipGetLastError() != hipSuccess) return DQ_ERR_HIP;
   return DQ_OK;
 }
@@ -299,7 +349,7 @@ template <int FMT, int DT, int L>
 int prepare_passes(const Plan::Group& G) {
   const size_t rl = rowpass_lds(FMT, G.cols);
   if (rl > 64 * 1024 &&
-      hipFuncSetAttribute((const void*)k_rowpass<FMT, DT, L>,
+      hipFuncSetAttribute((const void*)k_rowpass<FMT, DT, L, 0>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl) != hipSuccess)
     return DQ_ERR_HIP;
   if constexpr (grouped_int<FMT>()) {
@@ -439,8 +489,9 @@ int launch_quant_t(const void* X, int64_t rows, int64_t cols, int64_t ld, const 
   const int lpr = lanes_per_row(cols), H = row_slots(lpr);
   const int64_t groups = (rows + H - 1) / H;
   const unsigned grid = (unsigned)std::min<int64_t>(groups, kQuantGroupsMax);
-  hipLaunchKernelGGL((k_quant<FMT, DT, L, MODEV>), dim3(grid), dim3(lpr * H), 0, s, X, rows,
-                     cols, ld, r, c, codes, scales, ts, part, nparts, lpr, H);
+  for (int lbeg = 0; lbeg < cols / 16; lbeg += lpr)   // one launch per 16384 columns
+    hipLaunchKernelGGL((k_quant<FMT, DT, L, MODEV>), dim3(grid), dim3(lpr * H), 0, s, X, rows,
+                       cols, ld, r, c, codes, scales, ts, part, nparts, lpr, H, lbeg);
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
@@ -532,8 +583,10 @@ int launch_quant_multi_t(const void* X, int64_t rows, int64_t cols, int64_t ld,
   if (c_lds && c_bytes > 64 * 1024) {
     if (!lds_limit((const void*)k_quant_multi<FMT, DT, L>, (int)kMultiCLds)) return DQ_ERR_HIP;
   }
-  hipLaunchKernelGGL((k_quant_multi<FMT, DT, L>), dim3(grid), dim3(lpr * H), c_lds ? c_bytes : 0, s,
-                     X, rows, cols, ld, mo, part, nparts, lpr, H, c_lds);
+  for (int lbeg = 0; lbeg < cols / 16; lbeg += lpr)   // one launch per 16384 columns
+    hipLaunchKernelGGL((k_quant_multi<FMT, DT, L>), dim3(grid), dim3(lpr * H),
+                       c_lds ? c_bytes : 0, s, X, rows, cols, ld, mo, part, nparts, lpr, H, c_lds,
+                       lbeg);
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
@@ -571,7 +624,7 @@ const char* dq_status_string(int status) {
   switch (status) {
     case DQ_OK: return "ok";
     case DQ_ERR_NULL: return "a required pointer is NULL";
-    case DQ_ERR_SHAPE: return "invalid shape (rows/cols/ld, cols not a multiple of the group, or cols > 16384)";
+    case DQ_ERR_SHAPE: return "invalid shape (rows/cols/ld, cols not a multiple of the group, or cols > 65536)";
     case DQ_ERR_ALIGN: return "base pointer or row pitch not 16-byte aligned";
     case DQ_ERR_FORMAT: return "unknown format, group or dtype";
     case DQ_ERR_WORKSPACE: return "workspace missing or too small";

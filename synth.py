@@ -111,6 +111,12 @@ WORKLOADS = {
         W=MatrixSpec(4096, 14336, "student_t", 0.015, nu=3, outliers=outlier_count(14336, 0.005),
                      outlier_scale=25.0, stream=3),
         fmt="NVFP4", group=16, iters=16),
+    # down_proj-shaped 3584x18944 bf16 (Qwen2.5-7B widths: wider than the row pass keeps in LDS),
+    # same recipe as the 4096x14336 one; NVFP4, 16 iterations
+    "down3584x18944_nvfp4": dict(
+        W=MatrixSpec(3584, 18944, "student_t", 0.015, nu=3, outliers=outlier_count(18944, 0.005),
+                     outlier_scale=25.0, stream=6),
+        fmt="NVFP4", group=16, iters=16),
     # k_proj-shaped 1024x4096 bf16, Laplace std 0.02, 2% outlier columns x20; MXINT4, 16 iterations;
     # activations 2048x4096 N(0,1) with 1% channels x50 (drawn independently of W's columns)
     "k1024x4096_mxint4": dict(

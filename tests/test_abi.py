@@ -55,7 +55,7 @@ def test_solve_argument_errors(dq):
     assert _solve_rc(dq, [ok], fmt=8, group=16) == -4               # MX blocks are 32 elements
     assert _solve_rc(dq, [ok], fmt=0, group=32) == -4               # INT4 needs 64 or 128
     assert _solve_rc(dq, [_problem(dq, cols=200)]) == -2            # not a whole number of blocks
-    assert _solve_rc(dq, [_problem(dq, cols=32768)]) == -2          # wider than 16384
+    assert _solve_rc(dq, [_problem(dq, cols=65664)]) == -2          # wider than 65536
     assert _solve_rc(dq, [_problem(dq, ld=100)]) == -2              # ld < cols
     assert _solve_rc(dq, [_problem(dq, W=0x10004)]) == -3           # misaligned W
     assert _solve_rc(dq, [_problem(dq, ld=260)]) == -3              # row pitch not 16-byte multiple

@@ -11,7 +11,9 @@ from gpu_util import ALL_FORMATS, DEV, GROUPS, scales_np, to_dev
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(64, 256), (37, 512), (3, 16384), (1, 128), (130, 14336)]
+# (3, 16384): one pass of 1024 chunks; (3, 18944) and (2, 65536): several passes, the
+# first ragged
+SHAPES = [(64, 256), (37, 512), (3, 16384), (1, 128), (130, 14336), (3, 18944), (2, 65536)]
 
 
 def _w(rows, cols, dtype, seed):
@@ -96,6 +98,22 @@ def test_rescale_quantize_acts_multi(oracle_lib, fmt, dtype, shape):
         torch.cuda.synchronize()
         for a, b in zip(g, one):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("fmt", ["NVFP4", "MXFP6_E3M2", "INT4"])
+@pytest.mark.parametrize("n_out", [1, 3])
+def test_rescale_quantize_acts_multi_wide(oracle_lib, fmt, n_out):
+    """Rows wider than 16384 columns (two passes): column scales staged in LDS (one output)
+    and read from global memory (three outputs), each output bit-exact with the oracle."""
+    tokens, cols = 5, 18944
+    X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(tokens, cols), 6)
+    rng = np.random.default_rng(12)
+    cs = [oracle_lib.project(fmt, np.exp2(rng.uniform(-3, 3, cols)).astype(np.float32))
+          for _ in range(n_out)]
+    got = dq.rescale_quantize_acts_multi(to_dev(X), [to_dev(c) for c in cs], fmt)
+    torch.cuda.synchronize()
+    for c, g in zip(cs, got):
+        _check_acts(oracle_lib, X, c, fmt, GROUPS[fmt], g)
 
 
 @pytest.mark.parametrize("fmt", ["NVFP4", "MXINT4", "INT8"])

@@ -129,6 +129,25 @@ def test_end_to_end_mx_minifloat(oracle_lib, fmt, name, rows, cols, iters):
     _compare_e2e(oracle_lib, ref, got, fmt, f"{fmt} {name}", iters)
 
 
+# rows wider than 16384 columns: the row pass reads c and 1/c from global memory (the
+# down projections of 18944 and 17408 columns, a 28672-column ragged one, and the maximum)
+E2E_WIDE = [
+    ("NVFP4", "down4096x14336_nvfp4", 96, 18944, 10),
+    ("MXFP4", "down4096x14336_nvfp4", 64, 28672, 8),
+    ("INT4", "down4096x14336_nvfp4", 37, 17408, 8),
+    ("MXFP6_E2M3", "down4096x14336_nvfp4", 24, 65536, 6),
+]
+
+
+@pytest.mark.parametrize("fmt,name,rows,cols,iters", E2E_WIDE)
+def test_end_to_end_wide(oracle_lib, fmt, name, rows, cols, iters):
+    W = synth.matrix(synth.WORKLOADS[name]["W"].scaled(rows, cols), 0)
+    print(f"[e2e] wide {fmt} {rows}x{cols} T={iters}", flush=True)
+    ref = oracle_lib.solve(W, fmt, iters)
+    got = _gpu_solve(W, fmt, iters, trace=True)
+    _compare_e2e(oracle_lib, ref, got, fmt, f"wide {fmt} {rows}x{cols}", iters)
+
+
 @pytest.mark.parametrize("name", ["w256x512_int4", "k1024x4096_mxint4", "q4096x4096_mxfp4",
                                   "down4096x14336_nvfp4"])
 def test_end_to_end_full_size(oracle_lib, name):
