@@ -44,6 +44,11 @@ METRIC = "BCD solver Gelem/s per iteration + achieved HBM GB/s vs peak (4096×14
 
 
 KERNELS = ("k_rowpass", "k_colpass", "k_finalize")
+# The row pass is bound by VALU issue: 377 VALU instructions per 16-element chunk in a normal
+# sweep (NVFP4 codes, bf16 weight; counted in the gfx950 assembly) against 256 CUs x 64 lanes
+# x 2.4 GHz = 39.3 T lane-operations/s (unpacked fp32).
+ROWPASS_VALU_PER_ELEM = {("NVFP4", 2): 377 / 16}
+VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9
 
 
 def recorded_traffic(kernel: str, workload: str):
@@ -405,6 +410,15 @@ def main():
         "rejected_steps": int(reps[-1].rejected_steps),
         "nmse_first_last": [float(nm[0]), float(nm[-1])],
     }
+    vpe = ROWPASS_VALU_PER_ELEM.get((fmt, W.element_size()))
+    if dom == "k_rowpass" and vpe is not None:
+        # the roof that binds the row pass: VALU lane-operations per second
+        lane_ops = m * n * vpe / (avg[dom] * 1e-3)
+        out["roofline"]["valu"] = {"instr_per_elem": round(vpe, 3),
+                                   "achieved_lane_ops": round(lane_ops / 1e12, 2),
+                                   "peak_lane_ops": round(VALU_PEAK_LANE_OPS / 1e12, 2),
+                                   "unit": "T lane-ops/s",
+                                   "frac": round(lane_ops / VALU_PEAK_LANE_OPS, 4)}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", flush=True)
         out["cpu_baseline"] = cpu_baseline(W_np, X_np, fmt, T)
