@@ -89,10 +89,12 @@ int check_matrix(const void* X, int32_t dt, int64_t rows, int64_t cols, int64_t 
 constexpr int kRowWaves = 16;
 constexpr int kRowWgs = 256;
 constexpr int kTargetRowWaves = kRowWgs * kRowWaves;
-// Column pass: workgroups of 8 waves on a 1024-column strip and a range of rows; about
-// four per CU, so each CU has several workgroups' loads in flight (one per CU left the
-// HBM reads latency-bound: 34 us instead of 29.5 us on a 4096 x 14336 weight).
-constexpr int kTargetColWgs = 1024;
+// Column pass: workgroups of 8 waves on a 1024-column strip and a range of rows, two per CU
+// (registers).  A matrix takes at most its share of 512 workgroups, rounded down, so a
+// single matrix runs in one round: 4096 x 14336 gets 14 strips x 36 ranges = 504 (26.6 us
+// per launch; 896 workgroups in 1.75 rounds took 29.9 us, and 518 in just over one round
+// took 2.6 us more than that).
+constexpr int kTargetColWgs = 512;
 // The finalize pass reduces up to 64 row ranges per column with one round of loads.
 constexpr int64_t kMaxRowRanges = 64;
 // Caps for large batches: many workgroups of bounded size keep the last wave of workgroups
@@ -206,7 +208,7 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     d.rowblocks = (int32_t)((d.rows + d.rows_per_blk - 1) / d.rows_per_blk);
     d.nstrips = (int32_t)((d.cols / 16 + 63) / 64);
     int64_t want = (kTargetColWgs * d.rows + total_rows - 1) / total_rows;   // this matrix's share
-    int64_t rr = std::max<int64_t>(1, std::min<int64_t>(d.rows, (want + d.nstrips - 1) / d.nstrips));
+    int64_t rr = std::max<int64_t>(1, std::min<int64_t>(d.rows, want / d.nstrips));
     rr = std::min<int64_t>(rr, kMaxRowRanges);
     d.rows_per_range = (int32_t)std::min<int64_t>(kMaxRowsPerRange, (d.rows + rr - 1) / rr);
     d.rranges = (int32_t)((d.rows + d.rows_per_range - 1) / d.rows_per_range);
