@@ -148,6 +148,24 @@ def test_end_to_end_wide(oracle_lib, fmt, name, rows, cols, iters):
     _compare_e2e(oracle_lib, ref, got, fmt, f"wide {fmt} {rows}x{cols}", iters)
 
 
+# more rows than 16 per row-pass workgroup (one wave takes two rows, its neighbours one) and
+# larger column-pass row ranges: 5120 rows -> blocks of 20, 9000 rows -> blocks of 36
+E2E_TALL = [
+    ("NVFP4", "down4096x14336_nvfp4", 5120, 1024, 8),
+    ("MXFP4", "q4096x4096_mxfp4", 9000, 512, 8),
+    ("INT4", "w256x512_int4", 4500, 512, 10),
+]
+
+
+@pytest.mark.parametrize("fmt,name,rows,cols,iters", E2E_TALL)
+def test_end_to_end_tall(oracle_lib, fmt, name, rows, cols, iters):
+    W = synth.matrix(synth.WORKLOADS[name]["W"].scaled(rows, cols), 0)
+    print(f"[e2e] tall {fmt} {rows}x{cols} T={iters}", flush=True)
+    ref = oracle_lib.solve(W, fmt, iters)
+    got = _gpu_solve(W, fmt, iters, trace=True)
+    _compare_e2e(oracle_lib, ref, got, fmt, f"tall {fmt} {rows}x{cols}", iters)
+
+
 @pytest.mark.parametrize("name", ["w256x512_int4", "k1024x4096_mxint4", "q4096x4096_mxfp4",
                                   "down4096x14336_nvfp4"])
 def test_end_to_end_full_size(oracle_lib, name):
