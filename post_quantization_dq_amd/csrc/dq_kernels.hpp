@@ -981,15 +981,20 @@ __global__ __launch_bounds__(256) void k_qamax(const void* __restrict__ X, int64
                                                float* __restrict__ part, int nstrips,
                                                int rows_per_range) {
   constexpr int VEC = (DT == 1) ? 8 : 4;   // elements per 16-byte load
-  constexpr int U = 4;                      // loads in flight per thread
+  constexpr int U = 16;                     // loads in flight per thread (a 16-row range: one round)
   const int strip = (int)(blockIdx.x % nstrips), rr = (int)(blockIdx.x / nstrips);
   const int64_t nv = cols / VEC;
   const int64_t v = (int64_t)strip * 256 + threadIdx.x;
   const int64_t r0 = (int64_t)rr * rows_per_range, r1 = min(rows, r0 + rows_per_range);
   const int64_t rowbytes = ld * (DT == 1 ? 2 : 4);
-  float cm[VEC];
+  float cm[VEC], cj[VEC];
 #pragma unroll
-  for (int k = 0; k < VEC; ++k) cm[k] = 0.0f;
+  for (int k = 0; k < VEC; ++k) { cm[k] = 0.0f; cj[k] = 1.0f; }
+  // this thread's column scales, requested before the rows so they arrive under them
+  if (v < nv && c) {
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) cj[k] = gp(c)[v * VEC + k];
+  }
   if (v < nv) {
     for (int64_t i0 = r0; i0 < r1; i0 += U) {
       u32x4 u[U];
@@ -1021,7 +1026,7 @@ __global__ __launch_bounds__(256) void k_qamax(const void* __restrict__ X, int64
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
       float sj = 1.0f;
-      if (c) sj = (MODEV == 0) ? 1.0f / gp(c)[v * VEC + k] : fabsf(gp(c)[v * VEC + k]);
+      if (c) sj = (MODEV == 0) ? 1.0f / cj[k] : fabsf(cj[k]);
       m = fmaxf(m, (MODEV == 0) ? fabsf(cm[k] * sj) : cm[k] * sj);
     }
   }
