@@ -281,7 +281,10 @@ def bench_qkv_acts(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    # default: 200 steps of a single-matrix workload, so that the one timed step that also
+    # carries per-launch events (for the roofline) adds under 0.5% to the mean; 5 steps of
+    # the 224-matrix set; 20 of the layer and activation benchmarks
+    ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--format", default=None,
@@ -289,6 +292,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = {"llama31_8b_nvfp4": 5, "linear_w4a4_mxfp4": 20, "linear_w4a4_nvfp4": 20,
+                      "qkv_acts_nvfp4": 20}.get(args.workload, 200)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the solve runs on a single MI355X and the library "
