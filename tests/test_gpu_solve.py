@@ -139,10 +139,22 @@ E2E_WIDE = [
 ]
 
 
-@pytest.mark.parametrize("fmt,name,rows,cols,iters", E2E_WIDE)
-def test_end_to_end_wide(oracle_lib, fmt, name, rows, cols, iters):
-    W = synth.matrix(synth.WORKLOADS[name]["W"].scaled(rows, cols), 0)
-    print(f"[e2e] wide {fmt} {rows}x{cols} T={iters}", flush=True)
+# fp32 weights: 24576 and 20480 columns (NVFP4: past the LDS limit by its tables) read c
+# from L2; INT8 at 18432 keeps 144 KiB of column scales in LDS
+E2E_WIDE_F32 = [
+    ("MXFP4", "q4096x4096_mxfp4", 40, 24576, 8),
+    ("NVFP4", "down4096x14336_nvfp4", 33, 20480, 8),
+    ("INT8", "w256x512_int4", 33, 18432, 8),
+]
+
+
+@pytest.mark.parametrize("fmt,name,rows,cols,iters,dtype",
+                         [c + ("bf16",) for c in E2E_WIDE] + [c + ("f32",) for c in E2E_WIDE_F32])
+def test_end_to_end_wide(oracle_lib, fmt, name, rows, cols, iters, dtype):
+    from dataclasses import replace
+
+    W = synth.matrix(replace(synth.WORKLOADS[name]["W"].scaled(rows, cols), dtype=dtype), 0)
+    print(f"[e2e] wide {fmt} {dtype} {rows}x{cols} T={iters}", flush=True)
     ref = oracle_lib.solve(W, fmt, iters)
     got = _gpu_solve(W, fmt, iters, trace=True)
     _compare_e2e(oracle_lib, ref, got, fmt, f"wide {fmt} {rows}x{cols}", iters)
