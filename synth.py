@@ -117,6 +117,12 @@ WORKLOADS = {
         W=MatrixSpec(3584, 18944, "student_t", 0.015, nu=3, outliers=outlier_count(18944, 0.005),
                      outlier_scale=25.0, stream=6),
         fmt="NVFP4", group=16, iters=16),
+    # down_proj-shaped 5120x17408 bf16 (Qwen3-14B widths: 20 rows per row-pass workgroup), same
+    # recipe; NVFP4, 16 iterations
+    "down5120x17408_nvfp4": dict(
+        W=MatrixSpec(5120, 17408, "student_t", 0.015, nu=3, outliers=outlier_count(17408, 0.005),
+                     outlier_scale=25.0, stream=7),
+        fmt="NVFP4", group=16, iters=16),
     # k_proj-shaped 1024x4096 bf16, Laplace std 0.02, 2% outlier columns x20; MXINT4, 16 iterations;
     # activations 2048x4096 N(0,1) with 1% channels x50 (drawn independently of W's columns)
     "k1024x4096_mxint4": dict(
