@@ -378,7 +378,8 @@ def main():
     value = m * n * T / (ms_step * 1e-3) / 1e9
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if (m, n, fmt) == (4096, 14336, "NVFP4")
+                  else METRIC.replace("(4096×14336 NVFP4)", f"({m}×{n} {fmt})"),
         "value": round(value, 3),
         "unit": "Gelem/s",
         "n_gpus": 1,
