@@ -79,7 +79,8 @@ def lib():
         L.o_dequantize.argtypes = [C.c_int, C.c_int, p, p, C.c_float, i64, i64, p]
         L.o_dequantize.restype = C.c_int
         L.o_solve.argtypes = [p, C.c_int, i64, i64, i64, C.c_int, C.c_int, C.c_int, C.c_float,
-                              p, p, p, p, p, p, p, p, p, p, p, p, p, p, C.c_int]
+                              p, p, p, p, p, p, p, p, p, p, p, p, p, p, C.c_int, p, p,
+                              C.c_float]
         L.o_solve.restype = C.c_int
         L.o_rescale_quantize_acts.argtypes = [p, i64, i64, i64, p, C.c_int, C.c_int, p, p, p, p]
         L.o_rescale_quantize_acts.restype = C.c_int
@@ -235,12 +236,14 @@ def dequantize(codes, scales, tscale: float, fmt: str, rows: int, cols: int,
 
 
 def solve(W: np.ndarray, fmt: str, iters: int, group: int | None = None, r_init=None,
-          c_init=None, tol: float = 0.0, steps: int = 3) -> dict:
+          c_init=None, tol: float = 0.0, steps: int = 3, q_init=None) -> dict:
     """The BCD solve; returns r, c, codes, scales, tscale, nmse, relchg, rejected,
     iters_run, r_trace / c_trace (every iteration's unprojected closed forms, NaN where
     D = 0 or the step is frozen; r_pre / c_pre are the last rows) and flags.  `steps`
     selects the scale steps that run: 1 = row scales only, 2 = column scales only, 3 = both
-    (the ablation of the news summary: only one of the two scale sets turned on)."""
+    (the ablation of the news summary: only one of the two scale sets turned on).
+    `q_init` = (codes, scales, tscale) of a kept Qhat resumes a solve from the state
+    (r_init, c_init, that Qhat) instead of starting from FQ(W ./ r c^T)."""
     group = group or DEFAULT_GROUP[fmt]
     W = np.ascontiguousarray(W)
     rows, cols = W.shape
@@ -258,10 +261,18 @@ def solve(W: np.ndarray, fmt: str, iters: int, group: int | None = None, r_init=
     r_tr = np.full((max(iters, 1), rows), np.nan, dtype=np.float32)
     c_tr = np.full((max(iters, 1), cols), np.nan, dtype=np.float32)
     flags = np.zeros(1, dtype=np.uint32)
+    qc = qs = None
+    qt = 0.0
+    if q_init is not None:
+        qc = np.ascontiguousarray(q_init[0], dtype=np.uint8)
+        qs = np.ascontiguousarray(q_init[1], dtype=_scale_dtype(fmt))
+        qt = float(q_init[2])
+        assert qc.size == codes.size and qs.size == scales.size
     _check(lib().o_solve(_ptr(W), _w_dtype(W), rows, cols, cols, FMT[fmt], group, iters,
                          float(tol), _ptr(ri), _ptr(ci), _ptr(r), _ptr(c), _ptr(codes),
                          _ptr(scales), _ptr(ts), _ptr(nmse), _ptr(relchg), _ptr(rej), _ptr(run),
-                         _ptr(r_tr), _ptr(c_tr), _ptr(flags), int(steps)), "solve")
+                         _ptr(r_tr), _ptr(c_tr), _ptr(flags), int(steps), _ptr(qc), _ptr(qs),
+                         qt), "solve")
     k = int(run[0])
     return dict(r=r, c=c, codes=codes, scales=scales, tscale=float(ts[0]), nmse=nmse[:k + 1],
                 relchg=relchg[:k + 1], rejected=int(rej[0]), iters_run=k, r_trace=r_tr[:iters],

@@ -215,20 +215,17 @@ int floor_log2(float a) {
 // set (the conference abstract: "projecting scales onto their format-specific admissible
 // set after each update").  For a 1-D quadratic D (s - x)^2 the constrained minimiser is
 // the admissible point nearest to x, so "projection" is the nearest point.
-//   MX formats: powers of two 2^k, k in [-127, 127] (E8M0 range); ties go to the larger.
-//   NVFP4:      positive E4M3FN values [2^-9, 448]; ties to the even code.
-//   INT4, INT8: positive bf16 values [2^-126, max bf16]; ties to even.
+//   NVFP4:              positive E4M3FN values [2^-9, 448]; ties to the even code.
+//   INT, MX formats:    positive bf16 values [2^-126, max bf16]; ties to even.
+// The MX block scale itself stays an E8M0 power of two inside the quantiser.  The dual
+// scales are not: a power-of-two row scale would be absorbed exactly by every block's E8M0
+// exponent (same codes, same reconstruction), so the dual scales would change nothing for
+// MX, against the conference abstract's "formally support MX" and the news summary's
+// ablation in which row scales alone already help.  They multiply outside the block format
+// (r on the layer output, c on the activations before their quantiser), in the bf16 the
+// pages store their per-group weight scales in (listing page, Table 12).
 float project(int fmt, float x) {
-  if (is_mx(fmt)) {
-    double best = std::ldexp(1.0, -127), bestd = std::fabs((double)x - best);
-    for (int k = -126; k <= 127; ++k) {
-      double p = std::ldexp(1.0, k), d = std::fabs((double)x - p);
-      if (d <= bestd) { best = p; bestd = d; }  // ascending scan: ties go to the larger
-    }
-    return (float)best;
-  }
   if (fmt == FMT_NVFP4) return (float)e4m3_value(e4m3_encode_nonneg(x, 1));
-  // INT4 / INT8: bf16
   const float lo = std::ldexp(1.0f, -126);
   const float hi = f_of(0x7F7F0000u);
   float b = bf16_round(std::min(x, hi));
@@ -414,9 +411,14 @@ void fq_matrix(int fmt, int g, const float* V, int64_t rows, int64_t cols, FQOut
     s_t = A / 2688.0f;
     float six_st = 6.0f * s_t;
     k6 = (s_t > 0.0f) ? 1.0f / six_st : 0.0f;
-    // A tensor scale below 2^-100 (amax below about 2^-88.6) leaves block scales whose
-    // reciprocals overflow fp32; the whole matrix then quantises to zero (flag bit 16).
-    if (!(s_t >= std::ldexp(1.0f, -100)) || !std::isfinite(k6)) {
+    // The scheme divides twice: by 6 s_t for the block scales, and by each block factor
+    // d = e4m3(sb) s_t for the elements.  Both reciprocals must be finite fp32 numbers for
+    // every block scale that can occur, the smallest being 2^-9 (the least E4M3 subnormal).
+    // When A is so small that 1 / fl(2^-9 s_t) overflows (s_t at or below about 2^-119) or
+    // s_t underflows to 0, no block of the matrix can be encoded: it quantises to zero and
+    // flag bit 16 says so.
+    const float id_min = (s_t > 0.0f) ? 1.0f / ((float)e4m3_value(1) * s_t) : 0.0f;
+    if (!(s_t > 0.0f) || !std::isfinite(k6) || !std::isfinite(id_min)) {
       if (A > 0.0f) o.flags |= 16u;
       s_t = 0.0f;
       k6 = 0.0f;
@@ -632,11 +634,17 @@ int o_dequantize(int fmt, int g, const uint8_t* codes, const void* scales, float
 // traces of every iteration's unprojected closed-form values, r_trace [T][rows] and
 // c_trace [T][cols] (NaN where D = 0).  tol > 0 stops after the first iteration whose
 // relchg is <= tol (a rejected step has relchg 0); iters_run reports the count.
+// Resuming: the solver's whole state is (r, c, kept Qhat).  When q_codes is given, the
+// solve starts from r_init, c_init and the kept Qhat held in q_codes / q_scales /
+// q_tscale (the outputs of an earlier solve) instead of FQ(W ./ r c^T): after a rejected
+// step the kept Qhat is not the quantisation of W at the current scales, so the scales
+// alone would not resume exactly.
 int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int g,
             int iters, float tol, const float* r_init, const float* c_init, float* r_out,
             float* c_out, uint8_t* codes, void* scales, float* tscale, double* nmse_hist,
             double* relchg_hist, int* rejected_out, int* iters_run, float* r_trace,
-            float* c_trace, uint32_t* flags_out, int steps) {
+            float* c_trace, uint32_t* flags_out, int steps, const uint8_t* q_codes,
+            const void* q_scales, float q_tscale) {
   if (!W || !r_out || !c_out || !codes || !scales) return ERR_NULL;
   if (steps < 0 || steps > 3) return ERR_SHAPE;
   if (!group_ok(fmt, g)) return ERR_FORMAT;
@@ -663,8 +671,15 @@ int o_solve(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, in
   float tsA = 0.0f, tsC = 0.0f;
   uint32_t flags = 0;
 
-  normalise(Wf.data(), rows, cols, r.data(), c.data(), V.data());
-  {
+  if (q_codes) {
+    if (!q_scales) return ERR_NULL;
+    std::memcpy(codesA.data(), q_codes, codesA.size());
+    std::memcpy(scA.data(), q_scales, scA.size());
+    tsA = (fmt == FMT_NVFP4) ? q_tscale : 0.0f;
+    int rc = o_dequantize(fmt, g, codesA.data(), scA.data(), tsA, rows, cols, Q.data());
+    if (rc != OK) return rc;
+  } else {
+    normalise(Wf.data(), rows, cols, r.data(), c.data(), V.data());
     FQOut o{codesA.data(), scA.data(), &tsA, Q.data(), 0u};
     fq_matrix(fmt, g, V.data(), rows, cols, o);
     flags |= o.flags;

@@ -104,20 +104,18 @@ def test_sign_symmetry_and_zero_blocks(oracle_lib, fmt):
 @pytest.mark.parametrize("fmt", FORMATS8)
 def test_scale_steps_minimise_over_admissible_set(oracle_lib, fmt):
     """The r-step result is the admissible value minimising the row objective (brute
-    force over bf16 values near the closed form for INT8, over all powers of two for MX)."""
+    force over the 129 bf16 values around the closed form: bf16 is the dual scales'
+    admissible set for INT8 and for the MX formats)."""
     rng = np.random.default_rng(6)
     W = (rng.standard_t(4, (6, 256)) * 0.02).astype(np.float32)
     res = oracle_lib.solve(W, fmt, 1)
     Q0 = oracle_lib.quantize_weights(W, None, None, fmt)[3].astype(np.float64)
     for i in range(W.shape[0]):
         f = lambda s: np.sum((W[i].astype(np.float64) - s * Q0[i]) ** 2)   # c = 1 at the r-step
-        if fmt == "MXINT8":
-            cand = np.ldexp(1.0, np.arange(-127, 128))
-        else:
-            x = res["r_trace"][0][i]
-            base = torch.tensor([x], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).item()
-            cand = torch.tensor(np.arange(base - 64, base + 65), dtype=torch.int16).view(torch.bfloat16).double().numpy()
-            cand = cand[cand > 0]
+        x = res["r_trace"][0][i]
+        base = torch.tensor([x], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).item()
+        cand = torch.tensor(np.arange(base - 64, base + 65), dtype=torch.int16).view(torch.bfloat16).double().numpy()
+        cand = cand[cand > 0]
         best = min(f(s) for s in cand)
         assert f(float(res["r"][i])) <= best * (1 + 1e-12)
 

@@ -1,4 +1,5 @@
-"""Pins for the oracle's block fake-quantisers FQ_f (INT4, MXINT4, MXFP4, NVFP4).
+"""Pins for the oracle's block fake-quantisers FQ_f (INT4 with groups 128 and 64 -- the
+listing page's tables use G = 64 -- MXINT4, MXFP4, NVFP4).
 
 Pinned by what the format definitions fix independently of the oracle's code:
 exact invariants (idempotence for MX, power-of-two equivariance, sign symmetry,
@@ -18,6 +19,8 @@ import synth
 
 FORMATS = ["INT4", "MXINT4", "MXFP4", "NVFP4"]
 GROUPS = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16}
+# (format, group): INT4 with both group sizes
+CASES = [("INT4", 128), ("INT4", 64), ("MXINT4", 32), ("MXFP4", 32), ("NVFP4", 16)]
 E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
 
 
@@ -34,13 +37,12 @@ def _blocks(x, g):
     return x.reshape(x.shape[0], -1, g)
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
-def test_dequantize_roundtrip_and_grid(oracle_lib, fmt):
-    g = GROUPS[fmt]
+@pytest.mark.parametrize("fmt,g", CASES)
+def test_dequantize_roundtrip_and_grid(oracle_lib, fmt, g):
     V = _rand(24, 256, 1)
-    codes, scales, ts, qhat, flags = oracle_lib.fq(V, fmt)
+    codes, scales, ts, qhat, flags = oracle_lib.fq(V, fmt, g)
     assert codes.size == V.size // 2 and scales.size == V.size // g
-    deq = oracle_lib.dequantize(codes, scales, ts, fmt, *V.shape)
+    deq = oracle_lib.dequantize(codes, scales, ts, fmt, *V.shape, group=g)
     assert np.array_equal(deq.view(np.uint32), qhat.view(np.uint32))
     # every element lies on the element grid times its block scale
     nib = np.stack([codes & 0xF, codes >> 4], axis=1).reshape(V.shape)
@@ -69,12 +71,12 @@ def test_mx_idempotent(oracle_lib, fmt):
     assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("fmt,g", CASES)
 @pytest.mark.parametrize("k", [-5, 3])
-def test_power_of_two_equivariance(oracle_lib, fmt, k):
+def test_power_of_two_equivariance(oracle_lib, fmt, g, k):
     V = _rand(16, 256, 3)
-    c1, s1, t1, q1, _ = oracle_lib.fq(V, fmt)
-    c2, s2, t2, q2, _ = oracle_lib.fq(np.ldexp(V, k).astype(np.float32), fmt)
+    c1, s1, t1, q1, _ = oracle_lib.fq(V, fmt, g)
+    c2, s2, t2, q2, _ = oracle_lib.fq(np.ldexp(V, k).astype(np.float32), fmt, g)
     assert np.array_equal(c1, c2)
     assert np.array_equal(np.ldexp(q1, k), q2)
     if fmt in ("MXINT4", "MXFP4"):
@@ -83,28 +85,26 @@ def test_power_of_two_equivariance(oracle_lib, fmt, k):
         assert np.array_equal(s1, s2) and t2 == np.ldexp(np.float32(t1), k)
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
-def test_sign_symmetry_and_permutations(oracle_lib, fmt):
-    g = GROUPS[fmt]
+@pytest.mark.parametrize("fmt,g", CASES)
+def test_sign_symmetry_and_permutations(oracle_lib, fmt, g):
     V = _rand(12, 512, 4)
-    _, s1, t1, q1, _ = oracle_lib.fq(V, fmt)
-    _, s2, t2, q2, _ = oracle_lib.fq(-V, fmt)
+    _, s1, t1, q1, _ = oracle_lib.fq(V, fmt, g)
+    _, s2, t2, q2, _ = oracle_lib.fq(-V, fmt, g)
     assert np.array_equal(-q1, q2) and np.array_equal(s1, s2) and t1 == t2
     rng = np.random.default_rng(5)
     rp = rng.permutation(V.shape[0])
     bp = rng.permutation(V.shape[1] // g)
     Vp = _blocks(V[rp], g)[:, bp].reshape(V.shape)
-    _, s3, t3, q3, _ = oracle_lib.fq(np.ascontiguousarray(Vp), fmt)
+    _, s3, t3, q3, _ = oracle_lib.fq(np.ascontiguousarray(Vp), fmt, g)
     assert np.array_equal(q3, _blocks(q1[rp], g)[:, bp].reshape(V.shape))
     assert t3 == t1
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
-def test_nearest_point_brute_force(oracle_lib, fmt):
+@pytest.mark.parametrize("fmt,g", CASES)
+def test_nearest_point_brute_force(oracle_lib, fmt, g):
     """Each element is the nearest point of its block's representable set (ties either)."""
-    g = GROUPS[fmt]
     V = _rand(8, 128, 6)
-    codes, scales, ts, qhat, _ = oracle_lib.fq(V, fmt)
+    codes, scales, ts, qhat, _ = oracle_lib.fq(V, fmt, g)
     if fmt == "INT4":
         s = (scales.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         grid = np.arange(-7, 8, dtype=np.float64)[None, :] * s[:, None]
@@ -144,10 +144,11 @@ def test_mx_scale_rule_and_top_binade(oracle_lib):
     assert set(np.unique(topi)).issubset({4.0, 5.0, 6.0, 7.0})
 
 
-def test_int4_scale_is_bf16_of_amax_over_7(oracle_lib):
+@pytest.mark.parametrize("g", [128, 64])
+def test_int4_scale_is_bf16_of_amax_over_7(oracle_lib, g):
     V = _rand(16, 512, 8)
-    _, s, _, _, _ = oracle_lib.fq(V, "INT4")
-    amax = np.abs(V.reshape(-1, 128)).max(axis=1)
+    _, s, _, _, _ = oracle_lib.fq(V, "INT4", g)
+    amax = np.abs(V.reshape(-1, g)).max(axis=1)
     want = torch.from_numpy((amax / np.float32(7)).astype(np.float32)).to(torch.bfloat16)
     assert np.array_equal(s, want.view(torch.int16).numpy().view(np.uint16))
 
@@ -181,18 +182,18 @@ def test_zero_blocks(oracle_lib):
     assert ts == 0 and np.all(codes == 0) and np.all(scales == 0) and np.all(q == 0)
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
-def test_quantize_weights_is_fq_of_normalised(oracle_lib, fmt):
+@pytest.mark.parametrize("fmt,g", CASES)
+def test_quantize_weights_is_fq_of_normalised(oracle_lib, fmt, g):
     rng = np.random.default_rng(11)
     W = synth.f32_to_bf16_bits(_rand(16, 256, 12))
     r = oracle_lib.project(fmt, np.exp2(rng.uniform(-1, 1, 16)).astype(np.float32))
     c = oracle_lib.project(fmt, np.exp2(rng.uniform(-1, 1, 256)).astype(np.float32))
-    codes, scales, ts, q = oracle_lib.quantize_weights(W, r, c, fmt)
+    codes, scales, ts, q = oracle_lib.quantize_weights(W, r, c, fmt, g)
     Wf = synth.bf16_bits_to_f32(W)
     ir = (np.float32(1) / r).astype(np.float32)
     ic = (np.float32(1) / c).astype(np.float32)
     V = ((Wf * ir[:, None]).astype(np.float32) * ic[None, :]).astype(np.float32)
-    c2, s2, t2, q2, _ = oracle_lib.fq(V, fmt)
+    c2, s2, t2, q2, _ = oracle_lib.fq(V, fmt, g)
     assert np.array_equal(codes, c2) and np.array_equal(scales, s2) and ts == t2
 
 

@@ -122,19 +122,18 @@ def test_int_round_against_rint(oracle_lib):
     assert np.array_equal(got.astype(np.float64), want)
 
 
-def test_project_pow2(oracle_lib):
+def test_project_mx_is_bf16(oracle_lib):
+    """The MX formats' dual scales project onto bf16, like INT4's (their E8M0 power of two
+    is the block scale's set, inside the quantiser)."""
     rng = np.random.default_rng(4)
-    x = np.exp2(rng.uniform(-130, 130, 200_000)).astype(np.float32)
+    x = np.exp2(rng.uniform(-130, 127, 200_000)).astype(np.float32)
     x = np.concatenate([x, np.float32([1.0, 1.5, 1.4999999, 3.0, 0.75, 2.0 ** -127, 1e-45, 3e38]),
                         (1.5 * np.exp2(np.arange(-120, 120))).astype(np.float32)])
     x = x[(x > 0) & np.isfinite(x)]
-    got = oracle_lib.project("MXFP4", x)
-    m, e = np.frexp(x.astype(np.float64))          # x = m 2^e, m in [0.5, 1)
-    k = e - 1                                       # floor(log2 x)
-    want = np.where(m * 2 >= 1.5, np.ldexp(1.0, k + 1), np.ldexp(1.0, k))
-    want = np.clip(want, 2.0 ** -127, 2.0 ** 127)
-    assert np.array_equal(got.astype(np.float64), want)
-    assert np.array_equal(got, oracle_lib.project("MXINT4", x))
+    want = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    want = np.clip(want, 2.0 ** -126, np.float32(torch.finfo(torch.bfloat16).max))
+    for fmt in ("MXFP4", "MXINT4", "MXINT8", "MXFP8_E4M3", "MXFP8_E5M2", "MXFP6_E2M3", "MXFP6_E3M2"):
+        assert np.array_equal(oracle_lib.project(fmt, x), want), fmt
 
 
 def test_project_e4m3(oracle_lib):

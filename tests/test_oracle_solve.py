@@ -24,8 +24,8 @@ GROUPS = {"INT4": 128, "MXINT4": 32, "MXFP4": 32, "NVFP4": 16}
 
 
 def _admissible(fmt):
-    if fmt in ("MXINT4", "MXFP4"):
-        return np.ldexp(1.0, np.arange(-127, 128))
+    """Every admissible dual scale: positive E4M3 values (NVFP4), else positive normal
+    finite bf16 values (INT4 and the MX formats)."""
     if fmt == "NVFP4":
         return torch.arange(1, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
     bits = np.arange(0x0080, 0x7F80, dtype=np.uint32) << 16   # positive normal finite bf16
@@ -51,17 +51,18 @@ def _w(rows, cols, seed):
     return synth.matrix(spec, seed)
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
-def test_scale_steps_are_constrained_minimisers(oracle_lib, fmt):
-    rows, cols = 6, GROUPS[fmt] * 4
+@pytest.mark.parametrize("fmt,g", [("INT4", 128), ("INT4", 64), ("MXINT4", 32), ("MXFP4", 32),
+                                   ("NVFP4", 16)])
+def test_scale_steps_are_constrained_minimisers(oracle_lib, fmt, g):
+    rows, cols = 6, g * 4
     W = _w(rows, cols, 1)
     Wf = synth.bf16_bits_to_f32(W).astype(np.float64)
     rng = np.random.default_rng(2)
     r0 = oracle_lib.project(fmt, np.exp2(rng.uniform(-0.7, 0.7, rows)).astype(np.float32))
     c0 = oracle_lib.project(fmt, np.exp2(rng.uniform(-0.7, 0.7, cols)).astype(np.float32))
-    _, _, _, Q0 = oracle_lib.quantize_weights(W, r0, c0, fmt)
+    _, _, _, Q0 = oracle_lib.quantize_weights(W, r0, c0, fmt, g)
     Q0 = Q0.astype(np.float64)
-    res = oracle_lib.solve(W, fmt, 1, r_init=r0, c_init=c0)
+    res = oracle_lib.solve(W, fmt, 1, g, r_init=r0, c_init=c0)
     adm = _admissible(fmt)
     for i in range(rows):
         u = Q0[i] * c0
@@ -92,22 +93,19 @@ SMALL = [("w256x512_int4", 256, 512), ("q4096x4096_mxfp4", 256, 1024),
          ("down4096x14336_nvfp4", 256, 1792), ("k1024x4096_mxint4", 256, 1024)]
 
 
-@pytest.mark.parametrize("name,rows,cols", SMALL)
-def test_monotone_and_no_worse_than_single_scale(oracle_lib, name, rows, cols):
+@pytest.mark.parametrize("name,rows,cols,g", [s + (None,) for s in SMALL] + [("w256x512_int4", 256, 512, 64)])
+def test_monotone_and_no_worse_than_single_scale(oracle_lib, name, rows, cols, g):
     W, fmt = _workload_small(name, rows, cols)
-    res = oracle_lib.solve(W, fmt, 24)
+    res = oracle_lib.solve(W, fmt, 24, g)
     nm = res["nmse"]
     assert np.all(np.diff(nm) <= 0.0)
     assert nm[-1] <= nm[0]
     # single-scale start: nmse[0] is FQ(W) with r = c = 1
-    codes, scales, ts, Q = oracle_lib.quantize_weights(W, None, None, fmt)
+    codes, scales, ts, Q = oracle_lib.quantize_weights(W, None, None, fmt, g)
     Wf = (synth.bf16_bits_to_f32(W) if W.dtype == np.uint16 else W).astype(np.float64)
     assert np.isclose(nm[0], np.sum((Wf - Q) ** 2) / np.sum(Wf ** 2), rtol=1e-12)
-    # stabilisation: the change of Qhat reaches zero and stays there
-    rc = res["relchg"]
-    z = np.nonzero(rc[1:] > 0)[0]
-    last_change = (z[-1] + 1) if z.size else 0
-    assert last_change <= 22
+    # the dual-scale fit improves on the single-scale start (strictly, on these weights)
+    assert nm[-1] < nm[0]
 
 
 @pytest.mark.parametrize("name,rows,cols", SMALL[:3])
@@ -156,10 +154,10 @@ def test_history_recomputed_from_outputs(oracle_lib):
         prev = Q
 
 
-def _planted(fmt, rows, cols, seed):
+def _planted(fmt, rows, cols, seed, g=None):
     """W = diag(r0) Q0 diag(c0), Q0 exactly on the format's grid with every block's largest
     element at the top of its binade, so FQ(Q0) = Q0."""
-    g = GROUPS[fmt]
+    g = g or GROUPS[fmt]
     rng = np.random.default_rng(seed)
     nb = cols // g
     if fmt == "MXFP4":
@@ -194,13 +192,13 @@ def _bf16_values(x):
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).float().double().numpy()
 
 
-@pytest.mark.parametrize("fmt", ["MXFP4", "MXINT4", "INT4"])
-def test_planted_factorisation_is_fixed_point(oracle_lib, fmt):
-    W, r0, c0 = _planted(fmt, 8, GROUPS[fmt] * 4, 3)
+@pytest.mark.parametrize("fmt,g", [("MXFP4", 32), ("MXINT4", 32), ("INT4", 128), ("INT4", 64)])
+def test_planted_factorisation_is_fixed_point(oracle_lib, fmt, g):
+    W, r0, c0 = _planted(fmt, 8, g * 4, 3, g)
     if fmt != "INT4":   # MX products have few significant bits: exact in bf16
         assert np.array_equal(synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(W)), W)
         W = synth.f32_to_bf16_bits(W)
-    res = oracle_lib.solve(W, fmt, 4, r_init=r0, c_init=c0)
+    res = oracle_lib.solve(W, fmt, 4, g, r_init=r0, c_init=c0)
     assert np.all(res["nmse"] == 0.0)
     assert np.array_equal(res["r"], r0) and np.array_equal(res["c"], c0)
     assert res["rejected"] == 0
