@@ -87,7 +87,9 @@ enum {
   DQ_FLAG_ZERO_ROW = 2,            /* a row had D = 0 in an r-step: its scale was kept */
   DQ_FLAG_ZERO_COL = 4,            /* a column had D = 0 in a c-step: its scale was kept */
   DQ_FLAG_NV_BLOCK_UNDERFLOW = 8,  /* an NVFP4 block scale rounded to zero (block zeroed) */
-  DQ_FLAG_NV_TENSOR_UNDERFLOW = 16 /* NVFP4 tensor scale too small: matrix quantised to 0 */
+  DQ_FLAG_NV_TENSOR_UNDERFLOW = 16 /* NVFP4 tensor scale s_t = amax/2688 so small (about
+                                      2^-119 or less) that 1/(6 s_t) or 1/(2^-9 s_t) is not a
+                                      finite fp32 number: the matrix is quantised to 0 */
 };
 
 typedef struct {
@@ -156,8 +158,10 @@ size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_sp
  *           with the new r;  a scale whose D is 0 is kept;
  *   Qhat-step  candidate FQ_f(W ./ r c^T), kept unless it raises the MSE at the current
  *           scales (so the MSE never increases);
- * where Proj is the nearest admissible value: powers of two 2^k, k in [-127,127] (MX,
- * ties up), E4M3 values in [2^-9, 448] (NVFP4), bf16 values >= 2^-126 (INT4, INT8).
+ * where Proj is the nearest admissible value: E4M3 values in [2^-9, 448] (NVFP4), bf16
+ * values in [2^-126, max bf16] with ties to even (INT4, INT8 and the MX formats, whose
+ * block scales stay E8M0 powers of two inside the quantiser: a power-of-two dual scale
+ * would be absorbed by them exactly).
  * Problems are independent; count (1..65535) > 1 runs them together on one GPU.  Blocks
  * the calling thread until done (one synchronisation of `stream` per round of sweeps: a
  * second round only follows a rejected step whose iteration has to be re-solved).  `workspace` must hold dq_workspace_bytes(...) bytes of device
@@ -277,10 +281,11 @@ const char* dq_status_string(int status);
  *   DQ_ROUND_E4M3      x >= 0 -> E4M3FN code byte (ties to even, saturating at 448)
  *   DQ_ROUND_BF16      x -> nearest bf16 value (fp32 out)
  *   DQ_ROUND_INT4      x -> nearest integer in [-7, 7], ties to even (int8 out)
- *   DQ_PROJ_POW2 / DQ_PROJ_E4M3 / DQ_PROJ_BF16   x > 0 -> projected scale (fp32 out)
+ *   DQ_PROJ_MX / DQ_PROJ_E4M3 / DQ_PROJ_BF16     x > 0 -> projected dual scale of the MX
+ *                      formats (bf16 values), NVFP4 (E4M3 values), INT4/INT8 (bf16 values)
  * Used to check the device routines against an independent implementation. */
 enum { DQ_ROUND_E2M1 = 0, DQ_ROUND_E4M3 = 1, DQ_ROUND_BF16 = 2, DQ_ROUND_INT4 = 3,
-       DQ_PROJ_POW2 = 4, DQ_PROJ_E4M3 = 5, DQ_PROJ_BF16 = 6 };
+       DQ_PROJ_MX = 4, DQ_PROJ_E4M3 = 5, DQ_PROJ_BF16 = 6 };
 int dq_debug_round(int32_t fn, const float* x, void* out, int64_t n, void* stream);
 
 #ifdef __cplusplus

@@ -35,7 +35,7 @@ CODE_BITS = {"INT4": 4, "MXINT4": 4, "MXFP4": 4, "NVFP4": 4, "INT8": 8, "MXINT8"
              "MXFP8_E4M3": 8, "MXFP8_E5M2": 8, "MXFP6_E2M3": 6, "MXFP6_E3M2": 6}
 DT = {torch.float32: 0, torch.bfloat16: 1}
 FLAGS = {1: "nonfinite", 2: "zero_row", 4: "zero_col", 8: "nv_block_underflow", 16: "nv_tensor_underflow"}
-ROUND_FN = {"e2m1": 0, "e4m3": 1, "bf16": 2, "int4": 3, "proj_pow2": 4, "proj_e4m3": 5, "proj_bf16": 6}
+ROUND_FN = {"e2m1": 0, "e4m3": 1, "bf16": 2, "int4": 3, "proj_mx": 4, "proj_e4m3": 5, "proj_bf16": 6}
 
 
 class dq_quant_spec(C.Structure):

@@ -94,16 +94,12 @@ __device__ __forceinline__ float int8_round(float x) {
 }
 
 // ---------------------------------------------------------------- scale projections
-// Nearest admissible scale to x > 0 (conference entry: scales are projected onto the
+// Nearest admissible dual scale to x > 0 (conference entry: scales are projected onto the
 // format's admissible set after each update; the nearest point is the exact minimiser of
-// the 1-D quadratic each closed-form step solves).
-__device__ __forceinline__ float proj_pow2(float x) {   // 2^k, k in [-127, 127], ties up
-  int k = __builtin_amdgcn_frexp_expf(x);               // x = m 2^k, m in [0.5, 1)
-  float m = __builtin_amdgcn_frexp_mantf(x);
-  int e = (m >= 0.75f) ? k : k - 1;
-  e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  return ldexpf(1.0f, e);
-}
+// the 1-D quadratic each closed-form step solves).  NVFP4: E4M3 values.  INT and MX
+// formats: bf16 values -- a power-of-two row scale would be absorbed exactly by the MX
+// blocks' E8M0 exponents, so the MX dual scales live in bf16 like INT4's (the pages store
+// their per-group scales in bf16); E8M0 is the block scale's set, inside the quantiser.
 __device__ __forceinline__ float proj_e4m3(float x) {   // E4M3FN values in [2^-9, 448]
   uint32_t c = e4m3_code_sat(x);
   return e4m3_value(c ? c : 1u);
@@ -115,9 +111,8 @@ __device__ __forceinline__ float proj_bf16(float x) {   // bf16 values in [2^-12
 }
 template <int FMT>
 __device__ __forceinline__ float project(float x) {
-  if (FMT == MXINT4 || FMT == MXFP4 || FMT == MXINT8 || mx_mini<FMT>()) return proj_pow2(x);
   if (FMT == NVFP4) return proj_e4m3(x);
-  return proj_bf16(x);   // INT4, INT8
+  return proj_bf16(x);   // INT4, INT8 and every MX format
 }
 
 // ---------------------------------------------------------------- cross-lane helpers

@@ -79,8 +79,6 @@ struct alignas(16) StateOut {
   uint32_t flags, pad[3];
 };
 
-constexpr float kTinyTensorScale = 7.888609052210118e-31f;  // 2^-100
-
 // ---------------------------------------------------------------- loads and stores
 // Codes of chunk l of row i: 8 bytes (4-bit formats), 12 bytes (6-bit) or 16 bytes (8-bit).
 template <int FMT, int L>
@@ -129,13 +127,18 @@ __device__ __forceinline__ void build_nvtab(NvTab& tab, float s_t) {
   }
 }
 
-// NVFP4 tensor-scale terms from the normalised matrix's amax A.
+// NVFP4 tensor-scale terms from the normalised matrix's amax A: s_t = A / 2688 and
+// k6 = 1 / (6 s_t).  The scheme divides by 6 s_t and by every block factor e4m3(sb) s_t,
+// the smallest being 2^-9 s_t; when either reciprocal is not a finite fp32 number (s_t at
+// or below about 2^-119) or s_t is 0, no block can be encoded and the matrix quantises to
+// zero (`tiny`, flag bit 16 when A > 0).
 __device__ __forceinline__ void nv_tensor_terms(float A, float& s_t, float& k6, bool& tiny) {
   s_t = A / 2688.0f;
   float six = 6.0f * s_t;
   k6 = (s_t > 0.0f) ? 1.0f / six : 0.0f;
+  const float id_min = (s_t > 0.0f) ? 1.0f / (0x1p-9f * s_t) : 0.0f;
   tiny = false;
-  if (!(s_t >= kTinyTensorScale) || !isfinite(k6)) {
+  if (!(s_t > 0.0f) || !isfinite(k6) || !isfinite(id_min)) {
     tiny = (A > 0.0f);
     s_t = 0.0f;
     k6 = 0.0f;
@@ -1358,9 +1361,9 @@ __global__ void k_debug_round(int fn, const float* __restrict__ x, void* out, in
     case 1: ((uint8_t*)out)[e] = (uint8_t)e4m3_code_sat(v); break;
     case 2: ((float*)out)[e] = bf16_rne(v); break;
     case 3: ((int8_t*)out)[e] = (int8_t)(int)int4_round(v); break;
-    case 4: ((float*)out)[e] = proj_pow2(v); break;
-    case 5: ((float*)out)[e] = proj_e4m3(v); break;
-    case 6: ((float*)out)[e] = proj_bf16(v); break;
+    case 4: ((float*)out)[e] = project<MXFP4>(v); break;
+    case 5: ((float*)out)[e] = project<NVFP4>(v); break;
+    case 6: ((float*)out)[e] = project<INT4>(v); break;
     default: break;
   }
 }

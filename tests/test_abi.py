@@ -37,10 +37,13 @@ def test_status_strings(dq):
 
 
 def _problem(dq, rows=64, cols=256, ld=None, dtype=1, W=0x10000, codes=0x20000):
-    return dq.dq_problem(W=W, w_dtype=dtype, reserved=0, rows=rows, cols=cols,
-                         ld=ld if ld is not None else cols, r_init=None, c_init=None, r=0x30000,
-                         c=0x40000, codes=codes, block_scales=0x50000, tensor_scale=0x60000,
-                         nmse_hist=None, relchg_hist=None, r_pre=None, c_pre=None, report=None)
+    kw = dict(W=W, w_dtype=dtype, reserved=0, rows=rows, cols=cols,
+              ld=ld if ld is not None else cols, r_init=None, c_init=None, r=0x30000,
+              c=0x40000, codes=codes, block_scales=0x50000, tensor_scale=0x60000,
+              nmse_hist=None, relchg_hist=None, r_trace=None, c_trace=None, report=None)
+    # ctypes keeps an unknown keyword as a plain attribute: name every field exactly
+    assert set(kw) == {f[0] for f in dq.dq_problem._fields_}
+    return dq.dq_problem(**kw)
 
 
 def _solve_rc(dq, probs, fmt=3, group=0, iters=4, ws=0x70000, wsb=1 << 40):

@@ -55,7 +55,6 @@ def test_llama31_8b_set_batched(oracle_lib):
         if Wn is None:
             continue
         print(f"[llama] oracle check layer {layer} {name} {Wn.shape}", flush=True)
-        ref = oracle_lib.solve(Wn, "NVFP4", T)
         got = {"r": p.r.cpu().numpy(), "c": p.c.cpu().numpy(),
                "codes": p.codes.cpu().numpy(),
                "scales": scales_np(p.block_scales, "NVFP4"),
@@ -63,7 +62,7 @@ def test_llama31_8b_set_batched(oracle_lib):
                "nmse": p.nmse_hist.cpu().numpy(), "relchg": p.relchg_hist.cpu().numpy(),
                "r_trace": p.r_trace.cpu().numpy(), "c_trace": p.c_trace.cpu().numpy(),
                "iters_run": rep.iters_run, "rejected": rep.rejected_steps}
-        _compare_e2e(oracle_lib, ref, got, "NVFP4", f"llama L{layer} {name}", T)
+        _compare_e2e(oracle_lib, Wn, "NVFP4", T, got, f"llama L{layer} {name}")
 
     # batch == alone, bit for bit
     k = next(i for i, m in enumerate(meta) if m[2] is not None)

@@ -46,6 +46,39 @@ def test_quantize_weights_bit_exact(oracle_lib, fmt, dtype, shape):
             assert gt.item() == np.float32(ts)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_quantize_weights_int4_group64_bit_exact(oracle_lib, dtype, shape):
+    """INT4 with 64-element groups (the listing page's INT4 setting, Tables 1, 6, 10-12)."""
+    rows, cols = shape
+    W = _w(rows, cols, dtype, 2)
+    rng = np.random.default_rng(rows * 11 + cols)
+    for with_scales in (False, True):
+        r = c = None
+        if with_scales:
+            r = oracle_lib.project("INT4", np.exp2(rng.uniform(-2, 2, rows)).astype(np.float32))
+            c = oracle_lib.project("INT4", np.exp2(rng.uniform(-2, 2, cols)).astype(np.float32))
+        codes, scales, _, _ = oracle_lib.quantize_weights(W, r, c, "INT4", 64)
+        gc, gs, _ = dq.quantize_weights(to_dev(W), None if r is None else to_dev(r),
+                                        None if c is None else to_dev(c), "INT4", group=64)
+        torch.cuda.synchronize()
+        assert gs.numel() == rows * cols // 64
+        assert np.array_equal(gc.cpu().numpy(), codes)
+        assert np.array_equal(scales_np(gs, "INT4"), scales)
+
+
+def test_rescale_quantize_acts_int4_group64(oracle_lib):
+    X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(96, 1024), 0)
+    rng = np.random.default_rng(4)
+    c = oracle_lib.project("INT4", np.exp2(rng.uniform(-3, 3, 1024)).astype(np.float32))
+    for cc in (None, c):
+        codes, scales, _, _ = oracle_lib.rescale_quantize_acts(X, cc, "INT4", 64)
+        gc, gs, _ = dq.rescale_quantize_acts(to_dev(X), None if cc is None else to_dev(cc), "INT4", group=64)
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.cpu().numpy(), codes)
+        assert np.array_equal(scales_np(gs, "INT4"), scales)
+
+
 @pytest.mark.parametrize("fmt", ALL_FORMATS)
 def test_rescale_quantize_acts_bit_exact(oracle_lib, fmt):
     X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(96, 1024), 0)

@@ -59,7 +59,7 @@ def test_bf16_and_int4(oracle_lib):
     assert np.array_equal(got, oracle_lib.int_round(y, 7))
 
 
-@pytest.mark.parametrize("fn,fmt", [("proj_pow2", "MXFP4"), ("proj_e4m3", "NVFP4"), ("proj_bf16", "INT4")])
+@pytest.mark.parametrize("fn,fmt", [("proj_mx", "MXFP4"), ("proj_e4m3", "NVFP4"), ("proj_bf16", "INT4")])
 def test_projections(oracle_lib, fn, fmt):
     rng = np.random.default_rng(2)
     x = np.exp2(rng.uniform(-135, 130, 1 << 20)).astype(np.float32)
