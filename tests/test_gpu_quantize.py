@@ -226,3 +226,27 @@ def test_k_proj_activation_sqnr(oracle_lib):
         assert np.isfinite(out[label])
     print(f"[sqnr] k_proj MXINT4 activation SQNR: {out['with beta']:.3f} dB with the column "
           f"scales, {out['without beta']:.3f} dB without", flush=True)
+
+
+def test_nvfp4_tensor_scale_limit(oracle_lib):
+    """Around the NVFP4 limit derived from fp32 arithmetic (1 / (2^-9 s_t) overflows for s_t
+    at or below about 2^-119): codes, block scales and tensor scale bit-exact with the
+    oracle on both sides of it, zero codes and flag 16 in a solve below it."""
+    rng = np.random.default_rng(8)
+    base = (rng.standard_normal((4, 64)) * 0.25).astype(np.float32)
+    edge = np.float32(2.0 ** -119) * np.float32(2688)
+    for A in (np.nextafter(edge, np.float32(0)), edge, np.nextafter(edge, np.float32(1)),
+              np.float32(edge * 1.001), np.float32(edge * 4), np.float32(2.0 ** -100), np.float32(1e-44)):
+        V = (base / np.abs(base).max() * A).astype(np.float32)
+        V[0, 0] = A
+        codes, scales, ts, _ = oracle_lib.quantize_weights(V, None, None, "NVFP4")
+        gc, gs, gt = dq.quantize_weights(to_dev(V), None, None, "NVFP4")
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.cpu().numpy(), codes), A
+        assert np.array_equal(gs.cpu().numpy(), scales), A
+        assert gt.item() == np.float32(ts), A
+    V = (base / np.abs(base).max() * np.float32(2.0 ** -112)).astype(np.float32)
+    got = dq.solve(to_dev(V), "NVFP4", 2)
+    torch.cuda.synchronize()
+    assert got["flags"] & 16
+    assert torch.count_nonzero(got["codes"]).item() == 0 and got["tscale"].item() == 0.0
