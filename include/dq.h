@@ -189,6 +189,25 @@ int dq_rescale_quantize_acts(const void* X, int32_t x_dtype, int64_t tokens, int
                              void* block_scales, float* tensor_scale, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* dq_rescale_quantize_acts for callers that cannot allocate memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments without the workspace; same outputs, bit for bit.  The call allocates nothing.
+ * The scratch it needs (NVFP4: the amax pre-pass partials; the other formats need none) is a
+ * fixed array of DQ_NOALLOC_SCRATCH_BYTES bytes that the library keeps on every GPU it runs
+ * on until the process ends; its address is looked up on the first call on each device.
+ * Every call on one GPU shares that array and leaves its contents behind: calls that may
+ * overlap on one GPU (issued to different streams without ordering between them) race and
+ * give wrong results.  The stream must belong to the current device (DQ_ERR_ARG otherwise).
+ * Returns DQ_ERR_WORKSPACE if a call would need more scratch than the array holds (no input
+ * size does: the partials never exceed 1024 floats), DQ_ERR_HIP if the array's device
+ * address cannot be obtained, and otherwise what dq_rescale_quantize_acts returns.
+ * Asynchronous. */
+#define DQ_NOALLOC_SCRATCH_BYTES 4096
+int dq_rescale_quantize_acts_noalloc(const void* X, int32_t x_dtype, int64_t tokens,
+                                     int64_t cols, int64_t ld, const float* c,
+                                     dq_quant_spec spec, uint8_t* codes, void* block_scales,
+                                     float* tensor_scale, void* stream);
+
 /* Activation rescale + quantise for several projections that read the same activations
  * (q/k/v of an attention block, gate/up of an MLP block), each with its own solved column
  * scales c_k (same passages as dq_rescale_quantize_acts: beta is applied per consuming

@@ -1,7 +1,8 @@
 """Python binding of the DualQuant dual-scale solver library (libdq.so, gfx950).
 
 The functions named like the C entry points (``dq_solve``, ``dq_quantize_weights``,
-``dq_rescale_quantize_acts``, ``dq_rescale_quantize_acts_multi``, ``dq_quantized_linear``,
+``dq_rescale_quantize_acts``, ``dq_rescale_quantize_acts_noalloc``,
+``dq_rescale_quantize_acts_multi``, ``dq_quantized_linear``,
 ``dq_dequantize``,
 ``dq_workspace_bytes``, ``dq_quantize_workspace_bytes``, ``dq_quantize_multi_workspace_bytes``,
 ``dq_status_string``, ``dq_debug_round``) only marshal
@@ -80,6 +81,8 @@ _lib.dq_quantize_weights.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, dq_q
 _lib.dq_quantize_weights.restype = C.c_int
 _lib.dq_rescale_quantize_acts.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, dq_quant_spec, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dq_rescale_quantize_acts.restype = C.c_int
+_lib.dq_rescale_quantize_acts_noalloc.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, dq_quant_spec, _vp, _vp, _vp, _vp]
+_lib.dq_rescale_quantize_acts_noalloc.restype = C.c_int
 _lib.dq_quantize_multi_workspace_bytes.argtypes = [_i64, _i64, _i32, dq_quant_spec]
 _lib.dq_quantize_multi_workspace_bytes.restype = _sz
 _lib.dq_rescale_quantize_acts_multi.argtypes = [_vp, _i32, _i64, _i64, _i64, _i32, _vp, dq_quant_spec,
@@ -96,7 +99,8 @@ _lib.dq_debug_round.argtypes = [_i32, _vp, _vp, _i64, _vp]
 _lib.dq_debug_round.restype = C.c_int
 
 EXPORTED = ("dq_workspace_bytes", "dq_solve", "dq_quantize_workspace_bytes", "dq_quantize_weights",
-            "dq_rescale_quantize_acts", "dq_quantize_multi_workspace_bytes",
+            "dq_rescale_quantize_acts", "dq_rescale_quantize_acts_noalloc",
+            "dq_quantize_multi_workspace_bytes",
             "dq_rescale_quantize_acts_multi", "dq_quantized_linear", "dq_recode_mxint4_to_mxfp6",
             "dq_dequantize",
             "dq_status_string", "dq_debug_round")
@@ -207,6 +211,16 @@ def dq_rescale_quantize_acts(X, c, spec, codes, block_scales, tensor_scale, work
                                          _ptr(codes), _ptr(block_scales), _ptr(tensor_scale),
                                          _ptr(workspace), nbytes, _stream(stream)),
            "dq_rescale_quantize_acts")
+
+
+def dq_rescale_quantize_acts_noalloc(X, c, spec, codes, block_scales, tensor_scale, stream=None):
+    """The no-workspace variant: the library's fixed per-GPU scratch array stands in for the
+    workspace, and nothing is allocated."""
+    _check(_lib.dq_rescale_quantize_acts_noalloc(_ptr(X), DT.get(X.dtype, -1), X.shape[0], X.shape[1],
+                                                 X.stride(0) if X.numel() else X.shape[1], _ptr(c),
+                                                 spec, _ptr(codes), _ptr(block_scales),
+                                                 _ptr(tensor_scale), _stream(stream)),
+           "dq_rescale_quantize_acts_noalloc")
 
 
 def dq_quantize_multi_workspace_bytes(rows: int, cols: int, count: int, spec: dq_quant_spec) -> int:

@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <vector>
 
 #include "../../include/dq.h"
@@ -528,6 +529,31 @@ int launch_quant_any(int fmt, int g, int dt, const void* X, int64_t rows, int64_
 
 constexpr int kQuantParts = 1024;
 
+// ---------------------------------------------------------------- no-allocation scratch
+// The scratch of dq_rescale_quantize_acts_noalloc: the NVFP4 amax pre-pass partials (one per
+// pre-pass workgroup, at most kQuantParts).  Every GPU the library runs on holds its own
+// copy until the process ends.  Host code never uses this name as an address: the kernels
+// get the device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[kQuantParts];
+static_assert(sizeof(scratch) == DQ_NOALLOC_SCRATCH_BYTES, "scratch size and header differ");
+constexpr int kMaxScratchDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per device.
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxScratchDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return DQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DQ_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return DQ_OK;
+}
+
 // Quantised linear layer: dynamic LDS above 64 KiB is opted into once per instantiation.
 // FP4 codes with K a multiple of 256 and FP8 codes with K a multiple of 128, with 4-byte
 // aligned scale arrays, take the direct-to-LDS ring; everything else the register-staged
@@ -884,6 +910,36 @@ int dq_rescale_quantize_acts(const void* X, int32_t x_dtype, int64_t tokens, int
                              size_t workspace_bytes, void* stream) {
   return quantize_common(1, X, x_dtype, tokens, cols, ld, nullptr, c, spec, codes, block_scales,
                          tensor_scale, workspace, workspace_bytes, stream);
+}
+
+int dq_rescale_quantize_acts_noalloc(const void* X, int32_t x_dtype, int64_t tokens,
+                                     int64_t cols, int64_t ld, const float* c,
+                                     dq_quant_spec spec, uint8_t* codes, void* block_scales,
+                                     float* tensor_scale, void* stream) {
+  // argument checks first, exactly as the workspace variant makes them
+  int g = resolve_group(spec);
+  if (g < 0) return DQ_ERR_FORMAT;
+  int rc = check_matrix(X, x_dtype, tokens, cols, ld, g);
+  if (rc) return rc;
+  if (tokens == 0 || cols == 0) return DQ_OK;
+  const size_t need = dq_quantize_workspace_bytes(tokens, cols, spec);
+  if (need > sizeof(scratch)) return DQ_ERR_WORKSPACE;
+  if (need == 0)   // this format's kernels use no scratch
+    return quantize_common(1, X, x_dtype, tokens, cols, ld, nullptr, c, spec, codes,
+                           block_scales, tensor_scale, nullptr, 0, stream);
+  // the scratch is the current device's: the stream must run there
+  int dev = -1;
+  hipDevice_t sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DQ_ERR_HIP;
+  if (stream) {
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return DQ_ERR_HIP;
+    if (sdev != dev) return DQ_ERR_ARG;
+  }
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return quantize_common(1, X, x_dtype, tokens, cols, ld, nullptr, c, spec, codes, block_scales,
+                         tensor_scale, ws, sizeof(scratch), stream);
 }
 
 size_t dq_quantize_multi_workspace_bytes(int64_t tokens, int64_t cols, int32_t count,
