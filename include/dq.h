@@ -16,8 +16,9 @@
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers owned by the caller.  The library never
  *     allocates, frees or retains them; scratch memory comes in through `workspace`.
- *   - `stream` is a hipStream_t (NULL = the default stream).  Work is stream-ordered;
- *     dq_solve additionally blocks the calling thread until the solve has finished.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every compute call only
+ *     enqueues work on it and returns; its outputs are valid once that work has completed
+ *     (an event, a stream synchronisation, or later work on the same stream).
  *   - Matrices are row-major; `ld` is the row pitch in elements (ld >= cols).  Blocks of
  *     `group` consecutive elements run along a row.  Base pointers and the row pitch in
  *     bytes must be multiples of 16.  cols must be a multiple of the group and at most
@@ -87,9 +88,11 @@ enum {
   DQ_FLAG_ZERO_ROW = 2,            /* a row had D = 0 in an r-step: its scale was kept */
   DQ_FLAG_ZERO_COL = 4,            /* a column had D = 0 in a c-step: its scale was kept */
   DQ_FLAG_NV_BLOCK_UNDERFLOW = 8,  /* an NVFP4 block scale rounded to zero (block zeroed) */
-  DQ_FLAG_NV_TENSOR_UNDERFLOW = 16 /* NVFP4 tensor scale s_t = amax/2688 so small (about
+  DQ_FLAG_NV_TENSOR_UNDERFLOW = 16, /* NVFP4 tensor scale s_t = amax/2688 so small (about
                                       2^-119 or less) that 1/(6 s_t) or 1/(2^-9 s_t) is not a
                                       finite fp32 number: the matrix is quantised to 0 */
+  DQ_FLAG_UNFINISHED = 32          /* the solve did not finish in the sweeps dq_solve queued
+                                      (never expected: T iterations need at most 2T sweeps) */
 };
 
 typedef struct {
@@ -98,16 +101,9 @@ typedef struct {
 } dq_quant_spec;
 
 typedef struct {
-  int32_t iters;     /* BCD iterations T >= 0 */
+  int32_t iters;     /* BCD iterations T, 0 <= T <= 65536 */
   float tol_relchg;  /* > 0: stop after the first iteration whose relative change of Qhat is
                         <= tol_relchg; 0: run all T iterations */
-  float* pass_ms;     /* HOST array or NULL: per sweep over W, three durations in ms -- the
-                          row pass, the column pass, and the column finalize plus the
-                          safeguard decision (all problems of the call) -- from HIP event
-                          pairs attached to the kernel launches on `stream` (kernel begin
-                          and end) */
-  int32_t pass_ms_capacity;  /* sweeps that fit in pass_ms (3 floats each) */
-  int32_t pass_ms_count;     /* out: sweeps written */
   int32_t scale_steps;  /* which scale steps run: DQ_STEP_ROW | DQ_STEP_COL, 0 = both.  With
                            one bit the other scale vector stays at its initial value and its
                            trace rows stay NaN (the news summary's ablation: row scales only
@@ -117,7 +113,7 @@ typedef struct {
 #define DQ_STEP_ROW 1
 #define DQ_STEP_COL 2
 
-typedef struct {
+typedef struct {           /* written to DEVICE memory by the solve's last kernel */
   int32_t iters_run;       /* iterations completed */
   int32_t rejected_steps;  /* Qhat-steps whose candidate was not kept (it would raise the MSE) */
   uint32_t flags;          /* DQ_FLAG_* */
@@ -141,7 +137,8 @@ typedef struct {
   double* relchg_hist;  /* out [iters+1] or NULL: ||Qhat_t - Qhat_{t-1}|| / ||Qhat_{t-1}||, [0] = 0 */
   float* r_trace;       /* out [iters][rows] or NULL: each r-step's closed form N/D before projection (NaN if D = 0) */
   float* c_trace;       /* out [iters][cols] or NULL: each c-step's closed form N/D before projection (NaN if D = 0) */
-  dq_report* report;    /* HOST pointer or NULL: filled when dq_solve returns */
+  dq_report* report;    /* DEVICE pointer (4-byte aligned) or NULL: written by the solve's
+                           last kernel, valid when the solve's work on `stream` has completed */
 } dq_problem;
 
 /* Bytes of workspace dq_solve needs for this batch (0 on invalid arguments). */
@@ -162,12 +159,27 @@ size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_sp
  * values in [2^-126, max bf16] with ties to even (INT4, INT8 and the MX formats, whose
  * block scales stay E8M0 powers of two inside the quantiser: a power-of-two dual scale
  * would be absorbed by them exactly).
- * Problems are independent; count (1..65535) > 1 runs them together on one GPU.  Blocks
- * the calling thread until done (one synchronisation of `stream` per round of sweeps: a
- * second round only follows a rejected step whose iteration has to be re-solved).  `workspace` must hold dq_workspace_bytes(...) bytes of device
- * memory; its contents on entry do not matter. */
+ * Problems are independent; count (1..65535) > 1 runs them together on one GPU.
+ * Stream-ordered: the call uploads the problem descriptors (staged before it returns),
+ * enqueues every sweep the solve may need -- the INIT sweep, one per iteration and one
+ * re-solve after each rejected step, at most 2T -- and the output kernel, and returns without
+ * waiting.  The number of sweeps that actually run depends on the data; the queued ones
+ * that find every problem finished exit at once.  `workspace` must hold
+ * dq_workspace_bytes(...) bytes of device memory; its contents on entry do not matter, and
+ * it must stay untouched until the solve's work has completed. */
 int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
-             dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream);
+             const dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Diagnostic: dq_solve with a begin/end HIP event pair attached to each pass's kernel
+ * launches -- the row pass, the column pass, and the column finalize plus the safeguard
+ * decision (all problems of the call) -- of each queued sweep.  Synchronises `stream` before
+ * returning and writes three durations in ms per sweep to the HOST array pass_ms
+ * (pass_ms_capacity sweeps at most; *pass_ms_count = sweeps written).  Sweeps beyond the
+ * report's `sweeps` ran no work.  Same outputs as dq_solve. */
+int dq_solve_timed(const dq_problem* problems, int32_t count, dq_quant_spec spec,
+                   const dq_solve_opts* opts, void* workspace, size_t workspace_bytes,
+                   void* stream, float* pass_ms, int32_t pass_ms_capacity,
+                   int32_t* pass_ms_count);
 
 /* Bytes of workspace dq_quantize_weights / dq_rescale_quantize_acts need. */
 size_t dq_quantize_workspace_bytes(int64_t rows, int64_t cols, dq_quant_spec spec);

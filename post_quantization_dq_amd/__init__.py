@@ -48,9 +48,7 @@ DQ_MAX_MULTI = 8                   # outputs of one dq_rescale_quantize_acts_mul
 
 
 class dq_solve_opts(C.Structure):
-    _fields_ = [("iters", C.c_int32), ("tol_relchg", C.c_float),
-                ("pass_ms", C.POINTER(C.c_float)), ("pass_ms_capacity", C.c_int32),
-                ("pass_ms_count", C.c_int32), ("scale_steps", C.c_int32)]
+    _fields_ = [("iters", C.c_int32), ("tol_relchg", C.c_float), ("scale_steps", C.c_int32)]
 
 
 class dq_report(C.Structure):
@@ -65,7 +63,7 @@ class dq_problem(C.Structure):
                 ("c", C.c_void_p), ("codes", C.c_void_p), ("block_scales", C.c_void_p),
                 ("tensor_scale", C.c_void_p), ("nmse_hist", C.c_void_p),
                 ("relchg_hist", C.c_void_p), ("r_trace", C.c_void_p), ("c_trace", C.c_void_p),
-                ("report", C.POINTER(dq_report))]
+                ("report", C.c_void_p)]
 
 
 _vp, _i32, _i64, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
@@ -75,6 +73,9 @@ _lib.dq_workspace_bytes.argtypes = [C.POINTER(dq_problem), _i32, dq_quant_spec, 
 _lib.dq_workspace_bytes.restype = _sz
 _lib.dq_solve.argtypes = [C.POINTER(dq_problem), _i32, dq_quant_spec, C.POINTER(dq_solve_opts), _vp, _sz, _vp]
 _lib.dq_solve.restype = C.c_int
+_lib.dq_solve_timed.argtypes = [C.POINTER(dq_problem), _i32, dq_quant_spec, C.POINTER(dq_solve_opts), _vp,
+                                _sz, _vp, C.POINTER(C.c_float), _i32, C.POINTER(C.c_int32)]
+_lib.dq_solve_timed.restype = C.c_int
 _lib.dq_quantize_workspace_bytes.argtypes = [_i64, _i64, dq_quant_spec]
 _lib.dq_quantize_workspace_bytes.restype = _sz
 _lib.dq_quantize_weights.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, dq_quant_spec, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -98,7 +99,8 @@ _lib.dq_dequantize.restype = C.c_int
 _lib.dq_debug_round.argtypes = [_i32, _vp, _vp, _i64, _vp]
 _lib.dq_debug_round.restype = C.c_int
 
-EXPORTED = ("dq_workspace_bytes", "dq_solve", "dq_quantize_workspace_bytes", "dq_quantize_weights",
+EXPORTED = ("dq_workspace_bytes", "dq_solve", "dq_solve_timed", "dq_quantize_workspace_bytes",
+            "dq_quantize_weights",
             "dq_rescale_quantize_acts", "dq_rescale_quantize_acts_noalloc",
             "dq_quantize_multi_workspace_bytes",
             "dq_rescale_quantize_acts_multi", "dq_quantized_linear", "dq_recode_mxint4_to_mxfp6",
@@ -155,8 +157,9 @@ class Problem:
     relchg_hist: torch.Tensor | None = None
     r_trace: torch.Tensor | None = None
     c_trace: torch.Tensor | None = None
+    report: torch.Tensor | None = None   # int32 [4] on the device: a dq_report
 
-    def to_c(self, report: dq_report | None) -> dq_problem:
+    def to_c(self) -> dq_problem:
         W = self.W
         rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (0, 0)
         return dq_problem(
@@ -166,29 +169,48 @@ class Problem:
             codes=_ptr(self.codes), block_scales=_ptr(self.block_scales),
             tensor_scale=_ptr(self.tensor_scale), nmse_hist=_ptr(self.nmse_hist),
             relchg_hist=_ptr(self.relchg_hist), r_trace=_ptr(self.r_trace), c_trace=_ptr(self.c_trace),
-            report=C.pointer(report) if report is not None else None)
+            report=_ptr(self.report))
 
 
-def _problem_array(problems, reports):
+def _problem_array(problems):
     arr = (dq_problem * len(problems))()
     for k, p in enumerate(problems):
-        arr[k] = p.to_c(reports[k] if reports is not None else None)
+        arr[k] = p.to_c()
     return arr
 
 
 def dq_workspace_bytes(problems, spec: dq_quant_spec, opts: dq_solve_opts) -> int:
-    arr = _problem_array(problems, None)
+    arr = _problem_array(problems)
     return int(_lib.dq_workspace_bytes(arr, len(problems), spec, C.byref(opts)))
 
 
 def dq_solve(problems, spec: dq_quant_spec, opts: dq_solve_opts, workspace: torch.Tensor,
-             stream=None) -> list[dq_report]:
-    reports = [dq_report() for _ in problems]
-    arr = _problem_array(problems, reports)
+             stream=None) -> None:
+    """Enqueues the solve on the stream and returns; each problem's `report` tensor holds its
+    dq_report once the stream's work has completed."""
+    arr = _problem_array(problems)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.dq_solve(arr, len(problems), spec, C.byref(opts), _ptr(workspace), nbytes,
                          _stream(stream)), "dq_solve")
-    return reports
+
+
+def dq_solve_timed(problems, spec: dq_quant_spec, opts: dq_solve_opts, workspace: torch.Tensor,
+                   capacity: int, stream=None) -> list[tuple[float, float, float]]:
+    """The diagnostic variant: (row pass, column pass, finalize) durations in ms per queued
+    sweep, read after the library synchronises the stream."""
+    arr = _problem_array(problems)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    buf = (C.c_float * (3 * max(1, capacity)))()
+    n = C.c_int32(0)
+    _check(_lib.dq_solve_timed(arr, len(problems), spec, C.byref(opts), _ptr(workspace), nbytes,
+                               _stream(stream), buf, int(capacity), C.byref(n)), "dq_solve_timed")
+    return [tuple(float(buf[3 * k + q]) for q in range(3)) for k in range(n.value)]
+
+
+def read_report(problem: Problem) -> dq_report:
+    """The problem's dq_report, copied from the device (waits for the solve)."""
+    a = problem.report.cpu().numpy()
+    return dq_report(int(a[0]), int(a[1]), int(a[2]) & 0xFFFFFFFF, int(a[3]))
 
 
 def dq_quantize_workspace_bytes(rows: int, cols: int, spec: dq_quant_spec) -> int:
@@ -292,34 +314,36 @@ def make_problem(W: torch.Tensor, fmt: str, iters: int, group: int | None = None
         nmse_hist=torch.zeros(iters + 1, dtype=torch.float64, device=dev),
         relchg_hist=torch.zeros(iters + 1, dtype=torch.float64, device=dev),
         r_trace=torch.full((max(iters, 1), rows), float("nan"), device=dev) if trace else None,
-        c_trace=torch.full((max(iters, 1), cols), float("nan"), device=dev) if trace else None)
+        c_trace=torch.full((max(iters, 1), cols), float("nan"), device=dev) if trace else None,
+        report=torch.zeros(4, dtype=torch.int32, device=dev))
 
 
 def solve_many(problems, fmt: str, iters: int, group: int | None = None, tol: float = 0.0,
                stream=None, workspace: torch.Tensor | None = None, pass_ms: list | None = None,
-               steps: int = 0):
-    """Solve a batch of problems.  `workspace` may be passed in to reuse one allocation;
-    when `pass_ms` is a list it receives one (row pass, column pass, finalize) tuple of
-    event-timed durations in ms per sweep over W.  `steps` selects the scale steps
-    (DQ_STEP_ROW | DQ_STEP_COL; 0 = both)."""
+               steps: int = 0, read_reports: bool = True):
+    """Solve a batch of problems.  `workspace` may be passed in to reuse one allocation.
+    When `pass_ms` is a list, the diagnostic dq_solve_timed runs instead and appends one
+    (row pass, column pass, finalize) tuple of event-timed durations in ms per sweep that did
+    work.  `steps` selects the scale steps (DQ_STEP_ROW | DQ_STEP_COL; 0 = both).  Returns
+    the reports read back from the device (a synchronisation), or None with
+    read_reports=False (the solve is then only enqueued)."""
     spec = spec_of(fmt, group)
-    opts = dq_solve_opts(int(iters), float(tol), None, 0, 0, int(steps))
-    buf = None
-    if pass_ms is not None:
-        cap = 2 * int(iters) + 2
-        buf = (C.c_float * (3 * cap))()
-        opts.pass_ms = C.cast(buf, C.POINTER(C.c_float))
-        opts.pass_ms_capacity = cap
+    opts = dq_solve_opts(int(iters), float(tol), int(steps))
     nbytes = dq_workspace_bytes(problems, spec, opts)
     if nbytes == 0:
         raise DQError(-7, "dq_workspace_bytes")
     ws = workspace
     if ws is None or ws.numel() * ws.element_size() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=problems[0].W.device)
-    reps = dq_solve(problems, spec, opts, ws, stream)
     if pass_ms is not None:
-        pass_ms.extend(tuple(float(buf[3 * k + q]) for q in range(3)) for k in range(opts.pass_ms_count))
-    return reps
+        per = dq_solve_timed(problems, spec, opts, ws, 2 * int(iters) + 2, stream)
+        ran = max(read_report(p).sweeps for p in problems)
+        pass_ms.extend(per[:ran])
+    else:
+        dq_solve(problems, spec, opts, ws, stream)
+    if not read_reports:
+        return None
+    return [read_report(p) for p in problems]
 
 
 def solve(W: torch.Tensor, fmt: str, iters: int, group: int | None = None, r_init=None,

@@ -37,6 +37,13 @@ struct alignas(16) State {
   double normW2, qn2_acc;
 };
 
+// A solve's report as it lands in the caller's device memory (the layout of dq_report).
+struct ReportDev {
+  int32_t iters_run, rejected_steps;
+  uint32_t flags;
+  int32_t sweeps;
+};
+
 struct ProbDev {
   const void* W;
   int64_t rows, cols, ld;
@@ -61,6 +68,7 @@ struct ProbDev {
   float* r_out;     // the caller's outputs: final r [rows], c [cols], NVFP4 tensor scale [1]
   float* c_out;
   float* ts_out;    // null outside NVFP4
+  ReportDev* report;   // the caller's device report, or null
   int32_t rowblocks, rows_per_blk, fin_wgs, iters;   // row pass: blocks of rows per workgroup
   int32_t nstrips, rranges, rows_per_range, init_wgs; // column pass: 1024-column strips x row ranges
   int32_t dtype;
@@ -73,11 +81,9 @@ struct WgEntry {
   int32_t prob, idx;
 };
 
-// A problem's state and flags as the host reads them after a round of sweeps.
-struct alignas(16) StateOut {
-  State st;
-  uint32_t flags, pad[3];
-};
+// Flag bit of a solve whose state did not reach DONE within the sweeps that were queued
+// (cannot happen: a solve of T iterations needs at most 2T sweeps).
+constexpr uint32_t kFlagUnfinished = 32u;
 
 // ---------------------------------------------------------------- loads and stores
 // Codes of chunk l of row i: 8 bytes (4-bit formats), 12 bytes (6-bit) or 16 bytes (8-bit).
@@ -395,7 +401,9 @@ struct PassInfo {
 // stay in L2) instead of LDS.
 template <int FMT, int DT, int L, int CG>
 __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ probs,
-                                                  const WgEntry* __restrict__ table, int sw) {
+                                                  const WgEntry* __restrict__ table, int sw,
+                                                  const int32_t* __restrict__ live) {
+  if (*gp(live) == 0) return;   // every problem finished: this queued sweep has nothing to do
   const WgEntry we = table[blockIdx.x];
   const ProbDev& P = probs[we.prob];
   State* st = P.st + (sw & 1);
@@ -625,7 +633,9 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
 // budget.
 template <int FMT, int DT, int L>
 __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
-                                             const WgEntry* __restrict__ table, int sw) {
+                                             const WgEntry* __restrict__ table, int sw,
+                                             const int32_t* __restrict__ live) {
+  if (*gp(live) == 0) return;
   const WgEntry we = table[blockIdx.x];
   const ProbDev& P = probs[we.prob];
   const State* st = P.st + (sw & 1);
@@ -741,14 +751,16 @@ __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
 
 template <int FMT, int DT, int L>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_colpass(
-    const ProbDev* __restrict__ probs, const WgEntry* __restrict__ table, int sw) {
-  colpass_body<FMT, DT, L>(probs, table, sw);
+    const ProbDev* __restrict__ probs, const WgEntry* __restrict__ table, int sw,
+    const int32_t* __restrict__ live) {
+  colpass_body<FMT, DT, L>(probs, table, sw, live);
 }
 
 template <int FMT, int DT, int L>
 __global__ __launch_bounds__(512) void k_colpass_wide(const ProbDev* __restrict__ probs,
-                                                      const WgEntry* __restrict__ table, int sw) {
-  colpass_body<FMT, DT, L>(probs, table, sw);
+                                                      const WgEntry* __restrict__ table, int sw,
+                                                      const int32_t* __restrict__ live) {
+  colpass_body<FMT, DT, L>(probs, table, sw, live);
 }
 
 // ---------------------------------------------------------------- finalize
@@ -761,7 +773,11 @@ __global__ __launch_bounds__(512) void k_colpass_wide(const ProbDev* __restrict_
 // reduced by the next row pass.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ probs,
-                                                  const WgEntry* __restrict__ table, int sw) {
+                                                  const WgEntry* __restrict__ table, int sw,
+                                                  int32_t* __restrict__ live) {
+  // Once every problem is DONE the state slots are no longer read (the outputs kernel reads
+  // the slot of the last sweep a problem ran, recorded in its state), so nothing is carried.
+  if (*gp(live) == 0) return;
   const WgEntry we = table[blockIdx.x];
   const ProbDev& P = probs[we.prob];
   const State* st = P.st + (sw & 1);
@@ -909,6 +925,10 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   ns.needs_ts = 0;
   if (stop) {
     ns.mode = MODE_DONE;
+    ns.sweeps += 1;
+    *sn = ns;
+    atomicSub(live, 1);   // after the state: a later sweep that sees 0 reads no state
+    return;
   } else if (accepted) {
     ns.rs = 1 - st->rs;
     ns.cs = 1 - st->cs;
@@ -922,13 +942,11 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
 }
 
 // ---------------------------------------------------------------- outputs
-// After a round of sweeps: every problem's current state (slot `slot`) and flags go to
-// out[problem], so the host reads all of them in one copy, and a finished problem gets its
-// final r, c, NVFP4 tensor scale and, when its kept Qhat is in the second code buffer, its
-// codes and block scales copied into the caller's buffers.  (A problem that needs more
-// sweeps is copied after its last one; the first code buffer is the caller's, so a copy
-// into it is only made once nothing reads it any more.)  Grid: x = workgroups per problem,
-// y = problem; empty problems have no state and are skipped.
+// After the queued sweeps: each problem's final r, c, NVFP4 tensor scale and, when its kept
+// Qhat is in the second code buffer, its codes and block scales go to the caller's buffers,
+// and its report to the caller's device report.  The final state is the slot whose mode is
+// DONE (the decision that finished a problem wrote it; later sweeps that still ran for other
+// problems copied it to the other slot too).  Grid: x = workgroups per problem, y = problem.
 __device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, int64_t bytes,
                                            int64_t tid, int64_t nthr) {
   const int64_t n16 = bytes >> 4;   // both buffers are 16-byte aligned
@@ -946,19 +964,30 @@ __device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, int
   for (int64_t b = 16 * n16 + tid; b < bytes; b += nthr) gp(dst)[b] = gp(src)[b];
 }
 
-__global__ __launch_bounds__(256) void k_outputs(const ProbDev* __restrict__ probs, int slot,
-                                                 int code_bits, int scale_bytes, int g,
-                                                 StateOut* __restrict__ out) {
+__device__ __forceinline__ void write_report(ReportDev* rep, int32_t iters_run, int32_t rejected,
+                                             uint32_t flags, int32_t sweeps) {
+  DQ_GAS int32_t* q = gp((int32_t*)rep);   // 4-byte aligned: four word stores
+  q[0] = iters_run;
+  q[1] = rejected;
+  q[2] = (int32_t)flags;
+  q[3] = sweeps;
+}
+
+__global__ __launch_bounds__(256) void k_outputs(const ProbDev* __restrict__ probs,
+                                                 int code_bits, int scale_bytes, int g) {
   const ProbDev& P = probs[blockIdx.y];
-  if (!P.st) return;
-  const State s = P.st[slot];
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
-  if (tid == 0) {
-    out[blockIdx.y].st = s;
-    out[blockIdx.y].flags = *gp(P.flags);
+  if (!P.st) {   // an empty problem: all iterations "run", nothing else to write
+    if (tid == 0 && P.report) write_report(P.report, P.iters, 0, 0u, 0);
+    return;
   }
-  if (s.mode != MODE_DONE) return;
+  const bool d0 = P.st[0].mode == MODE_DONE, d1 = P.st[1].mode == MODE_DONE;
+  const State s = P.st[(d0 || !d1) ? 0 : 1];
+  if (tid == 0 && P.report) {
+    const uint32_t fl = *gp(P.flags) | ((d0 || d1) ? 0u : kFlagUnfinished);
+    write_report(P.report, s.it_done, s.rejected, fl, s.sweeps);
+  }
   for (int64_t i = tid; i < P.rows; i += nthr) gp(P.r_out)[i] = gp(P.r[s.rs])[i];
   for (int64_t j = tid; j < P.cols; j += nthr) gp(P.c_out)[j] = gp(P.c[s.cs])[j];
   if (tid == 0 && P.ts_out) *gp(P.ts_out) = s.st_acc;

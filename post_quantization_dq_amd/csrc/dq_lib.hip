@@ -101,6 +101,8 @@ constexpr int64_t kMaxRowRanges = 64;
 // Caps for large batches: many workgroups of bounded size keep the last wave of workgroups
 // short; a single projection-sized matrix stays below both.
 constexpr int64_t kMaxRowsPerBlk = 256;
+// Iterations per solve: the queued sweeps (2 T) and the history buffers stay modest.
+constexpr int kMaxIters = 1 << 16;
 constexpr int64_t kMaxRowsPerRange = 512;
 // Standalone quantiser geometry: one chunk per lane, up to 1024 threads; rows wider than
 // 16384 columns take several passes of 1024 chunks.
@@ -145,7 +147,10 @@ struct Plan {
     size_t row_off, col_off, fin_off;  // offsets of the tables in the workspace
   };
   std::vector<Group> groups;
-  size_t probs_off = 0, sout_off = 0, total = 0;   // [probs_off, sout_off): uploaded at once
+  // [live_off, up_end): uploaded at once -- the live-problem counter, the problem
+  // descriptors and every launch table
+  size_t live_off = 0, probs_off = 0, up_end = 0, total = 0;
+  int32_t live = 0;   // problems with work (rows and cols > 0)
   std::vector<size_t> prob_off;
 };
 
@@ -231,6 +236,10 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     G.fin.push_back(WgEntry{k, d.fin_wgs});   // the decision workgroup, dispatched first
     for (int f = 0; f < d.fin_wgs; ++f) G.fin.push_back(WgEntry{k, f});
   }
+  pl.live = 0;
+  for (int k = 0; k < count; ++k) pl.live += pl.group_of[k] >= 0 ? 1 : 0;
+  pl.live_off = off;
+  off = align_up(off + sizeof(int32_t));
   pl.probs_off = off;
   off = align_up(off + sizeof(ProbDev) * std::max(1, (int)count));
   for (auto& G : pl.groups) {
@@ -241,15 +250,19 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     G.fin_off = off;
     off = align_up(off + sizeof(WgEntry) * G.fin.size());
   }
-  pl.sout_off = off;
-  off = align_up(off + sizeof(StateOut) * std::max(1, (int)count));
+  pl.up_end = off;
   pl.total = off;
   return DQ_OK;
 }
 
 void bind_pointers(const dq_problem* p, int32_t count, int g, int fmt, int iters, char* ws,
                    Plan& pl) {
+  static_assert(sizeof(ReportDev) == sizeof(dq_report) &&
+                    offsetof(ReportDev, flags) == offsetof(dq_report, flags) &&
+                    offsetof(ReportDev, sweeps) == offsetof(dq_report, sweeps),
+                "device report layout differs from dq_report");
   for (int k = 0; k < count; ++k) {
+    pl.dev[k].report = (ReportDev*)p[k].report;
     if (pl.group_of[k] < 0) continue;
     ProbDev& d = pl.dev[k];
     char* q = ws + pl.prob_off[k];
@@ -313,38 +326,38 @@ bool lds_limit(const void* kernel, int bytes) {
 
 template <int FMT, int DT, int L>
 int launch_passes(const Plan::Group& G, const ProbDev* probs, const WgEntry* rtab,
-                  const WgEntry* ctab, hipStream_t s, int sw) {
+                  const WgEntry* ctab, hipStream_t s, int sw, int32_t* live) {
   const size_t rl = rowpass_lds(FMT, G.cols);
   if (rowpass_cg(FMT, G.cols))
     launch_timed(k_rowpass<FMT, DT, L, 1>, dim3((unsigned)G.row.size()), dim3(kRowWaves * 64), rl,
-                 s, probs, rtab, sw);
+                 s, probs, rtab, sw, (const int32_t*)live);
   else
     launch_timed(k_rowpass<FMT, DT, L, 0>, dim3((unsigned)G.row.size()), dim3(kRowWaves * 64), rl,
-                 s, probs, rtab, sw);
+                 s, probs, rtab, sw, (const int32_t*)live);
   if (hipGetLastError() != hipSuccess) return DQ_ERR_HIP;
   return DQ_OK;
 }
 
 template <int FMT, int DT, int L>
 int launch_colpass(const Plan::Group& G, const ProbDev* probs, const WgEntry* ctab, hipStream_t s,
-                   int sw) {
+                   int sw, int32_t* live) {
   if constexpr (grouped_int<FMT>())
     launch_timed(k_colpass_wide<FMT, DT, L>, dim3((unsigned)G.col.size()), dim3(512),
-                 colpass_lds(FMT), s, probs, ctab, sw);
+                 colpass_lds(FMT), s, probs, ctab, sw, (const int32_t*)live);
   else
     launch_timed(k_colpass<FMT, DT, L>, dim3((unsigned)G.col.size()), dim3(512), colpass_lds(FMT),
-                 s, probs, ctab, sw);
+                 s, probs, ctab, sw, (const int32_t*)live);
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
 template <int FMT, int L>
 int launch_pass_dt(int which, const Plan::Group& G, const ProbDev* probs, const WgEntry* rtab,
-                   const WgEntry* ctab, hipStream_t s, int sw) {
+                   const WgEntry* ctab, hipStream_t s, int sw, int32_t* live) {
   if (which == 0)
-    return G.dtype == DQ_F32 ? launch_passes<FMT, 0, L>(G, probs, rtab, ctab, s, sw)
-                             : launch_passes<FMT, 1, L>(G, probs, rtab, ctab, s, sw);
-  return G.dtype == DQ_F32 ? launch_colpass<FMT, 0, L>(G, probs, ctab, s, sw)
-                           : launch_colpass<FMT, 1, L>(G, probs, ctab, s, sw);
+    return G.dtype == DQ_F32 ? launch_passes<FMT, 0, L>(G, probs, rtab, ctab, s, sw, live)
+                             : launch_passes<FMT, 1, L>(G, probs, rtab, ctab, s, sw, live);
+  return G.dtype == DQ_F32 ? launch_colpass<FMT, 0, L>(G, probs, ctab, s, sw, live)
+                           : launch_colpass<FMT, 1, L>(G, probs, ctab, s, sw, live);
 }
 
 // Dynamic LDS limits of a group's pass kernels (set once per solve, before the launches).
@@ -387,39 +400,40 @@ int prepare_passes_any(int fmt, int g, const Plan::Group& G) {
 
 // which = 0: row pass, 1: column pass
 int launch_pass_any(int which, int fmt, int g, const Plan::Group& G, const ProbDev* probs,
-                    const WgEntry* rtab, const WgEntry* ctab, hipStream_t s, int sw) {
+                    const WgEntry* rtab, const WgEntry* ctab, hipStream_t s, int sw,
+                    int32_t* live) {
   switch (fmt) {
     case DQ_FMT_INT4:
-      return g == 64 ? launch_pass_dt<INT4, 4>(which, G, probs, rtab, ctab, s, sw)
-                     : launch_pass_dt<INT4, 8>(which, G, probs, rtab, ctab, s, sw);
+      return g == 64 ? launch_pass_dt<INT4, 4>(which, G, probs, rtab, ctab, s, sw, live)
+                     : launch_pass_dt<INT4, 8>(which, G, probs, rtab, ctab, s, sw, live);
     case DQ_FMT_INT8:
-      return g == 64 ? launch_pass_dt<INT8, 4>(which, G, probs, rtab, ctab, s, sw)
-                     : launch_pass_dt<INT8, 8>(which, G, probs, rtab, ctab, s, sw);
-    case DQ_FMT_MXINT4: return launch_pass_dt<MXINT4, 2>(which, G, probs, rtab, ctab, s, sw);
-    case DQ_FMT_MXINT8: return launch_pass_dt<MXINT8, 2>(which, G, probs, rtab, ctab, s, sw);
-    case DQ_FMT_MXFP8_E4M3: return launch_pass_dt<MXFP8_E4M3, 2>(which, G, probs, rtab, ctab, s, sw);
-    case DQ_FMT_MXFP8_E5M2: return launch_pass_dt<MXFP8_E5M2, 2>(which, G, probs, rtab, ctab, s, sw);
-    case DQ_FMT_MXFP6_E2M3: return launch_pass_dt<MXFP6_E2M3, 2>(which, G, probs, rtab, ctab, s, sw);
-    case DQ_FMT_MXFP6_E3M2: return launch_pass_dt<MXFP6_E3M2, 2>(which, G, probs, rtab, ctab, s, sw);
-    case DQ_FMT_MXFP4: return launch_pass_dt<MXFP4, 2>(which, G, probs, rtab, ctab, s, sw);
-    default: return launch_pass_dt<NVFP4, 1>(which, G, probs, rtab, ctab, s, sw);
+      return g == 64 ? launch_pass_dt<INT8, 4>(which, G, probs, rtab, ctab, s, sw, live)
+                     : launch_pass_dt<INT8, 8>(which, G, probs, rtab, ctab, s, sw, live);
+    case DQ_FMT_MXINT4: return launch_pass_dt<MXINT4, 2>(which, G, probs, rtab, ctab, s, sw, live);
+    case DQ_FMT_MXINT8: return launch_pass_dt<MXINT8, 2>(which, G, probs, rtab, ctab, s, sw, live);
+    case DQ_FMT_MXFP8_E4M3: return launch_pass_dt<MXFP8_E4M3, 2>(which, G, probs, rtab, ctab, s, sw, live);
+    case DQ_FMT_MXFP8_E5M2: return launch_pass_dt<MXFP8_E5M2, 2>(which, G, probs, rtab, ctab, s, sw, live);
+    case DQ_FMT_MXFP6_E2M3: return launch_pass_dt<MXFP6_E2M3, 2>(which, G, probs, rtab, ctab, s, sw, live);
+    case DQ_FMT_MXFP6_E3M2: return launch_pass_dt<MXFP6_E3M2, 2>(which, G, probs, rtab, ctab, s, sw, live);
+    case DQ_FMT_MXFP4: return launch_pass_dt<MXFP4, 2>(which, G, probs, rtab, ctab, s, sw, live);
+    default: return launch_pass_dt<NVFP4, 1>(which, G, probs, rtab, ctab, s, sw, live);
   }
 }
 
 int launch_finalize_any(int fmt, const Plan::Group& G, const ProbDev* probs,
-                        const WgEntry* tab, hipStream_t s, int sw) {
+                        const WgEntry* tab, hipStream_t s, int sw, int32_t* live) {
   dim3 grid((unsigned)G.fin.size()), block(256);
   switch (fmt) {
-    case DQ_FMT_INT4: launch_timed(k_finalize<INT4>, grid, block, 0, s, probs, tab, sw); break;
-    case DQ_FMT_INT8: launch_timed(k_finalize<INT8>, grid, block, 0, s, probs, tab, sw); break;
-    case DQ_FMT_MXINT8: launch_timed(k_finalize<MXINT8>, grid, block, 0, s, probs, tab, sw); break;
-    case DQ_FMT_MXFP8_E4M3: launch_timed(k_finalize<MXFP8_E4M3>, grid, block, 0, s, probs, tab, sw); break;
-    case DQ_FMT_MXFP8_E5M2: launch_timed(k_finalize<MXFP8_E5M2>, grid, block, 0, s, probs, tab, sw); break;
-    case DQ_FMT_MXFP6_E2M3: launch_timed(k_finalize<MXFP6_E2M3>, grid, block, 0, s, probs, tab, sw); break;
-    case DQ_FMT_MXFP6_E3M2: launch_timed(k_finalize<MXFP6_E3M2>, grid, block, 0, s, probs, tab, sw); break;
-    case DQ_FMT_MXINT4: launch_timed(k_finalize<MXINT4>, grid, block, 0, s, probs, tab, sw); break;
-    case DQ_FMT_MXFP4: launch_timed(k_finalize<MXFP4>, grid, block, 0, s, probs, tab, sw); break;
-    default: launch_timed(k_finalize<NVFP4>, grid, block, 0, s, probs, tab, sw); break;
+    case DQ_FMT_INT4: launch_timed(k_finalize<INT4>, grid, block, 0, s, probs, tab, sw, live); break;
+    case DQ_FMT_INT8: launch_timed(k_finalize<INT8>, grid, block, 0, s, probs, tab, sw, live); break;
+    case DQ_FMT_MXINT8: launch_timed(k_finalize<MXINT8>, grid, block, 0, s, probs, tab, sw, live); break;
+    case DQ_FMT_MXFP8_E4M3: launch_timed(k_finalize<MXFP8_E4M3>, grid, block, 0, s, probs, tab, sw, live); break;
+    case DQ_FMT_MXFP8_E5M2: launch_timed(k_finalize<MXFP8_E5M2>, grid, block, 0, s, probs, tab, sw, live); break;
+    case DQ_FMT_MXFP6_E2M3: launch_timed(k_finalize<MXFP6_E2M3>, grid, block, 0, s, probs, tab, sw, live); break;
+    case DQ_FMT_MXFP6_E3M2: launch_timed(k_finalize<MXFP6_E3M2>, grid, block, 0, s, probs, tab, sw, live); break;
+    case DQ_FMT_MXINT4: launch_timed(k_finalize<MXINT4>, grid, block, 0, s, probs, tab, sw, live); break;
+    case DQ_FMT_MXFP4: launch_timed(k_finalize<MXFP4>, grid, block, 0, s, probs, tab, sw, live); break;
+    default: launch_timed(k_finalize<NVFP4>, grid, block, 0, s, probs, tab, sw, live); break;
   }
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
@@ -664,16 +678,16 @@ const char* dq_status_string(int status) {
 
 static int validate_solve(const dq_problem* p, int32_t count, dq_quant_spec spec,
                           const dq_solve_opts* o, int* g_out) {
-  if (o && o->pass_ms && o->pass_ms_capacity < 0) return DQ_ERR_ARG;
   if (!p || !o) return DQ_ERR_NULL;
   if (count < 1 || count > 65535) return DQ_ERR_ARG;   // problems index the grid's y dimension
   int g = resolve_group(spec);
   if (g < 0) return DQ_ERR_FORMAT;
-  if (o->iters < 0 || !(o->tol_relchg >= 0.0f)) return DQ_ERR_ARG;
+  if (o->iters < 0 || o->iters > kMaxIters || !(o->tol_relchg >= 0.0f)) return DQ_ERR_ARG;
   if (o->scale_steps < 0 || o->scale_steps > (DQ_STEP_ROW | DQ_STEP_COL)) return DQ_ERR_ARG;
   for (int k = 0; k < count; ++k) {
     int rc = check_matrix(p[k].W, p[k].w_dtype, p[k].rows, p[k].cols, p[k].ld, g);
     if (rc) return rc;
+    if (p[k].report && ((uintptr_t)p[k].report & 3u)) return DQ_ERR_ALIGN;
     if (p[k].rows == 0 || p[k].cols == 0) continue;
     if (!p[k].r || !p[k].c || !p[k].codes || !p[k].block_scales) return DQ_ERR_NULL;
     if (spec.fmt == DQ_FMT_NVFP4 && !p[k].tensor_scale) return DQ_ERR_NULL;
@@ -694,8 +708,23 @@ size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_sp
   return pl.total;
 }
 
-int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
-             dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
+// Sweeps a solve of T iterations queues: the INIT sweep and one per iteration, plus one
+// re-solve sweep after each rejected step whose iteration is not the last (a rejection at
+// iteration T ends the solve), i.e. at most 2T (1 for T = 0).
+static int max_sweeps(int iters) { return iters > 0 ? 2 * iters : 1; }
+
+// The solve, stream-ordered.  With `timing` set, a begin/end event pair is attached to each
+// pass's launches (row pass, column pass, finalize + decision, all groups) of every queued
+// sweep, and the stream is synchronised at the end to read them.
+struct PassTiming {
+  float* ms;
+  int32_t capacity;
+  int32_t* count;
+};
+
+static int solve_impl(const dq_problem* problems, int32_t count, dq_quant_spec spec,
+                      const dq_solve_opts* opts, void* workspace, size_t workspace_bytes,
+                      void* stream, const PassTiming* timing) {
   int g = 0;
   int rc = validate_solve(problems, count, spec, opts, &g);
   if (rc) return rc;
@@ -713,7 +742,7 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
   }
   const int iters = opts->iters;
 
-  // empty problems: zero histories, report immediately
+  // empty problems: zero histories (their reports come from the outputs kernel)
   for (int k = 0; k < count; ++k) {
     if (pl.group_of[k] >= 0) continue;
     if (problems[k].nmse_hist)
@@ -721,92 +750,63 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
     if (problems[k].relchg_hist)
       DQ_HIP(hipMemsetAsync(problems[k].relchg_hist, 0, sizeof(double) * (iters + 1), s));
   }
-  if (pl.groups.empty()) {
-    DQ_HIP(hipStreamSynchronize(s));
-    for (int k = 0; k < count; ++k)
-      if (problems[k].report) *problems[k].report = dq_report{iters, 0, 0u, 0};
-    return DQ_OK;
-  }
 
-  // the problem descriptors and every launch table, in one upload
+  // the live-problem counter, the problem descriptors and every launch table, in one upload
+  // (the runtime stages pageable host memory before the call returns)
   ProbDev* dprobs = (ProbDev*)(ws + pl.probs_off);
-  std::vector<char> up(pl.sout_off - pl.probs_off);
-  std::memcpy(up.data(), pl.dev.data(), sizeof(ProbDev) * count);
+  int32_t* live = (int32_t*)(ws + pl.live_off);
+  std::vector<char> up(pl.up_end - pl.live_off);
+  std::memcpy(up.data(), &pl.live, sizeof(int32_t));
+  std::memcpy(up.data() + (pl.probs_off - pl.live_off), pl.dev.data(), sizeof(ProbDev) * count);
   for (auto& G : pl.groups) {
-    std::memcpy(up.data() + (G.row_off - pl.probs_off), G.row.data(), sizeof(WgEntry) * G.row.size());
-    std::memcpy(up.data() + (G.col_off - pl.probs_off), G.col.data(), sizeof(WgEntry) * G.col.size());
-    std::memcpy(up.data() + (G.fin_off - pl.probs_off), G.fin.data(), sizeof(WgEntry) * G.fin.size());
+    std::memcpy(up.data() + (G.row_off - pl.live_off), G.row.data(), sizeof(WgEntry) * G.row.size());
+    std::memcpy(up.data() + (G.col_off - pl.live_off), G.col.data(), sizeof(WgEntry) * G.col.size());
+    std::memcpy(up.data() + (G.fin_off - pl.live_off), G.fin.data(), sizeof(WgEntry) * G.fin.size());
   }
-  DQ_HIP(hipMemcpyAsync(dprobs, up.data(), up.size(), hipMemcpyHostToDevice, s));
+  DQ_HIP(hipMemcpyAsync(live, up.data(), up.size(), hipMemcpyHostToDevice, s));
 
-  int64_t maxdim = 1;
-  int max_init = 1;
-  for (int k = 0; k < count; ++k) {
-    if (pl.group_of[k] < 0) continue;
-    maxdim = std::max(maxdim, std::max(pl.dev[k].rows, pl.dev[k].cols));
-    max_init = std::max(max_init, pl.dev[k].init_wgs);
-  }
-  hipLaunchKernelGGL(k_setup, dim3((unsigned)((maxdim + 255) / 256), (unsigned)count), dim3(256),
-                     0, s, dprobs);
-  DQ_HIP(hipGetLastError());
-  for (int dt = 0; dt < 2; ++dt) {
-    bool any = false;
-    for (int k = 0; k < count; ++k) any |= (pl.group_of[k] >= 0 && problems[k].w_dtype == dt);
-    if (!any) continue;
-    rc = launch_init_any(spec.fmt, dt, dim3((unsigned)max_init, (unsigned)count), dprobs, s);
-    if (rc) return rc;
-  }
-  rc = launch_init_reduce_any(spec.fmt, count, dprobs, s);
-  if (rc) return rc;
-
-  for (auto& G : pl.groups) {
-    rc = prepare_passes_any(spec.fmt, g, G);
-    if (rc) return rc;
-  }
-
-  // optional per-kernel timing: a begin/end event pair attached to each pass's launches
-  const bool timed = opts->pass_ms != nullptr && opts->pass_ms_capacity > 0;
   std::vector<hipEvent_t> ev;
-  opts->pass_ms_count = 0;
   auto cleanup = [&]() {
     for (auto e : ev) (void)hipEventDestroy(e);
     ev.clear();
   };
-  auto new_event = [&](hipEvent_t* e) -> bool {
-    if (hipEventCreate(e) != hipSuccess) return false;
-    ev.push_back(*e);
-    return true;
-  };
-  std::vector<State> hst(count);
-  std::vector<uint32_t> hflags(count, 0u);
-  std::vector<StateOut> hout(count);
-  StateOut* dout = (StateOut*)(ws + pl.sout_off);
-  // workgroups per problem of the outputs kernel: one 64-byte slice per thread of the
-  // largest code copy, at most 2048 per problem and about 64 K over the batch (a problem whose
-  // kept codes are already in the caller's buffer leaves its workgroups idle)
-  int64_t max_copy = 1;
-  for (int k = 0; k < count; ++k)
-    if (pl.group_of[k] >= 0)
-      max_copy = std::max<int64_t>(max_copy, (int64_t)code_bytes(spec.fmt, pl.dev[k].rows, pl.dev[k].cols));
-  const int64_t out_x = std::max<int64_t>(
-      1, std::min<int64_t>({(max_copy + 16383) / 16384, 2048, std::max<int64_t>(1, 65536 / count)}));
-  const dim3 out_grid((unsigned)out_x, (unsigned)count);
-  int pending = 1 + iters;   // INIT sweep + one sweep per iteration, if nothing is rejected
-  // at most one extra (re-solve) sweep per rejected iteration
-  const int max_sweeps = 2 * iters + 2;
-  int launched = 0;
-  const size_t ng = pl.groups.size();
-  while (pending > 0) {
-    if (launched + pending > max_sweeps) { cleanup(); return DQ_ERR_HIP; }
-    launched += pending;
-    const size_t ev0 = ev.size();
-    for (int q = 0; q < pending; ++q) {
-      const int sw = launched - pending + q;   // sweep index: selects the state slot
-      const bool tm = timed && (int)(ev.size() / 6) < opts->pass_ms_capacity;
+  if (!pl.groups.empty()) {
+    int64_t maxdim = 1;
+    int max_init = 1;
+    for (int k = 0; k < count; ++k) {
+      if (pl.group_of[k] < 0) continue;
+      maxdim = std::max(maxdim, std::max(pl.dev[k].rows, pl.dev[k].cols));
+      max_init = std::max(max_init, pl.dev[k].init_wgs);
+    }
+    hipLaunchKernelGGL(k_setup, dim3((unsigned)((maxdim + 255) / 256), (unsigned)count), dim3(256),
+                       0, s, dprobs);
+    DQ_HIP(hipGetLastError());
+    for (int dt = 0; dt < 2; ++dt) {
+      bool any = false;
+      for (int k = 0; k < count; ++k) any |= (pl.group_of[k] >= 0 && problems[k].w_dtype == dt);
+      if (!any) continue;
+      rc = launch_init_any(spec.fmt, dt, dim3((unsigned)max_init, (unsigned)count), dprobs, s);
+      if (rc) return rc;
+    }
+    rc = launch_init_reduce_any(spec.fmt, count, dprobs, s);
+    if (rc) return rc;
+    for (auto& G : pl.groups) {
+      rc = prepare_passes_any(spec.fmt, g, G);
+      if (rc) return rc;
+    }
+    // Every sweep a solve may need is queued now; a sweep whose problems are all finished
+    // exits at its first instruction (the live counter), so nothing waits on the host.
+    const int nsw = max_sweeps(iters);
+    const size_t ng = pl.groups.size();
+    if (timing) *timing->count = 0;
+    for (int sw = 0; sw < nsw; ++sw) {
+      const bool tm = timing && *timing->count < timing->capacity;
       hipEvent_t e[6] = {};
       if (tm)
-        for (int q = 0; q < 6; ++q)
-          if (!new_event(&e[q])) { cleanup(); return DQ_ERR_HIP; }
+        for (int q = 0; q < 6; ++q) {
+          if (hipEventCreate(&e[q]) != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
+          ev.push_back(e[q]);
+        }
       for (int which = 0; which < 3; ++which) {
         for (size_t gi = 0; gi < ng; ++gi) {
           const auto& G = pl.groups[gi];
@@ -816,54 +816,57 @@ int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
           }
           rc = which < 2 ? launch_pass_any(which, spec.fmt, g, G, dprobs,
                                            (const WgEntry*)(ws + G.row_off),
-                                           (const WgEntry*)(ws + G.col_off), s, sw)
+                                           (const WgEntry*)(ws + G.col_off), s, sw, live)
                          : launch_finalize_any(spec.fmt, G, dprobs,
-                                               (const WgEntry*)(ws + G.fin_off), s, sw);
+                                               (const WgEntry*)(ws + G.fin_off), s, sw, live);
           t_ev_start = t_ev_stop = nullptr;
           if (rc) { cleanup(); return rc; }
         }
       }
+      if (tm) ++*timing->count;
     }
-    // states of all problems for the host; outputs of the finished ones
-    hipLaunchKernelGGL(k_outputs, out_grid, dim3(256), 0, s, dprobs, launched & 1,
-                       code_bits(spec.fmt), scale_bytes(spec.fmt), g, dout);
-    if (hipGetLastError() != hipSuccess ||
-        hipMemcpyAsync(hout.data(), dout, sizeof(StateOut) * count, hipMemcpyDeviceToHost, s) !=
-            hipSuccess ||
-        hipStreamSynchronize(s) != hipSuccess) {
-      cleanup();
-      return DQ_ERR_HIP;
-    }
-    for (size_t k = ev0; k + 5 < ev.size(); k += 6) {
+  }
+  // outputs and device reports: workgroups per problem of the outputs kernel -- one 64-byte
+  // slice per thread of the largest code copy, at most 2048 per problem and about 64 K over
+  // the batch (a problem whose kept codes are already in the caller's buffer leaves them idle)
+  int64_t max_copy = 1;
+  for (int k = 0; k < count; ++k)
+    if (pl.group_of[k] >= 0)
+      max_copy = std::max<int64_t>(max_copy, (int64_t)code_bytes(spec.fmt, pl.dev[k].rows, pl.dev[k].cols));
+  const int64_t out_x = std::max<int64_t>(
+      1, std::min<int64_t>({(max_copy + 16383) / 16384, 2048, std::max<int64_t>(1, 65536 / count)}));
+  hipLaunchKernelGGL(k_outputs, dim3((unsigned)out_x, (unsigned)count), dim3(256), 0, s, dprobs,
+                     code_bits(spec.fmt), scale_bytes(spec.fmt), g);
+  if (hipGetLastError() != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
+  if (timing) {
+    if (hipStreamSynchronize(s) != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
+    for (int k = 0; k < *timing->count; ++k)
       for (int q = 0; q < 3; ++q) {
         float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, ev[k + 2 * q], ev[k + 2 * q + 1]) != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
-        opts->pass_ms[3 * opts->pass_ms_count + q] = ms;
+        if (hipEventElapsedTime(&ms, ev[6 * k + 2 * q], ev[6 * k + 2 * q + 1]) != hipSuccess) {
+          cleanup();
+          return DQ_ERR_HIP;
+        }
+        timing->ms[3 * k + q] = ms;
       }
-      opts->pass_ms_count++;
-    }
-    pending = 0;
-    for (int k = 0; k < count; ++k) {
-      if (pl.group_of[k] < 0) continue;
-      // the decision of the last sweep launched wrote the slot of sweep `launched`
-      hst[k] = hout[k].st;
-      hflags[k] = hout[k].flags;
-      if (hst[k].mode == MODE_DONE) continue;
-      int need = (iters - hst[k].it_done) + (hst[k].mode == MODE_FIXUP ? 1 : 0);
-      pending = std::max(pending, need);
-    }
   }
-
   cleanup();
-  // every problem is finished: k_outputs of the last round wrote the final scales, kept
-  // codes and tensor scale, and the stream has been synchronised
-  for (int k = 0; k < count; ++k) {
-    if (!problems[k].report) continue;
-    if (pl.group_of[k] < 0) { *problems[k].report = dq_report{iters, 0, 0u, 0}; continue; }
-    const State& S = hst[k];
-    *problems[k].report = dq_report{S.it_done, S.rejected, hflags[k], S.sweeps};
-  }
   return DQ_OK;
+}
+
+int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
+             const dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
+  return solve_impl(problems, count, spec, opts, workspace, workspace_bytes, stream, nullptr);
+}
+
+int dq_solve_timed(const dq_problem* problems, int32_t count, dq_quant_spec spec,
+                   const dq_solve_opts* opts, void* workspace, size_t workspace_bytes,
+                   void* stream, float* pass_ms, int32_t pass_ms_capacity,
+                   int32_t* pass_ms_count) {
+  if (!pass_ms || !pass_ms_count) return DQ_ERR_NULL;
+  if (pass_ms_capacity < 0) return DQ_ERR_ARG;
+  PassTiming t{pass_ms, pass_ms_capacity, pass_ms_count};
+  return solve_impl(problems, count, spec, opts, workspace, workspace_bytes, stream, &t);
 }
 
 size_t dq_quantize_workspace_bytes(int64_t rows, int64_t cols, dq_quant_spec spec) {

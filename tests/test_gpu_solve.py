@@ -395,8 +395,8 @@ def test_scale_step_ablation(oracle_lib, steps, name, rows, cols, iters, group):
         assert np.all(got[v] == 1.0), v
 
 
-def test_batch_across_rounds_of_sweeps():
-    """A batch whose members finish in different rounds of sweeps (INT4 rejections add
+def test_batch_members_finishing_at_different_sweeps():
+    """A batch whose members finish after different numbers of sweeps (INT4 rejections add
     re-solve sweeps for some matrices only) plus an empty problem: every member equals its
     own solve (codes, scales, r, c, histories, report), whichever code buffer its kept Qhat
     ended in."""
@@ -421,3 +421,39 @@ def test_batch_across_rounds_of_sweeps():
         assert np.array_equal(p.nmse_hist.cpu().numpy(), one["nmse"])
         assert rep.rejected_steps == one["rejected"] and rep.iters_run == one["iters_run"]
         assert rep.sweeps == one["sweeps"]
+
+
+def test_stream_ordered_on_a_side_stream():
+    """dq_solve only enqueues: run it on a side stream, join that stream with an event, and the
+    results (codes, scales, r, c, histories, device report) equal a solve on the default
+    stream bit for bit.  Work queued on the side stream after the solve sees its outputs."""
+    W = synth.matrix(synth.WORKLOADS["down4096x14336_nvfp4"]["W"].scaled(300, 4096), 4)
+    Wd = to_dev(W)
+    ref = dq.solve(Wd, "NVFP4", 8)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    p = dq.make_problem(Wd, "NVFP4", 8)
+    done = torch.cuda.Event()
+    with torch.cuda.stream(side):
+        assert dq.solve_many([p], "NVFP4", 8, stream=side, read_reports=False) is None
+        c_copy = p.c.clone()          # stream-ordered after the solve
+        done.record(side)
+    torch.cuda.current_stream().wait_event(done)
+    rep = dq.read_report(p)
+    assert torch.equal(p.codes, ref["codes"]) and torch.equal(p.block_scales, ref["scales"])
+    assert torch.equal(p.r, ref["r"]) and torch.equal(p.c, ref["c"]) and torch.equal(c_copy, ref["c"])
+    assert torch.equal(p.nmse_hist, ref["nmse"]) and torch.equal(p.relchg_hist, ref["relchg"])
+    assert rep.iters_run == ref["iters_run"] == 8 and rep.rejected_steps == ref["rejected"]
+    assert rep.sweeps == ref["sweeps"] and rep.flags == ref["flags"]
+    assert (rep.flags & 32) == 0
+
+
+def test_device_reports_of_a_batch_with_an_empty_problem():
+    probs = [dq.make_problem(to_dev(synth.matrix(synth.WORKLOADS["w256x512_int4"]["W"].scaled(64, 512), 1)),
+                             "MXFP4", 5),
+             dq.make_problem(torch.empty(0, 512, dtype=torch.float32, device=DEV), "MXFP4", 5)]
+    for p in probs:
+        p.report.fill_(-1)
+    reps = dq.solve_many(probs, "MXFP4", 5)
+    assert reps[0].iters_run == 5 and reps[0].sweeps >= 6 and (reps[0].flags & 32) == 0
+    assert (reps[1].iters_run, reps[1].rejected_steps, reps[1].flags, reps[1].sweeps) == (5, 0, 0, 0)
