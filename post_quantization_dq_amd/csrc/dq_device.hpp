@@ -115,6 +115,15 @@ __device__ __forceinline__ float project(float x) {
   return proj_bf16(x);   // INT4, INT8 and every MX format
 }
 
+// Wait for this wave's LDS writes, then a bare workgroup barrier.  Global loads issued
+// earlier (later pipeline stages, the next row) stay in flight -- the fence of
+// __syncthreads would wait for them too; the memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0), vmcnt and expcnt free
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------- cross-lane helpers
 // Max over the L consecutive lanes that share a block (L in {1,2,4,8}).
 template <int L>

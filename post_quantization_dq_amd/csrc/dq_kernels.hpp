@@ -397,12 +397,27 @@ struct PassInfo {
 };
 
 // ---------------------------------------------------------------- row pass
+// Words of one entry of the row pass's queue of changed chunks: the chunk index and block
+// scale code in one word, then the candidate's code words; padded to 16 or 32 bytes.
+template <int FMT>
+constexpr int queue_words() { return code_words<FMT>() + 1 <= 4 ? 4 : 8; }
+constexpr int kQueueLen = 64;   // entries per wave: one flush runs one entry per lane
+
 // CG = 1 (matrices wider than the LDS holds): c and 1/c are read from global memory (they
 // stay in L2) instead of LDS.
+//
+// Kept-Qhat work on changed chunks only: a chunk whose candidate codes and block scale code
+// equal the kept ones (under equal block factors: always for the MX and integer formats,
+// for NVFP4 when the two tensor scales are equal) has the same dequantised values, so it adds
+// exactly 0 to the change of F and to the relchg numerator.  With `compact` set, a changed
+// chunk adds its candidate error to dF at once and is queued (per wave, in LDS); at the end
+// of the row, or when the queue is full, one lane per queued chunk reloads its W and kept
+// codes, subtracts the kept Qhat's error and adds its relchg term.  On the pages' NVFP4
+// weights a few percent of the chunks change per iteration.
 template <int FMT, int DT, int L, int CG>
 __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ probs,
                                                   const WgEntry* __restrict__ table, int sw,
-                                                  const int32_t* __restrict__ live) {
+                                                  const int32_t* __restrict__ live, int compact) {
   if (*gp(live) == 0) return;   // every problem finished: this queued sweep has nothing to do
   const WgEntry we = table[blockIdx.x];
   const ProbDev& P = probs[we.prob];
@@ -421,6 +436,8 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
   NvTab* tab_p = tab_c + 1;
   __shared__ double redw[16][4];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, nw = (int)(blockDim.x >> 6);
+  constexpr int QW = queue_words<FMT>();
+  uint32_t* queue = (uint32_t*)(tab_c + (FMT == NVFP4 ? 2 : 0)) + (size_t)wave * kQueueLen * QW;
 
   // NVFP4 tensor scale of this sweep's candidate.  After a kept step it follows from the
   // amax of W ./ r c^T at the new scales, i.e. from the finalize partials: every workgroup
@@ -482,11 +499,51 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
   const int64_t row0 = (int64_t)we.idx * P.rows_per_blk;
   const int64_t row1 = min(P.rows, row0 + P.rows_per_blk);
   const int nloop = (nch + 63) >> 6;
+  // equal block factors for equal scale codes (NVFP4: equal tensor scales)
+  const bool cq = compact && pi.stats && (FMT != NVFP4 || s_t == st->st_acc);
+
+  // the kept Qhat's error and the relchg terms of the `count` queued chunks of row i
+  auto flush = [&](int64_t i, float r_, int count) {
+    __builtin_amdgcn_wave_barrier();
+    if (lane < count) {
+      const uint32_t* e = queue + lane * QW;
+      const int chq = (int)(e[0] & 0xFFFFu);
+      const uint32_t scq = e[0] >> 16;
+      uint32_t cw[4] = {e[1], code_words<FMT>() > 1 ? e[2] : 0u, code_words<FMT>() > 2 ? e[3] : 0u,
+                        code_words<FMT>() > 3 ? e[4] : 0u};
+      RawRow<DT> rq;
+      rq.load(P.W, i, P.ld, 16 * chq);
+      uint32_t kq[4] = {0u, 0u, 0u, 0u}, ksq = 0u;
+      load_codes<FMT, L>(acodes, ascales, i, n, chq, g, kq, ksq);
+      float w[16], cc[16], pq[16], pp[16];
+      rq.unpack(w);
+      if (CG) load16_global(cglob + 16 * (int64_t)chq, true, cc);
+      else lds_load16(s_c4, nch, chq, cc);
+      decode_grid<FMT>(cw, pq);
+      decode_grid<FMT>(kq, pp);
+      const float f = block_factor<FMT>(scq, tab_c);
+      const float fp = block_factor<FMT>(ksq, tab_p);
+      const float rfp = r_ * fp;
+      float Fpl = 0.0f, rl = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float ppc = pp[k] * cc[k];
+        const float ep = fmaf(-rfp, ppc, w[k]);
+        Fpl = fmaf(ep, ep, Fpl);
+        const float df = pq[k] * f - pp[k] * fp;
+        rl = fmaf(df, df, rl);
+      }
+      adF -= (double)Fpl;
+      arel += (double)rl;
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
 
   for (int64_t i = row0 + wave; i < row1; i += nw) {
     const float r_ = rcur[i];
     const float ir_ = ircur[i];
     double Nrow = 0.0, Drow = 0.0;
+    int qn = 0;   // queued chunks of this row (wave-uniform)
     for (int kk = 0; kk < nloop; ++kk) {
       const int chn = lane + 64 * kk;
       const bool valid = chn < nch;
@@ -538,7 +595,27 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
           ql = fmaf(p[k], p[k], ql);
         }
         float Fpl = 0.0f, rl = 0.0f;
-        if (pi.stats) {
+        bool changed = false, queued = false;
+        if (cq) {
+#pragma unroll
+          for (int w4 = 0; w4 < code_words<FMT>(); ++w4) changed |= ch.code[w4] != pk[w4];
+          changed = valid && (changed || ch.scode != ps);
+          const uint64_t mask = __ballot(changed);
+          const int cnt = __popcll(mask);
+          queued = qn + cnt <= kQueueLen;   // wave-uniform; a full queue falls back to inline
+          if (queued && mask) {
+            const int pos = qn + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+            if (changed) {
+              uint32_t* e = queue + pos * QW;
+              e[0] = (uint32_t)chn | (ch.scode << 16);
+#pragma unroll
+              for (int w4 = 0; w4 < code_words<FMT>(); ++w4) e[1 + w4] = ch.code[w4];
+            }
+            qn += cnt;
+          }
+        }
+        if (pi.stats && !queued) {
           float pp[16];
           decode_grid<FMT>(pk, pp);
           const float fp = block_factor<FMT>(ps, tab_p);
@@ -556,7 +633,9 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         }
         if (valid) {
           aFc += (double)Fl;
-          adF += (double)Fl - (double)Fpl;
+          // queued chunks: the candidate's error now, the kept one's at the flush; unchanged
+          // chunks under compaction add 0
+          adF += queued ? (changed ? (double)Fl : 0.0) : (double)Fl - (double)Fpl;
           arel += (double)rl;
           aqn += (double)(f * f) * (double)ql;
         }
@@ -587,6 +666,7 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         }
       }
     }
+    if (qn > 0) flush(i, r_, qn);   // wave-uniform
     if (pi.next) {
       // r-step of the next iteration from the whole row (fixed butterfly order in fp64)
       const double N = wave_sum(Nrow), D = wave_sum(Drow);

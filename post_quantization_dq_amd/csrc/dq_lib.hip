@@ -135,6 +135,17 @@ bool rowpass_cg(int fmt, int64_t cols) {
 size_t rowpass_lds(int fmt, int64_t cols) {
   return (rowpass_cg(fmt, cols) ? 0 : 2 * sizeof(float) * (size_t)cols) + rowpass_tabs(fmt);
 }
+// The queue of changed chunks (kRowWaves waves x kQueueLen entries), when it fits beside the rest.
+size_t rowpass_queue(int fmt) {
+  const int words = code_bits(fmt) == 8 ? 8 : 4;   // queue_words<FMT>()
+  return (size_t)kRowWaves * kQueueLen * words * sizeof(uint32_t);
+}
+bool rowpass_compact(int fmt, int64_t cols) {
+  return rowpass_lds(fmt, cols) + rowpass_queue(fmt) <= (size_t)device_lds_limit();
+}
+size_t rowpass_lds_total(int fmt, int64_t cols) {
+  return rowpass_lds(fmt, cols) + (rowpass_compact(fmt, cols) ? rowpass_queue(fmt) : 0);
+}
 size_t colpass_lds(int fmt) { return (size_t)8 * 64 * 16 * (grouped_int_fmt(fmt) ? 8 : 4); }
 
 struct Plan {
@@ -327,13 +338,14 @@ bool lds_limit(const void* kernel, int bytes) {
 template <int FMT, int DT, int L>
 int launch_passes(const Plan::Group& G, const ProbDev* probs, const WgEntry* rtab,
                   const WgEntry* ctab, hipStream_t s, int sw, int32_t* live) {
-  const size_t rl = rowpass_lds(FMT, G.cols);
+  const size_t rl = rowpass_lds_total(FMT, G.cols);
+  const int compact = rowpass_compact(FMT, G.cols) ? 1 : 0;
   if (rowpass_cg(FMT, G.cols))
     launch_timed(k_rowpass<FMT, DT, L, 1>, dim3((unsigned)G.row.size()), dim3(kRowWaves * 64), rl,
-                 s, probs, rtab, sw, (const int32_t*)live);
+                 s, probs, rtab, sw, (const int32_t*)live, compact);
   else
     launch_timed(k_rowpass<FMT, DT, L, 0>, dim3((unsigned)G.row.size()), dim3(kRowWaves * 64), rl,
-                 s, probs, rtab, sw, (const int32_t*)live);
+                 s, probs, rtab, sw, (const int32_t*)live, compact);
   if (hipGetLastError() != hipSuccess) return DQ_ERR_HIP;
   return DQ_OK;
 }
@@ -363,9 +375,10 @@ int launch_pass_dt(int which, const Plan::Group& G, const ProbDev* probs, const 
 // Dynamic LDS limits of a group's pass kernels (set once per solve, before the launches).
 template <int FMT, int DT, int L>
 int prepare_passes(const Plan::Group& G) {
-  const size_t rl = rowpass_lds(FMT, G.cols);
+  const size_t rl = rowpass_lds_total(FMT, G.cols);
   if (rl > 64 * 1024 &&
-      hipFuncSetAttribute((const void*)k_rowpass<FMT, DT, L, 0>,
+      hipFuncSetAttribute(rowpass_cg(FMT, G.cols) ? (const void*)k_rowpass<FMT, DT, L, 1>
+                                                  : (const void*)k_rowpass<FMT, DT, L, 0>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)rl) != hipSuccess)
     return DQ_ERR_HIP;
   if constexpr (grouped_int<FMT>()) {

@@ -523,14 +523,6 @@ struct NvRaw {
   }
 };
 
-// Wait for this wave's LDS writes, then a bare workgroup barrier.  Global loads of later
-// stages stay in flight (the fence of __syncthreads would wait for them too); the memory
-// clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0), vmcnt and expcnt free
-  asm volatile("s_barrier" ::: "memory");
-}
-
 // Y tile 128 x 128 per workgroup, four waves of 64 x 64 (as k_linear).  Stages of 64 K:
 // raw codes are loaded into registers two stages ahead, dequantised into one of two f16
 // LDS buffers one stage ahead, and multiplied from the other.
