@@ -2,10 +2,12 @@
 that consumes the activation codes and the solved weight codes; listing page Tables 11-12).
 
 Pinned by:
-- a hand-computed MXFP4 example (codes and scales written out bit by bit);
+- hand-computed MXFP4, NVFP4 and INT4 (two groups of 64, nibble -8 included) examples,
+  codes and scales written out bit by bit;
 - one-hot weights, which turn the product into a gather of the activations and so expose
   any transposed operand or index slip;
-- MXFP8 products recomputed with torch's float8 decoding and a float64 matmul;
+- MXFP8 products recomputed with torch's float8 decoding and a float64 matmul, INT4
+  products with the format's decode written out in numpy (nibble, bf16 bits);
 - exact power-of-two scaling laws;
 - the sampled-entry variant equal to the full product.
 """
@@ -145,3 +147,80 @@ def test_nvfp4_one_hot_and_tensor_scales(oracle_lib):
     ye, ay = oracle_lib.quantized_linear_entries(pa, asc, M, pb, bsc, N, K, "NVFP4", [0, M - 1],
                                                  [N - 1, 0], r=r, a_ts=0.25, b_ts=1.0)
     assert np.array_equal(ye, y[[0, M - 1], [N - 1, 0]]) and np.all(ay >= np.abs(ye))
+
+
+# ---------------------------------------------------------------- INT4, bf16 group scales
+# INT4 (the listing page's W4A4 rows; Table 12's packed 4-bit weights with one bf16 scale
+# per group of 64 or 128 along K): element = two's-complement nibble q in [-8, 7] times the
+# group's bf16 scale.
+def _bf16_bits(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _int4_deq_numpy(nib, sc_bits, rows, K, g):
+    """The format's definition written out independently of the oracle: nibble -> signed
+    integer, bf16 bits -> float32 -> float64, one scale per g consecutive elements."""
+    q = ((nib.astype(np.int64) ^ 8) - 8).reshape(rows, K)
+    s = (sc_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(rows, K // g)
+    return q * np.repeat(s, g, axis=1)
+
+
+def test_hand_example_int4_g64(oracle_lib):
+    # K = 128, two groups of 64.
+    # group 0: A 3, -2, 6 at K 0, 1, 5 (scale 0.375);  B 5, 4, -1 (scale 1.25)
+    #          sum 15 - 8 - 6 = 1, times 0.375 * 1.25 = 0.46875
+    # group 1: A -8, 1 at K 64, 100 (scale 0.125);  B 3, -7 (scale 6.0)
+    #          sum -24 - 7 = -31, times 0.125 * 6 = -23.25
+    # total -22.78125, times r = 0.5 -> -11.390625
+    a = np.zeros(128, np.int64)
+    a[[0, 1, 5, 64, 100]] = [3, -2, 6, -8, 1]
+    b = np.zeros(128, np.int64)
+    b[[0, 1, 5, 64, 100]] = [5, 4, -1, 3, -7]
+    asc = np.array([0x3EC0, 0x3E00], np.uint16)   # 0.375, 0.125
+    bsc = np.array([0x3FA0, 0x40C0], np.uint16)   # 1.25, 6.0
+    y = oracle_lib.quantized_linear(_pack(a & 15, 4), asc, 1, _pack(b & 15, 4), bsc, 1, 128,
+                                    "INT4", group=64, r=np.array([0.5], np.float32))
+    assert y.shape == (1, 1) and y[0, 0] == -11.390625
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_int4_one_hot_weights_gather_activations(oracle_lib, g):
+    rng = np.random.default_rng(11)
+    M, N, K = 6, 9, 4 * g
+    an = rng.integers(0, 16, M * K).astype(np.uint8)             # every nibble, -8 included
+    asc = _bf16_bits(rng.uniform(0.01, 4.0, M * K // g))
+    perm = rng.permutation(K)[:N]
+    bn = np.zeros((N, K), np.uint8)
+    bn[np.arange(N), perm] = 1
+    bsc = np.full(N * K // g, 0x3F80, np.uint16)                  # 1.0
+    r = np.exp2(rng.integers(-3, 4, N)).astype(np.float32)
+    pa, pb = _pack(an, 4), _pack(bn.reshape(-1), 4)
+    y = oracle_lib.quantized_linear(pa, asc, M, pb, bsc, N, K, "INT4", group=g, r=r)
+    deqA = _int4_deq_numpy(an, asc, M, K, g)
+    assert np.array_equal(y, deqA[:, perm] * r[None, :])
+    # the sampled entries equal the full product, and bound it
+    mi, ni = rng.integers(0, M, 15), rng.integers(0, N, 15)
+    ye, ay = oracle_lib.quantized_linear_entries(pa, asc, M, pb, bsc, N, K, "INT4", mi, ni,
+                                                 group=g, r=r)
+    assert np.array_equal(ye, y[mi, ni]) and np.all(ay >= np.abs(ye))
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_int4_against_independent_decode(oracle_lib, g):
+    rng = np.random.default_rng(12)
+    M, N, K = 5, 7, 3 * g
+    an, bn = rng.integers(0, 16, M * K).astype(np.uint8), rng.integers(0, 16, N * K).astype(np.uint8)
+    asc = _bf16_bits(np.exp2(rng.uniform(-6, 6, M * K // g)))
+    bsc = _bf16_bits(np.exp2(rng.uniform(-6, 6, N * K // g)))
+    y = oracle_lib.quantized_linear(_pack(an, 4), asc, M, _pack(bn, 4), bsc, N, K, "INT4", group=g)
+    want = _int4_deq_numpy(an, asc, M, K, g) @ _int4_deq_numpy(bn, bsc, N, K, g).T
+    assert np.allclose(y, want, rtol=1e-13, atol=0.0)
+    # a group's scale doubled (bf16 exponent + 1) doubles exactly that group's share
+    asc2 = asc.reshape(M, K // g).copy()
+    asc2[:, 1] += 0x80
+    y2 = oracle_lib.quantized_linear(_pack(an, 4), asc2.reshape(-1), M, _pack(bn, 4), bsc, N, K,
+                                     "INT4", group=g)
+    qa = _int4_deq_numpy(an, asc, M, K, g)
+    qb = _int4_deq_numpy(bn, bsc, N, K, g)
+    share = qa[:, g:2 * g] @ qb[:, g:2 * g].T
+    assert np.allclose(y2, want + share, rtol=1e-13, atol=1e-300)
