@@ -19,6 +19,7 @@ on this host.
   python bench.py --workload llama31_8b_nvfp4 --steps 3 --warmup 1   # the batched 224-matrix set
   python bench.py --workload linear_w4a4_mxfp4   # the quantised linear layer on solved codes
   python bench.py --workload linear_w4a4_nvfp4   # the same layer in NVFP4 (f16 cores)
+  python bench.py --workload linear_w4a4_int4    # the same layer in INT4, groups of 64 (int8 cores)
   python bench.py --workload qkv_acts_nvfp4      # fused q/k/v activation quantise
 """
 
@@ -160,14 +161,21 @@ def bench_llama_set(args):
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 matrix-core peak
 F16_MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 matrix-core peak
+I8_MFMA_PEAK_TOPS = 5000.0       # MI355X dense int8 matrix-core peak
+# INT4 groups of 64 on the int8 cores: per 64-element group and wave (64 x 64 outputs) the
+# kernel issues 248 VALU instructions (64 conversions, 64 scale products, 64 fma, 56 to unpack
+# nibbles and index; counted in the gfx950 assembly) against 16 MFMA; at 39.3 T unpacked
+# lane-operations/s that caps it at 128 ops per output-group / (248 / 64) lane-operations.
+I4_VALU_PER_OUTPUT_GROUP = 248 / 64
 
 
 def bench_linear(args, fmt):
     """The quantised linear layer on codes the solver and the activation quantiser made:
-    the q_proj-shaped 4096x4096 weight solved to `fmt` (MXFP4 or NVFP4, T = 16), 2048 tokens
-    of activations rescaled by the solved c and quantised to the same format,
-    Y = Aq Q^T diag(r) in bf16.  MXFP4 runs on the FP4 block-scaled matrix cores, NVFP4 on
-    the f16 cores after an exact dequantisation in the kernel."""
+    the q_proj-shaped 4096x4096 weight solved to `fmt` (MXFP4, NVFP4 or INT4 with groups of
+    64; T = 16), 2048 tokens of activations rescaled by the solved c and quantised to the
+    same format, Y = Aq Q^T diag(r) in bf16.  MXFP4 runs on the FP4 block-scaled matrix
+    cores, NVFP4 on the f16 cores after an exact dequantisation in the kernel, INT4 on the
+    int8 cores (exact int32 per group, bf16 scale products applied in fp32)."""
     import torch
 
     import post_quantization_dq_amd as dq
@@ -179,13 +187,15 @@ def bench_linear(args, fmt):
     M = ACT_TOKENS
     X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(M, K), 0)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-    res = dq.solve(to_dev(W), fmt, T)
-    ac, asc, ats = dq.rescale_quantize_acts(to_dev(X), res["c"], fmt)
+    i4 = fmt == "INT4"
+    group = 64 if i4 else None
+    res = dq.solve(to_dev(W), fmt, T, group=group)
+    ac, asc, ats = dq.rescale_quantize_acts(to_dev(X), res["c"], fmt, group=group)
     nv = fmt == "NVFP4"
     bts = res["tscale"] if nv else None
     ats = ats if nv else None
     y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-    spec = dq.spec_of(fmt)
+    spec = dq.spec_of(fmt, group)
     call = lambda: dq.dq_quantized_linear(spec, ac, asc, ats, M, res["codes"], res["scales"], bts, N, K,
                                           res["r"], y)
     print(f"[bench] quantised linear {fmt}: Y[{M}x{N}] = A[{M}x{K}] Q^T diag(r), bf16 out", flush=True)
@@ -203,22 +213,33 @@ def bench_linear(args, fmt):
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
-    peak = F16_MFMA_PEAK_TFLOPS if nv else FP4_MFMA_PEAK_TFLOPS
+    peak = F16_MFMA_PEAK_TFLOPS if nv else I8_MFMA_PEAK_TOPS if i4 else FP4_MFMA_PEAK_TFLOPS
+    kernel = "k_linear_nv_dma" if nv else "k_linear_i4" if i4 else "k_linear_dma"
+    cores = ("f16 (exact e2m1 x e4m3 elements)" if nv else
+             "int8 (exact int32 per group of 64, fp32 scaling)" if i4 else "fp4 block-scaled")
+    fmt_name = f"{fmt} g{group}" if i4 else fmt
     out = {
-        "metric": f"quantised linear layer TFLOP/s (W4A4 {fmt} codes from the solver)",
+        "metric": f"quantised linear layer TFLOP/s (W4A4 {fmt_name} codes from the solver)",
         "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": fmt.lower(), "data": "synthetic",
-        "config": {"workload": f"q_proj-shaped {N}x{K} weight solved to {fmt} (T={T}); {M} tokens of "
-                               f"activations rescaled by the solved c and quantised to {fmt}; bf16 output",
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4" if i4 else fmt.lower(),
+        "data": "synthetic",
+        "config": {"workload": f"q_proj-shaped {N}x{K} weight solved to {fmt_name} (T={T}); {M} tokens "
+                               f"of activations rescaled by the solved c and quantised to {fmt_name}; "
+                               "bf16 output",
                    "M": M, "N": N, "K": K},
-        "roofline": {"bound": "mfma", "kernel": "k_linear_nv_dma" if nv else "k_linear_dma",
+        "roofline": {"bound": "mfma", "kernel": kernel,
                      "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": None,
                      "alg_flops_per_launch": flops, "avg_launch_ms": round(ms, 4),
-                     "cores": "f16 (exact e2m1 x e4m3 elements)" if nv else "fp4 block-scaled"},
+                     "cores": cores},
         "wall_ms_per_call": round(wall * 1e3, 4),
     }
+    if i4:
+        # the vector-ALU ceiling of this kernel (see I4_VALU_PER_OUTPUT_GROUP)
+        ceil = VALU_PEAK_LANE_OPS / I4_VALU_PER_OUTPUT_GROUP * 128 / 1e12
+        out["roofline"]["valu_ceiling"] = round(ceil, 1)
+        out["roofline"]["frac_of_valu_ceiling"] = round(tflops / ceil, 4)
     print(json.dumps(out), flush=True)
 
 
@@ -307,7 +328,7 @@ def main():
     if args.workload == "llama31_8b_nvfp4":
         bench_llama_set(args)
         return
-    if args.workload in ("linear_w4a4_mxfp4", "linear_w4a4_nvfp4"):
+    if args.workload in ("linear_w4a4_mxfp4", "linear_w4a4_nvfp4", "linear_w4a4_int4"):
         bench_linear(args, args.workload.rsplit("_", 1)[1].upper())
         return
     if args.workload == "qkv_acts_nvfp4":

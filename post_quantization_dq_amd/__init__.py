@@ -408,17 +408,17 @@ def recode_mxint4_to_mxfp6(codes, scales, rows: int, cols: int, stream=None):
 
 def quantized_linear(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, fmt: str,
                      r=None, out_dtype=torch.float32, stream=None, a_tensor_scale=None,
-                     b_tensor_scale=None) -> torch.Tensor:
+                     b_tensor_scale=None, group: int | None = None) -> torch.Tensor:
     """Y [M][N] = deq(A) deq(B)^T diag(r) from activation codes A [M][K] and weight codes
-    B [N][K] of an MX format or NVFP4 (which also takes the two [1] fp32 tensor scales).
-    MXINT4 operands are re-encoded as MXFP6 E2M3 first (exact; for weights this can be done
-    once and kept)."""
+    B [N][K] of an MX format, NVFP4 (which also takes the two [1] fp32 tensor scales) or
+    INT4 (bf16 scales per `group` = 64 or 128 elements).  MXINT4 operands are re-encoded as
+    MXFP6 E2M3 first (exact; for weights this can be done once and kept)."""
     if fmt == "MXINT4":
         a_codes, a_scales = recode_mxint4_to_mxfp6(a_codes, a_scales, M, K, stream)
         b_codes, b_scales = recode_mxint4_to_mxfp6(b_codes, b_scales, N, K, stream)
         fmt = "MXFP6_E2M3"
     y = torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
-    dq_quantized_linear(spec_of(fmt), a_codes, a_scales, a_tensor_scale, M, b_codes, b_scales,
+    dq_quantized_linear(spec_of(fmt, group), a_codes, a_scales, a_tensor_scale, M, b_codes, b_scales,
                         b_tensor_scale, N, K, r, y, stream)
     return y
 

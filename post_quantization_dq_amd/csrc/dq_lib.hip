@@ -611,6 +611,13 @@ int launch_linear_nv(dim3 grid, hipStream_t s, const LinArgs& p) {
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
+template <int GS, int OB>
+int launch_linear_i4(dim3 grid, hipStream_t s, const LinArgs& p) {
+  if (!lds_limit((const void*)k_linear_i4<GS, OB>, I4Geom::LDS)) return DQ_ERR_HIP;
+  hipLaunchKernelGGL((k_linear_i4<GS, OB>), grid, dim3(256), I4Geom::LDS, s, p);   // 72 KiB
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
 static_assert(kMaxMulti == DQ_MAX_MULTI, "kernel and header output limits differ");
 // The fused activation quantiser keeps every output's column scales in LDS up to this size
 // (q/k/v or gate/up of a 4096-wide model need 48 or 32 KiB); beyond it they are read from
@@ -1008,18 +1015,19 @@ int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_
   const int g = resolve_group(spec);
   if (g < 0) return DQ_ERR_FORMAT;
   const int f = spec.fmt;
-  const bool nv = f == DQ_FMT_NVFP4;
+  const bool nv = f == DQ_FMT_NVFP4, i4 = f == DQ_FMT_INT4;
   if (f != DQ_FMT_MXFP4 && f != DQ_FMT_MXFP8_E4M3 && f != DQ_FMT_MXFP8_E5M2 &&
-      f != DQ_FMT_MXFP6_E2M3 && f != DQ_FMT_MXFP6_E3M2 && !nv)
+      f != DQ_FMT_MXFP6_E2M3 && f != DQ_FMT_MXFP6_E3M2 && !nv && !i4)
     return DQ_ERR_FORMAT;
   if (y_dtype != DQ_F32 && y_dtype != DQ_BF16) return DQ_ERR_FORMAT;
-  if (M < 0 || N < 0 || K < 0 || K % 32 || ldy < N) return DQ_ERR_SHAPE;
+  if (M < 0 || N < 0 || K < 0 || K % (i4 ? g : 32) || ldy < N) return DQ_ERR_SHAPE;
   if (M == 0 || N == 0) return DQ_OK;
   if (!y) return DQ_ERR_NULL;
   if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return DQ_ERR_NULL;
   if (nv && (!a_tensor_scale || !b_tensor_scale)) return DQ_ERR_NULL;
   if (!aligned16(a_codes) || !aligned16(b_codes) || ((uintptr_t)y % (y_dtype == DQ_F32 ? 4 : 2)))
     return DQ_ERR_ALIGN;
+  if (i4 && (((uintptr_t)a_scales | (uintptr_t)b_scales) & 1u)) return DQ_ERR_ALIGN;   // bf16
   const int64_t tm = (M + kLinTile - 1) / kLinTile, tn = (N + kLinTile - 1) / kLinTile;
   if (tm * tn > (int64_t)0x7FFFFFFF) return DQ_ERR_SHAPE;
   LinArgs p{a_codes, a_scales, b_codes, b_scales, r, a_tensor_scale, b_tensor_scale, y,
@@ -1027,6 +1035,11 @@ int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_
   hipStream_t s = (hipStream_t)stream;
   dim3 grid((unsigned)(tm * tn)), block(256);
   if (nv) return y_dtype == DQ_BF16 ? launch_linear_nv<1>(grid, s, p) : launch_linear_nv<0>(grid, s, p);
+  if (i4) {
+    if (g == 64)
+      return y_dtype == DQ_BF16 ? launch_linear_i4<1, 1>(grid, s, p) : launch_linear_i4<1, 0>(grid, s, p);
+    return y_dtype == DQ_BF16 ? launch_linear_i4<2, 1>(grid, s, p) : launch_linear_i4<2, 0>(grid, s, p);
+  }
 #define DQ_L(F)                                                                          \
   rc = (y_dtype == DQ_BF16) ? launch_linear<F, 1>(grid, s, p) : launch_linear<F, 0>(grid, s, p); \
   break

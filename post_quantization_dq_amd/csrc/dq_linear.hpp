@@ -800,4 +800,204 @@ __global__ __launch_bounds__(256) void k_recode_mxint4_e2m3(const uint8_t* __res
   gp(out_scales)[b] = (uint8_t)(sc >= 2u ? sc - 2u : 0u);
 }
 
+// ---------------------------------------------------------------- INT4 on the int8 cores
+// INT4 (two's-complement nibbles, one bf16 scale per group of 64 or 128 elements along K)
+// has no block-scaled matrix-core form: its scales are bf16 values, not powers of two.
+// Within a group every product is an integer, so V_MFMA_I32_16X16X64_I8 sums a 64-element
+// step exactly in int32: each lane gives 16 of the 64 elements of its row, and since the A
+// and B lanes of one K-group pick the same 16, which 16 does not matter.  A nibble goes to
+// the high half of its byte (the byte is 16 q, so no sign extension is needed) and the
+// int32 sum is 256 P, P the group's integer dot product (|P| <= 64 * 64 per step).  Per
+// output and group the wave then converts 256 P to fp32 (exact), multiplies the two bf16
+// scales (an 8-bit by 8-bit significand product: exact in fp32) and adds P * sa * sb to the
+// fp32 accumulator with one fma; 2^-8 and r are applied at the store.
+//
+// Those three vector operations per output and group, plus one per four elements to
+// unpack the nibbles, outweigh the int8 cores' share (16 cycles per instruction of 16 x 16
+// x 64 against 4 x 4 cycles for one wave-wide vector operation): the kernel is bound by the
+// vector ALU, not by the matrix cores or HBM.
+//
+// Staging: a ring of two stages of 256 K (128 bytes of codes per tile row, as the FP4
+// direct-to-LDS kernel, chunks XOR-swizzled by row); codes go to LDS by direct-to-LDS
+// global loads, clamped to the row start past K (those steps are skipped); each thread
+// loads its share of the stage's bf16 scales into registers and writes them to LDS as fp32
+// after the products, so any K that is a multiple of the group runs in the one kernel.
+struct I4Geom {
+  static constexpr int KS = 256;                  // K per stage
+  static constexpr int SUB = KS / 64;             // 64-element steps per stage
+  static constexpr int ROWB = KS / 2;             // 128 bytes of codes per tile row
+  static constexpr int CPR = ROWB / 16;           // 8 chunks
+  static constexpr int RPI = 64 / CPR;            // 8 rows per wave load
+  static constexpr int TILE = kLinTile * ROWB;    // 16 KiB
+  static constexpr int STILE = SUB * kLinTile * 4;   // fp32 scales [4 slots][128 rows]: 2 KiB
+  static constexpr int STAGE = 2 * TILE + 2 * STILE;
+  static constexpr int D = 2;                     // ring depth
+  static constexpr int LDS = D * STAGE;           // 72 KiB
+  static constexpr int CODE_INSTS = kLinTile / RPI / 4;   // 4 loads per wave per operand
+};
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void i4_codes(const LinArgs& p, int64_t mt0, int64_t nt0, int64_t st,
+                                         uint8_t* buf) {
+  using G = I4Geom;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rowbytes = p.K / 2;
+#pragma unroll
+  for (int op = 0; op < 2; ++op) {
+    const uint8_t* codes = op ? p.b : p.a;
+    const int64_t r0 = op ? nt0 : mt0, rows = op ? p.N : p.M;
+    uint8_t* tile = buf + op * G::TILE;
+#pragma unroll
+    for (int ii = 0; ii < G::CODE_INSTS; ++ii) {
+      const int rbase = (wave * G::CODE_INSTS + ii) * G::RPI;
+      const int r = rbase + lane / G::CPR, c = lane % G::CPR;
+      int64_t row = r0 + r;
+      row = row < rows ? row : rows - 1;
+      int64_t off = st * G::ROWB + 16 * (c ^ swz128(r));
+      off = off < rowbytes ? off : 0;   // past K: the row's first chunk (never multiplied)
+      __builtin_amdgcn_global_load_lds((const DQ_GAS void*)(codes + row * rowbytes + off),
+                                       (__attribute__((address_space(3))) void*)(tile + rbase * G::ROWB),
+                                       16, 0, 0);
+    }
+  }
+}
+
+// This thread's share of a stage's scales: tile row t / 2 of both operands; with groups of
+// 64 the two bf16 of steps 2 (t % 2) and +1, with groups of 128 the one bf16 of group t % 2
+// of the stage.  Past K the row's first scale is read (its steps are skipped).
+template <int GS>
+__device__ __forceinline__ void i4_scales_load(const LinArgs& p, int64_t mt0, int64_t nt0,
+                                               int64_t st, uint32_t (&sv)[2]) {
+  const int rr = threadIdx.x >> 1, h = threadIdx.x & 1;
+  const int64_t ng = p.K / (64 * GS);
+#pragma unroll
+  for (int op = 0; op < 2; ++op) {
+    const uint16_t* sc = (const uint16_t*)(op ? p.bs : p.as);
+    const int64_t r0 = op ? nt0 : mt0, rows = op ? p.N : p.M;
+    int64_t row = r0 + rr;
+    row = row < rows ? row : rows - 1;
+    const DQ_GAS uint16_t* sr = gp(sc + row * ng);
+    if (GS == 1) {
+      int64_t g0 = 4 * st + 2 * h, g1 = g0 + 1;
+      g0 = g0 < ng ? g0 : 0;
+      g1 = g1 < ng ? g1 : 0;
+      sv[op] = (uint32_t)sr[g0] | ((uint32_t)sr[g1] << 16);
+    } else {
+      int64_t g0 = 2 * st + h;
+      g0 = g0 < ng ? g0 : 0;
+      sv[op] = sr[g0];
+    }
+  }
+}
+// LDS scale tile of an operand: fp32 [4 slots][128 rows], slot k = the scale of the
+// stage's k-th group (slots 2, 3 unused with groups of 128), so that the scales of four
+// consecutive rows are one 16-byte read.
+template <int GS>
+__device__ __forceinline__ void i4_scales_store(uint8_t* buf, const uint32_t (&sv)[2]) {
+  using G = I4Geom;
+  const int rr = threadIdx.x >> 1, h = threadIdx.x & 1;
+#pragma unroll
+  for (int op = 0; op < 2; ++op) {
+    float* t = (float*)(buf + 2 * G::TILE + op * G::STILE);
+    if (GS == 1) {
+      t[(2 * h) * kLinTile + rr] = u2f(sv[op] << 16);
+      t[(2 * h + 1) * kLinTile + rr] = u2f(sv[op] & 0xFFFF0000u);
+    } else {
+      t[h * kLinTile + rr] = u2f(sv[op] << 16);
+    }
+  }
+}
+
+// 16 nibbles (8 bytes, low nibble first) -> 16 bytes of 16 q for the int8 cores.  The byte
+// order differs from the element order; A and B are unpacked alike.
+__device__ __forceinline__ v4i i4_unpack(uint64_t x) {
+  const uint32_t w0 = (uint32_t)x, w1 = (uint32_t)(x >> 32), m = 0xF0F0F0F0u;
+  return v4i{(int)((w0 << 4) & m), (int)(w0 & m), (int)((w1 << 4) & m), (int)(w1 & m)};
+}
+
+template <int GS, int OUT_BF16>
+__global__ __launch_bounds__(256) void k_linear_i4(LinArgs p) {
+  using G = I4Geom;
+  extern __shared__ __align__(16) uint8_t lin_lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int tm, tn;
+  lin_tile(p.tiles_m * p.tiles_n, p.tiles_m, tm, tn);
+  const int64_t mt0 = (int64_t)tm * kLinTile, nt0 = (int64_t)tn * kLinTile;
+  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int g = lane >> 4, r16 = lane & 15;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int64_t nsub = p.K / 64;
+  const int64_t nst = (nsub + G::SUB - 1) / G::SUB;
+  uint32_t sv[2];
+  if (nst > 0) {
+    i4_scales_load<GS>(p, mt0, nt0, 0, sv);
+    i4_codes(p, mt0, nt0, 0, lin_lds);
+    i4_scales_store<GS>(lin_lds, sv);
+  }
+  for (int64_t st = 0; st < nst; ++st) {
+    // This stage's codes (the only loads outstanding) have landed and every thread has
+    // written its scales; the buffer refilled next was last read before this barrier.
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("s_barrier" ::: "memory");
+    const bool more = st + 1 < nst;
+    uint8_t* nxt = lin_lds + ((st + 1) & 1) * G::STAGE;
+    if (more) {
+      i4_scales_load<GS>(p, mt0, nt0, st + 1, sv);
+      i4_codes(p, mt0, nt0, st + 1, nxt);
+    }
+    const uint8_t* cur = lin_lds + (st & 1) * G::STAGE;
+    const float* sa_t = (const float*)(cur + 2 * G::TILE);
+    const float* sb_t = (const float*)(cur + 2 * G::TILE + G::STILE);
+#pragma unroll
+    for (int k = 0; k < G::SUB / GS; ++k) {
+      if (st * G::SUB + GS * k >= nsub) break;   // the same for the whole workgroup
+      v4i P[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) P[i][j] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int h = 0; h < GS; ++h) {
+        const int u = GS * k + h;   // 64-element step: chunks 2u, 2u + 1 of the row
+        v4i a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ra = wm + 16 * i + r16, rb = wn + 16 * i + r16;
+          const int ca = (2 * u + (g >> 1)) ^ swz128(ra), cb = (2 * u + (g >> 1)) ^ swz128(rb);
+          a[i] = i4_unpack(*(const uint64_t*)(cur + ra * G::ROWB + 16 * ca + 8 * (g & 1)));
+          b[i] = i4_unpack(*(const uint64_t*)(cur + G::TILE + rb * G::ROWB + 16 * cb + 8 * (g & 1)));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            P[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[j], a[i], P[i][j], 0, 0, 0);
+      }
+      // P[i][j][v] belongs to row wm + 16 i + r16 and column wn + 16 j + 4 g + v
+      float sa[4];
+      f32x4 sb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[i] = sa_t[k * kLinTile + wm + 16 * i + r16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sb[j] = *(const f32x4*)(sb_t + k * kLinTile + wn + 16 * j + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            acc[i][j][v] = __builtin_fmaf((float)P[i][j][v], sa[i] * sb[j][v], acc[i][j][v]);
+    }
+    if (more) i4_scales_store<GS>(nxt, sv);
+  }
+
+  lin_store<OUT_BF16>(acc, p, mt0 + wm, nt0 + wn, 1.0f / 256.0f);
+}
+
 }  // namespace dqk

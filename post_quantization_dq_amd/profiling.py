@@ -25,9 +25,16 @@ HERE = Path(__file__).resolve().parent
 
 
 def kernel_source_hash() -> str:
+    """Hash of everything that decides the device code: every source under csrc/ (kernels,
+    launch code) and the compiler flags of the build."""
+    from .build import FLAGS
+
     h = hashlib.sha256()
-    for f in ("dq_device.hpp", "dq_kernels.hpp"):
-        h.update((HERE / "csrc" / f).read_bytes())
+    for f in sorted((HERE / "csrc").iterdir()):
+        if f.suffix in (".hip", ".hpp", ".h"):
+            h.update(f.name.encode())
+            h.update(f.read_bytes())
+    h.update(" ".join(FLAGS).encode())
     return h.hexdigest()[:16]
 
 

@@ -365,3 +365,128 @@ def test_output_offsets_beyond_2_31(oracle_lib, fmt):
     ref, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, fmt, mi, ni, r=r, **kw)
     tol = (_nv_tol if fmt == "NVFP4" else (lambda K_, ab, yy, od: _tol(fmt, K_, ab, yy, od)))(K, absy, ref, torch.bfloat16)
     assert np.all(np.abs(got - ref) <= tol)
+
+
+# ---- INT4 (bf16 scale per group of 64 or 128) on the int8 matrix cores.  Each group's
+# integer dot product is exact in int32; per group the kernel rounds once converting
+# P * sa * sb into fp32 (the int32 and the bf16 scale product are exact) and once adding it
+# to the fp32 sum, then the r multiply rounds: |y - ref| <= (K/g + 3) 2^-24 sum |a b| |r|.
+
+def _i4_inputs(M, N, K, g, seed):
+    rng = np.random.default_rng(seed)
+    a = pack_codes(rng.integers(0, 16, M * K).astype(np.uint8), 4)     # nibble 8 = -8 included
+    b = pack_codes(rng.integers(0, 16, N * K).astype(np.uint8), 4)
+    bf = lambda x: (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    asc = bf(np.exp2(rng.uniform(-8, 8, M * K // g)) * rng.uniform(1, 2, M * K // g))
+    bsc = bf(np.exp2(rng.uniform(-8, 8, N * K // g)) * rng.uniform(1, 2, N * K // g))
+    r = np.exp2(rng.uniform(-2, 2, N)).astype(np.float32)
+    return a, asc, b, bsc, r
+
+
+def _i4_tol(K, g, absy, y, out_dtype):
+    t = (K // g + 3) * 2.0 ** -24 * absy
+    if out_dtype == torch.bfloat16:
+        t = t + 2.0 ** -8 * (np.abs(y) + t)
+    return t + 1e-37
+
+
+def _i4_run(a, asc, b, bsc, M, N, K, g, r, out_dtype):
+    dev = lambda x: torch.from_numpy(x).to(DEV)
+    y = dq.quantized_linear(dev(a), dev(asc.view(np.int16)), dev(b), dev(bsc.view(np.int16)),
+                            M, N, K, "INT4", r=None if r is None else to_dev(r),
+                            out_dtype=out_dtype, group=g)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("g", [64, 128])
+@pytest.mark.parametrize("shape", [(100, 70, 384), (1, 16, 128), (130, 257, 4224), (256, 256, 1024),
+                                   (3, 5, 64)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_int4_random_codes(oracle_lib, g, shape, out_dtype):
+    """Ragged M and N tiles; K = 384 and 4224 end in a half stage, K = 64 (groups of 64
+    only) in a quarter stage."""
+    M, N, K = shape
+    if K % g:
+        pytest.skip("K is not a multiple of the group")
+    print(f"[linear] INT4 g{g} {M}x{N}x{K} {out_dtype}", flush=True)
+    a, asc, b, bsc, r = _i4_inputs(M, N, K, g, M + N + K + g)
+    for rr in (r, None):
+        y = _i4_run(a, asc, b, bsc, M, N, K, g, rr, out_dtype)
+        ref = oracle_lib.quantized_linear(a, asc, M, b, bsc, N, K, "INT4", r=rr, group=g)
+        mi, ni = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        _, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, "INT4", mi.ravel(),
+                                                      ni.ravel(), r=rr, group=g)
+        absy = absy.reshape(M, N)
+        err = np.abs(y - ref)
+        print(f"[linear] INT4 max err / sum|ab| = {float((err / (absy + 1e-300)).max()):.3g}", flush=True)
+        assert np.all(err <= _i4_tol(K, g, absy, ref, out_dtype))
+
+
+def test_int4_exact_small_integers(oracle_lib):
+    """Scales 1.0 and K = 256: every output is an integer below 2^24, so the layer is exact."""
+    M, N, K = 64, 48, 256
+    rng = np.random.default_rng(21)
+    a = pack_codes(rng.integers(0, 16, M * K).astype(np.uint8), 4)
+    b = pack_codes(rng.integers(0, 16, N * K).astype(np.uint8), 4)
+    asc = np.full(M * K // 64, 0x3F80, np.uint16)
+    bsc = np.full(N * K // 64, 0x3F80, np.uint16)
+    y = _i4_run(a, asc, b, bsc, M, N, K, 64, None, torch.float32)
+    ref = oracle_lib.quantized_linear(a, asc, M, b, bsc, N, K, "INT4", group=64)
+    assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("K", [4096, 14336])
+def test_int4_full_size_sampled(oracle_lib, K):
+    """2048 tokens x 4096 outputs x K inputs (the q/o and the down projection), groups of
+    64: 384 sampled entries, the four corners among them."""
+    M, N, g = 2048, 4096, 64
+    print(f"[linear] INT4 g64 {M}x{N}x{K}", flush=True)
+    a, asc, b, bsc, r = _i4_inputs(M, N, K, g, K)
+    y = _i4_run(a, asc, b, bsc, M, N, K, g, r, torch.float32)
+    rng = np.random.default_rng(K + 1)
+    mi, ni = rng.integers(0, M, 384), rng.integers(0, N, 384)
+    mi[:4], ni[:4] = [0, M - 1, 0, M - 1], [0, 0, N - 1, N - 1]
+    ref, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, "INT4", mi, ni, r=r,
+                                                    group=g)
+    assert np.all(np.abs(y[mi, ni] - ref) <= _i4_tol(K, g, absy, ref, torch.float32))
+
+
+def test_int4_layer_from_solved_weights(oracle_lib):
+    """W4A4 with INT4 groups of 64 end to end on a 512 x 4096 slice of a weight: solve
+    (T = 4), quantise 256 tokens with the solved column scales, run the layer; the output
+    matches the oracle's product of the same codes and approximates X W^T."""
+    W, _, _, _, _ = synth.workload("q4096x4096_mxfp4")
+    W = np.ascontiguousarray(W[:512])
+    X = synth.matrix(synth.WORKLOADS["k1024x4096_mxint4"]["X"].scaled(256, 4096), 3)
+    res = dq.solve(to_dev(W), "INT4", 4, group=64)
+    codes_x, scales_x, _ = dq.rescale_quantize_acts(to_dev(X), res["c"], "INT4", group=64)
+    y = dq.quantized_linear(codes_x, scales_x, res["codes"], res["scales"], 256, 512, 4096, "INT4",
+                            r=res["r"], group=64)
+    torch.cuda.synchronize()
+    yc = y.cpu().numpy().astype(np.float64)
+    u16 = lambda t: t.cpu().numpy().view(np.uint16)
+    args = (codes_x.cpu().numpy(), u16(scales_x), 256, res["codes"].cpu().numpy(),
+            u16(res["scales"]), 512, 4096, "INT4")
+    rn = res["r"].cpu().numpy()
+    ref = oracle_lib.quantized_linear(*args, r=rn, group=64)
+    mi, ni = np.meshgrid(np.arange(256), np.arange(512), indexing="ij")
+    _, absy = oracle_lib.quantized_linear_entries(*args, mi.ravel(), ni.ravel(), r=rn, group=64)
+    assert np.all(np.abs(yc - ref) <= _i4_tol(4096, 64, absy.reshape(256, 512), ref, torch.float32))
+    Xf = (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    Wf = (W.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    exact = Xf @ Wf.T
+    rel = np.linalg.norm(yc - exact) / np.linalg.norm(exact)
+    print(f"[linear] W4A4 INT4 g64 layer relative error vs bf16 product: {rel:.4f}", flush=True)
+    assert rel < 0.5
+
+
+def test_int4_argument_errors():
+    """Host-side checks, before any launch: K not a multiple of the group, odd scale address."""
+    z = lambda n, dt=torch.uint8: torch.zeros(n, dtype=dt, device=DEV)
+    with pytest.raises(RuntimeError):
+        dq.quantized_linear(z(48), z(2, torch.int16), z(48), z(2, torch.int16), 1, 1, 96, "INT4",
+                            group=64)
+    buf = z(64)
+    with pytest.raises(RuntimeError):
+        dq.quantized_linear(z(32), buf[1:5], z(32), z(2, torch.int16), 1, 1, 64, "INT4", group=64)
