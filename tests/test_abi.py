@@ -127,7 +127,12 @@ def test_quantized_linear_argument_errors(dq):
         return L.dq_quantized_linear(spec, ac, asc, ats, M, bc, bsc, bts, N, K, r, y, dt, ldy, None)
 
     assert call(dq.dq_quant_spec(1, 0)) == -4            # MXINT4 (recode it first)
-    assert call(dq.dq_quant_spec(0, 0)) == -4            # INT4
+    assert call(dq.dq_quant_spec(4, 64)) == -4           # INT8 has no layer
+    assert call(dq.dq_quant_spec(0, 32)) == -4           # INT4 groups are 64 or 128
+    assert call(dq.dq_quant_spec(0, 64), K=96) == -2     # K not a multiple of the group
+    assert call(dq.dq_quant_spec(0, 128), K=192) == -2
+    assert call(dq.dq_quant_spec(0, 64), asc=0x20001) == -3   # bf16 scales at an odd address
+    assert call(dq.dq_quant_spec(0, 64), bsc=0x40001) == -3
     assert call(mx, dt=5) == -4                          # output dtype
     assert call(mx, ldy=63) == -2                        # ldy < N
     assert call(mx, K=100) == -2                         # K not a multiple of 32
