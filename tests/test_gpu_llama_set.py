@@ -1,8 +1,8 @@
 """The full synthetic Llama-3.1-8B projection set (32 layers x q, k, v, o, gate, up, down;
 6.98 G weights, 14 GB bf16), NVFP4, 20 BCD iterations, solved as ONE batch on the GPU.
 
-Three members are drawn with the numpy generator the oracle shares and compared with the
-oracle end to end; one of them is also solved alone and must equal its batched result
+Five members (the two 14336-long shapes among them) are drawn with the numpy generator the
+oracle shares and compared with the oracle end to end; one of them is also solved alone and must equal its batched result
 bit for bit.  Every member is checked for the properties that hold at any size: all 20
 iterations run, the normalised MSE never increases and ends no worse than the start, the
 scales are finite and admissible.
@@ -20,7 +20,9 @@ from test_gpu_solve import _compare_e2e
 pytestmark = pytest.mark.gpu
 
 T = 20
-SAMPLED = {(0, 1), (0, 2), (31, 1)}   # (layer, projection): k and v of layer 0, k of layer 31
+# (layer, projection): k and v of layer 0, k of layer 31, gate of layer 17 (14336 rows) and
+# down of layer 5 (14336 columns)
+SAMPLED = {(0, 1), (0, 2), (31, 1), (17, 4), (5, 6)}
 
 
 def test_llama31_8b_set_batched(oracle_lib):
