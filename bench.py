@@ -45,22 +45,23 @@ METRIC = "BCD solver Gelem/s per iteration + achieved HBM GB/s vs peak (4096×14
 
 
 KERNELS = ("k_rowpass", "k_colpass", "k_finalize")
-# The row pass is bound by VALU issue: 377 VALU instructions per 16-element chunk in a normal
-# sweep (NVFP4 codes, bf16 weight; counted in the gfx950 assembly) against 256 CUs x 64 lanes
-# x 2.4 GHz = 39.3 T lane-operations/s (unpacked fp32).
-ROWPASS_VALU_PER_ELEM = {("NVFP4", 2): 377 / 16}
+# The row pass leans on VALU issue: 306 VALU instructions per wave and 64 chunks of 16
+# elements (NVFP4 codes, bf16 weight; SQ_INSTS_VALU per working dispatch over its 57344
+# wave-trips), i.e. 306 / 16 lane-operations per element, against 256 CUs x 64 lanes x 2.4 GHz
+# = 39.3 T lane-operations/s (unpacked fp32).
+ROWPASS_VALU_PER_ELEM = {("NVFP4", 2): 306 / 16}
 VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9
 
 
 def recorded_traffic(kernel: str, workload: str):
     """Counter-measured HBM bytes per launch of `kernel` from profiles/, if the counters were
     taken on the current kernel source."""
-    f = ROOT / "profiles" / f"{kernel}_{workload}_counters.md"
+    f = ROOT / "profiles" / f"solver_{workload}_counters.md"
     if not f.exists():
         return None
     text = f.read_text()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch\[" + re.escape(kernel) + r"\]:\s*([0-9.eE+]+)", text)
     from post_quantization_dq_amd.profiling import kernel_source_hash
 
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
@@ -312,10 +313,15 @@ def main():
     ap.add_argument("--format", default=None,
                     help="solve the workload's weight in another format (e.g. INT8, MXINT8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mall-cold", action="store_true",
+                    help="solve three copies of the weight as one batch, so that each pass "
+                         "streams 3x the bytes and no matrix is still in the 256 MB MALL when "
+                         "the next pass reads it again")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.steps is None:
         args.steps = {"llama31_8b_nvfp4": 5, "linear_w4a4_mxfp4": 20, "linear_w4a4_nvfp4": 20,
+                      "linear_w4a4_int4": 20,
                       "qkv_acts_nvfp4": 20}.get(args.workload, 200)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -347,16 +353,20 @@ def main():
         fmt, group = args.format, None
     W_np = synth.matrix(wl["W"], 0)
     m, n = W_np.shape
+    copies = 3 if args.mall_cold else 1
     xspec = synth.MatrixSpec(ACT_TOKENS, n, "normal", 1.0, outliers=synth.outlier_count(n, 0.01),
                              outlier_scale=50.0, stream=9)
     X_np = synth.matrix(xspec, 0)
-    W = torch.from_numpy(W_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    Ws = [torch.from_numpy(W_np.view(np.int16)).view(torch.bfloat16).to(dev) for _ in range(copies)]
+    W = Ws[0]
     X = torch.from_numpy(X_np.view(np.int16)).view(torch.bfloat16).to(dev)
-    print(f"[bench] workload {args.workload}: W {m}x{n} bf16, {fmt}, T={T}; acts {ACT_TOKENS}x{n}", flush=True)
+    print(f"[bench] workload {args.workload}: W {m}x{n} bf16 x{copies}, {fmt}, T={T}; acts {ACT_TOKENS}x{n}",
+          flush=True)
 
-    prob = dq.make_problem(W, fmt, T, group)
+    probs = [dq.make_problem(Wk, fmt, T, group) for Wk in Ws]
+    prob = probs[0]
     spec = dq.spec_of(fmt, group)
-    ws = torch.empty(dq.dq_workspace_bytes([prob], spec, dq.dq_solve_opts(T, 0.0, 0)),
+    ws = torch.empty(dq.dq_workspace_bytes(probs, spec, dq.dq_solve_opts(T, 0.0, 0)),
                      dtype=torch.uint8, device=dev)
     a_codes, a_scales, a_ts = dq._outputs(ACT_TOKENS, n, fmt, group or dq.DEFAULT_GROUP[fmt], dev)
     a_ws = torch.empty(max(1, dq.dq_quantize_workspace_bytes(ACT_TOKENS, n, spec)), dtype=torch.uint8, device=dev)
@@ -364,7 +374,7 @@ def main():
     def step(passes=None):
         # enqueued only: nothing on the host waits for the GPU (the diagnostic timed solve,
         # used for one step, synchronises to read its events)
-        dq.solve_many([prob], fmt, T, group, workspace=ws, pass_ms=passes, read_reports=False)
+        dq.solve_many(probs, fmt, T, group, workspace=ws, pass_ms=passes, read_reports=False)
         dq.dq_rescale_quantize_acts(X, prob.c, spec, a_codes, a_scales, a_ts, a_ws)
 
     for _ in range(args.warmup):
@@ -393,13 +403,13 @@ def main():
     per_step = {k: float(per[:, q].sum()) for q, k in enumerate(KERNELS)}
     dom = max(KERNELS[:2], key=lambda k: per_step[k])
     print("[bench] per-launch ms: " + ", ".join(f"{k} {avg[k] * 1e3:.1f} us" for k in KERNELS), flush=True)
-    # algorithmic bytes of one pass over W: one read of W plus the r and c vectors
-    alg_bytes = m * n * W.element_size() + 8 * (m + n)
+    # algorithmic bytes of one pass over W: one read of W plus the r and c vectors (per copy)
+    alg_bytes = copies * (m * n * W.element_size() + 8 * (m + n))
     achieved = alg_bytes / (avg[dom] * 1e-3) / 1e9
     t_iter_ms = float(per.sum(axis=1).mean())
-    traffic = recorded_traffic(dom, args.workload)
+    traffic = recorded_traffic(dom, args.workload) if copies == 1 else None
     nm = prob.nmse_hist.cpu().numpy()
-    value = m * n * T / (ms_step * 1e-3) / 1e9
+    value = copies * m * n * T / (ms_step * 1e-3) / 1e9
 
     out = {
         "metric": METRIC if (m, n, fmt) == (4096, 14336, "NVFP4")
@@ -421,6 +431,7 @@ def main():
                         f"g={group or dq.DEFAULT_GROUP[fmt]}, {T} BCD iterations; then "
                         f"{ACT_TOKENS}x{n} bf16 activations rescaled by c and {fmt}-quantised",
             "rows": m, "cols": n, "format": fmt, "iters": T, "act_tokens": ACT_TOKENS,
+            "copies": copies,
         },
         "roofline": {
             "bound": "hbm",
@@ -450,7 +461,11 @@ def main():
                                    "peak_lane_ops": round(VALU_PEAK_LANE_OPS / 1e12, 2),
                                    "unit": "T lane-ops/s",
                                    "frac": round(lane_ops / VALU_PEAK_LANE_OPS, 4)}
-    if not args.no_cpu_baseline:
+    if copies > 1:
+        out["config"]["workload"] = (f"MALL-cold: {copies} copies of the weight solved as one batch "
+                                     f"({copies * m * n * W.element_size() / 1e6:.0f} MB per pass); "
+                                     + out["config"]["workload"])
+    if not args.no_cpu_baseline and copies == 1:
         print("[bench] timing the CPU oracle on a bounded sample ...", flush=True)
         out["cpu_baseline"] = cpu_baseline(W_np, X_np, fmt, T)
     print(json.dumps(out), flush=True)
