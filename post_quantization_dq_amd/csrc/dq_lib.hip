@@ -187,10 +187,11 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     pl.group_of[k] = it->second;
   }
   // Rows per row-pass workgroup.  A single matrix or a small batch takes the smallest block
-  // of at least 16 rows that puts every block in one round of one workgroup per CU, so the
-  // CUs share the rows evenly (5120 rows: 256 blocks of 20, not 160 blocks of 32 with 96
-  // CUs idle).  Otherwise: 16 rows per wave-round, at most kMaxRowsPerBlk (a large batch
-  // splits into many similar workgroups, balanced by the dispatcher).
+  // that puts every block in one round of one workgroup per CU, so the CUs share the rows
+  // evenly (5120 rows: 256 blocks of 20, not 160 blocks of 32 with 96 CUs idle; 1024 rows:
+  // 256 blocks of 4, some waves idle, rather than 64 blocks of 16 on a quarter of the CUs).
+  // Otherwise: 16 rows per wave-round, at most kMaxRowsPerBlk (a large batch splits into
+  // many similar workgroups, balanced by the dispatcher).
   const int64_t rows_per_wave = std::max<int64_t>(1, (total_rows + kTargetRowWaves - 1) / kTargetRowWaves);
   int64_t rows_per_blk = std::min<int64_t>(kMaxRowsPerBlk, kRowWaves * rows_per_wave);
   {
@@ -198,7 +199,7 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     for (int k = 0; k < count; ++k)
       if (pl.group_of[k] >= 0) rows_of.push_back(p[k].rows);
     if (!rows_of.empty() && rows_of.size() <= (size_t)kRowWgs) {
-      for (int64_t b = std::max<int64_t>(kRowWaves, (total_rows + kRowWgs - 1) / kRowWgs);
+      for (int64_t b = std::max<int64_t>(1, (total_rows + kRowWgs - 1) / kRowWgs);
            b <= kMaxRowsPerBlk; ++b) {
         int64_t wgs = 0;
         for (int64_t m : rows_of) wgs += (m + b - 1) / b;
