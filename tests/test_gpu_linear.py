@@ -287,27 +287,33 @@ def test_nvfp4_layer_from_solved_weights(oracle_lib):
     assert rel < 0.5
 
 
-@pytest.mark.parametrize("fmt", ["MXFP4", "MXFP6_E2M3", "NVFP4"])
+@pytest.mark.parametrize("fmt", ["MXFP4", "MXFP6_E2M3", "NVFP4", "INT4"])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_output_row_pitch(oracle_lib, fmt, out_dtype):
     """Y written into a wider buffer (ldy = N + 37): the columns past N keep their contents,
     the first N equal the contiguous call bitwise (direct-to-LDS, register-staged and NVFP4
     kernels)."""
     M, N, K = 130, 100, 512
+    group = None
     if fmt == "NVFP4":
         a, asc, b, bsc, r, ats, bts = _nv_inputs(M, N, K, 21)
         ts = dict(a_tensor_scale=to_dev(np.array([ats])), b_tensor_scale=to_dev(np.array([bts])))
+    elif fmt == "INT4":
+        group = 64
+        a, asc, b, bsc, r = _i4_inputs(M, N, K, group, 21)
+        asc, bsc = asc.view(np.int16), bsc.view(np.int16)
+        ts = dict(a_tensor_scale=None, b_tensor_scale=None)
     else:
         a, asc, b, bsc, r = _inputs(fmt, M, N, K, 21)
         ts = dict(a_tensor_scale=None, b_tensor_scale=None)
     dev = lambda x: torch.from_numpy(x).to(DEV)
     A, As, B, Bs, R = dev(a), dev(asc), dev(b), dev(bsc), to_dev(r)
-    y0 = dq.quantized_linear(A, As, B, Bs, M, N, K, fmt, r=R, out_dtype=out_dtype, **ts)
+    y0 = dq.quantized_linear(A, As, B, Bs, M, N, K, fmt, r=R, out_dtype=out_dtype, group=group, **ts)
     wide = torch.full((M, N + 37), -7.0, dtype=out_dtype, device=DEV)
     view = wide[:, :N]
     assert view.stride(0) == N + 37
-    dq.dq_quantized_linear(dq.spec_of(fmt), A, As, ts["a_tensor_scale"], M, B, Bs, ts["b_tensor_scale"],
-                           N, K, R, view)
+    dq.dq_quantized_linear(dq.spec_of(fmt, group), A, As, ts["a_tensor_scale"], M, B, Bs,
+                           ts["b_tensor_scale"], N, K, R, view)
     torch.cuda.synchronize()
     assert torch.equal(view, y0)
     assert torch.all(wide[:, N:] == -7.0)

@@ -320,6 +320,22 @@ def test_teacher_forced_step(oracle_lib, fmt):
         assert rel_err(got["nmse"][0], ref["nmse"][0]) <= 1e-6
 
 
+@pytest.mark.parametrize("fmt,group,name,rows,cols", [("NVFP4", None, "down4096x14336_nvfp4", 96, 2048),
+                                                    ("MXFP4", None, "q4096x4096_mxfp4", 130, 1024),
+                                                    ("INT4", 64, "w256x512_int4", 256, 512)])
+def test_end_to_end_from_given_scales(oracle_lib, fmt, group, name, rows, cols):
+    """A whole solve started from caller-given admissible scales (r_init, c_init), strict
+    parity with the oracle started from the same scales."""
+    W = synth.matrix(synth.WORKLOADS[name]["W"].scaled(rows, cols), 2)
+    rng = np.random.default_rng(rows + cols)
+    r0 = oracle_lib.project(fmt, np.exp2(rng.uniform(-1, 1, rows)).astype(np.float32))
+    c0 = oracle_lib.project(fmt, np.exp2(rng.uniform(-1, 1, cols)).astype(np.float32))
+    T = 8
+    got = _gpu_solve(W, fmt, T, group=group, r_init=to_dev(r0), c_init=to_dev(c0), trace=True)
+    _compare_e2e(oracle_lib, W, fmt, T, got, f"{name} {fmt} from given scales", group=group,
+                 r_init=r0, c_init=c0)
+
+
 @pytest.mark.parametrize("fmt", ALL_FORMATS)
 def test_iteration_zero_is_bit_exact(oracle_lib, fmt):
     W = synth.matrix(synth.WORKLOADS["down4096x14336_nvfp4"]["W"].scaled(77, 2048), 1)
