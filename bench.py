@@ -21,6 +21,8 @@ on this host.
   python bench.py --workload linear_w4a4_nvfp4   # the same layer in NVFP4 (f16 cores)
   python bench.py --workload linear_w4a4_int4    # the same layer in INT4, groups of 64 (int8 cores)
   python bench.py --workload qkv_acts_nvfp4      # fused q/k/v activation quantise
+  python bench.py --workload llama31_8b_w4a4 [--tokens 82|1312]   # a W4A4 INT4 g64 forward's
+                                                 # activation quantise + 224 layers
 """
 
 from __future__ import annotations
@@ -244,6 +246,118 @@ def bench_linear(args, fmt):
     print(json.dumps(out), flush=True)
 
 
+def bench_llama_w4a4(args):
+    """The pages' deployed path on Llama-3.1-8B shapes (the listing page's Table 11 splits a
+    W4A4 forward into "activation quantization (incl. beta)" and "quantized linears (224)"):
+    the 224 projection weights are solved to INT4 with groups of 64 (T = 20, one batched
+    dq_solve), then one forward of `tokens` tokens runs, layer by layer, the activation
+    rescale-and-quantise with each projection's solved c (q/k/v and gate/up fused, as they
+    read the same activations) and the 7 INT4 layers on the int8 cores.  The whole forward,
+    the 224 layers alone and the activation quantisation alone are timed with events."""
+    import torch
+
+    import post_quantization_dq_amd as dq
+    import synth
+
+    dev = torch.device("cuda:0")
+    fmt, g, T, tokens = "INT4", 64, 20, args.tokens
+    spec = dq.spec_of(fmt, g)
+    L, P = synth.LLAMA31_8B_LAYERS, synth.LLAMA31_8B_PROJ
+    probs = []
+    for layer in range(L):
+        for pi in range(len(P)):
+            W = synth.matrix_device(synth.llama_projection_spec(layer, pi), 0, dev)
+            probs.append(dq.make_problem(W, fmt, T, g))
+    ws = torch.empty(dq.dq_workspace_bytes(probs, spec, dq.dq_solve_opts(T, 0.0, 0)),
+                     dtype=torch.uint8, device=dev)
+    dq.solve_many(probs, fmt, T, g, workspace=ws, read_reports=False)
+    torch.cuda.synchronize()
+    del ws
+    for p in probs:
+        p.W = None   # the bf16 weights are not needed by the forward
+    torch.cuda.empty_cache()
+    elems = sum(r * c for _, r, c in P) * L
+    print(f"[bench] llama31_8b W4A4 INT4 g64: 224 weights solved (T={T}); forward of {tokens} tokens",
+          flush=True)
+
+    # activations: one bf16 input per projection group, shared by the layers
+    xs = {}
+    for name, K in (("qkv", 4096), ("o", 4096), ("gu", 4096), ("down", 14336)):
+        spec_x = synth.MatrixSpec(tokens, K, "normal", 1.0, outliers=synth.outlier_count(K, 0.01),
+                                  outlier_scale=50.0, stream=11)
+        xs[name] = torch.from_numpy(synth.matrix(spec_x, 0).view(np.int16)).view(torch.bfloat16).to(dev)
+    groups = (("qkv", (0, 1, 2)), ("o", (3,)), ("gu", (4, 5)), ("down", (6,)))
+    acts = {}   # (layer, proj) -> (codes, scales, tscale)
+    for layer in range(L):
+        for name, pis in groups:
+            K = xs[name].shape[1]
+            for pi in pis:
+                acts[(layer, pi)] = dq._outputs(tokens, K, fmt, g, dev)
+    qws = torch.empty(max(1, dq.dq_quantize_multi_workspace_bytes(tokens, 14336, 3, spec)),
+                      dtype=torch.uint8, device=dev)
+    ys = [torch.empty(tokens, r, dtype=torch.bfloat16, device=dev) for _, r, _ in P]
+    # split-K workspace for the few-token shapes (one buffer: the launches are stream-ordered)
+    lws_bytes = max(dq.dq_quantized_linear_workspace_bytes(spec, tokens, N, K) for _, N, K in P)
+    lws = torch.empty(max(lws_bytes, 16), dtype=torch.uint8, device=dev) if lws_bytes else None
+
+    def quantise(layer):
+        for name, pis in groups:
+            probs_l = [probs[layer * len(P) + pi] for pi in pis]
+            outs = [acts[(layer, pi)] for pi in pis]
+            dq.dq_rescale_quantize_acts_multi(xs[name], [p.c for p in probs_l], spec,
+                                              [o[0] for o in outs], [o[1] for o in outs],
+                                              [o[2] for o in outs], qws)
+
+    def linears(layer):
+        for pi, (_, N, K) in enumerate(P):
+            p = probs[layer * len(P) + pi]
+            a = acts[(layer, pi)]
+            dq.dq_quantized_linear_ws(spec, a[0], a[1], None, tokens, p.codes, p.block_scales, None,
+                                      N, K, p.r, ys[pi], lws)
+
+    def forward():
+        for layer in range(L):
+            quantise(layer)
+            linears(layer)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_fwd = timed(forward)
+    ms_lin = timed(lambda: [linears(layer) for layer in range(L)])
+    ms_act = timed(lambda: [quantise(layer) for layer in range(L)])
+    tops = 2.0 * tokens * elems / (ms_lin * 1e-3) / 1e12
+    out = {
+        "metric": "W4A4 INT4 g64 Llama-3.1-8B-shaped forward: activation quantisation (incl. beta) "
+                  "and the 224 quantised linears, ms per forward",
+        "value": round(ms_fwd, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_fwd, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4", "data": "synthetic",
+        "config": {"workload": f"224 Llama-3.1-8B-shaped projections solved to INT4 g64 (T={T}); "
+                               f"{tokens} tokens per forward; q/k/v and gate/up activations "
+                               "quantised together", "tokens": tokens, "elements": elems},
+        "linears_ms": round(ms_lin, 4), "act_quant_ms": round(ms_act, 4),
+        "split_k_workspace_bytes": int(lws_bytes),
+        "roofline": {"bound": "mfma", "kernel": "k_linear_i4 (all 224 launches)",
+                     "achieved": round(tops, 1), "peak": I8_MFMA_PEAK_TOPS, "unit": "TOP/s",
+                     "frac": round(tops / I8_MFMA_PEAK_TOPS, 4), "traffic": None},
+        # the pages' RTX 4090 figures for the same split (listing page Table 11, Llama-3.1-8B,
+        # INT4 G=64; prefill b=1 is 82 tokens, b=16 is 1312): context only, another machine
+        "context_rtx4090_ms": {"quantized_linears_224": {"82": 8.82, "1312": 32.98},
+                               "activation_quantization": {"82": 0.82, "1312": 3.09}},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_qkv_acts(args):
     """The fused multi-projection activation quantiser: 2048 tokens x 4096 bf16 activations
     quantised to NVFP4 for three projections (q, k, v), each with its own column scales, in
@@ -315,6 +429,9 @@ def main():
     ap.add_argument("--group", type=int, default=None,
                     help="group size with --format INT4 / INT8 (64 or 128; default 128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tokens", type=int, default=1312,
+                    help="tokens per forward for --workload llama31_8b_w4a4 (82: prefill b=1, "
+                         "1312: prefill b=16)")
     ap.add_argument("--mall-cold", action="store_true",
                     help="solve three copies of the weight as one batch, so that each pass "
                          "streams 3x the bytes and no matrix is still in the 256 MB MALL when "
@@ -323,7 +440,7 @@ def main():
     args = ap.parse_args()
     if args.steps is None:
         args.steps = {"llama31_8b_nvfp4": 5, "linear_w4a4_mxfp4": 20, "linear_w4a4_nvfp4": 20,
-                      "linear_w4a4_int4": 20,
+                      "linear_w4a4_int4": 20, "llama31_8b_w4a4": 10,
                       "qkv_acts_nvfp4": 20}.get(args.workload, 200)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -341,6 +458,9 @@ def main():
         return
     if args.workload == "qkv_acts_nvfp4":
         bench_qkv_acts(args)
+        return
+    if args.workload == "llama31_8b_w4a4":
+        bench_llama_w4a4(args)
         return
 
     import torch

@@ -255,15 +255,17 @@ int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t token
  * dequantised with its block scale (and, for NVFP4, its tensor scale).  With
  * W ~ diag(r) Q diag(c) this is Y ~ X W^T.
  *   spec       DQ_FMT_MXFP4, DQ_FMT_MXFP6_E2M3/E3M2, DQ_FMT_MXFP8_E4M3/E5M2 (group 32) on
- *              the block-scaled cores, or DQ_FMT_NVFP4 (group 16) on the f16 cores: its
+ *              the block-scaled cores, DQ_FMT_NVFP4 (group 16) on the f16 cores: its
  *              elements e2m1 * e4m3 are exact in fp16 and the tensor scales multiply the
- *              fp32 result.  The same format for both operands (MXINT4: see
- *              dq_recode_mxint4_to_mxfp6).
+ *              fp32 result; or DQ_FMT_INT4 (group 64 or 128, bf16 scales) on the int8 cores:
+ *              each group's integer dot product is exact in int32, then multiplied by the
+ *              two bf16 scales' product (exact in fp32) and added in fp32.  The same format
+ *              for both operands (MXINT4: see dq_recode_mxint4_to_mxfp6).
  *   a_codes    [M][K] activation codes in the format's layout (row pitch K*bits/8 bytes),
- *              16-byte aligned; a_scales [M][K/group] scale bytes; a_tensor_scale [1] fp32
- *              (NVFP4 only, else ignored and may be NULL).
+ *              16-byte aligned; a_scales [M][K/group] scale bytes (INT4: bf16 values, 2-byte
+ *              aligned); a_tensor_scale [1] fp32 (NVFP4 only, else ignored and may be NULL).
  *   b_codes    [N][K] weight codes, 16-byte aligned; b_scales [N][K/group]; b_tensor_scale.
- *   K          a multiple of 32 (0 gives Y = 0).
+ *   K          a multiple of 32 (INT4: of the group; 0 gives Y = 0).
  *   r          [N] fp32 row scales of the weights, or NULL (ones).
  *   y          [M][ldy] output, fp32 (y_dtype DQ_F32) or bf16 (DQ_BF16, round to nearest
  *              even); ldy >= N.
@@ -281,6 +283,28 @@ int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_
                         const uint8_t* b_scales, const float* b_tensor_scale, int64_t N,
                         int64_t K, const float* r, void* y, int32_t y_dtype, int64_t ldy,
                         void* stream);
+
+/* The same layer with a caller workspace, which lets an INT4 layer with few output tiles
+ * (few tokens: the listing page's Table 11 forwards of 82 tokens, and decoding) split K
+ * over several workgroups per tile: each writes unscaled fp32 partial sums to the
+ * workspace and a second kernel adds them in split order and applies 2^-8 and r.  The sum
+ * order differs from the unsplit kernel's (one more fp32 rounding per split: the bound is
+ * (K/group + splits + 3) 2^-24 sum |a b| |r|); a given shape always splits the same way, so
+ * results are reproducible.  Other formats, and INT4 shapes that fill the GPU without it,
+ * ignore the workspace.
+ *   workspace         16-byte-aligned device memory of at least
+ *                     dq_quantized_linear_workspace_bytes(spec, M, N, K) bytes, or NULL (no
+ *                     split: the same as dq_quantized_linear).
+ * Returns DQ_ERR_WORKSPACE when a non-NULL workspace is smaller than required, DQ_ERR_ALIGN
+ * when it is misaligned; otherwise as dq_quantized_linear.  Asynchronous. */
+int dq_quantized_linear_ws(dq_quant_spec spec, const uint8_t* a_codes, const uint8_t* a_scales,
+                           const float* a_tensor_scale, int64_t M, const uint8_t* b_codes,
+                           const uint8_t* b_scales, const float* b_tensor_scale, int64_t N,
+                           int64_t K, const float* r, void* y, int32_t y_dtype, int64_t ldy,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes dq_quantized_linear_ws uses for this shape (0: it does not split). */
+size_t dq_quantized_linear_workspace_bytes(dq_quant_spec spec, int64_t M, int64_t N, int64_t K);
 
 /* Exact re-encoding of MXINT4 codes as MXFP6 E2M3 codes, so that MXINT4 activations and
  * weights can run through dq_quantized_linear (whose matrix cores take FP4/FP6/FP8 elements

@@ -92,6 +92,11 @@ _lib.dq_rescale_quantize_acts_multi.restype = C.c_int
 _lib.dq_quantized_linear.argtypes = [dq_quant_spec, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64,
                                      _vp, _vp, _i32, _i64, _vp]
 _lib.dq_quantized_linear.restype = C.c_int
+_lib.dq_quantized_linear_ws.argtypes = [dq_quant_spec, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64,
+                                        _vp, _vp, _i32, _i64, _vp, _sz, _vp]
+_lib.dq_quantized_linear_ws.restype = C.c_int
+_lib.dq_quantized_linear_workspace_bytes.argtypes = [dq_quant_spec, _i64, _i64, _i64]
+_lib.dq_quantized_linear_workspace_bytes.restype = _sz
 _lib.dq_recode_mxint4_to_mxfp6.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp]
 _lib.dq_recode_mxint4_to_mxfp6.restype = C.c_int
 _lib.dq_dequantize.argtypes = [dq_quant_spec, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]
@@ -103,7 +108,8 @@ EXPORTED = ("dq_workspace_bytes", "dq_solve", "dq_solve_timed", "dq_quantize_wor
             "dq_quantize_weights",
             "dq_rescale_quantize_acts", "dq_rescale_quantize_acts_noalloc",
             "dq_quantize_multi_workspace_bytes",
-            "dq_rescale_quantize_acts_multi", "dq_quantized_linear", "dq_recode_mxint4_to_mxfp6",
+            "dq_rescale_quantize_acts_multi", "dq_quantized_linear", "dq_quantized_linear_ws",
+            "dq_quantized_linear_workspace_bytes", "dq_recode_mxint4_to_mxfp6",
             "dq_dequantize",
             "dq_status_string", "dq_debug_round")
 
@@ -278,6 +284,21 @@ def dq_quantized_linear(spec, a_codes, a_scales, a_tensor_scale, M, b_codes, b_s
            "dq_quantized_linear")
 
 
+def dq_quantized_linear_ws(spec, a_codes, a_scales, a_tensor_scale, M, b_codes, b_scales,
+                           b_tensor_scale, N, K, r, y, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.dq_quantized_linear_ws(spec, _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), M,
+                                       _ptr(b_codes), _ptr(b_scales), _ptr(b_tensor_scale), N, K,
+                                       _ptr(r), _ptr(y), DT.get(y.dtype, -1),
+                                       y.stride(0) if y.numel() else N, _ptr(workspace), nbytes,
+                                       _stream(stream)),
+           "dq_quantized_linear_ws")
+
+
+def dq_quantized_linear_workspace_bytes(spec, M, N, K) -> int:
+    return int(_lib.dq_quantized_linear_workspace_bytes(spec, M, N, K))
+
+
 def dq_recode_mxint4_to_mxfp6(codes, block_scales, rows, cols, out_codes, out_scales, stream=None):
     _check(_lib.dq_recode_mxint4_to_mxfp6(_ptr(codes), _ptr(block_scales), rows, cols, _ptr(out_codes),
                                           _ptr(out_scales), _stream(stream)), "dq_recode_mxint4_to_mxfp6")
@@ -408,18 +429,22 @@ def recode_mxint4_to_mxfp6(codes, scales, rows: int, cols: int, stream=None):
 
 def quantized_linear(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int, fmt: str,
                      r=None, out_dtype=torch.float32, stream=None, a_tensor_scale=None,
-                     b_tensor_scale=None, group: int | None = None) -> torch.Tensor:
+                     b_tensor_scale=None, group: int | None = None, split: bool = True) -> torch.Tensor:
     """Y [M][N] = deq(A) deq(B)^T diag(r) from activation codes A [M][K] and weight codes
     B [N][K] of an MX format, NVFP4 (which also takes the two [1] fp32 tensor scales) or
     INT4 (bf16 scales per `group` = 64 or 128 elements).  MXINT4 operands are re-encoded as
-    MXFP6 E2M3 first (exact; for weights this can be done once and kept)."""
+    MXFP6 E2M3 first (exact; for weights this can be done once and kept).  With `split`, an
+    INT4 layer with few output tiles splits K over a workspace allocated here."""
     if fmt == "MXINT4":
         a_codes, a_scales = recode_mxint4_to_mxfp6(a_codes, a_scales, M, K, stream)
         b_codes, b_scales = recode_mxint4_to_mxfp6(b_codes, b_scales, N, K, stream)
         fmt = "MXFP6_E2M3"
     y = torch.empty(M, N, dtype=out_dtype, device=a_codes.device)
-    dq_quantized_linear(spec_of(fmt, group), a_codes, a_scales, a_tensor_scale, M, b_codes, b_scales,
-                        b_tensor_scale, N, K, r, y, stream)
+    spec = spec_of(fmt, group)
+    nb = dq_quantized_linear_workspace_bytes(spec, M, N, K) if split else 0
+    ws = torch.empty(nb, dtype=torch.uint8, device=a_codes.device) if nb else None
+    dq_quantized_linear_ws(spec, a_codes, a_scales, a_tensor_scale, M, b_codes, b_scales,
+                           b_tensor_scale, N, K, r, y, ws, stream)
     return y
 
 

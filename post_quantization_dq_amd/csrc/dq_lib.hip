@@ -1008,11 +1008,45 @@ int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t token
                                 (float*)workspace, kQuantParts, (hipStream_t)stream);
 }
 
+// Split K for the INT4 layer when its output tiles alone cannot fill the GPU (few tokens):
+// about two workgroups per CU, but no more splits than the stages of K, and partial sums no
+// larger than the weight codes (K / 8M splits of M x N fp32 against N x K / 2 bytes).
+static void i4_split(int64_t M, int64_t N, int64_t K, int& ksplit, int& st_split) {
+  const int64_t tiles = ((M + kLinTile - 1) / kLinTile) * ((N + kLinTile - 1) / kLinTile);
+  const int64_t nst = (K / 64 + 3) / 4;   // stages of 256 K
+  int64_t k = 1;
+  if (tiles > 0 && tiles < 256 && nst > 1) {
+    k = (512 + tiles - 1) / tiles;
+    k = std::min<int64_t>(k, std::max<int64_t>(1, K / (8 * std::max<int64_t>(M, 1))));
+    k = std::min<int64_t>(std::min<int64_t>(k, nst), 64);
+  }
+  const int64_t per = nst > 0 ? (nst + k - 1) / k : 0;
+  st_split = (int)per;
+  ksplit = per > 0 ? (int)((nst + per - 1) / per) : 1;
+}
+static int64_t i4_part_pitch(int64_t N) { return (N + 3) & ~(int64_t)3; }
+
+size_t dq_quantized_linear_workspace_bytes(dq_quant_spec spec, int64_t M, int64_t N, int64_t K) {
+  if (spec.fmt != DQ_FMT_INT4 || resolve_group(spec) < 0 || M <= 0 || N <= 0 || K <= 0) return 0;
+  int ks = 1, per = 0;
+  i4_split(M, N, K, ks, per);
+  return ks > 1 ? (size_t)ks * (size_t)M * (size_t)i4_part_pitch(N) * sizeof(float) : 0;
+}
+
 int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_t* a_scales,
                         const float* a_tensor_scale, int64_t M, const uint8_t* b_codes,
                         const uint8_t* b_scales, const float* b_tensor_scale, int64_t N,
                         int64_t K, const float* r, void* y, int32_t y_dtype, int64_t ldy,
                         void* stream) {
+  return dq_quantized_linear_ws(spec, a_codes, a_scales, a_tensor_scale, M, b_codes, b_scales,
+                                b_tensor_scale, N, K, r, y, y_dtype, ldy, nullptr, 0, stream);
+}
+
+int dq_quantized_linear_ws(dq_quant_spec spec, const uint8_t* a_codes, const uint8_t* a_scales,
+                           const float* a_tensor_scale, int64_t M, const uint8_t* b_codes,
+                           const uint8_t* b_scales, const float* b_tensor_scale, int64_t N,
+                           int64_t K, const float* r, void* y, int32_t y_dtype, int64_t ldy,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   const int g = resolve_group(spec);
   if (g < 0) return DQ_ERR_FORMAT;
   const int f = spec.fmt;
@@ -1030,16 +1064,36 @@ int dq_quantized_linear(dq_quant_spec spec, const uint8_t* a_codes, const uint8_
     return DQ_ERR_ALIGN;
   if (i4 && (((uintptr_t)a_scales | (uintptr_t)b_scales) & 1u)) return DQ_ERR_ALIGN;   // bf16
   const int64_t tm = (M + kLinTile - 1) / kLinTile, tn = (N + kLinTile - 1) / kLinTile;
-  if (tm * tn > (int64_t)0x7FFFFFFF) return DQ_ERR_SHAPE;
+  if (tm * tn > (int64_t)0x7FFFFFFF / 64) return DQ_ERR_SHAPE;
   LinArgs p{a_codes, a_scales, b_codes, b_scales, r, a_tensor_scale, b_tensor_scale, y,
-            M, N, K, ldy, (int32_t)tm, (int32_t)tn};
+            M, N, K, ldy, (int32_t)tm, (int32_t)tn, nullptr, 0, 1, (int32_t)((K / 64 + 3) / 4)};
   hipStream_t s = (hipStream_t)stream;
   dim3 grid((unsigned)(tm * tn)), block(256);
   if (nv) return y_dtype == DQ_BF16 ? launch_linear_nv<1>(grid, s, p) : launch_linear_nv<0>(grid, s, p);
   if (i4) {
+    const size_t need = dq_quantized_linear_workspace_bytes(spec, M, N, K);
+    if (workspace && need > 0) {
+      if (workspace_bytes < need) return DQ_ERR_WORKSPACE;
+      if (!aligned16(workspace)) return DQ_ERR_ALIGN;
+      int ks = 1, per = 0;
+      i4_split(M, N, K, ks, per);
+      p.ksplit = ks;
+      p.st_split = per;
+      p.part = (float*)workspace;
+      p.ldp = i4_part_pitch(N);
+      grid = dim3((unsigned)(tm * tn * ks));
+    }
+    int rc;
     if (g == 64)
-      return y_dtype == DQ_BF16 ? launch_linear_i4<1, 1>(grid, s, p) : launch_linear_i4<1, 0>(grid, s, p);
-    return y_dtype == DQ_BF16 ? launch_linear_i4<2, 1>(grid, s, p) : launch_linear_i4<2, 0>(grid, s, p);
+      rc = y_dtype == DQ_BF16 ? launch_linear_i4<1, 1>(grid, s, p) : launch_linear_i4<1, 0>(grid, s, p);
+    else
+      rc = y_dtype == DQ_BF16 ? launch_linear_i4<2, 1>(grid, s, p) : launch_linear_i4<2, 0>(grid, s, p);
+    if (rc != DQ_OK || !p.part) return rc;
+    const int64_t threads = M * ((N + 3) / 4);
+    dim3 rg((unsigned)((threads + 255) / 256));
+    if (y_dtype == DQ_BF16) hipLaunchKernelGGL((k_linear_i4_reduce<1>), rg, block, 0, s, p);
+    else hipLaunchKernelGGL((k_linear_i4_reduce<0>), rg, block, 0, s, p);
+    return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
   }
 #define DQ_L(F)                                                                          \
   rc = (y_dtype == DQ_BF16) ? launch_linear<F, 1>(grid, s, p) : launch_linear<F, 0>(grid, s, p); \

@@ -51,14 +51,23 @@ struct LinArgs {
   void* y;             // output [M][ldy], fp32 or bf16
   int64_t M, N, K, ldy;
   int32_t tiles_m, tiles_n;
+  // split K (INT4): workgroups of one output tile take consecutive ranges of `st_split`
+  // stages each and write unscaled fp32 partial sums to part [ksplit][M][ldp]; a second
+  // kernel adds them in split order.  ksplit = 1 and part = null: no split.
+  float* part;
+  int64_t ldp;
+  int32_t ksplit, st_split;
 };
 
 // Tile of this workgroup.  Workgroups are dispatched round-robin over the 8 XCDs; each XCD
 // gets a contiguous range of tiles, ordered down the M tiles of one N column first, so the
 // tiles that share weight rows (and, across columns, the activations) meet in one L2.
+__device__ __forceinline__ int lin_item(int nitems) {
+  const int bid = blockIdx.x, x = bid & 7, q = nitems >> 3, rem = nitems & 7;
+  return x * q + (x < rem ? x : rem) + (bid >> 3);
+}
 __device__ __forceinline__ void lin_tile(int ntiles, int tiles_m, int& tm, int& tn) {
-  const int bid = blockIdx.x, x = bid & 7, q = ntiles >> 3, rem = ntiles & 7;
-  const int t = x * q + (x < rem ? x : rem) + (bid >> 3);
+  const int t = lin_item(ntiles);
   tm = t % tiles_m;
   tn = t / tiles_m;
 }
@@ -920,8 +929,11 @@ __global__ __launch_bounds__(256) void k_linear_i4(LinArgs p) {
   using G = I4Geom;
   extern __shared__ __align__(16) uint8_t lin_lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int tm, tn;
-  lin_tile(p.tiles_m * p.tiles_n, p.tiles_m, tm, tn);
+  // work item = (tile, split); the splits of one tile are consecutive items, so they run on
+  // one XCD and share the activation tile in its L2
+  const int item = lin_item(p.tiles_m * p.tiles_n * p.ksplit);
+  const int tile = item / p.ksplit, split = item % p.ksplit;
+  const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
   const int64_t mt0 = (int64_t)tm * kLinTile, nt0 = (int64_t)tn * kLinTile;
   const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
   const int g = lane >> 4, r16 = lane & 15;
@@ -933,25 +945,27 @@ __global__ __launch_bounds__(256) void k_linear_i4(LinArgs p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int64_t nsub = p.K / 64;
-  const int64_t nst = (nsub + G::SUB - 1) / G::SUB;
+  const int64_t nst_all = (nsub + G::SUB - 1) / G::SUB;
+  const int64_t st0 = (int64_t)split * p.st_split;                     // this split's stages
+  const int64_t nst = st0 + p.st_split < nst_all ? st0 + p.st_split : nst_all;
   uint32_t sv[2];
-  if (nst > 0) {
-    i4_scales_load<GS>(p, mt0, nt0, 0, sv);
-    i4_codes(p, mt0, nt0, 0, lin_lds);
+  if (st0 < nst) {
+    i4_scales_load<GS>(p, mt0, nt0, st0, sv);
+    i4_codes(p, mt0, nt0, st0, lin_lds);
     i4_scales_store<GS>(lin_lds, sv);
   }
-  for (int64_t st = 0; st < nst; ++st) {
+  for (int64_t st = st0; st < nst; ++st) {
     // This stage's codes (the only loads outstanding) have landed and every thread has
     // written its scales; the buffer refilled next was last read before this barrier.
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("s_barrier" ::: "memory");
     const bool more = st + 1 < nst;
-    uint8_t* nxt = lin_lds + ((st + 1) & 1) * G::STAGE;
+    uint8_t* nxt = lin_lds + ((st - st0 + 1) & 1) * G::STAGE;
     if (more) {
       i4_scales_load<GS>(p, mt0, nt0, st + 1, sv);
       i4_codes(p, mt0, nt0, st + 1, nxt);
     }
-    const uint8_t* cur = lin_lds + (st & 1) * G::STAGE;
+    const uint8_t* cur = lin_lds + ((st - st0) & 1) * G::STAGE;
     const float* sa_t = (const float*)(cur + 2 * G::TILE);
     const float* sb_t = (const float*)(cur + 2 * G::TILE + G::STILE);
 #pragma unroll
@@ -997,7 +1011,49 @@ __global__ __launch_bounds__(256) void k_linear_i4(LinArgs p) {
     if (more) i4_scales_store<GS>(nxt, sv);
   }
 
+  if (p.part) {
+    // unscaled partial sums of this split: acc[i][j][v] is the product at row
+    // mt0 + wm + 16 i + lane % 16, column nt0 + wn + 16 j + 4 (lane / 16) + v
+    float* base = p.part + (int64_t)split * p.M * p.ldp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = mt0 + wm + 16 * i + r16;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = nt0 + wn + 16 * j + 4 * g;
+        if (n < p.N) *gp((f32x4*)(base + m * p.ldp + n)) = acc[i][j];   // ldp >= N rounded to 4
+      }
+    }
+    return;
+  }
   lin_store<OUT_BF16>(acc, p, mt0 + wm, nt0 + wn, 1.0f / 256.0f);
+}
+
+// The split sums of k_linear_i4 added in split order, then scaled as the unsplit kernel
+// scales its accumulator: Y[m][n] = ((sum_s part[s][m][n]) * 2^-8) * r[n].  One thread per
+// four consecutive columns of a row.
+template <int OUT_BF16>
+__global__ __launch_bounds__(256) void k_linear_i4_reduce(LinArgs p) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = (p.N + 3) / 4;
+  if (q >= p.M * per_row) return;
+  const int64_t m = q / per_row, n = 4 * (q % per_row);
+  f32x4 s = *gp((const f32x4*)(p.part + m * p.ldp + n));
+  for (int k = 1; k < p.ksplit; ++k) {
+    const f32x4 t = *gp((const f32x4*)(p.part + ((int64_t)k * p.M + m) * p.ldp + n));
+    s = f32x4{s.x + t.x, s.y + t.y, s.z + t.z, s.w + t.w};
+  }
+  float yv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    if (n + v >= p.N) break;
+    const float rn = p.r ? gp(p.r)[n + v] : 1.0f;
+    const float x = (yv[v] * (1.0f / 256.0f)) * rn;
+    const int64_t o = m * p.ldy + n + v;
+    if (OUT_BF16) gp((uint16_t*)p.y)[o] = (uint16_t)(f2u(bf16_rne(x)) >> 16);
+    else gp((float*)p.y)[o] = x;
+  }
 }
 
 }  // namespace dqk

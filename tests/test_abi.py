@@ -147,6 +147,22 @@ def test_quantized_linear_argument_errors(dq):
     assert call(mx, ac=None, asc=None, M=0, bc=None, bsc=None, y=None) == 0   # M = 0
 
 
+def test_linear_workspace_sizes(dq):
+    """Host-side split plan of the INT4 layer: few output tiles split K, many do not, other
+    formats never; the size is splits x M x N (rounded to 4) fp32 values."""
+    i4 = dq.dq_quant_spec(0, 64)
+    nb = dq.dq_quantized_linear_workspace_bytes(i4, 82, 4096, 4096)
+    assert nb > 0 and nb % (82 * 4096 * 4) == 0
+    assert dq.dq_quantized_linear_workspace_bytes(i4, 2048, 4096, 4096) == 0
+    assert dq.dq_quantized_linear_workspace_bytes(dq.dq_quant_spec(2, 0), 82, 4096, 4096) == 0
+    assert dq.dq_quantized_linear_workspace_bytes(i4, 82, 4096, 64) == 0     # one stage of K
+    assert dq.dq_quantized_linear_workspace_bytes(i4, 0, 4096, 4096) == 0
+    L = dq._lib
+    # a workspace smaller than needed is refused before anything is launched
+    assert L.dq_quantized_linear_ws(i4, 0x10000, 0x20000, None, 82, 0x30000, 0x40000, None, 4096,
+                                    4096, None, 0x50000, 0, 4096, 0x60000, nb - 16, None) == -5
+
+
 def test_recode_argument_errors(dq):
     L = dq._lib
     assert L.dq_recode_mxint4_to_mxfp6(0x10000, 0x20000, 4, 48, 0x30000, 0x40000, None) == -2

@@ -389,8 +389,15 @@ def _i4_inputs(M, N, K, g, seed):
     return a, asc, b, bsc, r
 
 
-def _i4_tol(K, g, absy, y, out_dtype):
-    t = (K // g + 3) * 2.0 ** -24 * absy
+def _i4_splits(M, N, K, g):
+    """K splits the library takes for this shape (from its workspace size: splits x M x N
+    rounded to 4 fp32 values)."""
+    nb = dq.dq_quantized_linear_workspace_bytes(dq.spec_of("INT4", g), M, N, K)
+    return nb // (M * ((N + 3) // 4 * 4) * 4) if nb else 1
+
+
+def _i4_tol(K, g, absy, y, out_dtype, splits=1):
+    t = (K // g + splits + 3) * 2.0 ** -24 * absy
     if out_dtype == torch.bfloat16:
         t = t + 2.0 ** -8 * (np.abs(y) + t)
     return t + 1e-37
@@ -426,7 +433,7 @@ def test_int4_random_codes(oracle_lib, g, shape, out_dtype):
         absy = absy.reshape(M, N)
         err = np.abs(y - ref)
         print(f"[linear] INT4 max err / sum|ab| = {float((err / (absy + 1e-300)).max()):.3g}", flush=True)
-        assert np.all(err <= _i4_tol(K, g, absy, ref, out_dtype))
+        assert np.all(err <= _i4_tol(K, g, absy, ref, out_dtype, _i4_splits(M, N, K, g)))
 
 
 def test_int4_exact_small_integers(oracle_lib):
@@ -496,3 +503,51 @@ def test_int4_argument_errors():
     buf = z(64)
     with pytest.raises(RuntimeError):
         dq.quantized_linear(z(32), buf[1:5], z(32), z(2, torch.int16), 1, 1, 64, "INT4", group=64)
+
+
+@pytest.mark.parametrize("shape", [(82, 4096, 4096), (1, 1024, 4096), (16, 4096, 14336), (82, 14336, 4096),
+                                   (5, 300, 640)])
+def test_int4_split_k_few_tokens(oracle_lib, shape):
+    """Few tokens (the listing page's Table 11 forwards of 82 tokens, and decoding): the
+    layer splits K over a workspace.  Sampled entries (all of them for the small case)
+    against the oracle within the split bound; two calls bitwise equal; the unsplit kernel
+    on the same codes within the same bound."""
+    M, N, K = shape
+    g = 64
+    ks = _i4_splits(M, N, K, g)
+    print(f"[linear] INT4 split K {M}x{N}x{K}: {ks} splits", flush=True)
+    assert ks > 1
+    a, asc, b, bsc, r = _i4_inputs(M, N, K, g, M * 7 + N + K)
+    dev = lambda x: torch.from_numpy(x).to(DEV)
+    A, As, B, Bs, R = dev(a), dev(asc.view(np.int16)), dev(b), dev(bsc.view(np.int16)), to_dev(r)
+    y1 = dq.quantized_linear(A, As, B, Bs, M, N, K, "INT4", r=R, group=g)
+    y2 = dq.quantized_linear(A, As, B, Bs, M, N, K, "INT4", r=R, group=g)
+    y0 = dq.quantized_linear(A, As, B, Bs, M, N, K, "INT4", r=R, group=g, split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    rng = np.random.default_rng(M + N)
+    if M * N <= 4096:
+        mi, ni = [x.ravel() for x in np.meshgrid(np.arange(M), np.arange(N), indexing="ij")]
+    else:
+        mi, ni = rng.integers(0, M, 384), rng.integers(0, N, 384)
+        mi[:4], ni[:4] = [0, M - 1, 0, M - 1], [0, 0, N - 1, N - 1]
+    ref, absy = oracle_lib.quantized_linear_entries(a, asc, M, b, bsc, N, K, "INT4", mi, ni, r=r, group=g)
+    for y, splits in ((y1, ks), (y0, 1)):
+        got = y.cpu().numpy().astype(np.float64)[mi, ni]
+        assert np.all(np.abs(got - ref) <= _i4_tol(K, g, absy, ref, torch.float32, splits)), splits
+
+
+def test_int4_split_workspace_errors():
+    """A workspace smaller than the shape needs, or misaligned, is refused before any work."""
+    M, N, K, g = 8, 256, 4096, 64
+    spec = dq.spec_of("INT4", g)
+    nb = dq.dq_quantized_linear_workspace_bytes(spec, M, N, K)
+    assert nb > 0
+    z = lambda n, dt=torch.uint8: torch.zeros(n, dtype=dt, device=DEV)
+    a, asc, b, bsc = z(M * K // 2), z(M * K // g, torch.int16), z(N * K // 2), z(N * K // g, torch.int16)
+    y = torch.empty(M, N, device=DEV)
+    with pytest.raises(RuntimeError):
+        dq.dq_quantized_linear_ws(spec, a, asc, None, M, b, bsc, None, N, K, None, y, z(nb - 16))
+    buf = z(nb + 64)
+    with pytest.raises(RuntimeError):
+        dq.dq_quantized_linear_ws(spec, a, asc, None, M, b, bsc, None, N, K, None, y, buf[4:4 + nb])
