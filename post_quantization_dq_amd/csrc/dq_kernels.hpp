@@ -549,12 +549,13 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
     for (int kk = 0; kk < nloop; ++kk) {
       const int chn = lane + 64 * kk;
       const bool valid = chn < nch;
-      const int cl = valid ? chn : 0;   // c reads stay in range; invalid lanes work on zeros
-      const int j0 = 16 * chn;
+      // Lanes past the row's end load and work on the row's first chunk: every load stays in
+      // range, nothing needs zeroing or a branch, and none of their results is stored or summed.
+      const int cl = valid ? chn : 0;
       RawRow<DT> raw;
-      if (valid) raw.load(P.W, i, P.ld, j0); else raw.zero();
+      raw.load(P.W, i, P.ld, 16 * cl);
       uint32_t pk[4] = {0u, 0u, 0u, 0u}, ps = 0;
-      if (valid && !(pi.mode == MODE_INIT)) load_codes<FMT, L>(acodes, ascales, i, n, chn, g, pk, ps);
+      if (!(pi.mode == MODE_INIT)) load_codes<FMT, L>(acodes, ascales, i, n, cl, g, pk, ps);
       float w[16];
       raw.unpack(w);
       float p[16];
