@@ -642,7 +642,11 @@ int launch_quant_multi_t(const void* X, int64_t rows, int64_t cols, int64_t ld,
   const int64_t groups = (rows + H - 1) / H;
   const unsigned grid = (unsigned)std::min<int64_t>(groups, kQuantGroupsMax);
   const size_t c_bytes = (size_t)mo.count * cols * sizeof(float);
-  const int c_lds = c_bytes <= kMultiCLds ? 1 : 0;
+  // c is staged in LDS when it fits and every workgroup quantises two or more row groups;
+  // with one group per workgroup (a few tokens) the staging is a round of load latency that
+  // the rows do not pay back, and each row reads its c from L2 alongside its X instead
+  const int64_t groups_per_wg = (groups + grid - 1) / grid;
+  const int c_lds = (c_bytes <= kMultiCLds && groups_per_wg >= 2) ? 1 : 0;
   if (c_lds && c_bytes > 64 * 1024) {
     if (!lds_limit((const void*)k_quant_multi<FMT, DT, L>, (int)kMultiCLds)) return DQ_ERR_HIP;
   }

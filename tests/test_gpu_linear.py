@@ -537,6 +537,28 @@ def test_int4_split_k_few_tokens(oracle_lib, shape):
         assert np.all(np.abs(got - ref) <= _i4_tol(K, g, absy, ref, torch.float32, splits)), splits
 
 
+def test_int4_split_workspace_reused():
+    """One workspace kept across calls of different shapes and output types (as a forward
+    keeps it), filled with what earlier calls left: every call equals the same call on a
+    fresh workspace bit for bit."""
+    g = 64
+    shapes = [(82, 4096, 4096), (16, 4096, 14336), (5, 300, 640), (82, 14336, 4096), (82, 4096, 4096)]
+    spec = dq.spec_of("INT4", g)
+    nb = max(dq.dq_quantized_linear_workspace_bytes(spec, M, N, K) for M, N, K in shapes)
+    ws = torch.full((nb,), 0x7F, dtype=torch.uint8, device=DEV)
+    for k, (M, N, K) in enumerate(shapes):
+        out = torch.bfloat16 if k % 2 else torch.float32
+        print(f"[linear] INT4 split K reused workspace {M}x{N}x{K} {out}", flush=True)
+        a, asc, b, bsc, r = _i4_inputs(M, N, K, g, 1000 + k)
+        dev = lambda x: torch.from_numpy(x).to(DEV)
+        A, As, B, Bs, R = dev(a), dev(asc.view(np.int16)), dev(b), dev(bsc.view(np.int16)), to_dev(r)
+        y = torch.empty(M, N, dtype=out, device=DEV)
+        dq.dq_quantized_linear_ws(spec, A, As, None, M, B, Bs, None, N, K, R, y, ws)
+        ref = dq.quantized_linear(A, As, B, Bs, M, N, K, "INT4", r=R, out_dtype=out, group=g)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), (M, N, K)
+
+
 def test_int4_split_workspace_errors():
     """A workspace smaller than the shape needs, or misaligned, is refused before any work."""
     M, N, K, g = 8, 256, 4096, 64
