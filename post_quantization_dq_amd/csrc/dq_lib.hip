@@ -612,11 +612,15 @@ int launch_linear_nv(dim3 grid, hipStream_t s, const LinArgs& p) {
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
 
-template <int GS, int OB>
+template <int GS, int OB, int TM>
 int launch_linear_i4(dim3 grid, hipStream_t s, const LinArgs& p) {
-  if (!lds_limit((const void*)k_linear_i4<GS, OB>, I4Geom::LDS)) return DQ_ERR_HIP;
-  hipLaunchKernelGGL((k_linear_i4<GS, OB>), grid, dim3(256), I4Geom::LDS, s, p);   // 72 KiB
+  if (!lds_limit((const void*)k_linear_i4<GS, OB, TM>, I4Geom<TM>::LDS)) return DQ_ERR_HIP;
+  hipLaunchKernelGGL((k_linear_i4<GS, OB, TM>), grid, dim3(256), I4Geom<TM>::LDS, s, p);   // 72 / 45 KiB
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+template <int GS, int OB>
+int launch_linear_i4_tm(int tm_rows, dim3 grid, hipStream_t s, const LinArgs& p) {
+  return tm_rows == 32 ? launch_linear_i4<GS, OB, 32>(grid, s, p) : launch_linear_i4<GS, OB, 128>(grid, s, p);
 }
 
 static_assert(kMaxMulti == DQ_MAX_MULTI, "kernel and header output limits differ");
@@ -1012,14 +1016,20 @@ int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t token
                                 (float*)workspace, kQuantParts, (hipStream_t)stream);
 }
 
-// Split K for the INT4 layer when its output tiles alone cannot fill the GPU (few tokens):
-// about two workgroups per CU, but no more splits than the stages of K, and partial sums no
-// larger than the weight codes (K / 8M splits of M x N fp32 against N x K / 2 bytes).
+// Rows of the INT4 layer's activation tile: 32 for a few tokens (up to 96: 82 tokens fill
+// three tiles of 32 rather than one of 128), else 128.
+static int i4_tile_m(int64_t M) { return M <= 96 ? 32 : 128; }
+// Split K for the INT4 layer when its output tiles alone cannot fill the GPU twice over (few
+// tokens): about two workgroups per CU, but no more splits than the stages of K, and partial
+// sums no larger than the weight codes (K / 8M splits of M x N fp32 against N x K / 2
+// bytes).  With 32-row tiles, whose stages are short, up to 511 tiles are split in two: a
+// 14336-wide layer at 82 tokens (336 tiles) would otherwise run 16 stages back to back.
 static void i4_split(int64_t M, int64_t N, int64_t K, int& ksplit, int& st_split) {
-  const int64_t tiles = ((M + kLinTile - 1) / kLinTile) * ((N + kLinTile - 1) / kLinTile);
+  const int tmr = i4_tile_m(M);
+  const int64_t tiles = ((M + tmr - 1) / tmr) * ((N + kLinTile - 1) / kLinTile);
   const int64_t nst = (K / 64 + 3) / 4;   // stages of 256 K
   int64_t k = 1;
-  if (tiles > 0 && tiles < 256 && nst > 1) {
+  if (tiles > 0 && tiles < (tmr == 32 ? 512 : 256) && nst > 1) {
     k = (512 + tiles - 1) / tiles;
     k = std::min<int64_t>(k, std::max<int64_t>(1, K / (8 * std::max<int64_t>(M, 1))));
     k = std::min<int64_t>(std::min<int64_t>(k, nst), 64);
@@ -1067,7 +1077,8 @@ int dq_quantized_linear_ws(dq_quant_spec spec, const uint8_t* a_codes, const uin
   if (!aligned16(a_codes) || !aligned16(b_codes) || ((uintptr_t)y % (y_dtype == DQ_F32 ? 4 : 2)))
     return DQ_ERR_ALIGN;
   if (i4 && (((uintptr_t)a_scales | (uintptr_t)b_scales) & 1u)) return DQ_ERR_ALIGN;   // bf16
-  const int64_t tm = (M + kLinTile - 1) / kLinTile, tn = (N + kLinTile - 1) / kLinTile;
+  const int tm_rows = i4 ? i4_tile_m(M) : kLinTile;   // rows of the activation tile
+  const int64_t tm = (M + tm_rows - 1) / tm_rows, tn = (N + kLinTile - 1) / kLinTile;
   if (tm * tn > (int64_t)0x7FFFFFFF / 64) return DQ_ERR_SHAPE;
   LinArgs p{a_codes, a_scales, b_codes, b_scales, r, a_tensor_scale, b_tensor_scale, y,
             M, N, K, ldy, (int32_t)tm, (int32_t)tn, nullptr, 0, 1, (int32_t)((K / 64 + 3) / 4)};
@@ -1089,9 +1100,11 @@ int dq_quantized_linear_ws(dq_quant_spec spec, const uint8_t* a_codes, const uin
     }
     int rc;
     if (g == 64)
-      rc = y_dtype == DQ_BF16 ? launch_linear_i4<1, 1>(grid, s, p) : launch_linear_i4<1, 0>(grid, s, p);
+      rc = y_dtype == DQ_BF16 ? launch_linear_i4_tm<1, 1>(tm_rows, grid, s, p)
+                              : launch_linear_i4_tm<1, 0>(tm_rows, grid, s, p);
     else
-      rc = y_dtype == DQ_BF16 ? launch_linear_i4<2, 1>(grid, s, p) : launch_linear_i4<2, 0>(grid, s, p);
+      rc = y_dtype == DQ_BF16 ? launch_linear_i4_tm<2, 1>(tm_rows, grid, s, p)
+                              : launch_linear_i4_tm<2, 0>(tm_rows, grid, s, p);
     if (rc != DQ_OK || !p.part) return rc;
     const int64_t threads = M * ((N + 3) / 4);
     dim3 rg((unsigned)((threads + 255) / 256));

@@ -72,24 +72,24 @@ __device__ __forceinline__ void lin_tile(int ntiles, int tiles_m, int& tm, int& 
   tn = t / tiles_m;
 }
 
-// Stores one wave's 64 x 64 block of Y from accumulators of (B A^T) products (the weight
-// fragment is the instruction's first operand): acc[i][j][v] holds
-// Y[m0 + 16 i + lane % 16][n0 + 16 j + 4 (lane / 16) + v].  So each lane writes four
+// Stores one wave's (16 BI) x (16 BJ) block of Y (64 x 64 by default) from accumulators of
+// (B A^T) products (the weight fragment is the instruction's first operand): acc[i][j][v]
+// holds Y[m0 + 16 i + lane % 16][n0 + 16 j + 4 (lane / 16) + v].  So each lane writes four
 // consecutive columns of one row, one 8-byte (bf16) or 16-byte (fp32) store where the
 // output's alignment and row pitch allow it, as (acc * s) * r[n].
-template <int OUT_BF16>
-__device__ __forceinline__ void lin_store(const f32x4 (&acc)[4][4], const LinArgs& p, int64_t m0,
+template <int OUT_BF16, int BI = 4, int BJ = 4>
+__device__ __forceinline__ void lin_store(const f32x4 (&acc)[BI][BJ], const LinArgs& p, int64_t m0,
                                           int64_t n0, float s) {
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   const bool vec = (p.ldy & 3) == 0 && ((uintptr_t)p.y & (OUT_BF16 ? 7u : 15u)) == 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < BJ; ++j) {
     const int64_t n = n0 + 16 * j + 4 * g;
     float rn[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) rn[v] = (p.r && n + v < p.N) ? gp(p.r)[n + v] : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < BI; ++i) {
       const int64_t m = m0 + 16 * i + r16;
       if (m >= p.M) continue;
       float yv[4];
@@ -831,34 +831,47 @@ __global__ __launch_bounds__(256) void k_recode_mxint4_e2m3(const uint8_t* __res
 // global loads, clamped to the row start past K (those steps are skipped); each thread
 // loads its share of the stage's bf16 scales into registers and writes them to LDS as fp32
 // after the products, so any K that is a multiple of the group runs in the one kernel.
+// TM: rows of the activation tile.  128 (four waves of 64 x 64 over a 128 x 128 tile) for
+// many tokens; 32 (four waves of 32 x 32 side by side over a 32 x 128 tile) for a few, so
+// that 82 tokens fill 96 tile rows instead of 128 and three times as many tiles share the
+// GPU.  The weight tile is 128 rows either way.
+template <int TM>
 struct I4Geom {
   static constexpr int KS = 256;                  // K per stage
   static constexpr int SUB = KS / 64;             // 64-element steps per stage
   static constexpr int ROWB = KS / 2;             // 128 bytes of codes per tile row
   static constexpr int CPR = ROWB / 16;           // 8 chunks
   static constexpr int RPI = 64 / CPR;            // 8 rows per wave load
-  static constexpr int TILE = kLinTile * ROWB;    // 16 KiB
-  static constexpr int STILE = SUB * kLinTile * 4;   // fp32 scales [4 slots][128 rows]: 2 KiB
-  static constexpr int STAGE = 2 * TILE + 2 * STILE;
+  static constexpr int ATILE = TM * ROWB;         // activation codes: 16 or 4 KiB
+  static constexpr int BTILE = kLinTile * ROWB;   // weight codes: 16 KiB
+  static constexpr int ASTILE = SUB * TM * 4;     // fp32 scales [4 slots][TM rows]
+  static constexpr int BSTILE = SUB * kLinTile * 4;   // fp32 scales [4 slots][128 rows]: 2 KiB
+  static constexpr int STAGE = ATILE + BTILE + ASTILE + BSTILE;
   static constexpr int D = 2;                     // ring depth
-  static constexpr int LDS = D * STAGE;           // 72 KiB
-  static constexpr int CODE_INSTS = kLinTile / RPI / 4;   // 4 loads per wave per operand
+  static constexpr int LDS = D * STAGE;           // 72 or 45 KiB
+  static constexpr int A_INSTS = TM / RPI / 4;    // loads per wave: 4 or 1 (activations)
+  static constexpr int B_INSTS = kLinTile / RPI / 4;   // 4 (weights)
+  static constexpr int WM = TM == 128 ? 64 : 32;  // wave block
+  static constexpr int WN = TM == 128 ? 64 : 32;
+  static constexpr int BI = WM / 16, BJ = WN / 16;   // instruction tiles per wave block
 };
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+template <int TM>
 __device__ __forceinline__ void i4_codes(const LinArgs& p, int64_t mt0, int64_t nt0, int64_t st,
                                          uint8_t* buf) {
-  using G = I4Geom;
+  using G = I4Geom<TM>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t rowbytes = p.K / 2;
 #pragma unroll
   for (int op = 0; op < 2; ++op) {
     const uint8_t* codes = op ? p.b : p.a;
     const int64_t r0 = op ? nt0 : mt0, rows = op ? p.N : p.M;
-    uint8_t* tile = buf + op * G::TILE;
+    uint8_t* tile = buf + op * G::ATILE;
+    const int insts = op ? G::B_INSTS : G::A_INSTS;
 #pragma unroll
-    for (int ii = 0; ii < G::CODE_INSTS; ++ii) {
-      const int rbase = (wave * G::CODE_INSTS + ii) * G::RPI;
+    for (int ii = 0; ii < insts; ++ii) {
+      const int rbase = (wave * insts + ii) * G::RPI;
       const int r = rbase + lane / G::CPR, c = lane % G::CPR;
       int64_t row = r0 + r;
       row = row < rows ? row : rows - 1;
@@ -871,16 +884,21 @@ __device__ __forceinline__ void i4_codes(const LinArgs& p, int64_t mt0, int64_t 
   }
 }
 
-// This thread's share of a stage's scales: tile row t / 2 of both operands; with groups of
-// 64 the two bf16 of steps 2 (t % 2) and +1, with groups of 128 the one bf16 of group t % 2
-// of the stage.  Past K the row's first scale is read (its steps are skipped).
-template <int GS>
+// This thread's share of a stage's scales: tile row t / 2 of both operands (activation rows
+// only below TM); with groups of 64 the two bf16 of steps 2 (t % 2) and +1, with groups of
+// 128 the one bf16 of group t % 2 of the stage.  Past K the row's first scale is read (its
+// steps are skipped).  The values stay as loaded until i4_scales_store, so nothing waits for
+// these loads before the stage's products (combining the two halves here made every stage
+// wait a round of load latency before requesting the next stage's codes).
+template <int GS, int TM>
 __device__ __forceinline__ void i4_scales_load(const LinArgs& p, int64_t mt0, int64_t nt0,
-                                               int64_t st, uint32_t (&sv)[2]) {
+                                               int64_t st, uint32_t (&sv)[2][2]) {
   const int rr = threadIdx.x >> 1, h = threadIdx.x & 1;
   const int64_t ng = p.K / (64 * GS);
+  sv[0][0] = sv[0][1] = 0u;
 #pragma unroll
   for (int op = 0; op < 2; ++op) {
+    if (op == 0 && rr >= TM) continue;
     const uint16_t* sc = (const uint16_t*)(op ? p.bs : p.as);
     const int64_t r0 = op ? nt0 : mt0, rows = op ? p.N : p.M;
     int64_t row = r0 + rr;
@@ -890,29 +908,32 @@ __device__ __forceinline__ void i4_scales_load(const LinArgs& p, int64_t mt0, in
       int64_t g0 = 4 * st + 2 * h, g1 = g0 + 1;
       g0 = g0 < ng ? g0 : 0;
       g1 = g1 < ng ? g1 : 0;
-      sv[op] = (uint32_t)sr[g0] | ((uint32_t)sr[g1] << 16);
+      sv[op][0] = sr[g0];
+      sv[op][1] = sr[g1];
     } else {
       int64_t g0 = 2 * st + h;
       g0 = g0 < ng ? g0 : 0;
-      sv[op] = sr[g0];
+      sv[op][0] = sr[g0];
     }
   }
 }
-// LDS scale tile of an operand: fp32 [4 slots][128 rows], slot k = the scale of the
-// stage's k-th group (slots 2, 3 unused with groups of 128), so that the scales of four
-// consecutive rows are one 16-byte read.
-template <int GS>
-__device__ __forceinline__ void i4_scales_store(uint8_t* buf, const uint32_t (&sv)[2]) {
-  using G = I4Geom;
+// LDS scale tile of an operand: fp32 [4 slots][rows], slot k = the scale of the stage's k-th
+// group (slots 2, 3 unused with groups of 128), so that the scales of four consecutive rows
+// are one 16-byte read.
+template <int GS, int TM>
+__device__ __forceinline__ void i4_scales_store(uint8_t* buf, const uint32_t (&sv)[2][2]) {
+  using G = I4Geom<TM>;
   const int rr = threadIdx.x >> 1, h = threadIdx.x & 1;
 #pragma unroll
   for (int op = 0; op < 2; ++op) {
-    float* t = (float*)(buf + 2 * G::TILE + op * G::STILE);
+    if (op == 0 && rr >= TM) continue;
+    const int rows = op ? kLinTile : TM;
+    float* t = (float*)(buf + G::ATILE + G::BTILE + op * G::ASTILE);
     if (GS == 1) {
-      t[(2 * h) * kLinTile + rr] = u2f(sv[op] << 16);
-      t[(2 * h + 1) * kLinTile + rr] = u2f(sv[op] & 0xFFFF0000u);
+      t[(2 * h) * rows + rr] = u2f(sv[op][0] << 16);
+      t[(2 * h + 1) * rows + rr] = u2f(sv[op][1] << 16);
     } else {
-      t[h * kLinTile + rr] = u2f(sv[op] << 16);
+      t[h * rows + rr] = u2f(sv[op][0] << 16);
     }
   }
 }
@@ -924,9 +945,10 @@ __device__ __forceinline__ v4i i4_unpack(uint64_t x) {
   return v4i{(int)((w0 << 4) & m), (int)(w0 & m), (int)((w1 << 4) & m), (int)(w1 & m)};
 }
 
-template <int GS, int OUT_BF16>
+template <int GS, int OUT_BF16, int TM>
 __global__ __launch_bounds__(256) void k_linear_i4(LinArgs p) {
-  using G = I4Geom;
+  using G = I4Geom<TM>;
+  constexpr int BI = G::BI, BJ = G::BJ;
   extern __shared__ __align__(16) uint8_t lin_lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // work item = (tile, split); the splits of one tile are consecutive items, so they run on
@@ -934,25 +956,25 @@ __global__ __launch_bounds__(256) void k_linear_i4(LinArgs p) {
   const int item = lin_item(p.tiles_m * p.tiles_n * p.ksplit);
   const int tile = item / p.ksplit, split = item % p.ksplit;
   const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
-  const int64_t mt0 = (int64_t)tm * kLinTile, nt0 = (int64_t)tn * kLinTile;
-  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int64_t mt0 = (int64_t)tm * TM, nt0 = (int64_t)tn * kLinTile;
+  const int wm = TM == 128 ? (wave & 1) * 64 : 0, wn = TM == 128 ? (wave >> 1) * 64 : wave * 32;
   const int g = lane >> 4, r16 = lane & 15;
 
-  f32x4 acc[4][4];
+  f32x4 acc[BI][BJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < BI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < BJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int64_t nsub = p.K / 64;
   const int64_t nst_all = (nsub + G::SUB - 1) / G::SUB;
   const int64_t st0 = (int64_t)split * p.st_split;                     // this split's stages
   const int64_t nst = st0 + p.st_split < nst_all ? st0 + p.st_split : nst_all;
-  uint32_t sv[2];
+  uint32_t sv[2][2];
   if (st0 < nst) {
-    i4_scales_load<GS>(p, mt0, nt0, st0, sv);
-    i4_codes(p, mt0, nt0, st0, lin_lds);
-    i4_scales_store<GS>(lin_lds, sv);
+    i4_scales_load<GS, TM>(p, mt0, nt0, st0, sv);
+    i4_codes<TM>(p, mt0, nt0, st0, lin_lds);
+    i4_scales_store<GS, TM>(lin_lds, sv);
   }
   for (int64_t st = st0; st < nst; ++st) {
     // This stage's codes (the only loads outstanding) have landed and every thread has
@@ -962,53 +984,58 @@ __global__ __launch_bounds__(256) void k_linear_i4(LinArgs p) {
     const bool more = st + 1 < nst;
     uint8_t* nxt = lin_lds + ((st - st0 + 1) & 1) * G::STAGE;
     if (more) {
-      i4_scales_load<GS>(p, mt0, nt0, st + 1, sv);
-      i4_codes(p, mt0, nt0, st + 1, nxt);
+      i4_scales_load<GS, TM>(p, mt0, nt0, st + 1, sv);
+      i4_codes<TM>(p, mt0, nt0, st + 1, nxt);
     }
     const uint8_t* cur = lin_lds + ((st - st0) & 1) * G::STAGE;
-    const float* sa_t = (const float*)(cur + 2 * G::TILE);
-    const float* sb_t = (const float*)(cur + 2 * G::TILE + G::STILE);
+    const float* sa_t = (const float*)(cur + G::ATILE + G::BTILE);
+    const float* sb_t = (const float*)(cur + G::ATILE + G::BTILE + G::ASTILE);
 #pragma unroll
     for (int k = 0; k < G::SUB / GS; ++k) {
       if (st * G::SUB + GS * k >= nsub) break;   // the same for the whole workgroup
-      v4i P[4][4];
+      v4i P[BI][BJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < BI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) P[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < BJ; ++j) P[i][j] = v4i{0, 0, 0, 0};
 #pragma unroll
       for (int h = 0; h < GS; ++h) {
         const int u = GS * k + h;   // 64-element step: chunks 2u, 2u + 1 of the row
-        v4i a[4], b[4];
+        v4i a[BI], b[BJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ra = wm + 16 * i + r16, rb = wn + 16 * i + r16;
-          const int ca = (2 * u + (g >> 1)) ^ swz128(ra), cb = (2 * u + (g >> 1)) ^ swz128(rb);
+        for (int i = 0; i < BI; ++i) {
+          const int ra = wm + 16 * i + r16;
+          const int ca = (2 * u + (g >> 1)) ^ swz128(ra);
           a[i] = i4_unpack(*(const uint64_t*)(cur + ra * G::ROWB + 16 * ca + 8 * (g & 1)));
-          b[i] = i4_unpack(*(const uint64_t*)(cur + G::TILE + rb * G::ROWB + 16 * cb + 8 * (g & 1)));
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < BJ; ++j) {
+          const int rb = wn + 16 * j + r16;
+          const int cb = (2 * u + (g >> 1)) ^ swz128(rb);
+          b[j] = i4_unpack(*(const uint64_t*)(cur + G::ATILE + rb * G::ROWB + 16 * cb + 8 * (g & 1)));
+        }
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+          for (int j = 0; j < BJ; ++j)
             P[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[j], a[i], P[i][j], 0, 0, 0);
       }
       // P[i][j][v] belongs to row wm + 16 i + r16 and column wn + 16 j + 4 g + v
-      float sa[4];
-      f32x4 sb[4];
+      float sa[BI];
+      f32x4 sb[BJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa[i] = sa_t[k * kLinTile + wm + 16 * i + r16];
+      for (int i = 0; i < BI; ++i) sa[i] = sa_t[k * TM + wm + 16 * i + r16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sb[j] = *(const f32x4*)(sb_t + k * kLinTile + wn + 16 * j + 4 * g);
+      for (int j = 0; j < BJ; ++j) sb[j] = *(const f32x4*)(sb_t + k * kLinTile + wn + 16 * j + 4 * g);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < BI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < BJ; ++j)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
             acc[i][j][v] = __builtin_fmaf((float)P[i][j][v], sa[i] * sb[j][v], acc[i][j][v]);
     }
-    if (more) i4_scales_store<GS>(nxt, sv);
+    if (more) i4_scales_store<GS, TM>(nxt, sv);
   }
 
   if (p.part) {
@@ -1016,18 +1043,18 @@ __global__ __launch_bounds__(256) void k_linear_i4(LinArgs p) {
     // mt0 + wm + 16 i + lane % 16, column nt0 + wn + 16 j + 4 (lane / 16) + v
     float* base = p.part + (int64_t)split * p.M * p.ldp;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < BI; ++i) {
       const int64_t m = mt0 + wm + 16 * i + r16;
       if (m >= p.M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < BJ; ++j) {
         const int64_t n = nt0 + wn + 16 * j + 4 * g;
         if (n < p.N) *gp((f32x4*)(base + m * p.ldp + n)) = acc[i][j];   // ldp >= N rounded to 4
       }
     }
     return;
   }
-  lin_store<OUT_BF16>(acc, p, mt0 + wm, nt0 + wn, 1.0f / 256.0f);
+  lin_store<OUT_BF16, BI, BJ>(acc, p, mt0 + wm, nt0 + wn, 1.0f / 256.0f);
 }
 
 // The split sums of k_linear_i4 added in split order, then scaled as the unsplit kernel

@@ -505,7 +505,7 @@ def test_int4_argument_errors():
         dq.quantized_linear(z(32), buf[1:5], z(32), z(2, torch.int16), 1, 1, 64, "INT4", group=64)
 
 
-@pytest.mark.parametrize("shape", [(82, 4096, 4096), (1, 1024, 4096), (16, 4096, 14336), (82, 14336, 4096),
+@pytest.mark.parametrize("shape", [(82, 4096, 4096), (1, 1024, 4096), (16, 4096, 14336), (40, 14336, 4096),
                                    (5, 300, 640)])
 def test_int4_split_k_few_tokens(oracle_lib, shape):
     """Few tokens (the listing page's Table 11 forwards of 82 tokens, and decoding): the
@@ -535,6 +535,29 @@ def test_int4_split_k_few_tokens(oracle_lib, shape):
     for y, splits in ((y1, ks), (y0, 1)):
         got = y.cpu().numpy().astype(np.float64)[mi, ni]
         assert np.all(np.abs(got - ref) <= _i4_tol(K, g, absy, ref, torch.float32, splits)), splits
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_int4_small_tile_bitwise(g):
+    """Up to 96 tokens the INT4 layer tiles the activations 32 rows at a time, beyond that
+    128; each output element is the same sum in the same order either way, so the first rows
+    of a 200-token product equal the 1-, 40- and 96-token products of those rows bit for bit
+    (unsplit, fp32 and bf16 out)."""
+    Mb, N, K = 200, 300, 1024
+    a, asc, b, bsc, r = _i4_inputs(Mb, N, K, g, 77 + g)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    B, Bs, R = dev(b), dev(bsc.view(np.int16)), to_dev(r)
+    for out in (torch.float32, torch.bfloat16):
+        yb = dq.quantized_linear(dev(a), dev(asc.view(np.int16)), B, Bs, Mb, N, K, "INT4", r=R,
+                                 out_dtype=out, group=g, split=False)
+        for M in (1, 40, 96):
+            print(f"[linear] INT4 g{g} 32-row tiles, {M} of {Mb} rows, {out}", flush=True)
+            A = dev(a.reshape(Mb, K // 2)[:M])
+            As = dev(asc.view(np.int16).reshape(Mb, K // g)[:M])
+            ys = dq.quantized_linear(A, As, B, Bs, M, N, K, "INT4", r=R, out_dtype=out, group=g,
+                                     split=False)
+            torch.cuda.synchronize()
+            assert torch.equal(ys, yb[:M]), (M, out)
 
 
 def test_int4_split_workspace_reused():
