@@ -452,6 +452,8 @@ def main():
                       "linear_w4a4_int4": 20, "llama31_8b_w4a4": 10,
                       "qkv_acts_nvfp4": 20}.get(args.workload, 200)
 
+    if args.tokens < 1 or args.steps < 1 or args.warmup < 0:
+        ap.error("--tokens and --steps must be positive and --warmup not negative")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the solve runs on a single MI355X and the library "
               "has no multi-GPU path (pass --gpus 1).", file=sys.stderr)
