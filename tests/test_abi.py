@@ -170,3 +170,25 @@ def test_recode_argument_errors(dq):
     assert L.dq_recode_mxint4_to_mxfp6(0x10008, 0x20000, 4, 64, 0x30000, 0x40000, None) == -3
     assert L.dq_recode_mxint4_to_mxfp6(0x10000, 0x20000, 4, 64, 0x30004, 0x40000, None) == -3
     assert L.dq_recode_mxint4_to_mxfp6(None, None, 0, 64, None, None, None) == 0
+
+
+def test_header_is_plain_c(tmp_path):
+    """The header compiles as strict C99 (no C++ or HIP types in the ABI), and a C program
+    links against the library and calls it (status strings only: no device needed)."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    src = tmp_path / "abi.c"
+    src.write_text('#include <string.h>\n#include "dq.h"\n'
+                   'int main(void) {\n'
+                   '  const char* s = dq_status_string(DQ_ERR_WORKSPACE);\n'
+                   '  return (s && strstr(s, "workspace")) ? 0 : 1;\n}\n')
+    lib = ROOT / "post_quantization_dq_amd"
+    exe = tmp_path / "abi"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    f"-I{ROOT / 'include'}", str(src), f"-L{lib}", "-ldq",
+                    f"-Wl,-rpath,{lib}", "-o", str(exe)], check=True)
+    assert subprocess.run([str(exe)]).returncode == 0
