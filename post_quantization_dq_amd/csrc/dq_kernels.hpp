@@ -765,23 +765,22 @@ __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
       float rr_[U], irn[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t i = i0 + 8 * u;
-        if (i < row1) {
-          raw[u].load(P.W, i, P.ld, j0);
-          load_codes<FMT, L>(qcodes, qscales, i, n, chn, g, cw[u], sc[u]);
-          rr_[u] = rnew[i];
-          irn[u] = (FMT == NVFP4) ? irnew[i] : 0.0f;
-        } else {
-          raw[u].zero();
-          cw[u][0] = cw[u][1] = cw[u][2] = cw[u][3] = sc[u] = 0u;
-          rr_[u] = 0.0f;
-          irn[u] = 0.0f;
-        }
+        // rows past the range load the range's last row (not summed): every row's loads are
+        // issued on one path, so the compiler's wait before a row's products leaves the later
+        // rows' loads in flight
+        const int64_t i = i0 + 8 * u < row1 ? i0 + 8 * u : row1 - 1;
+        raw[u].load(P.W, i, P.ld, j0);
+        load_codes<FMT, L>(qcodes, qscales, i, n, chn, g, cw[u], sc[u]);
+        rr_[u] = rnew[i];
+        irn[u] = (FMT == NVFP4) ? irnew[i] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (i0 + 8 * u >= row1) break;
         float w[16], p[16];
+        // keep the scale code's use (and so the wait for it, which in order covers this row's
+        // other loads) here, after the previous row's products
+        asm volatile("" : "+v"(sc[u]));
         raw[u].unpack(w);
         decode_grid<FMT>(cw[u], p);
         const float f = block_factor<FMT>(sc[u], &tab);
