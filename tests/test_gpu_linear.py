@@ -506,10 +506,10 @@ def test_int4_argument_errors():
 
 
 @pytest.mark.parametrize("shape", [(82, 4096, 4096), (1, 1024, 4096), (16, 4096, 14336), (40, 14336, 4096),
-                                   (5, 300, 640)])
+                                   (5, 300, 640), (130, 1024, 4096)])
 def test_int4_split_k_few_tokens(oracle_lib, shape):
     """Few tokens (the listing page's Table 11 forwards of 82 tokens, and decoding): the
-    layer splits K over a workspace.  Sampled entries (all of them for the small case)
+    layer splits K over a workspace (32-row tiles up to 96 tokens, 128-row tiles beyond).  Sampled entries (all of them for the small case)
     against the oracle within the split bound; two calls bitwise equal; the unsplit kernel
     on the same codes within the same bound."""
     M, N, K = shape
