@@ -135,15 +135,17 @@ def bench_llama_set(args):
     for _ in range(args.warmup):
         dq.solve_many(probs, "NVFP4", T, workspace=ws, read_reports=False)
     torch.cuda.synchronize()
-    passes = []
+    work_sweeps = max(dq.read_report(p).sweeps for p in probs) if args.warmup > 0 else 0
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for k in range(args.steps):
-        dq.solve_many(probs, "NVFP4", T, workspace=ws, pass_ms=passes if k == args.steps - 1 else None,
-                      read_reports=False)
+        # the last step carries a begin/end event pair on each solver launch, read after the wait
+        dq.solve_many(probs, "NVFP4", T, workspace=ws, read_reports=False,
+                      timed_sweeps=(work_sweeps or 2 * T) if k == args.steps - 1 else 0)
     e1.record()
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
+    passes = dq.timed_passes(probs, T)
     per_all = np.asarray(passes, dtype=np.float64).reshape(-1, 3)
     # Sweeps 1..T run every matrix.  The INIT sweep is lighter, and the re-solve sweeps after
     # rejections only run the matrices that rejected, so both stay out of the per-pass figures.
@@ -504,16 +506,18 @@ def main():
     a_codes, a_scales, a_ts = dq._outputs(ACT_TOKENS, n, fmt, group or dq.DEFAULT_GROUP[fmt], dev)
     a_ws = torch.empty(max(1, dq.dq_quantize_workspace_bytes(ACT_TOKENS, n, spec)), dtype=torch.uint8, device=dev)
 
-    def step(passes=None):
-        # enqueued only: nothing on the host waits for the GPU (the diagnostic timed solve,
-        # used for one step, synchronises to read its events)
-        dq.solve_many(probs, fmt, T, group, workspace=ws, pass_ms=passes, read_reports=False)
+    def step(timed_sweeps=0):
+        # enqueued only: nothing on the host waits for the GPU (the timed step's events are
+        # read after the timed region)
+        dq.solve_many(probs, fmt, T, group, workspace=ws, timed_sweeps=timed_sweeps, read_reports=False)
         dq.dq_rescale_quantize_acts(X, prob.c, spec, a_codes, a_scales, a_ts, a_ws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    passes = []
+    # every step solves the same inputs, so the sweeps that did work in a warm-up step are the
+    # ones the timed step runs: only those carry events
+    work_sweeps = max(dq.read_report(p).sweeps for p in probs) if args.warmup > 0 else 0
     reps = []
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -522,11 +526,12 @@ def main():
     e0.record()
     for k in range(args.steps):
         # the last timed step also records a begin/end event pair on each solver kernel launch
-        step(passes if k == args.steps - 1 else None)
+        step((work_sweeps or 2 * T) if k == args.steps - 1 else 0)
     e1.record()
     torch.cuda.synchronize()
-    reps.append(dq.read_report(prob))
     wall = time.perf_counter() - t0
+    reps.append(dq.read_report(prob))
+    passes = dq.timed_passes(probs, T)
     ms_step = e0.elapsed_time(e1) / args.steps
     print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms)", flush=True)
 

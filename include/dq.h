@@ -181,6 +181,20 @@ int dq_solve_timed(const dq_problem* problems, int32_t count, dq_quant_spec spec
                    void* stream, float* pass_ms, int32_t pass_ms_capacity,
                    int32_t* pass_ms_count);
 
+/* The same diagnostic split in two so that timing adds no wait to the stream.
+ * dq_solve_timed_enqueue is dq_solve (same arguments, same outputs, asynchronous) with the
+ * event pairs attached to the first `timed_sweeps` (>= 1, else DQ_ERR_ARG) queued sweeps.
+ * dq_solve_timed_read, called on the same current device after the caller has waited for
+ * that stream, writes the three durations per sweep of the last timed solve enqueued on the
+ * device to the HOST array pass_ms (pass_ms_capacity sweeps at most; *pass_ms_count =
+ * sweeps written); DQ_ERR_HIP if the stream has not run them yet.  The events belong to the
+ * library, one set per device: timed solves on one device must not overlap between their
+ * enqueue and their read. */
+int dq_solve_timed_enqueue(const dq_problem* problems, int32_t count, dq_quant_spec spec,
+                           const dq_solve_opts* opts, void* workspace, size_t workspace_bytes,
+                           void* stream, int32_t timed_sweeps);
+int dq_solve_timed_read(float* pass_ms, int32_t pass_ms_capacity, int32_t* pass_ms_count);
+
 /* Bytes of workspace dq_quantize_weights / dq_rescale_quantize_acts need. */
 size_t dq_quantize_workspace_bytes(int64_t rows, int64_t cols, dq_quant_spec spec);
 

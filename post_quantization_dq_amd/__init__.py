@@ -76,6 +76,11 @@ _lib.dq_solve.restype = C.c_int
 _lib.dq_solve_timed.argtypes = [C.POINTER(dq_problem), _i32, dq_quant_spec, C.POINTER(dq_solve_opts), _vp,
                                 _sz, _vp, C.POINTER(C.c_float), _i32, C.POINTER(C.c_int32)]
 _lib.dq_solve_timed.restype = C.c_int
+_lib.dq_solve_timed_enqueue.argtypes = [C.POINTER(dq_problem), _i32, dq_quant_spec, C.POINTER(dq_solve_opts),
+                                        _vp, _sz, _vp, _i32]
+_lib.dq_solve_timed_enqueue.restype = C.c_int
+_lib.dq_solve_timed_read.argtypes = [C.POINTER(C.c_float), _i32, C.POINTER(C.c_int32)]
+_lib.dq_solve_timed_read.restype = C.c_int
 _lib.dq_quantize_workspace_bytes.argtypes = [_i64, _i64, dq_quant_spec]
 _lib.dq_quantize_workspace_bytes.restype = _sz
 _lib.dq_quantize_weights.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _vp, dq_quant_spec, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -104,7 +109,8 @@ _lib.dq_dequantize.restype = C.c_int
 _lib.dq_debug_round.argtypes = [_i32, _vp, _vp, _i64, _vp]
 _lib.dq_debug_round.restype = C.c_int
 
-EXPORTED = ("dq_workspace_bytes", "dq_solve", "dq_solve_timed", "dq_quantize_workspace_bytes",
+EXPORTED = ("dq_workspace_bytes", "dq_solve", "dq_solve_timed", "dq_solve_timed_enqueue",
+            "dq_solve_timed_read", "dq_quantize_workspace_bytes",
             "dq_quantize_weights",
             "dq_rescale_quantize_acts", "dq_rescale_quantize_acts_noalloc",
             "dq_quantize_multi_workspace_bytes",
@@ -210,6 +216,26 @@ def dq_solve_timed(problems, spec: dq_quant_spec, opts: dq_solve_opts, workspace
     n = C.c_int32(0)
     _check(_lib.dq_solve_timed(arr, len(problems), spec, C.byref(opts), _ptr(workspace), nbytes,
                                _stream(stream), buf, int(capacity), C.byref(n)), "dq_solve_timed")
+    return [tuple(float(buf[3 * k + q]) for q in range(3)) for k in range(n.value)]
+
+
+def dq_solve_timed_enqueue(problems, spec: dq_quant_spec, opts: dq_solve_opts,
+                           workspace: torch.Tensor, timed_sweeps: int, stream=None) -> None:
+    """dq_solve with event pairs on the first `timed_sweeps` queued sweeps; returns without
+    waiting.  Read the durations with dq_solve_timed_read once the stream has run them."""
+    arr = _problem_array(problems)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.dq_solve_timed_enqueue(arr, len(problems), spec, C.byref(opts), _ptr(workspace),
+                                       nbytes, _stream(stream), int(timed_sweeps)),
+           "dq_solve_timed_enqueue")
+
+
+def dq_solve_timed_read(capacity: int) -> list[tuple[float, float, float]]:
+    """(row pass, column pass, finalize) durations in ms per timed sweep of the last timed
+    solve enqueued on the current device; the caller has waited for its stream."""
+    buf = (C.c_float * (3 * max(1, capacity)))()
+    n = C.c_int32(0)
+    _check(_lib.dq_solve_timed_read(buf, int(capacity), C.byref(n)), "dq_solve_timed_read")
     return [tuple(float(buf[3 * k + q]) for q in range(3)) for k in range(n.value)]
 
 
@@ -341,13 +367,16 @@ def make_problem(W: torch.Tensor, fmt: str, iters: int, group: int | None = None
 
 def solve_many(problems, fmt: str, iters: int, group: int | None = None, tol: float = 0.0,
                stream=None, workspace: torch.Tensor | None = None, pass_ms: list | None = None,
-               steps: int = 0, read_reports: bool = True):
+               steps: int = 0, read_reports: bool = True, timed_sweeps: int = 0):
     """Solve a batch of problems.  `workspace` may be passed in to reuse one allocation.
     When `pass_ms` is a list, the diagnostic dq_solve_timed runs instead and appends one
     (row pass, column pass, finalize) tuple of event-timed durations in ms per sweep that did
-    work.  `steps` selects the scale steps (DQ_STEP_ROW | DQ_STEP_COL; 0 = both).  Returns
-    the reports read back from the device (a synchronisation), or None with
-    read_reports=False (the solve is then only enqueued)."""
+    work.  With timed_sweeps > 0 the solve is enqueued with those events attached to its
+    first `timed_sweeps` queued sweeps but nothing waits for it; timed_passes() reads them
+    afterwards.  `steps` selects the scale steps
+    (DQ_STEP_ROW | DQ_STEP_COL; 0 = both).  Returns the reports read back from the device
+    (a synchronisation), or None with read_reports=False (the solve is then only
+    enqueued)."""
     spec = spec_of(fmt, group)
     opts = dq_solve_opts(int(iters), float(tol), int(steps))
     nbytes = dq_workspace_bytes(problems, spec, opts)
@@ -360,11 +389,22 @@ def solve_many(problems, fmt: str, iters: int, group: int | None = None, tol: fl
         per = dq_solve_timed(problems, spec, opts, ws, 2 * int(iters) + 2, stream)
         ran = max(read_report(p).sweeps for p in problems)
         pass_ms.extend(per[:ran])
+    elif timed_sweeps > 0:
+        dq_solve_timed_enqueue(problems, spec, opts, ws, int(timed_sweeps), stream)
     else:
         dq_solve(problems, spec, opts, ws, stream)
     if not read_reports:
         return None
     return [read_report(p) for p in problems]
+
+
+def timed_passes(problems, iters: int) -> list[tuple[float, float, float]]:
+    """The per-sweep pass durations of the last timed solve_many(timed_sweeps=...) on the
+    current device, for the timed sweeps that did work; call after waiting for the solve's
+    stream."""
+    per = dq_solve_timed_read(2 * int(iters) + 2)
+    ran = max(read_report(p).sweeps for p in problems)
+    return per[:ran]
 
 
 def solve(W: torch.Tensor, fmt: str, iters: int, group: int | None = None, r_init=None,

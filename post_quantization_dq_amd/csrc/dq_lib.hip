@@ -742,18 +742,22 @@ size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_sp
 // iteration T ends the solve), i.e. at most 2T (1 for T = 0).
 static int max_sweeps(int iters) { return iters > 0 ? 2 * iters : 1; }
 
-// The solve, stream-ordered.  With `timing` set, a begin/end event pair is attached to each
-// pass's launches (row pass, column pass, finalize + decision, all groups) of every queued
-// sweep, and the stream is synchronised at the end to read them.
-struct PassTiming {
-  float* ms;
-  int32_t capacity;
-  int32_t* count;
-};
+// The solve, stream-ordered.  With `timed_sweeps` > 0, a begin/end event pair is attached to
+// each pass's launches (row pass, column pass, finalize + decision, all groups) of the first
+// `timed_sweeps` queued sweeps; the events are read later (dq_solve_timed_read), once the
+// caller's stream has run them, so timing adds no wait to the stream.
+//
+// Those events are created once per device and kept for the process (six per sweep created
+// on every call cost host time the GPU spent idle), with the number of sweeps the last timed
+// solve on the device attached them to.  The lock guards that state; timed solves on one
+// device must not overlap between their enqueue and their read.
+static std::mutex g_timing_mu;
+static std::vector<hipEvent_t> g_timing_events[64];
+static int32_t g_timing_count[64];
 
 static int solve_impl(const dq_problem* problems, int32_t count, dq_quant_spec spec,
                       const dq_solve_opts* opts, void* workspace, size_t workspace_bytes,
-                      void* stream, const PassTiming* timing) {
+                      void* stream, int32_t timed_sweeps) {
   int g = 0;
   int rc = validate_solve(problems, count, spec, opts, &g);
   if (rc) return rc;
@@ -794,11 +798,17 @@ static int solve_impl(const dq_problem* problems, int32_t count, dq_quant_spec s
   }
   DQ_HIP(hipMemcpyAsync(live, up.data(), up.size(), hipMemcpyHostToDevice, s));
 
-  std::vector<hipEvent_t> ev;
-  auto cleanup = [&]() {
-    for (auto e : ev) (void)hipEventDestroy(e);
-    ev.clear();
-  };
+  std::unique_lock<std::mutex> timing_lock(g_timing_mu, std::defer_lock);
+  std::vector<hipEvent_t>* evp = nullptr;
+  int32_t* timed_count = nullptr;
+  if (timed_sweeps > 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DQ_ERR_HIP;
+    timing_lock.lock();
+    evp = &g_timing_events[dev];
+    timed_count = &g_timing_count[dev];
+    *timed_count = 0;
+  }
   if (!pl.groups.empty()) {
     int64_t maxdim = 1;
     int max_init = 1;
@@ -827,15 +837,19 @@ static int solve_impl(const dq_problem* problems, int32_t count, dq_quant_spec s
     // exits at its first instruction (the live counter), so nothing waits on the host.
     const int nsw = max_sweeps(iters);
     const size_t ng = pl.groups.size();
-    if (timing) *timing->count = 0;
+    if (timed_count) {
+      const size_t need = 6 * (size_t)std::min(nsw, (int)timed_sweeps);
+      while (evp->size() < need) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return DQ_ERR_HIP;
+        evp->push_back(e);
+      }
+    }
     for (int sw = 0; sw < nsw; ++sw) {
-      const bool tm = timing && *timing->count < timing->capacity;
+      const bool tm = timed_count && *timed_count < timed_sweeps;
       hipEvent_t e[6] = {};
       if (tm)
-        for (int q = 0; q < 6; ++q) {
-          if (hipEventCreate(&e[q]) != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
-          ev.push_back(e[q]);
-        }
+        for (int q = 0; q < 6; ++q) e[q] = (*evp)[6 * (size_t)*timed_count + q];
       for (int which = 0; which < 3; ++which) {
         for (size_t gi = 0; gi < ng; ++gi) {
           const auto& G = pl.groups[gi];
@@ -849,10 +863,10 @@ static int solve_impl(const dq_problem* problems, int32_t count, dq_quant_spec s
                          : launch_finalize_any(spec.fmt, G, dprobs,
                                                (const WgEntry*)(ws + G.fin_off), s, sw, live);
           t_ev_start = t_ev_stop = nullptr;
-          if (rc) { cleanup(); return rc; }
+          if (rc) return rc;
         }
       }
-      if (tm) ++*timing->count;
+      if (tm) ++*timed_count;
     }
   }
   // outputs and device reports: workgroups per problem of the outputs kernel -- one 64-byte
@@ -866,26 +880,40 @@ static int solve_impl(const dq_problem* problems, int32_t count, dq_quant_spec s
       1, std::min<int64_t>({(max_copy + 16383) / 16384, 2048, std::max<int64_t>(1, 65536 / count)}));
   hipLaunchKernelGGL(k_outputs, dim3((unsigned)out_x, (unsigned)count), dim3(256), 0, s, dprobs,
                      code_bits(spec.fmt), scale_bytes(spec.fmt), g);
-  if (hipGetLastError() != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
-  if (timing) {
-    if (hipStreamSynchronize(s) != hipSuccess) { cleanup(); return DQ_ERR_HIP; }
-    for (int k = 0; k < *timing->count; ++k)
-      for (int q = 0; q < 3; ++q) {
-        float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, ev[6 * k + 2 * q], ev[6 * k + 2 * q + 1]) != hipSuccess) {
-          cleanup();
-          return DQ_ERR_HIP;
-        }
-        timing->ms[3 * k + q] = ms;
-      }
-  }
-  cleanup();
+  if (hipGetLastError() != hipSuccess) return DQ_ERR_HIP;
   return DQ_OK;
 }
 
 int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,
              const dq_solve_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
-  return solve_impl(problems, count, spec, opts, workspace, workspace_bytes, stream, nullptr);
+  return solve_impl(problems, count, spec, opts, workspace, workspace_bytes, stream, 0);
+}
+
+int dq_solve_timed_enqueue(const dq_problem* problems, int32_t count, dq_quant_spec spec,
+                           const dq_solve_opts* opts, void* workspace, size_t workspace_bytes,
+                           void* stream, int32_t timed_sweeps) {
+  if (timed_sweeps < 1) return DQ_ERR_ARG;
+  return solve_impl(problems, count, spec, opts, workspace, workspace_bytes, stream, timed_sweeps);
+}
+
+int dq_solve_timed_read(float* pass_ms, int32_t pass_ms_capacity, int32_t* pass_ms_count) {
+  if (!pass_ms || !pass_ms_count) return DQ_ERR_NULL;
+  if (pass_ms_capacity < 0) return DQ_ERR_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  const std::vector<hipEvent_t>& ev = g_timing_events[dev];
+  const int32_t n = std::min(g_timing_count[dev], pass_ms_capacity);
+  for (int k = 0; k < n; ++k)
+    for (int q = 0; q < 3; ++q) {
+      float ms = 0.0f;
+      // hipErrorNotReady: the stream has not run the timed launches yet
+      if (hipEventElapsedTime(&ms, ev[6 * k + 2 * q], ev[6 * k + 2 * q + 1]) != hipSuccess)
+        return DQ_ERR_HIP;
+      pass_ms[3 * k + q] = ms;
+    }
+  *pass_ms_count = n;
+  return DQ_OK;
 }
 
 int dq_solve_timed(const dq_problem* problems, int32_t count, dq_quant_spec spec,
@@ -894,8 +922,17 @@ int dq_solve_timed(const dq_problem* problems, int32_t count, dq_quant_spec spec
                    int32_t* pass_ms_count) {
   if (!pass_ms || !pass_ms_count) return DQ_ERR_NULL;
   if (pass_ms_capacity < 0) return DQ_ERR_ARG;
-  PassTiming t{pass_ms, pass_ms_capacity, pass_ms_count};
-  return solve_impl(problems, count, spec, opts, workspace, workspace_bytes, stream, &t);
+  int rc = pass_ms_capacity > 0
+               ? solve_impl(problems, count, spec, opts, workspace, workspace_bytes, stream,
+                            pass_ms_capacity)
+               : solve_impl(problems, count, spec, opts, workspace, workspace_bytes, stream, 0);
+  if (rc) return rc;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DQ_ERR_HIP;
+  if (pass_ms_capacity == 0) {
+    *pass_ms_count = 0;
+    return DQ_OK;
+  }
+  return dq_solve_timed_read(pass_ms, pass_ms_capacity, pass_ms_count);
 }
 
 size_t dq_quantize_workspace_bytes(int64_t rows, int64_t cols, dq_quant_spec spec) {

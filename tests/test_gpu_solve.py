@@ -464,6 +464,48 @@ def test_stream_ordered_on_a_side_stream():
     assert (rep.flags & 32) == 0
 
 
+def test_timed_solves_match_the_plain_solve():
+    """The diagnostic timed solves (synchronous, and enqueue + read after the caller's wait)
+    attach events and change nothing else: outputs and reports equal dq_solve's bit for bit,
+    both report one positive duration triple per sweep that did work, and a second timed
+    enqueue of a smaller problem replaces the first one's durations."""
+    iters = 40
+    W = synth.workload("w256x512_int4")[0]
+    ref = _gpu_solve(W, "INT4", iters)
+    assert ref["rejected"] > 0          # re-solve sweeps among the timed ones
+    for mode in ("sync", "enqueue"):
+        p = dq.make_problem(to_dev(W), "INT4", iters)
+        if mode == "sync":
+            per = []
+            rep = dq.solve_many([p], "INT4", iters, pass_ms=per)[0]
+        else:
+            assert dq.solve_many([p], "INT4", iters, timed_sweeps=2 * iters, read_reports=False) is None
+            torch.cuda.synchronize()
+            per = dq.timed_passes([p], iters)
+            rep = dq.read_report(p)
+        assert np.array_equal(p.codes.cpu().numpy(), ref["codes"]), mode
+        assert np.array_equal(p.block_scales.cpu().numpy().view(np.uint16), ref["scales"].view(np.uint16))
+        assert np.array_equal(p.r.cpu().numpy(), ref["r"]) and np.array_equal(p.c.cpu().numpy(), ref["c"])
+        assert np.array_equal(p.nmse_hist.cpu().numpy(), ref["nmse"])
+        assert rep.sweeps == ref["sweeps"] and rep.rejected_steps == ref["rejected"]
+        assert len(per) == ref["sweeps"], mode
+        assert all(t > 0.0 for trip in per for t in trip), mode
+    small = dq.make_problem(to_dev(synth.matrix(synth.WORKLOADS["w256x512_int4"]["W"].scaled(64, 512), 1)),
+                            "MXFP4", 3)
+    dq.solve_many([small], "MXFP4", 3, timed_sweeps=100, read_reports=False)
+    torch.cuda.synchronize()
+    per = dq.dq_solve_timed_read(2 * iters + 2)
+    assert len(per) == 2 * 3          # the smaller solve's 2T queued sweeps, not the earlier 80
+    assert len(dq.timed_passes([small], 3)) == dq.read_report(small).sweeps
+    # timing only the first sweeps leaves the outputs alone
+    again = dq.make_problem(small.W, "MXFP4", 3)
+    dq.solve_many([again], "MXFP4", 3, timed_sweeps=2, read_reports=False)
+    torch.cuda.synchronize()
+    assert len(dq.dq_solve_timed_read(10)) == 2
+    assert torch.equal(again.codes, small.codes) and torch.equal(again.r, small.r)
+    assert torch.equal(again.c, small.c) and torch.equal(again.nmse_hist, small.nmse_hist)
+
+
 def test_device_reports_of_a_batch_with_an_empty_problem():
     probs = [dq.make_problem(to_dev(synth.matrix(synth.WORKLOADS["w256x512_int4"]["W"].scaled(64, 512), 1)),
                              "MXFP4", 5),
