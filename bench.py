@@ -264,7 +264,9 @@ def bench_llama_w4a4(args):
     dq_solve), then one forward of `tokens` tokens runs, layer by layer, the activation
     rescale-and-quantise with each projection's solved c (q/k/v and gate/up fused, as they
     read the same activations) and the 7 INT4 layers on the int8 cores.  The whole forward,
-    the 224 layers alone and the activation quantisation alone are timed with events."""
+    the 224 layers alone and the activation quantisation alone are timed with events, both
+    replayed from a HIP graph recorded once (the reported figures) and issued call by call
+    from Python (the eager_* fields)."""
     import torch
 
     import post_quantization_dq_amd as dq
@@ -343,13 +345,39 @@ def bench_llama_w4a4(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    ms_fwd = timed(forward)
-    ms_lin = timed(lambda: [linears(layer) for layer in range(L)])
-    ms_act = timed(lambda: [quantise(layer) for layer in range(L)])
+    def all_linears():
+        for layer in range(L):
+            linears(layer)
+
+    def all_quantise():
+        for layer in range(L):
+            quantise(layer)
+
+    def graphed(fn):
+        # The same calls recorded once in a HIP graph and replayed: the launches no longer
+        # wait on the host (every call only enqueues kernels: no allocation, memset or wait)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        torch.cuda.synchronize()
+        ms = timed(gr.replay)
+        del gr
+        return ms
+
+    eager_fwd, eager_lin, eager_act = timed(forward), timed(all_linears), timed(all_quantise)
+    ms_fwd, ms_lin, ms_act = graphed(forward), graphed(all_linears), graphed(all_quantise)
+    print(f"[bench] eager: forward {eager_fwd:.3f} ms (layers {eager_lin:.3f}, act quant {eager_act:.3f}); "
+          f"graph: forward {ms_fwd:.3f} ms (layers {ms_lin:.3f}, act quant {ms_act:.3f})", flush=True)
     tops = 2.0 * tokens * elems / (ms_lin * 1e-3) / 1e12
     out = {
         "metric": "W4A4 INT4 g64 Llama-3.1-8B-shaped forward: activation quantisation (incl. beta) "
-                  "and the 224 quantised linears, ms per forward",
+                  "and the 224 quantised linears, ms per forward (one HIP graph per forward)",
         "value": round(ms_fwd, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_fwd, 4), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "int4", "data": "synthetic",
@@ -357,6 +385,9 @@ def bench_llama_w4a4(args):
                                f"{tokens} tokens per forward; q/k/v and gate/up activations "
                                "quantised together", "tokens": tokens, "elements": elems},
         "linears_ms": round(ms_lin, 4), "act_quant_ms": round(ms_act, 4),
+        # the same calls issued one by one from Python, each launch waiting on the host
+        "eager_ms": round(eager_fwd, 4), "eager_linears_ms": round(eager_lin, 4),
+        "eager_act_quant_ms": round(eager_act, 4),
         "split_k_workspace_bytes": int(lws_bytes),
         "roofline": {"bound": "mfma", "kernel": "k_linear_i4 (all 224 launches)",
                      "achieved": round(tops, 1), "peak": I8_MFMA_PEAK_TOPS, "unit": "TOP/s",

@@ -1,0 +1,107 @@
+"""The layer-side calls recorded in a HIP graph.
+
+dq_rescale_quantize_acts (NVFP4: amax partials in the workspace), its multi-output form
+(INT4 g64) and dq_quantized_linear_ws (INT4 with K split over a workspace; NVFP4) enqueue
+kernels only: no allocation, no memset, no host wait, and every workspace byte a kernel
+reads was written earlier in the same call.  So a forward made of them can be captured
+once and replayed.  Each replay here runs on new inputs, with eager work and host
+synchronisations between replays, and must equal the eager calls on the same inputs bit
+for bit (codes, scales, tensor scales and layer outputs)."""
+
+import pytest
+import torch
+
+import post_quantization_dq_amd as dq
+from gpu_util import DEV
+
+pytestmark = pytest.mark.gpu
+
+M, K, NQ, NN = 16, 4096, 1024, 512
+
+
+def _randn(rows, cols, seed, std, dtype=torch.bfloat16):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(rows, cols, generator=g) * std).to(dtype).to(DEV)
+
+
+def _col_scales(cols, seed):
+    g = torch.Generator().manual_seed(seed)
+    c = torch.exp2(torch.rand(cols, generator=g) * 2.0 - 1.0)
+    return c.to(torch.bfloat16).float().to(DEV)   # bf16 values, as the solver's c are
+
+
+class _Fwd:
+    """Buffers and workspaces of one mini forward: q/k/v-like INT4 g64 layers fed by one
+    fused activation quantise, and an NVFP4 layer fed by the single-output quantise."""
+
+    def __init__(self, w):
+        self.w = w
+        si, sn = dq.spec_of("INT4", 64), dq.spec_of("NVFP4")
+        self.si, self.sn = si, sn
+        self.acts = [dq._outputs(M, K, "INT4", 64, DEV) for _ in range(3)]
+        self.qws = torch.empty(max(1, dq.dq_quantize_multi_workspace_bytes(M, K, 3, si)),
+                               dtype=torch.uint8, device=DEV)
+        nb = dq.dq_quantized_linear_workspace_bytes(si, M, NQ, K)
+        assert nb > 0   # few tokens: K is split
+        self.lws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        self.ys = [torch.empty(M, NQ, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+        self.nact = dq._outputs(M, K, "NVFP4", 16, DEV)
+        self.nws = torch.empty(max(1, dq.dq_quantize_workspace_bytes(M, K, sn)), dtype=torch.uint8,
+                               device=DEV)
+        self.yn = torch.empty(M, NN, dtype=torch.float32, device=DEV)
+
+    def run(self, X, X2):
+        w = self.w
+        dq.dq_rescale_quantize_acts_multi(X, w["c"], self.si, [a[0] for a in self.acts],
+                                          [a[1] for a in self.acts], [a[2] for a in self.acts],
+                                          self.qws)
+        for o in range(3):
+            codes, scales, _ = w["q"][o]
+            dq.dq_quantized_linear_ws(self.si, self.acts[o][0], self.acts[o][1], None, M, codes,
+                                      scales, None, NQ, K, w["r"][o], self.ys[o], self.lws)
+        dq.dq_rescale_quantize_acts(X2, w["cn"], self.sn, *self.nact, self.nws)
+        codes, scales, ts = w["n"]
+        dq.dq_quantized_linear_ws(self.sn, self.nact[0], self.nact[1], self.nact[2], M, codes,
+                                  scales, ts, NN, K, w["rn"], self.yn, None)
+
+    def outputs(self):
+        out = [t for a in self.acts for t in a] + self.ys + list(self.nact) + [self.yn]
+        return [t.clone() for t in out]
+
+
+def test_captured_forward_replays_equal_eager():
+    w = {"c": [_col_scales(K, 10 + o) for o in range(3)], "cn": _col_scales(K, 20)}
+    w["q"] = [dq.quantize_weights(_randn(NQ, K, 30 + o, 0.02), fmt="INT4", group=64)
+              for o in range(3)]
+    w["r"] = [_col_scales(NQ, 40 + o) for o in range(3)]
+    w["n"] = dq.quantize_weights(_randn(NN, K, 50, 0.02), fmt="NVFP4")
+    w["rn"] = _col_scales(NN, 51)
+    X = _randn(M, K, 1, 1.0)
+    X2 = _randn(M, K, 2, 1.0)
+    eager, graphed = _Fwd(w), _Fwd(w)
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graphed.run(X, X2)   # a first run outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.run(X, X2)
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        # new inputs in place (eager work between replays), then eager calls and the replay
+        X.copy_(_randn(M, K, 100 + rep, 1.0 + rep))
+        X2.copy_(_randn(M, K, 200 + rep, 0.5 + rep))
+        torch.cuda.synchronize()
+        eager.run(X, X2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(eager.outputs(), graphed.outputs())):
+            assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                               b.view(torch.uint8) if b.dtype != torch.uint8 else b), (rep, k)
+        assert torch.count_nonzero(eager.ys[0]) > 0 and torch.count_nonzero(eager.yn) > 0
