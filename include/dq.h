@@ -44,6 +44,14 @@
  *   - Errors are returned synchronously.  Every argument check happens before any GPU work
  *     is enqueued, so a call that returns an error has enqueued nothing.  Conditions that
  *     depend on the data are reported as flag bits (DQ_FLAG_*) in dq_report.
+ *   - The quantisers (dq_quantize_weights, dq_rescale_quantize_acts and its _multi and
+ *     _noalloc forms), the layer (dq_quantized_linear, dq_quantized_linear_ws),
+ *     dq_recode_mxint4_to_mxfp6 and dq_dequantize enqueue kernel launches only: no
+ *     allocation, memset, copy or host wait, and every workspace byte a kernel reads was
+ *     written earlier in the same call.  They may be recorded by HIP stream capture and the
+ *     graph replayed (on new input values at the same addresses).  dq_solve is not
+ *     capture-safe: it clears the histories with memsets and stages its problem
+ *     descriptors with a host-to-device copy.
  */
 #ifndef DQ_H
 #define DQ_H

@@ -1,12 +1,13 @@
-"""The layer-side calls recorded in a HIP graph.
+"""The quantiser and layer calls recorded in a HIP graph.
 
-dq_rescale_quantize_acts (NVFP4: amax partials in the workspace), its multi-output form
-(INT4 g64) and dq_quantized_linear_ws (INT4 with K split over a workspace; NVFP4) enqueue
-kernels only: no allocation, no memset, no host wait, and every workspace byte a kernel
-reads was written earlier in the same call.  So a forward made of them can be captured
-once and replayed.  Each replay here runs on new inputs, with eager work and host
-synchronisations between replays, and must equal the eager calls on the same inputs bit
-for bit (codes, scales, tensor scales and layer outputs)."""
+dq_rescale_quantize_acts (NVFP4: amax partials in the workspace), its multi-output (INT4
+g64) and no-allocation forms, dq_quantize_weights, dq_quantized_linear_ws (INT4 with K split
+over a workspace; NVFP4), dq_recode_mxint4_to_mxfp6 and dq_dequantize enqueue kernels only:
+no allocation, no memset, no host wait, and every workspace byte a kernel reads was written
+earlier in the same call.  So a forward made of them can be captured once and replayed.
+Each replay here runs on new inputs, with eager work and host synchronisations between
+replays, and must equal the eager calls on the same inputs bit for bit (codes, scales,
+tensor scales, dequantised values and layer outputs)."""
 
 import pytest
 import torch
@@ -49,6 +50,17 @@ class _Fwd:
         self.nws = torch.empty(max(1, dq.dq_quantize_workspace_bytes(M, K, sn)), dtype=torch.uint8,
                                device=DEV)
         self.yn = torch.empty(M, NN, dtype=torch.float32, device=DEV)
+        # weight-side calls on a small weight that changes between replays
+        self.wq = dq._outputs(NN, K, "NVFP4", 16, DEV)
+        self.wws = torch.empty(max(1, dq.dq_quantize_workspace_bytes(NN, K, sn)), dtype=torch.uint8,
+                               device=DEV)
+        self.wdeq = torch.empty(NN, K, dtype=torch.float32, device=DEV)
+        self.na = dq._outputs(M, K, "NVFP4", 16, DEV)
+        self.mx = dq._outputs(M, K, "MXINT4", 32, DEV)
+        self.mxws = torch.empty(max(1, dq.dq_quantize_workspace_bytes(M, K, dq.spec_of("MXINT4"))),
+                                dtype=torch.uint8, device=DEV)
+        self.rc = (torch.empty(M * K * 3 // 4, dtype=torch.uint8, device=DEV),
+                   torch.empty(M * K // 32, dtype=torch.uint8, device=DEV))
 
     def run(self, X, X2):
         w = self.w
@@ -63,9 +75,15 @@ class _Fwd:
         codes, scales, ts = w["n"]
         dq.dq_quantized_linear_ws(self.sn, self.nact[0], self.nact[1], self.nact[2], M, codes,
                                   scales, ts, NN, K, w["rn"], self.yn, None)
+        dq.dq_quantize_weights(w["W"], w["rn"], w["cn"], self.sn, *self.wq, self.wws)
+        dq.dq_dequantize(self.sn, *self.wq, NN, K, w["rn"], w["cn"], self.wdeq)
+        dq.dq_rescale_quantize_acts_noalloc(X2, w["cn"], self.sn, *self.na)
+        dq.dq_rescale_quantize_acts(X, None, dq.spec_of("MXINT4"), *self.mx, self.mxws)
+        dq.dq_recode_mxint4_to_mxfp6(self.mx[0], self.mx[1], M, K, *self.rc)
 
     def outputs(self):
-        out = [t for a in self.acts for t in a] + self.ys + list(self.nact) + [self.yn]
+        out = ([t for a in self.acts for t in a] + self.ys + list(self.nact) + [self.yn] +
+               list(self.wq) + [self.wdeq] + list(self.na) + list(self.mx[:2]) + list(self.rc))
         return [t.clone() for t in out]
 
 
@@ -76,6 +94,7 @@ def test_captured_forward_replays_equal_eager():
     w["r"] = [_col_scales(NQ, 40 + o) for o in range(3)]
     w["n"] = dq.quantize_weights(_randn(NN, K, 50, 0.02), fmt="NVFP4")
     w["rn"] = _col_scales(NN, 51)
+    w["W"] = _randn(NN, K, 52, 0.02)
     X = _randn(M, K, 1, 1.0)
     X2 = _randn(M, K, 2, 1.0)
     eager, graphed = _Fwd(w), _Fwd(w)
@@ -96,6 +115,7 @@ def test_captured_forward_replays_equal_eager():
         # new inputs in place (eager work between replays), then eager calls and the replay
         X.copy_(_randn(M, K, 100 + rep, 1.0 + rep))
         X2.copy_(_randn(M, K, 200 + rep, 0.5 + rep))
+        w["W"].copy_(_randn(NN, K, 300 + rep, 0.01 * (rep + 1)))
         torch.cuda.synchronize()
         eager.run(X, X2)
         torch.cuda.synchronize()
@@ -105,3 +125,4 @@ def test_captured_forward_replays_equal_eager():
             assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
                                b.view(torch.uint8) if b.dtype != torch.uint8 else b), (rep, k)
         assert torch.count_nonzero(eager.ys[0]) > 0 and torch.count_nonzero(eager.yn) > 0
+        assert torch.count_nonzero(eager.wdeq) > 0 and torch.equal(eager.na[0], eager.nact[0])
