@@ -81,6 +81,15 @@ struct WgEntry {
   int32_t prob, idx;
 };
 
+// The solve's counter of problems still running is followed, kStatesOffset bytes on, by
+// the two state slots of every problem of the call (problem k: slots 2k, 2k + 1), so a
+// pass reaches its state from the launch-table entry alone, in parallel with the problem
+// descriptor, instead of through the descriptor's pointer.
+constexpr int kStatesOffset = 256;
+__device__ __forceinline__ State* state_slots(const int32_t* live, int prob) {
+  return (State*)((const char*)live + kStatesOffset) + 2 * prob;
+}
+
 // Flag bit of a solve whose state did not reach DONE within the sweeps that were queued
 // (cannot happen: a solve of T iterations needs at most 2T sweeps).
 constexpr uint32_t kFlagUnfinished = 32u;
@@ -418,10 +427,12 @@ template <int FMT, int DT, int L, int CG>
 __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ probs,
                                                   const WgEntry* __restrict__ table, int sw,
                                                   const int32_t* __restrict__ live, int compact) {
-  if (*gp(live) == 0) return;   // every problem finished: this queued sweep has nothing to do
+  // the counter and the table entry are requested together (one round of latency)
+  const int32_t nlive = *gp(live);
   const WgEntry we = table[blockIdx.x];
+  if (nlive == 0) return;   // every problem finished: this queued sweep has nothing to do
   const ProbDev& P = probs[we.prob];
-  State* st = P.st + (sw & 1);
+  State* st = state_slots(live, we.prob) + (sw & 1);
   if (st->mode == MODE_DONE) return;
   const PassInfo pi(st, P.iters);
   constexpr bool A64 = grouped_int<FMT>();   // INT4/INT8: exact products accumulated in fp64
@@ -721,10 +732,11 @@ template <int FMT, int DT, int L>
 __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
                                              const WgEntry* __restrict__ table, int sw,
                                              const int32_t* __restrict__ live) {
-  if (*gp(live) == 0) return;
+  const int32_t nlive = *gp(live);
   const WgEntry we = table[blockIdx.x];
+  if (nlive == 0) return;
   const ProbDev& P = probs[we.prob];
-  const State* st = P.st + (sw & 1);
+  const State* st = state_slots(live, we.prob) + (sw & 1);
   if (st->mode == MODE_DONE) return;
   const PassInfo pi(st, P.iters);
   if (!pi.next) return;
@@ -862,11 +874,12 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
                                                   int32_t* __restrict__ live) {
   // Once every problem is DONE the state slots are no longer read (the outputs kernel reads
   // the slot of the last sweep a problem ran, recorded in its state), so nothing is carried.
-  if (*gp(live) == 0) return;
+  const int32_t nlive = *gp(live);
   const WgEntry we = table[blockIdx.x];
+  if (nlive == 0) return;
   const ProbDev& P = probs[we.prob];
-  const State* st = P.st + (sw & 1);
-  State* sn = P.st + ((sw + 1) & 1);
+  const State* st = state_slots(live, we.prob) + (sw & 1);
+  State* sn = state_slots(live, we.prob) + ((sw + 1) & 1);
   const int mode = st->mode;
   // workgroups 0 .. fin_wgs-1 reduce columns; the one with index fin_wgs takes the
   // safeguard decision (it needs only the row pass's partials, so it runs alongside)

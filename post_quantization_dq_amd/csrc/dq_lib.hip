@@ -159,7 +159,8 @@ struct Plan {
   };
   std::vector<Group> groups;
   // [live_off, up_end): uploaded at once -- the live-problem counter, the problem
-  // descriptors and every launch table
+  // descriptors and every launch table (and the state slots between the counter and the
+  // descriptors, which k_setup then writes)
   size_t live_off = 0, probs_off = 0, up_end = 0, total = 0;
   int32_t live = 0;   // problems with work (rows and cols > 0)
   std::vector<size_t> prob_off;
@@ -233,7 +234,7 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     d.fin_wgs = (int32_t)((d.cols + 63) / 64);
     d.init_wgs = (int32_t)std::min<int64_t>(1024, d.rows);
     pl.prob_off[k] = off;
-    off = align_up(off + 2 * sizeof(State) + sizeof(uint32_t));
+    off = align_up(off + sizeof(uint32_t));                            // flags
     off = align_up(off + 4 * sizeof(float) * d.rows);                  // r[2], ir[2]
     off = align_up(off + 4 * sizeof(float) * d.cols);                  // c[2], ic[2]
     off = align_up(off + code_bytes(fmt, d.rows, d.cols));             // codes buffer 1
@@ -250,8 +251,8 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
   }
   pl.live = 0;
   for (int k = 0; k < count; ++k) pl.live += pl.group_of[k] >= 0 ? 1 : 0;
-  pl.live_off = off;
-  off = align_up(off + sizeof(int32_t));
+  pl.live_off = off;   // the counter, then (kStatesOffset on) every problem's two state slots
+  off = align_up(off + kStatesOffset + 2 * sizeof(State) * std::max(1, (int)count));
   pl.probs_off = off;
   off = align_up(off + sizeof(ProbDev) * std::max(1, (int)count));
   for (auto& G : pl.groups) {
@@ -279,11 +280,8 @@ void bind_pointers(const dq_problem* p, int32_t count, int g, int fmt, int iters
     ProbDev& d = pl.dev[k];
     char* q = ws + pl.prob_off[k];
     auto take = [&](size_t bytes) { char* r = q; q += align_up(bytes); return r; };
-    {
-      char* sp = take(2 * sizeof(State) + sizeof(uint32_t));
-      d.st = (State*)sp;
-      d.flags = (uint32_t*)(sp + 2 * sizeof(State));
-    }
+    d.st = (State*)(ws + pl.live_off + kStatesOffset) + 2 * k;
+    d.flags = (uint32_t*)take(sizeof(uint32_t));
     float* rr = (float*)take(4 * sizeof(float) * d.rows);
     d.r[0] = rr; d.r[1] = rr + d.rows; d.ir[0] = rr + 2 * d.rows; d.ir[1] = rr + 3 * d.rows;
     float* cc = (float*)take(4 * sizeof(float) * d.cols);
