@@ -110,6 +110,14 @@ int lanes_per_row(int64_t cols) {
   return (int)std::min<int64_t>(1024, std::max<int64_t>(64, (cols / 16 + 63) / 64 * 64));
 }
 int row_slots(int lpr) { return std::max(1, 1024 / lpr); }
+// Rows per quantiser workgroup: as many as 1024 threads hold, halved while that leaves fewer
+// row groups than the grid may take (a few tokens then spread over more CUs instead of
+// stacking 4 rows of 256 lanes on one).  Each row's result does not depend on it.
+int quant_rows_per_group(int lpr, int64_t rows, int64_t max_groups) {
+  int H = row_slots(lpr);
+  while (H > 1 && (rows + H - 1) / H < max_groups) H >>= 1;
+  return H;
+}
 // LDS one workgroup may take on the current device (160 KiB on gfx950), read once per device.
 int device_lds_limit() {
   static std::atomic<int> cache[64];   // 0: not read yet
@@ -515,7 +523,7 @@ int launch_quant_t(const void* X, int64_t rows, int64_t cols, int64_t ld, const 
     hipLaunchKernelGGL((k_qamax<DT, MODEV>), dim3((unsigned)nwg), dim3(256), 0, s, X, rows, cols,
                        ld, r, c, part, nstrips, rpr);
   }
-  const int lpr = lanes_per_row(cols), H = row_slots(lpr);
+  const int lpr = lanes_per_row(cols), H = quant_rows_per_group(lpr, rows, kQuantGroupsMax);
   const int64_t groups = (rows + H - 1) / H;
   const unsigned grid = (unsigned)std::min<int64_t>(groups, kQuantGroupsMax);
   for (int lbeg = 0; lbeg < cols / 16; lbeg += lpr)   // one launch per 16384 columns
@@ -640,7 +648,7 @@ int launch_quant_multi_t(const void* X, int64_t rows, int64_t cols, int64_t ld,
     hipLaunchKernelGGL((k_qamax_multi<DT>), dim3((unsigned)nwg), dim3(256), 0, s, X, rows, cols,
                        ld, mo, part, nstrips, rpr);
   }
-  const int lpr = lanes_per_row(cols), H = row_slots(lpr);
+  const int lpr = lanes_per_row(cols), H = quant_rows_per_group(lpr, rows, kQuantGroupsMax);
   const int64_t groups = (rows + H - 1) / H;
   const unsigned grid = (unsigned)std::min<int64_t>(groups, kQuantGroupsMax);
   const size_t c_bytes = (size_t)mo.count * cols * sizeof(float);
@@ -1056,7 +1064,7 @@ int dq_rescale_quantize_acts_multi(const void* X, int32_t x_dtype, int64_t token
 static int i4_tile_m(int64_t M) { return M <= 96 ? 32 : 128; }
 // Split K for the INT4 layer when its output tiles alone cannot fill the GPU twice over (few
 // tokens): about two workgroups per CU, but no more splits than the stages of K, and partial
-// sums no larger than the weight codes (K / 8M splits of M x N fp32 against N x K / 2
+// sums at most twice the weight codes (K / 4M splits of M x N fp32 against N x K / 2
 // bytes).  With 32-row tiles, whose stages are short, up to 511 tiles are split in two: a
 // 14336-wide layer at 82 tokens (336 tiles) would otherwise run 16 stages back to back.
 static void i4_split(int64_t M, int64_t N, int64_t K, int& ksplit, int& st_split) {
@@ -1066,7 +1074,7 @@ static void i4_split(int64_t M, int64_t N, int64_t K, int& ksplit, int& st_split
   int64_t k = 1;
   if (tiles > 0 && tiles < (tmr == 32 ? 512 : 256) && nst > 1) {
     k = (512 + tiles - 1) / tiles;
-    k = std::min<int64_t>(k, std::max<int64_t>(1, K / (8 * std::max<int64_t>(M, 1))));
+    k = std::min<int64_t>(k, std::max<int64_t>(1, K / (4 * std::max<int64_t>(M, 1))));
     k = std::min<int64_t>(std::min<int64_t>(k, nst), 64);
   }
   const int64_t per = nst > 0 ? (nst + k - 1) / k : 0;

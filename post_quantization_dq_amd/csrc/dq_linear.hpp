@@ -1067,9 +1067,18 @@ __global__ __launch_bounds__(256) void k_linear_i4_reduce(LinArgs p) {
   if (q >= p.M * per_row) return;
   const int64_t m = q / per_row, n = 4 * (q % per_row);
   f32x4 s = *gp((const f32x4*)(p.part + m * p.ldp + n));
-  for (int k = 1; k < p.ksplit; ++k) {
-    const f32x4 t = *gp((const f32x4*)(p.part + ((int64_t)k * p.M + m) * p.ldp + n));
-    s = f32x4{s.x + t.x, s.y + t.y, s.z + t.z, s.w + t.w};
+  // eight splits' loads requested at once (clamped to the last split, not added), then
+  // added in split order
+  for (int k0 = 1; k0 < p.ksplit; k0 += 8) {
+    f32x4 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u < p.ksplit ? k0 + u : p.ksplit - 1;
+      t[u] = *gp((const f32x4*)(p.part + ((int64_t)k * p.M + m) * p.ldp + n));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k0 + u < p.ksplit) s = f32x4{s.x + t[u].x, s.y + t[u].y, s.z + t[u].z, s.w + t[u].w};
   }
   float yv[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
