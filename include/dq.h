@@ -325,7 +325,8 @@ int dq_quantized_linear_ws(dq_quant_spec spec, const uint8_t* a_codes, const uin
                            int64_t K, const float* r, void* y, int32_t y_dtype, int64_t ldy,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes dq_quantized_linear_ws uses for this shape (0: it does not split). */
+/* Workspace bytes dq_quantized_linear_ws uses for this shape (0: it does not split); at most
+ * K (N + 3), twice the weight codes' bytes: the splits are capped so. */
 size_t dq_quantized_linear_workspace_bytes(dq_quant_spec spec, int64_t M, int64_t N, int64_t K);
 
 /* Exact re-encoding of MXINT4 codes as MXFP6 E2M3 codes, so that MXINT4 activations and

@@ -780,6 +780,26 @@ static int solve_impl(const dq_problem* problems, int32_t count, dq_quant_spec s
     d.steps = opts->scale_steps ? opts->scale_steps : (DQ_STEP_ROW | DQ_STEP_COL);
   }
   const int iters = opts->iters;
+  const int nsw = max_sweeps(iters);
+
+  // the timing events, before anything is enqueued
+  std::unique_lock<std::mutex> timing_lock(g_timing_mu, std::defer_lock);
+  std::vector<hipEvent_t>* evp = nullptr;
+  int32_t* timed_count = nullptr;
+  if (timed_sweeps > 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DQ_ERR_HIP;
+    timing_lock.lock();
+    evp = &g_timing_events[dev];
+    timed_count = &g_timing_count[dev];
+    *timed_count = 0;
+    const size_t need = 6 * (size_t)std::min(nsw, (int)timed_sweeps);
+    while (evp->size() < need) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return DQ_ERR_HIP;
+      evp->push_back(e);
+    }
+  }
 
   // empty problems: zero histories (their reports come from the outputs kernel)
   for (int k = 0; k < count; ++k) {
@@ -804,17 +824,6 @@ static int solve_impl(const dq_problem* problems, int32_t count, dq_quant_spec s
   }
   DQ_HIP(hipMemcpyAsync(live, up.data(), up.size(), hipMemcpyHostToDevice, s));
 
-  std::unique_lock<std::mutex> timing_lock(g_timing_mu, std::defer_lock);
-  std::vector<hipEvent_t>* evp = nullptr;
-  int32_t* timed_count = nullptr;
-  if (timed_sweeps > 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DQ_ERR_HIP;
-    timing_lock.lock();
-    evp = &g_timing_events[dev];
-    timed_count = &g_timing_count[dev];
-    *timed_count = 0;
-  }
   if (!pl.groups.empty()) {
     int64_t maxdim = 1;
     int max_init = 1;
@@ -841,16 +850,7 @@ static int solve_impl(const dq_problem* problems, int32_t count, dq_quant_spec s
     }
     // Every sweep a solve may need is queued now; a sweep whose problems are all finished
     // exits at its first instruction (the live counter), so nothing waits on the host.
-    const int nsw = max_sweeps(iters);
     const size_t ng = pl.groups.size();
-    if (timed_count) {
-      const size_t need = 6 * (size_t)std::min(nsw, (int)timed_sweeps);
-      while (evp->size() < need) {
-        hipEvent_t e = nullptr;
-        if (hipEventCreate(&e) != hipSuccess) return DQ_ERR_HIP;
-        evp->push_back(e);
-      }
-    }
     for (int sw = 0; sw < nsw; ++sw) {
       const bool tm = timed_count && *timed_count < timed_sweeps;
       hipEvent_t e[6] = {};

@@ -71,6 +71,26 @@ def test_solve_argument_errors(dq):
     assert dq._lib.dq_solve(arr, 0, dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(1, 0.0, 0)), 0x70000, 1 << 40, None) == -7
 
 
+def test_timed_solve_argument_errors(dq):
+    """The diagnostic timed solves check their own arguments, then the solve's, before any
+    HIP call."""
+    L = dq._lib
+    ok, bad = _problem(dq), _problem(dq, cols=200)
+    spec, opts = dq.dq_quant_spec(3, 0), C.byref(dq.dq_solve_opts(4, 0.0, 0))
+    arr, barr = (dq.dq_problem * 1)(ok), (dq.dq_problem * 1)(bad)
+    buf, n = (C.c_float * 30)(), C.c_int32(5)
+    for k in (0, -3):   # nothing to time
+        assert L.dq_solve_timed_enqueue(arr, 1, spec, opts, 0x70000, 1 << 40, None, k) == -7
+    assert L.dq_solve_timed_enqueue(barr, 1, spec, opts, 0x70000, 1 << 40, None, 8) == -2
+    assert L.dq_solve_timed_enqueue(arr, 1, spec, opts, 0, 0, None, 8) == -5
+    assert L.dq_solve_timed_read(None, 10, C.byref(n)) == -1
+    assert L.dq_solve_timed_read(buf, 10, None) == -1
+    assert L.dq_solve_timed_read(buf, -1, C.byref(n)) == -7
+    assert L.dq_solve_timed(arr, 1, spec, opts, 0x70000, 1 << 40, None, None, 10, C.byref(n)) == -1
+    assert L.dq_solve_timed(arr, 1, spec, opts, 0x70000, 1 << 40, None, buf, -1, C.byref(n)) == -7
+    assert L.dq_solve_timed(barr, 1, spec, opts, 0x70000, 1 << 40, None, buf, 10, C.byref(n)) == -2
+
+
 def test_workspace_bytes_accounting(dq):
     ok = _problem(dq, rows=4096, cols=14336)
     arr = (dq.dq_problem * 1)(ok)
@@ -157,6 +177,10 @@ def test_linear_workspace_sizes(dq):
     assert dq.dq_quantized_linear_workspace_bytes(dq.dq_quant_spec(2, 0), 82, 4096, 4096) == 0
     assert dq.dq_quantized_linear_workspace_bytes(i4, 82, 4096, 64) == 0     # one stage of K
     assert dq.dq_quantized_linear_workspace_bytes(i4, 0, 4096, 4096) == 0
+    for M, N, K in [(1, 1024, 4096), (16, 4096, 14336), (82, 1024, 4096), (82, 14336, 4096),
+                    (130, 1024, 4096), (5, 300, 640)]:
+        nb2 = dq.dq_quantized_linear_workspace_bytes(i4, M, N, K)
+        assert 0 < nb2 <= K * (N + 3), (M, N, K)   # within twice the weight codes
     L = dq._lib
     # a workspace smaller than needed is refused before anything is launched
     assert L.dq_quantized_linear_ws(i4, 0x10000, 0x20000, None, 82, 0x30000, 0x40000, None, 4096,

@@ -126,3 +126,58 @@ def test_captured_forward_replays_equal_eager():
                                b.view(torch.uint8) if b.dtype != torch.uint8 else b), (rep, k)
         assert torch.count_nonzero(eager.ys[0]) > 0 and torch.count_nonzero(eager.yn) > 0
         assert torch.count_nonzero(eager.wdeq) > 0 and torch.equal(eager.na[0], eager.nact[0])
+
+
+def test_captured_side_streams_equal_serial():
+    """The independent layers of a group recorded on side streams (each with its own split
+    workspace, joined back before the next call) replay to the same bits as the same calls
+    issued one after another on one stream."""
+    si = dq.spec_of("INT4", 64)
+    w = [dq.quantize_weights(_randn(NQ, K, 60 + o, 0.02), fmt="INT4", group=64) for o in range(3)]
+    r = [_col_scales(NQ, 70 + o) for o in range(3)]
+    acts = dq.quantize_weights(_randn(M, K, 80, 1.0), fmt="INT4", group=64)   # M x K codes
+    nb = dq.dq_quantized_linear_workspace_bytes(si, M, NQ, K)
+    wss = [torch.empty(nb, dtype=torch.uint8, device=DEV) for _ in range(3)]
+    ys_serial = [torch.empty(M, NQ, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    ys_graph = [torch.empty(M, NQ, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+
+    def layer(o, y, ws):
+        dq.dq_quantized_linear_ws(si, acts[0], acts[1], None, M, w[o][0], w[o][1], None, NQ, K,
+                                  r[o], y, ws)
+
+    side = [torch.cuda.Stream() for _ in range(3)]
+
+    def branches():
+        main = torch.cuda.current_stream()
+        for o in range(3):
+            side[o].wait_stream(main)
+            with torch.cuda.stream(side[o]):
+                layer(o, ys_graph[o], wss[o])
+        for o in range(3):
+            main.wait_stream(side[o])
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        branches()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        branches()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        new = dq.quantize_weights(_randn(M, K, 90 + rep, 1.0 + rep), fmt="INT4", group=64)
+        acts[0].copy_(new[0])
+        acts[1].copy_(new[1])
+        for y in ys_graph:
+            y.zero_()
+        torch.cuda.synchronize()
+        for o in range(3):
+            layer(o, ys_serial[o], wss[0])   # one stream, one workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o in range(3):
+            assert torch.equal(ys_serial[o].view(torch.uint8), ys_graph[o].view(torch.uint8)), (rep, o)
+            assert torch.count_nonzero(ys_graph[o]) > 0
