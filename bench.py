@@ -183,13 +183,46 @@ I8_MFMA_PEAK_TOPS = 5000.0       # MI355X dense int8 matrix-core peak
 I4_VALU_PER_OUTPUT_GROUP = 248 / 64
 
 
+def graph_ms_per_call(fn, steps, warmup):
+    """`fn` (calls that only enqueue kernels on the current stream) recorded `steps` times in
+    one HIP graph; ms per call from events around one replay.  Replayed, the launches follow
+    each other on the GPU without waiting on the host, so the figure is the kernels' time
+    and not the host's cost of issuing them from Python."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g
+    return ms
+
+
 def bench_linear(args, fmt):
     """The quantised linear layer on codes the solver and the activation quantiser made:
     the q_proj-shaped 4096x4096 weight solved to `fmt` (MXFP4, NVFP4 or INT4 with groups of
     64; T = 16), 2048 tokens of activations rescaled by the solved c and quantised to the
     same format, Y = Aq Q^T diag(r) in bf16.  MXFP4 runs on the FP4 block-scaled matrix
     cores, NVFP4 on the f16 cores after an exact dequantisation in the kernel, INT4 on the
-    int8 cores (exact int32 per group, bf16 scale products applied in fp32)."""
+    int8 cores (exact int32 per group, bf16 scale products applied in fp32).  Timed from a
+    HIP graph of `steps` calls (eager_* and wall_* fields: the calls issued from Python)."""
     import torch
 
     import post_quantization_dq_amd as dq
@@ -224,7 +257,8 @@ def bench_linear(args, fmt):
         b.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    eager_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms = graph_ms_per_call(call, args.steps, 1)
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     peak = F16_MFMA_PEAK_TFLOPS if nv else I8_MFMA_PEAK_TOPS if i4 else FP4_MFMA_PEAK_TFLOPS
@@ -247,7 +281,9 @@ def bench_linear(args, fmt):
                      "frac": round(tflops / peak, 4), "traffic": None,
                      "alg_flops_per_launch": flops, "avg_launch_ms": round(ms, 4),
                      "cores": cores},
-        "wall_ms_per_call": round(wall * 1e3, 4),
+        # the same calls issued one by one from Python: events around each call, and the
+        # host's wall time per call (issuing a call can take longer than its kernel)
+        "eager_ms_per_call": round(eager_ms, 4), "wall_ms_per_call": round(wall * 1e3, 4),
     }
     if i4:
         # the vector-ALU ceiling of this kernel (see I4_VALU_PER_OUTPUT_GROUP)
@@ -449,7 +485,8 @@ def bench_llama_w4a4(args):
 def bench_qkv_acts(args):
     """The fused multi-projection activation quantiser: 2048 tokens x 4096 bf16 activations
     quantised to NVFP4 for three projections (q, k, v), each with its own column scales, in
-    one dq_rescale_quantize_acts_multi call; three single calls are timed beside it."""
+    one dq_rescale_quantize_acts_multi call; three single calls are timed beside it.  Timed
+    from HIP graphs of `steps` calls (eager_ms_per_call: the fused call issued from Python)."""
     import torch
 
     import post_quantization_dq_amd as dq
@@ -483,7 +520,9 @@ def bench_qkv_acts(args):
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    ms_multi, ms_single = timed(multi), timed(singles)
+    eager_multi = timed(multi)
+    ms_multi = graph_ms_per_call(multi, args.steps, 1)
+    ms_single = graph_ms_per_call(singles, args.steps, 1)
     # algorithmic bytes: X read twice (amax pre-pass, quantise), codes + block scales written
     alg = 2 * M * K * 2 + n_out * (M * K // 2 + M * K // 16)
     gbs = alg / (ms_multi * 1e-3) / 1e9
@@ -499,6 +538,7 @@ def bench_qkv_acts(args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": None, "alg_bytes_per_call": alg},
         "three_single_calls_ms": round(ms_single, 4),
+        "eager_ms_per_call": round(eager_multi, 4),
     }
     print(json.dumps(out), flush=True)
 
