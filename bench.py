@@ -141,14 +141,14 @@ def bench_llama_set(args):
     for k in range(args.steps):
         # the last step carries a begin/end event pair on each solver launch, read after the wait
         dq.solve_many(probs, "NVFP4", T, workspace=ws, read_reports=False,
-                      timed_sweeps=(work_sweeps or 2 * T) if k == args.steps - 1 else 0)
+                      timed_sweeps=(work_sweeps or T + 1) if k == args.steps - 1 else 0)
     e1.record()
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
     passes = dq.timed_passes(probs, T)
     per_all = np.asarray(passes, dtype=np.float64).reshape(-1, 3)
-    # Sweeps 1..T run every matrix.  The INIT sweep is lighter, and the re-solve sweeps after
-    # rejections only run the matrices that rejected, so both stay out of the per-pass figures.
+    # Sweeps 1..T run every matrix; the INIT sweep is lighter and stays out of the per-pass
+    # figures.
     per = per_all[1:T + 1]
     avg = {k: float(per[:, q].mean()) for q, k in enumerate(KERNELS)}
     dom = max(KERNELS[:2], key=lambda k: float(per[:, KERNELS.index(k)].sum()))
@@ -643,7 +643,7 @@ def main():
     e0.record()
     for k in range(args.steps):
         # the last timed step also records a begin/end event pair on each solver kernel launch
-        step((work_sweeps or 2 * T) if k == args.steps - 1 else 0)
+        step((work_sweeps or T + 1) if k == args.steps - 1 else 0)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -665,8 +665,6 @@ def main():
     traffic = recorded_traffic(dom, args.workload) if copies == 1 else None
     nm = prob.nmse_hist.cpu().numpy()
     value = copies * m * n * T / (ms_step * 1e-3) / 1e9
-    # the step's solve queues 2T sweeps (room for a re-solve after every rejected step);
-    # those that find the solve finished exit at once
 
     out = {
         "metric": METRIC if (m, n, fmt) == (4096, 14336, "NVFP4")

@@ -100,7 +100,7 @@ enum {
                                       2^-119 or less) that 1/(6 s_t) or 1/(2^-9 s_t) is not a
                                       finite fp32 number: the matrix is quantised to 0 */
   DQ_FLAG_UNFINISHED = 32          /* the solve did not finish in the sweeps dq_solve queued
-                                      (never expected: T iterations need at most 2T sweeps) */
+                                      (never expected: T iterations take T + 1 sweeps) */
 };
 
 typedef struct {
@@ -169,10 +169,11 @@ size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_sp
  * would be absorbed by them exactly).
  * Problems are independent; count (1..65535) > 1 runs them together on one GPU.
  * Stream-ordered: the call uploads the problem descriptors (staged before it returns),
- * enqueues every sweep the solve may need -- the INIT sweep, one per iteration and one
- * re-solve after each rejected step, at most 2T -- and the output kernel, and returns without
- * waiting.  The number of sweeps that actually run depends on the data; the queued ones
- * that find every problem finished exit at once.  `workspace` must hold
+ * enqueues its T + 1 sweeps -- the INIT sweep and one per iteration; each sweep computes the
+ * next r- and c-steps for both outcomes of its Qhat-step's safeguard, so a rejected
+ * candidate costs no extra sweep -- and the output kernel, and returns without waiting.
+ * With tol_relchg > 0 a solve can finish early; the queued sweeps that find every problem
+ * finished exit at once.  `workspace` must hold
  * dq_workspace_bytes(...) bytes of device memory; its contents on entry do not matter, and
  * it must stay untouched until the solve's work has completed. */
 int dq_solve(const dq_problem* problems, int32_t count, dq_quant_spec spec,

@@ -6,15 +6,19 @@
 //               (Qhat-step of iteration s) and stores its codes, measures F(r^s,c^s,Qc), the
 //               change against the kept Qhat^{s-1} read back from its codes (relchg numerator,
 //               and dF = F(Qc) - F(Qhat^{s-1}) accumulated per lane, so unchanged elements add
-//               exactly 0 to the safeguard decision), and, assuming the candidate is kept,
-//               runs the r-step of iteration s+1 (whole-row sums, fp64 across lanes).
-//   k_colpass   workgroups own 1024-column strips and a range of rows; with the new r it
-//               accumulates the c-step sums N_j, D_j (and the NVFP4 column amax of W ./ r)
-//               in registers and writes one partial per row range.
+//               exactly 0 to the safeguard decision), and runs the r-step of iteration s+1
+//               for both outcomes of the safeguard: from the candidate (kept if dF <= 0) and
+//               from the kept Qhat^{s-1} (whole-row sums, fp64 across lanes).  The two differ
+//               only on the chunks whose codes changed.
+//   k_colpass   workgroups own 1024-column strips and a range of rows; each wave first
+//               reduces the row pass's dF partials (a fixed order, so every workgroup and the
+//               finalize reach the same decision), then, with the r of the outcome taken, it
+//               accumulates the c-step sums N_j, D_j (and the NVFP4 column amax of W ./ r) of
+//               that outcome's Qhat in registers and writes one partial per row range.
 //   k_finalize  reduces the partials and projects c; its first workgroup per problem takes
-//               the safeguard decision and writes the next sweep's state.  If the candidate
-//               is rejected the speculative r/c are discarded and the next iteration re-runs
-//               the r/c steps from the kept Qhat (FIXUP mode).
+//               the safeguard decision and writes the next sweep's state (after a rejection
+//               it moves the kept-Qhat r-step into place).  Every sweep therefore completes
+//               one iteration: a solve of T iterations is T + 1 sweeps, rejected steps or not.
 // Lane l of a wave owns chunks of 16 consecutive columns; blocks of MX (32) and INT4/INT8
 // (64/128) formats span 2..8 adjacent lanes.
 
@@ -25,7 +29,7 @@
 
 namespace dqk {
 
-enum Mode { MODE_INIT = 0, MODE_NORMAL = 1, MODE_FIXUP = 2, MODE_DONE = 3 };
+enum Mode { MODE_INIT = 0, MODE_NORMAL = 1, MODE_DONE = 3 };
 
 // Per-problem solver state.  It is double-buffered by sweep parity: the kernels of sweep sw
 // read st[sw & 1], and the decision at the end of sweep sw (k_finalize) writes the whole of
@@ -47,8 +51,8 @@ struct ReportDev {
 struct ProbDev {
   const void* W;
   int64_t rows, cols, ld;
-  float* r[2];
-  float* ir[2];
+  float* r[3];      // row scales: the current slot (state rs) and one per outcome of the next
+  float* ir[3];     // r-step, (rs + 1) % 3 from the candidate, (rs + 2) % 3 from the kept Qhat
   float* c[2];
   float* ic[2];
   uint8_t* codes[2];
@@ -61,6 +65,8 @@ struct ProbDev {
   uint32_t* flags;  // DQ_FLAG_* bits, set with atomics by any kernel
   double* nmse;     // [iters+1]
   double* relchg;   // [iters+1]
+  float* x_alt;     // [rows]: unprojected kept-Qhat r-step values (NaN: no closed form)
+  uint32_t* altz;   // nonzero: a row's kept-Qhat r-step had D = 0 in this sweep
   float* r_trace;   // [iters][rows] or null: unprojected r-step values
   float* c_trace;   // [iters][cols] or null: unprojected c-step values
   const float* r_init;
@@ -91,7 +97,7 @@ __device__ __forceinline__ State* state_slots(const int32_t* live, int prob) {
 }
 
 // Flag bit of a solve whose state did not reach DONE within the sweeps that were queued
-// (cannot happen: a solve of T iterations needs at most 2T sweeps).
+// (cannot happen: a solve of T iterations takes T + 1 sweeps).
 constexpr uint32_t kFlagUnfinished = 32u;
 
 // ---------------------------------------------------------------- loads and stores
@@ -190,6 +196,7 @@ __global__ void k_setup(const ProbDev* __restrict__ probs) {
     s->normW2 = 0.0;
     s->qn2_acc = 0.0;
     *P.flags = 0u;
+    *P.altz = 0u;
   }
 }
 
@@ -390,20 +397,64 @@ __device__ __forceinline__ void load16_global(const float* p, bool aligned, floa
 // Which iteration a pass belongs to, read from the problem's state at kernel entry.
 struct PassInfo {
   int mode, it, rs, cs, acc, cb, tr;
-  bool cand, stats, next;
+  bool stats, next, alt;
   __device__ __forceinline__ PassInfo(const State* st, int iters) {
     mode = st->mode;
     it = (mode == MODE_INIT) ? 0 : st->it_done + 1;
-    cand = (mode != MODE_FIXUP);
-    stats = (mode == MODE_NORMAL);
-    next = (mode == MODE_FIXUP) || (it < iters);
+    stats = (mode == MODE_NORMAL);           // a kept Qhat exists: safeguard and relchg
+    next = (it < iters);                     // the r/c steps of iteration it + 1 run now
+    alt = stats && next;                     // ... for both outcomes of the safeguard
     rs = st->rs;
     cs = st->cs;
     acc = st->acc;
-    cb = (mode == MODE_INIT) ? 0 : 1 - acc;      // buffer the candidate is written to
-    tr = (mode == MODE_FIXUP) ? it - 1 : it;     // trace row of the r/c steps computed now
+    cb = (mode == MODE_INIT) ? 0 : 1 - acc;  // buffer the candidate is written to
+    tr = it;                                 // trace row of the r/c steps computed now
   }
 };
+
+// Row-scale slots written by a sweep whose current slot is rs: the r-step from the candidate
+// and the one from the kept Qhat.
+__device__ __forceinline__ int slot_next(int rs) { return rs == 2 ? 0 : rs + 1; }
+__device__ __forceinline__ int slot_alt(int rs) { return rs == 0 ? 2 : rs - 1; }
+
+// dF = F(Qc) - F(kept Qhat) summed over the row pass's workgroup partials in one fixed order
+// (lane-strided, four partials per lane requested at once, then a butterfly whose result is
+// the same in every lane), so the column pass's workgroups and the finalize's decision all
+// reach the same value.  Every lane of the wave must take part in the butterfly.
+__device__ __forceinline__ double rowpass_dF_part(const ProbDev& P) {
+  const int lane = threadIdx.x & 63;
+  double s = 0.0;
+  for (int b0 = 0; b0 < P.rowblocks; b0 += 256) {
+    double v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = b0 + 64 * u + lane;
+      v[u] = b < P.rowblocks ? gp(P.swp)[4 * (size_t)b + 1] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s += v[u];
+  }
+  return s;
+}
+__device__ __forceinline__ double rowpass_dF_sum(double part) { return wave_sum(part); }
+__device__ __forceinline__ double rowpass_dF(const ProbDev& P) {
+  return rowpass_dF_sum(rowpass_dF_part(P));
+}
+
+// Exact products of the grouped integer formats' kept-Qhat r-step sums, as doubles.  With
+// projected (bf16) column scales, q = p c has at most 3 + 8 (INT4) or 7 + 8 (INT8) significant
+// bits, so w q for a bf16 weight (8 bits) and q^2 for INT4 are exact in fp32 and one fp32
+// multiply gives the same double as an fp64 multiply; the others are taken in fp64.
+template <int FMT, int DT>
+__device__ __forceinline__ double exact_wq(float w, float q) {
+  if (DT == 1) return (double)(w * q);
+  return (double)w * (double)q;
+}
+template <int FMT>
+__device__ __forceinline__ double exact_qq(float q) {
+  if (FMT == INT4) return (double)(q * q);
+  return (double)q * (double)q;
+}
 
 // ---------------------------------------------------------------- row pass
 // Words of one entry of the row pass's queue of changed chunks: the chunk index and block
@@ -497,8 +548,8 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
 
   const DQ_GAS float* rcur = gp(P.r[pi.rs]);
   const DQ_GAS float* ircur = gp(P.ir[pi.rs]);
-  DQ_GAS float* rnext = gp(P.r[1 - pi.rs]);
-  DQ_GAS float* irnext = gp(P.ir[1 - pi.rs]);
+  DQ_GAS float* rnext = gp(P.r[slot_next(pi.rs)]);
+  DQ_GAS float* irnext = gp(P.ir[slot_next(pi.rs)]);
   uint8_t* ccodes = P.codes[pi.cb];
   void* cscales = P.scales[pi.cb];
   const uint8_t* acodes = P.codes[pi.acc];
@@ -514,8 +565,12 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
   const int nloop = (nch + 63) >> 6;
   // equal block factors for equal scale codes (NVFP4: equal tensor scales)
   const bool cq = compact && pi.stats && (FMT != NVFP4 || s_t == st->st_acc);
+  const bool alt = pi.alt;
 
-  // the kept Qhat's error and the relchg terms of the `count` queued chunks of row i
+  // kept-Qhat r-step sums of the current row (the safeguard's other outcome)
+  double Nk = 0.0, Dk = 0.0;
+  // the kept Qhat's error, the relchg terms and the kept-Qhat r-step sums of the `count`
+  // queued chunks of row i
   auto flush = [&](int64_t i, float r_, int count) {
     __builtin_amdgcn_wave_barrier();
     if (lane < count) {
@@ -537,7 +592,8 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
       const float f = block_factor<FMT>(scq, tab_c);
       const float fp = block_factor<FMT>(ksq, tab_p);
       const float rfp = r_ * fp;
-      float Fpl = 0.0f, rl = 0.0f;
+      float Fpl = 0.0f, rl = 0.0f, Nbk = 0.0f, Dbk = 0.0f;
+      double Nbkd = 0.0, Dbkd = 0.0;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const float ppc = pp[k] * cc[k];
@@ -545,9 +601,27 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         Fpl = fmaf(ep, ep, Fpl);
         const float df = pq[k] * f - pp[k] * fp;
         rl = fmaf(df, df, rl);
+        if (alt) {   // the kept Qhat's r-step sums, as for the chunks computed inline
+          if (A64) {
+            Nbkd += exact_wq<FMT, DT>(w[k], ppc);
+            Dbkd += exact_qq<FMT>(ppc);
+          } else {
+            Nbk = fmaf(w[k], ppc, Nbk);
+            Dbk = fmaf(ppc, ppc, Dbk);
+          }
+        }
       }
       adF -= (double)Fpl;
       arel += (double)rl;
+      if (alt) {
+        if (A64) {
+          Nk += (double)fp * Nbkd;
+          Dk += ((double)fp * (double)fp) * Dbkd;
+        } else {
+          Nk += (double)fp * (double)Nbk;
+          Dk += (double)(fp * fp) * (double)Dbk;
+        }
+      }
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -556,6 +630,8 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
     const float r_ = rcur[i];
     const float ir_ = ircur[i];
     double Nrow = 0.0, Drow = 0.0;
+    Nk = 0.0;
+    Dk = 0.0;
     int qn = 0;   // queued chunks of this row (wave-uniform)
     for (int kk = 0; kk < nloop; ++kk) {
       const int chn = lane + 64 * kk;
@@ -570,123 +646,136 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
       float w[16];
       raw.unpack(w);
       float p[16];
-      float f;
       float Nb = 0.0f, Db = 0.0f;
       double Nbd = 0.0, Dbd = 0.0;
       float cc[16];
-      if (pi.cand) {
-        float v[16];
-        {
-          float icc[16];
-          if (CG) load16_global(icglob + 16 * (int64_t)cl, true, icc);
-          else lds_load16(s_ic4, nch, cl, icc);
+      float v[16];
+      {
+        float icc[16];
+        if (CG) load16_global(icglob + 16 * (int64_t)cl, true, icc);
+        else lds_load16(s_ic4, nch, cl, icc);
 #pragma unroll
-          for (int k = 0; k < 16; ++k) v[k] = (w[k] * ir_) * icc[k];
+        for (int k = 0; k < 16; ++k) v[k] = (w[k] * ir_) * icc[k];
+      }
+      Chunk ch;
+      quantize_chunk<FMT, L>(v, qc, ch);
+      // Every chunk is written, changed or not: skipping the unchanged ones (a few percent
+      // change per iteration) leaves sparse 8-byte writes in partly written lines, and the
+      // pass got slower (43.9 against 38.3 us on 4096 x 14336 NVFP4).
+      if (valid) store_chunk<FMT, L>(ccodes, cscales, i, n, chn, g, ch);
+      uflow |= ch.underflow && valid;
+      const float f = ch.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) p[k] = ch.p[k];
+      if (CG) load16_global(cglob + 16 * (int64_t)cl, true, cc);
+      else lds_load16(s_c4, nch, cl, cc);
+      const float rf = r_ * f;
+      float Fl = 0.0f, ql = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float pc = p[k] * cc[k];
+        const float e = fmaf(-rf, pc, w[k]);
+        Fl = fmaf(e, e, Fl);
+        if (A64) {
+          Nbd = fma((double)w[k], (double)pc, Nbd);
+          Dbd = fma((double)pc, (double)pc, Dbd);
+        } else {
+          Nb = fmaf(w[k], pc, Nb);
+          Db = fmaf(pc, pc, Db);
         }
-        Chunk ch;
-        quantize_chunk<FMT, L>(v, qc, ch);
-        // Every chunk is written, changed or not: skipping the unchanged ones (a few percent
-        // change per iteration) leaves sparse 8-byte writes in partly written lines, and the
-        // pass got slower (43.9 against 38.3 us on 4096 x 14336 NVFP4).
-        if (valid) store_chunk<FMT, L>(ccodes, cscales, i, n, chn, g, ch);
-        uflow |= ch.underflow && valid;
-        f = ch.f;
+        ql = fmaf(p[k], p[k], ql);
+      }
+      float Fpl = 0.0f, rl = 0.0f;
+      bool changed = false, queued = false;
+      if (cq) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) p[k] = ch.p[k];
-        if (CG) load16_global(cglob + 16 * (int64_t)cl, true, cc);
-        else lds_load16(s_c4, nch, cl, cc);
-        const float rf = r_ * f;
-        float Fl = 0.0f, ql = 0.0f;
+        for (int w4 = 0; w4 < code_words<FMT>(); ++w4) changed |= ch.code[w4] != pk[w4];
+        changed = valid && (changed || ch.scode != ps);
+        const uint64_t mask = __ballot(changed);
+        const int cnt = __popcll(mask);
+        queued = qn + cnt <= kQueueLen;   // wave-uniform; a full queue falls back to inline
+        if (queued && mask) {
+          const int pos = qn + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+          if (changed) {
+            uint32_t* e = queue + pos * QW;
+            e[0] = (uint32_t)chn | (ch.scode << 16);
+#pragma unroll
+            for (int w4 = 0; w4 < code_words<FMT>(); ++w4) e[1 + w4] = ch.code[w4];
+          }
+          qn += cnt;
+        }
+      }
+      // kept-Qhat r-step terms of this chunk: its own where they are computed inline (here),
+      // the candidate's where the codes are unchanged (below), at the flush where queued
+      double kN = 0.0, kD = 0.0;
+      if (pi.stats && !queued) {
+        float pp[16];
+        decode_grid<FMT>(pk, pp);
+        const float fp = block_factor<FMT>(ps, tab_p);
+        const float rfp = r_ * fp;
+        float Nbk = 0.0f, Dbk = 0.0f;
+        double Nbkd = 0.0, Dbkd = 0.0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          const float pc = p[k] * cc[k];
-          const float e = fmaf(-rf, pc, w[k]);
-          Fl = fmaf(e, e, Fl);
-          if (A64) {
-            Nbd = fma((double)w[k], (double)pc, Nbd);
-            Dbd = fma((double)pc, (double)pc, Dbd);
-          } else {
-            Nb = fmaf(w[k], pc, Nb);
-            Db = fmaf(pc, pc, Db);
-          }
-          ql = fmaf(p[k], p[k], ql);
-        }
-        float Fpl = 0.0f, rl = 0.0f;
-        bool changed = false, queued = false;
-        if (cq) {
-#pragma unroll
-          for (int w4 = 0; w4 < code_words<FMT>(); ++w4) changed |= ch.code[w4] != pk[w4];
-          changed = valid && (changed || ch.scode != ps);
-          const uint64_t mask = __ballot(changed);
-          const int cnt = __popcll(mask);
-          queued = qn + cnt <= kQueueLen;   // wave-uniform; a full queue falls back to inline
-          if (queued && mask) {
-            const int pos = qn + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-            if (changed) {
-              uint32_t* e = queue + pos * QW;
-              e[0] = (uint32_t)chn | (ch.scode << 16);
-#pragma unroll
-              for (int w4 = 0; w4 < code_words<FMT>(); ++w4) e[1 + w4] = ch.code[w4];
+          const float ppc = pp[k] * cc[k];
+          const float ep = fmaf(-rfp, ppc, w[k]);
+          Fpl = fmaf(ep, ep, Fpl);
+          // difference of the two dequantised values, each rounded to fp32 as the
+          // values themselves are: exactly 0 where Qhat did not change
+          const float df = p[k] * f - pp[k] * fp;
+          rl = fmaf(df, df, rl);
+          if (alt) {
+            if (A64) {   // exact products, summed in fp64 as in the candidate's sums
+              Nbkd += exact_wq<FMT, DT>(w[k], ppc);
+              Dbkd += exact_qq<FMT>(ppc);
+            } else {
+              Nbk = fmaf(w[k], ppc, Nbk);
+              Dbk = fmaf(ppc, ppc, Dbk);
             }
-            qn += cnt;
           }
         }
-        if (pi.stats && !queued) {
-          float pp[16];
-          decode_grid<FMT>(pk, pp);
-          const float fp = block_factor<FMT>(ps, tab_p);
-          const float rfp = r_ * fp;
-#pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const float ppc = pp[k] * cc[k];
-            const float ep = fmaf(-rfp, ppc, w[k]);
-            Fpl = fmaf(ep, ep, Fpl);
-            // difference of the two dequantised values, each rounded to fp32 as the
-            // values themselves are: exactly 0 where Qhat did not change
-            const float df = p[k] * f - pp[k] * fp;
-            rl = fmaf(df, df, rl);
-          }
-        }
-        if (valid) {
-          aFc += (double)Fl;
-          // queued chunks: the candidate's error now, the kept one's at the flush; unchanged
-          // chunks under compaction add 0
-          adF += queued ? (changed ? (double)Fl : 0.0) : (double)Fl - (double)Fpl;
-          arel += (double)rl;
-          aqn += (double)(f * f) * (double)ql;
-        }
-      } else {
-        decode_grid<FMT>(pk, p);
-        f = block_factor<FMT>(ps, tab_p);
-        if (CG) load16_global(cglob + 16 * (int64_t)cl, true, cc);
-        else lds_load16(s_c4, nch, cl, cc);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const float pc = p[k] * cc[k];
-          if (A64) {
-            Nbd = fma((double)w[k], (double)pc, Nbd);
-            Dbd = fma((double)pc, (double)pc, Dbd);
-          } else {
-            Nb = fmaf(w[k], pc, Nb);
-            Db = fmaf(pc, pc, Db);
-          }
+        if (A64) {
+          kN = (double)fp * Nbkd;
+          kD = ((double)fp * (double)fp) * Dbkd;
+        } else {
+          kN = (double)fp * (double)Nbk;
+          kD = (double)(fp * fp) * (double)Dbk;
         }
       }
       if (valid) {
+        aFc += (double)Fl;
+        // queued chunks: the candidate's error now, the kept one's at the flush; unchanged
+        // chunks under compaction add 0
+        adF += queued ? (changed ? (double)Fl : 0.0) : (double)Fl - (double)Fpl;
+        arel += (double)rl;
+        aqn += (double)(f * f) * (double)ql;
+        double cN, cD;
         if (A64) {
-          Nrow += (double)f * Nbd;
-          Drow += ((double)f * (double)f) * Dbd;
+          cN = (double)f * Nbd;
+          cD = ((double)f * (double)f) * Dbd;
         } else {
-          Nrow += (double)f * (double)Nb;
-          Drow += (double)(f * f) * (double)Db;
+          cN = (double)f * (double)Nb;
+          cD = (double)(f * f) * (double)Db;
+        }
+        Nrow += cN;
+        Drow += cD;
+        if (alt && !(queued && changed)) {
+          Nk += queued ? cN : kN;
+          Dk += queued ? cD : kD;
         }
       }
     }
     if (qn > 0) flush(i, r_, qn);   // wave-uniform
     if (pi.next) {
-      // r-step of the next iteration from the whole row (fixed butterfly order in fp64)
+      // r-step of the next iteration from the whole row (fixed butterfly order in fp64), from
+      // the candidate and, when a kept Qhat exists, from the kept one
       const double N = wave_sum(Nrow), D = wave_sum(Drow);
+      double N2 = 0.0, D2 = 0.0;
+      if (alt) {
+        N2 = wave_sum(Nk);
+        D2 = wave_sum(Dk);
+      }
       if (lane == 0) {
         float x = __builtin_nanf(""), rnew = r_;
         if (!(P.steps & 1)) {
@@ -700,23 +789,35 @@ __global__ __launch_bounds__(1024) void k_rowpass(const ProbDev* __restrict__ pr
         rnext[i] = rnew;
         irnext[i] = 1.0f / rnew;
         if (P.r_trace) gp(P.r_trace)[(int64_t)pi.tr * P.rows + i] = x;
+        if (alt) {
+          // a row with D = 0 here is flagged by the finalize if this outcome is taken
+          float x2 = __builtin_nanf(""), r2 = r_;
+          if (!(P.steps & 1)) {
+          } else if (D2 > 0.0) {
+            x2 = (float)(N2 / D2);
+            r2 = project<FMT>(x2);
+          } else {
+            atomicOr(P.altz, 1u);
+          }
+          gp(P.r[slot_alt(pi.rs)])[i] = r2;
+          gp(P.ir[slot_alt(pi.rs)])[i] = 1.0f / r2;
+          if (P.r_trace) gp(P.x_alt)[i] = x2;
+        }
       }
     }
   }
 
-  if (pi.cand) {
+  {
     const double a0 = wave_sum(aFc), a1 = wave_sum(adF), a2 = wave_sum(arel), a3 = wave_sum(aqn);
     if (lane == 0) { redw[wave][0] = a0; redw[wave][1] = a1; redw[wave][2] = a2; redw[wave][3] = a3; }
   }
   const bool anyu = __syncthreads_or(uflow);
   const bool anyz = __syncthreads_or(zrow);
   if (t == 0) {
-    if (pi.cand) {
-      double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-      for (int k = 0; k < nw; ++k) { s0 += redw[k][0]; s1 += redw[k][1]; s2 += redw[k][2]; s3 += redw[k][3]; }
-      DQ_GAS double* o = gp(P.swp + 4 * (size_t)we.idx);
-      o[0] = s0; o[1] = s1; o[2] = s2; o[3] = s3;
-    }
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    for (int k = 0; k < nw; ++k) { s0 += redw[k][0]; s1 += redw[k][1]; s2 += redw[k][2]; s3 += redw[k][3]; }
+    DQ_GAS double* o = gp(P.swp + 4 * (size_t)we.idx);
+    o[0] = s0; o[1] = s1; o[2] = s2; o[3] = s3;
     const uint32_t fl = (anyu ? 8u : 0u) | (anyz ? 2u : 0u);
     if (fl) atomicOr(P.flags, fl);
   }
@@ -749,19 +850,31 @@ __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
   const int strip = we.idx % P.nstrips, rr = we.idx / P.nstrips;
   const int t = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int chn = strip * 64 + lane;
-  const bool act = chn < nch;
-  const int j0 = 16 * chn;
-  // the Qhat these sums use: the candidate just written (kept speculatively), or the kept one
-  const int qb = (pi.mode == MODE_FIXUP) ? pi.acc : pi.cb;
+  // lanes past the matrix's last chunk work on its first chunk; their sums are never stored
+  const int chl = chn < nch ? chn : 0;
+  const int j0 = 16 * chl;
+  // The outcome of the safeguard is the same in every wave and workgroup: a kept candidate
+  // gives the sums over its codes with the r-step from it, a rejected one the sums over the
+  // kept Qhat with the r-step from that.  Each wave requests the row pass's dF partials and,
+  // alongside, its first rows with the candidate's codes (kept on most sweeps); it learns the
+  // outcome before its first products and reloads those rows' codes and r after a rejection.
+  const bool decide = pi.stats;
+  int qb = pi.cb, rslot = slot_next(pi.rs);
   const uint8_t* qcodes = P.codes[qb];
   const void* qscales = P.scales[qb];
-  const DQ_GAS float* rnew = gp(P.r[1 - pi.rs]);
-  const DQ_GAS float* irnew = gp(P.ir[1 - pi.rs]);
-  __shared__ NvTab tab;
+  const DQ_GAS float* rnew = gp(P.r[rslot]);
+  const DQ_GAS float* irnew = gp(P.ir[rslot]);
+  __shared__ NvTab tabs[2];   // [0]: the candidate's tensor scale, [1]: the kept Qhat's
+  const NvTab* tab = &tabs[0];
   if (FMT == NVFP4) {
-    build_nvtab(tab, (pi.mode == MODE_FIXUP) ? st->st_acc : st->st_cur);
+    build_nvtab(tabs[0], st->st_cur);
+    if (decide) build_nvtab(tabs[1], st->st_acc);
     __syncthreads();
   }
+  // requested after the barrier, which would otherwise wait for them
+  double dpart = 0.0;
+  if (decide) dpart = rowpass_dF_part(P);
+  bool pending = decide;   // wave-uniform: the outcome is not applied yet
 
   acc_t cN[16], cD[16];
   float cM[16];
@@ -770,47 +883,64 @@ __device__ __forceinline__ void colpass_body(const ProbDev* __restrict__ probs,
   const int64_t row0 = (int64_t)rr * P.rows_per_range;
   const int64_t row1 = min(P.rows, row0 + P.rows_per_range);
   constexpr int U = A64 ? 1 : 2;   // rows in flight per wave
-  if (act) {
-    for (int64_t i0 = row0 + wave; i0 < row1; i0 += 8 * U) {
-      RawRow<DT> raw[U];
-      uint32_t cw[U][4], sc[U];
-      float rr_[U], irn[U];
+  for (int64_t i0 = row0 + wave; i0 < row1; i0 += 8 * U) {
+    RawRow<DT> raw[U];
+    uint32_t cw[U][4], sc[U];
+    float rr_[U], irn[U];
+    int64_t ix[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        // rows past the range load the range's last row (not summed): every row's loads are
-        // issued on one path, so the compiler's wait before a row's products leaves the later
-        // rows' loads in flight
-        const int64_t i = i0 + 8 * u < row1 ? i0 + 8 * u : row1 - 1;
-        raw[u].load(P.W, i, P.ld, j0);
-        load_codes<FMT, L>(qcodes, qscales, i, n, chn, g, cw[u], sc[u]);
-        rr_[u] = rnew[i];
-        irn[u] = (FMT == NVFP4) ? irnew[i] : 0.0f;
-      }
+    for (int u = 0; u < U; ++u) {
+      // rows past the range load the range's last row (not summed): every row's loads are
+      // issued on one path, so the compiler's wait before a row's products leaves the later
+      // rows' loads in flight
+      ix[u] = i0 + 8 * u < row1 ? i0 + 8 * u : row1 - 1;
+      raw[u].load(P.W, ix[u], P.ld, j0);
+      load_codes<FMT, L>(qcodes, qscales, ix[u], n, chl, g, cw[u], sc[u]);
+      rr_[u] = rnew[ix[u]];
+      irn[u] = (FMT == NVFP4) ? irnew[ix[u]] : 0.0f;
+    }
+    if (pending) {   // first trip of the wave
+      pending = false;
+      if (!(rowpass_dF_sum(dpart) <= 0.0)) {
+        qb = pi.acc;
+        rslot = slot_alt(pi.rs);
+        qcodes = P.codes[qb];
+        qscales = P.scales[qb];
+        rnew = gp(P.r[rslot]);
+        irnew = gp(P.ir[rslot]);
+        tab = &tabs[1];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (i0 + 8 * u >= row1) break;
-        float w[16], p[16];
-        // keep the scale code's use (and so the wait for it, which in order covers this row's
-        // other loads) here, after the previous row's products
-        asm volatile("" : "+v"(sc[u]));
-        raw[u].unpack(w);
-        decode_grid<FMT>(cw[u], p);
-        const float f = block_factor<FMT>(sc[u], &tab);
-        const float rf = rr_[u] * f;
-        const float rf2 = rf * rf;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          if (A64) {   // INT4/INT8: rf = r * s and rf * p are exact in fp32 (bf16 x bf16 x at
-                       // most 7 bits); products exact in fp64
-            cN[k] = fma((double)rf, (double)w[k] * (double)p[k], (double)cN[k]);
-            const double rp = (double)(rf * p[k]);
-            cD[k] = fma(rp, rp, (double)cD[k]);
-          } else {
-            cN[k] = fmaf(rf, w[k] * p[k], (float)cN[k]);
-            cD[k] = fmaf(rf2, p[k] * p[k], (float)cD[k]);
-          }
-          if (FMT == NVFP4) cM[k] = fmaxf(cM[k], fabsf(w[k] * irn[u]));
+        for (int u = 0; u < U; ++u) {
+          load_codes<FMT, L>(qcodes, qscales, ix[u], n, chl, g, cw[u], sc[u]);
+          rr_[u] = rnew[ix[u]];
+          irn[u] = (FMT == NVFP4) ? irnew[ix[u]] : 0.0f;
         }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + 8 * u >= row1) break;
+      float w[16], p[16];
+      // keep the scale code's use (and so the wait for it, which in order covers this row's
+      // other loads) here, after the previous row's products
+      asm volatile("" : "+v"(sc[u]));
+      raw[u].unpack(w);
+      decode_grid<FMT>(cw[u], p);
+      const float f = block_factor<FMT>(sc[u], tab);
+      const float rf = rr_[u] * f;
+      const float rf2 = rf * rf;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (A64) {   // INT4/INT8: rf = r * s and rf * p are exact in fp32 (bf16 x bf16 x at
+                     // most 7 bits); products exact in fp64
+          cN[k] = fma((double)rf, (double)w[k] * (double)p[k], (double)cN[k]);
+          const double rp = (double)(rf * p[k]);
+          cD[k] = fma(rp, rp, (double)cD[k]);
+        } else {
+          cN[k] = fmaf(rf, w[k] * p[k], (float)cN[k]);
+          cD[k] = fmaf(rf2, p[k] * p[k], (float)cD[k]);
+        }
+        if (FMT == NVFP4) cM[k] = fmaxf(cM[k], fabsf(w[k] * irn[u]));
       }
     }
   }
@@ -889,7 +1019,7 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
     return;
   }
   const int it = (mode == MODE_INIT) ? 0 : st->it_done + 1;
-  const bool next = (mode == MODE_FIXUP) || (it < P.iters);
+  const bool next = (it < P.iters);
   const int cs = st->cs;
   const int64_t n = P.cols;
 
@@ -954,7 +1084,7 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
         const float icn = 1.0f / cnew;
         gp(P.c[1 - cs])[j] = cnew;
         gp(P.ic[1 - cs])[j] = icn;
-        if (P.c_trace) gp(P.c_trace)[(int64_t)((mode == MODE_FIXUP) ? it - 1 : it) * n + j] = x;
+        if (P.c_trace) gp(P.c_trace)[(int64_t)it * n + j] = x;
         if (FMT == NVFP4) am = M * icn;
       }
       if (FMT == NVFP4 && part == 0) {
@@ -970,14 +1100,19 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
     return;
   }
 
-  // decision: fixed-order reductions of the row pass's partials, strided per thread, then a
-  // pairwise tree over the 256 threads
+  // decision: dF in the column pass's order (the same outcome there and here); after a
+  // rejection the next sweep takes the kept-Qhat r-step (its slot, its trace row, its flag)
+  // statistics: fixed-order reductions of the row pass's partials, strided per thread, then
+  // a pairwise tree over the 256 threads (F(Qc), relchg numerator, ||Qc||^2; dF as above)
   double f[4] = {0.0, 0.0, 0.0, 0.0};
-  if (mode != MODE_FIXUP) {
-    for (int s = t; s < P.rowblocks; s += 256) {
-      const DQ_GAS double* o = gp(P.swp + 4 * (size_t)s);
-      f[0] += o[0]; f[1] += o[1]; f[2] += o[2]; f[3] += o[3];
-    }
+  for (int s = t; s < P.rowblocks; s += 256) {
+    const DQ_GAS double* o = gp(P.swp + 4 * (size_t)s);
+    f[0] += o[0]; f[2] += o[2]; f[3] += o[3];
+  }
+  const double dF = rowpass_dF(P);
+  if (mode == MODE_NORMAL && next && !(dF <= 0.0) && P.r_trace) {
+    const int64_t m = P.rows;
+    for (int64_t i = t; i < m; i += 256) gp(P.r_trace)[(int64_t)it * m + i] = gp(P.x_alt)[i];
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) tr[q * 256 + t] = f[q];
@@ -990,7 +1125,9 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
   }
   __syncthreads();
   if (t != 0) return;
-  const double Fc = tr[0], dF = tr[256], rel = tr[512], qn = tr[768];
+  const double Fc = tr[0], rel = tr[512], qn = tr[768];
+  const uint32_t az = *gp(P.altz);
+  *gp(P.altz) = 0u;   // read by this decision only; the next row pass runs after it
 
   State ns = *st;
   const double nW = st->normW2;
@@ -1014,12 +1151,12 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
     } else {
       ns.rejected += 1;
       if (P.nmse) P.nmse[it] = nW > 0.0 ? (Fc - dF) / nW : 0.0;
+      if (az && next) atomicOr(P.flags, 2u);   // a row whose kept Qhat is all zero
     }
     if (P.relchg) P.relchg[it] = relv;
     ns.it_done = it;
   }
-  const bool stop = (mode != MODE_FIXUP) &&
-                    (it >= P.iters || (mode == MODE_NORMAL && P.tol > 0.0f && relv <= (double)P.tol));
+  const bool stop = it >= P.iters || (mode == MODE_NORMAL && P.tol > 0.0f && relv <= (double)P.tol);
   ns.needs_ts = 0;
   if (stop) {
     ns.mode = MODE_DONE;
@@ -1027,14 +1164,13 @@ __global__ __launch_bounds__(256) void k_finalize(const ProbDev* __restrict__ pr
     *sn = ns;
     atomicSub(live, 1);   // after the state: a later sweep that sees 0 reads no state
     return;
-  } else if (accepted) {
-    ns.rs = 1 - st->rs;
-    ns.cs = 1 - st->cs;
-    ns.needs_ts = (FMT == NVFP4) ? 1 : 0;   // from this finalize's amax partials
-    ns.mode = MODE_NORMAL;
-  } else {
-    ns.mode = MODE_FIXUP;
   }
+  // the r and c of the outcome taken (r moved into place above after a rejection); the kept
+  // Qhat stays in its buffer after a rejection
+  ns.rs = accepted ? slot_next(st->rs) : slot_alt(st->rs);
+  ns.cs = 1 - st->cs;
+  ns.needs_ts = (FMT == NVFP4) ? 1 : 0;   // from this finalize's amax partials
+  ns.mode = MODE_NORMAL;
   ns.sweeps += 1;
   *sn = ns;
 }

@@ -101,7 +101,7 @@ constexpr int64_t kMaxRowRanges = 64;
 // Caps for large batches: many workgroups of bounded size keep the last wave of workgroups
 // short; a single projection-sized matrix stays below both.
 constexpr int64_t kMaxRowsPerBlk = 256;
-// Iterations per solve: the queued sweeps (2 T) and the history buffers stay modest.
+// Iterations per solve: the queued sweeps (T + 1) and the history buffers stay modest.
 constexpr int kMaxIters = 1 << 16;
 constexpr int64_t kMaxRowsPerRange = 512;
 // Standalone quantiser geometry: one chunk per lane, up to 1024 threads; rows wider than
@@ -242,8 +242,8 @@ int make_plan(const dq_problem* p, int32_t count, int g, int fmt, int iters, Pla
     d.fin_wgs = (int32_t)((d.cols + 63) / 64);
     d.init_wgs = (int32_t)std::min<int64_t>(1024, d.rows);
     pl.prob_off[k] = off;
-    off = align_up(off + sizeof(uint32_t));                            // flags
-    off = align_up(off + 4 * sizeof(float) * d.rows);                  // r[2], ir[2]
+    off = align_up(off + 2 * sizeof(uint32_t));                        // flags, altz
+    off = align_up(off + 7 * sizeof(float) * d.rows);                  // r[3], ir[3], x_alt
     off = align_up(off + 4 * sizeof(float) * d.cols);                  // c[2], ic[2]
     off = align_up(off + code_bytes(fmt, d.rows, d.cols));             // codes buffer 1
     off = align_up(off + (size_t)d.rows * d.cols / g * scale_bytes(fmt));
@@ -289,9 +289,14 @@ void bind_pointers(const dq_problem* p, int32_t count, int g, int fmt, int iters
     char* q = ws + pl.prob_off[k];
     auto take = [&](size_t bytes) { char* r = q; q += align_up(bytes); return r; };
     d.st = (State*)(ws + pl.live_off + kStatesOffset) + 2 * k;
-    d.flags = (uint32_t*)take(sizeof(uint32_t));
-    float* rr = (float*)take(4 * sizeof(float) * d.rows);
-    d.r[0] = rr; d.r[1] = rr + d.rows; d.ir[0] = rr + 2 * d.rows; d.ir[1] = rr + 3 * d.rows;
+    d.flags = (uint32_t*)take(2 * sizeof(uint32_t));
+    d.altz = d.flags + 1;
+    float* rr = (float*)take(7 * sizeof(float) * d.rows);
+    for (int q = 0; q < 3; ++q) {
+      d.r[q] = rr + q * d.rows;
+      d.ir[q] = rr + (3 + q) * d.rows;
+    }
+    d.x_alt = rr + 6 * d.rows;
     float* cc = (float*)take(4 * sizeof(float) * d.cols);
     d.c[0] = cc; d.c[1] = cc + d.cols; d.ic[0] = cc + 2 * d.cols; d.ic[1] = cc + 3 * d.cols;
     d.codes[0] = p[k].codes;
@@ -743,10 +748,10 @@ size_t dq_workspace_bytes(const dq_problem* problems, int32_t count, dq_quant_sp
   return pl.total;
 }
 
-// Sweeps a solve of T iterations queues: the INIT sweep and one per iteration, plus one
-// re-solve sweep after each rejected step whose iteration is not the last (a rejection at
-// iteration T ends the solve), i.e. at most 2T (1 for T = 0).
-static int max_sweeps(int iters) { return iters > 0 ? 2 * iters : 1; }
+// Sweeps a solve of T iterations queues: the INIT sweep and one per iteration.  Each sweep
+// computes the next r and c steps for both outcomes of its safeguard, so a rejected step
+// costs no extra sweep.
+static int max_sweeps(int iters) { return iters + 1; }
 
 // The solve, stream-ordered.  With `timed_sweeps` > 0, a begin/end event pair is attached to
 // each pass's launches (row pass, column pass, finalize + decision, all groups) of the first
