@@ -47,11 +47,11 @@ METRIC = "BCD solver Gelem/s per iteration + achieved HBM GB/s vs peak (4096×14
 
 
 KERNELS = ("k_rowpass", "k_colpass", "k_finalize")
-# The row pass's second roof, VALU issue: 299 VALU instructions per wave and 64 chunks of 16
-# elements (NVFP4 codes, bf16 weight; SQ_INSTS_VALU per working dispatch over its 57344
-# wave-trips), i.e. 299 / 16 lane-operations per element, against 256 CUs x 64 lanes x 2.4 GHz
-# = 39.3 T lane-operations/s (unpacked fp32).
-ROWPASS_VALU_PER_ELEM = {("NVFP4", 2): 299 / 16}
+# The row pass's second roof, VALU issue: 310.6 VALU instructions per wave and 64 chunks of
+# 16 elements (NVFP4 codes, bf16 weight; SQ_INSTS_VALU per working dispatch over its 57344
+# wave-trips), i.e. 310.6 / 16 lane-operations per element, against 256 CUs x 64 lanes x
+# 2.4 GHz = 39.3 T lane-operations/s (unpacked fp32).
+ROWPASS_VALU_PER_ELEM = {("NVFP4", 2): 310.6 / 16}
 VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9
 
 
