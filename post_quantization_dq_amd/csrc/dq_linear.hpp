@@ -404,22 +404,30 @@ __global__ __launch_bounds__(256) void k_linear_dma(LinArgs p) {
     const uint8_t* cur = lin_lds + (st % G::D) * G::STAGE;
     const uint8_t* sa_t = cur + 2 * G::TILE;
     const uint8_t* sb_t = sa_t + G::STILE;
-    // every fragment and scale read of the stage first, then its products: one wait for
-    // the LDS instead of one per row of products
+    // LDS reads of the stage: the scale words and the first instruction step's fragments,
+    // which its products wait for in full; each later step's fragments are issued before the
+    // products of the step before it, so those reads overlap products (never more than 15
+    // reads outstanding, so the waits the compiler inserts count them exactly)
     v8i a[G::NI][4], b[G::NI][4];
     int sa[G::NI][4], sb[G::NI][4];
+    uint64_t sw8s[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int op = 0; op < 2; ++op) {
-        const int r = (op ? wn : wm) + 16 * i + r16;
-        const uint8_t* rp = cur + op * G::TILE + r * G::ROWB;
-        const int sw = dma_swz<FMT>(r);
         // the row's scale bytes of this stage in one read (the four lanes of a row share it)
-        const uint8_t* srow = (op ? sb_t : sa_t) + r * G::SPR;
-        const uint64_t sw8 = (G::SPR == 8) ? *(const uint64_t*)srow : (uint64_t)*(const uint32_t*)srow;
+        const uint8_t* srow = (op ? sb_t : sa_t) + ((op ? wn : wm) + 16 * i + r16) * G::SPR;
+        sw8s[i][op] = (G::SPR == 8) ? *(const uint64_t*)srow : (uint64_t)*(const uint32_t*)srow;
+      }
+    }
+    auto frags = [&](int u) {
 #pragma unroll
-        for (int u = 0; u < G::NI; ++u) {
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int op = 0; op < 2; ++op) {
+          const int r = (op ? wn : wm) + 16 * i + r16;
+          const uint8_t* rp = cur + op * G::TILE + r * G::ROWB;
+          const int sw = dma_swz<FMT>(r);
           v8i v;
           if (G::EB == 4) {
             const u32x4 x = *(const u32x4*)(rp + 16 * ((4 * u + g) ^ sw));
@@ -429,20 +437,36 @@ __global__ __launch_bounds__(256) void k_linear_dma(LinArgs p) {
             const u32x4 y = *(const u32x4*)(rp + 16 * ((4 + g) ^ sw));
             v = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
           }
-          const int sv = (int)((sw8 >> (8 * (4 * u + g))) & 0xFFu);
-          if (op) { b[u][i] = v; sb[u][i] = sv; } else { a[u][i] = v; sa[u][i] = sv; }
+          if (op) b[u][i] = v; else a[u][i] = v;
         }
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < G::NI; ++u)
+    };
+    auto products = [&](int u) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[u][j], a[u][i], acc[i][j], F,
                                                                         F, 0, sb[u][j], 0, sa[u][i]);
+    };
+    frags(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < G::NI; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa[u][i] = (int)((sw8s[i][0] >> (8 * (4 * u + g))) & 0xFFu);
+        sb[u][i] = (int)((sw8s[i][1] >> (8 * (4 * u + g))) & 0xFFu);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 1; u < G::NI; ++u) {
+      frags(u);
+      __builtin_amdgcn_sched_barrier(0);
+      products(u - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    products(G::NI - 1);
   }
 
   lin_store<OUT_BF16>(acc, p, mt0 + wm, nt0 + wn, 1.0f);
